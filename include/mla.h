@@ -1,0 +1,203 @@
+/*
+ * mla.h - C ABI of the latent-KV chunk-attention library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The library implements one layer's streaming chunk-attention step of
+ * VideoMLA ("VideoMLA: Low-Rank Latent KV Cache for Minute-Scale
+ * Autoregressive Video Diffusion"):
+ *   - every token x_t is compressed to a shared content latent
+ *     c_t = W_dkv x_t and one head-shared, unrotated positional key
+ *     kR_t = W_kR x_t, and only those d_c + d_rope scalars are cached
+ *     (hyper.ai summary, Method section; 192 + 32 = 224 instead of 3072 at
+ *     the Wan2.1-1.3B shape: ai-papers.net explainer, paragraph under Fig. 1);
+ *   - the cache is a fixed-size sliding window of frames (chatpaper.ai,
+ *     English abstract);
+ *   - at attention time the positional key is rotated by 3D-RoPE over
+ *     (t, y, x), and head h's score is the content part q_nope . (W_uk[h] c)
+ *     plus the positional part R(p_q) qR . R(p_k) kR; the value is
+ *     W_uv[h] c (hyper.ai summary, Method section).
+ * The library evaluates the content score and the value through the latent
+ * (the "absorbed" form: (W_uk[h]^T q_nope) . c, and W_uv[h] (sum_j p_j c_j)),
+ * which is the same value re-associated.
+ *
+ * Conventions for every entry point
+ *   - Pointers marked (device) are HIP device memory; (host) are host memory
+ *     read only during the call. The caller owns every buffer; the library
+ *     keeps no pointer after returning and allocates nothing.
+ *   - stream is a hipStream_t (NULL = the default stream). Every call is
+ *     asynchronous on that stream: it validates on the host, enqueues its
+ *     kernels and returns. Calls are reentrant; calls that write the same
+ *     buffers must be ordered by the caller.
+ *   - Arrays are row-major and contiguous. Element type of x, weights,
+ *     cache, queries and outputs is shape->dtype: MLA_BF16 (bfloat16) or
+ *     MLA_F32 (float). Accumulation is fp32 in both cases. RoPE tables are
+ *     always float.
+ *   - Every device pointer must be 16-byte aligned.
+ *   - Errors are reported by return value before anything is enqueued
+ *     (MLA_ERR_NULL, _SHAPE, _DTYPE, _ALIGN, _WORKSPACE, _UNSUPPORTED,
+ *     _RANGE), or MLA_ERR_HIP if a launch fails. No C++ exception crosses
+ *     this boundary.
+ *   - Supported latent widths (d_c, d_rope): (192, 32) and (16, 8), either
+ *     dtype. d_head must be a multiple of 8 and at most 256; hidden a
+ *     multiple of 8; window_frames at most 64; each RoPE axis width even.
+ *
+ * Token positions: a frame has grid_y * grid_x tokens in row-major order;
+ * token k of frame f sits at (t, y, x) = (f, k / grid_x, k % grid_x).
+ * RoPE: the d_rope dims are three contiguous blocks [t | y | x] of widths
+ * d_rope_t, d_rope_y, d_rope_x; inside each block the interleaved pair
+ * (2i, 2i+1) is rotated by pos * rope_base^(-2i/d_axis).
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,        /* a required pointer is NULL */
+  MLA_ERR_SHAPE = 2,       /* dimensions inconsistent or out of range */
+  MLA_ERR_DTYPE = 3,       /* dtype is neither MLA_BF16 nor MLA_F32 */
+  MLA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
+  MLA_ERR_WORKSPACE = 5,   /* workspace smaller than the *_workspace_bytes query */
+  MLA_ERR_UNSUPPORTED = 6, /* (d_c, d_rope) has no kernel instantiation */
+  MLA_ERR_HIP = 7,         /* a HIP launch failed */
+  MLA_ERR_RANGE = 8        /* frame or table index arguments out of range */
+} mla_status;
+
+typedef enum mla_dtype { MLA_BF16 = 0, MLA_F32 = 1 } mla_dtype;
+
+/* Layer and stream geometry (host memory). */
+typedef struct mla_shape {
+  int32_t batch;         /* B independent streams, each with its own window */
+  int32_t hidden;        /* token width (input of the down-projections) */
+  int32_t n_heads;       /* H */
+  int32_t d_head;        /* per-head key / value width */
+  int32_t d_c;           /* content latent width */
+  int32_t d_rope;        /* positional key width = d_rope_t + d_rope_y + d_rope_x */
+  int32_t d_rope_t;      /* rotary dims driven by the frame index t */
+  int32_t d_rope_y;      /* rotary dims driven by the grid row y */
+  int32_t d_rope_x;      /* rotary dims driven by the grid column x */
+  int32_t grid_y;        /* tokens per frame = grid_y * grid_x */
+  int32_t grid_x;
+  int32_t window_frames; /* W: ring slots; frame f lives in slot f mod W */
+  int32_t dtype;         /* mla_dtype */
+  float rope_base;       /* RoPE base (10000 for the Wan shapes) */
+  float softmax_scale;   /* <= 0 selects 1/sqrt(d_head + d_rope) */
+} mla_shape;
+
+/* Library version; equals MLA_ABI_VERSION of the header it was built from. */
+int32_t mla_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* mla_status_string(int32_t status);
+
+/* Host-only validation of a shape; enqueues nothing. */
+mla_status mla_shape_check(const mla_shape* shape);
+
+/* Width of one absorbed-query row: d_c + d_rope rounded up to 32 (padding
+ * columns are zero). 0 if the shape is invalid. */
+int32_t mla_qabs_dim(const mla_shape* shape);
+
+/* ---------------------------------------------------------------- a1
+ * 3D-RoPE tables (hyper.ai summary, Method: the positional key is rotated
+ * by 3D-RoPE at attention time; axes (t, h, w) = (t, y, x)).
+ * Fills `tables` (device, float) with, in order:
+ *   cos_t[n_t][d_rope_t/2], sin_t[n_t][d_rope_t/2]   positions t_first + i
+ *   cos_y[grid_y][d_rope_y/2], sin_y[grid_y][d_rope_y/2]
+ *   cos_x[grid_x][d_rope_x/2], sin_x[grid_x][d_rope_x/2]
+ * Angles are formed in double precision and rounded to float.
+ * mla_rope3d_table_floats gives the element count (0 if invalid). */
+size_t mla_rope3d_table_floats(const mla_shape* shape, int32_t n_t);
+mla_status mla_rope3d_tables(const mla_shape* shape, int32_t t_first, int32_t n_t, float* tables,
+                             void* stream);
+
+/* ---------------------------------------------------------------- a2 + a6
+ * Cache write (hyper.ai summary, Method: c = W_dkv x is written to the
+ * compressed cache; kR = W_kR x is stored unrotated; chatpaper.ai abstract:
+ * fixed-size sliding window).
+ *   x          (device) [B][n_frames * T][hidden]   tokens of frames
+ *                       frame_first .. frame_first + n_frames - 1, T = grid_y*grid_x
+ *   w_dkv      (device) [d_c][hidden]
+ *   w_kr       (device) [d_rope][hidden]
+ *   cache      (device) [B][W][T][d_c + d_rope]   row = [c | kR], rounded to dtype
+ *   slot_frame (device) [B][W] int32               frame held by each slot, -1 = empty
+ * Frame f goes to slot f mod W (evicting what the slot held) and
+ * slot_frame[b][f mod W] = f. Requires 0 <= frame_first, 1 <= n_frames <= W
+ * (else MLA_ERR_RANGE). Writing the same frame again is idempotent. The
+ * caller initialises slot_frame to -1 before the first write. */
+mla_status mla_cache_write(const mla_shape* shape, const void* x, const void* w_dkv, const void* w_kr,
+                           int32_t frame_first, int32_t n_frames, void* cache, int32_t* slot_frame,
+                           void* stream);
+
+/* ---------------------------------------------------------------- a3
+ * Query absorb and rotate (hyper.ai summary, Method: score = content part
+ * + positional part). For query token i of the chunk (frame
+ * q_frame_first + i / T) and head h:
+ *   q_abs[b][i][h][0:d_c]            = W_uk[h]^T q_nope[b][i][h]
+ *   q_abs[b][i][h][d_c:d_c+d_rope]   = R(t, y, x) q_r[b][i][h]
+ *   q_abs[b][i][h][d_c+d_rope:Q]     = 0,    Q = mla_qabs_dim(shape)
+ *   q_nope (device) [B][N_q][H][d_head], q_r (device) [B][N_q][H][d_rope]
+ *   (unrotated), w_uk (device) [H][d_head][d_c], N_q = q_n_frames * T.
+ *   rope_tables (device) from mla_rope3d_tables(shape, rope_t_first,
+ *   rope_n_t, ...); the chunk's frames must lie in
+ *   [rope_t_first, rope_t_first + rope_n_t) (else MLA_ERR_RANGE).
+ *   q_abs (device) [B][N_q][H][Q], dtype. */
+mla_status mla_absorb_q(const mla_shape* shape, const void* q_nope, const void* q_r, int32_t q_frame_first,
+                        int32_t q_n_frames, const void* w_uk, const float* rope_tables, int32_t rope_t_first,
+                        int32_t rope_n_t, void* q_abs, void* stream);
+
+/* ---------------------------------------------------------------- a4
+ * Latent flash attention (hyper.ai summary, Method; chatpaper.ai abstract:
+ * softmax over the sliding window). For every row (b, i, h):
+ *   s_j   = scale * q_abs[b][i][h] . [c_j | R(t_j, y_j, x_j) kR_j]
+ *   o_lat = sum_j softmax(s)_j c_j                       -> [d_c]
+ * over every key j of every slot of stream b with slot_frame[b][s] >= 0
+ * (no intra-chunk mask); rows with no valid key get zeros.
+ *   q_abs (device) [B][N_q][H][Q] from mla_absorb_q; cache, slot_frame as
+ *   written by mla_cache_write; rope_tables as for mla_absorb_q (every
+ *   frame held in the window must lie in the table range: frames outside it
+ *   are read from the clamped table row, a wrong but memory-safe result).
+ *   o_lat (device) [B][N_q][H][d_c], dtype.
+ *   workspace (device) of at least mla_flash_workspace_bytes(shape,
+ *   q_n_frames, kv_splits) bytes; its contents on entry do not matter.
+ *   kv_splits: number of key-range partitions per row block combined by a
+ *   log-sum-exp pass; 0 chooses automatically; at most 16. */
+size_t mla_flash_workspace_bytes(const mla_shape* shape, int32_t q_n_frames, int32_t kv_splits);
+mla_status mla_flash_attend(const mla_shape* shape, const void* q_abs, int32_t q_n_frames, const void* cache,
+                            const int32_t* slot_frame, const float* rope_tables, int32_t rope_t_first,
+                            int32_t rope_n_t, void* o_lat, int32_t kv_splits, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- a5
+ * Value up-projection (hyper.ai summary, Method: v = W_uv[h] c, so
+ * sum_j p_j v_j = W_uv[h] sum_j p_j c_j):
+ *   out[b][i][h][:] = W_uv[h] o_lat[b][i][h][:]
+ *   o_lat (device) [B][N_q][H][d_c], w_uv (device) [H][d_head][d_c],
+ *   out (device) [B][N_q][H][d_head], dtype. */
+mla_status mla_up_v(const mla_shape* shape, const void* o_lat, int32_t q_n_frames, const void* w_uv, void* out,
+                    void* stream);
+
+/* ---------------------------------------------------------------- a3..a5
+ * The whole attention side of the step: mla_absorb_q, mla_flash_attend and
+ * mla_up_v in sequence on `stream`, with q_abs and o_lat carved from
+ * `workspace` (at least mla_chunk_attend_workspace_bytes bytes).
+ * Arguments as above; out (device) [B][N_q][H][d_head]. */
+size_t mla_chunk_attend_workspace_bytes(const mla_shape* shape, int32_t q_n_frames);
+mla_status mla_chunk_attend(const mla_shape* shape, const void* q_nope, const void* q_r, int32_t q_frame_first,
+                            int32_t q_n_frames, const void* w_uk, const void* w_uv, const void* cache,
+                            const int32_t* slot_frame, const float* rope_tables, int32_t rope_t_first,
+                            int32_t rope_n_t, void* out, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,105 @@
+// Query absorb and rotate (hyper.ai summary of VideoMLA, Method section: the
+// score of head h is q_nope . k_nope + q_rope . k_rope with k_nope = W_uk[h] c
+// and k_rope the rotated shared key). Since q . (W_uk[h] c) = (W_uk[h]^T q) . c,
+// the query is mapped once into latent space:
+//   q_abs[b,i,h] = [ W_uk[h]^T q_nope[b,i,h] | R(t,y,x) q_r[b,i,h] | 0 ... ]
+// Work-group: 64 query tokens x one head. The 32-row slabs of W_uk[h] are
+// staged in LDS and read with the transposing LDS load, because the
+// contraction runs over W_uk's row index.
+#include "mla_common.hpp"
+#include "mla_internal.hpp"
+#include "rope_device.hpp"
+
+namespace mla {
+
+template <typename T, int DC, int DR>
+__global__ __launch_bounds__(256) void absorb_q_kernel(AbsorbParams p) {
+  typedef typename V8<T>::type v8;
+  constexpr int KP = (DC + DR + 31) / 32 * 32;
+  constexpr int PADE = 16 / sizeof(T);
+  constexpr int LS = DC + PADE;
+  constexpr int NNB = DC / 16;
+  __shared__ __attribute__((aligned(16))) T wl[32 * LS];
+
+  const int h = blockIdx.y;
+  const int row0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int H = p.H, dh = p.d_head;
+
+  const int arow = row0 + wave * 16 + li;
+  const bool arow_ok = arow < p.rows;
+  const T* qrow = (const T*)p.q_nope + ((size_t)(arow_ok ? arow : 0) * H + h) * dh;
+  const T* wbase = (const T*)p.w_uk + (size_t)h * dh * DC;
+
+  f32x4 acc[NNB] = {};
+  for (int k0 = 0; k0 < dh; k0 += 32) {
+    __syncthreads();
+    for (int e = tid; e < 32 * (DC / 8); e += 256) {
+      const int r = e / (DC / 8), c8 = (e % (DC / 8)) * 8;
+      const v8 v = (k0 + r < dh) ? load8<T>(wbase + (size_t)(k0 + r) * DC + c8) : zero8<T>();
+      store8<T>(wl + r * LS + c8, v);
+    }
+    __syncthreads();
+    const v8 a = (arow_ok && k0 + lg * 8 < dh) ? load8<T>(qrow + k0 + lg * 8) : zero8<T>();
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb) {
+      const typename V8<T>::type bop = lds_tr8(wl, LS, lg * 8, lg * 8 + 4, nb * 16);
+      acc[nb] = mma16(a, bop, acc[nb]);
+    }
+  }
+
+  T* qa = (T*)p.q_abs;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = row0 + wave * 16 + lg * 4 + i;
+    if (r >= p.rows) continue;
+    T* dst = qa + ((size_t)r * H + h) * KP;
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb) dst[nb * 16 + li] = to_t<T>(acc[nb][i]);
+  }
+
+  // rotated positional part and zero padding
+  constexpr int NPR = DR / 2;
+  for (int e = tid; e < 64 * NPR; e += 256) {
+    const int r = row0 + e / NPR, pr = e % NPR;
+    if (r >= p.rows) continue;
+    const int i = r % p.n_q;
+    const int t = p.q_frame_first + i / p.T, tok = i % p.T;
+    const int y = tok / p.grid_x, x = tok % p.grid_x;
+    const T* src = (const T*)p.q_r + ((size_t)r * H + h) * DR + 2 * pr;
+    float a0 = to_f<T>(src[0]), a1 = to_f<T>(src[1]);
+    float c, s;
+    rope_cos_sin(p.rl, p.tables, pr, t, y, x, c, s);
+    rotate_pair(a0, a1, c, s);
+    T* dst = qa + ((size_t)r * H + h) * KP + DC + 2 * pr;
+    dst[0] = to_t<T>(a0);
+    dst[1] = to_t<T>(a1);
+  }
+  if constexpr (KP > DC + DR) {
+    constexpr int NPAD = KP - DC - DR;
+    for (int e = tid; e < 64 * NPAD; e += 256) {
+      const int r = row0 + e / NPAD;
+      if (r >= p.rows) continue;
+      qa[((size_t)r * H + h) * KP + DC + DR + e % NPAD] = to_t<T>(0.f);
+    }
+  }
+}
+
+template <typename T, int DC, int DR>
+static hipError_t launch_absorb_t(const AbsorbParams& p, hipStream_t s) {
+  dim3 grid((p.rows + 63) / 64, p.H);
+  hipLaunchKernelGGL((absorb_q_kernel<T, DC, DR>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_absorb_q(int dtype, int d_c, int d_rope, const AbsorbParams& p, hipStream_t s) {
+  if (p.rows <= 0) return hipSuccess;
+  if (d_c == 192 && d_rope == 32)
+    return dtype == 0 ? launch_absorb_t<bf16, 192, 32>(p, s) : launch_absorb_t<float, 192, 32>(p, s);
+  if (d_c == 16 && d_rope == 8)
+    return dtype == 0 ? launch_absorb_t<bf16, 16, 8>(p, s) : launch_absorb_t<float, 16, 8>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mla

@@ -1,0 +1,511 @@
+// Latent flash attention: the core of one VideoMLA chunk step.
+//
+// hyper.ai summary of VideoMLA, Method section: head h scores key j with
+// q_nope . (W_uk[h] c_j) + q_rope . R(p_j) kR_j and takes the value
+// W_uv[h] c_j, so one read of the cached [c_j | kR_j] serves every head.
+// chatpaper.ai abstract: the keys are the frames of a fixed-size sliding
+// window. With the absorbed query q_abs = [W_uk[h]^T q_nope | R(p_i) qR | 0]
+// this file computes, for every row (b, i, h),
+//   s_j   = q_abs . [c_j | R(t_j, y_j, x_j) kR_j | 0]
+//   o_lat = sum_j softmax(scale * s)_j c_j
+// over every key of every valid ring slot.
+//
+// Softmax with a fixed per-row reference. exp is shift-invariant, so any
+// reference r_i gives o = sum_j 2^((s_j - r_i) c) c_j / sum_j 2^((s_j - r_i) c)
+// (c = scale * log2 e). Each row takes r_i = the exact maximum of its scores
+// over the first 32 keys it visits; later keys may score higher, so a
+// probability can exceed 1, but fp32 (and bf16) reach 2^127 and the largest
+// probability is at least 1, so nothing underflows. No running maximum is
+// tracked and the output accumulators are never rescaled, so they stay in the
+// matrix-core accumulator registers. A row whose probability sum exceeds 2^100
+// (a logit gap beyond ~70 nats) is listed and recomputed by an exact
+// two-pass kernel instead.
+//
+// Layout of the work (bf16):
+//   * the 12 heads of a query are consecutive rows (all heads share the
+//     keys); a work-group owns 256 rows, each of its 4 waves 64 rows held as
+//     four 16-row blocks, queries kept in registers for the whole key loop;
+//   * keys stream in 64-key tiles through LDS, double-buffered. The latent
+//     part goes global -> LDS directly (no registers); the kR part goes
+//     through registers and is rotated by 3D-RoPE on its way into LDS;
+//   * scores are formed transposed, S^T = K Q^T (keys as rows), so a lane
+//     holds 4 keys of one query row and the probabilities already sit in the
+//     lane layout of the B operand of O^T = C^T P^T. The C^T operand is read
+//     from the same LDS tile with the transposing LDS load: the latent is
+//     staged once for both products.
+//   * kv_splits > 1 partitions the key tiles; splits share the reference, so
+//     a second pass just adds their (output, sum) pairs.
+#include "mla_common.hpp"
+#include "mla_internal.hpp"
+#include "rope_device.hpp"
+
+namespace mla {
+
+namespace {
+constexpr int kWaves = 4;
+constexpr int kMaxSlots = 64;
+constexpr float kSumLimit = 1.2676506e30f;  // 2^100
+}  // namespace
+
+// bf16: 64-key tiles and 64 rows per wave; float operands are twice as wide,
+// so float uses 32-key tiles and 32 rows per wave to stay inside LDS and the
+// register file.
+template <typename T, int DC, int DR>
+struct FlashTile {
+  static constexpr int kBN = sizeof(T) == 2 ? 64 : 32;  // keys per tile
+  static constexpr int kNMB = sizeof(T) == 2 ? 4 : 2;   // 16-row blocks per wave
+  static constexpr int kRowsWave = kNMB * 16;
+  static constexpr int kRowsBlock = kWaves * kRowsWave;
+  static constexpr int NKC2 = kBN / 32;                 // 32-key halves per tile
+  static constexpr int KP = (DC + DR + 31) / 32 * 32;   // contraction width of QK (zero padded)
+  static constexpr int DK = DC + DR;                    // cached row width
+  static constexpr int NKC = KP / 32;
+  static constexpr int NDB = DC / 16;
+  static constexpr int CB = 16 / sizeof(T);             // elements per 16-byte chunk
+  static constexpr int LS = KP + CB;                    // LDS row stride (elements), one pad chunk
+  static constexpr int CPR = LS / CB;                   // 16-byte chunks per LDS row
+  static constexpr int CC = DC / CB;                    // latent chunks per key
+  static constexpr int RC = DR / CB;                    // kR chunks per key
+  static constexpr int TILE_CHUNKS = kBN * CPR;
+  static constexpr int N_INSTR = (TILE_CHUNKS + 63) / 64;  // direct-load instructions per tile
+  static constexpr int N_INSTR_WAVE = (N_INSTR + kWaves - 1) / kWaves;
+  static constexpr int TILE_ELEMS = N_INSTR * 64 * CB;  // LDS elements per buffer (whole instructions)
+};
+
+// Clears the count of rows handed to the exact fallback.
+__global__ void flash_prep_kernel(FlashParams p) { *p.fallback_count = 0; }
+
+// ---------------------------------------------------------------- main kernel
+template <typename T, int DC, int DR>
+__global__ __launch_bounds__(256, 1) void flash_mla_kernel(FlashParams p) {
+  typedef FlashTile<T, DC, DR> F;
+  typedef typename V8<T>::type v8;
+  constexpr int kBN = F::kBN, kNMB = F::kNMB;
+  __shared__ __attribute__((aligned(16))) T kv[2][F::TILE_ELEMS];
+  __shared__ int slot_of[kMaxSlots];
+  __shared__ int frame_of[kMaxSlots];
+  __shared__ int n_valid_sh;
+  __shared__ int4 keytab[2][kBN];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int b = blockIdx.z, split = blockIdx.y;
+  const int row_wave = blockIdx.x * F::kRowsBlock + wave * F::kRowsWave;
+
+  // valid ring slots of stream b in slot order
+  if (wave == 0) {
+    const int f = lane < p.W ? p.slot_frame[b * p.W + lane] : -1;
+    const unsigned long long mask = __ballot(f >= 0);
+    if (f >= 0) {
+      const int rank = __popcll(mask & ((1ull << lane) - 1ull));
+      slot_of[rank] = lane;
+      frame_of[rank] = f;
+    }
+    if (lane == 0) n_valid_sh = __popcll(mask);
+  }
+  __syncthreads();
+
+  const int n_keys = n_valid_sh * p.T;
+  const int n_tiles = (n_keys + kBN - 1) / kBN;
+  const int tiles_per_split = (n_tiles + p.splits - 1) / p.splits;
+  const int tile_begin = split * tiles_per_split;
+  const int tile_end = min(n_tiles, tile_begin + tiles_per_split);
+
+  // queries of this wave (B operand of S^T = K Q^T), kept in registers
+  v8 qf[kNMB][F::NKC];
+  {
+    const T* qb = (const T*)p.q_abs + (size_t)b * p.Mb * F::KP;
+#pragma unroll
+    for (int mb = 0; mb < kNMB; ++mb) {
+      const int row = row_wave + mb * 16 + li;
+#pragma unroll
+      for (int kc = 0; kc < F::NKC; ++kc)
+        qf[mb][kc] = row < p.Mb ? load8<T>(qb + (size_t)row * F::KP + kc * 32 + lg * 8) : zero8<T>();
+    }
+  }
+  float ref[kNMB];  // reference (times c) of the row of this lane in each row block
+  bool have_ref = false;
+
+  f32x4 o[F::NDB][kNMB];
+#pragma unroll
+  for (int db = 0; db < F::NDB; ++db)
+#pragma unroll
+    for (int mb = 0; mb < kNMB; ++mb) o[db][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float l_run[kNMB];
+#pragma unroll
+  for (int mb = 0; mb < kNMB; ++mb) l_run[mb] = 0.f;
+
+  const T* cache_b = (const T*)p.cache + (size_t)b * p.W * p.T * F::DK;
+
+  // Per-tile key descriptors {row offset, t, y, x}, written one tile ahead by
+  // wave 0 into a ping-pong table, so the address of every load below is one
+  // LDS read plus an add. Keys past the end of the window alias the last key
+  // (their probabilities are forced to 0).
+  auto describe = [&](int tile, int4* tab) {
+    if (wave == 0) {
+      const int v = min(tile * kBN + lane, n_keys - 1);
+      const int rank = v / p.T, tok = v - rank * p.T;
+      const int y = tok / p.grid_x;
+      if (lane < kBN)
+        tab[lane] = int4{(slot_of[rank] * p.T + tok) * F::DK, frame_of[rank], y, tok - y * p.grid_x};
+    }
+  };
+
+  // ---- latent part: global -> LDS, lane order = LDS order (no registers).
+  // Instruction k of this wave covers LDS chunks [64 i, 64 i + 64), i = wave + 4k;
+  // the key and chunk of each lane's slot do not depend on the tile.
+  int lat_key[F::N_INSTR_WAVE];
+  int lat_off[F::N_INSTR_WAVE];  // element offset inside the key row, -1 = not a latent chunk
+#pragma unroll
+  for (int k = 0; k < F::N_INSTR_WAVE; ++k) {
+    const int instr = wave + kWaves * k;
+    const int pos = instr * 64 + lane;
+    const int n = pos / F::CPR, c = pos % F::CPR;
+    const bool ok = instr < F::N_INSTR && n < kBN && c < F::CC;
+    lat_key[k] = ok ? n : 0;
+    lat_off[k] = ok ? c * F::CB : -1;
+  }
+  auto issue_latent = [&](const int4* tab, T* buf) {
+#pragma unroll
+    for (int k = 0; k < F::N_INSTR_WAVE; ++k) {
+      const int instr = wave + kWaves * k;
+      if (instr < F::N_INSTR && lat_off[k] >= 0) {
+        const T* src = cache_b + tab[lat_key[k]].x + lat_off[k];
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (MLA_LDS void*)(MLA_LDS T*)(buf + instr * 64 * F::CB), 16, 0, 0);
+      }
+    }
+  };
+
+  // ---- kR part: one 16-byte chunk per thread via registers, rotated on store
+  constexpr int RCH = kBN * F::RC;  // kR chunks per tile
+  const bool has_r = tid < RCH;
+  const int r_key = tid / F::RC, r_chunk = tid % F::RC;
+  u32x4 st_r = {};
+  int4 st_d = {0, 0, 0, 0};
+  auto fetch_rope = [&](const int4* tab) {
+    if (has_r) {
+      st_d = tab[r_key];
+      st_r = *reinterpret_cast<const u32x4*>(cache_b + st_d.x + DC + r_chunk * F::CB);
+    }
+  };
+  auto stash_rope = [&](T* buf) {
+    if (has_r) {
+      float f[F::CB];
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          f[2 * k] = __builtin_bit_cast(float, st_r[k] << 16);
+          f[2 * k + 1] = __builtin_bit_cast(float, st_r[k] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(st_r[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < F::CB / 2; ++k) {
+        float cs, sn;
+        rope_cos_sin(p.rl, p.tables, r_chunk * (F::CB / 2) + k, st_d.y, st_d.z, st_d.w, cs, sn);
+        rotate_pair(f[2 * k], f[2 * k + 1], cs, sn);
+      }
+      u32x4 out;
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t lo = __builtin_bit_cast(uint16_t, (bf16)f[2 * k]);
+          const uint32_t hi = __builtin_bit_cast(uint16_t, (bf16)f[2 * k + 1]);
+          out[k] = lo | (hi << 16);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) out[k] = __builtin_bit_cast(uint32_t, f[k]);
+      }
+      *reinterpret_cast<u32x4*>(buf + (r_key * F::CPR + F::CC + r_chunk) * F::CB) = out;
+    }
+  };
+
+  // zero the padding chunks of both buffers once (they are never written again)
+  if constexpr (F::KP > F::DK) {
+    constexpr int PADC = (F::KP - F::DK) / F::CB;
+    for (int e = tid; e < 2 * kBN * PADC; e += 256) {
+      const int buf = e / (kBN * PADC), q = e % (kBN * PADC);
+      const u32x4 z = {};
+      *reinterpret_cast<u32x4*>(&kv[buf][((q / PADC) * F::CPR + F::CC + F::RC + q % PADC) * F::CB]) = z;
+    }
+  }
+
+  if (tile_begin < tile_end) {
+    describe(tile_begin, keytab[0]);
+    if (tile_begin + 1 < tile_end) describe(tile_begin + 1, keytab[1]);
+  }
+  __syncthreads();
+  if (tile_begin < tile_end) {
+    issue_latent(keytab[0], kv[0]);
+    fetch_rope(keytab[0]);
+    stash_rope(kv[0]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // Iteration of tile j: start the loads of tile j+1 (descriptors ready),
+  // describe tile j+2, consume tile j, stash the kR part of tile j+1, wait for
+  // its latent loads, barrier.
+  for (int tile = tile_begin; tile < tile_end; ++tile) {
+    const int cur = (tile - tile_begin) & 1;
+    const bool has_next = tile + 1 < tile_end;
+    if (has_next) {
+      issue_latent(keytab[cur ^ 1], kv[cur ^ 1]);
+      fetch_rope(keytab[cur ^ 1]);
+    }
+    if (tile + 2 < tile_end) describe(tile + 2, keytab[cur]);
+    const T* kt = kv[cur];
+    const int kbase = tile * kBN;
+    const bool ragged = kbase + kBN > n_keys;
+
+#pragma unroll 1
+    for (int half = 0; half < F::NKC2; ++half) {
+      // S^T[key][row] for 2 key blocks x kNMB row blocks
+      f32x4 s[2][kNMB];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int mb = 0; mb < kNMB; ++mb) s[kb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < F::NKC; ++kc) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const v8 a = lds_load8<T>(kt + ((half * 2 + kb) * 16 + li) * F::LS + kc * 32 + lg * 8);
+#pragma unroll
+          for (int mb = 0; mb < kNMB; ++mb) s[kb][mb] = mma16(a, qf[mb][kc], s[kb][mb]);
+        }
+      }
+
+      if (ragged) {  // keys past the window end (last tile only)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kbase + (half * 2 + kb) * 16 + lg * 4 + i >= n_keys) {
+#pragma unroll
+              for (int mb = 0; mb < kNMB; ++mb) s[kb][mb][i] = -__builtin_inff();
+            }
+      }
+      if (!have_ref) {  // first 32 keys: the exact row maximum becomes the reference
+#pragma unroll
+        for (int mb = 0; mb < kNMB; ++mb) {
+          float mx = s[0][mb][0];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][mb][i]);
+          ref[mb] = wave_max_across_groups(mx) * p.scale_log2;
+        }
+        have_ref = true;
+      }
+
+      // probabilities against the fixed reference -> B operand of PV
+      v8 pb[kNMB];
+#pragma unroll
+      for (int mb = 0; mb < kNMB; ++mb) {
+        float f8[8];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float e = fast_exp2(s[kb][mb][i] * p.scale_log2 - ref[mb]);
+            f8[kb * 4 + i] = e;
+            l_run[mb] += e;
+          }
+        pb[mb] = pack8<T>(f8);
+      }
+
+      // O^T[d][row] += C^T[d][key] P^T[key][row]; key slot j of lane group g
+      // is key 4g+j (j < 4) or 16+4g+(j-4) of this half, matching S^T's layout
+#pragma unroll
+      for (int db = 0; db < F::NDB; ++db) {
+        const v8 a = lds_tr8(kt, F::LS, half * 32 + lg * 4, half * 32 + 16 + lg * 4, db * 16);
+#pragma unroll
+        for (int mb = 0; mb < kNMB; ++mb) o[db][mb] = mma16(a, pb[mb], o[db][mb]);
+      }
+    }
+
+    if (has_next) stash_rope(kv[cur ^ 1]);
+    __builtin_amdgcn_s_waitcnt(0);  // latent loads of the next tile have landed
+    __syncthreads();
+  }
+
+  // ---- epilogue
+#pragma unroll
+  for (int mb = 0; mb < kNMB; ++mb) {
+    const float l = wave_sum_across_groups(l_run[mb]);
+    const int row = row_wave + mb * 16 + li;
+    if (row >= p.Mb) continue;
+    if (p.splits == 1) {
+      const bool ok = l <= kSumLimit;  // false for inf / NaN as well
+      const float inv = (ok && l > 0.f) ? 1.f / l : 0.f;
+      T* dst = (T*)p.o_lat + ((size_t)b * p.Mb + row) * DC;
+#pragma unroll
+      for (int db = 0; db < F::NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[db * 16 + lg * 4 + i] = to_t<T>(o[db][mb][i] * inv);
+      if (!ok && lg == 0) p.fallback_rows[atomicAdd(p.fallback_count, 1)] = b * p.Mb + row;
+    } else {
+      const size_t prow = ((size_t)split * p.batch + b) * p.Mb + row;
+      float* dst = p.part_o + prow * DC;
+#pragma unroll
+      for (int db = 0; db < F::NDB; ++db) *reinterpret_cast<f32x4*>(dst + db * 16 + lg * 4) = o[db][mb];
+      if (lg == 0) {
+        p.part_l[prow * 2] = have_ref ? ref[mb] : -__builtin_inff();  // empty split: no keys, weight 0
+        p.part_l[prow * 2 + 1] = l;
+      }
+    }
+  }
+}
+
+// Merge of the per-split (reference, output, probability sum) of one row:
+// with M = max_s r_s and w_s = 2^(r_s - M), o = sum_s w_s o_s / sum_s w_s l_s.
+template <typename T, int DC>
+__global__ __launch_bounds__(256) void flash_combine_kernel(FlashParams p) {
+  constexpr int D4 = DC / 4;
+  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long n_rows = (long long)p.batch * p.Mb;
+  if (e >= n_rows * D4) return;
+  const long long r = e / D4;
+  const int d = (int)(e % D4) * 4;
+  float M = -__builtin_inff();
+  bool ok = true;
+  for (int sp = 0; sp < p.splits; ++sp) {
+    const size_t pr = (size_t)sp * n_rows + r;
+    M = fmaxf(M, p.part_l[pr * 2]);
+    ok = ok && (p.part_l[pr * 2 + 1] <= kSumLimit);
+  }
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (M > -__builtin_inff()) {
+    for (int sp = 0; sp < p.splits; ++sp) {
+      const size_t pr = (size_t)sp * n_rows + r;
+      const float w = fast_exp2(p.part_l[pr * 2] - M);
+      L += w * p.part_l[pr * 2 + 1];
+      acc += w * *reinterpret_cast<const f32x4*>(p.part_o + pr * DC + d);
+    }
+  }
+  const float inv = (ok && L > 0.f) ? 1.f / L : 0.f;
+  T* dst = (T*)p.o_lat + (size_t)r * DC + d;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = to_t<T>(acc[i] * inv);
+  if (!ok && d == 0) p.fallback_rows[atomicAdd(p.fallback_count, 1)] = (int)r;
+}
+
+// ---------------------------------------------------------------- exact fallback
+// Rows whose probabilities underflowed against the bound are recomputed with
+// the textbook two-pass softmax: exact row maximum first, then the weighted
+// sum. One work-group per listed row (grid-stride over the list), keys striped
+// over threads. Slow, and only reached for rows whose bound was very loose.
+template <typename T, int DC, int DR>
+__global__ __launch_bounds__(256) void flash_exact_kernel(FlashParams p) {
+  constexpr int DK = DC + DR;
+  constexpr int KP = (DC + DR + 31) / 32 * 32;
+  constexpr int CHUNK = 256;
+  __shared__ float q[DK];
+  __shared__ float pr[CHUNK];
+  __shared__ float red[256];
+  __shared__ int slot_of[kMaxSlots];
+  __shared__ int frame_of[kMaxSlots];
+  __shared__ int n_valid_sh;
+  const int tid = threadIdx.x;
+  const int count = *p.fallback_count;
+  for (int idx = blockIdx.x; idx < count; idx += gridDim.x) {
+    const int grow = p.fallback_rows[idx];
+    const int b = grow / p.Mb;
+    __syncthreads();
+    if (tid < 64) {
+      const int f = tid < p.W ? p.slot_frame[b * p.W + tid] : -1;
+      const unsigned long long mask = __ballot(f >= 0);
+      if (f >= 0) {
+        const int rank = __popcll(mask & ((1ull << tid) - 1ull));
+        slot_of[rank] = tid;
+        frame_of[rank] = f;
+      }
+      if (tid == 0) n_valid_sh = __popcll(mask);
+    }
+    for (int d = tid; d < DK; d += 256) q[d] = to_f<T>(((const T*)p.q_abs)[(size_t)grow * KP + d]);
+    __syncthreads();
+    const int n_keys = n_valid_sh * p.T;
+    const T* cache_b = (const T*)p.cache + (size_t)b * p.W * p.T * DK;
+    auto score = [&](int v) {
+      const int rank = v / p.T, tok = v - rank * p.T;
+      const T* row = cache_b + ((size_t)slot_of[rank] * p.T + tok) * DK;
+      const int y = tok / p.grid_x, x = tok - y * p.grid_x;
+      float s = 0.f;
+      for (int d = 0; d < DC; ++d) s += q[d] * to_f<T>(row[d]);
+      for (int k = 0; k < DR / 2; ++k) {
+        float a0 = to_f<T>(row[DC + 2 * k]), a1 = to_f<T>(row[DC + 2 * k + 1]), cs, sn;
+        rope_cos_sin(p.rl, p.tables, k, frame_of[rank], y, x, cs, sn);
+        rotate_pair(a0, a1, cs, sn);
+        s += q[DC + 2 * k] * to_f<T>(to_t<T>(a0)) + q[DC + 2 * k + 1] * to_f<T>(to_t<T>(a1));
+      }
+      return s;
+    };
+    // pass 1: exact maximum
+    float mx = -__builtin_inff();
+    for (int v = tid; v < n_keys; v += 256) mx = fmaxf(mx, score(v));
+    red[tid] = mx;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+      if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
+      __syncthreads();
+    }
+    const float m = red[0];
+    __syncthreads();
+    // pass 2: probabilities chunk by chunk, threads then sweep the latent dims
+    float acc = 0.f, lsum = 0.f;
+    for (int v0 = 0; v0 < n_keys; v0 += CHUNK) {
+      const int v = v0 + tid;
+      pr[tid] = v < n_keys ? fast_exp2((score(v) - m) * p.scale_log2) : 0.f;
+      __syncthreads();
+      if (tid < DC) {
+        const int nv = min(CHUNK, n_keys - v0);
+        for (int j = 0; j < nv; ++j) {
+          const int vv = v0 + j;
+          const int rank = vv / p.T, tok = vv - rank * p.T;
+          acc += pr[j] * to_f<T>(cache_b[((size_t)slot_of[rank] * p.T + tok) * DK + tid]);
+          lsum += pr[j];
+        }
+      }
+      __syncthreads();
+    }
+    if (tid < DC) {
+      ((T*)p.o_lat)[(size_t)grow * DC + tid] = to_t<T>(n_keys > 0 && lsum > 0.f ? acc / lsum : 0.f);
+    }
+  }
+}
+
+template <typename T, int DC, int DR>
+static hipError_t launch_flash_t(const FlashParams& p, hipStream_t s) {
+  typedef FlashTile<T, DC, DR> F;
+  hipLaunchKernelGGL(flash_prep_kernel, dim3(1), dim3(1), 0, s, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  dim3 grid((p.Mb + F::kRowsBlock - 1) / F::kRowsBlock, p.splits, p.batch);
+  hipLaunchKernelGGL((flash_mla_kernel<T, DC, DR>), grid, dim3(256), 0, s, p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (p.splits > 1) {
+    const long long total = (long long)p.batch * p.Mb * (DC / 4);
+    const int blocks = (int)((total + 255) / 256);
+    hipLaunchKernelGGL((flash_combine_kernel<T, DC>), dim3(blocks), dim3(256), 0, s, p);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL((flash_exact_kernel<T, DC, DR>), dim3(kFallbackBlocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_flash(int dtype, int d_c, int d_rope, const FlashParams& p, hipStream_t s) {
+  if (p.Mb <= 0 || p.batch <= 0) return hipSuccess;
+  if (d_c == 192 && d_rope == 32)
+    return dtype == 0 ? launch_flash_t<bf16, 192, 32>(p, s) : launch_flash_t<float, 192, 32>(p, s);
+  if (d_c == 16 && d_rope == 8)
+    return dtype == 0 ? launch_flash_t<bf16, 16, 8>(p, s) : launch_flash_t<float, 16, 8>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mla

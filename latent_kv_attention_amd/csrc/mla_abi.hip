@@ -1,0 +1,353 @@
+// C ABI layer: argument validation, workspace sizing and kernel dispatch.
+// Everything here runs on the host; no entry point allocates memory, and no
+// C++ exception leaves this file.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/mla.h"
+#include "mla_internal.hpp"
+
+#define MLA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using mla::RopeLayout;
+
+constexpr int kMaxWindow = 64;
+constexpr int kMaxHeadDim = 256;
+constexpr int kMaxSplits = 16;
+constexpr int kAssumedCUs = 256;  // MI355X; only steers the automatic split choice
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elt_size(const mla_shape* s) { return s->dtype == MLA_BF16 ? 2 : 4; }
+
+bool latent_supported(int d_c, int d_rope) { return (d_c == 192 && d_rope == 32) || (d_c == 16 && d_rope == 8); }
+
+mla_status check_shape(const mla_shape* s) {
+  if (!s) return MLA_ERR_NULL;
+  if (s->dtype != MLA_BF16 && s->dtype != MLA_F32) return MLA_ERR_DTYPE;
+  if (s->batch < 1 || s->n_heads < 1 || s->grid_y < 1 || s->grid_x < 1) return MLA_ERR_SHAPE;
+  if (s->hidden < 8 || s->hidden % 8 != 0) return MLA_ERR_SHAPE;
+  if (s->d_head < 8 || s->d_head % 8 != 0 || s->d_head > kMaxHeadDim) return MLA_ERR_SHAPE;
+  if (s->window_frames < 1 || s->window_frames > kMaxWindow) return MLA_ERR_SHAPE;
+  if (s->d_rope_t < 0 || s->d_rope_y < 0 || s->d_rope_x < 0) return MLA_ERR_SHAPE;
+  if (s->d_rope_t % 2 || s->d_rope_y % 2 || s->d_rope_x % 2) return MLA_ERR_SHAPE;
+  if (s->d_rope_t + s->d_rope_y + s->d_rope_x != s->d_rope) return MLA_ERR_SHAPE;
+  if (s->d_c < 1 || s->d_rope < 1) return MLA_ERR_SHAPE;
+  if (!(s->rope_base > 0.f) || !isfinite(s->rope_base)) return MLA_ERR_SHAPE;
+  if (!isfinite(s->softmax_scale)) return MLA_ERR_SHAPE;
+  const int64_t T = (int64_t)s->grid_y * s->grid_x;
+  // per-stream cache element offsets are 32-bit inside the kernels
+  if (T * s->window_frames * (s->d_c + s->d_rope) > INT32_MAX) return MLA_ERR_SHAPE;
+  if ((int64_t)s->batch * s->window_frames * T * (s->d_c + s->d_rope) > INT64_C(1) << 40) return MLA_ERR_SHAPE;
+  if (!latent_supported(s->d_c, s->d_rope)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+int64_t tokens_per_frame(const mla_shape* s) { return (int64_t)s->grid_y * s->grid_x; }
+
+int qabs_dim(const mla_shape* s) { return (s->d_c + s->d_rope + 31) / 32 * 32; }
+
+float scale_log2(const mla_shape* s) {
+  const double scale = s->softmax_scale > 0.f ? (double)s->softmax_scale : 1.0 / sqrt((double)(s->d_head + s->d_rope));
+  return (float)(scale * 1.4426950408889634);  // log2(e)
+}
+
+RopeLayout rope_layout(const mla_shape* s, int t_first, int n_t) {
+  RopeLayout rl;
+  rl.d_t = s->d_rope_t;
+  rl.d_y = s->d_rope_y;
+  rl.d_x = s->d_rope_x;
+  rl.t_first = t_first;
+  rl.n_t = n_t;
+  rl.off_ct = 0;
+  rl.off_st = rl.off_ct + n_t * (rl.d_t / 2);
+  rl.off_cy = rl.off_st + n_t * (rl.d_t / 2);
+  rl.off_sy = rl.off_cy + s->grid_y * (rl.d_y / 2);
+  rl.off_cx = rl.off_sy + s->grid_y * (rl.d_y / 2);
+  rl.off_sx = rl.off_cx + s->grid_x * (rl.d_x / 2);
+  return rl;
+}
+
+size_t table_floats(const mla_shape* s, int n_t) {
+  return 2 * ((size_t)n_t * (s->d_rope_t / 2) + (size_t)s->grid_y * (s->d_rope_y / 2) +
+              (size_t)s->grid_x * (s->d_rope_x / 2));
+}
+
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+int flash_rows_per_block(const mla_shape* s) { return s->dtype == MLA_BF16 ? 256 : 128; }
+
+int choose_splits(const mla_shape* s, int q_n_frames, int requested) {
+  if (requested > 0) return requested;
+  const int64_t Mb = (int64_t)q_n_frames * tokens_per_frame(s) * s->n_heads;
+  const int64_t blocks = (int64_t)s->batch * ((Mb + flash_rows_per_block(s) - 1) / flash_rows_per_block(s));
+  if (blocks >= kAssumedCUs / 2) return 1;
+  int64_t sp = (kAssumedCUs + blocks - 1) / blocks;
+  return (int)(sp > 8 ? 8 : sp);
+}
+
+// Flash workspace: the fallback row list and, for kv_splits > 1, the
+// per-split partial outputs, references and probability sums.
+struct FlashWs {
+  size_t count, rows, part_o, part_l, total;
+};
+
+FlashWs flash_ws_layout(const mla_shape* s, int q_n_frames, int splits) {
+  const size_t rows = (size_t)s->batch * q_n_frames * tokens_per_frame(s) * s->n_heads;
+  FlashWs w;
+  w.count = 0;
+  w.rows = w.count + 256;
+  w.part_o = w.rows + round256(rows * sizeof(int));
+  w.part_l = w.part_o + (splits > 1 ? round256((size_t)splits * rows * s->d_c * sizeof(float)) : 0);
+  w.total = w.part_l + (splits > 1 ? round256((size_t)splits * rows * 2 * sizeof(float)) : 0);
+  return w;
+}
+
+size_t flash_ws_bytes(const mla_shape* s, int q_n_frames, int splits) {
+  return flash_ws_layout(s, q_n_frames, splits).total;
+}
+
+mla_status from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+mla_status check_tables(const mla_shape* s, const float* tables, int t_first, int n_t) {
+  (void)s;
+  if (!tables) return MLA_ERR_NULL;
+  if (!aligned16(tables)) return MLA_ERR_ALIGN;
+  if (n_t < 1 || t_first < 0) return MLA_ERR_RANGE;
+  return MLA_OK;
+}
+
+mla_status do_absorb(const mla_shape* s, const void* q_nope, const void* q_r, int q_frame_first, int q_n_frames,
+                     const void* w_uk, const float* tables, int rope_t_first, int rope_n_t, void* q_abs,
+                     hipStream_t st) {
+  mla::AbsorbParams p;
+  p.q_nope = q_nope;
+  p.q_r = q_r;
+  p.w_uk = w_uk;
+  p.tables = tables;
+  p.q_abs = q_abs;
+  p.rl = rope_layout(s, rope_t_first, rope_n_t);
+  p.n_q = (int)(q_n_frames * tokens_per_frame(s));
+  p.rows = s->batch * p.n_q;
+  p.H = s->n_heads;
+  p.d_head = s->d_head;
+  p.T = (int)tokens_per_frame(s);
+  p.grid_x = s->grid_x;
+  p.q_frame_first = q_frame_first;
+  return from_hip(mla::launch_absorb_q(s->dtype, s->d_c, s->d_rope, p, st));
+}
+
+mla_status do_flash(const mla_shape* s, const void* q_abs, int q_n_frames, const void* cache,
+                    const int32_t* slot_frame, const float* tables, int rope_t_first, int rope_n_t, void* o_lat,
+                    int splits, void* ws, hipStream_t st) {
+  mla::FlashParams p;
+  p.q_abs = q_abs;
+  p.cache = cache;
+  p.slot_frame = slot_frame;
+  p.tables = tables;
+  p.o_lat = o_lat;
+  const FlashWs w = flash_ws_layout(s, q_n_frames, splits);
+  char* base = (char*)ws;
+  p.fallback_count = (int*)(base + w.count);
+  p.fallback_rows = (int*)(base + w.rows);
+  p.part_o = splits > 1 ? (float*)(base + w.part_o) : nullptr;
+  p.part_l = splits > 1 ? (float*)(base + w.part_l) : nullptr;
+  p.rl = rope_layout(s, rope_t_first, rope_n_t);
+  p.Mb = (int)(q_n_frames * tokens_per_frame(s) * s->n_heads);
+  p.W = s->window_frames;
+  p.T = (int)tokens_per_frame(s);
+  p.grid_x = s->grid_x;
+  p.batch = s->batch;
+  p.splits = splits;
+  p.scale_log2 = scale_log2(s);
+  return from_hip(mla::launch_flash(s->dtype, s->d_c, s->d_rope, p, st));
+}
+
+mla_status do_up_v(const mla_shape* s, const void* o_lat, int q_n_frames, const void* w_uv, void* out,
+                   hipStream_t st) {
+  mla::UpVParams p;
+  p.o_lat = o_lat;
+  p.w_uv = w_uv;
+  p.out = out;
+  p.rows = (int)(s->batch * q_n_frames * tokens_per_frame(s));
+  p.H = s->n_heads;
+  p.d_head = s->d_head;
+  return from_hip(mla::launch_up_v(s->dtype, s->d_c, s->d_rope, p, st));
+}
+
+mla_status check_query_args(const mla_shape* s, int q_frame_first, int q_n_frames) {
+  if (q_frame_first < 0 || q_n_frames < 1) return MLA_ERR_RANGE;
+  const int64_t rows = (int64_t)s->batch * q_n_frames * tokens_per_frame(s) * s->n_heads;
+  if (rows > INT32_MAX / 2) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
+}  // namespace
+
+MLA_API int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+MLA_API const char* mla_status_string(int32_t status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "dimensions inconsistent or out of range";
+    case MLA_ERR_DTYPE: return "dtype must be MLA_BF16 or MLA_F32";
+    case MLA_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case MLA_ERR_WORKSPACE: return "workspace too small";
+    case MLA_ERR_UNSUPPORTED: return "(d_c, d_rope) has no kernel instantiation";
+    case MLA_ERR_HIP: return "HIP launch failed";
+    case MLA_ERR_RANGE: return "frame or table index out of range";
+    default: return "unknown status";
+  }
+}
+
+MLA_API mla_status mla_shape_check(const mla_shape* shape) { return check_shape(shape); }
+
+MLA_API int32_t mla_qabs_dim(const mla_shape* shape) {
+  return check_shape(shape) == MLA_OK ? qabs_dim(shape) : 0;
+}
+
+MLA_API size_t mla_rope3d_table_floats(const mla_shape* shape, int32_t n_t) {
+  if (check_shape(shape) != MLA_OK || n_t < 1) return 0;
+  return table_floats(shape, n_t);
+}
+
+MLA_API mla_status mla_rope3d_tables(const mla_shape* shape, int32_t t_first, int32_t n_t, float* tables,
+                                     void* stream) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!tables) return MLA_ERR_NULL;
+  if (!aligned16(tables)) return MLA_ERR_ALIGN;
+  if (n_t < 1 || t_first < 0 || (int64_t)t_first + n_t > INT32_MAX) return MLA_ERR_RANGE;
+  mla::RopeTableParams p;
+  p.tables = tables;
+  p.rl = rope_layout(shape, t_first, n_t);
+  p.grid_y = shape->grid_y;
+  p.grid_x = shape->grid_x;
+  p.base = (double)shape->rope_base;
+  p.total = (int)(table_floats(shape, n_t) / 2);
+  return from_hip(mla::launch_rope_tables(p, (hipStream_t)stream));
+}
+
+MLA_API mla_status mla_cache_write(const mla_shape* shape, const void* x, const void* w_dkv, const void* w_kr,
+                                   int32_t frame_first, int32_t n_frames, void* cache, int32_t* slot_frame,
+                                   void* stream) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!x || !w_dkv || !w_kr || !cache || !slot_frame) return MLA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_dkv) || !aligned16(w_kr) || !aligned16(cache) || !aligned16(slot_frame))
+    return MLA_ERR_ALIGN;
+  if (frame_first < 0 || n_frames < 1 || n_frames > shape->window_frames ||
+      (int64_t)frame_first + n_frames > INT32_MAX)
+    return MLA_ERR_RANGE;
+  const int64_t rows = (int64_t)shape->batch * n_frames * tokens_per_frame(shape);
+  if (rows > INT32_MAX / 2) return MLA_ERR_SHAPE;
+  mla::CacheWriteParams p;
+  p.x = x;
+  p.w_dkv = w_dkv;
+  p.w_kr = w_kr;
+  p.cache = cache;
+  p.slot_frame = slot_frame;
+  p.rows = (int)rows;
+  p.rows_per_b = (int)(n_frames * tokens_per_frame(shape));
+  p.hidden = shape->hidden;
+  p.d_c = shape->d_c;
+  p.d_rope = shape->d_rope;
+  p.W = shape->window_frames;
+  p.T = (int)tokens_per_frame(shape);
+  p.frame_first = frame_first;
+  p.n_frames = n_frames;
+  p.batch = shape->batch;
+  return from_hip(mla::launch_cache_write(shape->dtype, shape->d_c, shape->d_rope, p, (hipStream_t)stream));
+}
+
+MLA_API mla_status mla_absorb_q(const mla_shape* shape, const void* q_nope, const void* q_r, int32_t q_frame_first,
+                                int32_t q_n_frames, const void* w_uk, const float* rope_tables,
+                                int32_t rope_t_first, int32_t rope_n_t, void* q_abs, void* stream) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!q_nope || !q_r || !w_uk || !q_abs) return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || !aligned16(q_r) || !aligned16(w_uk) || !aligned16(q_abs)) return MLA_ERR_ALIGN;
+  if ((st = check_tables(shape, rope_tables, rope_t_first, rope_n_t)) != MLA_OK) return st;
+  if ((st = check_query_args(shape, q_frame_first, q_n_frames)) != MLA_OK) return st;
+  if (q_frame_first < rope_t_first || (int64_t)q_frame_first + q_n_frames > (int64_t)rope_t_first + rope_n_t)
+    return MLA_ERR_RANGE;
+  return do_absorb(shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk, rope_tables, rope_t_first, rope_n_t, q_abs,
+                   (hipStream_t)stream);
+}
+
+MLA_API size_t mla_flash_workspace_bytes(const mla_shape* shape, int32_t q_n_frames, int32_t kv_splits) {
+  if (check_shape(shape) != MLA_OK || q_n_frames < 1 || kv_splits < 0 || kv_splits > kMaxSplits) return 0;
+  return flash_ws_bytes(shape, q_n_frames, choose_splits(shape, q_n_frames, kv_splits));
+}
+
+MLA_API mla_status mla_flash_attend(const mla_shape* shape, const void* q_abs, int32_t q_n_frames, const void* cache,
+                                    const int32_t* slot_frame, const float* rope_tables, int32_t rope_t_first,
+                                    int32_t rope_n_t, void* o_lat, int32_t kv_splits, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!q_abs || !cache || !slot_frame || !o_lat) return MLA_ERR_NULL;
+  if (!aligned16(q_abs) || !aligned16(cache) || !aligned16(slot_frame) || !aligned16(o_lat)) return MLA_ERR_ALIGN;
+  if ((st = check_tables(shape, rope_tables, rope_t_first, rope_n_t)) != MLA_OK) return st;
+  if ((st = check_query_args(shape, 0, q_n_frames)) != MLA_OK) return st;
+  if (kv_splits < 0 || kv_splits > kMaxSplits) return MLA_ERR_RANGE;
+  const int splits = choose_splits(shape, q_n_frames, kv_splits);
+  if (!workspace) return MLA_ERR_NULL;
+  if (!aligned16(workspace)) return MLA_ERR_ALIGN;
+  if (workspace_bytes < flash_ws_bytes(shape, q_n_frames, splits)) return MLA_ERR_WORKSPACE;
+  return do_flash(shape, q_abs, q_n_frames, cache, slot_frame, rope_tables, rope_t_first, rope_n_t, o_lat, splits,
+                  workspace, (hipStream_t)stream);
+}
+
+MLA_API mla_status mla_up_v(const mla_shape* shape, const void* o_lat, int32_t q_n_frames, const void* w_uv,
+                            void* out, void* stream) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!o_lat || !w_uv || !out) return MLA_ERR_NULL;
+  if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  if ((st = check_query_args(shape, 0, q_n_frames)) != MLA_OK) return st;
+  return do_up_v(shape, o_lat, q_n_frames, w_uv, out, (hipStream_t)stream);
+}
+
+MLA_API size_t mla_chunk_attend_workspace_bytes(const mla_shape* shape, int32_t q_n_frames) {
+  if (check_shape(shape) != MLA_OK || q_n_frames < 1) return 0;
+  const size_t rows = (size_t)shape->batch * q_n_frames * tokens_per_frame(shape) * shape->n_heads;
+  return round256(rows * qabs_dim(shape) * elt_size(shape)) + round256(rows * shape->d_c * elt_size(shape)) +
+         flash_ws_bytes(shape, q_n_frames, choose_splits(shape, q_n_frames, 0));
+}
+
+MLA_API mla_status mla_chunk_attend(const mla_shape* shape, const void* q_nope, const void* q_r, int32_t q_frame_first,
+                                    int32_t q_n_frames, const void* w_uk, const void* w_uv, const void* cache,
+                                    const int32_t* slot_frame, const float* rope_tables, int32_t rope_t_first,
+                                    int32_t rope_n_t, void* out, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!q_nope || !q_r || !w_uk || !w_uv || !cache || !slot_frame || !out || !workspace) return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || !aligned16(q_r) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(cache) ||
+      !aligned16(slot_frame) || !aligned16(out) || !aligned16(workspace))
+    return MLA_ERR_ALIGN;
+  if ((st = check_tables(shape, rope_tables, rope_t_first, rope_n_t)) != MLA_OK) return st;
+  if ((st = check_query_args(shape, q_frame_first, q_n_frames)) != MLA_OK) return st;
+  if (q_frame_first < rope_t_first || (int64_t)q_frame_first + q_n_frames > (int64_t)rope_t_first + rope_n_t)
+    return MLA_ERR_RANGE;
+  if (workspace_bytes < mla_chunk_attend_workspace_bytes(shape, q_n_frames)) return MLA_ERR_WORKSPACE;
+  const size_t rows = (size_t)shape->batch * q_n_frames * tokens_per_frame(shape) * shape->n_heads;
+  char* ws = (char*)workspace;
+  void* q_abs = ws;
+  ws += round256(rows * qabs_dim(shape) * elt_size(shape));
+  void* o_lat = ws;
+  ws += round256(rows * shape->d_c * elt_size(shape));
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = do_absorb(shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk, rope_tables, rope_t_first, rope_n_t,
+                      q_abs, s)) != MLA_OK)
+    return st;
+  const int splits = choose_splits(shape, q_n_frames, 0);
+  if ((st = do_flash(shape, q_abs, q_n_frames, cache, slot_frame, rope_tables, rope_t_first, rope_n_t, o_lat, splits,
+                     ws, s)) != MLA_OK)
+    return st;
+  return do_up_v(shape, o_lat, q_n_frames, w_uv, out, s);
+}

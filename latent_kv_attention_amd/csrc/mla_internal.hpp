@@ -1,0 +1,78 @@
+// Internal launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Offsets (in floats) of the six RoPE tables inside one table buffer.
+struct RopeLayout {
+  int d_t, d_y, d_x;
+  int t_first, n_t;
+  int off_ct, off_st, off_cy, off_sy, off_cx, off_sx;
+};
+
+struct RopeTableParams {
+  float* tables;
+  RopeLayout rl;
+  int grid_y, grid_x;
+  double base;
+  int total;  // number of (position, pair) entries over the three axes
+};
+
+struct CacheWriteParams {
+  const void* x;       // [rows][hidden]
+  const void* w_dkv;   // [d_c][hidden]
+  const void* w_kr;    // [d_rope][hidden]
+  void* cache;         // [B][W][T][d_c + d_rope]
+  int32_t* slot_frame; // [B][W]
+  int rows;            // B * n_frames * T
+  int rows_per_b;      // n_frames * T
+  int hidden, d_c, d_rope, W, T, frame_first, n_frames, batch;
+};
+
+struct AbsorbParams {
+  const void* q_nope;  // [B*Nq][H][d_head]
+  const void* q_r;     // [B*Nq][H][d_rope]
+  const void* w_uk;    // [H][d_head][d_c]
+  const float* tables;
+  void* q_abs;         // [B*Nq][H][Q]
+  RopeLayout rl;
+  int rows;            // B * Nq
+  int n_q, H, d_head, T, grid_x, q_frame_first;
+};
+
+struct FlashParams {
+  const void* q_abs;       // [B][Mb][Q]
+  const void* cache;       // [B][W][T][d_c + d_rope]
+  const int32_t* slot_frame;
+  const float* tables;
+  void* o_lat;             // [B][Mb][d_c]
+  float* part_o;           // [splits][B][Mb][d_c] when splits > 1
+  float* part_l;           // [splits][B][Mb][2] (reference, sum) when splits > 1
+  int* fallback_count;     // rows listed for the exact fallback
+  int* fallback_rows;      // [B * Mb]
+  RopeLayout rl;
+  int Mb;                  // Nq * H
+  int W, T, grid_x, batch, splits;
+  float scale_log2;        // softmax scale * log2(e)
+};
+
+constexpr int kFallbackBlocks = 64;
+
+struct UpVParams {
+  const void* o_lat;  // [B*Nq][H][d_c]
+  const void* w_uv;   // [H][d_head][d_c]
+  void* out;          // [B*Nq][H][d_head]
+  int rows, H, d_head;
+};
+
+hipError_t launch_rope_tables(const RopeTableParams& p, hipStream_t s);
+hipError_t launch_cache_write(int dtype, int d_c, int d_rope, const CacheWriteParams& p, hipStream_t s);
+hipError_t launch_absorb_q(int dtype, int d_c, int d_rope, const AbsorbParams& p, hipStream_t s);
+hipError_t launch_flash(int dtype, int d_c, int d_rope, const FlashParams& p, hipStream_t s);
+hipError_t launch_up_v(int dtype, int d_c, int d_rope, const UpVParams& p, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,81 @@
+// Value up-projection (hyper.ai summary of VideoMLA, Method section: the
+// value of head h is v = W_uv[h] c). The softmax-weighted sum of the values is
+// W_uv[h] applied once to the softmax-weighted latent:
+//   out[b,i,h,:] = W_uv[h] o_lat[b,i,h,:]
+// GEMM per head with both operands contiguous along the contraction (d_c):
+// A = o_lat rows, B[k][n] = W_uv[h][n][k]. Work-group: 64 tokens x one head,
+// each wave 16 tokens x all d_head outputs; W_uv[h] is staged in LDS in
+// slabs of 64 output rows shared by the four waves.
+#include "mla_common.hpp"
+#include "mla_internal.hpp"
+
+namespace mla {
+
+template <typename T, int DC>
+__global__ __launch_bounds__(256) void up_v_kernel(UpVParams p) {
+  typedef typename V8<T>::type v8;
+  constexpr int NKC = (DC + 31) / 32;
+  constexpr int PADE = 16 / sizeof(T);
+  constexpr int LS = NKC * 32 + PADE;  // LDS row stride, contraction zero-padded to 32
+  constexpr int SLAB = 64;             // output rows (d) per LDS slab
+  __shared__ __attribute__((aligned(16))) T wl[SLAB * LS];
+
+  const int h = blockIdx.y;
+  const int row0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int H = p.H, dh = p.d_head;
+
+  const int arow = row0 + wave * 16 + li;
+  const bool arow_ok = arow < p.rows;
+  const T* orow = (const T*)p.o_lat + ((size_t)(arow_ok ? arow : 0) * H + h) * DC;
+  v8 a[NKC];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc)
+    a[kc] = (arow_ok && kc * 32 + lg * 8 < DC) ? load8<T>(orow + kc * 32 + lg * 8) : zero8<T>();
+
+  const T* wbase = (const T*)p.w_uv + (size_t)h * dh * DC;
+  T* out = (T*)p.out;
+  for (int n0 = 0; n0 < dh; n0 += SLAB) {
+    __syncthreads();
+    for (int e = tid; e < SLAB * (NKC * 4); e += 256) {
+      const int r = e / (NKC * 4), c8 = (e % (NKC * 4)) * 8;
+      const v8 v = (n0 + r < dh && c8 < DC) ? load8<T>(wbase + (size_t)(n0 + r) * DC + c8) : zero8<T>();
+      store8<T>(wl + r * LS + c8, v);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < SLAB / 16; ++nb) {
+      if (n0 + nb * 16 >= dh) break;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const v8 bop = lds_load8<T>(wl + (nb * 16 + li) * LS + kc * 32 + lg * 8);
+        acc = mma16(a[kc], bop, acc);
+      }
+      const int n = n0 + nb * 16 + li;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = row0 + wave * 16 + lg * 4 + i;
+        if (r < p.rows && n < dh) out[((size_t)r * H + h) * dh + n] = to_t<T>(acc[i]);
+      }
+    }
+  }
+}
+
+template <typename T, int DC>
+static hipError_t launch_up_v_t(const UpVParams& p, hipStream_t s) {
+  dim3 grid((p.rows + 63) / 64, p.H);
+  hipLaunchKernelGGL((up_v_kernel<T, DC>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_up_v(int dtype, int d_c, int d_rope, const UpVParams& p, hipStream_t s) {
+  (void)d_rope;
+  if (p.rows <= 0) return hipSuccess;
+  if (d_c == 192) return dtype == 0 ? launch_up_v_t<bf16, 192>(p, s) : launch_up_v_t<float, 192>(p, s);
+  if (d_c == 16) return dtype == 0 ? launch_up_v_t<bf16, 16>(p, s) : launch_up_v_t<float, 16>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mla

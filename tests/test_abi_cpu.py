@@ -1,0 +1,104 @@
+"""The C-ABI library loads, exports every symbol include/mla.h declares, and
+rejects bad arguments on the host before touching the GPU (no compute calls
+here: every call below fails validation, so nothing is enqueued)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import latent_kv_attention_amd as mla
+from harness import get_config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert _declared() == sorted(mla.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(built_lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", built_lib], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\b(mla_[a-z0-9_]+)\b", out))
+    missing = set(_declared()) - exported
+    assert not missing, missing
+    lib = mla.lib()
+    for name in _declared():
+        assert getattr(lib, name) is not None
+
+
+def test_abi_version_and_status_strings(built_lib):
+    assert mla.abi_version() == 1
+    lib = mla.lib()
+    for code in range(9):
+        s = lib.mla_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.mla_status_string(99) == b"unknown status"
+
+
+def _shape(name="wan", **kw):
+    s = mla.make_shape(get_config(name))
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("dtype", 7, 3), ("batch", 0, 2), ("hidden", 12, 2), ("d_head", 12, 2), ("d_head", 512, 2),
+    ("window_frames", 0, 2), ("window_frames", 65, 2), ("d_rope_t", 7, 2), ("d_rope_x", 10, 2),
+    ("rope_base", 0.0, 2), ("grid_x", 0, 2), ("d_c", 128, 6),
+])
+def test_shape_validation(built_lib, field, value, code):
+    assert mla.shape_check(_shape()) == 0
+    assert mla.shape_check(_shape(**{field: value})) == code
+
+
+def test_host_queries(built_lib):
+    wan = _shape()
+    assert mla.qabs_dim(wan) == 224
+    assert mla.qabs_dim(_shape("tiny")) == 32
+    assert mla.qabs_dim(_shape(d_c=100)) == 0
+    # tables: 2 * (n_t*4 + 30*6 + 52*6)
+    assert mla.rope3d_table_floats(wan, 21) == 2 * (21 * 4 + 30 * 6 + 52 * 6)
+    assert mla.rope3d_table_floats(wan, 0) == 0
+    ws = mla.chunk_attend_workspace_bytes(wan, 3)
+    rows = 3 * 1560 * 12
+    assert ws >= rows * 224 * 2 + rows * 192 * 2
+    assert mla.flash_workspace_bytes(wan, 3, 4) > mla.flash_workspace_bytes(wan, 3, 1)
+    assert mla.flash_workspace_bytes(wan, 3, 17) == 0
+
+
+def test_entry_points_reject_bad_arguments_before_launch(built_lib):
+    lib = mla.lib()
+    s = _shape()
+    sp = ctypes.byref(s)
+    fake = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: validation fails first
+    odd = ctypes.c_void_p(0x100008)
+    # NULL pointers
+    assert lib.mla_cache_write(sp, None, fake, fake, 0, 3, fake, fake, None) == 1
+    assert lib.mla_rope3d_tables(sp, 0, 21, None, None) == 1
+    assert lib.mla_up_v(sp, fake, 3, None, fake, None) == 1
+    # misalignment
+    assert lib.mla_cache_write(sp, odd, fake, fake, 0, 3, fake, fake, None) == 4
+    # frame ranges: n_frames > window, negative first frame
+    assert lib.mla_cache_write(sp, fake, fake, fake, 0, 22, fake, fake, None) == 8
+    assert lib.mla_cache_write(sp, fake, fake, fake, -1, 3, fake, fake, None) == 8
+    # query frames outside the RoPE table range
+    assert lib.mla_absorb_q(sp, fake, fake, 30, 3, fake, fake, 0, 21, fake, None) == 8
+    # workspace too small / splits out of range
+    assert lib.mla_flash_attend(sp, fake, 3, fake, fake, fake, 0, 21, fake, 0, fake, 16, None) == 5
+    assert lib.mla_flash_attend(sp, fake, 3, fake, fake, fake, 0, 21, fake, 17, fake, 1 << 30, None) == 8
+    assert lib.mla_chunk_attend(sp, fake, fake, 0, 3, fake, fake, fake, fake, fake, 0, 21, fake, fake, 16,
+                                None) == 5
+    # unsupported latent width
+    bad = _shape(d_c=128)
+    assert lib.mla_cache_write(ctypes.byref(bad), fake, fake, fake, 0, 3, fake, fake, None) == 6
+    assert lib.mla_shape_check(None) == 1

@@ -1,0 +1,315 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Every step of the hot path is checked on its own against the oracle's value
+for that step (inputs made by the oracle and rounded to the storage type),
+and the whole step (cache write + absorb + flash + up-projection) against the
+oracle's explicit per-head reconstruction. Sizes span several tiles with
+ragged tails; the Wan-shaped full-size step is checked on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import latent_kv_attention_amd as mla
+from latent_kv_attention_amd.layer import LatentLayer
+from harness import get_config, round_to
+from oracle import mla_oracle as O
+
+from .gpu_common import (Stream, assert_rounded_close, assert_step_close, device_weights, oracle_step_rows,
+                         to_numpy, to_torch)
+
+pytestmark = pytest.mark.gpu
+
+STAGE_CONFIGS = ["tiny", "tiny_bf16", "wan_small", "wan_small_f32"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib(built_lib):
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    mla.lib()
+    yield
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ a1 RoPE tables
+
+@pytest.mark.parametrize("name,t_first,n_t", [("tiny", 0, 8), ("wan", 0, 21), ("wan", 200, 50)])
+def test_rope_tables(name, t_first, n_t):
+    cfg = get_config(name)
+    shape = mla.make_shape(cfg)
+    tab = torch.empty(mla.rope3d_table_floats(shape, n_t), dtype=torch.float32, device="cuda")
+    mla.rope3d_tables(shape, t_first, n_t, tab)
+    _sync()
+    ref = O.rope_tables_flat(cfg.rope_split, cfg.rope_base, t_first, n_t, cfg.grid_y, cfg.grid_x)
+    ref32 = ref.astype(np.float32)
+    got = tab.cpu().numpy()
+    assert got.shape == ref32.shape
+    ulp = np.spacing(np.abs(ref32)).astype(np.float64)
+    assert np.all(np.abs(got.astype(np.float64) - ref32.astype(np.float64)) <= ulp), \
+        float(np.abs(got - ref32).max())
+
+
+# ------------------------------------------------------------------ a2 + a6 cache write, ring
+
+@pytest.mark.parametrize("name", STAGE_CONFIGS)
+def test_cache_write_and_ring(name):
+    cfg = get_config(name)
+    w, wd = device_weights(cfg, seed=3)
+    st = Stream(cfg, seed=3)
+    layer = LatentLayer(cfg, wd, batch=1)
+    W = cfg.window_frames
+    written = {}
+    # fill the window in chunks of 2, then wrap around twice (eviction)
+    f = 0
+    while f < 2 * W + 3:
+        n = min(2, W)
+        x = st.xs(f, n)
+        layer.write(to_torch(x, cfg.dtype).reshape(1, n * cfg.tokens_per_frame, cfg.hidden), f, n)
+        for i in range(n):
+            written[(f + i) % W] = f + i
+        f += n
+        _sync()
+        sf = layer.slot_frame.cpu().numpy()[0]
+        exp = np.full(W, -1)
+        for s_, fr in written.items():
+            exp[s_] = fr
+        assert sf.tolist() == exp.tolist()
+    cache = to_numpy(layer.cache)[0]
+    for s_, fr in written.items():
+        c, kr = O.latents(st.x(fr), w["w_dkv"], w["w_kr"])
+        assert_rounded_close(cache[s_, :, :cfg.d_c], c, cfg.dtype, label=f"{name} c slot {s_}")
+        assert_rounded_close(cache[s_, :, cfg.d_c:], kr, cfg.dtype, label=f"{name} kR slot {s_}")
+
+
+def test_cache_write_batch_streams():
+    cfg = get_config("wan_small")
+    w, wd = device_weights(cfg, seed=4)
+    B = 3
+    layer = LatentLayer(cfg, wd, batch=B)
+    xs = [Stream(cfg, seed=4, stream=b).xs(5, 2) for b in range(B)]
+    layer.write(to_torch(np.stack(xs), cfg.dtype), 5, 2)
+    _sync()
+    cache = to_numpy(layer.cache)
+    assert layer.slot_frame.cpu().numpy().tolist() == [[5, 6, -1, -1, -1]] * B
+    for b in range(B):
+        for i in range(2):
+            c, kr = O.latents(xs[b][i * cfg.tokens_per_frame:(i + 1) * cfg.tokens_per_frame], w["w_dkv"], w["w_kr"])
+            assert_rounded_close(cache[b, (5 + i) % 5, :, :cfg.d_c], c, cfg.dtype, label=f"b{b} f{5 + i}")
+            assert_rounded_close(cache[b, (5 + i) % 5, :, cfg.d_c:], kr, cfg.dtype, label=f"b{b} f{5 + i} kR")
+
+
+# ------------------------------------------------------------------ a3 absorb + rotate
+
+@pytest.mark.parametrize("name", STAGE_CONFIGS)
+def test_absorb_q(name):
+    cfg = get_config(name)
+    w, wd = device_weights(cfg, seed=5)
+    shape = mla.make_shape(cfg)
+    qf = 7
+    qn, qr = Stream(cfg, seed=5).q(qf)
+    tables = torch.empty(mla.rope3d_table_floats(shape, 16), dtype=torch.float32, device="cuda")
+    mla.rope3d_tables(shape, 0, 16, tables)
+    Q = mla.qabs_dim(shape)
+    out = torch.empty(cfg.n_q, cfg.n_heads, Q, dtype=wd["w_uk"].dtype, device="cuda")
+    mla.absorb_q(shape, to_torch(qn, cfg.dtype), to_torch(qr, cfg.dtype), qf, cfg.chunk_frames, wd["w_uk"], tables,
+                 0, 16, out)
+    _sync()
+    t, y, x = O.frame_positions(qf + np.arange(cfg.chunk_frames), cfg.grid_y, cfg.grid_x)
+    ref = O.absorbed_query(qn, qr, w["w_uk"], t, y, x, cfg.rope_split, cfg.rope_base)
+    got = to_numpy(out)
+    assert_rounded_close(got[..., :cfg.d_c + cfg.d_rope], ref, cfg.dtype, abs_=2e-5, label=f"{name} q_abs")
+    assert not got[..., cfg.d_c + cfg.d_rope:].any()
+
+
+# ------------------------------------------------------------------ a4 latent flash attention
+
+def _flash_inputs(cfg, seed, fill_frames, q_frame, q_scale=1.0):
+    """Oracle-made, storage-rounded inputs of the flash step: cache rows,
+    slot map and absorbed queries, plus the oracle's latent output."""
+    st = Stream(cfg, seed=seed)
+    from harness import layer_weights
+    wts = layer_weights(cfg, seed)
+    W, T = cfg.window_frames, cfg.tokens_per_frame
+    cache = np.zeros((W, T, cfg.d_c + cfg.d_rope))
+    slot_frame = np.full(W, -1, dtype=np.int32)
+    for f in fill_frames:
+        c, kr = O.latents(st.x(f), wts["w_dkv"], wts["w_kr"])
+        cache[f % W, :, :cfg.d_c] = round_to(c, cfg.dtype)
+        cache[f % W, :, cfg.d_c:] = round_to(kr, cfg.dtype)
+        slot_frame[f % W] = f
+    qn, qr = st.q(q_frame, q_scale=q_scale)
+    t, y, x = O.frame_positions(q_frame + np.arange(cfg.chunk_frames), cfg.grid_y, cfg.grid_x)
+    q_abs = round_to(O.absorbed_query(qn, qr, wts["w_uk"], t, y, x, cfg.rope_split, cfg.rope_base), cfg.dtype)
+    valid = [s_ for s_ in range(W) if slot_frame[s_] >= 0]
+    c_all = cache[valid, :, :cfg.d_c].reshape(-1, cfg.d_c)
+    kr_all = cache[valid, :, cfg.d_c:].reshape(-1, cfg.d_rope)
+    tk, yk, xk = O.frame_positions(slot_frame[valid], cfg.grid_y, cfg.grid_x)
+    k_rope = O.rope3d(kr_all, tk, yk, xk, cfg.rope_split, cfg.rope_base)
+    ref = O.attend_latent(q_abs, c_all, k_rope, O.default_scale(cfg.d_head, cfg.d_rope))
+    return cache, slot_frame, q_abs, ref
+
+
+def _run_flash(cfg, cache, slot_frame, q_abs, kv_splits=0, n_t=64, want_fallback_count=False):
+    shape = mla.make_shape(cfg)
+    Q = mla.qabs_dim(shape)
+    qa = np.zeros(q_abs.shape[:-1] + (Q,))
+    qa[..., :q_abs.shape[-1]] = q_abs
+    tables = torch.empty(mla.rope3d_table_floats(shape, n_t), dtype=torch.float32, device="cuda")
+    mla.rope3d_tables(shape, 0, n_t, tables)
+    o_lat = torch.empty(q_abs.shape[0], cfg.n_heads, cfg.d_c, dtype=torch.bfloat16 if cfg.dtype == "bf16"
+                        else torch.float32, device="cuda")
+    ws = torch.empty(mla.flash_workspace_bytes(shape, cfg.chunk_frames, kv_splits), dtype=torch.uint8, device="cuda")
+    mla.flash_attend(shape, to_torch(qa, cfg.dtype), cfg.chunk_frames, to_torch(cache[None], cfg.dtype),
+                     torch.from_numpy(slot_frame[None].copy()).cuda(), tables, 0, n_t, o_lat, ws, kv_splits)
+    _sync()
+    if want_fallback_count:  # the fallback row count sits at the start of the flash workspace
+        return to_numpy(o_lat), int(ws[:4].view(torch.int32).item())
+    return to_numpy(o_lat)
+
+
+@pytest.mark.parametrize("name", STAGE_CONFIGS)
+@pytest.mark.parametrize("kv_splits", [1, 3])
+def test_flash_attend(name, kv_splits):
+    cfg = get_config(name)
+    W = cfg.window_frames
+    cache, sf, q_abs, ref = _flash_inputs(cfg, 6, list(range(W + 2)), W + 2 - cfg.chunk_frames)
+    got = _run_flash(cfg, cache, sf, q_abs, kv_splits)
+    assert_step_close(got, ref, cfg.dtype, label=f"{name} flash splits={kv_splits}")
+
+
+@pytest.mark.parametrize("name", ["wan_small", "wan_small_f32"])
+def test_flash_attend_sharp_and_partial_window(name):
+    cfg = get_config(name)
+    # two of five slots filled, sharp queries (logit std ~4)
+    cache, sf, q_abs, ref = _flash_inputs(cfg, 7, [3, 4], 3, q_scale=4.0)
+    got = _run_flash(cfg, cache, sf, q_abs)
+    assert_step_close(got, ref, cfg.dtype, label=f"{name} flash sharp partial", sharp=True)
+
+
+def test_flash_attend_extreme_logits_use_exact_fallback():
+    """Logit gaps beyond the fixed-reference range (q x 50: logit std ~50):
+    those rows are listed and recomputed by the exact two-pass kernel. At such
+    logits the fp32 rounding of the scores themselves moves the output by
+    ~1e-3, so this case is gated at 5e-3 (max) and 5e-3 (relative RMS)."""
+    cfg = get_config("wan_small_f32")
+    cache, sf, q_abs, ref = _flash_inputs(cfg, 8, [0, 1, 2, 3], 3, q_scale=50.0)
+    for splits in (1, 2):
+        got, n_fallback = _run_flash(cfg, cache, sf, q_abs, splits, want_fallback_count=True)
+        from .gpu_common import errors
+        e = errors(got, ref)
+        print(f"[parity] extreme logits splits={splits} fallback rows={n_fallback} {e}", flush=True)
+        assert n_fallback > 0
+        assert e["max_abs"] <= 5e-3 and e["rel_rms"] <= 5e-3, e
+
+
+def test_flash_attend_empty_window_gives_zeros():
+    cfg = get_config("wan_small")
+    cache, sf, q_abs, _ = _flash_inputs(cfg, 9, [0, 1], 1)
+    sf[:] = -1
+    got = _run_flash(cfg, cache, sf, q_abs)
+    assert not got.any()
+
+
+# ------------------------------------------------------------------ a5 up-projection
+
+@pytest.mark.parametrize("name", STAGE_CONFIGS)
+def test_up_v(name):
+    cfg = get_config(name)
+    w, wd = device_weights(cfg, seed=10)
+    rng = np.random.default_rng(10)
+    o_lat = round_to(rng.standard_normal((cfg.n_q, cfg.n_heads, cfg.d_c)) * 0.1, cfg.dtype)
+    out = torch.empty(cfg.n_q, cfg.n_heads, cfg.d_head, dtype=wd["w_uv"].dtype, device="cuda")
+    mla.up_v(mla.make_shape(cfg), to_torch(o_lat, cfg.dtype), cfg.chunk_frames, wd["w_uv"], out)
+    _sync()
+    assert_rounded_close(to_numpy(out), O.up_project(o_lat, w["w_uv"]), cfg.dtype, abs_=1e-5, label=f"{name} up_v")
+
+
+# ------------------------------------------------------------------ the whole step
+
+def _full_step(cfg, seed=0, q_scale=1.0, B=1, fill=None):
+    """Prefill the window, write the chunk, attend; returns (gpu, oracle) per stream."""
+    w, wd = device_weights(cfg, seed)
+    W, T = cfg.window_frames, cfg.tokens_per_frame
+    fill = W if fill is None else fill
+    chunk_first = fill - cfg.chunk_frames
+    layer = LatentLayer(cfg, wd, batch=B, rope_n_t=max(64, fill + 1))
+    streams = [Stream(cfg, seed=seed, stream=b) for b in range(B)]
+    if chunk_first > 0:
+        pre = np.stack([s_.xs(0, chunk_first) for s_ in streams])
+        # prefill in pieces no larger than the window
+        for f0 in range(0, chunk_first, W):
+            n = min(W, chunk_first - f0)
+            layer.write(to_torch(pre[:, f0 * T:(f0 + n) * T], cfg.dtype).contiguous(), f0, n)
+    xc = np.stack([s_.xs(chunk_first, cfg.chunk_frames) for s_ in streams])
+    layer.write(to_torch(xc, cfg.dtype), chunk_first, cfg.chunk_frames)
+    qs = [s_.q(chunk_first, q_scale=q_scale) for s_ in streams]
+    out = layer.attend(to_torch(np.stack([q[0] for q in qs]), cfg.dtype),
+                       to_torch(np.stack([q[1] for q in qs]), cfg.dtype), chunk_first, cfg.chunk_frames)
+    _sync()
+    got = to_numpy(out)
+    refs = []
+    for b, s_ in enumerate(streams):
+        frames = list(range(max(0, fill - W), fill))
+        xs = {f: s_.x(f) for f in frames}
+        refs.append(oracle_step_rows(cfg, w, xs, frames, qs[b][0], qs[b][1], chunk_first))
+    return got, np.stack(refs)
+
+
+@pytest.mark.parametrize("name", STAGE_CONFIGS)
+@pytest.mark.parametrize("q_scale", [1.0, 4.0])
+def test_full_step(name, q_scale):
+    cfg = get_config(name)
+    got, ref = _full_step(cfg, seed=11, q_scale=q_scale)
+    assert_step_close(got, ref, cfg.dtype, label=f"{name} step q*{q_scale}", sharp=q_scale > 1.0)
+
+
+def test_full_step_batch_and_partial_fill():
+    cfg = get_config("wan_small")
+    got, ref = _full_step(cfg, seed=12, B=3, fill=3)
+    assert_step_close(got, ref, cfg.dtype, label="wan_small B=3 fill=3")
+
+
+def test_rollout_ring_eviction_and_time_advance():
+    """Successive 1-frame chunks over a 3-frame window: eviction starts at the
+    4th chunk and t advances to 9; every step matches the oracle's ring."""
+    cfg = get_config("wan_small").with_(window_frames=3, chunk_frames=1)
+    w, wd = device_weights(cfg, seed=13)
+    layer = LatentLayer(cfg, wd, batch=1, rope_n_t=16)
+    st = Stream(cfg, seed=13)
+    ring = O.RingCache(3, cfg.tokens_per_frame, cfg.d_c, cfg.d_rope)
+    for f in range(10):
+        x = st.x(f)
+        layer.write(to_torch(x[None], cfg.dtype), f, 1)
+        qn, qr = st.q(f)
+        out = layer.attend(to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype), f, 1)
+        _sync()
+        ref = O.chunk_step(O.dims_of(cfg), w, ring, x, f, qn, qr)
+        assert sorted(layer.slot_frame.cpu().numpy()[0].tolist()) == sorted(ring.slot_frame.tolist())
+        assert_step_close(to_numpy(out)[0], ref, cfg.dtype, label=f"rollout frame {f}")
+
+
+def test_wan_full_size_sampled_rows():
+    """Wan2.1-1.3B shape, 3-frame chunk over a full 21-frame window (4680 q x
+    32760 k), in the launch configuration the benchmark times; the oracle
+    checks 96 sampled query rows (all heads, full window), including the
+    first and last rows and tile-boundary rows."""
+    cfg = get_config("wan")
+    w, wd = device_weights(cfg, seed=0)
+    T = cfg.tokens_per_frame
+    layer = LatentLayer(cfg, wd, batch=1, rope_n_t=64)
+    st = Stream(cfg, seed=0)
+    layer.write(to_torch(st.xs(0, 18)[None], cfg.dtype), 0, 18)
+    layer.write(to_torch(st.xs(18, 3)[None], cfg.dtype), 18, 3)
+    qn, qr = st.q(18)
+    out = layer.attend(to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype), 18, 3)
+    _sync()
+    got = to_numpy(out)[0]
+    rng = np.random.default_rng(0)
+    edge = [0, 1, 21, 22, 42, 43, cfg.n_q // 2, T - 1, T, 2 * T - 1, 2 * T, cfg.n_q - 22, cfg.n_q - 1]
+    rows = np.unique(np.concatenate([edge, rng.choice(cfg.n_q, 96 - len(edge), replace=False)]))
+    xs = {f: st.x(f) for f in range(21)}
+    ref = oracle_step_rows(cfg, w, xs, list(range(21)), qn, qr, 18, rows)
+    assert_step_close(got[rows], ref, cfg.dtype, label="wan full size, sampled rows")
