@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of one latent-KV (VideoMLA) chunk step on one MI355X.
+
+Workload: one Wan2.1-1.3B-shaped layer (hidden 1536, 12 heads x 128, latent
+192 + positional 32), a 3-frame chunk (3 x 30 x 52 = 4680 query tokens)
+written into and attending over a full 21-frame ring window (32760 cached
+tokens), bf16 storage with fp32 accumulation, batch 1, seeded synthetic
+inputs (x ~ N(0,1), weights ~ N(0, 1/fan_in), queries ~ N(0,1)).
+
+One step = cache write of the chunk's 3 frames (down-projection into the
+ring) + query absorb/rotate + latent flash attention + W_uv up-projection,
+all inputs resident in HBM. Prints one JSON line (see the keys below).
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA chunk-attention TFLOP/s + cache-write GB/s, Wan-1.3B shape, 1 MI355X"
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak (AMD spec)
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "flash_mla_wan_traffic.json")
+FLASH_SOURCES = ["latent_kv_attention_amd/csrc/flash_mla.hip", "latent_kv_attention_amd/csrc/mla_common.hpp",
+                 "latent_kv_attention_amd/csrc/rope_device.hpp"]
+
+
+def flash_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in FLASH_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def step_flops(cfg):
+    """Algorithmic FLOPs of one step, absorbed form (what the kernels compute)."""
+    nq, nk, H = cfg.n_q, cfg.n_k, cfg.n_heads
+    cache_write = 2.0 * nq * cfg.hidden * (cfg.d_c + cfg.d_rope)
+    absorb = 2.0 * nq * H * cfg.d_head * cfg.d_c
+    flash = 2.0 * nq * H * nk * (cfg.d_c + cfg.d_rope + cfg.d_c)
+    up = 2.0 * nq * H * cfg.d_c * cfg.d_head
+    nonabs = 2.0 * nq * H * nk * (cfg.d_head + cfg.d_rope + cfg.d_head)
+    return dict(cache_write=cache_write, absorb=absorb, flash=flash, up_v=up,
+                total=cache_write + absorb + flash + up, flash_nonabsorbed_equiv=nonabs)
+
+
+def cache_write_bytes(cfg):
+    """Algorithmic HBM bytes of the chunk's cache write: x read once, the
+    stacked down-projection read once, the new cache rows written once."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    return e * (cfg.n_q * cfg.hidden + (cfg.d_c + cfg.d_rope) * cfg.hidden + cfg.n_q * (cfg.d_c + cfg.d_rope))
+
+
+def cpu_baseline(cfg, sample_tokens: int, seed: int = 0):
+    """The fp64 oracle as it stands, on a bounded sample of the same workload:
+    latents of the whole 21-frame window, explicit per-head reconstruction of
+    every key and value, and attention for the first `sample_tokens` query
+    tokens of the chunk (all heads, full window). Credited with the absorbed-
+    path FLOPs of that sample (cache write of the chunk + attention of those
+    rows), so the rate is in the metric's unit."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from harness import chunk_queries, frame_tokens, layer_weights
+    from oracle import mla_oracle as O
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    w = layer_weights(cfg, seed)
+    frames = list(range(cfg.window_frames))
+    xs = [frame_tokens(cfg, f, seed) for f in frames]
+    chunk_first = cfg.window_frames - cfg.chunk_frames
+    qn, qr = chunk_queries(cfg, chunk_first, seed)
+    with threadpool_limits(limits=cores):
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        t0 = time.perf_counter()
+        c, kr = O.latents(np.concatenate(xs), w["w_dkv"], w["w_kr"])
+        k_nope, v = O.reconstruct(c, w["w_uk"], w["w_uv"])
+        t, y, x = O.frame_positions(frames, cfg.grid_y, cfg.grid_x)
+        k_rope = O.rope3d(kr, t, y, x, cfg.rope_split, cfg.rope_base)
+        rows = np.arange(sample_tokens)
+        tq, yq, xq = O.frame_positions(chunk_first + np.arange(cfg.chunk_frames), cfg.grid_y, cfg.grid_x)
+        q_rope = O.rope3d(qr[rows], tq[rows], yq[rows], xq[rows], cfg.rope_split, cfg.rope_base)
+        O.attend(qn[rows], q_rope, k_nope, k_rope, v, O.default_scale(cfg.d_head, cfg.d_rope))
+        dt = time.perf_counter() - t0
+    fl = step_flops(cfg)
+    frac = sample_tokens / cfg.n_q
+    credited = fl["cache_write"] + frac * (fl["absorb"] + fl["flash"] + fl["up_v"])
+    return {"value": credited / dt / 1e12, "unit": "TFLOP/s", "cores": int(min(cores, used)), "kind": "oracle",
+            "sample": f"fp64 oracle: latents of 21 frames x 1560 tokens, per-head reconstruction of all "
+                      f"32760 keys and values, attention of the first {sample_tokens} of 4680 query tokens "
+                      f"(all 12 heads, full window); {dt:.2f} s, credited with the chunk cache write plus "
+                      f"{sample_tokens}/4680 of the attention-side FLOPs",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--kv-splits", type=int, default=0, help="flash key-range splits (0 = automatic)")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2340)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-buffers", type=int, default=40,
+                    help="rotating x buffers for the cold-cache cache-write measurement (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (to scale HBM byte counters) and exit")
+    args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        n = 1 << 29  # bf16 elements = 1 GiB
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "launches": 3}), flush=True)
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import latent_kv_attention_amd as mla
+    from harness import chunk_queries, frame_tokens, get_config, layer_weights
+    from harness.torch_io import to_torch
+
+    if not os.path.exists(mla.LIB_PATH):
+        from latent_kv_attention_amd import build as _build
+        _build.build()
+    mla.lib()
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    cfg = get_config("wan")
+    T = cfg.tokens_per_frame
+    dev = "cuda"
+    print(f"[bench] generating inputs ({cfg.note})", file=sys.stderr, flush=True)
+    w = {k: to_torch(v, cfg.dtype, dev) for k, v in layer_weights(cfg, 0).items()}
+    chunk_first = cfg.window_frames - cfg.chunk_frames
+    x_pre = to_torch(np.concatenate([frame_tokens(cfg, f) for f in range(chunk_first)]), cfg.dtype, dev)
+    x_chunk = to_torch(np.concatenate([frame_tokens(cfg, chunk_first + i) for i in range(cfg.chunk_frames)]),
+                       cfg.dtype, dev)
+    qn_h, qr_h = chunk_queries(cfg, chunk_first)
+    qn, qr = to_torch(qn_h, cfg.dtype, dev), to_torch(qr_h, cfg.dtype, dev)
+
+    shape = mla.make_shape(cfg, batch=1)
+    n_t = 64
+    tables = torch.empty(mla.rope3d_table_floats(shape, n_t), dtype=torch.float32, device=dev)
+    mla.rope3d_tables(shape, 0, n_t, tables)
+    cache = torch.zeros(1, cfg.window_frames, T, cfg.d_c + cfg.d_rope, dtype=torch.bfloat16, device=dev)
+    slot_frame = torch.full((1, cfg.window_frames), -1, dtype=torch.int32, device=dev)
+    mla.cache_write(shape, x_pre, w["w_dkv"], w["w_kr"], 0, chunk_first, cache, slot_frame)
+    Q = mla.qabs_dim(shape)
+    q_abs = torch.empty(cfg.n_q, cfg.n_heads, Q, dtype=torch.bfloat16, device=dev)
+    o_lat = torch.empty(cfg.n_q, cfg.n_heads, cfg.d_c, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(cfg.n_q, cfg.n_heads, cfg.d_head, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(mla.flash_workspace_bytes(shape, cfg.chunk_frames, args.kv_splits), dtype=torch.uint8,
+                     device=dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        mla.cache_write(shape, x_chunk, w["w_dkv"], w["w_kr"], chunk_first, cfg.chunk_frames, cache, slot_frame)
+        if ev:
+            ev[1].record()
+        mla.absorb_q(shape, qn, qr, chunk_first, cfg.chunk_frames, w["w_uk"], tables, 0, n_t, q_abs)
+        if ev:
+            ev[2].record()
+        mla.flash_attend(shape, q_abs, cfg.chunk_frames, cache, slot_frame, tables, 0, n_t, o_lat, ws,
+                         args.kv_splits)
+        if ev:
+            ev[3].record()
+        mla.up_v(shape, o_lat, cfg.chunk_frames, w["w_uv"], out)
+        if ev:
+            ev[4].record()
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    names = ["cache_write", "absorb_q", "flash_attend", "up_v"]
+    per = {n: float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs])) for k, n in enumerate(names)}
+    print(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step {per}", file=sys.stderr, flush=True)
+    assert torch.isfinite(out.float()).all(), "non-finite output"
+
+    # cold-cache cache write: rotate the input over more distinct buffers than the
+    # 256 MB last-level cache holds
+    cold = None
+    if args.cold_buffers > 0:
+        xs_cold = [x_chunk.clone() for _ in range(args.cold_buffers)]
+        for i in range(3):
+            mla.cache_write(shape, xs_cold[i], w["w_dkv"], w["w_kr"], chunk_first, cfg.chunk_frames, cache,
+                            slot_frame)
+        torch.cuda.synchronize()
+        ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.cold_buffers)]
+        for i, xb in enumerate(xs_cold):
+            ce[i][0].record()
+            mla.cache_write(shape, xb, w["w_dkv"], w["w_kr"], chunk_first, cfg.chunk_frames, cache, slot_frame)
+            ce[i][1].record()
+        torch.cuda.synchronize()
+        cold = float(np.mean([a.elapsed_time(b) for a, b in ce[3:]]))
+        del xs_cold
+
+    fl = step_flops(cfg)
+    cw_bytes = cache_write_bytes(cfg)
+    flash_tflops = fl["flash"] / (per["flash_attend"] * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(COUNTERS_FILE):
+        rec = json.load(open(COUNTERS_FILE))
+        if rec.get("source_hash") == flash_source_hash():
+            traffic = rec.get("hbm_bytes_per_launch")
+    result = {
+        "metric": METRIC,
+        "value": round(fl["total"] / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Wan2.1-1.3B-shaped layer, 3-frame chunk (4680 queries) over a full 21-frame "
+                               "window (32760 latent tokens), batch 1",
+                   "hidden": cfg.hidden, "n_heads": cfg.n_heads, "d_head": cfg.d_head, "d_c": cfg.d_c,
+                   "d_rope": cfg.d_rope, "rope_split": list(cfg.rope_split), "grid": [cfg.grid_y, cfg.grid_x],
+                   "chunk_frames": cfg.chunk_frames, "window_frames": cfg.window_frames, "batch": 1,
+                   "kv_splits": args.kv_splits},
+        "roofline": {"kernel": "flash_mla_kernel", "bound": "mfma", "achieved": round(flash_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(flash_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "flops_per_launch": fl["flash"]},
+        "cache_write_GBps": round(cw_bytes / (per["cache_write"] * 1e-3) / 1e9, 1),
+        "cache_write_cold_GBps": round(cw_bytes / (cold * 1e-3) / 1e9, 1) if cold else None,
+        "cache_write_hbm_frac_cold": round(cw_bytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4) if cold else None,
+        "kernel_ms": {k: round(v, 4) for k, v in per.items()},
+        "cache_write_cold_ms": round(cold, 4) if cold else None,
+        "flash_TFLOPs_nonabsorbed_equiv": round(fl["flash_nonabsorbed_equiv"] / (per["flash_attend"] * 1e-3) / 1e12,
+                                                2),
+        "step_flops": fl["total"],
+        "cache_write_bytes": cw_bytes,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline: oracle on {args.cpu_sample_tokens} query tokens", file=sys.stderr,
+              flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

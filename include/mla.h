@@ -139,9 +139,10 @@ mla_status mla_cache_write(const mla_shape* shape, const void* x, const void* w_
 /* ---------------------------------------------------------------- a3
  * Query absorb and rotate (hyper.ai summary, Method: score = content part
  * + positional part). For query token i of the chunk (frame
- * q_frame_first + i / T) and head h:
- *   q_abs[b][i][h][0:d_c]            = W_uk[h]^T q_nope[b][i][h]
- *   q_abs[b][i][h][d_c:d_c+d_rope]   = R(t, y, x) q_r[b][i][h]
+ * q_frame_first + i / T) and head h, with g = softmax_scale * log2(e) (the
+ * temperature folded in, so scores come out in log2 units):
+ *   q_abs[b][i][h][0:d_c]            = g W_uk[h]^T q_nope[b][i][h]
+ *   q_abs[b][i][h][d_c:d_c+d_rope]   = g R(t, y, x) q_r[b][i][h]
  *   q_abs[b][i][h][d_c+d_rope:Q]     = 0,    Q = mla_qabs_dim(shape)
  *   q_nope (device) [B][N_q][H][d_head], q_r (device) [B][N_q][H][d_rope]
  *   (unrotated), w_uk (device) [H][d_head][d_c], N_q = q_n_frames * T.
@@ -155,9 +156,10 @@ mla_status mla_absorb_q(const mla_shape* shape, const void* q_nope, const void* 
 
 /* ---------------------------------------------------------------- a4
  * Latent flash attention (hyper.ai summary, Method; chatpaper.ai abstract:
- * softmax over the sliding window). For every row (b, i, h):
- *   s_j   = scale * q_abs[b][i][h] . [c_j | R(t_j, y_j, x_j) kR_j]
- *   o_lat = sum_j softmax(s)_j c_j                       -> [d_c]
+ * softmax over the sliding window). For every row (b, i, h), with q_abs as
+ * mla_absorb_q writes it (temperature and log2 e already folded in):
+ *   s_j   = q_abs[b][i][h] . [c_j | R(t_j, y_j, x_j) kR_j]
+ *   o_lat = sum_j 2^(s_j) c_j / sum_j 2^(s_j)            -> [d_c]
  * over every key j of every slot of stream b with slot_frame[b][s] >= 0
  * (no intra-chunk mask); rows with no valid key get zeros.
  *   q_abs (device) [B][N_q][H][Q] from mla_absorb_q; cache, slot_frame as

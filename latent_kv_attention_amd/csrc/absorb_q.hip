@@ -1,8 +1,10 @@
 // Query absorb and rotate (hyper.ai summary of VideoMLA, Method section: the
 // score of head h is q_nope . k_nope + q_rope . k_rope with k_nope = W_uk[h] c
 // and k_rope the rotated shared key). Since q . (W_uk[h] c) = (W_uk[h]^T q) . c,
-// the query is mapped once into latent space:
-//   q_abs[b,i,h] = [ W_uk[h]^T q_nope[b,i,h] | R(t,y,x) q_r[b,i,h] | 0 ... ]
+// the query is mapped once into latent space, multiplied by the softmax
+// temperature in log2 units (qscale = scale * log2 e) so that scores come out
+// of the matrix product ready for exp2:
+//   q_abs[b,i,h] = qscale [ W_uk[h]^T q_nope[b,i,h] | R(t,y,x) q_r[b,i,h] | 0 ... ]
 // Work-group: 64 query tokens x one head. The 32-row slabs of W_uk[h] are
 // staged in LDS and read with the transposing LDS load, because the
 // contraction runs over W_uk's row index.
@@ -56,7 +58,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(AbsorbParams p) {
     if (r >= p.rows) continue;
     T* dst = qa + ((size_t)r * H + h) * KP;
 #pragma unroll
-    for (int nb = 0; nb < NNB; ++nb) dst[nb * 16 + li] = to_t<T>(acc[nb][i]);
+    for (int nb = 0; nb < NNB; ++nb) dst[nb * 16 + li] = to_t<T>(acc[nb][i] * p.qscale);
   }
 
   // rotated positional part and zero padding
@@ -73,8 +75,8 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(AbsorbParams p) {
     rope_cos_sin(p.rl, p.tables, pr, t, y, x, c, s);
     rotate_pair(a0, a1, c, s);
     T* dst = qa + ((size_t)r * H + h) * KP + DC + 2 * pr;
-    dst[0] = to_t<T>(a0);
-    dst[1] = to_t<T>(a1);
+    dst[0] = to_t<T>(a0 * p.qscale);
+    dst[1] = to_t<T>(a1 * p.qscale);
   }
   if constexpr (KP > DC + DR) {
     constexpr int NPAD = KP - DC - DR;

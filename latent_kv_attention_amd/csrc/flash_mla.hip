@@ -4,37 +4,43 @@
 // q_nope . (W_uk[h] c_j) + q_rope . R(p_j) kR_j and takes the value
 // W_uv[h] c_j, so one read of the cached [c_j | kR_j] serves every head.
 // chatpaper.ai abstract: the keys are the frames of a fixed-size sliding
-// window. With the absorbed query q_abs = [W_uk[h]^T q_nope | R(p_i) qR | 0]
-// this file computes, for every row (b, i, h),
-//   s_j   = q_abs . [c_j | R(t_j, y_j, x_j) kR_j | 0]
-//   o_lat = sum_j softmax(scale * s)_j c_j
+// window. With the absorbed query (already multiplied by c = scale * log2 e)
+// q_abs = c [W_uk[h]^T q_nope | R(p_i) qR | 0] this file computes, for every
+// row (b, i, h),
+//   s_j   = q_abs . [c_j | R(t_j, y_j, x_j) kR_j | 0]      (log2 units)
+//   o_lat = sum_j 2^(s_j) c_j / sum_j 2^(s_j)
 // over every key of every valid ring slot.
 //
-// Softmax with a fixed per-row reference. exp is shift-invariant, so any
-// reference r_i gives o = sum_j 2^((s_j - r_i) c) c_j / sum_j 2^((s_j - r_i) c)
-// (c = scale * log2 e). Each row takes r_i = the exact maximum of its scores
-// over the first 32 keys it visits; later keys may score higher, so a
-// probability can exceed 1, but fp32 (and bf16) reach 2^127 and the largest
-// probability is at least 1, so nothing underflows. No running maximum is
-// tracked and the output accumulators are never rescaled, so they stay in the
-// matrix-core accumulator registers. A row whose probability sum exceeds 2^100
-// (a logit gap beyond ~70 nats) is listed and recomputed by an exact
-// two-pass kernel instead.
+// Softmax with a fixed per-row reference. 2^s is shift-invariant, so any
+// reference r_i gives the same o. Each row takes r_i = the exact maximum of
+// its scores over the first 32 keys it visits; later keys may score higher,
+// so a probability can exceed 1, but fp32 (and bf16) reach 2^127 and the
+// largest probability is at least 1, so nothing underflows. The reference is
+// folded into the score product itself (the first product of every score
+// block starts from -r_i instead of 0), so a probability costs one exp2; no
+// running maximum is tracked and the output accumulators are never rescaled.
+// A row whose probability sum exceeds 2^100 (a logit gap beyond ~70 nats) is
+// listed and recomputed by an exact two-pass kernel.
 //
 // Layout of the work (bf16):
 //   * the 12 heads of a query are consecutive rows (all heads share the
-//     keys); a work-group owns 256 rows, each of its 4 waves 64 rows held as
-//     four 16-row blocks, queries kept in registers for the whole key loop;
-//   * keys stream in 64-key tiles through LDS, double-buffered. The latent
-//     part goes global -> LDS directly (no registers); the kR part goes
-//     through registers and is rotated by 3D-RoPE on its way into LDS;
+//     keys); a work-group owns 256 rows in 8 waves of 32 rows (two 16-row
+//     blocks), two waves per SIMD, so one wave's exp2 work overlaps the
+//     other's matrix products; queries stay in registers for the key loop;
+//   * keys stream in 64-key tiles through LDS, double-buffered, one barrier
+//     per tile. The latent part goes global -> LDS directly (no registers);
+//     the kR part goes through registers and is rotated by 3D-RoPE on its way
+//     into LDS. LDS rows are 480 bytes apart, which keeps both LDS read
+//     patterns below free of bank conflicts;
 //   * scores are formed transposed, S^T = K Q^T (keys as rows), so a lane
 //     holds 4 keys of one query row and the probabilities already sit in the
 //     lane layout of the B operand of O^T = C^T P^T. The C^T operand is read
 //     from the same LDS tile with the transposing LDS load: the latent is
-//     staged once for both products.
-//   * kv_splits > 1 partitions the key tiles; splits share the reference, so
-//     a second pass just adds their (output, sum) pairs.
+//     staged once for both products;
+//   * kv_splits > 1 partitions the key tiles; each split keeps its own
+//     reference and a second pass merges the (reference, output, sum) triples.
+#include <type_traits>
+
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 #include "rope_device.hpp"
@@ -42,18 +48,21 @@
 namespace mla {
 
 namespace {
-constexpr int kWaves = 4;
 constexpr int kMaxSlots = 64;
 constexpr float kSumLimit = 1.2676506e30f;  // 2^100
 }  // namespace
 
-// bf16: 64-key tiles and 64 rows per wave; float operands are twice as wide,
-// so float uses 32-key tiles and 32 rows per wave to stay inside LDS and the
-// register file.
+// bf16: 8 waves x 32 rows (two waves per SIMD) and 64-key tiles; float
+// operands are twice as wide, so float runs 4 waves x 32 rows with 32-key
+// tiles (it exists for the fp32 configurations, where precision rather than
+// speed is the point).
 template <typename T, int DC, int DR>
 struct FlashTile {
-  static constexpr int kBN = sizeof(T) == 2 ? 64 : 32;  // keys per tile
-  static constexpr int kNMB = sizeof(T) == 2 ? 4 : 2;   // 16-row blocks per wave
+  static constexpr bool kBf16 = sizeof(T) == 2;
+  static constexpr int kWaves = kBf16 ? 8 : 4;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kBN = kBf16 ? 64 : 32;           // keys per tile
+  static constexpr int kNMB = 2;                        // 16-row blocks per wave
   static constexpr int kRowsWave = kNMB * 16;
   static constexpr int kRowsBlock = kWaves * kRowsWave;
   static constexpr int NKC2 = kBN / 32;                 // 32-key halves per tile
@@ -62,14 +71,17 @@ struct FlashTile {
   static constexpr int NKC = KP / 32;
   static constexpr int NDB = DC / 16;
   static constexpr int CB = 16 / sizeof(T);             // elements per 16-byte chunk
-  static constexpr int LS = KP + CB;                    // LDS row stride (elements), one pad chunk
+  static constexpr int LS = kBf16 ? KP + 16 : KP + CB;  // LDS row stride (elements)
   static constexpr int CPR = LS / CB;                   // 16-byte chunks per LDS row
   static constexpr int CC = DC / CB;                    // latent chunks per key
   static constexpr int RC = DR / CB;                    // kR chunks per key
+  static constexpr int PADC = (KP - DK) / CB;           // zero chunks read by QK
   static constexpr int TILE_CHUNKS = kBN * CPR;
   static constexpr int N_INSTR = (TILE_CHUNKS + 63) / 64;  // direct-load instructions per tile
   static constexpr int N_INSTR_WAVE = (N_INSTR + kWaves - 1) / kWaves;
   static constexpr int TILE_ELEMS = N_INSTR * 64 * CB;  // LDS elements per buffer (whole instructions)
+  static_assert(kBN * RC <= kThreads, "one kR chunk per thread");
+  static_assert(LS % 4 == 0 && (LS * sizeof(T)) % 16 == 0, "LDS rows must stay 16-byte aligned");
 };
 
 // Clears the count of rows handed to the exact fallback.
@@ -77,10 +89,10 @@ __global__ void flash_prep_kernel(FlashParams p) { *p.fallback_count = 0; }
 
 // ---------------------------------------------------------------- main kernel
 template <typename T, int DC, int DR>
-__global__ __launch_bounds__(256, 1) void flash_mla_kernel(FlashParams p) {
+__global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla_kernel(FlashParams p) {
   typedef FlashTile<T, DC, DR> F;
   typedef typename V8<T>::type v8;
-  constexpr int kBN = F::kBN, kNMB = F::kNMB;
+  constexpr int kBN = F::kBN, kNMB = F::kNMB, kWaves = F::kWaves;
   __shared__ __attribute__((aligned(16))) T kv[2][F::TILE_ELEMS];
   __shared__ int slot_of[kMaxSlots];
   __shared__ int frame_of[kMaxSlots];
@@ -123,17 +135,16 @@ __global__ __launch_bounds__(256, 1) void flash_mla_kernel(FlashParams p) {
         qf[mb][kc] = row < p.Mb ? load8<T>(qb + (size_t)row * F::KP + kc * 32 + lg * 8) : zero8<T>();
     }
   }
-  float ref[kNMB];  // reference (times c) of the row of this lane in each row block
-  bool have_ref = false;
-
+  f32x4 negref[kNMB];  // -reference of this lane's row, in every element
   f32x4 o[F::NDB][kNMB];
+  float l_run[kNMB];   // this lane's share of the row's probability sum
 #pragma unroll
-  for (int db = 0; db < F::NDB; ++db)
+  for (int mb = 0; mb < kNMB; ++mb) {
+    negref[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_run[mb] = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < kNMB; ++mb) o[db][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float l_run[kNMB];
-#pragma unroll
-  for (int mb = 0; mb < kNMB; ++mb) l_run[mb] = 0.f;
+    for (int db = 0; db < F::NDB; ++db) o[db][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const T* cache_b = (const T*)p.cache + (size_t)b * p.W * p.T * F::DK;
 
@@ -152,7 +163,7 @@ __global__ __launch_bounds__(256, 1) void flash_mla_kernel(FlashParams p) {
   };
 
   // ---- latent part: global -> LDS, lane order = LDS order (no registers).
-  // Instruction k of this wave covers LDS chunks [64 i, 64 i + 64), i = wave + 4k;
+  // Instruction k of this wave covers LDS chunks [64 i, 64 i + 64), i = wave + kWaves k;
   // the key and chunk of each lane's slot do not depend on the tile.
   int lat_key[F::N_INSTR_WAVE];
   int lat_off[F::N_INSTR_WAVE];  // element offset inside the key row, -1 = not a latent chunk
@@ -218,21 +229,78 @@ __global__ __launch_bounds__(256, 1) void flash_mla_kernel(FlashParams p) {
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) out[k] = __builtin_bit_cast(uint32_t, f[k]);
+        for (int k = 0; k < 4; ++k) out[k] = __float_as_uint(f[k]);
       }
       *reinterpret_cast<u32x4*>(buf + (r_key * F::CPR + F::CC + r_chunk) * F::CB) = out;
     }
   };
 
   // zero the padding chunks of both buffers once (they are never written again)
-  if constexpr (F::KP > F::DK) {
-    constexpr int PADC = (F::KP - F::DK) / F::CB;
-    for (int e = tid; e < 2 * kBN * PADC; e += 256) {
-      const int buf = e / (kBN * PADC), q = e % (kBN * PADC);
+  if constexpr (F::PADC > 0) {
+    for (int e = tid; e < 2 * kBN * F::PADC; e += F::kThreads) {
+      const int buf = e / (kBN * F::PADC), q = e % (kBN * F::PADC);
       const u32x4 z = {};
-      *reinterpret_cast<u32x4*>(&kv[buf][((q / PADC) * F::CPR + F::CC + F::RC + q % PADC) * F::CB]) = z;
+      *reinterpret_cast<u32x4*>(&kv[buf][((q / F::PADC) * F::CPR + F::CC + F::RC + q % F::PADC) * F::CB]) = z;
     }
   }
+
+  // ---- one 32-key half of a tile; RAGGED: keys at or past n_keys get
+  // probability 0 (only the last tile of the window can be ragged)
+  auto half_step = [&](const T* kt, int half, int kbase, auto ragged_c) {
+    constexpr bool RAGGED = decltype(ragged_c)::value;
+    f32x4 s[2][kNMB];
+#pragma unroll
+    for (int kc = 0; kc < F::NKC; ++kc) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const v8 a = lds_load8<T>(kt + ((half * 2 + kb) * 16 + li) * F::LS + kc * 32 + lg * 8);
+#pragma unroll
+        for (int mb = 0; mb < kNMB; ++mb) s[kb][mb] = mma16(a, qf[mb][kc], kc == 0 ? negref[mb] : s[kb][mb]);
+      }
+    }
+    v8 pb[kNMB];
+#pragma unroll
+    for (int mb = 0; mb < kNMB; ++mb) {
+      float f8[8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float e = fast_exp2(s[kb][mb][i]);
+          if constexpr (RAGGED) e = kbase + (half * 2 + kb) * 16 + lg * 4 + i < n_keys ? e : 0.f;
+          f8[kb * 4 + i] = e;
+          l_run[mb] += e;
+        }
+      pb[mb] = pack8<T>(f8);
+    }
+    // O^T[d][row] += C^T[d][key] P^T[key][row]; key slot j of lane group g
+    // is key 4g+j (j < 4) or 16+4g+(j-4) of this half, matching S^T's layout
+#pragma unroll
+    for (int db = 0; db < F::NDB; ++db) {
+      const v8 a = lds_tr8(kt, F::LS, half * 32 + lg * 4, half * 32 + 16 + lg * 4, db * 16);
+#pragma unroll
+      for (int mb = 0; mb < kNMB; ++mb) o[db][mb] = mma16(a, pb[mb], o[db][mb]);
+    }
+  };
+
+  // ---- one tile: start the loads of tile+1 (descriptors ready), describe
+  // tile+2, consume the tile, stash the kR part of tile+1, wait for its
+  // latent loads, barrier
+  auto tile_step = [&](int tile, auto ragged_c) {
+    const int cur = (tile - tile_begin) & 1;
+    const bool has_next = tile + 1 < tile_end;
+    if (has_next) {
+      issue_latent(keytab[cur ^ 1], kv[cur ^ 1]);
+      fetch_rope(keytab[cur ^ 1]);
+    }
+    if (tile + 2 < tile_end) describe(tile + 2, keytab[cur]);
+    const T* kt = kv[cur];
+#pragma unroll 1
+    for (int half = 0; half < F::NKC2; ++half) half_step(kt, half, tile * kBN, ragged_c);
+    if (has_next) stash_rope(kv[cur ^ 1]);
+    __builtin_amdgcn_s_waitcnt(0);  // latent loads of the next tile have landed
+    __syncthreads();
+  };
 
   if (tile_begin < tile_end) {
     describe(tile_begin, keytab[0]);
@@ -247,92 +315,40 @@ __global__ __launch_bounds__(256, 1) void flash_mla_kernel(FlashParams p) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // Iteration of tile j: start the loads of tile j+1 (descriptors ready),
-  // describe tile j+2, consume tile j, stash the kR part of tile j+1, wait for
-  // its latent loads, barrier.
-  for (int tile = tile_begin; tile < tile_end; ++tile) {
-    const int cur = (tile - tile_begin) & 1;
-    const bool has_next = tile + 1 < tile_end;
-    if (has_next) {
-      issue_latent(keytab[cur ^ 1], kv[cur ^ 1]);
-      fetch_rope(keytab[cur ^ 1]);
+  // reference: exact maximum of each row's scores over the first 32 keys
+  if (tile_begin < tile_end) {
+    const T* kt = kv[0];
+    const int kbase = tile_begin * kBN;
+    f32x4 s[2][kNMB];
+#pragma unroll
+    for (int kc = 0; kc < F::NKC; ++kc) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const v8 a = lds_load8<T>(kt + (kb * 16 + li) * F::LS + kc * 32 + lg * 8);
+#pragma unroll
+        for (int mb = 0; mb < kNMB; ++mb)
+          s[kb][mb] = mma16(a, qf[mb][kc], kc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kb][mb]);
+      }
     }
-    if (tile + 2 < tile_end) describe(tile + 2, keytab[cur]);
-    const T* kt = kv[cur];
-    const int kbase = tile * kBN;
-    const bool ragged = kbase + kBN > n_keys;
-
-#pragma unroll 1
-    for (int half = 0; half < F::NKC2; ++half) {
-      // S^T[key][row] for 2 key blocks x kNMB row blocks
-      f32x4 s[2][kNMB];
+#pragma unroll
+    for (int mb = 0; mb < kNMB; ++mb) {
+      float mx = -__builtin_inff();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int mb = 0; mb < kNMB; ++mb) s[kb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < F::NKC; ++kc) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const v8 a = lds_load8<T>(kt + ((half * 2 + kb) * 16 + li) * F::LS + kc * 32 + lg * 8);
-#pragma unroll
-          for (int mb = 0; mb < kNMB; ++mb) s[kb][mb] = mma16(a, qf[mb][kc], s[kb][mb]);
-        }
-      }
-
-      if (ragged) {  // keys past the window end (last tile only)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (kbase + (half * 2 + kb) * 16 + lg * 4 + i >= n_keys) {
-#pragma unroll
-              for (int mb = 0; mb < kNMB; ++mb) s[kb][mb][i] = -__builtin_inff();
-            }
-      }
-      if (!have_ref) {  // first 32 keys: the exact row maximum becomes the reference
-#pragma unroll
-        for (int mb = 0; mb < kNMB; ++mb) {
-          float mx = s[0][mb][0];
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][mb][i]);
-          ref[mb] = wave_max_across_groups(mx) * p.scale_log2;
-        }
-        have_ref = true;
-      }
-
-      // probabilities against the fixed reference -> B operand of PV
-      v8 pb[kNMB];
-#pragma unroll
-      for (int mb = 0; mb < kNMB; ++mb) {
-        float f8[8];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float e = fast_exp2(s[kb][mb][i] * p.scale_log2 - ref[mb]);
-            f8[kb * 4 + i] = e;
-            l_run[mb] += e;
-          }
-        pb[mb] = pack8<T>(f8);
-      }
-
-      // O^T[d][row] += C^T[d][key] P^T[key][row]; key slot j of lane group g
-      // is key 4g+j (j < 4) or 16+4g+(j-4) of this half, matching S^T's layout
-#pragma unroll
-      for (int db = 0; db < F::NDB; ++db) {
-        const v8 a = lds_tr8(kt, F::LS, half * 32 + lg * 4, half * 32 + 16 + lg * 4, db * 16);
-#pragma unroll
-        for (int mb = 0; mb < kNMB; ++mb) o[db][mb] = mma16(a, pb[mb], o[db][mb]);
-      }
+        for (int i = 0; i < 4; ++i)
+          if (kbase + kb * 16 + lg * 4 + i < n_keys) mx = fmaxf(mx, s[kb][mb][i]);
+      mx = wave_max_across_groups(mx);
+      negref[mb] = f32x4{-mx, -mx, -mx, -mx};
     }
-
-    if (has_next) stash_rope(kv[cur ^ 1]);
-    __builtin_amdgcn_s_waitcnt(0);  // latent loads of the next tile have landed
-    __syncthreads();
   }
+
+  // full tiles, then a ragged last tile with its own (masking) instantiation,
+  // so the steady-state body carries no data-dependent branches
+  const bool ragged_last = tile_begin < tile_end && tile_end * kBN > n_keys;
+  const int full_end = ragged_last ? tile_end - 1 : tile_end;
+  for (int tile = tile_begin; tile < full_end; ++tile) tile_step(tile, std::integral_constant<bool, false>());
+  if (ragged_last) tile_step(tile_end - 1, std::integral_constant<bool, true>());
 
   // ---- epilogue
 #pragma unroll
@@ -355,7 +371,8 @@ __global__ __launch_bounds__(256, 1) void flash_mla_kernel(FlashParams p) {
 #pragma unroll
       for (int db = 0; db < F::NDB; ++db) *reinterpret_cast<f32x4*>(dst + db * 16 + lg * 4) = o[db][mb];
       if (lg == 0) {
-        p.part_l[prow * 2] = have_ref ? ref[mb] : -__builtin_inff();  // empty split: no keys, weight 0
+        const bool empty = tile_begin >= tile_end;  // no keys: weight 0 in the merge
+        p.part_l[prow * 2] = empty ? -__builtin_inff() : -negref[mb][0];
         p.part_l[prow * 2 + 1] = l;
       }
     }
@@ -461,7 +478,7 @@ __global__ __launch_bounds__(256) void flash_exact_kernel(FlashParams p) {
     float acc = 0.f, lsum = 0.f;
     for (int v0 = 0; v0 < n_keys; v0 += CHUNK) {
       const int v = v0 + tid;
-      pr[tid] = v < n_keys ? fast_exp2((score(v) - m) * p.scale_log2) : 0.f;
+      pr[tid] = v < n_keys ? fast_exp2(score(v) - m) : 0.f;  // scores are log2-scaled
       __syncthreads();
       if (tid < DC) {
         const int nv = min(CHUNK, n_keys - v0);
@@ -487,7 +504,7 @@ static hipError_t launch_flash_t(const FlashParams& p, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   dim3 grid((p.Mb + F::kRowsBlock - 1) / F::kRowsBlock, p.splits, p.batch);
-  hipLaunchKernelGGL((flash_mla_kernel<T, DC, DR>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((flash_mla_kernel<T, DC, DR>), grid, dim3(F::kThreads), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (p.splits > 1) {
     const long long total = (long long)p.batch * p.Mb * (DC / 4);

@@ -136,6 +136,7 @@ mla_status do_absorb(const mla_shape* s, const void* q_nope, const void* q_r, in
   p.T = (int)tokens_per_frame(s);
   p.grid_x = s->grid_x;
   p.q_frame_first = q_frame_first;
+  p.qscale = scale_log2(s);
   return from_hip(mla::launch_absorb_q(s->dtype, s->d_c, s->d_rope, p, st));
 }
 

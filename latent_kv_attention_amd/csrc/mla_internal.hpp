@@ -42,6 +42,7 @@ struct AbsorbParams {
   RopeLayout rl;
   int rows;            // B * Nq
   int n_q, H, d_head, T, grid_x, q_frame_first;
+  float qscale;        // softmax scale * log2(e)
 };
 
 struct FlashParams {

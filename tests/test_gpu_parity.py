@@ -118,13 +118,19 @@ def test_absorb_q(name):
                  0, 16, out)
     _sync()
     t, y, x = O.frame_positions(qf + np.arange(cfg.chunk_frames), cfg.grid_y, cfg.grid_x)
-    ref = O.absorbed_query(qn, qr, w["w_uk"], t, y, x, cfg.rope_split, cfg.rope_base)
+    ref = O.absorbed_query(qn, qr, w["w_uk"], t, y, x, cfg.rope_split, cfg.rope_base) * _qscale(cfg)
     got = to_numpy(out)
     assert_rounded_close(got[..., :cfg.d_c + cfg.d_rope], ref, cfg.dtype, abs_=2e-5, label=f"{name} q_abs")
     assert not got[..., cfg.d_c + cfg.d_rope:].any()
 
 
 # ------------------------------------------------------------------ a4 latent flash attention
+
+def _qscale(cfg):
+    """The absorbed query carries the softmax temperature in log2 units,
+    scale * log2(e), as the float the library computes."""
+    return float(np.float32(O.default_scale(cfg.d_head, cfg.d_rope) * np.log2(np.e)))
+
 
 def _flash_inputs(cfg, seed, fill_frames, q_frame, q_scale=1.0):
     """Oracle-made, storage-rounded inputs of the flash step: cache rows,
@@ -142,13 +148,16 @@ def _flash_inputs(cfg, seed, fill_frames, q_frame, q_scale=1.0):
         slot_frame[f % W] = f
     qn, qr = st.q(q_frame, q_scale=q_scale)
     t, y, x = O.frame_positions(q_frame + np.arange(cfg.chunk_frames), cfg.grid_y, cfg.grid_x)
-    q_abs = round_to(O.absorbed_query(qn, qr, wts["w_uk"], t, y, x, cfg.rope_split, cfg.rope_base), cfg.dtype)
+    # the absorbed query carries scale * log2(e); with it, exp(ln2 * s') is the
+    # softmax weight, so the oracle runs at temperature ln 2 on the same values
+    q_abs = round_to(O.absorbed_query(qn, qr, wts["w_uk"], t, y, x, cfg.rope_split, cfg.rope_base) * _qscale(cfg),
+                     cfg.dtype)
     valid = [s_ for s_ in range(W) if slot_frame[s_] >= 0]
     c_all = cache[valid, :, :cfg.d_c].reshape(-1, cfg.d_c)
     kr_all = cache[valid, :, cfg.d_c:].reshape(-1, cfg.d_rope)
     tk, yk, xk = O.frame_positions(slot_frame[valid], cfg.grid_y, cfg.grid_x)
     k_rope = O.rope3d(kr_all, tk, yk, xk, cfg.rope_split, cfg.rope_base)
-    ref = O.attend_latent(q_abs, c_all, k_rope, O.default_scale(cfg.d_head, cfg.d_rope))
+    ref = O.attend_latent(q_abs, c_all, k_rope, float(np.log(2.0)))
     return cache, slot_frame, q_abs, ref
 
 
