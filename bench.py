@@ -108,7 +108,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--kv-splits", type=int, default=0, help="flash key-range splits (0 = automatic)")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2340)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4680)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-buffers", type=int, default=40,
                     help="rotating x buffers for the cold-cache cache-write measurement (0 = skip)")
