@@ -39,7 +39,11 @@
  *     this boundary.
  *   - Supported latent widths (d_c, d_rope): (192, 32) and (16, 8), either
  *     dtype. d_head must be a multiple of 8 and at most 256; hidden a
- *     multiple of 8; window_frames at most 64; each RoPE axis width even.
+ *     multiple of 8; window_frames at most 64; each RoPE axis width even;
+ *     window_frames * grid_y * grid_x at most 2^22 keys; and
+ *     window_frames * d_rope_t/2 + grid_y * d_rope_y/2 + grid_x * d_rope_x/2
+ *     at most 2048 (RoPE rows of one window held on chip). Shapes outside
+ *     these limits return MLA_ERR_SHAPE.
  *
  * Token positions: a frame has grid_y * grid_x tokens in row-major order;
  * token k of frame f sits at (t, y, x) = (f, k / grid_x, k % grid_x).

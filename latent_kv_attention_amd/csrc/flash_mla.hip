@@ -80,7 +80,10 @@ struct FlashTile {
   static constexpr int N_INSTR = (TILE_CHUNKS + 63) / 64;  // direct-load instructions per tile
   static constexpr int N_INSTR_WAVE = (N_INSTR + kWaves - 1) / kWaves;
   static constexpr int TILE_ELEMS = N_INSTR * 64 * CB;  // LDS elements per buffer (whole instructions)
-  static_assert(kBN * RC <= kThreads, "one kR chunk per thread");
+  static constexpr int RU = 4;                          // kR elements rotated per thread (two pairs)
+  static constexpr int NU = DR / RU;                    // rotation units per key
+  static constexpr int RCH = kBN * NU;                  // rotation units per tile
+  static_assert(DR % RU == 0 && RCH <= kThreads, "one rotation unit per thread");
   static_assert(LS % 4 == 0 && (LS * sizeof(T)) % 16 == 0, "LDS rows must stay 16-byte aligned");
 };
 
@@ -93,11 +96,17 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
   typedef FlashTile<T, DC, DR> F;
   typedef typename V8<T>::type v8;
   constexpr int kBN = F::kBN, kNMB = F::kNMB, kWaves = F::kWaves;
-  __shared__ __attribute__((aligned(16))) T kv[2][F::TILE_ELEMS];
+  // Two separately declared buffers (not one 2-D array): with the parity of
+  // every access known at compile time, the compiler can tell that reads of
+  // one buffer do not depend on the direct global->LDS loads into the other,
+  // and does not wait for the prefetch before consuming the current tile.
+  __shared__ __attribute__((aligned(16))) T kv0[F::TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) T kv1[F::TILE_ELEMS];
   __shared__ int slot_of[kMaxSlots];
   __shared__ int frame_of[kMaxSlots];
   __shared__ int n_valid_sh;
-  __shared__ int4 keytab[2][kBN];
+  __shared__ int4 keytab[2][kBN];     // per key of a tile: {row offset, slot rank, y, x}
+  __shared__ f32x2 rcs[kRopeLdsEntries];  // (cos, sin): t rows by slot rank, then y rows, then x rows
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -117,11 +126,34 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
   }
   __syncthreads();
 
+  // (cos, sin) of every rotary pair the window's keys need, from the global
+  // tables: t by slot rank (frames clamped into the table range), y, x
+  const int pt = p.rl.d_t / 2, py = p.rl.d_y / 2, px = p.rl.d_x / 2;
+  const int y_base = n_valid_sh * pt, x_base = y_base + p.grid_y * py;
+  for (int e = tid; e < x_base + p.grid_x * px; e += F::kThreads) {
+    int oc, os;
+    if (e < y_base) {
+      const int r = e / pt, j = e - r * pt;
+      int tt = frame_of[r] - p.rl.t_first;
+      tt = tt < 0 ? 0 : (tt >= p.rl.n_t ? p.rl.n_t - 1 : tt);
+      oc = p.rl.off_ct + tt * pt + j;
+      os = p.rl.off_st + tt * pt + j;
+    } else if (e < x_base) {
+      oc = p.rl.off_cy + e - y_base;
+      os = p.rl.off_sy + e - y_base;
+    } else {
+      oc = p.rl.off_cx + e - x_base;
+      os = p.rl.off_sx + e - x_base;
+    }
+    rcs[e] = f32x2{p.tables[oc], p.tables[os]};
+  }
+
   const int n_keys = n_valid_sh * p.T;
   const int n_tiles = (n_keys + kBN - 1) / kBN;
   const int tiles_per_split = (n_tiles + p.splits - 1) / p.splits;
   const int tile_begin = split * tiles_per_split;
   const int tile_end = min(n_tiles, tile_begin + tiles_per_split);
+  const int n_visit = max(0, tile_end - tile_begin);
 
   // queries of this wave (B operand of S^T = K Q^T), kept in registers
   v8 qf[kNMB][F::NKC];
@@ -148,17 +180,23 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
 
   const T* cache_b = (const T*)p.cache + (size_t)b * p.W * p.T * F::DK;
 
-  // Per-tile key descriptors {row offset, t, y, x}, written one tile ahead by
-  // wave 0 into a ping-pong table, so the address of every load below is one
-  // LDS read plus an add. Keys past the end of the window alias the last key
-  // (their probabilities are forced to 0).
-  auto describe = [&](int tile, int4* tab) {
+  // Per-tile key descriptors {row offset, slot rank, y, x}, written one tile
+  // ahead by wave 0 into a ping-pong table, so the address of every load
+  // below is one LDS read plus an add. Keys past the end of the window alias
+  // the last key (their probabilities are forced to 0). Quotients come from a
+  // float reciprocal, exact after one correction for indices below 2^22.
+  auto div_floor = [](int a, int d, float inv_d) {
+    int q = (int)((float)a * inv_d);
+    const int r = a - q * d;
+    return q + (r >= d ? 1 : 0) - (r < 0 ? 1 : 0);
+  };
+  auto describe = [&](int pos, int4* tab) {
     if (wave == 0) {
+      const int tile = pos == 0 ? tile_end - 1 : tile_begin + pos - 1;
       const int v = min(tile * kBN + lane, n_keys - 1);
-      const int rank = v / p.T, tok = v - rank * p.T;
-      const int y = tok / p.grid_x;
-      if (lane < kBN)
-        tab[lane] = int4{(slot_of[rank] * p.T + tok) * F::DK, frame_of[rank], y, tok - y * p.grid_x};
+      const int rank = div_floor(v, p.T, p.inv_T), tok = v - rank * p.T;
+      const int y = div_floor(tok, p.grid_x, p.inv_grid_x);
+      if (lane < kBN) tab[lane] = int4{(slot_of[rank] * p.T + tok) * F::DK, rank, y, tok - y * p.grid_x};
     }
   };
 
@@ -177,52 +215,55 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     lat_off[k] = ok ? c * F::CB : -1;
   }
   auto issue_latent = [&](const int4* tab, T* buf) {
+    int ro[F::N_INSTR_WAVE];
+#pragma unroll
+    for (int k = 0; k < F::N_INSTR_WAVE; ++k) ro[k] = tab[lat_key[k]].x;
 #pragma unroll
     for (int k = 0; k < F::N_INSTR_WAVE; ++k) {
       const int instr = wave + kWaves * k;
       if (instr < F::N_INSTR && lat_off[k] >= 0) {
-        const T* src = cache_b + tab[lat_key[k]].x + lat_off[k];
+        const T* src = cache_b + ro[k] + lat_off[k];
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                          (MLA_LDS void*)(MLA_LDS T*)(buf + instr * 64 * F::CB), 16, 0, 0);
       }
     }
   };
 
-  // ---- kR part: one 16-byte chunk per thread via registers, rotated on store
-  constexpr int RCH = kBN * F::RC;  // kR chunks per tile
-  const bool has_r = tid < RCH;
-  const int r_key = tid / F::RC, r_chunk = tid % F::RC;
-  u32x4 st_r = {};
-  int4 st_d = {0, 0, 0, 0};
+  // ---- kR part: two rotary pairs per thread via registers, rotated with the
+  // LDS (cos, sin) rows on their way into LDS
+  typedef typename std::conditional<sizeof(T) == 2, u32x2, u32x4>::type ru_t;  // RU elements
+  const bool has_r = tid < F::RCH;
+  const int r_key = tid / F::NU, r_unit = tid % F::NU;
+  ru_t st_r = {};
   auto fetch_rope = [&](const int4* tab) {
-    if (has_r) {
-      st_d = tab[r_key];
-      st_r = *reinterpret_cast<const u32x4*>(cache_b + st_d.x + DC + r_chunk * F::CB);
-    }
+    if (has_r) st_r = *reinterpret_cast<const ru_t*>(cache_b + tab[r_key].x + DC + r_unit * F::RU);
   };
-  auto stash_rope = [&](T* buf) {
+  auto stash_rope = [&](const int4* tab, T* buf) {
     if (has_r) {
-      float f[F::CB];
+      const int4 d = tab[r_key];
+      float f[F::RU];
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          f[2 * k] = __builtin_bit_cast(float, st_r[k] << 16);
-          f[2 * k + 1] = __builtin_bit_cast(float, st_r[k] & 0xffff0000u);
+        for (int k = 0; k < 2; ++k) {
+          f[2 * k] = __uint_as_float(st_r[k] << 16);
+          f[2 * k + 1] = __uint_as_float(st_r[k] & 0xffff0000u);
         }
       } else {
 #pragma unroll
         for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(st_r[k]);
       }
 #pragma unroll
-      for (int k = 0; k < F::CB / 2; ++k) {
-        float cs, sn;
-        rope_cos_sin(p.rl, p.tables, r_chunk * (F::CB / 2) + k, st_d.y, st_d.z, st_d.w, cs, sn);
-        rotate_pair(f[2 * k], f[2 * k + 1], cs, sn);
+      for (int k = 0; k < 2; ++k) {
+        const int pr = r_unit * 2 + k;
+        const int idx = pr < pt ? d.y * pt + pr
+                                : (pr < pt + py ? y_base + d.z * py + pr - pt : x_base + d.w * px + pr - pt - py);
+        const f32x2 cs = rcs[idx];
+        rotate_pair(f[2 * k], f[2 * k + 1], cs.x, cs.y);
       }
-      u32x4 out;
+      ru_t out;
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 2; ++k) {
           const uint32_t lo = __builtin_bit_cast(uint16_t, (bf16)f[2 * k]);
           const uint32_t hi = __builtin_bit_cast(uint16_t, (bf16)f[2 * k + 1]);
           out[k] = lo | (hi << 16);
@@ -231,7 +272,7 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
 #pragma unroll
         for (int k = 0; k < 4; ++k) out[k] = __float_as_uint(f[k]);
       }
-      *reinterpret_cast<u32x4*>(buf + (r_key * F::CPR + F::CC + r_chunk) * F::CB) = out;
+      *reinterpret_cast<ru_t*>(buf + r_key * F::LS + DC + r_unit * F::RU) = out;
     }
   };
 
@@ -240,7 +281,7 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     for (int e = tid; e < 2 * kBN * F::PADC; e += F::kThreads) {
       const int buf = e / (kBN * F::PADC), q = e % (kBN * F::PADC);
       const u32x4 z = {};
-      *reinterpret_cast<u32x4*>(&kv[buf][((q / F::PADC) * F::CPR + F::CC + F::RC + q % F::PADC) * F::CB]) = z;
+      *reinterpret_cast<u32x4*>(&(buf ? kv1 : kv0)[((q / F::PADC) * F::CPR + F::CC + F::RC + q % F::PADC) * F::CB]) = z;
     }
   }
 
@@ -285,40 +326,43 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
 
   // ---- one tile: start the loads of tile+1 (descriptors ready), describe
   // tile+2, consume the tile, stash the kR part of tile+1, wait for its
-  // latent loads, barrier
-  auto tile_step = [&](int tile, auto ragged_c) {
-    const int cur = (tile - tile_begin) & 1;
-    const bool has_next = tile + 1 < tile_end;
+  // latent loads, barrier. PAR = buffer holding this tile (static).
+  auto tile_step = [&](int pos, auto par_c, auto ragged_c) {
+    constexpr int PAR = decltype(par_c)::value;
+    T* cur_buf = PAR ? kv1 : kv0;
+    T* nxt_buf = PAR ? kv0 : kv1;
+    const bool has_next = pos + 1 < n_visit;
     if (has_next) {
-      issue_latent(keytab[cur ^ 1], kv[cur ^ 1]);
-      fetch_rope(keytab[cur ^ 1]);
+      issue_latent(keytab[PAR ^ 1], nxt_buf);
+      fetch_rope(keytab[PAR ^ 1]);
     }
-    if (tile + 2 < tile_end) describe(tile + 2, keytab[cur]);
-    const T* kt = kv[cur];
+    if (pos + 2 < n_visit) describe(pos + 2, keytab[PAR]);
+    const int kbase = (pos == 0 ? tile_end - 1 : tile_begin + pos - 1) * kBN;
 #pragma unroll 1
-    for (int half = 0; half < F::NKC2; ++half) half_step(kt, half, tile * kBN, ragged_c);
-    if (has_next) stash_rope(kv[cur ^ 1]);
+    for (int half = 0; half < F::NKC2; ++half) half_step(cur_buf, half, kbase, ragged_c);
+    if (has_next) stash_rope(keytab[PAR ^ 1], nxt_buf);
     __builtin_amdgcn_s_waitcnt(0);  // latent loads of the next tile have landed
     __syncthreads();
   };
 
   if (tile_begin < tile_end) {
-    describe(tile_begin, keytab[0]);
-    if (tile_begin + 1 < tile_end) describe(tile_begin + 1, keytab[1]);
+    describe(0, keytab[0]);
+    if (n_visit > 1) describe(1, keytab[1]);
   }
   __syncthreads();
   if (tile_begin < tile_end) {
-    issue_latent(keytab[0], kv[0]);
+    issue_latent(keytab[0], kv0);
     fetch_rope(keytab[0]);
-    stash_rope(kv[0]);
+    stash_rope(keytab[0], kv0);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // reference: exact maximum of each row's scores over the first 32 keys
+  // reference: exact maximum of each row's scores over the first 32 keys it
+  // visits (the first half of position 0)
   if (tile_begin < tile_end) {
-    const T* kt = kv[0];
-    const int kbase = tile_begin * kBN;
+    const T* kt = kv0;
+    const int kbase = (tile_end - 1) * kBN;  // position 0 visits the last tile
     f32x4 s[2][kNMB];
 #pragma unroll
     for (int kc = 0; kc < F::NKC; ++kc) {
@@ -343,12 +387,21 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     }
   }
 
-  // full tiles, then a ragged last tile with its own (masking) instantiation,
-  // so the steady-state body carries no data-dependent branches
-  const bool ragged_last = tile_begin < tile_end && tile_end * kBN > n_keys;
-  const int full_end = ragged_last ? tile_end - 1 : tile_end;
-  for (int tile = tile_begin; tile < full_end; ++tile) tile_step(tile, std::integral_constant<bool, false>());
-  if (ragged_last) tile_step(tile_end - 1, std::integral_constant<bool, true>());
+  // Visit order: the (possibly ragged) last tile of the range first, with
+  // masking, then the others in order; the sum is order independent. So
+  // position 0 always uses buffer 0 and the masking variant, and the loop
+  // body holds one static-parity step per buffer.
+  typedef std::integral_constant<int, 0> P0;
+  typedef std::integral_constant<int, 1> P1;
+  typedef std::integral_constant<bool, false> Full;
+  typedef std::integral_constant<bool, true> Ragged;
+  if (n_visit > 0) tile_step(0, P0(), Ragged());
+  int pos = 1;
+  for (; pos + 1 < n_visit; pos += 2) {
+    tile_step(pos, P1(), Full());
+    tile_step(pos + 1, P0(), Full());
+  }
+  if (pos < n_visit) tile_step(pos, P1(), Full());
 
   // ---- epilogue
 #pragma unroll

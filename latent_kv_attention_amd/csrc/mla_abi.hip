@@ -41,6 +41,12 @@ mla_status check_shape(const mla_shape* s) {
   // per-stream cache element offsets are 32-bit inside the kernels
   if (T * s->window_frames * (s->d_c + s->d_rope) > INT32_MAX) return MLA_ERR_SHAPE;
   if ((int64_t)s->batch * s->window_frames * T * (s->d_c + s->d_rope) > INT64_C(1) << 40) return MLA_ERR_SHAPE;
+  // the attention kernel splits key indices with a float reciprocal (exact
+  // below 2^22 keys per window) and keeps the window's RoPE rows in LDS
+  if (T * s->window_frames > mla::kMaxWindowKeys) return MLA_ERR_SHAPE;
+  if ((int64_t)s->window_frames * (s->d_rope_t / 2) + (int64_t)s->grid_y * (s->d_rope_y / 2) +
+          (int64_t)s->grid_x * (s->d_rope_x / 2) > mla::kRopeLdsEntries)
+    return MLA_ERR_SHAPE;
   if (!latent_supported(s->d_c, s->d_rope)) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
@@ -159,7 +165,10 @@ mla_status do_flash(const mla_shape* s, const void* q_abs, int q_n_frames, const
   p.Mb = (int)(q_n_frames * tokens_per_frame(s) * s->n_heads);
   p.W = s->window_frames;
   p.T = (int)tokens_per_frame(s);
+  p.grid_y = s->grid_y;
   p.grid_x = s->grid_x;
+  p.inv_T = 1.f / (float)p.T;
+  p.inv_grid_x = 1.f / (float)s->grid_x;
   p.batch = s->batch;
   p.splits = splits;
   p.scale_log2 = scale_log2(s);

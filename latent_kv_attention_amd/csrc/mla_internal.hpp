@@ -57,11 +57,17 @@ struct FlashParams {
   int* fallback_rows;      // [B * Mb]
   RopeLayout rl;
   int Mb;                  // Nq * H
-  int W, T, grid_x, batch, splits;
+  int W, T, grid_y, grid_x, batch, splits;
+  float inv_T, inv_grid_x; // 1/T and 1/grid_x (key index -> slot, row, column)
   float scale_log2;        // softmax scale * log2(e)
 };
 
 constexpr int kFallbackBlocks = 64;
+// Limits of the attention kernel: keys per window (index arithmetic in
+// float) and (cos, sin) entries of the window's RoPE rows kept in LDS
+// (window_frames * d_rope_t/2 + grid_y * d_rope_y/2 + grid_x * d_rope_x/2).
+constexpr int kMaxWindowKeys = 1 << 22;
+constexpr int kRopeLdsEntries = 2048;
 
 struct UpVParams {
   const void* o_lat;  // [B*Nq][H][d_c]
