@@ -49,6 +49,16 @@ namespace mla {
 
 namespace {
 constexpr int kMaxSlots = 64;
+
+// A copy of x that the compiler cannot see through. Per-lane addresses
+// derived from it are recomputed where they are used (a few integer
+// operations) instead of being hoisted out of the key loop and held in
+// registers across it, where they would crowd out the loop's own operands.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 constexpr float kSumLimit = 1.2676506e30f;  // 2^100
 }  // namespace
 
@@ -80,10 +90,14 @@ struct FlashTile {
   static constexpr int N_INSTR = (TILE_CHUNKS + 63) / 64;  // direct-load instructions per tile
   static constexpr int N_INSTR_WAVE = (N_INSTR + kWaves - 1) / kWaves;
   static constexpr int TILE_ELEMS = N_INSTR * 64 * CB;  // LDS elements per buffer (whole instructions)
-  static constexpr int RU = 4;                          // kR elements rotated per thread (two pairs)
+  // kR rotation: RP pairs (RU elements) per thread, at most one unit per thread
+  static constexpr int RP0 = kBN * DR / 2 / kThreads;
+  static constexpr int RP = RP0 < 1 ? 1 : RP0;
+  static constexpr int RU = 2 * RP;                     // kR elements rotated per thread
   static constexpr int NU = DR / RU;                    // rotation units per key
   static constexpr int RCH = kBN * NU;                  // rotation units per tile
-  static_assert(DR % RU == 0 && RCH <= kThreads, "one rotation unit per thread");
+  static constexpr int RW = RU * (int)sizeof(T) / 4;    // 32-bit words per unit
+  static_assert(DR % RU == 0 && RCH <= kThreads && (RW == 1 || RW == 2 || RW == 4), "one rotation unit per thread");
   static_assert(LS % 4 == 0 && (LS * sizeof(T)) % 16 == 0, "LDS rows must stay 16-byte aligned");
 };
 
@@ -95,346 +109,392 @@ template <typename T, int DC, int DR>
 __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla_kernel(FlashParams p) {
   typedef FlashTile<T, DC, DR> F;
   typedef typename V8<T>::type v8;
-  constexpr int kBN = F::kBN, kNMB = F::kNMB, kWaves = F::kWaves;
-  // Two separately declared buffers (not one 2-D array): with the parity of
-  // every access known at compile time, the compiler can tell that reads of
-  // one buffer do not depend on the direct global->LDS loads into the other,
-  // and does not wait for the prefetch before consuming the current tile.
+  constexpr int kBN = F::kBN, kNMB = F::kNMB, kWaves = F::kWaves, NKC2 = F::NKC2;
+  // Two separately declared tile buffers (not one 2-D array). Position p of
+  // the key loop uses buffer p mod 2 and the loop is unrolled twice, so every
+  // buffer access has a compile-time buffer: the compiler can then tell that
+  // reads of the current tile do not depend on the direct global->LDS loads
+  // into the other buffer, and does not wait for the prefetch before reading.
   __shared__ __attribute__((aligned(16))) T kv0[F::TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) T kv1[F::TILE_ELEMS];
   __shared__ int slot_of[kMaxSlots];
   __shared__ int frame_of[kMaxSlots];
   __shared__ int n_valid_sh;
-  __shared__ int4 keytab[2][kBN];     // per key of a tile: {row offset, slot rank, y, x}
+  __shared__ int4 keytab[2][kBN];         // per key of a tile: {row byte offset, slot rank, y, x}
   __shared__ f32x2 rcs[kRopeLdsEntries];  // (cos, sin): t rows by slot rank, then y rows, then x rows
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
-  const int b = blockIdx.z, split = blockIdx.y;
-  const int row_wave = blockIdx.x * F::kRowsBlock + wave * F::kRowsWave;
 
-  // valid ring slots of stream b in slot order
-  if (wave == 0) {
-    const int f = lane < p.W ? p.slot_frame[b * p.W + lane] : -1;
-    const unsigned long long mask = __ballot(f >= 0);
-    if (f >= 0) {
-      const int rank = __popcll(mask & ((1ull << lane) - 1ull));
-      slot_of[rank] = lane;
-      frame_of[rank] = f;
-    }
-    if (lane == 0) n_valid_sh = __popcll(mask);
-  }
-  __syncthreads();
-
-  // (cos, sin) of every rotary pair the window's keys need, from the global
-  // tables: t by slot rank (frames clamped into the table range), y, x
-  const int pt = p.rl.d_t / 2, py = p.rl.d_y / 2, px = p.rl.d_x / 2;
-  const int y_base = n_valid_sh * pt, x_base = y_base + p.grid_y * py;
-  for (int e = tid; e < x_base + p.grid_x * px; e += F::kThreads) {
-    int oc, os;
-    if (e < y_base) {
-      const int r = e / pt, j = e - r * pt;
-      int tt = frame_of[r] - p.rl.t_first;
-      tt = tt < 0 ? 0 : (tt >= p.rl.n_t ? p.rl.n_t - 1 : tt);
-      oc = p.rl.off_ct + tt * pt + j;
-      os = p.rl.off_st + tt * pt + j;
-    } else if (e < x_base) {
-      oc = p.rl.off_cy + e - y_base;
-      os = p.rl.off_sy + e - y_base;
-    } else {
-      oc = p.rl.off_cx + e - x_base;
-      os = p.rl.off_sx + e - x_base;
-    }
-    rcs[e] = f32x2{p.tables[oc], p.tables[os]};
-  }
-
-  const int n_keys = n_valid_sh * p.T;
-  const int n_tiles = (n_keys + kBN - 1) / kBN;
-  const int tiles_per_split = (n_tiles + p.splits - 1) / p.splits;
-  const int tile_begin = split * tiles_per_split;
-  const int tile_end = min(n_tiles, tile_begin + tiles_per_split);
-  const int n_visit = max(0, tile_end - tile_begin);
-
-  // queries of this wave (B operand of S^T = K Q^T), kept in registers
-  v8 qf[kNMB][F::NKC];
-  {
-    const T* qb = (const T*)p.q_abs + (size_t)b * p.Mb * F::KP;
-#pragma unroll
-    for (int mb = 0; mb < kNMB; ++mb) {
-      const int row = row_wave + mb * 16 + li;
-#pragma unroll
-      for (int kc = 0; kc < F::NKC; ++kc)
-        qf[mb][kc] = row < p.Mb ? load8<T>(qb + (size_t)row * F::KP + kc * 32 + lg * 8) : zero8<T>();
-    }
-  }
-  f32x4 negref[kNMB];  // -reference of this lane's row, in every element
-  f32x4 o[F::NDB][kNMB];
-  float l_run[kNMB];   // this lane's share of the row's probability sum
-#pragma unroll
-  for (int mb = 0; mb < kNMB; ++mb) {
-    negref[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    l_run[mb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < F::NDB; ++db) o[db][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const T* cache_b = (const T*)p.cache + (size_t)b * p.W * p.T * F::DK;
-
-  // Per-tile key descriptors {row offset, slot rank, y, x}, written one tile
-  // ahead by wave 0 into a ping-pong table, so the address of every load
-  // below is one LDS read plus an add. Keys past the end of the window alias
-  // the last key (their probabilities are forced to 0). Quotients come from a
-  // float reciprocal, exact after one correction for indices below 2^22.
-  auto div_floor = [](int a, int d, float inv_d) {
-    int q = (int)((float)a * inv_d);
-    const int r = a - q * d;
-    return q + (r >= d ? 1 : 0) - (r < 0 ? 1 : 0);
-  };
-  auto describe = [&](int pos, int4* tab) {
-    if (wave == 0) {
-      const int tile = pos == 0 ? tile_end - 1 : tile_begin + pos - 1;
-      const int v = min(tile * kBN + lane, n_keys - 1);
-      const int rank = div_floor(v, p.T, p.inv_T), tok = v - rank * p.T;
-      const int y = div_floor(tok, p.grid_x, p.inv_grid_x);
-      if (lane < kBN) tab[lane] = int4{(slot_of[rank] * p.T + tok) * F::DK, rank, y, tok - y * p.grid_x};
-    }
-  };
-
-  // ---- latent part: global -> LDS, lane order = LDS order (no registers).
-  // Instruction k of this wave covers LDS chunks [64 i, 64 i + 64), i = wave + kWaves k;
-  // the key and chunk of each lane's slot do not depend on the tile.
-  int lat_key[F::N_INSTR_WAVE];
-  int lat_off[F::N_INSTR_WAVE];  // element offset inside the key row, -1 = not a latent chunk
+  // Direct-load slots of this lane: instruction k of the wave fills LDS
+  // chunks [64 i, 64 i + 64), i = wave + kWaves k; the lane's chunk is chunk
+  // c of key n. Packed as (n << 16) | (byte offset of the chunk in the key
+  // row), or -1 where the chunk is not part of the latent.
+  int lat_pk[F::N_INSTR_WAVE];
 #pragma unroll
   for (int k = 0; k < F::N_INSTR_WAVE; ++k) {
     const int instr = wave + kWaves * k;
     const int pos = instr * 64 + lane;
-    const int n = pos / F::CPR, c = pos % F::CPR;
-    const bool ok = instr < F::N_INSTR && n < kBN && c < F::CC;
-    lat_key[k] = ok ? n : 0;
-    lat_off[k] = ok ? c * F::CB : -1;
-  }
-  auto issue_latent = [&](const int4* tab, T* buf) {
-    int ro[F::N_INSTR_WAVE];
-#pragma unroll
-    for (int k = 0; k < F::N_INSTR_WAVE; ++k) ro[k] = tab[lat_key[k]].x;
-#pragma unroll
-    for (int k = 0; k < F::N_INSTR_WAVE; ++k) {
-      const int instr = wave + kWaves * k;
-      if (instr < F::N_INSTR && lat_off[k] >= 0) {
-        const T* src = cache_b + ro[k] + lat_off[k];
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                         (MLA_LDS void*)(MLA_LDS T*)(buf + instr * 64 * F::CB), 16, 0, 0);
-      }
-    }
-  };
-
-  // ---- kR part: two rotary pairs per thread via registers, rotated with the
-  // LDS (cos, sin) rows on their way into LDS
-  typedef typename std::conditional<sizeof(T) == 2, u32x2, u32x4>::type ru_t;  // RU elements
-  const bool has_r = tid < F::RCH;
-  const int r_key = tid / F::NU, r_unit = tid % F::NU;
-  ru_t st_r = {};
-  auto fetch_rope = [&](const int4* tab) {
-    if (has_r) st_r = *reinterpret_cast<const ru_t*>(cache_b + tab[r_key].x + DC + r_unit * F::RU);
-  };
-  auto stash_rope = [&](const int4* tab, T* buf) {
-    if (has_r) {
-      const int4 d = tab[r_key];
-      float f[F::RU];
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          f[2 * k] = __uint_as_float(st_r[k] << 16);
-          f[2 * k + 1] = __uint_as_float(st_r[k] & 0xffff0000u);
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(st_r[k]);
-      }
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int pr = r_unit * 2 + k;
-        const int idx = pr < pt ? d.y * pt + pr
-                                : (pr < pt + py ? y_base + d.z * py + pr - pt : x_base + d.w * px + pr - pt - py);
-        const f32x2 cs = rcs[idx];
-        rotate_pair(f[2 * k], f[2 * k + 1], cs.x, cs.y);
-      }
-      ru_t out;
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const uint32_t lo = __builtin_bit_cast(uint16_t, (bf16)f[2 * k]);
-          const uint32_t hi = __builtin_bit_cast(uint16_t, (bf16)f[2 * k + 1]);
-          out[k] = lo | (hi << 16);
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) out[k] = __float_as_uint(f[k]);
-      }
-      *reinterpret_cast<ru_t*>(buf + r_key * F::LS + DC + r_unit * F::RU) = out;
-    }
-  };
-
-  // zero the padding chunks of both buffers once (they are never written again)
-  if constexpr (F::PADC > 0) {
-    for (int e = tid; e < 2 * kBN * F::PADC; e += F::kThreads) {
-      const int buf = e / (kBN * F::PADC), q = e % (kBN * F::PADC);
-      const u32x4 z = {};
-      *reinterpret_cast<u32x4*>(&(buf ? kv1 : kv0)[((q / F::PADC) * F::CPR + F::CC + F::RC + q % F::PADC) * F::CB]) = z;
-    }
+    const int n = pos / F::CPR, c = pos - n * F::CPR;
+    lat_pk[k] = (instr < F::N_INSTR && n < kBN && c < F::CC) ? (n << 16) | (c * 16) : -1;
   }
 
-  // ---- one 32-key half of a tile; RAGGED: keys at or past n_keys get
-  // probability 0 (only the last tile of the window can be ragged)
-  auto half_step = [&](const T* kt, int half, int kbase, auto ragged_c) {
-    constexpr bool RAGGED = decltype(ragged_c)::value;
-    f32x4 s[2][kNMB];
-#pragma unroll
-    for (int kc = 0; kc < F::NKC; ++kc) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const v8 a = lds_load8<T>(kt + ((half * 2 + kb) * 16 + li) * F::LS + kc * 32 + lg * 8);
-#pragma unroll
-        for (int mb = 0; mb < kNMB; ++mb) s[kb][mb] = mma16(a, qf[mb][kc], kc == 0 ? negref[mb] : s[kb][mb]);
-      }
-    }
-    v8 pb[kNMB];
-#pragma unroll
-    for (int mb = 0; mb < kNMB; ++mb) {
-      float f8[8];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float e = fast_exp2(s[kb][mb][i]);
-          if constexpr (RAGGED) e = kbase + (half * 2 + kb) * 16 + lg * 4 + i < n_keys ? e : 0.f;
-          f8[kb * 4 + i] = e;
-          l_run[mb] += e;
-        }
-      pb[mb] = pack8<T>(f8);
-    }
-    // O^T[d][row] += C^T[d][key] P^T[key][row]; key slot j of lane group g
-    // is key 4g+j (j < 4) or 16+4g+(j-4) of this half, matching S^T's layout
-#pragma unroll
-    for (int db = 0; db < F::NDB; ++db) {
-      const v8 a = lds_tr8(kt, F::LS, half * 32 + lg * 4, half * 32 + 16 + lg * 4, db * 16);
-#pragma unroll
-      for (int mb = 0; mb < kNMB; ++mb) o[db][mb] = mma16(a, pb[mb], o[db][mb]);
-    }
-  };
+  // Work-group g takes units [g U / G, (g + 1) U / G) of the (row block, key
+  // tile) grid, as consecutive segments of at most one row block each. A
+  // segment that covers its whole row block writes the normalised output; a
+  // partial one writes (output, reference, sum) to slot 0 (the work-group's
+  // first segment) or 1 (its last) for the merge pass.
+  const long long G = p.grid;
+  const long long u_first = (long long)blockIdx.x * p.units / G;
+  const long long u_last = ((long long)blockIdx.x + 1) * p.units / G;
+  for (long long u = u_first; u < u_last;) {
+    const long long rbg = u / p.nt_max;  // row block over all streams
+    const int j0 = (int)(u - rbg * p.nt_max);
+    const int j1 = (int)min((long long)p.nt_max, j0 + (u_last - u));
+    const bool first_seg = u == u_first;
+    const bool whole = j0 == 0 && j1 == p.nt_max;
+    u += j1 - j0;
+    const int b = (int)(rbg / p.n_rb), rb = (int)(rbg - (long long)b * p.n_rb);
+    const int row_wave = rb * F::kRowsBlock + wave * F::kRowsWave;
+    __syncthreads();  // LDS of the previous segment is no longer read
 
-  // ---- one tile: start the loads of tile+1 (descriptors ready), describe
-  // tile+2, consume the tile, stash the kR part of tile+1, wait for its
-  // latent loads, barrier. PAR = buffer holding this tile (static).
-  auto tile_step = [&](int pos, auto par_c, auto ragged_c) {
-    constexpr int PAR = decltype(par_c)::value;
-    T* cur_buf = PAR ? kv1 : kv0;
-    T* nxt_buf = PAR ? kv0 : kv1;
-    const bool has_next = pos + 1 < n_visit;
-    if (has_next) {
-      issue_latent(keytab[PAR ^ 1], nxt_buf);
-      fetch_rope(keytab[PAR ^ 1]);
+    // valid ring slots of stream b in slot order
+    if (wave == 0) {
+      const int f = lane < p.W ? p.slot_frame[b * p.W + lane] : -1;
+      const unsigned long long mask = __ballot(f >= 0);
+      if (f >= 0) {
+        const int rank = __popcll(mask & ((1ull << lane) - 1ull));
+        slot_of[rank] = lane;
+        frame_of[rank] = f;
+      }
+      if (lane == 0) n_valid_sh = __popcll(mask);
     }
-    if (pos + 2 < n_visit) describe(pos + 2, keytab[PAR]);
-    const int kbase = (pos == 0 ? tile_end - 1 : tile_begin + pos - 1) * kBN;
-#pragma unroll 1
-    for (int half = 0; half < F::NKC2; ++half) half_step(cur_buf, half, kbase, ragged_c);
-    if (has_next) stash_rope(keytab[PAR ^ 1], nxt_buf);
-    __builtin_amdgcn_s_waitcnt(0);  // latent loads of the next tile have landed
     __syncthreads();
-  };
 
-  if (tile_begin < tile_end) {
-    describe(0, keytab[0]);
-    if (n_visit > 1) describe(1, keytab[1]);
-  }
-  __syncthreads();
-  if (tile_begin < tile_end) {
-    issue_latent(keytab[0], kv0);
-    fetch_rope(keytab[0]);
-    stash_rope(keytab[0], kv0);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+    // (cos, sin) of every rotary pair the window's keys need, from the global
+    // tables: t by slot rank (frames clamped into the table range), y, x
+    const int pt = p.rl.d_t / 2, py = p.rl.d_y / 2, px = p.rl.d_x / 2;
+    const int y_base = n_valid_sh * pt, x_base = y_base + p.grid_y * py;
+    for (int e = tid; e < x_base + p.grid_x * px; e += F::kThreads) {
+      int oc, os;
+      if (e < y_base) {
+        const int r = e / pt, j = e - r * pt;
+        int tt = frame_of[r] - p.rl.t_first;
+        tt = tt < 0 ? 0 : (tt >= p.rl.n_t ? p.rl.n_t - 1 : tt);
+        oc = p.rl.off_ct + tt * pt + j;
+        os = p.rl.off_st + tt * pt + j;
+      } else if (e < x_base) {
+        oc = p.rl.off_cy + e - y_base;
+        os = p.rl.off_sy + e - y_base;
+      } else {
+        oc = p.rl.off_cx + e - x_base;
+        os = p.rl.off_sx + e - x_base;
+      }
+      rcs[e] = f32x2{p.tables[oc], p.tables[os]};
+    }
 
-  // reference: exact maximum of each row's scores over the first 32 keys it
-  // visits (the first half of position 0)
-  if (tile_begin < tile_end) {
-    const T* kt = kv0;
-    const int kbase = (tile_end - 1) * kBN;  // position 0 visits the last tile
-    f32x4 s[2][kNMB];
+    const int n_keys = n_valid_sh * p.T;
+    const int n_tiles = (n_keys + kBN - 1) / kBN;
+    // this segment's share of the window's tiles (units map onto the tiles
+    // of a full window; a partly filled window scales proportionally)
+    const int tile_begin = (int)((long long)j0 * n_tiles / p.nt_max);
+    const int tile_end = (int)((long long)j1 * n_tiles / p.nt_max);
+    const int n_visit = max(0, tile_end - tile_begin);
+
+    // queries of this wave (B operand of S^T = K Q^T), kept in registers
+    v8 qf[kNMB][F::NKC];
+    {
+      const T* qb = (const T*)p.q_abs + (size_t)b * p.Mb * F::KP;
 #pragma unroll
-    for (int kc = 0; kc < F::NKC; ++kc) {
+      for (int mb = 0; mb < kNMB; ++mb) {
+        const int row = row_wave + mb * 16 + li;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const v8 a = lds_load8<T>(kt + (kb * 16 + li) * F::LS + kc * 32 + lg * 8);
-#pragma unroll
-        for (int mb = 0; mb < kNMB; ++mb)
-          s[kb][mb] = mma16(a, qf[mb][kc], kc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[kb][mb]);
+        for (int kc = 0; kc < F::NKC; ++kc)
+          qf[mb][kc] = row < p.Mb ? load8<T>(qb + (size_t)row * F::KP + kc * 32 + lg * 8) : zero8<T>();
       }
     }
+    f32x4 negref[kNMB];  // -reference of this lane's row, in every element
+    f32x4 o[F::NDB][kNMB];
+    float l_run[kNMB];   // this lane's share of the row's probability sum
 #pragma unroll
     for (int mb = 0; mb < kNMB; ++mb) {
-      float mx = -__builtin_inff();
+      negref[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      l_run[mb] = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (kbase + kb * 16 + lg * 4 + i < n_keys) mx = fmaxf(mx, s[kb][mb][i]);
-      mx = wave_max_across_groups(mx);
-      negref[mb] = f32x4{-mx, -mx, -mx, -mx};
+      for (int db = 0; db < F::NDB; ++db) o[db][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  }
 
-  // Visit order: the (possibly ragged) last tile of the range first, with
-  // masking, then the others in order; the sum is order independent. So
-  // position 0 always uses buffer 0 and the masking variant, and the loop
-  // body holds one static-parity step per buffer.
-  typedef std::integral_constant<int, 0> P0;
-  typedef std::integral_constant<int, 1> P1;
-  typedef std::integral_constant<bool, false> Full;
-  typedef std::integral_constant<bool, true> Ragged;
-  if (n_visit > 0) tile_step(0, P0(), Ragged());
-  int pos = 1;
-  for (; pos + 1 < n_visit; pos += 2) {
-    tile_step(pos, P1(), Full());
-    tile_step(pos + 1, P0(), Full());
-  }
-  if (pos < n_visit) tile_step(pos, P1(), Full());
+    // stream base (uniform); per-key byte offsets fit 32 bits because a window
+    // holds at most 2^22 keys of at most 224 elements of at most 4 bytes
+    const char* cache_b = (const char*)p.cache + (size_t)b * p.W * p.T * F::DK * sizeof(T);
 
-  // ---- epilogue
+    // Per-tile key descriptors {row byte offset, slot rank, y, x}, written one
+    // tile ahead by wave 0 into a ping-pong table, so the address of
+    // every load below is one LDS read plus an add. Keys past the end of the
+    // window alias the last key (their scores are masked). Quotients come
+    // from a float reciprocal, exact after one correction below 2^22.
+    auto div_floor = [](int a, int d, float inv_d) {
+      int q = (int)((float)a * inv_d);
+      const int r = a - q * d;
+      return q + (r >= d ? 1 : 0) - (r < 0 ? 1 : 0);
+    };
+    // position 0 visits the last tile of the range (the one that can be
+    // ragged), positions 1.. the others in order
+    auto tile_of = [&](int pos) { return pos == 0 ? tile_end - 1 : tile_begin + pos - 1; };
+    auto describe = [&](int pos, int4* tab) {
+      if (wave == 0) {
+        const int ln = opaque(lane);
+        const int v = min(tile_of(pos) * kBN + ln, n_keys - 1);
+        const int rank = div_floor(v, p.T, p.inv_T), tok = v - rank * p.T;
+        const int y = div_floor(tok, p.grid_x, p.inv_grid_x);
+        if (ln < kBN)
+          tab[ln] = int4{(slot_of[rank] * p.T + tok) * F::DK * (int)sizeof(T), rank, y, tok - y * p.grid_x};
+      }
+    };
+
+    // ---- latent part: global -> LDS, lane order = LDS order (no registers)
+    auto issue_latent = [&](const int4* tab, T* buf) {
 #pragma unroll
-  for (int mb = 0; mb < kNMB; ++mb) {
-    const float l = wave_sum_across_groups(l_run[mb]);
-    const int row = row_wave + mb * 16 + li;
-    if (row >= p.Mb) continue;
-    if (p.splits == 1) {
-      const bool ok = l <= kSumLimit;  // false for inf / NaN as well
-      const float inv = (ok && l > 0.f) ? 1.f / l : 0.f;
-      T* dst = (T*)p.o_lat + ((size_t)b * p.Mb + row) * DC;
+      for (int k = 0; k < F::N_INSTR_WAVE; ++k) {
+        const int instr = wave + kWaves * k;
+        const int pk = opaque(lat_pk[k]);
+        if (instr < F::N_INSTR && pk >= 0) {
+          const char* src = cache_b + (unsigned)(tab[pk >> 16].x + (pk & 0xffff));
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                           (MLA_LDS void*)(MLA_LDS T*)(buf + instr * 64 * F::CB), 16, 0, 0);
+        }
+      }
+    };
+
+    // ---- kR part: RP rotary pairs per thread via registers, rotated with the
+    // LDS (cos, sin) rows on their way into LDS
+    typedef typename std::conditional<F::RW == 1, uint32_t,
+                                      typename std::conditional<F::RW == 2, u32x2, u32x4>::type>::type ru_t;
+    ru_t st_r = {};
+    auto word = [&](const ru_t& v, int k) -> uint32_t {
+      if constexpr (F::RW == 1) return v;
+      else return v[k];
+    };
+    auto fetch_rope = [&](const int4* tab) {
+      const int t2 = opaque(tid);
+      const int r_key = t2 / F::NU, r_unit = t2 % F::NU;
+      if (t2 < F::RCH)
+        st_r = *reinterpret_cast<const ru_t*>(cache_b + (unsigned)(tab[r_key].x + (DC + r_unit * F::RU) *
+                                                                                    (int)sizeof(T)));
+    };
+    auto stash_rope = [&](const int4* tab, T* buf) {
+      const int t2 = opaque(tid);
+      const int r_key = t2 / F::NU, r_unit = t2 % F::NU;
+      if (t2 < F::RCH) {
+        const int4 d = tab[r_key];
+        float f[F::RU];
+        if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int db = 0; db < F::NDB; ++db)
+          for (int k = 0; k < F::RW; ++k) {
+            f[2 * k] = __uint_as_float(word(st_r, k) << 16);
+            f[2 * k + 1] = __uint_as_float(word(st_r, k) & 0xffff0000u);
+          }
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[db * 16 + lg * 4 + i] = to_t<T>(o[db][mb][i] * inv);
-      if (!ok && lg == 0) p.fallback_rows[atomicAdd(p.fallback_count, 1)] = b * p.Mb + row;
-    } else {
-      const size_t prow = ((size_t)split * p.batch + b) * p.Mb + row;
-      float* dst = p.part_o + prow * DC;
+          for (int k = 0; k < F::RW; ++k) f[k] = __uint_as_float(word(st_r, k));
+        }
 #pragma unroll
-      for (int db = 0; db < F::NDB; ++db) *reinterpret_cast<f32x4*>(dst + db * 16 + lg * 4) = o[db][mb];
-      if (lg == 0) {
-        const bool empty = tile_begin >= tile_end;  // no keys: weight 0 in the merge
-        p.part_l[prow * 2] = empty ? -__builtin_inff() : -negref[mb][0];
-        p.part_l[prow * 2 + 1] = l;
+        for (int k = 0; k < F::RP; ++k) {
+          const int pr = r_unit * F::RP + k;
+          const int idx = pr < pt ? d.y * pt + pr
+                                  : (pr < pt + py ? y_base + d.z * py + pr - pt : x_base + d.w * px + pr - pt - py);
+          const f32x2 cs = rcs[idx];
+          rotate_pair(f[2 * k], f[2 * k + 1], cs.x, cs.y);
+        }
+        uint32_t w[F::RW];
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int k = 0; k < F::RW; ++k) {
+            const uint32_t lo = __builtin_bit_cast(uint16_t, (bf16)f[2 * k]);
+            const uint32_t hi = __builtin_bit_cast(uint16_t, (bf16)f[2 * k + 1]);
+            w[k] = lo | (hi << 16);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < F::RW; ++k) w[k] = __float_as_uint(f[k]);
+        }
+        ru_t out;
+        if constexpr (F::RW == 1) {
+          out = w[0];
+        } else {
+#pragma unroll
+          for (int k = 0; k < F::RW; ++k) out[k] = w[k];
+        }
+        *reinterpret_cast<ru_t*>(buf + r_key * F::LS + DC + r_unit * F::RU) = out;
+      }
+    };
+
+    // zero the padding chunks of both buffers once (never written again)
+    if constexpr (F::PADC > 0) {
+      for (int e = tid; e < 2 * kBN * F::PADC; e += F::kThreads) {
+        const int bi = e / (kBN * F::PADC), q = e % (kBN * F::PADC);
+        T* bp = bi == 0 ? kv0 : kv1;
+        const u32x4 z = {};
+        *reinterpret_cast<u32x4*>(&bp[((q / F::PADC) * F::CPR + F::CC + F::RC + q % F::PADC) * F::CB]) = z;
+      }
+    }
+
+    // ---- the three pieces of the key loop, for one 32-key half of a tile.
+    // Scores S^T = K Q^T of half `half` of the tile in `kt`, seeded with
+    // `seed` (the negated reference of each row).
+    typedef f32x4 sblk[2][kNMB];
+    auto scores = [&](const T* kt, int half, sblk& s, const f32x4 (&seed)[kNMB]) {
+#pragma unroll
+      for (int kc = 0; kc < F::NKC; ++kc) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const v8 a = lds_load8<T>(kt + ((half * 2 + kb) * 16 + li) * F::LS + kc * 32 + lg * 8);
+#pragma unroll
+          for (int mb = 0; mb < kNMB; ++mb) s[kb][mb] = mma16(a, qf[mb][kc], kc == 0 ? seed[mb] : s[kb][mb]);
+        }
+      }
+    };
+    // probabilities 2^s, packed into the B operand of the value product; with
+    // RAGGED, keys at or past n_keys (kfirst = key index of the half) get 0
+    auto probs = [&](const sblk& s, v8 (&pb)[kNMB], int kfirst, auto ragged_c) {
+      constexpr bool RAGGED = decltype(ragged_c)::value;
+#pragma unroll
+      for (int mb = 0; mb < kNMB; ++mb) {
+        float f8[8];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float e = fast_exp2(s[kb][mb][i]);
+            if constexpr (RAGGED) e = kfirst + kb * 16 + lg * 4 + i < n_keys ? e : 0.f;
+            f8[kb * 4 + i] = e;
+            l_run[mb] += e;
+          }
+        pb[mb] = pack8<T>(f8);
+      }
+    };
+    // O^T[d][row] += C^T[d][key] P^T[key][row]; key slot j of lane group g is
+    // key 4g+j (j < 4) or 16+4g+(j-4) of the half, matching S^T's layout
+    auto values = [&](const T* kt, int half, const v8 (&pb)[kNMB]) {
+#pragma unroll
+      for (int db = 0; db < F::NDB; ++db) {
+        const v8 a = lds_tr8(kt, F::LS, half * 32 + lg * 4, half * 32 + 16 + lg * 4, db * 16);
+#pragma unroll
+        for (int mb = 0; mb < kNMB; ++mb) o[db][mb] = mma16(a, pb[mb], o[db][mb]);
+      }
+    };
+    auto buf_of = [&](auto par_c) -> T* { return decltype(par_c)::value == 0 ? kv0 : kv1; };
+    typedef std::integral_constant<int, 0> B0;
+    typedef std::integral_constant<int, 1> B1;
+
+    // One tile: start the loads of the next position (descriptors ready),
+    // describe the one after, consume this tile half by half, stash the next
+    // tile's kR part, wait for its latent loads, barrier.
+    auto step = [&](int pos, auto cur_c, auto ragged_c) {
+      constexpr int CUR = decltype(cur_c)::value;
+      T* cur = buf_of(cur_c);
+      T* nxt = buf_of(std::integral_constant<int, CUR ^ 1>());
+      const bool has_next = pos + 1 < n_visit;
+      if (has_next) {
+        issue_latent(keytab[CUR ^ 1], nxt);
+        fetch_rope(keytab[CUR ^ 1]);
+      }
+      if (pos + 2 < n_visit) describe(pos + 2, keytab[CUR]);
+      const int kbase = tile_of(pos) * kBN;
+#pragma unroll 1
+      for (int half = 0; half < NKC2; ++half) {
+        sblk s;
+        scores(cur, half, s, negref);
+        v8 pb[kNMB];
+        probs(s, pb, kbase + half * 32, ragged_c);
+        values(cur, half, pb);
+      }
+      if (has_next) stash_rope(keytab[CUR ^ 1], nxt);
+      __builtin_amdgcn_s_waitcnt(0);  // direct loads of the next tile have landed
+      __syncthreads();
+    };
+
+    // ---- prologue: descriptors of positions 0 and 1, tile 0 into buffer 0,
+    // then the reference from its first 32 keys
+    if (n_visit > 0) {
+      describe(0, keytab[0]);
+      if (n_visit > 1) describe(1, keytab[1]);
+    }
+    __syncthreads();
+    if (n_visit > 0) {
+      issue_latent(keytab[0], kv0);
+      fetch_rope(keytab[0]);
+      stash_rope(keytab[0], kv0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (n_visit > 0) {
+      const int kbase = tile_of(0) * kBN;
+      sblk s;
+      const f32x4 zs[kNMB] = {};
+      scores(kv0, 0, s, zs);
+#pragma unroll
+      for (int mb = 0; mb < kNMB; ++mb) {
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kbase + kb * 16 + lg * 4 + i < n_keys) mx = fmaxf(mx, s[kb][mb][i]);
+        mx = wave_max_across_groups(mx);
+        negref[mb] = f32x4{-mx, -mx, -mx, -mx};
+      }
+      // position 0 is the only tile that can be ragged
+      step(0, B0(), std::integral_constant<bool, true>());
+    }
+    {
+      typedef std::integral_constant<bool, false> Full;
+      int pos = 1;
+      for (; pos + 1 < n_visit; pos += 2) {
+        step(pos, B1(), Full());
+        step(pos + 1, B0(), Full());
+      }
+      if (pos < n_visit) step(pos, B1(), Full());
+    }
+
+    // ---- epilogue
+    const int eln = opaque(lane);
+    const int eli = eln & 15, elg = eln >> 4;
+#pragma unroll
+    for (int mb = 0; mb < kNMB; ++mb) {
+      const float l = wave_sum_across_groups(l_run[mb]);
+      const int row = rb * F::kRowsBlock + wave * F::kRowsWave + mb * 16 + eli;
+      if (row >= p.Mb) continue;
+      if (whole) {
+        const bool ok = l <= kSumLimit;  // false for inf / NaN as well
+        const float inv = (ok && l > 0.f) ? 1.f / l : 0.f;
+        T* dst = (T*)p.o_lat + ((size_t)b * p.Mb + row) * DC;
+#pragma unroll
+        for (int db = 0; db < F::NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[db * 16 + elg * 4 + i] = to_t<T>(o[db][mb][i] * inv);
+        if (!ok && elg == 0) p.fallback_rows[atomicAdd(p.fallback_count, 1)] = b * p.Mb + row;
+      } else {
+        const size_t prow = ((size_t)blockIdx.x * 2 + (first_seg ? 0 : 1)) * F::kRowsBlock + row - rb * F::kRowsBlock;
+        float* dst = p.part_o + prow * DC;
+#pragma unroll
+        for (int db = 0; db < F::NDB; ++db) *reinterpret_cast<f32x4*>(dst + db * 16 + elg * 4) = o[db][mb];
+        if (elg == 0) {
+          const bool empty = n_visit == 0;  // no keys: weight 0 in the merge
+          p.part_l[prow * 2] = empty ? -__builtin_inff() : -negref[mb][0];
+          p.part_l[prow * 2 + 1] = l;
+        }
       }
     }
   }
 }
 
-// Merge of the per-split (reference, output, probability sum) of one row:
-// with M = max_s r_s and w_s = 2^(r_s - M), o = sum_s w_s o_s / sum_s w_s l_s.
-template <typename T, int DC>
+// Merge of the partial results of a row block shared by work-groups
+// g0..g1 (the work-groups whose unit ranges meet the row block's units
+// [a, a + nt_max)): with M = max_g r_g and w_g = 2^(r_g - M),
+// o = sum_g w_g o_g / sum_g w_g l_g. Work-group g's piece sits in its slot 0
+// when its range starts inside the row block, else in its slot 1.
+template <typename T, int DC, int RB>
 __global__ __launch_bounds__(256) void flash_combine_kernel(FlashParams p) {
   constexpr int D4 = DC / 4;
   const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -442,18 +502,30 @@ __global__ __launch_bounds__(256) void flash_combine_kernel(FlashParams p) {
   if (e >= n_rows * D4) return;
   const long long r = e / D4;
   const int d = (int)(e % D4) * 4;
+  const int b = (int)(r / p.Mb), row = (int)(r - (long long)b * p.Mb);
+  const int rb = row / RB, local = row - rb * RB;
+  const long long G = p.grid;
+  const long long a = ((long long)b * p.n_rb + rb) * p.nt_max;
+  // largest g whose range starts at or before unit x
+  auto owner = [&](long long x) { return ((x + 1) * G - 1) / p.units; };
+  const long long g0 = owner(a), g1 = owner(a + p.nt_max - 1);
+  if (g0 == g1) return;  // one work-group covered the row block and wrote it
+  auto slot_row = [&](long long g) {
+    const long long start = g * p.units / G;
+    return (size_t)((g * 2 + (start >= a ? 0 : 1)) * RB + local);
+  };
   float M = -__builtin_inff();
   bool ok = true;
-  for (int sp = 0; sp < p.splits; ++sp) {
-    const size_t pr = (size_t)sp * n_rows + r;
+  for (long long g = g0; g <= g1; ++g) {
+    const size_t pr = slot_row(g);
     M = fmaxf(M, p.part_l[pr * 2]);
     ok = ok && (p.part_l[pr * 2 + 1] <= kSumLimit);
   }
   float L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (M > -__builtin_inff()) {
-    for (int sp = 0; sp < p.splits; ++sp) {
-      const size_t pr = (size_t)sp * n_rows + r;
+    for (long long g = g0; g <= g1; ++g) {
+      const size_t pr = slot_row(g);
       const float w = fast_exp2(p.part_l[pr * 2] - M);
       L += w * p.part_l[pr * 2 + 1];
       acc += w * *reinterpret_cast<const f32x4*>(p.part_o + pr * DC + d);
@@ -551,30 +623,29 @@ __global__ __launch_bounds__(256) void flash_exact_kernel(FlashParams p) {
 }
 
 template <typename T, int DC, int DR>
-static hipError_t launch_flash_t(const FlashParams& p, hipStream_t s) {
+static hipError_t launch_flash_t(const FlashParams& p, bool split, hipStream_t s) {
   typedef FlashTile<T, DC, DR> F;
   hipLaunchKernelGGL(flash_prep_kernel, dim3(1), dim3(1), 0, s, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  dim3 grid((p.Mb + F::kRowsBlock - 1) / F::kRowsBlock, p.splits, p.batch);
-  hipLaunchKernelGGL((flash_mla_kernel<T, DC, DR>), grid, dim3(F::kThreads), 0, s, p);
+  hipLaunchKernelGGL((flash_mla_kernel<T, DC, DR>), dim3(p.grid), dim3(F::kThreads), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (p.splits > 1) {
+  if (split) {
     const long long total = (long long)p.batch * p.Mb * (DC / 4);
     const int blocks = (int)((total + 255) / 256);
-    hipLaunchKernelGGL((flash_combine_kernel<T, DC>), dim3(blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((flash_combine_kernel<T, DC, F::kRowsBlock>), dim3(blocks), dim3(256), 0, s, p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   hipLaunchKernelGGL((flash_exact_kernel<T, DC, DR>), dim3(kFallbackBlocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_flash(int dtype, int d_c, int d_rope, const FlashParams& p, hipStream_t s) {
-  if (p.Mb <= 0 || p.batch <= 0) return hipSuccess;
+hipError_t launch_flash(int dtype, int d_c, int d_rope, const FlashParams& p, bool split, hipStream_t s) {
+  if (p.Mb <= 0 || p.batch <= 0 || p.grid <= 0) return hipSuccess;
   if (d_c == 192 && d_rope == 32)
-    return dtype == 0 ? launch_flash_t<bf16, 192, 32>(p, s) : launch_flash_t<float, 192, 32>(p, s);
+    return dtype == 0 ? launch_flash_t<bf16, 192, 32>(p, split, s) : launch_flash_t<float, 192, 32>(p, split, s);
   if (d_c == 16 && d_rope == 8)
-    return dtype == 0 ? launch_flash_t<bf16, 16, 8>(p, s) : launch_flash_t<float, 16, 8>(p, s);
+    return dtype == 0 ? launch_flash_t<bf16, 16, 8>(p, split, s) : launch_flash_t<float, 16, 8>(p, split, s);
   return hipErrorInvalidValue;
 }
 

@@ -84,35 +84,70 @@ size_t table_floats(const mla_shape* s, int n_t) {
 size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
 int flash_rows_per_block(const mla_shape* s) { return s->dtype == MLA_BF16 ? 256 : 128; }
+int flash_tile_keys(const mla_shape* s) { return s->dtype == MLA_BF16 ? 64 : 32; }
 
-int choose_splits(const mla_shape* s, int q_n_frames, int requested) {
-  if (requested > 0) return requested;
-  const int64_t Mb = (int64_t)q_n_frames * tokens_per_frame(s) * s->n_heads;
-  const int64_t blocks = (int64_t)s->batch * ((Mb + flash_rows_per_block(s) - 1) / flash_rows_per_block(s));
-  if (blocks >= kAssumedCUs / 2) return 1;
-  int64_t sp = (kAssumedCUs + blocks - 1) / blocks;
-  return (int)(sp > 8 ? 8 : sp);
+// Compute units of the current device (the automatic work split uses one
+// work-group per compute unit); falls back to the MI355X count.
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return kAssumedCUs;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return kAssumedCUs;
+  return n;
 }
 
-// Flash workspace: the fallback row list and, for kv_splits > 1, the
-// per-split partial outputs, references and probability sums.
+// Work split of the attention kernel: `grid` work-groups share `units`
+// (row block, key tile) pairs evenly. kv_splits = s > 0 gives every row
+// block s equal key ranges (s = 1: one work-group per row block);
+// kv_splits = 0 uses one work-group per compute unit.
+struct FlashPlan {
+  int n_rb, nt_max;
+  int64_t units;
+  int grid;
+  bool split;  // some row block is shared by several work-groups
+};
+
+FlashPlan flash_plan(const mla_shape* s, int q_n_frames, int kv_splits) {
+  FlashPlan f;
+  const int64_t Mb = (int64_t)q_n_frames * tokens_per_frame(s) * s->n_heads;
+  const int rpb = flash_rows_per_block(s), tk = flash_tile_keys(s);
+  f.n_rb = (int)((Mb + rpb - 1) / rpb);
+  f.nt_max = (int)((s->window_frames * tokens_per_frame(s) + tk - 1) / tk);
+  f.units = (int64_t)s->batch * f.n_rb * f.nt_max;
+  int64_t g = kv_splits > 0 ? (int64_t)s->batch * f.n_rb * kv_splits : device_cus();
+  if (g > f.units) g = f.units;
+  if (g < 1) g = 1;
+  if (g > (INT64_C(1) << 23)) g = INT64_C(1) << 23;  // rejected by flash_plan_ok
+  f.grid = (int)g;
+  f.split = !(f.units % g == 0 && (f.units / g) % f.nt_max == 0);
+  return f;
+}
+
+// unit and work-group indices stay far from 64-bit overflow (g * units)
+bool flash_plan_ok(const FlashPlan& f) {
+  return f.units <= (INT64_C(1) << 40) && f.grid <= (1 << 22);
+}
+
+// Flash workspace: the fallback row list and, when row blocks are shared,
+// two partial (output, reference, sum) slots per work-group.
 struct FlashWs {
   size_t count, rows, part_o, part_l, total;
 };
 
-FlashWs flash_ws_layout(const mla_shape* s, int q_n_frames, int splits) {
+FlashWs flash_ws_layout(const mla_shape* s, int q_n_frames, const FlashPlan& f) {
   const size_t rows = (size_t)s->batch * q_n_frames * tokens_per_frame(s) * s->n_heads;
+  const size_t slots = f.split ? (size_t)f.grid * 2 * flash_rows_per_block(s) : 0;
   FlashWs w;
   w.count = 0;
   w.rows = w.count + 256;
   w.part_o = w.rows + round256(rows * sizeof(int));
-  w.part_l = w.part_o + (splits > 1 ? round256((size_t)splits * rows * s->d_c * sizeof(float)) : 0);
-  w.total = w.part_l + (splits > 1 ? round256((size_t)splits * rows * 2 * sizeof(float)) : 0);
+  w.part_l = w.part_o + round256(slots * s->d_c * sizeof(float));
+  w.total = w.part_l + round256(slots * 2 * sizeof(float));
   return w;
 }
 
-size_t flash_ws_bytes(const mla_shape* s, int q_n_frames, int splits) {
-  return flash_ws_layout(s, q_n_frames, splits).total;
+size_t flash_ws_bytes(const mla_shape* s, int q_n_frames, int kv_splits) {
+  return flash_ws_layout(s, q_n_frames, flash_plan(s, q_n_frames, kv_splits)).total;
 }
 
 mla_status from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
@@ -148,19 +183,20 @@ mla_status do_absorb(const mla_shape* s, const void* q_nope, const void* q_r, in
 
 mla_status do_flash(const mla_shape* s, const void* q_abs, int q_n_frames, const void* cache,
                     const int32_t* slot_frame, const float* tables, int rope_t_first, int rope_n_t, void* o_lat,
-                    int splits, void* ws, hipStream_t st) {
+                    int kv_splits, void* ws, hipStream_t st) {
+  const FlashPlan f = flash_plan(s, q_n_frames, kv_splits);
   mla::FlashParams p;
   p.q_abs = q_abs;
   p.cache = cache;
   p.slot_frame = slot_frame;
   p.tables = tables;
   p.o_lat = o_lat;
-  const FlashWs w = flash_ws_layout(s, q_n_frames, splits);
+  const FlashWs w = flash_ws_layout(s, q_n_frames, f);
   char* base = (char*)ws;
   p.fallback_count = (int*)(base + w.count);
   p.fallback_rows = (int*)(base + w.rows);
-  p.part_o = splits > 1 ? (float*)(base + w.part_o) : nullptr;
-  p.part_l = splits > 1 ? (float*)(base + w.part_l) : nullptr;
+  p.part_o = f.split ? (float*)(base + w.part_o) : nullptr;
+  p.part_l = f.split ? (float*)(base + w.part_l) : nullptr;
   p.rl = rope_layout(s, rope_t_first, rope_n_t);
   p.Mb = (int)(q_n_frames * tokens_per_frame(s) * s->n_heads);
   p.W = s->window_frames;
@@ -170,9 +206,12 @@ mla_status do_flash(const mla_shape* s, const void* q_abs, int q_n_frames, const
   p.inv_T = 1.f / (float)p.T;
   p.inv_grid_x = 1.f / (float)s->grid_x;
   p.batch = s->batch;
-  p.splits = splits;
+  p.n_rb = f.n_rb;
+  p.nt_max = f.nt_max;
+  p.units = f.units;
+  p.grid = f.grid;
   p.scale_log2 = scale_log2(s);
-  return from_hip(mla::launch_flash(s->dtype, s->d_c, s->d_rope, p, st));
+  return from_hip(mla::launch_flash(s->dtype, s->d_c, s->d_rope, p, f.split, st));
 }
 
 mla_status do_up_v(const mla_shape* s, const void* o_lat, int q_n_frames, const void* w_uv, void* out,
@@ -290,7 +329,7 @@ MLA_API mla_status mla_absorb_q(const mla_shape* shape, const void* q_nope, cons
 
 MLA_API size_t mla_flash_workspace_bytes(const mla_shape* shape, int32_t q_n_frames, int32_t kv_splits) {
   if (check_shape(shape) != MLA_OK || q_n_frames < 1 || kv_splits < 0 || kv_splits > kMaxSplits) return 0;
-  return flash_ws_bytes(shape, q_n_frames, choose_splits(shape, q_n_frames, kv_splits));
+  return flash_ws_bytes(shape, q_n_frames, kv_splits);
 }
 
 MLA_API mla_status mla_flash_attend(const mla_shape* shape, const void* q_abs, int32_t q_n_frames, const void* cache,
@@ -304,11 +343,11 @@ MLA_API mla_status mla_flash_attend(const mla_shape* shape, const void* q_abs, i
   if ((st = check_tables(shape, rope_tables, rope_t_first, rope_n_t)) != MLA_OK) return st;
   if ((st = check_query_args(shape, 0, q_n_frames)) != MLA_OK) return st;
   if (kv_splits < 0 || kv_splits > kMaxSplits) return MLA_ERR_RANGE;
-  const int splits = choose_splits(shape, q_n_frames, kv_splits);
   if (!workspace) return MLA_ERR_NULL;
   if (!aligned16(workspace)) return MLA_ERR_ALIGN;
-  if (workspace_bytes < flash_ws_bytes(shape, q_n_frames, splits)) return MLA_ERR_WORKSPACE;
-  return do_flash(shape, q_abs, q_n_frames, cache, slot_frame, rope_tables, rope_t_first, rope_n_t, o_lat, splits,
+  if (!flash_plan_ok(flash_plan(shape, q_n_frames, kv_splits))) return MLA_ERR_SHAPE;
+  if (workspace_bytes < flash_ws_bytes(shape, q_n_frames, kv_splits)) return MLA_ERR_WORKSPACE;
+  return do_flash(shape, q_abs, q_n_frames, cache, slot_frame, rope_tables, rope_t_first, rope_n_t, o_lat, kv_splits,
                   workspace, (hipStream_t)stream);
 }
 
@@ -326,7 +365,7 @@ MLA_API size_t mla_chunk_attend_workspace_bytes(const mla_shape* shape, int32_t 
   if (check_shape(shape) != MLA_OK || q_n_frames < 1) return 0;
   const size_t rows = (size_t)shape->batch * q_n_frames * tokens_per_frame(shape) * shape->n_heads;
   return round256(rows * qabs_dim(shape) * elt_size(shape)) + round256(rows * shape->d_c * elt_size(shape)) +
-         flash_ws_bytes(shape, q_n_frames, choose_splits(shape, q_n_frames, 0));
+         flash_ws_bytes(shape, q_n_frames, 0);
 }
 
 MLA_API mla_status mla_chunk_attend(const mla_shape* shape, const void* q_nope, const void* q_r, int32_t q_frame_first,
@@ -344,6 +383,7 @@ MLA_API mla_status mla_chunk_attend(const mla_shape* shape, const void* q_nope, 
   if ((st = check_query_args(shape, q_frame_first, q_n_frames)) != MLA_OK) return st;
   if (q_frame_first < rope_t_first || (int64_t)q_frame_first + q_n_frames > (int64_t)rope_t_first + rope_n_t)
     return MLA_ERR_RANGE;
+  if (!flash_plan_ok(flash_plan(shape, q_n_frames, 0))) return MLA_ERR_SHAPE;
   if (workspace_bytes < mla_chunk_attend_workspace_bytes(shape, q_n_frames)) return MLA_ERR_WORKSPACE;
   const size_t rows = (size_t)shape->batch * q_n_frames * tokens_per_frame(shape) * shape->n_heads;
   char* ws = (char*)workspace;
@@ -355,8 +395,7 @@ MLA_API mla_status mla_chunk_attend(const mla_shape* shape, const void* q_nope, 
   if ((st = do_absorb(shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk, rope_tables, rope_t_first, rope_n_t,
                       q_abs, s)) != MLA_OK)
     return st;
-  const int splits = choose_splits(shape, q_n_frames, 0);
-  if ((st = do_flash(shape, q_abs, q_n_frames, cache, slot_frame, rope_tables, rope_t_first, rope_n_t, o_lat, splits,
+  if ((st = do_flash(shape, q_abs, q_n_frames, cache, slot_frame, rope_tables, rope_t_first, rope_n_t, o_lat, 0,
                      ws, s)) != MLA_OK)
     return st;
   return do_up_v(shape, o_lat, q_n_frames, w_uv, out, s);

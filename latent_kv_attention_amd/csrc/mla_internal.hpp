@@ -45,20 +45,28 @@ struct AbsorbParams {
   float qscale;        // softmax scale * log2(e)
 };
 
+// The attention work is a grid of units (row block, key tile): n_rb row
+// blocks per stream, nt_max tiles of a full window per row block, units =
+// batch * n_rb * nt_max in row-block-major order. Work-group g of G takes
+// units [g U / G, (g + 1) U / G); a row block that falls to several
+// work-groups is finished by a merge pass over their partial results.
 struct FlashParams {
   const void* q_abs;       // [B][Mb][Q]
   const void* cache;       // [B][W][T][d_c + d_rope]
   const int32_t* slot_frame;
   const float* tables;
   void* o_lat;             // [B][Mb][d_c]
-  float* part_o;           // [splits][B][Mb][d_c] when splits > 1
-  float* part_l;           // [splits][B][Mb][2] (reference, sum) when splits > 1
+  float* part_o;           // [G][2][rows per block][d_c] partial outputs (split row blocks only)
+  float* part_l;           // [G][2][rows per block][2] (reference, sum)
   int* fallback_count;     // rows listed for the exact fallback
   int* fallback_rows;      // [B * Mb]
   RopeLayout rl;
   int Mb;                  // Nq * H
-  int W, T, grid_y, grid_x, batch, splits;
+  int W, T, grid_y, grid_x, batch;
   float inv_T, inv_grid_x; // 1/T and 1/grid_x (key index -> slot, row, column)
+  int n_rb, nt_max;        // row blocks per stream, key tiles of a full window
+  long long units;         // batch * n_rb * nt_max
+  int grid;                // G, work-groups of the attention kernel
   float scale_log2;        // softmax scale * log2(e)
 };
 
@@ -79,7 +87,7 @@ struct UpVParams {
 hipError_t launch_rope_tables(const RopeTableParams& p, hipStream_t s);
 hipError_t launch_cache_write(int dtype, int d_c, int d_rope, const CacheWriteParams& p, hipStream_t s);
 hipError_t launch_absorb_q(int dtype, int d_c, int d_rope, const AbsorbParams& p, hipStream_t s);
-hipError_t launch_flash(int dtype, int d_c, int d_rope, const FlashParams& p, hipStream_t s);
+hipError_t launch_flash(int dtype, int d_c, int d_rope, const FlashParams& p, bool split, hipStream_t s);
 hipError_t launch_up_v(int dtype, int d_c, int d_rope, const UpVParams& p, hipStream_t s);
 
 }  // namespace mla

@@ -180,8 +180,12 @@ def _run_flash(cfg, cache, slot_frame, q_abs, kv_splits=0, n_t=64, want_fallback
 
 
 @pytest.mark.parametrize("name", STAGE_CONFIGS)
-@pytest.mark.parametrize("kv_splits", [1, 3])
+@pytest.mark.parametrize("kv_splits", [0, 1, 3, 5])
 def test_flash_attend(name, kv_splits):
+    """kv_splits 0 spreads the (row block, key tile) units evenly over one
+    work-group per compute unit, so row blocks are shared by several
+    work-groups and merged; 1 gives one work-group per row block; 3 and 5
+    cut every row block's keys into that many ranges (uneven for 5)."""
     cfg = get_config(name)
     W = cfg.window_frames
     cache, sf, q_abs, ref = _flash_inputs(cfg, 6, list(range(W + 2)), W + 2 - cfg.chunk_frames)
@@ -202,15 +206,18 @@ def test_flash_attend_extreme_logits_use_exact_fallback():
     """Logit gaps beyond the fixed-reference range (q x 50: logit std ~50):
     those rows are listed and recomputed by the exact two-pass kernel. At such
     logits the fp32 rounding of the scores themselves moves the output by
-    ~1e-3, so this case is gated at 5e-3 (max) and 5e-3 (relative RMS)."""
+    ~1e-3, so this case is gated at 5e-3 (max) and 5e-3 (relative RMS). With
+    the automatic split each work-group's key range is short and takes its own
+    reference, so there the fallback may not be needed at all."""
     cfg = get_config("wan_small_f32")
     cache, sf, q_abs, ref = _flash_inputs(cfg, 8, [0, 1, 2, 3], 3, q_scale=50.0)
-    for splits in (1, 2):
+    for splits in (0, 1, 2):
         got, n_fallback = _run_flash(cfg, cache, sf, q_abs, splits, want_fallback_count=True)
         from .gpu_common import errors
         e = errors(got, ref)
         print(f"[parity] extreme logits splits={splits} fallback rows={n_fallback} {e}", flush=True)
-        assert n_fallback > 0
+        if splits in (1, 2):  # long key ranges: some rows outgrow their reference
+            assert n_fallback > 0
         assert e["max_abs"] <= 5e-3 and e["rel_rms"] <= 5e-3, e
 
 
