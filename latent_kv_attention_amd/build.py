@@ -28,6 +28,13 @@ HIPCC_FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
+# Per-source additions. The attention kernel runs at the register limit; the
+# backend's own register-pressure trackers give its scheduler a tighter
+# estimate there (about 2% faster, measured).
+SOURCE_FLAGS = {
+    "flash_mla.hip": ["-mllvm", "-amdgpu-use-amdgpu-trackers"],
+}
+
 
 def _hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -56,7 +63,8 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        _run([hipcc, *HIPCC_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        _run([hipcc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *inc, "-c", os.path.join(CSRC, src), "-o", obj],
+             verbose)
         return obj
 
     jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 4)))

@@ -5,11 +5,20 @@
 // slot f mod W.
 //
 // GEMM view: out[r][n] = sum_k x[r][k] * Wcat[n][k], Wcat = [W_dkv ; W_kR]
-// (N = d_c + d_rope). Both operands are contiguous along k, so every lane
-// loads 8 consecutive elements straight into its matrix-core operand.
-// Work-group tile: 64 token rows x 32 outputs, four waves of 16 rows each.
-// The 1-D grid is walked XCD-major so that the output tiles sharing a block
-// of token rows run on one XCD and its L2 serves the repeated x reads.
+// (N = d_c + d_rope). The step is bound by HBM: every x byte is read once
+// from memory and 14x fewer bytes are written.
+//
+// bf16 with hidden = 1536 (the Wan2.1-1.3B width): work-group tiles of 80
+// token rows x 64 outputs (236 tiles for a 3-frame Wan chunk, all resident
+// at once). Both operands stream through LDS in 128-wide K steps with direct
+// global->LDS loads, two steps in flight; each staged row is 256 bytes and
+// its 16-byte chunks are XOR-permuted by the row index so the 16 rows that a
+// matrix-core operand read touches hit different banks. Each wave owns one
+// 16-column block of all five 16-row blocks. The output tile goes through
+// LDS once more so that rows leave in 16-byte stores.
+//
+// Other shapes (fp32, small latents, other widths) use a plain kernel
+// with 64 x 32 tiles and operands loaded straight from global memory.
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
@@ -19,14 +28,163 @@ namespace {
 constexpr int kRowsPerBlock = 64;
 constexpr int kColsPerBlock = 32;
 constexpr int kXcds = 8;
+
+// staged bf16 kernel
+constexpr int kSM = 80;                           // token rows per tile (5 x 16)
+constexpr int kSN = 64;                           // outputs per tile (4 x 16, one block per wave)
+constexpr int kSK = 128;                          // K per stage
+constexpr int kSChunks = kSK * 2 / 16;            // 16-byte chunks per staged row (16)
+constexpr int kSRows = kSM + kSN;                 // staged rows per stage
+constexpr int kSInstr = kSRows * kSChunks / 64;   // direct-load instructions per stage (36)
+constexpr int kSInstrWave = (kSInstr + 3) / 4;    // per wave (9)
+constexpr int kSElems = kSRows * kSK;             // bf16 elements per stage buffer
+constexpr int kSOutLd = kSN + 8;                  // output staging row stride (elements)
+constexpr int kSBufs = 3;                         // stage buffers; kSBufs - 1 stages in flight
+static_assert(kSRows * kSChunks % 64 == 0, "whole direct-load instructions per stage");
+static_assert(kSM * kSOutLd <= kSElems, "output staging fits in one stage buffer");
+static_assert(kSBufs == 3 && (kSBufs - 2) * kSInstrWave < 64, "three named stage buffers; vmcnt range");
 }  // namespace
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// XCD-major order: consecutive logical tiles (which share token rows) land on
+// one XCD, whose L2 then serves the repeated x reads.
+__device__ __forceinline__ int xcd_logical(int id, int per_xcd) { return (id % kXcds) * per_xcd + id / kXcds; }
+
+template <int NSTAGE>
+__global__ __launch_bounds__(256) void cache_write_staged_kernel(CacheWriteParams p, int n_tiles_n, int n_logical,
+                                                                 int per_xcd) {
+  __shared__ __attribute__((aligned(16))) bf16 sb0[kSElems];
+  __shared__ __attribute__((aligned(16))) bf16 sb1[kSElems];
+  __shared__ __attribute__((aligned(16))) bf16 sb2[kSElems];
+  const int logical = xcd_logical(blockIdx.x, per_xcd);
+  if (logical >= n_logical) return;
+  const int row0 = (logical / n_tiles_n) * kSM;
+  const int col0 = (logical % n_tiles_n) * kSN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int n_out = p.d_c + p.d_rope;
+
+  if (logical == 0) {
+    for (int e = tid; e < p.batch * p.n_frames; e += blockDim.x) {
+      const int b = e / p.n_frames, f = p.frame_first + e % p.n_frames;
+      p.slot_frame[b * p.W + f % p.W] = f;
+    }
+  }
+
+  // direct-load sources: instruction k of this wave fills LDS chunks
+  // [64 i, 64 i + 64), i = wave + 4k; chunk q of staged row sr holds global
+  // chunk q ^ (sr % kSChunks) of that row. Rows past the end repeat the last row.
+  const char* src[kSInstrWave];
+  int dst_off[kSInstrWave];
+#pragma unroll
+  for (int k = 0; k < kSInstrWave; ++k) {
+    const int instr = min(wave + 4 * k, kSInstr - 1);
+    const int pos = instr * 64 + lane;
+    const int sr = pos / kSChunks, c = (pos % kSChunks) ^ (sr & (kSChunks - 1));
+    const bf16* rowp;
+    if (sr < kSM) {
+      rowp = (const bf16*)p.x + (size_t)min(row0 + sr, p.rows - 1) * p.hidden;
+    } else {
+      const int n = min(col0 + sr - kSM, n_out - 1);
+      rowp = n < p.d_c ? (const bf16*)p.w_dkv + (size_t)n * p.hidden
+                       : (const bf16*)p.w_kr + (size_t)(n - p.d_c) * p.hidden;
+    }
+    src[k] = (const char*)(rowp + c * 8);
+    dst_off[k] = instr * 64 * 8;  // elements
+  }
+  // Work-groups walk K from different starting steps, so the many tiles that
+  // share W rows (and the few that share x rows) do not all ask the L2 for
+  // the same lines at the same moment. The sum is the same in any order.
+  const int k_start = logical % NSTAGE;
+  auto issue = [&](int stage, bf16* buf) {
+    int ks = stage + k_start;
+    ks = ks >= NSTAGE ? ks - NSTAGE : ks;
+#pragma unroll
+    for (int k = 0; k < kSInstrWave; ++k)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[k] + ks * kSK * 2),
+                                       (MLA_LDS void*)(MLA_LDS bf16*)(buf + dst_off[k]), 16, 0, 0);
+  };
+
+  const bool active = col0 + wave * 16 < n_out;  // this wave's 16 outputs exist
+  f32x4 acc[kSM / 16] = {};
+  // operand reads: staged row r, logical chunk c -> element (r * kSChunks + (c ^ (r % kSChunks))) * 8
+  auto compute = [&](const bf16* buf) {
+    if (!active) return;
+#pragma unroll
+    for (int kc = 0; kc < kSK / 32; ++kc) {
+      const int c = kc * 4 + lg;
+      const int rb = kSM + wave * 16 + li;
+      const bf16x8 bop = load8<bf16>(buf + (rb * kSChunks + (c ^ (rb & (kSChunks - 1)))) * 8);
+#pragma unroll
+      for (int mb = 0; mb < kSM / 16; ++mb) {
+        const int ra = mb * 16 + li;
+        const bf16x8 aop = load8<bf16>(buf + (ra * kSChunks + (c ^ (ra & (kSChunks - 1)))) * 8);
+        acc[mb] = mma16(aop, bop, acc[mb]);
+      }
+    }
+  };
+
+  // kSBufs - 1 stages in flight: wait for this wave's loads of stage s
+  // (leaving the kSBufs - 2 later ones outstanding), barrier, start stage
+  // s + kSBufs - 1 into the buffer that stage s - 1 used, compute stage s. The
+  // barrier is the bare instruction: a full __syncthreads() would also wait
+  // for every outstanding load. The stage loop is unrolled completely
+  // (NSTAGE = hidden / 64 is a template parameter) so that every buffer is
+  // known at compile time and the compiler adds no waits of its own for the
+  // loads still in flight.
+  auto buf = [&](int i) -> bf16* { return i == 0 ? sb0 : i == 1 ? sb1 : sb2; };
+#pragma unroll
+  for (int s = 0; s < kSBufs - 1 && s < NSTAGE; ++s) issue(s, buf(s));
+#pragma unroll
+  for (int s = 0; s < NSTAGE; ++s) {
+    // stages issued after s that may stay in flight (folds to a constant)
+    switch (min(NSTAGE - 1 - s, kSBufs - 2)) {
+      case 0: wait_vm<0>(); break;
+      case 1: wait_vm<kSInstrWave>(); break;
+      case 2: wait_vm<2 * kSInstrWave>(); break;
+      case 3: wait_vm<3 * kSInstrWave>(); break;
+      default: wait_vm<4 * kSInstrWave>(); break;
+    }
+    __builtin_amdgcn_s_barrier();
+    if (s + kSBufs - 1 < NSTAGE) issue(s + kSBufs - 1, buf((s + kSBufs - 1) % kSBufs));
+    compute(buf(s % kSBufs));
+  }
+
+  // output tile -> LDS (bf16) -> 16-byte stores of whole row segments
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  bf16* ot = sb0;
+  if (active) {
+#pragma unroll
+    for (int mb = 0; mb < kSM / 16; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ot[(mb * 16 + lg * 4 + i) * kSOutLd + wave * 16 + li] = (bf16)acc[mb][i];
+  }
+  __syncthreads();
+  const int n_cols = min(kSN, n_out - col0);  // a multiple of 8
+  for (int e = tid; e < kSM * (kSN / 8); e += 256) {
+    const int r = e / (kSN / 8), c8 = (e % (kSN / 8)) * 8;
+    const int row = row0 + r;
+    if (row >= p.rows || c8 >= n_cols) continue;
+    const int b = row / p.rows_per_b, local = row - b * p.rows_per_b;
+    const int f = p.frame_first + local / p.T, tok = local % p.T;
+    bf16* dst = (bf16*)p.cache + (((size_t)b * p.W + f % p.W) * p.T + tok) * n_out + col0 + c8;
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(ot + r * kSOutLd + c8);
+  }
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p, int n_tiles_n, int n_logical,
                                                           int per_xcd) {
   typedef typename V8<T>::type v8;
   const int id = blockIdx.x;
-  const int logical = (id % kXcds) * per_xcd + id / kXcds;
+  const int logical = xcd_logical(id, per_xcd);
   if (logical >= n_logical) return;
   const int row_tile = logical / n_tiles_n;
   const int col_tile = logical % n_tiles_n;
@@ -88,6 +246,14 @@ hipError_t launch_cache_write(int dtype, int d_c, int d_rope, const CacheWritePa
   (void)d_c;
   (void)d_rope;
   const int n_out = p.d_c + p.d_rope;
+  if (dtype == 0 && p.hidden == 1536 && n_out % 8 == 0 && p.rows >= 1) {
+    const int n_tiles_n = (n_out + kSN - 1) / kSN;
+    const int n_logical = ((p.rows + kSM - 1) / kSM) * n_tiles_n;
+    const int per_xcd = (n_logical + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL(cache_write_staged_kernel<1536 / kSK>, dim3(per_xcd * kXcds), dim3(256), 0, s, p, n_tiles_n,
+                       n_logical, per_xcd);
+    return hipGetLastError();
+  }
   const int n_tiles_n = (n_out + kColsPerBlock - 1) / kColsPerBlock;
   const int n_tiles_m = (p.rows + kRowsPerBlock - 1) / kRowsPerBlock;
   const int n_logical = n_tiles_m * n_tiles_n;
