@@ -147,13 +147,18 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
   const long long G = p.grid;
   const long long u_first = (long long)blockIdx.x * p.units / G;
   const long long u_last = ((long long)blockIdx.x + 1) * p.units / G;
-  for (long long u = u_first; u < u_last;) {
-    const long long rbg = u / p.nt_max;  // row block over all streams
-    const int j0 = (int)(u - rbg * p.nt_max);
-    const int j1 = (int)min((long long)p.nt_max, j0 + (u_last - u));
-    const bool first_seg = u == u_first;
+  //
+  // Segments are taken last to first: a range that ends inside a row block
+  // starts with that block's first tiles, so at any moment most work-groups
+  // read the same few key tiles and share them through the L2.
+  for (long long u = u_last; u > u_first;) {
+    const long long rbg = (u - 1) / p.nt_max;  // row block over all streams
+    const long long seg0 = max(u_first, rbg * p.nt_max);
+    const int j0 = (int)(seg0 - rbg * p.nt_max);
+    const int j1 = (int)(u - rbg * p.nt_max);
+    const bool first_seg = seg0 == u_first;
     const bool whole = j0 == 0 && j1 == p.nt_max;
-    u += j1 - j0;
+    u = seg0;
     const int b = (int)(rbg / p.n_rb), rb = (int)(rbg - (long long)b * p.n_rb);
     const int row_wave = rb * F::kRowsBlock + wave * F::kRowsWave;
     __syncthreads();  // LDS of the previous segment is no longer read
