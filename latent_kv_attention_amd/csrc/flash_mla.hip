@@ -480,10 +480,17 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
           for (int i = 0; i < 4; ++i) dst[db * 16 + elg * 4 + i] = to_t<T>(o[db][mb][i] * inv);
         if (!ok && elg == 0) p.fallback_rows[atomicAdd(p.fallback_count, 1)] = b * p.Mb + row;
       } else {
+        // partial output normalised by its own sum (values of the size of
+        // the latent, so the cache's element type holds them), plus the
+        // reference and the sum in float for the merge
         const size_t prow = ((size_t)blockIdx.x * 2 + (first_seg ? 0 : 1)) * F::kRowsBlock + row - rb * F::kRowsBlock;
-        float* dst = p.part_o + prow * DC;
+        const bool ok = l <= kSumLimit;
+        const float inv = (ok && l > 0.f) ? 1.f / l : 0.f;
+        T* dst = (T*)p.part_o + prow * DC;
 #pragma unroll
-        for (int db = 0; db < F::NDB; ++db) *reinterpret_cast<f32x4*>(dst + db * 16 + elg * 4) = o[db][mb];
+        for (int db = 0; db < F::NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[db * 16 + elg * 4 + i] = to_t<T>(o[db][mb][i] * inv);
         if (elg == 0) {
           const bool empty = n_visit == 0;  // no keys: weight 0 in the merge
           p.part_l[prow * 2] = empty ? -__builtin_inff() : -negref[mb][0];
@@ -496,8 +503,9 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
 
 // Merge of the partial results of a row block shared by work-groups
 // g0..g1 (the work-groups whose unit ranges meet the row block's units
-// [a, a + nt_max)): with M = max_g r_g and w_g = 2^(r_g - M),
-// o = sum_g w_g o_g / sum_g w_g l_g. Work-group g's piece sits in its slot 0
+// [a, a + nt_max)): with M = max_g r_g and w_g = 2^(r_g - M), and each piece
+// stored as o_g / l_g, o = sum_g w_g l_g (o_g / l_g) / sum_g w_g l_g.
+// Work-group g's piece sits in its slot 0
 // when its range starts inside the row block, else in its slot 1.
 template <typename T, int DC, int RB>
 __global__ __launch_bounds__(256) void flash_combine_kernel(FlashParams p) {
@@ -531,9 +539,11 @@ __global__ __launch_bounds__(256) void flash_combine_kernel(FlashParams p) {
   if (M > -__builtin_inff()) {
     for (long long g = g0; g <= g1; ++g) {
       const size_t pr = slot_row(g);
-      const float w = fast_exp2(p.part_l[pr * 2] - M);
-      L += w * p.part_l[pr * 2 + 1];
-      acc += w * *reinterpret_cast<const f32x4*>(p.part_o + pr * DC + d);
+      const float wl = fast_exp2(p.part_l[pr * 2] - M) * p.part_l[pr * 2 + 1];
+      L += wl;
+      const T* src = (const T*)p.part_o + pr * DC + d;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += wl * to_f<T>(src[i]);
     }
   }
   const float inv = (ok && L > 0.f) ? 1.f / L : 0.f;

@@ -129,7 +129,8 @@ bool flash_plan_ok(const FlashPlan& f) {
 }
 
 // Flash workspace: the fallback row list and, when row blocks are shared,
-// two partial (output, reference, sum) slots per work-group.
+// two partial (output / sum in the cache's element type, reference and sum
+// in float) slots per work-group.
 struct FlashWs {
   size_t count, rows, part_o, part_l, total;
 };
@@ -141,7 +142,7 @@ FlashWs flash_ws_layout(const mla_shape* s, int q_n_frames, const FlashPlan& f) 
   w.count = 0;
   w.rows = w.count + 256;
   w.part_o = w.rows + round256(rows * sizeof(int));
-  w.part_l = w.part_o + round256(slots * s->d_c * sizeof(float));
+  w.part_l = w.part_o + round256(slots * s->d_c * elt_size(s));
   w.total = w.part_l + round256(slots * 2 * sizeof(float));
   return w;
 }
@@ -195,7 +196,7 @@ mla_status do_flash(const mla_shape* s, const void* q_abs, int q_n_frames, const
   char* base = (char*)ws;
   p.fallback_count = (int*)(base + w.count);
   p.fallback_rows = (int*)(base + w.rows);
-  p.part_o = f.split ? (float*)(base + w.part_o) : nullptr;
+  p.part_o = f.split ? (void*)(base + w.part_o) : nullptr;
   p.part_l = f.split ? (float*)(base + w.part_l) : nullptr;
   p.rl = rope_layout(s, rope_t_first, rope_n_t);
   p.Mb = (int)(q_n_frames * tokens_per_frame(s) * s->n_heads);

@@ -56,7 +56,8 @@ struct FlashParams {
   const int32_t* slot_frame;
   const float* tables;
   void* o_lat;             // [B][Mb][d_c]
-  float* part_o;           // [G][2][rows per block][d_c] partial outputs (split row blocks only)
+  void* part_o;            // [G][2][rows per block][d_c] partial outputs o_g / l_g, element type of the
+                           // cache (split row blocks only)
   float* part_l;           // [G][2][rows per block][2] (reference, sum)
   int* fallback_count;     // rows listed for the exact fallback
   int* fallback_rows;      // [B * Mb]
