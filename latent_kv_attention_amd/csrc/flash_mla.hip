@@ -71,7 +71,7 @@ struct FlashTile {
   static constexpr bool kBf16 = sizeof(T) == 2;
   static constexpr int kWaves = kBf16 ? 8 : 4;
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kBN = kBf16 ? 64 : 32;           // keys per tile
+  static constexpr int kBN = kBf16 ? 128 : 32;          // keys per tile
   static constexpr int kNMB = 2;                        // 16-row blocks per wave
   static constexpr int kRowsWave = kNMB * 16;
   static constexpr int kRowsBlock = kWaves * kRowsWave;
@@ -247,8 +247,8 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     // ragged), positions 1.. the others in order
     auto tile_of = [&](int pos) { return pos == 0 ? tile_end - 1 : tile_begin + pos - 1; };
     auto describe = [&](int pos, int4* tab) {
-      if (wave == 0) {
-        const int ln = opaque(lane);
+      if (wave < (kBN + 63) / 64) {
+        const int ln = opaque(lane) + wave * 64;
         const int v = min(tile_of(pos) * kBN + ln, n_keys - 1);
         const int rank = div_floor(v, p.T, p.inv_T), tok = v - rank * p.T;
         const int y = div_floor(tok, p.grid_x, p.inv_grid_x);

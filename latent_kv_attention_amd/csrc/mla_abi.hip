@@ -84,7 +84,7 @@ size_t table_floats(const mla_shape* s, int n_t) {
 size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
 int flash_rows_per_block(const mla_shape* s) { return s->dtype == MLA_BF16 ? 256 : 128; }
-int flash_tile_keys(const mla_shape* s) { return s->dtype == MLA_BF16 ? 64 : 32; }
+int flash_tile_keys(const mla_shape* s) { return s->dtype == MLA_BF16 ? 128 : 32; }
 
 // Compute units of the current device (the automatic work split uses one
 // work-group per compute unit); falls back to the MI355X count.
