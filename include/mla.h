@@ -173,8 +173,16 @@ mla_status mla_absorb_q(const mla_shape* shape, const void* q_nope, const void* 
  *   o_lat (device) [B][N_q][H][d_c], dtype.
  *   workspace (device) of at least mla_flash_workspace_bytes(shape,
  *   q_n_frames, kv_splits) bytes; its contents on entry do not matter.
- *   kv_splits: number of key-range partitions per row block combined by a
- *   log-sum-exp pass; 0 chooses automatically; at most 16. */
+ *   kv_splits: how the (row block, key tile) work is split between
+ *   work-groups. 0 (recommended): one work-group per compute unit of the
+ *   current device, each taking an equal share; row blocks shared by
+ *   several work-groups are finished by a merge pass over their partial
+ *   (output, reference, sum). s in 1..16: every row block gets s equal key
+ *   ranges (1 = no merge). The result is the same up to rounding. With 0
+ *   the workspace size depends on the compute-unit count of the current
+ *   device: query it with the device that will run the call current.
+ *   Returns MLA_ERR_SHAPE if the work grid is too large to index
+ *   (more than 2^40 units). */
 size_t mla_flash_workspace_bytes(const mla_shape* shape, int32_t q_n_frames, int32_t kv_splits);
 mla_status mla_flash_attend(const mla_shape* shape, const void* q_abs, int32_t q_n_frames, const void* cache,
                             const int32_t* slot_frame, const float* rope_tables, int32_t rope_t_first,
