@@ -88,5 +88,41 @@ def oracle_step_rows(cfg, w, stream_frames_x: dict, window_frames, q_nope, q_r, 
     return O.attend(q_nope[rows], q_rope, k_nope, k_rope, v, O.default_scale(cfg.d_head, cfg.d_rope))
 
 
+class LatentMemo:
+    """Oracle latents (c, kR) of one stream's frames under one layer's weights,
+    computed once per frame and reused across chunks."""
+
+    def __init__(self, cfg, w, stream: Stream):
+        self.cfg, self.w, self.stream, self.memo = cfg, w, stream, {}
+
+    def get(self, f):
+        if f not in self.memo:
+            self.memo[f] = O.latents(self.stream.x(f), self.w["w_dkv"], self.w["w_kr"])
+        return self.memo[f]
+
+
+def oracle_rows_memo(cfg, w, memo: LatentMemo, window_frames, q_nope, q_r, q_frame_first, rows):
+    """oracle_step_rows with the window's latents taken from a LatentMemo."""
+    window_frames = list(window_frames)
+    c = np.concatenate([memo.get(f)[0] for f in window_frames])
+    kr = np.concatenate([memo.get(f)[1] for f in window_frames])
+    t, y, x = O.frame_positions(window_frames, cfg.grid_y, cfg.grid_x)
+    k_nope, v = O.reconstruct(c, w["w_uk"], w["w_uv"])
+    k_rope = O.rope3d(kr, t, y, x, cfg.rope_split, cfg.rope_base)
+    nq = q_nope.shape[0]
+    tq, yq, xq = O.frame_positions(q_frame_first + np.arange(nq // cfg.tokens_per_frame), cfg.grid_y, cfg.grid_x)
+    q_rope = O.rope3d(q_r[rows], tq[rows], yq[rows], xq[rows], cfg.rope_split, cfg.rope_base)
+    return O.attend(q_nope[rows], q_rope, k_nope, k_rope, v, O.default_scale(cfg.d_head, cfg.d_rope))
+
+
+def sample_rows(cfg, n, seed):
+    """n query rows of a chunk: first/last, frame and 128-key-tile boundaries, random rest."""
+    T, nq = cfg.tokens_per_frame, cfg.chunk_frames * cfg.tokens_per_frame
+    edge = [r for r in (0, 1, 10, 11, 21, 22, T - 1, T, nq // 2, nq - 22, nq - 1) if r < nq]
+    rng = np.random.default_rng(seed)
+    rest = rng.choice(nq, max(0, n - len(edge)), replace=False)
+    return np.unique(np.concatenate([edge, rest]).astype(np.int64))
+
+
 __all__ = ["errors", "assert_step_close", "assert_rounded_close", "Stream", "device_weights", "oracle_step_rows",
-           "to_numpy", "to_torch"]
+           "LatentMemo", "oracle_rows_memo", "sample_rows", "to_numpy", "to_torch"]

@@ -16,7 +16,7 @@ from harness import get_config, round_to
 from oracle import mla_oracle as O
 
 from .gpu_common import (Stream, assert_rounded_close, assert_step_close, device_weights, oracle_step_rows,
-                         to_numpy, to_torch)
+                         to_numpy, to_torch, LatentMemo, oracle_rows_memo, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -329,3 +329,80 @@ def test_wan_full_size_sampled_rows():
     xs = {f: st.x(f) for f in range(21)}
     ref = oracle_step_rows(cfg, w, xs, list(range(21)), qn, qr, 18, rows)
     assert_step_close(got[rows], ref, cfg.dtype, label="wan full size, sampled rows")
+
+
+def test_wan_window_fill_over_chunks_and_layers():
+    """Thirty-layer chunk step shape: each layer has its own weights and ring;
+    chunk k writes frames 3k..3k+2 and attends over frames 0..3k+2 (window
+    filling 3 -> 21 frames over 7 chunks). Checked: layer 0 at every chunk,
+    layers 1 and 29 at the first and last chunk, sampled rows (all heads)."""
+    cfg = get_config("wan_fill30")
+    checks = {0: range(7), 1: (0, 6), 29: (0, 6)}
+    for layer_id, chunks in checks.items():
+        w, wd = device_weights(cfg, seed=3, layer=layer_id)
+        st = Stream(cfg, seed=3, layer=layer_id, pooled=True)
+        memo = LatentMemo(cfg, w, st)
+        layer = LatentLayer(cfg, wd, batch=1, rope_n_t=64)
+        for k in range(max(chunks) + 1):
+            f0 = 3 * k
+            layer.write(to_torch(st.xs(f0, 3)[None], cfg.dtype), f0, 3)
+            qn, qr = st.q(f0)
+            out = layer.attend(to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype), f0, 3)
+            _sync()
+            if k not in chunks:
+                continue
+            rows = sample_rows(cfg, 24, seed=100 * layer_id + k)
+            ref = oracle_rows_memo(cfg, w, memo, range(f0 + 3), qn, qr, f0, rows)
+            assert_step_close(to_numpy(out)[0][rows], ref, cfg.dtype, label=f"fill layer {layer_id} chunk {k}")
+
+
+def test_wan_batch8_streams_full_windows():
+    """Eight independent streams in one call, each with its own full 21-frame
+    window: 1760 row blocks over one work-group per compute unit, so
+    work-group ranges cross stream boundaries. Sampled rows of every stream."""
+    cfg = get_config("wan_batch8")
+    B = cfg.batch
+    w, wd = device_weights(cfg, seed=4)
+    streams = [Stream(cfg, seed=4, stream=s, pooled=True) for s in range(B)]
+    layer = LatentLayer(cfg, wd, batch=B, rope_n_t=64)
+    for f0 in range(0, 21, 3):  # three frames of all streams per write (bounded host memory)
+        layer.write(to_torch(np.stack([s.xs(f0, 3) for s in streams]), cfg.dtype), f0, 3)
+    qs = [s.q(18) for s in streams]
+    out = layer.attend(to_torch(np.stack([q[0] for q in qs]), cfg.dtype),
+                       to_torch(np.stack([q[1] for q in qs]), cfg.dtype), 18, 3)
+    _sync()
+    got = to_numpy(out)
+    sf = layer.slot_frame.cpu().numpy()
+    assert (sf == np.arange(21)[None, :]).all()
+    for b in range(B):
+        rows = sample_rows(cfg, 12, seed=b)
+        memo = LatentMemo(cfg, w, streams[b])
+        ref = oracle_rows_memo(cfg, w, memo, range(21), qs[b][0], qs[b][1], 18, rows)
+        assert_step_close(got[b][rows], ref, cfg.dtype, label=f"batch8 stream {b}")
+
+
+def test_wan_rollout_80_chunks_ring_eviction():
+    """Minute-scale rollout shape: 80 successive 3-frame chunks (frames
+    0..239) through a 21-frame ring. Checked at the last chunk before the
+    ring wraps, the first chunk that evicts, a middle chunk and the last
+    chunk (frames 219..239, t up to 239), sampled rows; the slot table is
+    checked after every chunk."""
+    cfg = get_config("wan_rollout")
+    W = cfg.window_frames
+    w, wd = device_weights(cfg, seed=5)
+    st = Stream(cfg, seed=5, pooled=True)
+    memo = LatentMemo(cfg, w, st)
+    layer = LatentLayer(cfg, wd, batch=1, rope_n_t=256)
+    checks = (6, 7, 40, 79)
+    for k in range(80):
+        f0 = 3 * k
+        layer.write(to_torch(st.xs(f0, 3)[None], cfg.dtype), f0, 3)
+        qn, qr = st.q(f0)
+        out = layer.attend(to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype), f0, 3)
+        _sync()
+        held = sorted(f for f in range(max(0, f0 + 3 - W), f0 + 3))
+        assert sorted(layer.slot_frame.cpu().numpy()[0].tolist()) == sorted(held + [-1] * (W - len(held)))
+        if k in checks:
+            rows = sample_rows(cfg, 24, seed=k)
+            ref = oracle_rows_memo(cfg, w, memo, held, qn, qr, f0, rows)
+            assert_step_close(to_numpy(out)[0][rows], ref, cfg.dtype, label=f"rollout chunk {k}")
