@@ -505,52 +505,77 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
 // g0..g1 (the work-groups whose unit ranges meet the row block's units
 // [a, a + nt_max)): with M = max_g r_g and w_g = 2^(r_g - M), and each piece
 // stored as o_g / l_g, o = sum_g w_g l_g (o_g / l_g) / sum_g w_g l_g.
-// Work-group g's piece sits in its slot 0
-// when its range starts inside the row block, else in its slot 1.
+// Work-group g's piece sits in its slot 0 when its range starts inside the
+// row block, else in its slot 1. A work-group takes kMergeRows rows of one
+// row block: the piece bookkeeping is computed once (uniform), then threads
+// sweep (row, 16-byte chunk) pairs.
+constexpr int kMergeRows = 32;
+
 template <typename T, int DC, int RB>
 __global__ __launch_bounds__(256) void flash_combine_kernel(FlashParams p) {
-  constexpr int D4 = DC / 4;
-  const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long n_rows = (long long)p.batch * p.Mb;
-  if (e >= n_rows * D4) return;
-  const long long r = e / D4;
-  const int d = (int)(e % D4) * 4;
-  const int b = (int)(r / p.Mb), row = (int)(r - (long long)b * p.Mb);
-  const int rb = row / RB, local = row - rb * RB;
+  constexpr int CH = 16 / sizeof(T);  // values per 16-byte chunk
+  constexpr int NCH = DC / CH;
+  typedef typename std::conditional<sizeof(T) == 2, u32x4, f32x4>::type chunk_t;
+  __shared__ long long slot_base[kMaxMergePieces];  // first partial row of each piece
   const long long G = p.grid;
-  const long long a = ((long long)b * p.n_rb + rb) * p.nt_max;
+  const long long rbg = blockIdx.x / (RB / kMergeRows);
+  const int row_lo = (int)(blockIdx.x % (RB / kMergeRows)) * kMergeRows;
+  const long long a = rbg * p.nt_max;
   // largest g whose range starts at or before unit x
   auto owner = [&](long long x) { return ((x + 1) * G - 1) / p.units; };
   const long long g0 = owner(a), g1 = owner(a + p.nt_max - 1);
   if (g0 == g1) return;  // one work-group covered the row block and wrote it
-  auto slot_row = [&](long long g) {
+  const int np = (int)(g1 - g0 + 1);  // <= kMaxMergePieces by the host's cap on G
+  if ((int)threadIdx.x < np) {
+    const long long g = g0 + threadIdx.x;
     const long long start = g * p.units / G;
-    return (size_t)((g * 2 + (start >= a ? 0 : 1)) * RB + local);
-  };
-  float M = -__builtin_inff();
-  bool ok = true;
-  for (long long g = g0; g <= g1; ++g) {
-    const size_t pr = slot_row(g);
-    M = fmaxf(M, p.part_l[pr * 2]);
-    ok = ok && (p.part_l[pr * 2 + 1] <= kSumLimit);
+    slot_base[threadIdx.x] = (g * 2 + (start >= a ? 0 : 1)) * RB;
   }
-  float L = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (M > -__builtin_inff()) {
-    for (long long g = g0; g <= g1; ++g) {
-      const size_t pr = slot_row(g);
-      const float wl = fast_exp2(p.part_l[pr * 2] - M) * p.part_l[pr * 2 + 1];
-      L += wl;
-      const T* src = (const T*)p.part_o + pr * DC + d;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += wl * to_f<T>(src[i]);
+  __syncthreads();
+  const int b = (int)(rbg / p.n_rb), rb = (int)(rbg - (long long)b * p.n_rb);
+  const int rows = min(kMergeRows, p.Mb - rb * RB - row_lo);
+  for (int e = threadIdx.x; e < rows * NCH; e += blockDim.x) {
+    const int local = row_lo + e / NCH, c0 = (e % NCH) * CH;
+    float M = -__builtin_inff();
+    bool ok = true;
+    for (int k = 0; k < np; ++k) {
+      const size_t pr = (size_t)slot_base[k] + local;
+      M = fmaxf(M, p.part_l[pr * 2]);
+      ok = ok && (p.part_l[pr * 2 + 1] <= kSumLimit);
     }
-  }
-  const float inv = (ok && L > 0.f) ? 1.f / L : 0.f;
-  T* dst = (T*)p.o_lat + (size_t)r * DC + d;
+    float L = 0.f, acc[CH] = {};
+    if (M > -__builtin_inff()) {
+      for (int k = 0; k < np; ++k) {
+        const size_t pr = (size_t)slot_base[k] + local;
+        const float wl = fast_exp2(p.part_l[pr * 2] - M) * p.part_l[pr * 2 + 1];
+        L += wl;
+        const chunk_t raw = *reinterpret_cast<const chunk_t*>((const T*)p.part_o + pr * DC + c0);
+        float v[CH];
+        if constexpr (sizeof(T) == 2) {
+          unpack8<T>(__builtin_bit_cast(typename V8<T>::type, raw), v);
+        } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dst[i] = to_t<T>(acc[i] * inv);
-  if (!ok && d == 0) p.fallback_rows[atomicAdd(p.fallback_count, 1)] = (int)r;
+          for (int i = 0; i < CH; ++i) v[i] = raw[i];
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) acc[i] += wl * v[i];
+      }
+    }
+    const float inv = (ok && L > 0.f) ? 1.f / L : 0.f;
+    const size_t r = (size_t)b * p.Mb + rb * RB + local;
+    chunk_t out;
+    if constexpr (sizeof(T) == 2) {
+      float f[CH];
+#pragma unroll
+      for (int i = 0; i < CH; ++i) f[i] = acc[i] * inv;
+      out = __builtin_bit_cast(chunk_t, pack8<T>(f));
+    } else {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) out[i] = acc[i] * inv;
+    }
+    *reinterpret_cast<chunk_t*>((T*)p.o_lat + r * DC + c0) = out;
+    if (!ok && c0 == 0) p.fallback_rows[atomicAdd(p.fallback_count, 1)] = (int)r;
+  }
 }
 
 // ---------------------------------------------------------------- exact fallback
@@ -646,9 +671,9 @@ static hipError_t launch_flash_t(const FlashParams& p, bool split, hipStream_t s
   hipLaunchKernelGGL((flash_mla_kernel<T, DC, DR>), dim3(p.grid), dim3(F::kThreads), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (split) {
-    const long long total = (long long)p.batch * p.Mb * (DC / 4);
-    const int blocks = (int)((total + 255) / 256);
-    hipLaunchKernelGGL((flash_combine_kernel<T, DC, F::kRowsBlock>), dim3(blocks), dim3(256), 0, s, p);
+    static_assert(F::kRowsBlock % kMergeRows == 0, "merge groups tile a row block");
+    hipLaunchKernelGGL((flash_combine_kernel<T, DC, F::kRowsBlock>),
+                       dim3(p.batch * p.n_rb * (F::kRowsBlock / kMergeRows)), dim3(256), 0, s, p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   hipLaunchKernelGGL((flash_exact_kernel<T, DC, DR>), dim3(kFallbackBlocks), dim3(256), 0, s, p);

@@ -114,8 +114,11 @@ FlashPlan flash_plan(const mla_shape* s, int q_n_frames, int kv_splits) {
   f.n_rb = (int)((Mb + rpb - 1) / rpb);
   f.nt_max = (int)((s->window_frames * tokens_per_frame(s) + tk - 1) / tk);
   f.units = (int64_t)s->batch * f.n_rb * f.nt_max;
-  int64_t g = kv_splits > 0 ? (int64_t)s->batch * f.n_rb * kv_splits : device_cus();
+  const int64_t row_blocks = (int64_t)s->batch * f.n_rb;
+  int64_t g = kv_splits > 0 ? row_blocks * kv_splits : device_cus();
   if (g > f.units) g = f.units;
+  // a row block meets fewer than units/(units/G) + 1 ranges: keep that <= kMaxMergePieces
+  if (g > (mla::kMaxMergePieces - 1) * row_blocks) g = (mla::kMaxMergePieces - 1) * row_blocks;
   if (g < 1) g = 1;
   if (g > (INT64_C(1) << 23)) g = INT64_C(1) << 23;  // rejected by flash_plan_ok
   f.grid = (int)g;

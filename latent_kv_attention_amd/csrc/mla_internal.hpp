@@ -72,6 +72,10 @@ struct FlashParams {
 };
 
 constexpr int kFallbackBlocks = 64;
+// At most this many work-groups share one row block of the attention kernel
+// (the host caps its work-group count at (kMaxMergePieces - 1) row blocks'
+// worth, which bounds the pieces of a row block by kMaxMergePieces).
+constexpr int kMaxMergePieces = 64;
 // Limits of the attention kernel: keys per window (index arithmetic in
 // float) and (cos, sin) entries of the window's RoPE rows kept in LDS
 // (window_frames * d_rope_t/2 + grid_y * d_rope_y/2 + grid_x * d_rope_x/2).

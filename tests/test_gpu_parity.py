@@ -193,6 +193,17 @@ def test_flash_attend(name, kv_splits):
     assert_step_close(got, ref, cfg.dtype, label=f"{name} flash splits={kv_splits}")
 
 
+def test_flash_attend_one_row_block_long_window():
+    """One head, one 16x16 frame of queries (256 rows = one row block) over a
+    64-frame window (16384 keys, 128 tiles): the automatic split caps the
+    work-groups at 63 per row block, so the merge combines up to 64 pieces."""
+    cfg = get_config("wan_small").with_(n_heads=1, grid_y=16, grid_x=16, window_frames=64, chunk_frames=1)
+    cache, sf, q_abs, ref = _flash_inputs(cfg, 9, list(range(64)), 63)
+    for splits in (0, 16):
+        got = _run_flash(cfg, cache, sf, q_abs, splits, n_t=64)
+        assert_step_close(got, ref, cfg.dtype, label=f"one row block, 128 tiles, splits={splits}")
+
+
 @pytest.mark.parametrize("name", ["wan_small", "wan_small_f32"])
 def test_flash_attend_sharp_and_partial_window(name):
     cfg = get_config(name)
