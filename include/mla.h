@@ -40,10 +40,8 @@
  *   - Supported latent widths (d_c, d_rope): (192, 32) and (16, 8), either
  *     dtype. d_head must be a multiple of 8 and at most 256; hidden a
  *     multiple of 8; window_frames at most 64; each RoPE axis width even;
- *     window_frames * grid_y * grid_x at most 2^22 keys; and
- *     window_frames * d_rope_t/2 + grid_y * d_rope_y/2 + grid_x * d_rope_x/2
- *     at most 2048 (RoPE rows of one window held on chip). Shapes outside
- *     these limits return MLA_ERR_SHAPE.
+ *     and window_frames * grid_y * grid_x at most 2^22 keys. Shapes
+ *     outside these limits return MLA_ERR_SHAPE.
  *
  * Token positions: a frame has grid_y * grid_x tokens in row-major order;
  * token k of frame f sits at (t, y, x) = (f, k / grid_x, k % grid_x).
@@ -172,7 +170,10 @@ mla_status mla_absorb_q(const mla_shape* shape, const void* q_nope, const void* 
  *   are read from the clamped table row, a wrong but memory-safe result).
  *   o_lat (device) [B][N_q][H][d_c], dtype.
  *   workspace (device) of at least mla_flash_workspace_bytes(shape,
- *   q_n_frames, kv_splits) bytes; its contents on entry do not matter.
+ *   q_n_frames, kv_splits) bytes; its contents on entry do not matter. The
+ *   call keeps there the window's positional keys after 3D-RoPE (rotated
+ *   once per call, d_rope values per key), the list of rows for the exact
+ *   fallback and, when row blocks are shared, the partial results.
  *   kv_splits: how the (row block, key tile) work is split between
  *   work-groups. 0 (recommended): one work-group per compute unit of the
  *   current device, each taking an equal share; row blocks shared by

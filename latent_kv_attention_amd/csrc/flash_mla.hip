@@ -27,11 +27,14 @@
 //     keys); a work-group owns 256 rows in 8 waves of 32 rows (two 16-row
 //     blocks), two waves per SIMD, so one wave's exp2 work overlaps the
 //     other's matrix products; queries stay in registers for the key loop;
-//   * keys stream in 64-key tiles through LDS, double-buffered, one barrier
-//     per tile. The latent part goes global -> LDS directly (no registers);
-//     the kR part goes through registers and is rotated by 3D-RoPE on its way
-//     into LDS. LDS rows are 480 bytes apart, which keeps both LDS read
-//     patterns below free of bank conflicts;
+//   * the window's positional keys are rotated by 3D-RoPE once per call
+//     (rope_window_kernel, into the workspace, in key order), not once per
+//     work-group that visits them: every row block visits every key;
+//   * keys stream in 128-key tiles through LDS, double-buffered, one barrier
+//     per tile. Both parts go global -> LDS directly (no registers): the
+//     latent into rows 480 bytes apart, which keeps both LDS read patterns
+//     below free of bank conflicts, the rotated kR into a packed region
+//     whose 16-byte units are XOR-swizzled by key for the same reason;
 //   * scores are formed transposed, S^T = K Q^T (keys as rows), so a lane
 //     holds 4 keys of one query row and the probabilities already sit in the
 //     lane layout of the B operand of O^T = C^T P^T. The C^T operand is read
@@ -62,7 +65,7 @@ __device__ __forceinline__ int opaque(int x) {
 constexpr float kSumLimit = 1.2676506e30f;  // 2^100
 }  // namespace
 
-// bf16: 8 waves x 32 rows (two waves per SIMD) and 64-key tiles; float
+// bf16: 8 waves x 32 rows (two waves per SIMD) and 128-key tiles; float
 // operands are twice as wide, so float runs 4 waves x 32 rows with 32-key
 // tiles (it exists for the fp32 configurations, where precision rather than
 // speed is the point).
@@ -81,28 +84,63 @@ struct FlashTile {
   static constexpr int NKC = KP / 32;
   static constexpr int NDB = DC / 16;
   static constexpr int CB = 16 / sizeof(T);             // elements per 16-byte chunk
+  // Latent region of a tile buffer: one row of LS elements per key, the d_c
+  // latent values then padding (a 480-byte stride for bf16 keeps both operand
+  // read patterns free of bank conflicts).
   static constexpr int LS = kBf16 ? KP + 16 : KP + CB;  // LDS row stride (elements)
   static constexpr int CPR = LS / CB;                   // 16-byte chunks per LDS row
   static constexpr int CC = DC / CB;                    // latent chunks per key
-  static constexpr int RC = DR / CB;                    // kR chunks per key
-  static constexpr int PADC = (KP - DK) / CB;           // zero chunks read by QK
   static constexpr int TILE_CHUNKS = kBN * CPR;
   static constexpr int N_INSTR = (TILE_CHUNKS + 63) / 64;  // direct-load instructions per tile
   static constexpr int N_INSTR_WAVE = (N_INSTR + kWaves - 1) / kWaves;
   static constexpr int TILE_ELEMS = N_INSTR * 64 * CB;  // LDS elements per buffer (whole instructions)
-  // kR rotation: RP pairs (RU elements) per thread, at most one unit per thread
-  static constexpr int RP0 = kBN * DR / 2 / kThreads;
-  static constexpr int RP = RP0 < 1 ? 1 : RP0;
-  static constexpr int RU = 2 * RP;                     // kR elements rotated per thread
-  static constexpr int NU = DR / RU;                    // rotation units per key
-  static constexpr int RCH = kBN * NU;                  // rotation units per tile
-  static constexpr int RW = RU * (int)sizeof(T) / 4;    // 32-bit words per unit
-  static_assert(DR % RU == 0 && RCH <= kThreads && (RW == 1 || RW == 2 || RW == 4), "one rotation unit per thread");
+  // Rotated-kR region: DR elements per key, no padding, in units of 8
+  // elements (the S^T read granularity) whose order within a key is
+  // XOR-swizzled by the key index.
+  static constexpr int U8 = DR / 8;                     // 8-element units per key
+  static constexpr int CPU = 8 * (int)sizeof(T) / 16;   // 16-byte chunks per unit
+  static constexpr int RCK = U8 * CPU;                  // 16-byte chunks per key
+  static constexpr int KR_ELEMS = kBN * DR;
+  static constexpr int KR_INSTR = (kBN * RCK + 63) / 64;
+  static constexpr int KR_INSTR_WAVE = (KR_INSTR + kWaves - 1) / kWaves;
+  // unit slot of unit u of tile key n (an involution in u): with four units
+  // per key the 16 keys of one S^T read land in 16 different bank groups
+  __host__ __device__ static constexpr int kr_slot(int n, int u) { return U8 == 4 ? (u ^ ((n >> 2) & 3)) : u; }
+  static_assert(DC % 8 == 0 && DR % 8 == 0, "latent and kR split into 8-element units");
   static_assert(LS % 4 == 0 && (LS * sizeof(T)) % 16 == 0, "LDS rows must stay 16-byte aligned");
 };
 
 // Clears the count of rows handed to the exact fallback.
 __global__ void flash_prep_kernel(FlashParams p) { *p.fallback_count = 0; }
+
+// 3D-RoPE of the window's positional keys, once per call: key v = (slot
+// rank r, token tok) of stream b gets R(t, y, x) kR, with t the frame held
+// by the r-th valid slot and (y, x) the token's grid cell, rounded to the
+// cache's element type. Row v of the stream's block of p.krot. One thread per
+// rotary pair; grid (pair blocks, slots, stream groups).
+template <typename T, int DC, int DR>
+__global__ __launch_bounds__(256) void rope_window_kernel(FlashParams p) {
+  constexpr int NP = DR / 2;
+  const int slot = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= p.T * NP) return;
+  const int tok = e / NP, k = e - tok * NP;
+  const int y = tok / p.grid_x, x = tok - y * p.grid_x;
+  for (int b = blockIdx.z; b < p.batch; b += gridDim.z) {
+    const int32_t* sf = p.slot_frame + (size_t)b * p.W;
+    const int f = sf[slot];
+    if (f < 0) continue;
+    int rank = 0;
+    for (int j = 0; j < slot; ++j) rank += sf[j] >= 0 ? 1 : 0;
+    const T* src = (const T*)p.cache + (((size_t)b * p.W + slot) * p.T + tok) * (DC + DR) + DC + 2 * k;
+    float a0 = to_f<T>(src[0]), a1 = to_f<T>(src[1]), cs, sn;
+    rope_cos_sin(p.rl, p.tables, k, f, y, x, cs, sn);
+    rotate_pair(a0, a1, cs, sn);
+    T* dst = (T*)p.krot + ((size_t)b * p.W * p.T + (size_t)rank * p.T + tok) * DR + 2 * k;
+    dst[0] = to_t<T>(a0);
+    dst[1] = to_t<T>(a1);
+  }
+}
 
 // ---------------------------------------------------------------- main kernel
 template <typename T, int DC, int DR>
@@ -117,11 +155,11 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
   // into the other buffer, and does not wait for the prefetch before reading.
   __shared__ __attribute__((aligned(16))) T kv0[F::TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) T kv1[F::TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) T kr0[F::KR_ELEMS];
+  __shared__ __attribute__((aligned(16))) T kr1[F::KR_ELEMS];
   __shared__ int slot_of[kMaxSlots];
-  __shared__ int frame_of[kMaxSlots];
   __shared__ int n_valid_sh;
-  __shared__ int4 keytab[2][kBN];         // per key of a tile: {row byte offset, slot rank, y, x}
-  __shared__ f32x2 rcs[kRopeLdsEntries];  // (cos, sin): t rows by slot rank, then y rows, then x rows
+  __shared__ int keytab[2][kBN];  // per key of a tile: byte offset of its cache row
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -137,6 +175,19 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     const int pos = instr * 64 + lane;
     const int n = pos / F::CPR, c = pos - n * F::CPR;
     lat_pk[k] = (instr < F::N_INSTR && n < kBN && c < F::CC) ? (n << 16) | (c * 16) : -1;
+  }
+  // Rotated-kR slots: instruction k of the wave fills chunks [64 i, 64 i + 64)
+  // of the kR region, i = wave + kWaves k; the lane's chunk holds unit slot
+  // us of key n, i.e. unit kr_slot(n, us) of the key's row in the rotated
+  // buffer. Packed as (n << 16) | (byte offset in that row), or -1.
+  int kr_pk[F::KR_INSTR_WAVE];
+#pragma unroll
+  for (int k = 0; k < F::KR_INSTR_WAVE; ++k) {
+    const int instr = wave + kWaves * k;
+    const int q = instr * 64 + lane;
+    const int n = q / F::RCK, cs = q - n * F::RCK;
+    const int us = cs / F::CPU, ci = cs - us * F::CPU;
+    kr_pk[k] = (instr < F::KR_INSTR && n < kBN) ? (n << 16) | ((F::kr_slot(n, us) * F::CPU + ci) * 16) : -1;
   }
 
   // Work-group g takes units [g U / G, (g + 1) U / G) of the (row block, key
@@ -167,36 +218,10 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     if (wave == 0) {
       const int f = lane < p.W ? p.slot_frame[b * p.W + lane] : -1;
       const unsigned long long mask = __ballot(f >= 0);
-      if (f >= 0) {
-        const int rank = __popcll(mask & ((1ull << lane) - 1ull));
-        slot_of[rank] = lane;
-        frame_of[rank] = f;
-      }
+      if (f >= 0) slot_of[__popcll(mask & ((1ull << lane) - 1ull))] = lane;
       if (lane == 0) n_valid_sh = __popcll(mask);
     }
     __syncthreads();
-
-    // (cos, sin) of every rotary pair the window's keys need, from the global
-    // tables: t by slot rank (frames clamped into the table range), y, x
-    const int pt = p.rl.d_t / 2, py = p.rl.d_y / 2, px = p.rl.d_x / 2;
-    const int y_base = n_valid_sh * pt, x_base = y_base + p.grid_y * py;
-    for (int e = tid; e < x_base + p.grid_x * px; e += F::kThreads) {
-      int oc, os;
-      if (e < y_base) {
-        const int r = e / pt, j = e - r * pt;
-        int tt = frame_of[r] - p.rl.t_first;
-        tt = tt < 0 ? 0 : (tt >= p.rl.n_t ? p.rl.n_t - 1 : tt);
-        oc = p.rl.off_ct + tt * pt + j;
-        os = p.rl.off_st + tt * pt + j;
-      } else if (e < x_base) {
-        oc = p.rl.off_cy + e - y_base;
-        os = p.rl.off_sy + e - y_base;
-      } else {
-        oc = p.rl.off_cx + e - x_base;
-        os = p.rl.off_sx + e - x_base;
-      }
-      rcs[e] = f32x2{p.tables[oc], p.tables[os]};
-    }
 
     const int n_keys = n_valid_sh * p.T;
     const int n_tiles = (n_keys + kBN - 1) / kBN;
@@ -232,8 +257,11 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     // stream base (uniform); per-key byte offsets fit 32 bits because a window
     // holds at most 2^22 keys of at most 224 elements of at most 4 bytes
     const char* cache_b = (const char*)p.cache + (size_t)b * p.W * p.T * F::DK * sizeof(T);
+    // rotated kR of the stream's window, one row of DR elements per key in
+    // key order (slot rank major)
+    const char* krot_b = (const char*)p.krot + (size_t)b * p.W * p.T * DR * sizeof(T);
 
-    // Per-tile key descriptors {row byte offset, slot rank, y, x}, written one
+    // Per-tile key descriptors (byte offset of the key's cache row), written one
     // tile ahead by wave 0 into a ping-pong table, so the address of
     // every load below is one LDS read plus an add. Keys past the end of the
     // window alias the last key (their scores are masked). Quotients come
@@ -246,114 +274,66 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     // position 0 visits the last tile of the range (the one that can be
     // ragged), positions 1.. the others in order
     auto tile_of = [&](int pos) { return pos == 0 ? tile_end - 1 : tile_begin + pos - 1; };
-    auto describe = [&](int pos, int4* tab) {
+    auto describe = [&](int pos, int* tab) {
       if (wave < (kBN + 63) / 64) {
         const int ln = opaque(lane) + wave * 64;
         const int v = min(tile_of(pos) * kBN + ln, n_keys - 1);
         const int rank = div_floor(v, p.T, p.inv_T), tok = v - rank * p.T;
-        const int y = div_floor(tok, p.grid_x, p.inv_grid_x);
-        if (ln < kBN)
-          tab[ln] = int4{(slot_of[rank] * p.T + tok) * F::DK * (int)sizeof(T), rank, y, tok - y * p.grid_x};
+        if (ln < kBN) tab[ln] = (slot_of[rank] * p.T + tok) * F::DK * (int)sizeof(T);
       }
     };
 
     // ---- latent part: global -> LDS, lane order = LDS order (no registers)
-    auto issue_latent = [&](const int4* tab, T* buf) {
+    auto issue_latent = [&](const int* tab, T* buf) {
 #pragma unroll
       for (int k = 0; k < F::N_INSTR_WAVE; ++k) {
         const int instr = wave + kWaves * k;
         const int pk = opaque(lat_pk[k]);
         if (instr < F::N_INSTR && pk >= 0) {
-          const char* src = cache_b + (unsigned)(tab[pk >> 16].x + (pk & 0xffff));
+          const char* src = cache_b + (unsigned)(tab[pk >> 16] + (pk & 0xffff));
           __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                            (MLA_LDS void*)(MLA_LDS T*)(buf + instr * 64 * F::CB), 16, 0, 0);
         }
       }
     };
 
-    // ---- kR part: RP rotary pairs per thread via registers, rotated with the
-    // LDS (cos, sin) rows on their way into LDS
-    typedef typename std::conditional<F::RW == 1, uint32_t,
-                                      typename std::conditional<F::RW == 2, u32x2, u32x4>::type>::type ru_t;
-    ru_t st_r = {};
-    auto word = [&](const ru_t& v, int k) -> uint32_t {
-      if constexpr (F::RW == 1) return v;
-      else return v[k];
-    };
-    auto fetch_rope = [&](const int4* tab) {
-      const int t2 = opaque(tid);
-      const int r_key = t2 / F::NU, r_unit = t2 % F::NU;
-      if (t2 < F::RCH)
-        st_r = *reinterpret_cast<const ru_t*>(cache_b + (unsigned)(tab[r_key].x + (DC + r_unit * F::RU) *
-                                                                                    (int)sizeof(T)));
-    };
-    auto stash_rope = [&](const int4* tab, T* buf) {
-      const int t2 = opaque(tid);
-      const int r_key = t2 / F::NU, r_unit = t2 % F::NU;
-      if (t2 < F::RCH) {
-        const int4 d = tab[r_key];
-        float f[F::RU];
-        if constexpr (sizeof(T) == 2) {
+    // ---- rotated kR part: the tile's keys are consecutive rows of the
+    // rotated buffer (keys past the end of the window alias the last key)
+    auto issue_rope = [&](int kbase, T* buf) {
 #pragma unroll
-          for (int k = 0; k < F::RW; ++k) {
-            f[2 * k] = __uint_as_float(word(st_r, k) << 16);
-            f[2 * k + 1] = __uint_as_float(word(st_r, k) & 0xffff0000u);
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < F::RW; ++k) f[k] = __uint_as_float(word(st_r, k));
+      for (int k = 0; k < F::KR_INSTR_WAVE; ++k) {
+        const int instr = wave + kWaves * k;
+        const int pk = opaque(kr_pk[k]);
+        if (instr < F::KR_INSTR && pk >= 0) {
+          const int v = min(kbase + (pk >> 16), n_keys - 1);
+          const char* src = krot_b + (unsigned)(v * DR * (int)sizeof(T) + (pk & 0xffff));
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                           (MLA_LDS void*)(MLA_LDS T*)(buf + instr * 64 * F::CB), 16, 0, 0);
         }
-#pragma unroll
-        for (int k = 0; k < F::RP; ++k) {
-          const int pr = r_unit * F::RP + k;
-          const int idx = pr < pt ? d.y * pt + pr
-                                  : (pr < pt + py ? y_base + d.z * py + pr - pt : x_base + d.w * px + pr - pt - py);
-          const f32x2 cs = rcs[idx];
-          rotate_pair(f[2 * k], f[2 * k + 1], cs.x, cs.y);
-        }
-        uint32_t w[F::RW];
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-          for (int k = 0; k < F::RW; ++k) {
-            const uint32_t lo = __builtin_bit_cast(uint16_t, (bf16)f[2 * k]);
-            const uint32_t hi = __builtin_bit_cast(uint16_t, (bf16)f[2 * k + 1]);
-            w[k] = lo | (hi << 16);
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < F::RW; ++k) w[k] = __float_as_uint(f[k]);
-        }
-        ru_t out;
-        if constexpr (F::RW == 1) {
-          out = w[0];
-        } else {
-#pragma unroll
-          for (int k = 0; k < F::RW; ++k) out[k] = w[k];
-        }
-        *reinterpret_cast<ru_t*>(buf + r_key * F::LS + DC + r_unit * F::RU) = out;
       }
     };
-
-    // zero the padding chunks of both buffers once (never written again)
-    if constexpr (F::PADC > 0) {
-      for (int e = tid; e < 2 * kBN * F::PADC; e += F::kThreads) {
-        const int bi = e / (kBN * F::PADC), q = e % (kBN * F::PADC);
-        T* bp = bi == 0 ? kv0 : kv1;
-        const u32x4 z = {};
-        *reinterpret_cast<u32x4*>(&bp[((q / F::PADC) * F::CPR + F::CC + F::RC + q % F::PADC) * F::CB]) = z;
-      }
-    }
 
     // ---- the three pieces of the key loop, for one 32-key half of a tile.
     // Scores S^T = K Q^T of half `half` of the tile in `kt`, seeded with
     // `seed` (the negated reference of each row).
     typedef f32x4 sblk[2][kNMB];
-    auto scores = [&](const T* kt, int half, sblk& s, const f32x4 (&seed)[kNMB]) {
+    auto scores = [&](const T* kt, const T* ktr, int half, sblk& s, const f32x4 (&seed)[kNMB]) {
 #pragma unroll
       for (int kc = 0; kc < F::NKC; ++kc) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const v8 a = lds_load8<T>(kt + ((half * 2 + kb) * 16 + li) * F::LS + kc * 32 + lg * 8);
+          const int row = (half * 2 + kb) * 16 + li, dim = kc * 32 + lg * 8;
+          auto rope_unit = [&]() {
+            return lds_load8<T>(ktr + row * DR + F::kr_slot(row, (dim - DC) / 8) * 8);
+          };
+          v8 a;
+          if ((kc + 1) * 32 <= DC) {
+            a = lds_load8<T>(kt + row * F::LS + dim);
+          } else if (kc * 32 >= DC && (kc + 1) * 32 <= F::DK) {
+            a = rope_unit();
+          } else {  // a block mixing latent, kR and zero padding (small shapes)
+            a = dim < DC ? lds_load8<T>(kt + row * F::LS + dim) : (dim < F::DK ? rope_unit() : zero8<T>());
+          }
 #pragma unroll
           for (int mb = 0; mb < kNMB; ++mb) s[kb][mb] = mma16(a, qf[mb][kc], kc == 0 ? seed[mb] : s[kb][mb]);
         }
@@ -389,32 +369,33 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
       }
     };
     auto buf_of = [&](auto par_c) -> T* { return decltype(par_c)::value == 0 ? kv0 : kv1; };
+    auto kr_of = [&](auto par_c) -> T* { return decltype(par_c)::value == 0 ? kr0 : kr1; };
     typedef std::integral_constant<int, 0> B0;
     typedef std::integral_constant<int, 1> B1;
 
     // One tile: start the loads of the next position (descriptors ready),
-    // describe the one after, consume this tile half by half, stash the next
-    // tile's kR part, wait for its latent loads, barrier.
+    // describe the one after, consume this tile half by half, wait for the
+    // next tile's loads, barrier.
     auto step = [&](int pos, auto cur_c, auto ragged_c) {
       constexpr int CUR = decltype(cur_c)::value;
+      typedef std::integral_constant<int, CUR ^ 1> nxt_c;
       T* cur = buf_of(cur_c);
-      T* nxt = buf_of(std::integral_constant<int, CUR ^ 1>());
+      T* cur_r = kr_of(cur_c);
       const bool has_next = pos + 1 < n_visit;
       if (has_next) {
-        issue_latent(keytab[CUR ^ 1], nxt);
-        fetch_rope(keytab[CUR ^ 1]);
+        issue_latent(keytab[CUR ^ 1], buf_of(nxt_c()));
+        issue_rope(tile_of(pos + 1) * kBN, kr_of(nxt_c()));
       }
       if (pos + 2 < n_visit) describe(pos + 2, keytab[CUR]);
       const int kbase = tile_of(pos) * kBN;
 #pragma unroll 1
       for (int half = 0; half < NKC2; ++half) {
         sblk s;
-        scores(cur, half, s, negref);
+        scores(cur, cur_r, half, s, negref);
         v8 pb[kNMB];
         probs(s, pb, kbase + half * 32, ragged_c);
         values(cur, half, pb);
       }
-      if (has_next) stash_rope(keytab[CUR ^ 1], nxt);
       __builtin_amdgcn_s_waitcnt(0);  // direct loads of the next tile have landed
       __syncthreads();
     };
@@ -428,8 +409,7 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     __syncthreads();
     if (n_visit > 0) {
       issue_latent(keytab[0], kv0);
-      fetch_rope(keytab[0]);
-      stash_rope(keytab[0], kv0);
+      issue_rope(tile_of(0) * kBN, kr0);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -437,7 +417,7 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
       const int kbase = tile_of(0) * kBN;
       sblk s;
       const f32x4 zs[kNMB] = {};
-      scores(kv0, 0, s, zs);
+      scores(kv0, kr0, 0, s, zs);
 #pragma unroll
       for (int mb = 0; mb < kNMB; ++mb) {
         float mx = -__builtin_inff();
@@ -668,6 +648,9 @@ static hipError_t launch_flash_t(const FlashParams& p, bool split, hipStream_t s
   hipLaunchKernelGGL(flash_prep_kernel, dim3(1), dim3(1), 0, s, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((rope_window_kernel<T, DC, DR>), dim3((p.T * (DR / 2) + 255) / 256, p.W, min(p.batch, 65535)), dim3(256), 0,
+                     s, p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL((flash_mla_kernel<T, DC, DR>), dim3(p.grid), dim3(F::kThreads), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (split) {

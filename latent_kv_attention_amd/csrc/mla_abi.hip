@@ -42,11 +42,8 @@ mla_status check_shape(const mla_shape* s) {
   if (T * s->window_frames * (s->d_c + s->d_rope) > INT32_MAX) return MLA_ERR_SHAPE;
   if ((int64_t)s->batch * s->window_frames * T * (s->d_c + s->d_rope) > INT64_C(1) << 40) return MLA_ERR_SHAPE;
   // the attention kernel splits key indices with a float reciprocal (exact
-  // below 2^22 keys per window) and keeps the window's RoPE rows in LDS
+  // below 2^22 keys per window)
   if (T * s->window_frames > mla::kMaxWindowKeys) return MLA_ERR_SHAPE;
-  if ((int64_t)s->window_frames * (s->d_rope_t / 2) + (int64_t)s->grid_y * (s->d_rope_y / 2) +
-          (int64_t)s->grid_x * (s->d_rope_x / 2) > mla::kRopeLdsEntries)
-    return MLA_ERR_SHAPE;
   if (!latent_supported(s->d_c, s->d_rope)) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
@@ -131,11 +128,12 @@ bool flash_plan_ok(const FlashPlan& f) {
   return f.units <= (INT64_C(1) << 40) && f.grid <= (1 << 22);
 }
 
-// Flash workspace: the fallback row list and, when row blocks are shared,
-// two partial (output / sum in the cache's element type, reference and sum
-// in float) slots per work-group.
+// Flash workspace: the fallback row list, the window's rotated kR (one row
+// of d_rope elements per key) and, when row blocks are shared, two partial
+// (output / sum in the cache's element type, reference and sum in float)
+// slots per work-group.
 struct FlashWs {
-  size_t count, rows, part_o, part_l, total;
+  size_t count, rows, krot, part_o, part_l, total;
 };
 
 FlashWs flash_ws_layout(const mla_shape* s, int q_n_frames, const FlashPlan& f) {
@@ -144,7 +142,8 @@ FlashWs flash_ws_layout(const mla_shape* s, int q_n_frames, const FlashPlan& f) 
   FlashWs w;
   w.count = 0;
   w.rows = w.count + 256;
-  w.part_o = w.rows + round256(rows * sizeof(int));
+  w.krot = w.rows + round256(rows * sizeof(int));
+  w.part_o = w.krot + round256((size_t)s->batch * s->window_frames * tokens_per_frame(s) * s->d_rope * elt_size(s));
   w.part_l = w.part_o + round256(slots * s->d_c * elt_size(s));
   w.total = w.part_l + round256(slots * 2 * sizeof(float));
   return w;
@@ -201,6 +200,7 @@ mla_status do_flash(const mla_shape* s, const void* q_abs, int q_n_frames, const
   p.fallback_rows = (int*)(base + w.rows);
   p.part_o = f.split ? (void*)(base + w.part_o) : nullptr;
   p.part_l = f.split ? (float*)(base + w.part_l) : nullptr;
+  p.krot = base + w.krot;
   p.rl = rope_layout(s, rope_t_first, rope_n_t);
   p.Mb = (int)(q_n_frames * tokens_per_frame(s) * s->n_heads);
   p.W = s->window_frames;

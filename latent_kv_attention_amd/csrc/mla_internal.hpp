@@ -59,6 +59,7 @@ struct FlashParams {
   void* part_o;            // [G][2][rows per block][d_c] partial outputs o_g / l_g, element type of the
                            // cache (split row blocks only)
   float* part_l;           // [G][2][rows per block][2] (reference, sum)
+  void* krot;              // [B][W * T][d_rope] rotated kR of each stream's valid keys, in key order
   int* fallback_count;     // rows listed for the exact fallback
   int* fallback_rows;      // [B * Mb]
   RopeLayout rl;
@@ -76,11 +77,8 @@ constexpr int kFallbackBlocks = 64;
 // (the host caps its work-group count at (kMaxMergePieces - 1) row blocks'
 // worth, which bounds the pieces of a row block by kMaxMergePieces).
 constexpr int kMaxMergePieces = 64;
-// Limits of the attention kernel: keys per window (index arithmetic in
-// float) and (cos, sin) entries of the window's RoPE rows kept in LDS
-// (window_frames * d_rope_t/2 + grid_y * d_rope_y/2 + grid_x * d_rope_x/2).
+// Limit of the attention kernel: keys per window (index arithmetic in float).
 constexpr int kMaxWindowKeys = 1 << 22;
-constexpr int kRopeLdsEntries = 2048;
 
 struct UpVParams {
   const void* o_lat;  // [B*Nq][H][d_c]

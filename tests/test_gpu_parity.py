@@ -213,6 +213,22 @@ def test_flash_attend_sharp_and_partial_window(name):
     assert_step_close(got, ref, cfg.dtype, label=f"{name} flash sharp partial", sharp=True)
 
 
+@pytest.mark.parametrize("name", ["wan_small", "wan_small_f32"])
+def test_flash_attend_slots_with_holes(name):
+    """Valid slots with empty slots between them and frames out of slot
+    order: a key's position in the window follows its slot's rank among the
+    valid slots, and its temporal rotation follows the frame the slot holds."""
+    cfg = get_config(name)
+    W = cfg.window_frames
+    assert W >= 4
+    frames = [W + 1, 3] + ([2 * W - 1] if W >= 5 else [])  # slots 1, 3 (and W - 1)
+    cache, sf, q_abs, ref = _flash_inputs(cfg, 11, frames, 2 * W - 1)
+    assert sorted(np.flatnonzero(sf >= 0).tolist()) == sorted(f % W for f in frames)
+    for splits in (0, 1):
+        got = _run_flash(cfg, cache, sf, q_abs, splits)
+        assert_step_close(got, ref, cfg.dtype, label=f"{name} flash slots with holes splits={splits}")
+
+
 def test_flash_attend_extreme_logits_use_exact_fallback():
     """Logit gaps beyond the fixed-reference range (q x 50: logit std ~50):
     those rows are listed and recomputed by the exact two-pass kernel. At such
