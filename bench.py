@@ -37,9 +37,8 @@ FLASH_SOURCES = ["latent_kv_attention_amd/csrc/flash_mla.hip", "latent_kv_attent
 # The roofline unit: one mla_flash_attend call. HIP events on the launch
 # stream bracket the call, which launches these kernels (the main kernel is
 # about 95% of the time; the merge combines row blocks split between
-# work-groups; the window's kR rotation and the other two are small).
-FLASH_KERNELS = ["flash_mla_kernel", "flash_combine_kernel", "rope_window_kernel", "flash_prep_kernel",
-                 "flash_exact_kernel"]
+# work-groups; the window's kR rotation and the exact fallback are small).
+FLASH_KERNELS = ["flash_mla_kernel", "flash_combine_kernel", "rope_window_kernel", "flash_exact_kernel"]
 
 
 def flash_source_hash() -> str:

@@ -85,9 +85,10 @@ struct FlashTile {
   static constexpr int NDB = DC / 16;
   static constexpr int CB = 16 / sizeof(T);             // elements per 16-byte chunk
   // Latent region of a tile buffer: one row of LS elements per key, the d_c
-  // latent values then padding (a 480-byte stride for bf16 keeps both operand
-  // read patterns free of bank conflicts).
-  static constexpr int LS = kBf16 ? KP + 16 : KP + CB;  // LDS row stride (elements)
+  // latent values then 32 bytes of padding for bf16 (a 416-byte stride at
+  // d_c = 192, which keeps both operand read patterns nearly free of bank
+  // conflicts).
+  static constexpr int LS = kBf16 ? DC + 16 : KP + CB;  // LDS row stride (elements)
   static constexpr int CPR = LS / CB;                   // 16-byte chunks per LDS row
   static constexpr int CC = DC / CB;                    // latent chunks per key
   static constexpr int TILE_CHUNKS = kBN * CPR;
@@ -110,17 +111,16 @@ struct FlashTile {
   static_assert(LS % 4 == 0 && (LS * sizeof(T)) % 16 == 0, "LDS rows must stay 16-byte aligned");
 };
 
-// Clears the count of rows handed to the exact fallback.
-__global__ void flash_prep_kernel(FlashParams p) { *p.fallback_count = 0; }
-
 // 3D-RoPE of the window's positional keys, once per call: key v = (slot
 // rank r, token tok) of stream b gets R(t, y, x) kR, with t the frame held
 // by the r-th valid slot and (y, x) the token's grid cell, rounded to the
 // cache's element type. Row v of the stream's block of p.krot. One thread per
-// rotary pair; grid (pair blocks, slots, stream groups).
+// rotary pair; grid (pair blocks, slots, stream groups). It also clears the
+// count of rows handed to the exact fallback.
 template <typename T, int DC, int DR>
 __global__ __launch_bounds__(256) void rope_window_kernel(FlashParams p) {
   constexpr int NP = DR / 2;
+  if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *p.fallback_count = 0;
   const int slot = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= p.T * NP) return;
@@ -645,12 +645,10 @@ __global__ __launch_bounds__(256) void flash_exact_kernel(FlashParams p) {
 template <typename T, int DC, int DR>
 static hipError_t launch_flash_t(const FlashParams& p, bool split, hipStream_t s) {
   typedef FlashTile<T, DC, DR> F;
-  hipLaunchKernelGGL(flash_prep_kernel, dim3(1), dim3(1), 0, s, p);
+  hipLaunchKernelGGL((rope_window_kernel<T, DC, DR>), dim3((p.T * (DR / 2) + 255) / 256, p.W, min(p.batch, 65535)),
+                     dim3(256), 0, s, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((rope_window_kernel<T, DC, DR>), dim3((p.T * (DR / 2) + 255) / 256, p.W, min(p.batch, 65535)), dim3(256), 0,
-                     s, p);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL((flash_mla_kernel<T, DC, DR>), dim3(p.grid), dim3(F::kThreads), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (split) {
