@@ -229,6 +229,37 @@ def test_flash_attend_slots_with_holes(name):
         assert_step_close(got, ref, cfg.dtype, label=f"{name} flash slots with holes splits={splits}")
 
 
+@pytest.mark.parametrize("kv_splits", [0, 1])
+def test_flash_attend_streams_with_different_slots(kv_splits):
+    """Two streams in one call whose windows hold different frames in
+    different slots (one full and wrapped, one with holes): each stream's
+    keys, their ranks and their rotations come from its own slot map."""
+    cfg = get_config("wan_small")
+    W = cfg.window_frames
+    q_frame = 2 * W - 1
+    ins = [_flash_inputs(cfg, 21, list(range(W - 1, 2 * W - 1)), q_frame),
+           _flash_inputs(cfg, 22, [W + 2, 1, 2 * W - 1], q_frame)]
+    shape = mla.make_shape(cfg, batch=2)
+    Q = mla.qabs_dim(shape)
+    nrow = ins[0][2].shape[0]
+    qa = np.zeros((2, nrow, cfg.n_heads, Q))
+    for b_, (_, _, q_abs, _) in enumerate(ins):
+        qa[b_, :, :, :q_abs.shape[-1]] = q_abs
+    n_t = 64
+    tables = torch.empty(mla.rope3d_table_floats(shape, n_t), dtype=torch.float32, device="cuda")
+    mla.rope3d_tables(shape, 0, n_t, tables)
+    o_lat = torch.empty(2, nrow, cfg.n_heads, cfg.d_c, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mla.flash_workspace_bytes(shape, cfg.chunk_frames, kv_splits), dtype=torch.uint8, device="cuda")
+    cache = np.stack([i[0] for i in ins])
+    sf = np.stack([i[1] for i in ins])
+    mla.flash_attend(shape, to_torch(qa, cfg.dtype), cfg.chunk_frames, to_torch(cache, cfg.dtype),
+                     torch.from_numpy(sf.copy()).cuda(), tables, 0, n_t, o_lat, ws, kv_splits)
+    _sync()
+    got = to_numpy(o_lat)
+    for b_, (_, _, _, ref) in enumerate(ins):
+        assert_step_close(got[b_], ref, cfg.dtype, label=f"stream {b_} of 2, splits={kv_splits}")
+
+
 def test_flash_attend_extreme_logits_use_exact_fallback():
     """Logit gaps beyond the fixed-reference range (q x 50: logit std ~50):
     those rows are listed and recomputed by the exact two-pass kernel. At such
