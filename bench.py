@@ -110,6 +110,120 @@ def cpu_baseline(cfg, sample_tokens: int, seed: int = 0):
             "seconds": round(dt, 3)}
 
 
+def setup_step(cfg, kv_splits, dev="cuda"):
+    """Seeded inputs and buffers of one chunk step at `cfg`: the window's first
+    frames are written, then step() writes the chunk and runs absorb, attention
+    and up-projection. Returns a namespace with the buffers and step()."""
+    import types
+
+    import numpy as np
+    import torch
+
+    import latent_kv_attention_amd as mla
+    from harness import chunk_queries, frame_tokens, layer_weights
+    from harness.torch_io import to_torch
+
+    T = cfg.tokens_per_frame
+    print(f"[bench] generating inputs ({cfg.name}: d_c {cfg.d_c}, d_rope {cfg.d_rope})", file=sys.stderr, flush=True)
+    w = {k: to_torch(v, cfg.dtype, dev) for k, v in layer_weights(cfg, 0).items()}
+    chunk_first = cfg.window_frames - cfg.chunk_frames
+    x_pre = to_torch(np.concatenate([frame_tokens(cfg, f) for f in range(chunk_first)]), cfg.dtype, dev)
+    x_chunk = to_torch(np.concatenate([frame_tokens(cfg, chunk_first + i) for i in range(cfg.chunk_frames)]),
+                       cfg.dtype, dev)
+    qn_h, qr_h = chunk_queries(cfg, chunk_first)
+    qn, qr = to_torch(qn_h, cfg.dtype, dev), to_torch(qr_h, cfg.dtype, dev)
+
+    shape = mla.make_shape(cfg, batch=1)
+    n_t = 64
+    tables = torch.empty(mla.rope3d_table_floats(shape, n_t), dtype=torch.float32, device=dev)
+    mla.rope3d_tables(shape, 0, n_t, tables)
+    cache = torch.zeros(1, cfg.window_frames, T, cfg.d_c + cfg.d_rope, dtype=torch.bfloat16, device=dev)
+    slot_frame = torch.full((1, cfg.window_frames), -1, dtype=torch.int32, device=dev)
+    mla.cache_write(shape, x_pre, w["w_dkv"], w["w_kr"], 0, chunk_first, cache, slot_frame)
+    del x_pre
+    Q = mla.qabs_dim(shape)
+    q_abs = torch.empty(cfg.n_q, cfg.n_heads, Q, dtype=torch.bfloat16, device=dev)
+    o_lat = torch.empty(cfg.n_q, cfg.n_heads, cfg.d_c, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(cfg.n_q, cfg.n_heads, cfg.d_head, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(mla.flash_workspace_bytes(shape, cfg.chunk_frames, kv_splits), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        mla.cache_write(shape, x_chunk, w["w_dkv"], w["w_kr"], chunk_first, cfg.chunk_frames, cache, slot_frame)
+        if ev:
+            ev[1].record()
+        mla.absorb_q(shape, qn, qr, chunk_first, cfg.chunk_frames, w["w_uk"], tables, 0, n_t, q_abs)
+        if ev:
+            ev[2].record()
+        mla.flash_attend(shape, q_abs, cfg.chunk_frames, cache, slot_frame, tables, 0, n_t, o_lat, ws, kv_splits)
+        if ev:
+            ev[3].record()
+        mla.up_v(shape, o_lat, cfg.chunk_frames, w["w_uv"], out)
+        if ev:
+            ev[4].record()
+
+    return types.SimpleNamespace(shape=shape, w=w, x_chunk=x_chunk, chunk_first=chunk_first, cache=cache,
+                                 slot_frame=slot_frame, out=out, step=step)
+
+
+def time_steps(ctx, steps, warmup):
+    """W untimed steps, then K timed ones between events on the launch stream;
+    returns (ms per step, mean ms of each of the four calls)."""
+    import numpy as np
+    import torch
+
+    print(f"[bench] warmup {warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        ctx.step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(steps):
+        ctx.step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / steps
+    names = ["cache_write", "absorb_q", "flash_attend", "up_v"]
+    per = {n: float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs])) for k, n in enumerate(names)}
+    print(f"[bench] timed {steps} steps: {ms_step:.4f} ms/step {per}", file=sys.stderr, flush=True)
+    assert torch.isfinite(ctx.out.float()).all(), "non-finite output"
+    return ms_step, per
+
+
+# latent widths of the sweep: (d_c, d_rope, RoPE axis split)
+SWEEP_WIDTHS = [(128, 32, (8, 12, 12)), (192, 32, (8, 12, 12)), (160, 64, (16, 24, 24)), (192, 64, (16, 24, 24))]
+
+
+def latent_sweep(base, args):
+    """The same chunk step at each latent width the library instantiates (the
+    pages' ablations vary the latent size and the content/positional split;
+    performance only, weights are synthetic). One JSON line per width; these
+    lines are a separate report, not the bench line."""
+    import torch
+
+    for dc, dr, split in SWEEP_WIDTHS:
+        cfg = base.with_(d_c=dc, d_rope=dr, rope_split=split)
+        ctx = setup_step(cfg, args.kv_splits)
+        ms_step, per = time_steps(ctx, args.steps, args.warmup)
+        fl = step_flops(cfg)
+        fl_tf = fl["flash"] / (per["flash_attend"] * 1e-3) / 1e12
+        print(json.dumps({
+            "report": "latent-width sweep, Wan2.1-1.3B-shaped chunk step (4680 queries x 32760 keys), 1 MI355X",
+            "d_c": dc, "d_rope": dr, "rope_split": list(split), "cached_scalars_per_token": dc + dr,
+            "window_cache_MB": round(cfg.window_frames * cfg.tokens_per_frame * (dc + dr) * 2 / 1e6, 2),
+            "ms_per_step": round(ms_step, 4), "kernel_ms": {k: round(v, 4) for k, v in per.items()},
+            "step_TFLOPs": round(fl["total"] / (ms_step * 1e-3) / 1e12, 2), "flash_TFLOPs": round(fl_tf, 2),
+            "flash_frac_of_bf16_peak": round(fl_tf / PEAK_BF16_TFLOPS, 4),
+            "flash_TFLOPs_nonabsorbed_equiv": round(fl["flash_nonabsorbed_equiv"] / (per["flash_attend"] * 1e-3)
+                                                    / 1e12, 2),
+            "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic"}), flush=True)
+        del ctx
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +234,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-buffers", type=int, default=40,
                     help="rotating x buffers for the cold-cache cache-write measurement (0 = skip)")
+    ap.add_argument("--latent-sweep", action="store_true",
+                    help="time the step at every latent width with kernels (one report line each) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to scale HBM byte counters) and exit")
     args = ap.parse_args()
@@ -145,8 +261,7 @@ def main():
     import torch
 
     import latent_kv_attention_amd as mla
-    from harness import chunk_queries, frame_tokens, get_config, layer_weights
-    from harness.torch_io import to_torch
+    from harness import get_config
 
     if not os.path.exists(mla.LIB_PATH):
         from latent_kv_attention_amd import build as _build
@@ -154,65 +269,13 @@ def main():
     mla.lib()
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     cfg = get_config("wan")
-    T = cfg.tokens_per_frame
-    dev = "cuda"
-    print(f"[bench] generating inputs ({cfg.note})", file=sys.stderr, flush=True)
-    w = {k: to_torch(v, cfg.dtype, dev) for k, v in layer_weights(cfg, 0).items()}
-    chunk_first = cfg.window_frames - cfg.chunk_frames
-    x_pre = to_torch(np.concatenate([frame_tokens(cfg, f) for f in range(chunk_first)]), cfg.dtype, dev)
-    x_chunk = to_torch(np.concatenate([frame_tokens(cfg, chunk_first + i) for i in range(cfg.chunk_frames)]),
-                       cfg.dtype, dev)
-    qn_h, qr_h = chunk_queries(cfg, chunk_first)
-    qn, qr = to_torch(qn_h, cfg.dtype, dev), to_torch(qr_h, cfg.dtype, dev)
-
-    shape = mla.make_shape(cfg, batch=1)
-    n_t = 64
-    tables = torch.empty(mla.rope3d_table_floats(shape, n_t), dtype=torch.float32, device=dev)
-    mla.rope3d_tables(shape, 0, n_t, tables)
-    cache = torch.zeros(1, cfg.window_frames, T, cfg.d_c + cfg.d_rope, dtype=torch.bfloat16, device=dev)
-    slot_frame = torch.full((1, cfg.window_frames), -1, dtype=torch.int32, device=dev)
-    mla.cache_write(shape, x_pre, w["w_dkv"], w["w_kr"], 0, chunk_first, cache, slot_frame)
-    Q = mla.qabs_dim(shape)
-    q_abs = torch.empty(cfg.n_q, cfg.n_heads, Q, dtype=torch.bfloat16, device=dev)
-    o_lat = torch.empty(cfg.n_q, cfg.n_heads, cfg.d_c, dtype=torch.bfloat16, device=dev)
-    out = torch.empty(cfg.n_q, cfg.n_heads, cfg.d_head, dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(mla.flash_workspace_bytes(shape, cfg.chunk_frames, args.kv_splits), dtype=torch.uint8,
-                     device=dev)
-
-    def step(ev=None):
-        if ev:
-            ev[0].record()
-        mla.cache_write(shape, x_chunk, w["w_dkv"], w["w_kr"], chunk_first, cfg.chunk_frames, cache, slot_frame)
-        if ev:
-            ev[1].record()
-        mla.absorb_q(shape, qn, qr, chunk_first, cfg.chunk_frames, w["w_uk"], tables, 0, n_t, q_abs)
-        if ev:
-            ev[2].record()
-        mla.flash_attend(shape, q_abs, cfg.chunk_frames, cache, slot_frame, tables, 0, n_t, o_lat, ws,
-                         args.kv_splits)
-        if ev:
-            ev[3].record()
-        mla.up_v(shape, o_lat, cfg.chunk_frames, w["w_uv"], out)
-        if ev:
-            ev[4].record()
-
-    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        step(evs[i])
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    names = ["cache_write", "absorb_q", "flash_attend", "up_v"]
-    per = {n: float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs])) for k, n in enumerate(names)}
-    print(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step {per}", file=sys.stderr, flush=True)
-    assert torch.isfinite(out.float()).all(), "non-finite output"
+    if args.latent_sweep:
+        latent_sweep(cfg, args)
+        return
+    ctx = setup_step(cfg, args.kv_splits)
+    ms_step, per = time_steps(ctx, args.steps, args.warmup)
+    shape, w, x_chunk, chunk_first, cache, slot_frame = (ctx.shape, ctx.w, ctx.x_chunk, ctx.chunk_first, ctx.cache,
+                                                        ctx.slot_frame)
 
     # cold-cache cache write: rotate the input over more distinct buffers than the
     # 256 MB last-level cache holds

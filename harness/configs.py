@@ -96,6 +96,14 @@ CONFIGS = {
                                window_frames=4, chunk_frames=1, dtype="f32"),
 }
 
+# Other latent widths on the small Wan-headed grid: a smaller latent, the same
+# 224 cached scalars with more positional channels, and a larger latent (the
+# pages' ablations vary the latent size and the content/positional split).
+for _dc, _dr, _split in ((128, 32, (8, 12, 12)), (160, 64, (16, 24, 24)), (192, 64, (16, 24, 24))):
+    for _dt in ("bf16", "f32"):
+        _n = f"wan_small_c{_dc}r{_dr}" + ("_f32" if _dt == "f32" else "")
+        CONFIGS[_n] = CONFIGS["wan_small"].with_(name=_n, d_c=_dc, d_rope=_dr, rope_split=_split, dtype=_dt)
+
 
 def get_config(name: str) -> MLAConfig:
     return CONFIGS[name]

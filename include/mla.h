@@ -37,8 +37,8 @@
  *     (MLA_ERR_NULL, _SHAPE, _DTYPE, _ALIGN, _WORKSPACE, _UNSUPPORTED,
  *     _RANGE), or MLA_ERR_HIP if a launch fails. No C++ exception crosses
  *     this boundary.
- *   - Supported latent widths (d_c, d_rope): (192, 32) and (16, 8), either
- *     dtype. d_head must be a multiple of 8 and at most 256; hidden a
+ *   - Supported latent widths (d_c, d_rope): (192, 32) (the Wan2.1 split),
+ *     (128, 32), (160, 64), (192, 64) and (16, 8), either dtype. d_head must be a multiple of 8 and at most 256; hidden a
  *     multiple of 8; window_frames at most 64; each RoPE axis width even;
  *     and window_frames * grid_y * grid_x at most 2^22 keys. Shapes
  *     outside these limits return MLA_ERR_SHAPE.

@@ -97,10 +97,14 @@ static hipError_t launch_absorb_t(const AbsorbParams& p, hipStream_t s) {
 
 hipError_t launch_absorb_q(int dtype, int d_c, int d_rope, const AbsorbParams& p, hipStream_t s) {
   if (p.rows <= 0) return hipSuccess;
-  if (d_c == 192 && d_rope == 32)
-    return dtype == 0 ? launch_absorb_t<bf16, 192, 32>(p, s) : launch_absorb_t<float, 192, 32>(p, s);
-  if (d_c == 16 && d_rope == 8)
-    return dtype == 0 ? launch_absorb_t<bf16, 16, 8>(p, s) : launch_absorb_t<float, 16, 8>(p, s);
+#define MLA_ABSORB_CASE(DCV, DRV) \
+  if (d_c == DCV && d_rope == DRV) return dtype == 0 ? launch_absorb_t<bf16, DCV, DRV>(p, s) : launch_absorb_t<float, DCV, DRV>(p, s);
+  MLA_ABSORB_CASE(192, 32)
+  MLA_ABSORB_CASE(128, 32)
+  MLA_ABSORB_CASE(160, 64)
+  MLA_ABSORB_CASE(192, 64)
+  MLA_ABSORB_CASE(16, 8)
+#undef MLA_ABSORB_CASE
   return hipErrorInvalidValue;
 }
 

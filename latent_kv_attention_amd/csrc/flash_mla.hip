@@ -104,10 +104,16 @@ struct FlashTile {
   static constexpr int KR_ELEMS = kBN * DR;
   static constexpr int KR_INSTR = (kBN * RCK + 63) / 64;
   static constexpr int KR_INSTR_WAVE = (KR_INSTR + kWaves - 1) / kWaves;
-  // unit slot of unit u of tile key n (an involution in u): with four units
-  // per key the 16 keys of one S^T read land in 16 different bank groups
-  __host__ __device__ static constexpr int kr_slot(int n, int u) { return U8 == 4 ? (u ^ ((n >> 2) & 3)) : u; }
-  static_assert(DC % 8 == 0 && DR % 8 == 0, "latent and kR split into 8-element units");
+  // unit slot of unit u of tile key n (an involution in u): 16 / U8 keys
+  // fill one 256-byte bank cycle, and the XOR moves the next such group of
+  // keys to other units, so the 16 keys of one bf16 S^T read land in 16
+  // different bank groups
+  static constexpr int KR_SH = U8 >= 16 ? 0 : U8 == 8 ? 1 : U8 == 4 ? 2 : U8 == 2 ? 3 : 4;  // log2(16 / U8)
+  __host__ __device__ static constexpr int kr_slot(int n, int u) {
+    return U8 > 1 && U8 <= 16 ? (u ^ ((n >> KR_SH) & (U8 - 1))) : u;
+  }
+  static_assert(DC % 16 == 0 && DR % 8 == 0 && (DR / 8 & (DR / 8 - 1)) == 0,
+                "latent in 16-wide blocks; kR in a power-of-two number of 8-element units");
   static_assert(LS % 4 == 0 && (LS * sizeof(T)) % 16 == 0, "LDS rows must stay 16-byte aligned");
 };
 
@@ -663,10 +669,15 @@ static hipError_t launch_flash_t(const FlashParams& p, bool split, hipStream_t s
 
 hipError_t launch_flash(int dtype, int d_c, int d_rope, const FlashParams& p, bool split, hipStream_t s) {
   if (p.Mb <= 0 || p.batch <= 0 || p.grid <= 0) return hipSuccess;
-  if (d_c == 192 && d_rope == 32)
-    return dtype == 0 ? launch_flash_t<bf16, 192, 32>(p, split, s) : launch_flash_t<float, 192, 32>(p, split, s);
-  if (d_c == 16 && d_rope == 8)
-    return dtype == 0 ? launch_flash_t<bf16, 16, 8>(p, split, s) : launch_flash_t<float, 16, 8>(p, split, s);
+#define MLA_FLASH_CASE(DCV, DRV)                                                                  \
+  if (d_c == DCV && d_rope == DRV)                                                                \
+    return dtype == 0 ? launch_flash_t<bf16, DCV, DRV>(p, split, s) : launch_flash_t<float, DCV, DRV>(p, split, s);
+  MLA_FLASH_CASE(192, 32)
+  MLA_FLASH_CASE(128, 32)
+  MLA_FLASH_CASE(160, 64)
+  MLA_FLASH_CASE(192, 64)
+  MLA_FLASH_CASE(16, 8)
+#undef MLA_FLASH_CASE
   return hipErrorInvalidValue;
 }
 

@@ -22,7 +22,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t elt_size(const mla_shape* s) { return s->dtype == MLA_BF16 ? 2 : 4; }
 
-bool latent_supported(int d_c, int d_rope) { return (d_c == 192 && d_rope == 32) || (d_c == 16 && d_rope == 8); }
+// latent widths with kernel instantiations: the Wan2.1 split (192, 32), a
+// smaller latent (128, 32), the same 224 scalars split (160, 64), a larger
+// latent (192, 64), and the small test widths (16, 8)
+bool latent_supported(int d_c, int d_rope) {
+  return (d_c == 192 && d_rope == 32) || (d_c == 128 && d_rope == 32) || (d_c == 160 && d_rope == 64) ||
+         (d_c == 192 && d_rope == 64) || (d_c == 16 && d_rope == 8);
+}
 
 mla_status check_shape(const mla_shape* s) {
   if (!s) return MLA_ERR_NULL;

@@ -74,6 +74,8 @@ hipError_t launch_up_v(int dtype, int d_c, int d_rope, const UpVParams& p, hipSt
   (void)d_rope;
   if (p.rows <= 0) return hipSuccess;
   if (d_c == 192) return dtype == 0 ? launch_up_v_t<bf16, 192>(p, s) : launch_up_v_t<float, 192>(p, s);
+  if (d_c == 160) return dtype == 0 ? launch_up_v_t<bf16, 160>(p, s) : launch_up_v_t<float, 160>(p, s);
+  if (d_c == 128) return dtype == 0 ? launch_up_v_t<bf16, 128>(p, s) : launch_up_v_t<float, 128>(p, s);
   if (d_c == 16) return dtype == 0 ? launch_up_v_t<bf16, 16>(p, s) : launch_up_v_t<float, 16>(p, s);
   return hipErrorInvalidValue;
 }

@@ -54,11 +54,24 @@ def _shape(name="wan", **kw):
 @pytest.mark.parametrize("field,value,code", [
     ("dtype", 7, 3), ("batch", 0, 2), ("hidden", 12, 2), ("d_head", 12, 2), ("d_head", 512, 2),
     ("window_frames", 0, 2), ("window_frames", 65, 2), ("d_rope_t", 7, 2), ("d_rope_x", 10, 2),
-    ("rope_base", 0.0, 2), ("grid_x", 0, 2), ("d_c", 128, 6),
+    ("rope_base", 0.0, 2), ("grid_x", 0, 2), ("d_c", 96, 6),
 ])
 def test_shape_validation(built_lib, field, value, code):
     assert mla.shape_check(_shape()) == 0
     assert mla.shape_check(_shape(**{field: value})) == code
+
+
+SUPPORTED_LATENTS = [(192, 32, (8, 12, 12)), (128, 32, (8, 12, 12)), (160, 64, (16, 24, 24)),
+                     (192, 64, (16, 24, 24)), (16, 8, (2, 2, 4))]
+
+
+def test_latent_widths_with_kernels(built_lib):
+    """Every (d_c, d_rope) pair with kernel instantiations passes the shape
+    check; other pairs are rejected as unsupported before any launch."""
+    for dc, dr, (t, y, x) in SUPPORTED_LATENTS:
+        assert mla.shape_check(_shape(d_c=dc, d_rope=dr, d_rope_t=t, d_rope_y=y, d_rope_x=x)) == 0, (dc, dr)
+    for dc, dr, (t, y, x) in [(224, 32, (8, 12, 12)), (160, 32, (8, 12, 12)), (128, 64, (16, 24, 24))]:
+        assert mla.shape_check(_shape(d_c=dc, d_rope=dr, d_rope_t=t, d_rope_y=y, d_rope_x=x)) == 6, (dc, dr)
 
 
 def test_host_queries(built_lib):
@@ -99,6 +112,6 @@ def test_entry_points_reject_bad_arguments_before_launch(built_lib):
     assert lib.mla_chunk_attend(sp, fake, fake, 0, 3, fake, fake, fake, fake, fake, 0, 21, fake, fake, 16,
                                 None) == 5
     # unsupported latent width
-    bad = _shape(d_c=128)
+    bad = _shape(d_c=96)
     assert lib.mla_cache_write(ctypes.byref(bad), fake, fake, fake, 0, 3, fake, fake, None) == 6
     assert lib.mla_shape_check(None) == 1

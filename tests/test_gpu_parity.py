@@ -340,6 +340,28 @@ def test_full_step(name, q_scale):
     assert_step_close(got, ref, cfg.dtype, label=f"{name} step q*{q_scale}", sharp=q_scale > 1.0)
 
 
+LATENT_WIDTH_CONFIGS = ["wan_small_c128r32", "wan_small_c160r64", "wan_small_c192r64", "wan_small_c160r64_f32"]
+
+
+@pytest.mark.parametrize("name", LATENT_WIDTH_CONFIGS)
+def test_full_step_other_latent_widths(name):
+    """The whole step (cache write, absorb, attention, up-projection) at the
+    other latent widths the library instantiates."""
+    cfg = get_config(name)
+    got, ref = _full_step(cfg, seed=14)
+    assert_step_close(got, ref, cfg.dtype, label=f"{name} step")
+
+
+@pytest.mark.parametrize("name", LATENT_WIDTH_CONFIGS[:3])
+@pytest.mark.parametrize("kv_splits", [1, 3])
+def test_flash_attend_other_latent_widths(name, kv_splits):
+    cfg = get_config(name)
+    W = cfg.window_frames
+    cache, sf, q_abs, ref = _flash_inputs(cfg, 15, list(range(W + 2)), W + 2 - cfg.chunk_frames)
+    got = _run_flash(cfg, cache, sf, q_abs, kv_splits)
+    assert_step_close(got, ref, cfg.dtype, label=f"{name} flash splits={kv_splits}")
+
+
 def test_full_step_batch_and_partial_fill():
     cfg = get_config("wan_small")
     got, ref = _full_step(cfg, seed=12, B=3, fill=3)
