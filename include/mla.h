@@ -211,6 +211,30 @@ mla_status mla_chunk_attend(const mla_shape* shape, const void* q_nope, const vo
                             int32_t rope_n_t, void* out, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* ---------------------------------------------------------------- a3'..a5'
+ * Per-head form of the same step (hyper.ai summary, Method: per-head keys
+ * and values are reconstructed from the shared latent when needed). Same
+ * arguments and result as mla_chunk_attend, up to rounding: the window's
+ * keys and values are expanded once per call for every head,
+ *   k[h][j] = W_uk[h] c_j,  v[h][j] = W_uv[h] c_j   (bf16, in the workspace),
+ * and each head attends with the score
+ *   scale * (q_nope . k[h][j] + R(p_i) qR . R(p_j) kR_j)
+ * over every key of every valid slot. It does
+ * 2 N_q N_k H (d_head + d_rope + d_head) products in the attention against
+ * the latent form's 2 N_q N_k H (d_c + d_rope + d_c), plus the expansion
+ * (4 N_k H d_head d_c products and 4 N_k H d_head bytes). Only bf16 with
+ * d_head = 128 and a latent width the library instantiates; other shapes
+ * return MLA_ERR_UNSUPPORTED (and a workspace size of 0).
+ *   workspace (device) of at least mla_chunk_attend_heads_workspace_bytes
+ *   bytes (about 4 B H W T d_head bytes: 201 MB at the Wan2.1 shape);
+ *   contents on entry do not matter. */
+size_t mla_chunk_attend_heads_workspace_bytes(const mla_shape* shape, int32_t q_n_frames);
+mla_status mla_chunk_attend_heads(const mla_shape* shape, const void* q_nope, const void* q_r,
+                                  int32_t q_frame_first, int32_t q_n_frames, const void* w_uk, const void* w_uv,
+                                  const void* cache, const int32_t* slot_frame, const float* rope_tables,
+                                  int32_t rope_t_first, int32_t rope_n_t, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,8 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libmla355.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["mla_abi.hip", "rope_tables.hip", "cache_write.hip", "absorb_q.hip", "flash_mla.hip", "up_v.hip"]
+SOURCES = ["mla_abi.hip", "rope_tables.hip", "cache_write.hip", "absorb_q.hip", "flash_mla.hip", "up_v.hip",
+           "heads_mha.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU instructions.
 HIPCC_FLAGS = [

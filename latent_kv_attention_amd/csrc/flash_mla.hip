@@ -667,6 +667,27 @@ static hipError_t launch_flash_t(const FlashParams& p, bool split, hipStream_t s
   return hipGetLastError();
 }
 
+template <typename T, int DC, int DR>
+static hipError_t launch_rope_window_t(const FlashParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((rope_window_kernel<T, DC, DR>), dim3((p.T * (DR / 2) + 255) / 256, p.W, min(p.batch, 65535)),
+                     dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_window(int dtype, int d_c, int d_rope, const FlashParams& p, hipStream_t s) {
+  if (p.batch <= 0) return hipSuccess;
+#define MLA_ROPE_CASE(DCV, DRV) \
+  if (d_c == DCV && d_rope == DRV) \
+    return dtype == 0 ? launch_rope_window_t<bf16, DCV, DRV>(p, s) : launch_rope_window_t<float, DCV, DRV>(p, s);
+  MLA_ROPE_CASE(192, 32)
+  MLA_ROPE_CASE(128, 32)
+  MLA_ROPE_CASE(160, 64)
+  MLA_ROPE_CASE(192, 64)
+  MLA_ROPE_CASE(16, 8)
+#undef MLA_ROPE_CASE
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_flash(int dtype, int d_c, int d_rope, const FlashParams& p, bool split, hipStream_t s) {
   if (p.Mb <= 0 || p.batch <= 0 || p.grid <= 0) return hipSuccess;
 #define MLA_FLASH_CASE(DCV, DRV)                                                                  \

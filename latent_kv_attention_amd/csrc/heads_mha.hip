@@ -1,0 +1,513 @@
+// Per-head form of the chunk attention. hyper.ai summary of VideoMLA,
+// Method section: the cache holds only the shared latent c_j and the
+// positional key kR_j, and the per-head keys and values are reconstructed
+// from c_j when they are needed. This file reconstructs them for the whole
+// window once per call,
+//   k_exp[h][j] = W_uk[h] c_j,   v_exp[h][j] = W_uv[h] c_j   (j in key order),
+// and then runs, per head, attention with the two-part score
+//   s_ij = scale * (q_nope_ih . k_exp[h][j] + R(p_i) qR_ih . R(p_j) kR_j)
+//   out_ih = sum_j softmax_j(s_ij) v_exp[h][j].
+// The attention does 2 Nq Nk H (d_head + d_rope + d_head) products against
+// the latent form's 2 Nq Nk H (d_c + d_rope + d_c); the expansion adds
+// 4 Nk H d_head d_c products and writes 4 Nk H d_head bytes (bf16).
+//
+// Attention layout (bf16): a work-group owns 256 query tokens of one head
+// (8 waves x 32 rows, two waves per SIMD) and visits every key tile of the
+// window. Key tiles of 128 keys are staged in LDS, double buffered, with
+// direct global->LDS loads from three contiguous row sets: k_exp (rows 272
+// bytes apart), the rotated kR (packed, 16-byte units XOR-swizzled by key)
+// and v_exp (rows 288 bytes apart, the stride at which the transposing reads
+// of the value product do not conflict). Scores are formed transposed,
+// S^T = K Q^T, so the probabilities land in the operand layout of
+// O^T = V^T P^T; the softmax uses a fixed per-row reference (the maximum of
+// the first 32 keys' scores) and lists rows whose sum overflows for an
+// exact two-pass kernel, as the latent form does.
+#include <type_traits>
+
+#include "mla_common.hpp"
+#include "mla_internal.hpp"
+#include "rope_device.hpp"
+
+namespace mla {
+
+namespace {
+constexpr int kSlots = 64;
+constexpr float kHeadsSumLimit = 1.2676506e30f;  // 2^100
+constexpr int kExpWaves = 8;
+constexpr int kExpKeys = kExpWaves * 64;  // keys per expansion work-group
+
+__device__ __forceinline__ int opaque_h(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ __forceinline__ void store4_bf16(bf16* dst, float a, float b, float c, float d) {
+  const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)a) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)b) << 16);
+  const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)c) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)d) << 16);
+  *reinterpret_cast<u32x2*>(dst) = u32x2{w0, w1};
+}
+
+// valid slots of stream b in slot order (wave 0); returns nothing, fills LDS
+__device__ __forceinline__ void slot_ranks(const HeadsParams& p, int b, int lane, int* slot_of, int* n_valid) {
+  const int f = lane < p.W ? p.slot_frame[b * p.W + lane] : -1;
+  const unsigned long long mask = __ballot(f >= 0);
+  if (f >= 0) slot_of[__popcll(mask & ((1ull << lane) - 1ull))] = lane;
+  if (lane == 0) *n_valid = __popcll(mask);
+}
+}  // namespace
+
+// ---------------------------------------------------------------- expansion
+// k_exp / v_exp rows of 512 keys of one head of one stream. Both weight
+// matrices of the head are staged in LDS; each wave takes 64 keys and
+// computes out^T = W c^T in 16 x 16 blocks, so a lane holds four consecutive
+// outputs of one key and stores them as one 8-byte piece.
+template <int DC, int DR, int DH>
+__global__ __launch_bounds__(512) void expand_kv_kernel(HeadsParams p) {
+  constexpr int LSW = DC + 16;  // LDS row stride of the staged weights (elements)
+  constexpr int NKC = DC / 32;
+  constexpr int NNB = DH / 16;
+  __shared__ __attribute__((aligned(16))) bf16 wl[2 * DH * LSW];
+  __shared__ int slot_of[kSlots];
+  __shared__ int n_valid_sh;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  if (wave == 0) slot_ranks(p, b, lane, slot_of, &n_valid_sh);
+  for (int e = tid; e < 2 * DH * (DC / 8); e += 512) {
+    const int r = e / (DC / 8), c8 = (e - r * (DC / 8)) * 8;
+    const bf16* src = (const bf16*)(r < DH ? p.w_uk : p.w_uv) + ((size_t)h * DH + (r < DH ? r : r - DH)) * DC + c8;
+    store8<bf16>(wl + r * LSW + c8, load8<bf16>(src));
+  }
+  __syncthreads();
+  const int n_keys = n_valid_sh * p.T;
+  const int v0 = blockIdx.x * kExpKeys + wave * 64;
+  if (v0 >= n_keys) return;
+
+  // c of this wave's 64 keys (keys past the window alias the last key; their
+  // outputs are not stored), as the B operand: key li of block mb, dims
+  // kc * 32 + lg * 8
+  const bf16* cache_b = (const bf16*)p.cache + (size_t)b * p.W * p.T * (DC + DR);
+  bf16x8 cb[4][NKC];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int v = min(v0 + mb * 16 + li, n_keys - 1);
+    const int rank = v / p.T, tok = v - rank * p.T;
+    const bf16* row = cache_b + ((size_t)slot_of[rank] * p.T + tok) * (DC + DR);
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) cb[mb][kc] = load8<bf16>(row + kc * 32 + lg * 8);
+  }
+  const size_t head_rows = (size_t)(b * p.H + h) * p.W * p.T;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    bf16* dst = (bf16*)(which == 0 ? p.k_exp : p.v_exp) + head_rows * DH;
+#pragma unroll 2
+    for (int nb = 0; nb < NNB; ++nb) {
+      f32x4 acc[4] = {};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const bf16x8 a = lds_load8<bf16>(wl + (which * DH + nb * 16 + li) * LSW + kc * 32 + lg * 8);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) acc[mb] = mma16(a, cb[mb][kc], acc[mb]);
+      }
+      // lane: outputs nb * 16 + lg * 4 + (0..3) of key v0 + mb * 16 + li
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int v = v0 + mb * 16 + li;
+        if (v < n_keys)
+          store4_bf16(dst + (size_t)v * DH + nb * 16 + lg * 4, acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- queries
+// q_cat[b][h][i] = qscale * [q_nope | R(t, y, x) qR] for the chunk's tokens;
+// one thread per 8-element piece.
+template <int DH, int DR>
+__global__ __launch_bounds__(256) void heads_qcat_kernel(HeadsParams p) {
+  constexpr int QP = DH + DR, NC = QP / 8;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long rows = (long long)p.batch * p.Nq * p.H;
+  if (e >= rows * NC) return;
+  const long long row = e / NC;  // (b, i, h) in the order of q_nope
+  const int c = (int)(e - row * NC);
+  const int h = (int)(row % p.H);
+  const long long bi = row / p.H;
+  const int i = (int)(bi % p.Nq), b = (int)(bi / p.Nq);
+  float f[8];
+  if (c < DH / 8) {
+    unpack8<bf16>(load8<bf16>((const bf16*)p.q_nope + row * DH + c * 8), f);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) f[k] *= p.qscale;
+  } else {
+    const int e0 = c * 8 - DH;  // first q_r element of the piece
+    unpack8<bf16>(load8<bf16>((const bf16*)p.q_r + row * DR + e0), f);
+    const int t = p.q_frame_first + i / p.T, tok = i % p.T;
+    const int y = tok / p.grid_x, x = tok - y * p.grid_x;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float cs, sn;
+      rope_cos_sin(p.rl, p.tables, e0 / 2 + k, t, y, x, cs, sn);
+      rotate_pair(f[2 * k], f[2 * k + 1], cs, sn);
+      f[2 * k] *= p.qscale;
+      f[2 * k + 1] *= p.qscale;
+    }
+  }
+  store8<bf16>((bf16*)p.q_cat + (((size_t)b * p.H + h) * p.Nq + i) * QP + c * 8, pack8<bf16>(f));
+}
+
+// ---------------------------------------------------------------- attention
+template <int DH, int DR>
+struct HeadsTile {
+  static constexpr int kWaves = 8, kThreads = 512, kNMB = 2;
+  static constexpr int kRowsWave = kNMB * 16, kRowsBlock = kWaves * kRowsWave;
+  static constexpr int QP = DH + DR;           // contraction width of QK
+  static constexpr int NKC = QP / 32, NKCH = DH / 32, NDB = DH / 16;
+  static constexpr int LSK = DH + 8;           // k rows (elements): 16 rows of a QK read hit 16 bank groups
+  static constexpr int LSV = DH + 16;          // v rows: four rows of a transposing read hit disjoint banks
+  static constexpr int CPRK = LSK / 8, CPRV = LSV / 8, CH = DH / 8;
+  static constexpr int U8 = DR / 8;            // 16-byte kR units per key
+  static constexpr int KR_SH = U8 >= 16 ? 0 : U8 == 8 ? 1 : U8 == 4 ? 2 : U8 == 2 ? 3 : 4;
+  __host__ __device__ static constexpr int kr_slot(int n, int u) {
+    return U8 > 1 && U8 <= 16 ? (u ^ ((n >> KR_SH) & (U8 - 1))) : u;
+  }
+  static constexpr int instr(int keys, int chunks_per_key) { return (keys * chunks_per_key + 63) / 64; }
+  static constexpr int buf_bytes(int keys) {
+    return (instr(keys, CPRK) + instr(keys, CPRV) + instr(keys, U8)) * 64 * 16;
+  }
+  static constexpr int kBN = 2 * buf_bytes(128) <= 160 * 1024 - 1024 ? 128 : 64;  // keys per tile
+  static constexpr int NKC2 = kBN / 32;
+  static constexpr int K_INSTR = instr(kBN, CPRK), V_INSTR = instr(kBN, CPRV), R_INSTR = instr(kBN, U8);
+  static constexpr int K_IW = (K_INSTR + kWaves - 1) / kWaves;
+  static constexpr int V_IW = (V_INSTR + kWaves - 1) / kWaves;
+  static constexpr int R_IW = (R_INSTR + kWaves - 1) / kWaves;
+  static constexpr int K_ELEMS = K_INSTR * 64 * 8, V_ELEMS = V_INSTR * 64 * 8, R_ELEMS = R_INSTR * 64 * 8;
+  static_assert(DH % 32 == 0 && DR % 32 == 0 && (U8 & (U8 - 1)) == 0, "whole 32-wide contraction blocks");
+};
+
+template <int DH, int DR>
+__global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
+  typedef HeadsTile<DH, DR> F;
+  constexpr int kBN = F::kBN, kNMB = F::kNMB, kWaves = F::kWaves, NKC2 = F::NKC2;
+  // one separately declared array per buffer and region, so every LDS access
+  // has a compile-time array and the compiler does not wait for the
+  // prefetch of the other buffer before reading the current one
+  __shared__ __attribute__((aligned(16))) bf16 k0[F::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 k1[F::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 v0[F::V_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 v1[F::V_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 r0[F::R_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 r1[F::R_ELEMS];
+  __shared__ int n_valid_sh;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int rb = blockIdx.x % p.n_rb;
+  const int bh = blockIdx.x / p.n_rb;  // b * H + h
+  const int h = bh % p.H, b = bh / p.H;
+
+  // direct-load slots: instruction k of the wave fills chunks [64 i, 64 i + 64)
+  // of a region, i = wave + kWaves k; packed (key << 16) | byte offset in the
+  // key's source row, or -1 for padding chunks and spare instructions
+  int kpk[F::K_IW], vpk[F::V_IW], rpk[F::R_IW];
+#pragma unroll
+  for (int k = 0; k < F::K_IW; ++k) {
+    const int ins = wave + kWaves * k, q = ins * 64 + lane, n = q / F::CPRK, c = q - n * F::CPRK;
+    kpk[k] = (ins < F::K_INSTR && n < kBN && c < F::CH) ? (n << 16) | (c * 16) : -1;
+  }
+#pragma unroll
+  for (int k = 0; k < F::V_IW; ++k) {
+    const int ins = wave + kWaves * k, q = ins * 64 + lane, n = q / F::CPRV, c = q - n * F::CPRV;
+    vpk[k] = (ins < F::V_INSTR && n < kBN && c < F::CH) ? (n << 16) | (c * 16) : -1;
+  }
+#pragma unroll
+  for (int k = 0; k < F::R_IW; ++k) {
+    const int ins = wave + kWaves * k, q = ins * 64 + lane, n = q / F::U8, us = q - n * F::U8;
+    rpk[k] = (ins < F::R_INSTR && n < kBN) ? (n << 16) | (F::kr_slot(n, us) * 16) : -1;
+  }
+
+  if (wave == 0) {
+    const int f = lane < p.W ? p.slot_frame[b * p.W + lane] : -1;
+    const unsigned long long mask = __ballot(f >= 0);
+    if (lane == 0) n_valid_sh = __popcll(mask);
+  }
+  __syncthreads();
+  const int n_keys = n_valid_sh * p.T;
+  const int n_tiles = (n_keys + kBN - 1) / kBN;
+
+  // queries of this wave (B operand of S^T = K Q^T), kept in registers
+  typedef bf16x8 v8;
+  const int tok_wave = rb * F::kRowsBlock + wave * F::kRowsWave;
+  const bf16* qb = (const bf16*)p.q_cat + (size_t)bh * p.Nq * F::QP;
+  v8 qf[kNMB][F::NKC];
+#pragma unroll
+  for (int mb = 0; mb < kNMB; ++mb) {
+    const int tok = tok_wave + mb * 16 + li;
+#pragma unroll
+    for (int kc = 0; kc < F::NKC; ++kc)
+      qf[mb][kc] = tok < p.Nq ? load8<bf16>(qb + (size_t)tok * F::QP + kc * 32 + lg * 8) : zero8<bf16>();
+  }
+  f32x4 negref[kNMB];
+  f32x4 o[F::NDB][kNMB];
+  float l_run[kNMB];
+#pragma unroll
+  for (int mb = 0; mb < kNMB; ++mb) {
+    negref[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_run[mb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < F::NDB; ++db) o[db][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const size_t head_rows = (size_t)bh * p.W * p.T;
+  const char* kb_src = (const char*)((const bf16*)p.k_exp + head_rows * DH);
+  const char* vb_src = (const char*)((const bf16*)p.v_exp + head_rows * DH);
+  const char* rb_src = (const char*)((const bf16*)p.krot + (size_t)b * p.W * p.T * DR);
+
+  // position 0 visits the last tile (the one that can be ragged), positions
+  // 1.. the others in order
+  auto tile_of = [&](int pos) { return pos == 0 ? n_tiles - 1 : pos - 1; };
+  auto issue = [&](int pos, bf16* kt, bf16* vt, bf16* rt) {
+    const int kbase = tile_of(pos) * kBN;
+#pragma unroll
+    for (int k = 0; k < F::K_IW; ++k) {
+      const int pk = opaque_h(kpk[k]);
+      if (pk >= 0) {
+        const int v = min(kbase + (pk >> 16), n_keys - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(kb_src + (unsigned)(v * DH * 2 + (pk & 0xffff))),
+            (MLA_LDS void*)(MLA_LDS bf16*)(kt + (wave + kWaves * k) * 64 * 8), 16, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < F::V_IW; ++k) {
+      const int pk = opaque_h(vpk[k]);
+      if (pk >= 0) {
+        const int v = min(kbase + (pk >> 16), n_keys - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(vb_src + (unsigned)(v * DH * 2 + (pk & 0xffff))),
+            (MLA_LDS void*)(MLA_LDS bf16*)(vt + (wave + kWaves * k) * 64 * 8), 16, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < F::R_IW; ++k) {
+      const int pk = opaque_h(rpk[k]);
+      if (pk >= 0) {
+        const int v = min(kbase + (pk >> 16), n_keys - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(rb_src + (unsigned)(v * DR * 2 + (pk & 0xffff))),
+            (MLA_LDS void*)(MLA_LDS bf16*)(rt + (wave + kWaves * k) * 64 * 8), 16, 0, 0);
+      }
+    }
+  };
+
+  typedef f32x4 sblk[2][kNMB];
+  auto scores = [&](const bf16* kt, const bf16* rt, int half, sblk& s, const f32x4 (&seed)[kNMB]) {
+#pragma unroll
+    for (int kc = 0; kc < F::NKC; ++kc) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = (half * 2 + kb) * 16 + li, dim = kc * 32 + lg * 8;
+        const v8 a = kc < F::NKCH ? lds_load8<bf16>(kt + row * F::LSK + dim)
+                                  : lds_load8<bf16>(rt + row * DR + F::kr_slot(row, (dim - DH) / 8) * 8);
+#pragma unroll
+        for (int mb = 0; mb < kNMB; ++mb) s[kb][mb] = mma16(a, qf[mb][kc], kc == 0 ? seed[mb] : s[kb][mb]);
+      }
+    }
+  };
+  auto probs = [&](const sblk& s, v8 (&pb)[kNMB], int kfirst, auto ragged_c) {
+    constexpr bool RAGGED = decltype(ragged_c)::value;
+#pragma unroll
+    for (int mb = 0; mb < kNMB; ++mb) {
+      float f8[8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float e = fast_exp2(s[kb][mb][i]);
+          if constexpr (RAGGED) e = kfirst + kb * 16 + lg * 4 + i < n_keys ? e : 0.f;
+          f8[kb * 4 + i] = e;
+          l_run[mb] += e;
+        }
+      pb[mb] = pack8<bf16>(f8);
+    }
+  };
+  auto values = [&](const bf16* vt, int half, const v8 (&pb)[kNMB]) {
+#pragma unroll
+    for (int db = 0; db < F::NDB; ++db) {
+      const v8 a = lds_tr8(vt, F::LSV, half * 32 + lg * 4, half * 32 + 16 + lg * 4, db * 16);
+#pragma unroll
+      for (int mb = 0; mb < kNMB; ++mb) o[db][mb] = mma16(a, pb[mb], o[db][mb]);
+    }
+  };
+  typedef std::integral_constant<int, 0> B0;
+  typedef std::integral_constant<int, 1> B1;
+  auto step = [&](int pos, auto cur_c, auto ragged_c) {
+    constexpr int CUR = decltype(cur_c)::value;
+    const bf16* kt = CUR == 0 ? k0 : k1;
+    const bf16* vt = CUR == 0 ? v0 : v1;
+    const bf16* rt = CUR == 0 ? r0 : r1;
+    if (pos + 1 < n_tiles) {
+      if constexpr (CUR == 0) issue(pos + 1, k1, v1, r1);
+      else issue(pos + 1, k0, v0, r0);
+    }
+    const int kbase = tile_of(pos) * kBN;
+#pragma unroll 1
+    for (int half = 0; half < NKC2; ++half) {
+      sblk s;
+      scores(kt, rt, half, s, negref);
+      v8 pb[kNMB];
+      probs(s, pb, kbase + half * 32, ragged_c);
+      values(vt, half, pb);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // direct loads of the next tile have landed
+    __syncthreads();
+  };
+
+  if (n_tiles > 0) {
+    issue(0, k0, v0, r0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // reference of each row: the maximum of its scores over the first 32 keys
+    const int kbase = tile_of(0) * kBN;
+    sblk s;
+    const f32x4 zs[kNMB] = {};
+    scores(k0, r0, 0, s, zs);
+#pragma unroll
+    for (int mb = 0; mb < kNMB; ++mb) {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kbase + kb * 16 + lg * 4 + i < n_keys) mx = fmaxf(mx, s[kb][mb][i]);
+      mx = wave_max_across_groups(mx);
+      negref[mb] = f32x4{-mx, -mx, -mx, -mx};
+    }
+    step(0, B0(), std::integral_constant<bool, true>());
+    typedef std::integral_constant<bool, false> Full;
+    int pos = 1;
+    for (; pos + 1 < n_tiles; pos += 2) {
+      step(pos, B1(), Full());
+      step(pos + 1, B0(), Full());
+    }
+    if (pos < n_tiles) step(pos, B1(), Full());
+  }
+
+  // epilogue: out[b][i][h][:] = o / l; a lane holds four consecutive outputs
+  const int eln = opaque_h(lane);
+  const int eli = eln & 15, elg = eln >> 4;
+#pragma unroll
+  for (int mb = 0; mb < kNMB; ++mb) {
+    const float l = wave_sum_across_groups(l_run[mb]);
+    const int tok = tok_wave + mb * 16 + eli;
+    if (tok >= p.Nq) continue;
+    const bool ok = l <= kHeadsSumLimit;  // false for inf / NaN as well
+    const float inv = (ok && l > 0.f) ? 1.f / l : 0.f;
+    bf16* dst = (bf16*)p.out + (((size_t)b * p.Nq + tok) * p.H + h) * DH;
+#pragma unroll
+    for (int db = 0; db < F::NDB; ++db)
+      store4_bf16(dst + db * 16 + elg * 4, o[db][mb][0] * inv, o[db][mb][1] * inv, o[db][mb][2] * inv,
+                  o[db][mb][3] * inv);
+    if (!ok && elg == 0) p.fallback_rows[atomicAdd(p.fallback_count, 1)] = bh * p.Nq + tok;
+  }
+}
+
+// Rows listed by the attention kernel, recomputed with the textbook two-pass
+// softmax over the expanded keys and values. One work-group per listed row
+// (grid-stride over the list).
+template <int DH, int DR>
+__global__ __launch_bounds__(256) void heads_exact_kernel(HeadsParams p) {
+  constexpr int QP = DH + DR, CHUNK = 256;
+  __shared__ float q[QP];
+  __shared__ float pr[CHUNK];
+  __shared__ float red[256];
+  __shared__ int n_valid_sh;
+  const int tid = threadIdx.x;
+  const int count = *p.fallback_count;
+  for (int idx = blockIdx.x; idx < count; idx += gridDim.x) {
+    const int row = p.fallback_rows[idx];  // (b * H + h) * Nq + i
+    const int bh = row / p.Nq, i = row - bh * p.Nq, h = bh % p.H, b = bh / p.H;
+    __syncthreads();
+    if (tid < 64) {
+      const int f = tid < p.W ? p.slot_frame[b * p.W + tid] : -1;
+      const unsigned long long mask = __ballot(f >= 0);
+      if (tid == 0) n_valid_sh = __popcll(mask);
+    }
+    for (int d = tid; d < QP; d += 256) q[d] = to_f<bf16>(((const bf16*)p.q_cat)[(size_t)row * QP + d]);
+    __syncthreads();
+    const int n_keys = n_valid_sh * p.T;
+    const size_t head_rows = (size_t)bh * p.W * p.T;
+    const bf16* kx = (const bf16*)p.k_exp + head_rows * DH;
+    const bf16* vx = (const bf16*)p.v_exp + head_rows * DH;
+    const bf16* kr = (const bf16*)p.krot + (size_t)b * p.W * p.T * DR;
+    auto score = [&](int v) {
+      float s = 0.f;
+      for (int d = 0; d < DH; ++d) s += q[d] * to_f<bf16>(kx[(size_t)v * DH + d]);
+      for (int d = 0; d < DR; ++d) s += q[DH + d] * to_f<bf16>(kr[(size_t)v * DR + d]);
+      return s;
+    };
+    float mx = -__builtin_inff();
+    for (int v = tid; v < n_keys; v += 256) mx = fmaxf(mx, score(v));
+    red[tid] = mx;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+      if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
+      __syncthreads();
+    }
+    const float m = red[0];
+    __syncthreads();
+    float acc = 0.f, lsum = 0.f;
+    for (int j0 = 0; j0 < n_keys; j0 += CHUNK) {
+      const int v = j0 + tid;
+      pr[tid] = v < n_keys ? fast_exp2(score(v) - m) : 0.f;  // scores are log2-scaled
+      __syncthreads();
+      if (tid < DH) {
+        const int nv = min(CHUNK, n_keys - j0);
+        for (int j = 0; j < nv; ++j) {
+          acc += pr[j] * to_f<bf16>(vx[(size_t)(j0 + j) * DH + tid]);
+          lsum += pr[j];
+        }
+      }
+      __syncthreads();
+    }
+    if (tid < DH)
+      ((bf16*)p.out)[(((size_t)b * p.Nq + i) * p.H + h) * DH + tid] = (bf16)(n_keys > 0 && lsum > 0.f ? acc / lsum : 0.f);
+  }
+}
+
+template <int DC, int DR, int DH>
+static hipError_t launch_heads_t(const HeadsParams& p, hipStream_t s) {
+  typedef HeadsTile<DH, DR> F;
+  const int nk_max = p.W * p.T;
+  hipLaunchKernelGGL((expand_kv_kernel<DC, DR, DH>), dim3((nk_max + kExpKeys - 1) / kExpKeys, p.H, p.batch),
+                     dim3(512), 0, s, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const long long pieces = (long long)p.batch * p.Nq * p.H * ((DH + DR) / 8);
+  hipLaunchKernelGGL((heads_qcat_kernel<DH, DR>), dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL((heads_flash_kernel<DH, DR>), dim3(p.batch * p.H * p.n_rb), dim3(F::kThreads), 0, s, p);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL((heads_exact_kernel<DH, DR>), dim3(kFallbackBlocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+bool heads_supported(int dtype, int d_c, int d_rope, int d_head) {
+  return dtype == 0 && d_head == 128 &&
+         ((d_c == 192 && d_rope == 32) || (d_c == 128 && d_rope == 32) || (d_c == 160 && d_rope == 64) ||
+          (d_c == 192 && d_rope == 64));
+}
+
+hipError_t launch_heads(int d_c, int d_rope, int d_head, const HeadsParams& p, hipStream_t s) {
+  if (p.batch <= 0 || p.Nq <= 0) return hipSuccess;
+  if (d_head != 128) return hipErrorInvalidValue;
+  if (d_c == 192 && d_rope == 32) return launch_heads_t<192, 32, 128>(p, s);
+  if (d_c == 128 && d_rope == 32) return launch_heads_t<128, 32, 128>(p, s);
+  if (d_c == 160 && d_rope == 64) return launch_heads_t<160, 64, 128>(p, s);
+  if (d_c == 192 && d_rope == 64) return launch_heads_t<192, 64, 128>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mla

@@ -243,6 +243,27 @@ mla_status check_query_args(const mla_shape* s, int q_frame_first, int q_n_frame
   return MLA_OK;
 }
 
+// Per-head form workspace: fallback count and row list, the window's rotated
+// kR, the expanded keys and values of every head, the concatenated queries.
+struct HeadsWs {
+  size_t count, rows, krot, k_exp, v_exp, q_cat, total;
+};
+
+HeadsWs heads_ws_layout(const mla_shape* s, int q_n_frames) {
+  const size_t nq = (size_t)q_n_frames * tokens_per_frame(s);
+  const size_t nk = (size_t)s->window_frames * tokens_per_frame(s);
+  const size_t e = elt_size(s);
+  HeadsWs w;
+  w.count = 0;
+  w.rows = 256;
+  w.krot = w.rows + round256((size_t)s->batch * s->n_heads * nq * sizeof(int));
+  w.k_exp = w.krot + round256((size_t)s->batch * nk * s->d_rope * e);
+  w.v_exp = w.k_exp + round256((size_t)s->batch * s->n_heads * nk * s->d_head * e);
+  w.q_cat = w.v_exp + round256((size_t)s->batch * s->n_heads * nk * s->d_head * e);
+  w.total = w.q_cat + round256((size_t)s->batch * s->n_heads * nq * (s->d_head + s->d_rope) * e);
+  return w;
+}
+
 }  // namespace
 
 MLA_API int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
@@ -410,3 +431,76 @@ MLA_API mla_status mla_chunk_attend(const mla_shape* shape, const void* q_nope, 
     return st;
   return do_up_v(shape, o_lat, q_n_frames, w_uv, out, s);
 }
+
+MLA_API size_t mla_chunk_attend_heads_workspace_bytes(const mla_shape* shape, int32_t q_n_frames) {
+  if (check_shape(shape) != MLA_OK || q_n_frames < 1) return 0;
+  if (!mla::heads_supported(shape->dtype == MLA_BF16 ? 0 : 1, shape->d_c, shape->d_rope, shape->d_head)) return 0;
+  return heads_ws_layout(shape, q_n_frames).total;
+}
+
+MLA_API mla_status mla_chunk_attend_heads(const mla_shape* shape, const void* q_nope, const void* q_r,
+                                          int32_t q_frame_first, int32_t q_n_frames, const void* w_uk,
+                                          const void* w_uv, const void* cache, const int32_t* slot_frame,
+                                          const float* rope_tables, int32_t rope_t_first, int32_t rope_n_t,
+                                          void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!mla::heads_supported(shape->dtype == MLA_BF16 ? 0 : 1, shape->d_c, shape->d_rope, shape->d_head))
+    return MLA_ERR_UNSUPPORTED;
+  if (!q_nope || !q_r || !w_uk || !w_uv || !cache || !slot_frame || !out || !workspace) return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || !aligned16(q_r) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(cache) ||
+      !aligned16(slot_frame) || !aligned16(out) || !aligned16(workspace))
+    return MLA_ERR_ALIGN;
+  if ((st = check_tables(shape, rope_tables, rope_t_first, rope_n_t)) != MLA_OK) return st;
+  if ((st = check_query_args(shape, q_frame_first, q_n_frames)) != MLA_OK) return st;
+  if (q_frame_first < rope_t_first || (int64_t)q_frame_first + q_n_frames > (int64_t)rope_t_first + rope_n_t)
+    return MLA_ERR_RANGE;
+  const HeadsWs w = heads_ws_layout(shape, q_n_frames);
+  if (workspace_bytes < w.total) return MLA_ERR_WORKSPACE;
+  char* base = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  const int T = (int)tokens_per_frame(shape);
+  // rotated kR of the window (and the fallback count cleared) by the latent
+  // form's rotation pass
+  mla::FlashParams fp = {};
+  fp.cache = cache;
+  fp.slot_frame = slot_frame;
+  fp.tables = rope_tables;
+  fp.krot = base + w.krot;
+  fp.fallback_count = (int*)(base + w.count);
+  fp.rl = rope_layout(shape, rope_t_first, rope_n_t);
+  fp.W = shape->window_frames;
+  fp.T = T;
+  fp.grid_y = shape->grid_y;
+  fp.grid_x = shape->grid_x;
+  fp.batch = shape->batch;
+  hipError_t e = mla::launch_rope_window(shape->dtype == MLA_BF16 ? 0 : 1, shape->d_c, shape->d_rope, fp, s);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  mla::HeadsParams p = {};
+  p.q_nope = q_nope;
+  p.q_r = q_r;
+  p.w_uk = w_uk;
+  p.w_uv = w_uv;
+  p.cache = cache;
+  p.slot_frame = slot_frame;
+  p.tables = rope_tables;
+  p.out = out;
+  p.q_cat = base + w.q_cat;
+  p.k_exp = base + w.k_exp;
+  p.v_exp = base + w.v_exp;
+  p.krot = base + w.krot;
+  p.fallback_count = (int*)(base + w.count);
+  p.fallback_rows = (int*)(base + w.rows);
+  p.rl = fp.rl;
+  p.batch = shape->batch;
+  p.H = shape->n_heads;
+  p.Nq = (int)(q_n_frames * T);
+  p.T = T;
+  p.W = shape->window_frames;
+  p.grid_x = shape->grid_x;
+  p.q_frame_first = q_frame_first;
+  p.n_rb = (p.Nq + 255) / 256;
+  p.qscale = scale_log2(shape);
+  return from_hip(mla::launch_heads(shape->d_c, shape->d_rope, shape->d_head, p, s));
+}
+

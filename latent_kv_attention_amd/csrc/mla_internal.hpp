@@ -87,10 +87,38 @@ struct UpVParams {
   int rows, H, d_head;
 };
 
+// Per-head form of the attention: keys and values of every head are
+// reconstructed from the latent for the window once per call, then a
+// standard two-part-score attention runs per head.
+struct HeadsParams {
+  const void* q_nope;      // [B][Nq][H][d_head]
+  const void* q_r;         // [B][Nq][H][d_rope], unrotated
+  const void* w_uk;        // [H][d_head][d_c]
+  const void* w_uv;        // [H][d_head][d_c]
+  const void* cache;       // [B][W][T][d_c + d_rope]
+  const int32_t* slot_frame;
+  const float* tables;
+  void* out;               // [B][Nq][H][d_head]
+  void* q_cat;             // [B][H][Nq][d_head + d_rope]: [q_nope | R(p) q_r] * scale * log2 e
+  void* k_exp;             // [B][H][W * T][d_head]: W_uk[h] c_j of each valid key j, in key order
+  void* v_exp;             // [B][H][W * T][d_head]: W_uv[h] c_j
+  const void* krot;        // [B][W * T][d_rope]: rotated kR (the rotation pass of the latent form)
+  int* fallback_count;     // rows listed for the exact fallback
+  int* fallback_rows;      // [B * H * Nq], as (b * H + h) * Nq + i
+  RopeLayout rl;
+  int batch, H, Nq, T, W, grid_x, q_frame_first, n_rb;
+  float qscale;            // softmax scale * log2(e)
+};
+
 hipError_t launch_rope_tables(const RopeTableParams& p, hipStream_t s);
 hipError_t launch_cache_write(int dtype, int d_c, int d_rope, const CacheWriteParams& p, hipStream_t s);
 hipError_t launch_absorb_q(int dtype, int d_c, int d_rope, const AbsorbParams& p, hipStream_t s);
 hipError_t launch_flash(int dtype, int d_c, int d_rope, const FlashParams& p, bool split, hipStream_t s);
 hipError_t launch_up_v(int dtype, int d_c, int d_rope, const UpVParams& p, hipStream_t s);
+// the rotation pass of the attention kernel alone (rotated kR of the window
+// into p.krot, fallback count cleared)
+hipError_t launch_rope_window(int dtype, int d_c, int d_rope, const FlashParams& p, hipStream_t s);
+bool heads_supported(int dtype, int d_c, int d_rope, int d_head);
+hipError_t launch_heads(int d_c, int d_rope, int d_head, const HeadsParams& p, hipStream_t s);
 
 }  // namespace mla

@@ -37,6 +37,7 @@ class LatentLayer:
         self.max_chunk_frames = nf
         self.workspace = torch.empty(_lib.chunk_attend_workspace_bytes(self.shape, nf), dtype=torch.uint8,
                                      device=device)
+        self.heads_workspace = None  # allocated on the first per-head call
 
     def write(self, x, frame_first: int, n_frames: int, stream=None) -> None:
         """Cache write of frames frame_first .. +n_frames (x [B][n_frames*T][hidden])."""
@@ -53,4 +54,22 @@ class LatentLayer:
         _lib.chunk_attend(self.shape, q_nope, q_r, q_frame_first, q_n_frames, self.w["w_uk"], self.w["w_uv"],
                           self.cache, self.slot_frame, self.tables, self.rope_t_first, self.rope_n_t, out,
                           self.workspace, stream)
+        return out
+
+    def attend_heads(self, q_nope, q_r, q_frame_first: int, q_n_frames: int, out=None, stream=None):
+        """Same as attend(), by the per-head form (keys and values of every head
+        expanded for the window, then per-head attention)."""
+        if q_n_frames > self.max_chunk_frames:
+            raise ValueError("chunk larger than the workspace was sized for")
+        if self.heads_workspace is None:
+            n = _lib.chunk_attend_heads_workspace_bytes(self.shape, self.max_chunk_frames)
+            if n == 0:
+                raise ValueError("the per-head form does not support this shape")
+            self.heads_workspace = torch.empty(n, dtype=torch.uint8, device=self.device)
+        if out is None:
+            out = torch.empty(self.B, q_n_frames * self.T, self.cfg.n_heads, self.cfg.d_head, dtype=self.dtype,
+                              device=self.device)
+        _lib.chunk_attend_heads(self.shape, q_nope, q_r, q_frame_first, q_n_frames, self.w["w_uk"], self.w["w_uv"],
+                                self.cache, self.slot_frame, self.tables, self.rope_t_first, self.rope_n_t, out,
+                                self.heads_workspace, stream)
         return out

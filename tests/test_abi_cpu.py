@@ -87,6 +87,11 @@ def test_host_queries(built_lib):
     assert ws >= rows * 224 * 2 + rows * 192 * 2
     assert mla.flash_workspace_bytes(wan, 3, 4) > mla.flash_workspace_bytes(wan, 3, 1)
     assert mla.flash_workspace_bytes(wan, 3, 17) == 0
+    # per-head form: expanded keys and values of every head dominate its workspace
+    hws = mla.chunk_attend_heads_workspace_bytes(wan, 3)
+    assert hws >= 2 * 12 * 21 * 1560 * 128 * 2 + 12 * rows // 12 * (128 + 32) * 2
+    assert mla.chunk_attend_heads_workspace_bytes(_shape("wan_small_f32"), 1) == 0
+    assert mla.chunk_attend_heads_workspace_bytes(_shape(d_head=64), 3) == 0
 
 
 def test_entry_points_reject_bad_arguments_before_launch(built_lib):
@@ -111,6 +116,12 @@ def test_entry_points_reject_bad_arguments_before_launch(built_lib):
     assert lib.mla_flash_attend(sp, fake, 3, fake, fake, fake, 0, 21, fake, 17, fake, 1 << 30, None) == 8
     assert lib.mla_chunk_attend(sp, fake, fake, 0, 3, fake, fake, fake, fake, fake, 0, 21, fake, fake, 16,
                                 None) == 5
+    # per-head form: workspace too small; shapes it does not cover (fp32, other head widths)
+    assert lib.mla_chunk_attend_heads(sp, fake, fake, 0, 3, fake, fake, fake, fake, fake, 0, 21, fake, fake, 16,
+                                      None) == 5
+    f32 = _shape("wan_small_f32")
+    assert lib.mla_chunk_attend_heads(ctypes.byref(f32), fake, fake, 0, 1, fake, fake, fake, fake, fake, 0, 21,
+                                      fake, fake, 1 << 40, None) == 6
     # unsupported latent width
     bad = _shape(d_c=96)
     assert lib.mla_cache_write(ctypes.byref(bad), fake, fake, fake, 0, 3, fake, fake, None) == 6
