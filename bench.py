@@ -163,8 +163,12 @@ def setup_step(cfg, kv_splits, dev="cuda"):
         if ev:
             ev[4].record()
 
+    def write():
+        mla.cache_write(shape, x_chunk, w["w_dkv"], w["w_kr"], chunk_first, cfg.chunk_frames, cache, slot_frame)
+
     return types.SimpleNamespace(shape=shape, w=w, x_chunk=x_chunk, chunk_first=chunk_first, cache=cache,
-                                 slot_frame=slot_frame, out=out, step=step)
+                                 slot_frame=slot_frame, out=out, step=step, write=write, qn=qn, qr=qr,
+                                 tables=tables, n_t=n_t)
 
 
 def time_steps(ctx, steps, warmup):
@@ -224,6 +228,63 @@ def latent_sweep(base, args):
         torch.cuda.empty_cache()
 
 
+def per_head_report(base, args):
+    """The chunk step by the per-head form (cache write, then
+    mla_chunk_attend_heads: kR rotation, key/value expansion for every head,
+    query scaling and rotation, per-head attention) next to the latent form,
+    at each latent width of the sweep. One JSON report line per width; not
+    the bench line."""
+    import numpy as np
+    import torch
+
+    import latent_kv_attention_amd as mla
+
+    for dc, dr, split in SWEEP_WIDTHS:
+        cfg = base.with_(d_c=dc, d_rope=dr, rope_split=split)
+        ctx = setup_step(cfg, args.kv_splits)
+        ms_latent, per_latent = time_steps(ctx, args.steps, args.warmup)
+        ws = torch.empty(mla.chunk_attend_heads_workspace_bytes(ctx.shape, cfg.chunk_frames), dtype=torch.uint8,
+                         device="cuda")
+        out_h = torch.empty_like(ctx.out)
+
+        def attend():
+            mla.chunk_attend_heads(ctx.shape, ctx.qn, ctx.qr, ctx.chunk_first, cfg.chunk_frames, ctx.w["w_uk"],
+                                   ctx.w["w_uv"], ctx.cache, ctx.slot_frame, ctx.tables, 0, ctx.n_t, out_h, ws)
+
+        for _ in range(args.warmup):
+            ctx.write()
+            attend()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for e in evs:
+            e[0].record()
+            ctx.write()
+            e[1].record()
+            attend()
+            e[2].record()
+        torch.cuda.synchronize()
+        ms_w = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        ms_a = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        diff = (out_h.float() - ctx.out.float()).abs()
+        nq, nk, H = cfg.n_q, cfg.n_k, cfg.n_heads
+        attn_fl = 2.0 * nq * nk * H * (cfg.d_head + cfg.d_rope + cfg.d_head)
+        expand_fl = 4.0 * nk * H * cfg.d_head * cfg.d_c
+        latent_ms = per_latent["absorb_q"] + per_latent["flash_attend"] + per_latent["up_v"]
+        print(json.dumps({
+            "report": "per-head form vs latent form, Wan2.1-1.3B-shaped chunk step (4680 queries x 32760 keys), "
+                      "1 MI355X",
+            "d_c": dc, "d_rope": dr, "d_head": cfg.d_head,
+            "per_head_attend_ms": round(ms_a, 4), "latent_attend_ms": round(latent_ms, 4),
+            "per_head_step_ms": round(ms_w + ms_a, 4), "latent_step_ms": round(ms_latent, 4),
+            "speedup_attend": round(latent_ms / ms_a, 3),
+            "per_head_own_TFLOPs": round((attn_fl + expand_fl) / (ms_a * 1e-3) / 1e12, 2),
+            "per_head_attention_flops": attn_fl, "per_head_expansion_flops": expand_fl,
+            "max_abs_diff_vs_latent_form": round(float(diff.max()), 5),
+            "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic"}), flush=True)
+        del ctx, ws, out_h
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +295,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-buffers", type=int, default=40,
                     help="rotating x buffers for the cold-cache cache-write measurement (0 = skip)")
+    ap.add_argument("--per-head", action="store_true",
+                    help="time the per-head form against the latent form at every width (report lines) and exit")
     ap.add_argument("--latent-sweep", action="store_true",
                     help="time the step at every latent width with kernels (one report line each) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -271,6 +334,9 @@ def main():
     cfg = get_config("wan")
     if args.latent_sweep:
         latent_sweep(cfg, args)
+        return
+    if args.per_head:
+        per_head_report(cfg, args)
         return
     ctx = setup_step(cfg, args.kv_splits)
     ms_step, per = time_steps(ctx, args.steps, args.warmup)

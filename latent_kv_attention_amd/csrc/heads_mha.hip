@@ -11,9 +11,10 @@
 // the latent form's 2 Nq Nk H (d_c + d_rope + d_c); the expansion adds
 // 4 Nk H d_head d_c products and writes 4 Nk H d_head bytes (bf16).
 //
-// Attention layout (bf16): a work-group owns 256 query tokens of one head
-// (8 waves x 32 rows, two waves per SIMD) and visits every key tile of the
-// window. Key tiles of 128 keys are staged in LDS, double buffered, with
+// Attention layout (bf16): a row block is 256 query tokens of one head (8
+// waves x 32 rows, two waves per SIMD); one work-group per compute unit
+// takes an equal share of the (row block, key tile) units, and row blocks
+// shared by several work-groups are merged afterwards. Key tiles of 128 keys are staged in LDS, double buffered, with
 // direct global->LDS loads from three contiguous row sets: k_exp (rows 272
 // bytes apart), the rotated kR (packed, 16-byte units XOR-swizzled by key)
 // and v_exp (rows 288 bytes apart, the stride at which the transposing reads
@@ -204,10 +205,6 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
-  const int rb = blockIdx.x % p.n_rb;
-  const int bh = blockIdx.x / p.n_rb;  // b * H + h
-  const int h = bh % p.H, b = bh / p.H;
-
   // direct-load slots: instruction k of the wave fills chunks [64 i, 64 i + 64)
   // of a region, i = wave + kWaves k; packed (key << 16) | byte offset in the
   // key's source row, or -1 for padding chunks and spare instructions
@@ -228,189 +225,285 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
     rpk[k] = (ins < F::R_INSTR && n < kBN) ? (n << 16) | (F::kr_slot(n, us) * 16) : -1;
   }
 
-  if (wave == 0) {
-    const int f = lane < p.W ? p.slot_frame[b * p.W + lane] : -1;
-    const unsigned long long mask = __ballot(f >= 0);
-    if (lane == 0) n_valid_sh = __popcll(mask);
-  }
-  __syncthreads();
-  const int n_keys = n_valid_sh * p.T;
-  const int n_tiles = (n_keys + kBN - 1) / kBN;
-
-  // queries of this wave (B operand of S^T = K Q^T), kept in registers
   typedef bf16x8 v8;
-  const int tok_wave = rb * F::kRowsBlock + wave * F::kRowsWave;
-  const bf16* qb = (const bf16*)p.q_cat + (size_t)bh * p.Nq * F::QP;
-  v8 qf[kNMB][F::NKC];
-#pragma unroll
-  for (int mb = 0; mb < kNMB; ++mb) {
-    const int tok = tok_wave + mb * 16 + li;
-#pragma unroll
-    for (int kc = 0; kc < F::NKC; ++kc)
-      qf[mb][kc] = tok < p.Nq ? load8<bf16>(qb + (size_t)tok * F::QP + kc * 32 + lg * 8) : zero8<bf16>();
-  }
-  f32x4 negref[kNMB];
-  f32x4 o[F::NDB][kNMB];
-  float l_run[kNMB];
-#pragma unroll
-  for (int mb = 0; mb < kNMB; ++mb) {
-    negref[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    l_run[mb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < F::NDB; ++db) o[db][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const size_t head_rows = (size_t)bh * p.W * p.T;
-  const char* kb_src = (const char*)((const bf16*)p.k_exp + head_rows * DH);
-  const char* vb_src = (const char*)((const bf16*)p.v_exp + head_rows * DH);
-  const char* rb_src = (const char*)((const bf16*)p.krot + (size_t)b * p.W * p.T * DR);
-
-  // position 0 visits the last tile (the one that can be ragged), positions
-  // 1.. the others in order
-  auto tile_of = [&](int pos) { return pos == 0 ? n_tiles - 1 : pos - 1; };
-  auto issue = [&](int pos, bf16* kt, bf16* vt, bf16* rt) {
-    const int kbase = tile_of(pos) * kBN;
-#pragma unroll
-    for (int k = 0; k < F::K_IW; ++k) {
-      const int pk = opaque_h(kpk[k]);
-      if (pk >= 0) {
-        const int v = min(kbase + (pk >> 16), n_keys - 1);
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(kb_src + (unsigned)(v * DH * 2 + (pk & 0xffff))),
-            (MLA_LDS void*)(MLA_LDS bf16*)(kt + (wave + kWaves * k) * 64 * 8), 16, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < F::V_IW; ++k) {
-      const int pk = opaque_h(vpk[k]);
-      if (pk >= 0) {
-        const int v = min(kbase + (pk >> 16), n_keys - 1);
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(vb_src + (unsigned)(v * DH * 2 + (pk & 0xffff))),
-            (MLA_LDS void*)(MLA_LDS bf16*)(vt + (wave + kWaves * k) * 64 * 8), 16, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < F::R_IW; ++k) {
-      const int pk = opaque_h(rpk[k]);
-      if (pk >= 0) {
-        const int v = min(kbase + (pk >> 16), n_keys - 1);
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(rb_src + (unsigned)(v * DR * 2 + (pk & 0xffff))),
-            (MLA_LDS void*)(MLA_LDS bf16*)(rt + (wave + kWaves * k) * 64 * 8), 16, 0, 0);
-      }
-    }
-  };
-
   typedef f32x4 sblk[2][kNMB];
-  auto scores = [&](const bf16* kt, const bf16* rt, int half, sblk& s, const f32x4 (&seed)[kNMB]) {
-#pragma unroll
-    for (int kc = 0; kc < F::NKC; ++kc) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int row = (half * 2 + kb) * 16 + li, dim = kc * 32 + lg * 8;
-        const v8 a = kc < F::NKCH ? lds_load8<bf16>(kt + row * F::LSK + dim)
-                                  : lds_load8<bf16>(rt + row * DR + F::kr_slot(row, (dim - DH) / 8) * 8);
-#pragma unroll
-        for (int mb = 0; mb < kNMB; ++mb) s[kb][mb] = mma16(a, qf[mb][kc], kc == 0 ? seed[mb] : s[kb][mb]);
-      }
-    }
-  };
-  auto probs = [&](const sblk& s, v8 (&pb)[kNMB], int kfirst, auto ragged_c) {
-    constexpr bool RAGGED = decltype(ragged_c)::value;
-#pragma unroll
-    for (int mb = 0; mb < kNMB; ++mb) {
-      float f8[8];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float e = fast_exp2(s[kb][mb][i]);
-          if constexpr (RAGGED) e = kfirst + kb * 16 + lg * 4 + i < n_keys ? e : 0.f;
-          f8[kb * 4 + i] = e;
-          l_run[mb] += e;
-        }
-      pb[mb] = pack8<bf16>(f8);
-    }
-  };
-  auto values = [&](const bf16* vt, int half, const v8 (&pb)[kNMB]) {
-#pragma unroll
-    for (int db = 0; db < F::NDB; ++db) {
-      const v8 a = lds_tr8(vt, F::LSV, half * 32 + lg * 4, half * 32 + 16 + lg * 4, db * 16);
-#pragma unroll
-      for (int mb = 0; mb < kNMB; ++mb) o[db][mb] = mma16(a, pb[mb], o[db][mb]);
-    }
-  };
   typedef std::integral_constant<int, 0> B0;
   typedef std::integral_constant<int, 1> B1;
-  auto step = [&](int pos, auto cur_c, auto ragged_c) {
-    constexpr int CUR = decltype(cur_c)::value;
-    const bf16* kt = CUR == 0 ? k0 : k1;
-    const bf16* vt = CUR == 0 ? v0 : v1;
-    const bf16* rt = CUR == 0 ? r0 : r1;
-    if (pos + 1 < n_tiles) {
-      if constexpr (CUR == 0) issue(pos + 1, k1, v1, r1);
-      else issue(pos + 1, k0, v0, r0);
-    }
-    const int kbase = tile_of(pos) * kBN;
-#pragma unroll 1
-    for (int half = 0; half < NKC2; ++half) {
-      sblk s;
-      scores(kt, rt, half, s, negref);
-      v8 pb[kNMB];
-      probs(s, pb, kbase + half * 32, ragged_c);
-      values(vt, half, pb);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // direct loads of the next tile have landed
-    __syncthreads();
-  };
 
-  if (n_tiles > 0) {
-    issue(0, k0, v0, r0);
-    __builtin_amdgcn_s_waitcnt(0);
+  // Work-group g takes units [g U / G, (g + 1) U / G) of the (row block, key
+  // tile) grid as segments of at most one row block each, last to first (so
+  // most work-groups read the same few key tiles at any moment). A segment
+  // covering its whole row block writes the output; a partial one writes
+  // (output / sum, reference, sum) to slot 0 (the work-group's first segment)
+  // or 1 (its last) for the merge pass.
+  const long long G = p.grid;
+  const long long u_first = (long long)blockIdx.x * p.units / G;
+  const long long u_last = ((long long)blockIdx.x + 1) * p.units / G;
+  for (long long u = u_last; u > u_first;) {
+    const long long rbg = (u - 1) / p.nt_max;  // row block over all (stream, head) pairs
+    const long long seg0 = max(u_first, rbg * p.nt_max);
+    const int j0 = (int)(seg0 - rbg * p.nt_max), j1 = (int)(u - rbg * p.nt_max);
+    const bool first_seg = seg0 == u_first;
+    const bool whole = j0 == 0 && j1 == p.nt_max;
+    u = seg0;
+    const int bh = (int)(rbg / p.n_rb), rb = (int)(rbg - (long long)bh * p.n_rb);  // bh = b * H + h
+    const int h = bh % p.H, b = bh / p.H;
+    __syncthreads();  // LDS of the previous segment is no longer read
+    if (wave == 0) {
+      const int f = lane < p.W ? p.slot_frame[b * p.W + lane] : -1;
+      const unsigned long long mask = __ballot(f >= 0);
+      if (lane == 0) n_valid_sh = __popcll(mask);
+    }
     __syncthreads();
-    // reference of each row: the maximum of its scores over the first 32 keys
-    const int kbase = tile_of(0) * kBN;
-    sblk s;
-    const f32x4 zs[kNMB] = {};
-    scores(k0, r0, 0, s, zs);
+    const int n_keys = n_valid_sh * p.T;
+    const int n_tiles = (n_keys + kBN - 1) / kBN;
+    // this segment's share of the window's tiles (units map onto the tiles
+    // of a full window; a partly filled window scales proportionally)
+    const int tile_begin = (int)((long long)j0 * n_tiles / p.nt_max);
+    const int tile_end = (int)((long long)j1 * n_tiles / p.nt_max);
+    const int n_visit = max(0, tile_end - tile_begin);
+
+    // queries of this wave (B operand of S^T = K Q^T), kept in registers
+    const int tok_wave = rb * F::kRowsBlock + wave * F::kRowsWave;
+    const bf16* qb = (const bf16*)p.q_cat + (size_t)bh * p.Nq * F::QP;
+    v8 qf[kNMB][F::NKC];
 #pragma unroll
     for (int mb = 0; mb < kNMB; ++mb) {
-      float mx = -__builtin_inff();
+      const int tok = tok_wave + mb * 16 + li;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kc = 0; kc < F::NKC; ++kc)
+        qf[mb][kc] = tok < p.Nq ? load8<bf16>(qb + (size_t)tok * F::QP + kc * 32 + lg * 8) : zero8<bf16>();
+    }
+    f32x4 negref[kNMB];
+    f32x4 o[F::NDB][kNMB];
+    float l_run[kNMB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (kbase + kb * 16 + lg * 4 + i < n_keys) mx = fmaxf(mx, s[kb][mb][i]);
-      mx = wave_max_across_groups(mx);
-      negref[mb] = f32x4{-mx, -mx, -mx, -mx};
+    for (int mb = 0; mb < kNMB; ++mb) {
+      negref[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      l_run[mb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < F::NDB; ++db) o[db][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    step(0, B0(), std::integral_constant<bool, true>());
-    typedef std::integral_constant<bool, false> Full;
-    int pos = 1;
-    for (; pos + 1 < n_tiles; pos += 2) {
-      step(pos, B1(), Full());
-      step(pos + 1, B0(), Full());
-    }
-    if (pos < n_tiles) step(pos, B1(), Full());
-  }
 
-  // epilogue: out[b][i][h][:] = o / l; a lane holds four consecutive outputs
-  const int eln = opaque_h(lane);
-  const int eli = eln & 15, elg = eln >> 4;
+    const size_t head_rows = (size_t)bh * p.W * p.T;
+    const char* kb_src = (const char*)((const bf16*)p.k_exp + head_rows * DH);
+    const char* vb_src = (const char*)((const bf16*)p.v_exp + head_rows * DH);
+    const char* rb_src = (const char*)((const bf16*)p.krot + (size_t)b * p.W * p.T * DR);
+
+    // position 0 visits the last tile of the range (the one that can be
+    // ragged), positions 1.. the others in order
+    auto tile_of = [&](int pos) { return pos == 0 ? tile_end - 1 : tile_begin + pos - 1; };
+    auto issue = [&](int pos, bf16* kt, bf16* vt, bf16* rt) {
+      const int kbase = tile_of(pos) * kBN;
 #pragma unroll
-  for (int mb = 0; mb < kNMB; ++mb) {
-    const float l = wave_sum_across_groups(l_run[mb]);
-    const int tok = tok_wave + mb * 16 + eli;
-    if (tok >= p.Nq) continue;
-    const bool ok = l <= kHeadsSumLimit;  // false for inf / NaN as well
-    const float inv = (ok && l > 0.f) ? 1.f / l : 0.f;
-    bf16* dst = (bf16*)p.out + (((size_t)b * p.Nq + tok) * p.H + h) * DH;
+      for (int k = 0; k < F::K_IW; ++k) {
+        const int pk = opaque_h(kpk[k]);
+        if (pk >= 0) {
+          const int v = min(kbase + (pk >> 16), n_keys - 1);
+          __builtin_amdgcn_global_load_lds(
+              (const __attribute__((address_space(1))) void*)(kb_src + (unsigned)(v * DH * 2 + (pk & 0xffff))),
+              (MLA_LDS void*)(MLA_LDS bf16*)(kt + (wave + kWaves * k) * 64 * 8), 16, 0, 0);
+        }
+      }
 #pragma unroll
-    for (int db = 0; db < F::NDB; ++db)
-      store4_bf16(dst + db * 16 + elg * 4, o[db][mb][0] * inv, o[db][mb][1] * inv, o[db][mb][2] * inv,
-                  o[db][mb][3] * inv);
-    if (!ok && elg == 0) p.fallback_rows[atomicAdd(p.fallback_count, 1)] = bh * p.Nq + tok;
+      for (int k = 0; k < F::V_IW; ++k) {
+        const int pk = opaque_h(vpk[k]);
+        if (pk >= 0) {
+          const int v = min(kbase + (pk >> 16), n_keys - 1);
+          __builtin_amdgcn_global_load_lds(
+              (const __attribute__((address_space(1))) void*)(vb_src + (unsigned)(v * DH * 2 + (pk & 0xffff))),
+              (MLA_LDS void*)(MLA_LDS bf16*)(vt + (wave + kWaves * k) * 64 * 8), 16, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < F::R_IW; ++k) {
+        const int pk = opaque_h(rpk[k]);
+        if (pk >= 0) {
+          const int v = min(kbase + (pk >> 16), n_keys - 1);
+          __builtin_amdgcn_global_load_lds(
+              (const __attribute__((address_space(1))) void*)(rb_src + (unsigned)(v * DR * 2 + (pk & 0xffff))),
+              (MLA_LDS void*)(MLA_LDS bf16*)(rt + (wave + kWaves * k) * 64 * 8), 16, 0, 0);
+        }
+      }
+    };
+    auto scores = [&](const bf16* kt, const bf16* rt, int half, sblk& s, const f32x4 (&seed)[kNMB]) {
+#pragma unroll
+      for (int kc = 0; kc < F::NKC; ++kc) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int row = (half * 2 + kb) * 16 + li, dim = kc * 32 + lg * 8;
+          const v8 a = kc < F::NKCH ? lds_load8<bf16>(kt + row * F::LSK + dim)
+                                    : lds_load8<bf16>(rt + row * DR + F::kr_slot(row, (dim - DH) / 8) * 8);
+#pragma unroll
+          for (int mb = 0; mb < kNMB; ++mb) s[kb][mb] = mma16(a, qf[mb][kc], kc == 0 ? seed[mb] : s[kb][mb]);
+        }
+      }
+    };
+    auto probs = [&](const sblk& s, v8 (&pb)[kNMB], int kfirst, auto ragged_c) {
+      constexpr bool RAGGED = decltype(ragged_c)::value;
+#pragma unroll
+      for (int mb = 0; mb < kNMB; ++mb) {
+        float f8[8];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float e = fast_exp2(s[kb][mb][i]);
+            if constexpr (RAGGED) e = kfirst + kb * 16 + lg * 4 + i < n_keys ? e : 0.f;
+            f8[kb * 4 + i] = e;
+            l_run[mb] += e;
+          }
+        pb[mb] = pack8<bf16>(f8);
+      }
+    };
+    auto values = [&](const bf16* vt, int half, const v8 (&pb)[kNMB]) {
+#pragma unroll
+      for (int db = 0; db < F::NDB; ++db) {
+        const v8 a = lds_tr8(vt, F::LSV, half * 32 + lg * 4, half * 32 + 16 + lg * 4, db * 16);
+#pragma unroll
+        for (int mb = 0; mb < kNMB; ++mb) o[db][mb] = mma16(a, pb[mb], o[db][mb]);
+      }
+    };
+    auto step = [&](int pos, auto cur_c, auto ragged_c) {
+      constexpr int CUR = decltype(cur_c)::value;
+      const bf16* kt = CUR == 0 ? k0 : k1;
+      const bf16* vt = CUR == 0 ? v0 : v1;
+      const bf16* rt = CUR == 0 ? r0 : r1;
+      if (pos + 1 < n_visit) {
+        if constexpr (CUR == 0) issue(pos + 1, k1, v1, r1);
+        else issue(pos + 1, k0, v0, r0);
+      }
+      const int kbase = tile_of(pos) * kBN;
+#pragma unroll 1
+      for (int half = 0; half < NKC2; ++half) {
+        sblk s;
+        scores(kt, rt, half, s, negref);
+        v8 pb[kNMB];
+        probs(s, pb, kbase + half * 32, ragged_c);
+        values(vt, half, pb);
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // direct loads of the next tile have landed
+      __syncthreads();
+    };
+
+    if (n_visit > 0) {
+      issue(0, k0, v0, r0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      // reference of each row: the maximum of its scores over the first 32 keys
+      const int kbase = tile_of(0) * kBN;
+      sblk s;
+      const f32x4 zs[kNMB] = {};
+      scores(k0, r0, 0, s, zs);
+#pragma unroll
+      for (int mb = 0; mb < kNMB; ++mb) {
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kbase + kb * 16 + lg * 4 + i < n_keys) mx = fmaxf(mx, s[kb][mb][i]);
+        mx = wave_max_across_groups(mx);
+        negref[mb] = f32x4{-mx, -mx, -mx, -mx};
+      }
+      step(0, B0(), std::integral_constant<bool, true>());
+      typedef std::integral_constant<bool, false> Full;
+      int pos = 1;
+      for (; pos + 1 < n_visit; pos += 2) {
+        step(pos, B1(), Full());
+        step(pos + 1, B0(), Full());
+      }
+      if (pos < n_visit) step(pos, B1(), Full());
+    }
+
+    // epilogue: a lane holds four consecutive outputs of one row
+    const int eln = opaque_h(lane);
+    const int eli = eln & 15, elg = eln >> 4;
+#pragma unroll
+    for (int mb = 0; mb < kNMB; ++mb) {
+      const float l = wave_sum_across_groups(l_run[mb]);
+      const int tok = tok_wave + mb * 16 + eli;
+      if (tok >= p.Nq) continue;
+      const bool ok = l <= kHeadsSumLimit;  // false for inf / NaN as well
+      const float inv = (ok && l > 0.f) ? 1.f / l : 0.f;
+      if (whole) {
+        bf16* dst = (bf16*)p.out + (((size_t)b * p.Nq + tok) * p.H + h) * DH;
+#pragma unroll
+        for (int db = 0; db < F::NDB; ++db)
+          store4_bf16(dst + db * 16 + elg * 4, o[db][mb][0] * inv, o[db][mb][1] * inv, o[db][mb][2] * inv,
+                      o[db][mb][3] * inv);
+        if (!ok && elg == 0) p.fallback_rows[atomicAdd(p.fallback_count, 1)] = bh * p.Nq + tok;
+      } else {
+        const size_t prow =
+            ((size_t)blockIdx.x * 2 + (first_seg ? 0 : 1)) * F::kRowsBlock + (tok - rb * F::kRowsBlock);
+        bf16* dst = (bf16*)p.part_o + prow * DH;
+#pragma unroll
+        for (int db = 0; db < F::NDB; ++db)
+          store4_bf16(dst + db * 16 + elg * 4, o[db][mb][0] * inv, o[db][mb][1] * inv, o[db][mb][2] * inv,
+                      o[db][mb][3] * inv);
+        if (elg == 0) {
+          p.part_l[prow * 2] = n_visit == 0 ? -__builtin_inff() : -negref[mb][0];
+          p.part_l[prow * 2 + 1] = l;
+        }
+      }
+    }
+  }
+}
+
+// Merge of the partial results of a row block shared by work-groups g0..g1
+// (the work-groups whose unit ranges meet the row block's units): with
+// M = max_g r_g and w_g = 2^(r_g - M) l_g, out = sum_g w_g (o_g / l_g) / sum_g w_g.
+// A work-group takes 32 rows of one row block.
+constexpr int kHeadsMergeRows = 32;
+
+template <int DH>
+__global__ __launch_bounds__(256) void heads_combine_kernel(HeadsParams p) {
+  constexpr int RB = 256, NCH = DH / 8;
+  __shared__ long long slot_base[kMaxMergePieces];
+  const long long G = p.grid;
+  const long long rbg = blockIdx.x / (RB / kHeadsMergeRows);
+  const int row_lo = (int)(blockIdx.x % (RB / kHeadsMergeRows)) * kHeadsMergeRows;
+  const long long a = rbg * p.nt_max;
+  auto owner = [&](long long x) { return ((x + 1) * G - 1) / p.units; };  // largest g starting at or before x
+  const long long g0 = owner(a), g1 = owner(a + p.nt_max - 1);
+  if (g0 == g1) return;  // one work-group covered the row block and wrote it
+  const int np = (int)(g1 - g0 + 1);  // <= kMaxMergePieces by the host's cap on G
+  if ((int)threadIdx.x < np) {
+    const long long g = g0 + threadIdx.x;
+    const long long start = g * p.units / G;
+    slot_base[threadIdx.x] = (g * 2 + (start >= a ? 0 : 1)) * RB;
+  }
+  __syncthreads();
+  const int bh = (int)(rbg / p.n_rb), rb = (int)(rbg - (long long)bh * p.n_rb);
+  const int h = bh % p.H, b = bh / p.H;
+  const int rows = min(kHeadsMergeRows, p.Nq - rb * RB - row_lo);
+  for (int e = threadIdx.x; e < rows * NCH; e += blockDim.x) {
+    const int local = row_lo + e / NCH, c0 = (e % NCH) * 8;
+    float M = -__builtin_inff();
+    bool ok = true;
+    for (int k = 0; k < np; ++k) {
+      const size_t pr = (size_t)slot_base[k] + local;
+      M = fmaxf(M, p.part_l[pr * 2]);
+      ok = ok && (p.part_l[pr * 2 + 1] <= kHeadsSumLimit);
+    }
+    float L = 0.f, acc[8] = {};
+    if (M > -__builtin_inff()) {
+      for (int k = 0; k < np; ++k) {
+        const size_t pr = (size_t)slot_base[k] + local;
+        const float wl = fast_exp2(p.part_l[pr * 2] - M) * p.part_l[pr * 2 + 1];
+        L += wl;
+        float v[8];
+        unpack8<bf16>(load8<bf16>((const bf16*)p.part_o + pr * DH + c0), v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += wl * v[i];
+      }
+    }
+    const float inv = (ok && L > 0.f) ? 1.f / L : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= inv;
+    const int tok = rb * RB + local;
+    store8<bf16>((bf16*)p.out + (((size_t)b * p.Nq + tok) * p.H + h) * DH + c0, pack8<bf16>(acc));
+    if (!ok && c0 == 0) p.fallback_rows[atomicAdd(p.fallback_count, 1)] = bh * p.Nq + tok;
   }
 }
 
@@ -478,7 +571,7 @@ __global__ __launch_bounds__(256) void heads_exact_kernel(HeadsParams p) {
 }
 
 template <int DC, int DR, int DH>
-static hipError_t launch_heads_t(const HeadsParams& p, hipStream_t s) {
+static hipError_t launch_heads_t(const HeadsParams& p, bool split, hipStream_t s) {
   typedef HeadsTile<DH, DR> F;
   const int nk_max = p.W * p.T;
   hipLaunchKernelGGL((expand_kv_kernel<DC, DR, DH>), dim3((nk_max + kExpKeys - 1) / kExpKeys, p.H, p.batch),
@@ -488,8 +581,14 @@ static hipError_t launch_heads_t(const HeadsParams& p, hipStream_t s) {
   const long long pieces = (long long)p.batch * p.Nq * p.H * ((DH + DR) / 8);
   hipLaunchKernelGGL((heads_qcat_kernel<DH, DR>), dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL((heads_flash_kernel<DH, DR>), dim3(p.batch * p.H * p.n_rb), dim3(F::kThreads), 0, s, p);
+  hipLaunchKernelGGL((heads_flash_kernel<DH, DR>), dim3(p.grid), dim3(F::kThreads), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (split) {
+    static_assert(F::kRowsBlock == 256, "merge groups tile a 256-row block");
+    hipLaunchKernelGGL((heads_combine_kernel<DH>), dim3(p.batch * p.H * p.n_rb * (256 / kHeadsMergeRows)),
+                       dim3(256), 0, s, p);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   hipLaunchKernelGGL((heads_exact_kernel<DH, DR>), dim3(kFallbackBlocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
@@ -500,13 +599,20 @@ bool heads_supported(int dtype, int d_c, int d_rope, int d_head) {
           (d_c == 192 && d_rope == 64));
 }
 
-hipError_t launch_heads(int d_c, int d_rope, int d_head, const HeadsParams& p, hipStream_t s) {
-  if (p.batch <= 0 || p.Nq <= 0) return hipSuccess;
+int heads_tile_keys(int d_head, int d_rope) {
+  if (d_head != 128) return 0;
+  if (d_rope == 32) return HeadsTile<128, 32>::kBN;
+  if (d_rope == 64) return HeadsTile<128, 64>::kBN;
+  return 0;
+}
+
+hipError_t launch_heads(int d_c, int d_rope, int d_head, const HeadsParams& p, bool split, hipStream_t s) {
+  if (p.batch <= 0 || p.Nq <= 0 || p.grid <= 0) return hipSuccess;
   if (d_head != 128) return hipErrorInvalidValue;
-  if (d_c == 192 && d_rope == 32) return launch_heads_t<192, 32, 128>(p, s);
-  if (d_c == 128 && d_rope == 32) return launch_heads_t<128, 32, 128>(p, s);
-  if (d_c == 160 && d_rope == 64) return launch_heads_t<160, 64, 128>(p, s);
-  if (d_c == 192 && d_rope == 64) return launch_heads_t<192, 64, 128>(p, s);
+  if (d_c == 192 && d_rope == 32) return launch_heads_t<192, 32, 128>(p, split, s);
+  if (d_c == 128 && d_rope == 32) return launch_heads_t<128, 32, 128>(p, split, s);
+  if (d_c == 160 && d_rope == 64) return launch_heads_t<160, 64, 128>(p, split, s);
+  if (d_c == 192 && d_rope == 64) return launch_heads_t<192, 64, 128>(p, split, s);
   return hipErrorInvalidValue;
 }
 

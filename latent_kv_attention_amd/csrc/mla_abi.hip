@@ -243,10 +243,31 @@ mla_status check_query_args(const mla_shape* s, int q_frame_first, int q_n_frame
   return MLA_OK;
 }
 
+// Work split of the per-head attention kernel: (row block of 256 tokens of
+// one (stream, head), key tile) units shared evenly by one work-group per
+// compute unit, as for the latent form.
+FlashPlan heads_plan(const mla_shape* s, int q_n_frames) {
+  FlashPlan f;
+  const int64_t nq = (int64_t)q_n_frames * tokens_per_frame(s);
+  const int tk = mla::heads_tile_keys(s->d_head, s->d_rope);
+  f.n_rb = (int)((nq + 255) / 256);
+  f.nt_max = (int)((s->window_frames * tokens_per_frame(s) + tk - 1) / tk);
+  const int64_t row_blocks = (int64_t)s->batch * s->n_heads * f.n_rb;
+  f.units = row_blocks * f.nt_max;
+  int64_t g = device_cus();
+  if (g > f.units) g = f.units;
+  if (g > (mla::kMaxMergePieces - 1) * row_blocks) g = (mla::kMaxMergePieces - 1) * row_blocks;
+  if (g < 1) g = 1;
+  f.grid = (int)g;
+  f.split = !(f.units % g == 0 && (f.units / g) % f.nt_max == 0);
+  return f;
+}
+
 // Per-head form workspace: fallback count and row list, the window's rotated
-// kR, the expanded keys and values of every head, the concatenated queries.
+// kR, the expanded keys and values of every head, the concatenated queries,
+// and the partial-result slots of split row blocks.
 struct HeadsWs {
-  size_t count, rows, krot, k_exp, v_exp, q_cat, total;
+  size_t count, rows, krot, k_exp, v_exp, q_cat, part_o, part_l, total;
 };
 
 HeadsWs heads_ws_layout(const mla_shape* s, int q_n_frames) {
@@ -260,7 +281,11 @@ HeadsWs heads_ws_layout(const mla_shape* s, int q_n_frames) {
   w.k_exp = w.krot + round256((size_t)s->batch * nk * s->d_rope * e);
   w.v_exp = w.k_exp + round256((size_t)s->batch * s->n_heads * nk * s->d_head * e);
   w.q_cat = w.v_exp + round256((size_t)s->batch * s->n_heads * nk * s->d_head * e);
-  w.total = w.q_cat + round256((size_t)s->batch * s->n_heads * nq * (s->d_head + s->d_rope) * e);
+  w.part_o = w.q_cat + round256((size_t)s->batch * s->n_heads * nq * (s->d_head + s->d_rope) * e);
+  const FlashPlan f = heads_plan(s, q_n_frames);
+  const size_t slots = f.split ? (size_t)f.grid * 2 * 256 : 0;
+  w.part_l = w.part_o + round256(slots * s->d_head * e);
+  w.total = w.part_l + round256(slots * 2 * sizeof(float));
   return w;
 }
 
@@ -455,6 +480,8 @@ MLA_API mla_status mla_chunk_attend_heads(const mla_shape* shape, const void* q_
   if ((st = check_query_args(shape, q_frame_first, q_n_frames)) != MLA_OK) return st;
   if (q_frame_first < rope_t_first || (int64_t)q_frame_first + q_n_frames > (int64_t)rope_t_first + rope_n_t)
     return MLA_ERR_RANGE;
+  const FlashPlan f = heads_plan(shape, q_n_frames);
+  if (!flash_plan_ok(f)) return MLA_ERR_SHAPE;
   const HeadsWs w = heads_ws_layout(shape, q_n_frames);
   if (workspace_bytes < w.total) return MLA_ERR_WORKSPACE;
   char* base = (char*)workspace;
@@ -499,8 +526,13 @@ MLA_API mla_status mla_chunk_attend_heads(const mla_shape* shape, const void* q_
   p.W = shape->window_frames;
   p.grid_x = shape->grid_x;
   p.q_frame_first = q_frame_first;
-  p.n_rb = (p.Nq + 255) / 256;
+  p.part_o = f.split ? (void*)(base + w.part_o) : nullptr;
+  p.part_l = f.split ? (float*)(base + w.part_l) : nullptr;
+  p.n_rb = f.n_rb;
+  p.nt_max = f.nt_max;
+  p.units = f.units;
+  p.grid = f.grid;
   p.qscale = scale_log2(shape);
-  return from_hip(mla::launch_heads(shape->d_c, shape->d_rope, shape->d_head, p, s));
+  return from_hip(mla::launch_heads(shape->d_c, shape->d_rope, shape->d_head, p, f.split, s));
 }
 
