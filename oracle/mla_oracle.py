@@ -31,6 +31,10 @@ the design notes of the repository):
   * scale defaults to 1/sqrt(d_head + d_rope).
   * Every query attends every valid window key (no intra-chunk mask); a query
     with no valid key outputs zeros.
+  * Frame-causal variant (chunk-wise autoregressive reading, hyper.ai summary,
+    Method, and chatpaper.ai abstract): a query of frame f attends only keys of
+    frames <= f; earlier chunks are wholly visible and the query's own frame is
+    visible. Off unless asked for.
   * The ring buffer keeps frame f in slot f mod W; a slot is valid iff its
     recorded frame index is >= 0.
 
@@ -45,7 +49,7 @@ import numpy as np
 __all__ = [
     "default_scale", "rope_inv_freq", "rope_axis_cos_sin", "rope_tables", "rope_tables_flat",
     "rotate_pairs", "rope3d", "frame_positions", "latents", "reconstruct", "attend",
-    "RingCache", "chunk_step", "absorbed_query", "attend_latent", "up_project",
+    "RingCache", "chunk_step", "absorbed_query", "attend_latent", "up_project", "frame_causal_mask",
     "chunk_step_absorbed", "cache_scalars_per_token", "dense_scalars_per_token",
 ]
 
@@ -165,13 +169,31 @@ def reconstruct(c: np.ndarray, w_uk: np.ndarray, w_uv: np.ndarray):
 
 # ---------------------------------------------------------------- attention [Method], [Abstract]
 
-def attend(q_nope, q_rope, k_nope, k_rope, v, scale: float, block: int = 64) -> np.ndarray:
+def frame_causal_mask(q_frames, k_frames) -> np.ndarray:
+    """visible[i, j] = key j's frame <= query i's frame (the frame-causal variant)."""
+    return np.asarray(q_frames)[:, None] >= np.asarray(k_frames)[None, :]
+
+
+def _masked_softmax_rows(s: np.ndarray, visible) -> np.ndarray:
+    """Row softmax of s [..., Nk] over the keys marked visible (all when None);
+    rows with no visible key get all-zero weights."""
+    if visible is not None:
+        s = np.where(visible, s, -np.inf)
+    m = s.max(axis=-1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    p = np.exp(s - m)
+    tot = p.sum(axis=-1, keepdims=True)
+    return np.divide(p, tot, out=np.zeros_like(p), where=tot > 0)
+
+
+def attend(q_nope, q_rope, k_nope, k_rope, v, scale: float, block: int = 64, visible=None) -> np.ndarray:
     """Two-part-score softmax attention with explicit per-head keys and values.
 
     q_nope [Nq, H, dh], q_rope [Nq, H, dr] (already rotated), k_nope [Nk, H, dh],
     k_rope [Nk, dr] (already rotated, shared by all heads), v [Nk, H, dh].
-    Softmax over all Nk keys, max-subtracted, two passes. Returns [Nq, H, dh];
-    zeros when Nk == 0.
+    Softmax over all Nk keys (or over the keys visible[i] marks for query i),
+    max-subtracted, two passes. Returns [Nq, H, dh]; zeros for a query with no
+    key.
     """
     q_nope = np.asarray(q_nope, np.float64)
     nq, nh, dh = q_nope.shape
@@ -186,9 +208,7 @@ def attend(q_nope, q_rope, k_nope, k_rope, v, scale: float, block: int = 64) -> 
         qn = np.transpose(q_nope[i0:i1], (1, 0, 2))  # [H, b, dh]
         qr = np.transpose(np.asarray(q_rope[i0:i1], np.float64), (1, 0, 2))  # [H, b, dr]
         s = (np.matmul(qn, kn) + np.matmul(qr, krt)) * scale  # [H, b, Nk]
-        s -= s.max(axis=-1, keepdims=True)
-        p = np.exp(s)
-        p /= p.sum(axis=-1, keepdims=True)
+        p = _masked_softmax_rows(s, None if visible is None else visible[None, i0:i1])
         out[i0:i1] = np.transpose(np.matmul(p, vv), (1, 0, 2))
     return out
 
@@ -229,14 +249,15 @@ class RingCache:
 
 
 def chunk_step(cfg_dims: dict, w: dict, ring: RingCache, x_chunk, frame_first: int,
-               q_nope, q_r, scale: float | None = None, write: bool = True) -> np.ndarray:
+               q_nope, q_r, scale: float | None = None, write: bool = True,
+               frame_causal: bool = False) -> np.ndarray:
     """One layer's streaming chunk step for one stream, reconstructing per-head
     keys and values explicitly (no absorption).
 
     cfg_dims: d_head, d_rope, rope_split, rope_base, grid_y, grid_x.
     w: w_dkv, w_kr, w_uk, w_uv. x_chunk [n_frames*T, hidden] are the chunk's
     tokens (frames frame_first ..), q_nope/q_r their queries. Returns
-    out [Nq, n_h, d_h].
+    out [Nq, n_h, d_h]. frame_causal: a query of frame f sees keys of frames <= f.
     """
     gy, gx = cfg_dims["grid_y"], cfg_dims["grid_x"]
     split, base = cfg_dims["rope_split"], cfg_dims["rope_base"]
@@ -251,7 +272,8 @@ def chunk_step(cfg_dims: dict, w: dict, ring: RingCache, x_chunk, frame_first: i
     nq = np.asarray(q_nope).shape[0]
     tq, yq, xq = frame_positions(frame_first + np.arange(nq // (gy * gx)), gy, gx)
     q_rope = rope3d(q_r, tq, yq, xq, split, base)
-    return attend(q_nope, q_rope, k_nope, k_rope, v, scale)
+    visible = frame_causal_mask(tq, t) if frame_causal else None
+    return attend(q_nope, q_rope, k_nope, k_rope, v, scale, visible=visible)
 
 
 # ---------------------------------------------------------------- absorbed form (stage checks)
@@ -265,10 +287,11 @@ def absorbed_query(q_nope, q_r, w_uk, t, y, x, split, base) -> np.ndarray:
     return np.concatenate([qa, qr], axis=-1)
 
 
-def attend_latent(q_abs, c, k_rope, scale: float, block: int = 64) -> np.ndarray:
+def attend_latent(q_abs, c, k_rope, scale: float, block: int = 64, visible=None) -> np.ndarray:
     """Attention in latent space: s = scale * q_abs . [c ; k_rope], softmax over
-    keys, output sum_j p_j c_j. q_abs [Nq, H, d_c + dr], c [Nk, d_c],
-    k_rope [Nk, dr] (rotated). Returns [Nq, H, d_c]; zeros when Nk == 0."""
+    keys (those visible[i] marks, when given), output sum_j p_j c_j.
+    q_abs [Nq, H, d_c + dr], c [Nk, d_c], k_rope [Nk, dr] (rotated). Returns
+    [Nq, H, d_c]; zeros for a query with no key."""
     q_abs = np.asarray(q_abs, np.float64)
     nq, nh, _ = q_abs.shape
     dc = c.shape[-1]
@@ -279,9 +302,8 @@ def attend_latent(q_abs, c, k_rope, scale: float, block: int = 64) -> np.ndarray
     for i0 in range(0, nq, block):
         i1 = min(nq, i0 + block)
         s = (q_abs[i0:i1].reshape(-1, q_abs.shape[-1]) @ kt) * scale  # [b*H, Nk]
-        s -= s.max(axis=-1, keepdims=True)
-        p = np.exp(s)
-        p /= p.sum(axis=-1, keepdims=True)
+        vis = None if visible is None else np.repeat(visible[i0:i1], nh, axis=0)
+        p = _masked_softmax_rows(s, vis)
         out[i0:i1] = (p @ c).reshape(i1 - i0, nh, dc)
     return out
 

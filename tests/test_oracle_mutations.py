@@ -34,12 +34,20 @@ _orig_reconstruct = O.reconstruct
 _orig_rope3d = O.rope3d
 
 
-def _attend_no_rope(qn, qr, kn, kr, v, scale, block=64):
-    return _orig_attend(qn, np.zeros_like(qr), kn, np.zeros_like(kr), v, scale, block)
+def _attend_no_rope(qn, qr, kn, kr, v, scale, block=64, visible=None):
+    return _orig_attend(qn, np.zeros_like(qr), kn, np.zeros_like(kr), v, scale, block, visible=visible)
 
 
-def _attend_wrong_scale(qn, qr, kn, kr, v, scale, block=64):
-    return _orig_attend(qn, qr, kn, kr, v, scale * np.sqrt(160.0 / 128.0), block)
+def _attend_wrong_scale(qn, qr, kn, kr, v, scale, block=64, visible=None):
+    return _orig_attend(qn, qr, kn, kr, v, scale * np.sqrt(160.0 / 128.0), block, visible=visible)
+
+
+def _attend_mask_ignored(qn, qr, kn, kr, v, scale, block=64, visible=None):
+    return _orig_attend(qn, qr, kn, kr, v, scale, block)
+
+
+def _causal_strict(q_frames, k_frames):
+    return np.asarray(q_frames)[:, None] > np.asarray(k_frames)[None, :]
 
 
 def _reconstruct_swapped(c, w_uk, w_uv):
@@ -51,7 +59,7 @@ def _rope3d_axes_swapped(v, t, y, x, split, base):
     return _orig_rope3d(v, t, x, y, split, base)
 
 
-def _attend_softmax_over_heads(qn, qr, kn, kr, v, scale, block=64):
+def _attend_softmax_over_heads(qn, qr, kn, kr, v, scale, block=64, visible=None):
     s = (np.einsum("qhd,khd->qhk", qn, kn) + np.einsum("qhr,kr->qhk", qr, kr)) * scale
     s = s - s.max(axis=1, keepdims=True)
     p = np.exp(s)
@@ -68,6 +76,8 @@ MUTATIONS = {
     "keys_values_swapped": ("reconstruct", _reconstruct_swapped),
     "rope_axes_swapped": ("rope3d", _rope3d_axes_swapped),
     "softmax_axis": ("attend", _attend_softmax_over_heads),
+    "causal_mask_ignored": ("attend", _attend_mask_ignored),
+    "causal_mask_strict": ("frame_causal_mask", _causal_strict),
 }
 
 
@@ -77,7 +87,7 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
     monkeypatch.setattr(O, attr, fn)
     caught = 0
     for check in (P.test_oracle_matches_brute_force_tiny, P.test_rope3d_blocks_equal_textbook_1d,
-                  P.test_oracle_matches_brute_force_partial_window):
+                  P.test_oracle_matches_brute_force_partial_window, P.test_frame_causal_matches_brute_force):
         try:
             check()
         except AssertionError:
@@ -91,3 +101,4 @@ def test_unmutated_oracle_passes_same_checks():
     P.test_oracle_matches_brute_force_tiny()
     P.test_rope3d_blocks_equal_textbook_1d()
     P.test_oracle_matches_brute_force_partial_window()
+    P.test_frame_causal_matches_brute_force()

@@ -310,9 +310,11 @@ def test_mla_with_full_rank_latent_equals_dense_mha():
 
 # ------------------------------------------------------------------ pure-Python brute force
 
-def _brute_force_step(cfg, w, xs_window, frames_window, x_chunk_frames, qn, qr, q_frame_first):
+def _brute_force_step(cfg, w, xs_window, frames_window, x_chunk_frames, qn, qr, q_frame_first,
+                      frame_causal=False):
     """Triple loop over (query, head, key) with explicit reconstruction, from the
-    definitions only (math module, Python floats)."""
+    definitions only (math module, Python floats). frame_causal: a query of
+    frame f skips the keys of later frames."""
     gy, gx = cfg.grid_y, cfg.grid_x
     dc, dr, dh, nh = cfg.d_c, cfg.d_rope, cfg.d_head, cfg.n_heads
     split, base = cfg.rope_split, cfg.rope_base
@@ -336,20 +338,23 @@ def _brute_force_step(cfg, w, xs_window, frames_window, x_chunk_frames, qn, qr, 
             kr = [sum(w["w_kr"][a][b] * xv[b] for b in range(len(xv))) for a in range(dr)]
             kn = [[sum(w["w_uk"][h][d][a] * c[a] for a in range(dc)) for d in range(dh)] for h in range(nh)]
             vv = [[sum(w["w_uv"][h][d][a] * c[a] for a in range(dc)) for d in range(dh)] for h in range(nh)]
-            keys.append((kn, vv, rot(kr, f, tok // gx, tok % gx)))
+            keys.append((kn, vv, rot(kr, f, tok // gx, tok % gx), f))
     out = np.zeros((qn.shape[0], nh, dh))
     for i in range(qn.shape[0]):
         f = q_frame_first + i // (gy * gx)
         tok = i % (gy * gx)
+        seen = [k for k in keys if not frame_causal or k[3] <= f]
+        if not seen:
+            continue
         for h in range(nh):
             qrot = rot(list(qr[i, h]), f, tok // gx, tok % gx)
             s = [scale * (sum(qn[i, h, d] * kn[h][d] for d in range(dh))
-                          + sum(qrot[d] * krr[d] for d in range(dr))) for kn, _, krr in keys]
+                          + sum(qrot[d] * krr[d] for d in range(dr))) for kn, _, krr, _ in seen]
             m = max(s)
             e = [math.exp(z - m) for z in s]
             tot = sum(e)
             for d in range(dh):
-                out[i, h, d] = sum(e[j] * keys[j][1][h][d] for j in range(len(keys))) / tot
+                out[i, h, d] = sum(e[j] * seen[j][1][h][d] for j in range(len(seen))) / tot
     return out
 
 
@@ -402,3 +407,57 @@ def test_bf16_rounding_is_round_to_nearest_even():
     assert from_bf16_bits(to_bf16_bits([1.0 + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6
     assert from_bf16_bits(to_bf16_bits([-2.5]))[0] == -2.5
     assert to_bf16_bits([1.0])[0] == 0x3F80
+
+
+# ------------------------------------------------------------------ frame-causal variant
+
+def _causal_ring(cfg, seed, frames_before, chunk_first):
+    w = layer_weights(cfg, seed)
+    ring = O.RingCache(cfg.window_frames, cfg.tokens_per_frame, cfg.d_c, cfg.d_rope)
+    for f in frames_before:
+        c, kr = O.latents(frame_tokens(cfg, f, seed), w["w_dkv"], w["w_kr"])
+        ring.write(f, c, kr)
+    x_chunk = np.concatenate([frame_tokens(cfg, chunk_first + i, seed) for i in range(cfg.chunk_frames)])
+    qn, qr = chunk_queries(cfg, chunk_first, seed)
+    return w, ring, x_chunk, qn, qr
+
+
+def test_frame_causal_matches_brute_force():
+    """Two-frame chunk: queries of its first frame skip the second frame's keys
+    (brute force from the definition, with the skip written out)."""
+    cfg = get_config("tiny").with_(chunk_frames=2, window_frames=4)
+    w, ring, x_chunk, qn, qr = _causal_ring(cfg, 21, [0, 1], 2)
+    out = O.chunk_step(_dims(cfg), w, ring, x_chunk, 2, qn, qr, frame_causal=True)
+    xs = [frame_tokens(cfg, f, 21) for f in range(4)]
+    bf = _brute_force_step(cfg, w, xs, [0, 1, 2, 3], None, qn, qr, 2, frame_causal=True)
+    np.testing.assert_allclose(out, bf, rtol=0, atol=1e-12)
+
+
+def test_frame_causal_equals_window_without_later_frames():
+    """The frame-causal rows of chunk frame f equal the unmasked step of a ring
+    that never received the frames after f (a different route: what is in the
+    window instead of which scores are masked), here with the ring wrapped:
+    after the chunk the window holds frames 3..6."""
+    cfg = get_config("tiny").with_(chunk_frames=3, window_frames=4)
+    T = cfg.tokens_per_frame
+    w, ring, x_chunk, qn, qr = _causal_ring(cfg, 22, [0, 1, 2, 3], 4)
+    out = O.chunk_step(_dims(cfg), w, ring, x_chunk, 4, qn, qr, frame_causal=True)
+    assert sorted(ring.slot_frame.tolist()) == [3, 4, 5, 6]
+    for k in range(3):  # chunk frame 4 + k
+        f = 4 + k
+        ring_k = O.RingCache(cfg.window_frames, T, cfg.d_c, cfg.d_rope)
+        for g in range(3, f + 1):
+            c, kr = O.latents(frame_tokens(cfg, g, 22), w["w_dkv"], w["w_kr"])
+            ring_k.write(g, c, kr)
+        ref = O.chunk_step(_dims(cfg), w, ring_k, None, f, qn[k * T:(k + 1) * T], qr[k * T:(k + 1) * T],
+                           write=False)
+        np.testing.assert_allclose(out[k * T:(k + 1) * T], ref, rtol=0, atol=1e-12)
+
+
+def test_frame_causal_single_frame_chunk_is_unmasked():
+    cfg = get_config("tiny").with_(chunk_frames=1)
+    w, ring, x_chunk, qn, qr = _causal_ring(cfg, 23, [0, 1], 2)
+    a = O.chunk_step(_dims(cfg), w, ring, x_chunk, 2, qn, qr, frame_causal=True)
+    b = O.chunk_step(_dims(cfg), w, ring, None, 2, qn, qr, write=False)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
