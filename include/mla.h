@@ -211,6 +211,21 @@ mla_status mla_chunk_attend(const mla_shape* shape, const void* q_nope, const vo
                             int32_t rope_n_t, void* out, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* ---------------------------------------------------------------- a3..a5, frame-causal
+ * mla_chunk_attend with a frame-causal mask inside the chunk (the
+ * chunk-wise autoregressive reading of the hyper.ai summary, Method, and the
+ * chatpaper.ai abstract): a query of frame f = q_frame_first + i / T attends
+ * only the keys of frames <= f. Keys of earlier chunks are all visible and
+ * a query always sees its own frame's keys (when they are in the window).
+ * Same arguments, workspace (mla_chunk_attend_workspace_bytes) and errors as
+ * mla_chunk_attend. Key tiles that no row of a 256-row block can see are
+ * skipped; tiles that every row sees run unmasked. */
+mla_status mla_chunk_attend_frame_causal(const mla_shape* shape, const void* q_nope, const void* q_r,
+                                         int32_t q_frame_first, int32_t q_n_frames, const void* w_uk,
+                                         const void* w_uv, const void* cache, const int32_t* slot_frame,
+                                         const float* rope_tables, int32_t rope_t_first, int32_t rope_n_t,
+                                         void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------- a3'..a5'
  * Per-head form of the same step (hyper.ai summary, Method: per-head keys
  * and values are reconstructed from the shared latent when needed). Same

@@ -26,7 +26,7 @@ EXPORTS = [
     "mla_rope3d_table_floats", "mla_rope3d_tables", "mla_cache_write", "mla_absorb_q",
     "mla_flash_workspace_bytes", "mla_flash_attend", "mla_up_v",
     "mla_chunk_attend_workspace_bytes", "mla_chunk_attend",
-    "mla_chunk_attend_heads_workspace_bytes", "mla_chunk_attend_heads",
+    "mla_chunk_attend_heads_workspace_bytes", "mla_chunk_attend_heads", "mla_chunk_attend_frame_causal",
 ]
 
 
@@ -65,6 +65,7 @@ _SIGS = {
     "mla_chunk_attend_workspace_bytes": (_SZ, [_SP, _I]),
     "mla_chunk_attend": (_I, [_SP, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
     "mla_chunk_attend_heads_workspace_bytes": (_SZ, [_SP, _I]),
+    "mla_chunk_attend_frame_causal": (_I, [_SP, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
     "mla_chunk_attend_heads": (_I, [_SP, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
 }
 
@@ -188,3 +189,14 @@ def chunk_attend_heads(shape: MlaShape, q_nope, q_r, q_frame_first: int, q_n_fra
                                         _ptr(w_uk), _ptr(w_uv), _ptr(cache), _ptr(slot_frame), _ptr(tables),
                                         rope_t_first, rope_n_t, _ptr(out), _ptr(workspace), nbytes,
                                         _stream(stream)))
+
+
+def chunk_attend_frame_causal(shape: MlaShape, q_nope, q_r, q_frame_first: int, q_n_frames: int, w_uk, w_uv, cache,
+                              slot_frame, tables, rope_t_first: int, rope_n_t: int, out, workspace,
+                              stream=None) -> None:
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("mla_chunk_attend_frame_causal",
+           lib().mla_chunk_attend_frame_causal(ctypes.byref(shape), _ptr(q_nope), _ptr(q_r), q_frame_first,
+                                               q_n_frames, _ptr(w_uk), _ptr(w_uv), _ptr(cache), _ptr(slot_frame),
+                                               _ptr(tables), rope_t_first, rope_n_t, _ptr(out), _ptr(workspace),
+                                               nbytes, _stream(stream)))

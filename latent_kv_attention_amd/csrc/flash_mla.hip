@@ -149,7 +149,11 @@ __global__ __launch_bounds__(256) void rope_window_kernel(FlashParams p) {
 }
 
 // ---------------------------------------------------------------- main kernel
-template <typename T, int DC, int DR>
+// CAUSAL: the frame-causal variant (a query of frame f attends only keys of
+// frames <= f); tiles whose keys are all visible to the row block run
+// unmasked, tiles with no visible key are skipped, the rest are masked per
+// key.
+template <typename T, int DC, int DR, bool CAUSAL>
 __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla_kernel(FlashParams p) {
   typedef FlashTile<T, DC, DR> F;
   typedef typename V8<T>::type v8;
@@ -164,6 +168,7 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
   __shared__ __attribute__((aligned(16))) T kr0[F::KR_ELEMS];
   __shared__ __attribute__((aligned(16))) T kr1[F::KR_ELEMS];
   __shared__ int slot_of[kMaxSlots];
+  __shared__ int frame_of[kMaxSlots];  // frame held by the r-th valid slot (frame-causal variant)
   __shared__ int n_valid_sh;
   __shared__ int keytab[2][kBN];  // per key of a tile: byte offset of its cache row
 
@@ -224,7 +229,11 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     if (wave == 0) {
       const int f = lane < p.W ? p.slot_frame[b * p.W + lane] : -1;
       const unsigned long long mask = __ballot(f >= 0);
-      if (f >= 0) slot_of[__popcll(mask & ((1ull << lane) - 1ull))] = lane;
+      if (f >= 0) {
+        const int rank = __popcll(mask & ((1ull << lane) - 1ull));
+        slot_of[rank] = lane;
+        if constexpr (CAUSAL) frame_of[rank] = f;
+      }
       if (lane == 0) n_valid_sh = __popcll(mask);
     }
     __syncthreads();
@@ -236,6 +245,23 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     const int tile_begin = (int)((long long)j0 * n_tiles / p.nt_max);
     const int tile_end = (int)((long long)j1 * n_tiles / p.nt_max);
     const int n_visit = max(0, tile_end - tile_begin);
+
+    // frame-causal variant: query frame of this lane's two rows (rows are
+    // (token, head) pairs, H per token, T tokens per frame) and the range of
+    // query frames of the row block
+    int qfr[kNMB] = {};
+    int rb_fmin = 0, rb_fmax = 0;
+    if constexpr (CAUSAL) {
+      const int rows_per_frame = p.T * p.H;
+#pragma unroll
+      for (int mb = 0; mb < kNMB; ++mb) {
+        const int row = row_wave + mb * 16 + li;
+        qfr[mb] = row < p.Mb ? p.q_frame_first + row / rows_per_frame : 0x7fffffff;
+      }
+      const int r_first = rb * F::kRowsBlock, r_last = min(r_first + F::kRowsBlock, p.Mb) - 1;
+      rb_fmin = p.q_frame_first + r_first / rows_per_frame;
+      rb_fmax = p.q_frame_first + r_last / rows_per_frame;
+    }
 
     // queries of this wave (B operand of S^T = K Q^T), kept in registers
     v8 qf[kNMB][F::NKC];
@@ -347,7 +373,7 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     };
     // probabilities 2^s, packed into the B operand of the value product; with
     // RAGGED, keys at or past n_keys (kfirst = key index of the half) get 0
-    auto probs = [&](const sblk& s, v8 (&pb)[kNMB], int kfirst, auto ragged_c) {
+    auto probs = [&](const sblk& s, v8 (&pb)[kNMB], int kfirst, auto ragged_c, bool masked) {
       constexpr bool RAGGED = decltype(ragged_c)::value;
 #pragma unroll
       for (int mb = 0; mb < kNMB; ++mb) {
@@ -358,6 +384,12 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
           for (int i = 0; i < 4; ++i) {
             float e = fast_exp2(s[kb][mb][i]);
             if constexpr (RAGGED) e = kfirst + kb * 16 + lg * 4 + i < n_keys ? e : 0.f;
+            if constexpr (CAUSAL) {
+              if (masked) {
+                const int key = min(kfirst + kb * 16 + lg * 4 + i, n_keys - 1);
+                e = frame_of[div_floor(key, p.T, p.inv_T)] <= qfr[mb] ? e : 0.f;
+              }
+            }
             f8[kb * 4 + i] = e;
             l_run[mb] += e;
           }
@@ -379,6 +411,19 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     typedef std::integral_constant<int, 0> B0;
     typedef std::integral_constant<int, 1> B1;
 
+    // frame-causal variant: frames of the tile's keys against the row
+    // block's query frames (a tile spans at most kBN / T + 2 slot ranks)
+    auto tile_class = [&](int kbase) -> int {
+      const int r0 = kbase / p.T, r1 = (min(kbase + kBN, n_keys) - 1) / p.T;
+      int fmin = 0x7fffffff, fmax = -0x7fffffff;
+      for (int r = r0; r <= r1; ++r) {
+        const int f = frame_of[r];
+        fmin = min(fmin, f);
+        fmax = max(fmax, f);
+      }
+      return fmin > rb_fmax ? 2 : (fmax <= rb_fmin ? 0 : 1);
+    };
+
     // One tile: start the loads of the next position (descriptors ready),
     // describe the one after, consume this tile half by half, wait for the
     // next tile's loads, barrier.
@@ -394,13 +439,17 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
       }
       if (pos + 2 < n_visit) describe(pos + 2, keytab[CUR]);
       const int kbase = tile_of(pos) * kBN;
+      int cls = 0;  // 0: all keys visible to the block, 1: masked per key, 2: none visible
+      if constexpr (CAUSAL) cls = tile_class(kbase);
+      if (cls != 2) {
 #pragma unroll 1
-      for (int half = 0; half < NKC2; ++half) {
-        sblk s;
-        scores(cur, cur_r, half, s, negref);
-        v8 pb[kNMB];
-        probs(s, pb, kbase + half * 32, ragged_c);
-        values(cur, half, pb);
+        for (int half = 0; half < NKC2; ++half) {
+          sblk s;
+          scores(cur, cur_r, half, s, negref);
+          v8 pb[kNMB];
+          probs(s, pb, kbase + half * 32, ragged_c, cls == 1);
+          values(cur, half, pb);
+        }
       }
       __builtin_amdgcn_s_waitcnt(0);  // direct loads of the next tile have landed
       __syncthreads();
@@ -427,12 +476,32 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
 #pragma unroll
       for (int mb = 0; mb < kNMB; ++mb) {
         float mx = -__builtin_inff();
+        if constexpr (!CAUSAL) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (kbase + kb * 16 + lg * 4 + i < n_keys) mx = fmaxf(mx, s[kb][mb][i]);
-        mx = wave_max_across_groups(mx);
+            for (int i = 0; i < 4; ++i)
+              if (kbase + kb * 16 + lg * 4 + i < n_keys) mx = fmaxf(mx, s[kb][mb][i]);
+          mx = wave_max_across_groups(mx);
+        } else {
+          // the maximum over the visible keys among the first 32, else over
+          // all of them (a row that sees none of them still gets a reference
+          // of the scores' scale)
+          float mx_all = -__builtin_inff();
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = kbase + kb * 16 + lg * 4 + i;
+              if (key < n_keys) {
+                mx_all = fmaxf(mx_all, s[kb][mb][i]);
+                if (frame_of[div_floor(key, p.T, p.inv_T)] <= qfr[mb]) mx = fmaxf(mx, s[kb][mb][i]);
+              }
+            }
+          mx = wave_max_across_groups(mx);
+          mx_all = wave_max_across_groups(mx_all);
+          mx = mx > -__builtin_inff() ? mx : mx_all;
+        }
         negref[mb] = f32x4{-mx, -mx, -mx, -mx};
       }
       // position 0 is the only tile that can be ragged
@@ -569,7 +638,7 @@ __global__ __launch_bounds__(256) void flash_combine_kernel(FlashParams p) {
 // the textbook two-pass softmax: exact row maximum first, then the weighted
 // sum. One work-group per listed row (grid-stride over the list), keys striped
 // over threads. Slow, and only reached for rows whose bound was very loose.
-template <typename T, int DC, int DR>
+template <typename T, int DC, int DR, bool CAUSAL>
 __global__ __launch_bounds__(256) void flash_exact_kernel(FlashParams p) {
   constexpr int DK = DC + DR;
   constexpr int KP = (DC + DR + 31) / 32 * 32;
@@ -600,6 +669,9 @@ __global__ __launch_bounds__(256) void flash_exact_kernel(FlashParams p) {
     __syncthreads();
     const int n_keys = n_valid_sh * p.T;
     const T* cache_b = (const T*)p.cache + (size_t)b * p.W * p.T * DK;
+    // frame-causal variant: keys of frames after the row's query frame are skipped
+    const int qframe = p.q_frame_first + (grow - b * p.Mb) / (p.T * p.H);
+    auto visible = [&](int v) { return !CAUSAL || frame_of[v / p.T] <= qframe; };
     auto score = [&](int v) {
       const int rank = v / p.T, tok = v - rank * p.T;
       const T* row = cache_b + ((size_t)slot_of[rank] * p.T + tok) * DK;
@@ -616,7 +688,8 @@ __global__ __launch_bounds__(256) void flash_exact_kernel(FlashParams p) {
     };
     // pass 1: exact maximum
     float mx = -__builtin_inff();
-    for (int v = tid; v < n_keys; v += 256) mx = fmaxf(mx, score(v));
+    for (int v = tid; v < n_keys; v += 256)
+      if (visible(v)) mx = fmaxf(mx, score(v));
     red[tid] = mx;
     __syncthreads();
     for (int s = 128; s > 0; s >>= 1) {
@@ -629,7 +702,7 @@ __global__ __launch_bounds__(256) void flash_exact_kernel(FlashParams p) {
     float acc = 0.f, lsum = 0.f;
     for (int v0 = 0; v0 < n_keys; v0 += CHUNK) {
       const int v = v0 + tid;
-      pr[tid] = v < n_keys ? fast_exp2(score(v) - m) : 0.f;  // scores are log2-scaled
+      pr[tid] = v < n_keys && visible(v) ? fast_exp2(score(v) - m) : 0.f;  // scores are log2-scaled
       __syncthreads();
       if (tid < DC) {
         const int nv = min(CHUNK, n_keys - v0);
@@ -648,14 +721,14 @@ __global__ __launch_bounds__(256) void flash_exact_kernel(FlashParams p) {
   }
 }
 
-template <typename T, int DC, int DR>
-static hipError_t launch_flash_t(const FlashParams& p, bool split, hipStream_t s) {
+template <typename T, int DC, int DR, bool CAUSAL>
+static hipError_t launch_flash_v(const FlashParams& p, bool split, hipStream_t s) {
   typedef FlashTile<T, DC, DR> F;
   hipLaunchKernelGGL((rope_window_kernel<T, DC, DR>), dim3((p.T * (DR / 2) + 255) / 256, p.W, min(p.batch, 65535)),
                      dim3(256), 0, s, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((flash_mla_kernel<T, DC, DR>), dim3(p.grid), dim3(F::kThreads), 0, s, p);
+  hipLaunchKernelGGL((flash_mla_kernel<T, DC, DR, CAUSAL>), dim3(p.grid), dim3(F::kThreads), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (split) {
     static_assert(F::kRowsBlock % kMergeRows == 0, "merge groups tile a row block");
@@ -663,8 +736,13 @@ static hipError_t launch_flash_t(const FlashParams& p, bool split, hipStream_t s
                        dim3(p.batch * p.n_rb * (F::kRowsBlock / kMergeRows)), dim3(256), 0, s, p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  hipLaunchKernelGGL((flash_exact_kernel<T, DC, DR>), dim3(kFallbackBlocks), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((flash_exact_kernel<T, DC, DR, CAUSAL>), dim3(kFallbackBlocks), dim3(256), 0, s, p);
   return hipGetLastError();
+}
+
+template <typename T, int DC, int DR>
+static hipError_t launch_flash_t(const FlashParams& p, bool split, bool causal, hipStream_t s) {
+  return causal ? launch_flash_v<T, DC, DR, true>(p, split, s) : launch_flash_v<T, DC, DR, false>(p, split, s);
 }
 
 template <typename T, int DC, int DR>
@@ -688,11 +766,13 @@ hipError_t launch_rope_window(int dtype, int d_c, int d_rope, const FlashParams&
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_flash(int dtype, int d_c, int d_rope, const FlashParams& p, bool split, hipStream_t s) {
+hipError_t launch_flash(int dtype, int d_c, int d_rope, const FlashParams& p, bool split, bool causal,
+                        hipStream_t s) {
   if (p.Mb <= 0 || p.batch <= 0 || p.grid <= 0) return hipSuccess;
 #define MLA_FLASH_CASE(DCV, DRV)                                                                  \
   if (d_c == DCV && d_rope == DRV)                                                                \
-    return dtype == 0 ? launch_flash_t<bf16, DCV, DRV>(p, split, s) : launch_flash_t<float, DCV, DRV>(p, split, s);
+    return dtype == 0 ? launch_flash_t<bf16, DCV, DRV>(p, split, causal, s)                       \
+                      : launch_flash_t<float, DCV, DRV>(p, split, causal, s);
   MLA_FLASH_CASE(192, 32)
   MLA_FLASH_CASE(128, 32)
   MLA_FLASH_CASE(160, 64)

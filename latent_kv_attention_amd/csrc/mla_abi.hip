@@ -192,7 +192,7 @@ mla_status do_absorb(const mla_shape* s, const void* q_nope, const void* q_r, in
 
 mla_status do_flash(const mla_shape* s, const void* q_abs, int q_n_frames, const void* cache,
                     const int32_t* slot_frame, const float* tables, int rope_t_first, int rope_n_t, void* o_lat,
-                    int kv_splits, void* ws, hipStream_t st) {
+                    int kv_splits, void* ws, hipStream_t st, bool frame_causal = false, int q_frame_first = 0) {
   const FlashPlan f = flash_plan(s, q_n_frames, kv_splits);
   mla::FlashParams p;
   p.q_abs = q_abs;
@@ -221,7 +221,9 @@ mla_status do_flash(const mla_shape* s, const void* q_abs, int q_n_frames, const
   p.units = f.units;
   p.grid = f.grid;
   p.scale_log2 = scale_log2(s);
-  return from_hip(mla::launch_flash(s->dtype, s->d_c, s->d_rope, p, f.split, st));
+  p.H = s->n_heads;
+  p.q_frame_first = q_frame_first;
+  return from_hip(mla::launch_flash(s->dtype, s->d_c, s->d_rope, p, f.split, frame_causal, st));
 }
 
 mla_status do_up_v(const mla_shape* s, const void* o_lat, int q_n_frames, const void* w_uv, void* out,
@@ -424,11 +426,11 @@ MLA_API size_t mla_chunk_attend_workspace_bytes(const mla_shape* shape, int32_t 
          flash_ws_bytes(shape, q_n_frames, 0);
 }
 
-MLA_API mla_status mla_chunk_attend(const mla_shape* shape, const void* q_nope, const void* q_r, int32_t q_frame_first,
-                                    int32_t q_n_frames, const void* w_uk, const void* w_uv, const void* cache,
-                                    const int32_t* slot_frame, const float* rope_tables, int32_t rope_t_first,
-                                    int32_t rope_n_t, void* out, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
+static mla_status chunk_attend_impl(const mla_shape* shape, const void* q_nope, const void* q_r,
+                                    int32_t q_frame_first, int32_t q_n_frames, const void* w_uk, const void* w_uv,
+                                    const void* cache, const int32_t* slot_frame, const float* rope_tables,
+                                    int32_t rope_t_first, int32_t rope_n_t, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream, bool frame_causal) {
   mla_status st = check_shape(shape);
   if (st != MLA_OK) return st;
   if (!q_nope || !q_r || !w_uk || !w_uv || !cache || !slot_frame || !out || !workspace) return MLA_ERR_NULL;
@@ -452,9 +454,27 @@ MLA_API mla_status mla_chunk_attend(const mla_shape* shape, const void* q_nope, 
                       q_abs, s)) != MLA_OK)
     return st;
   if ((st = do_flash(shape, q_abs, q_n_frames, cache, slot_frame, rope_tables, rope_t_first, rope_n_t, o_lat, 0,
-                     ws, s)) != MLA_OK)
+                     ws, s, frame_causal, q_frame_first)) != MLA_OK)
     return st;
   return do_up_v(shape, o_lat, q_n_frames, w_uv, out, s);
+}
+
+MLA_API mla_status mla_chunk_attend(const mla_shape* shape, const void* q_nope, const void* q_r, int32_t q_frame_first,
+                                    int32_t q_n_frames, const void* w_uk, const void* w_uv, const void* cache,
+                                    const int32_t* slot_frame, const float* rope_tables, int32_t rope_t_first,
+                                    int32_t rope_n_t, void* out, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  return chunk_attend_impl(shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk, w_uv, cache, slot_frame, rope_tables,
+                           rope_t_first, rope_n_t, out, workspace, workspace_bytes, stream, false);
+}
+
+MLA_API mla_status mla_chunk_attend_frame_causal(const mla_shape* shape, const void* q_nope, const void* q_r,
+                                                 int32_t q_frame_first, int32_t q_n_frames, const void* w_uk,
+                                                 const void* w_uv, const void* cache, const int32_t* slot_frame,
+                                                 const float* rope_tables, int32_t rope_t_first, int32_t rope_n_t,
+                                                 void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_attend_impl(shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk, w_uv, cache, slot_frame, rope_tables,
+                           rope_t_first, rope_n_t, out, workspace, workspace_bytes, stream, true);
 }
 
 MLA_API size_t mla_chunk_attend_heads_workspace_bytes(const mla_shape* shape, int32_t q_n_frames) {

@@ -67,6 +67,7 @@ struct FlashParams {
   int W, T, grid_y, grid_x, batch;
   float inv_T, inv_grid_x; // 1/T and 1/grid_x (key index -> slot, row, column)
   int n_rb, nt_max;        // row blocks per stream, key tiles of a full window
+  int H, q_frame_first;    // heads; first query frame (frame-causal variant)
   long long units;         // batch * n_rb * nt_max
   int grid;                // G, work-groups of the attention kernel
   float scale_log2;        // softmax scale * log2(e)
@@ -118,7 +119,9 @@ struct HeadsParams {
 hipError_t launch_rope_tables(const RopeTableParams& p, hipStream_t s);
 hipError_t launch_cache_write(int dtype, int d_c, int d_rope, const CacheWriteParams& p, hipStream_t s);
 hipError_t launch_absorb_q(int dtype, int d_c, int d_rope, const AbsorbParams& p, hipStream_t s);
-hipError_t launch_flash(int dtype, int d_c, int d_rope, const FlashParams& p, bool split, hipStream_t s);
+// causal: the frame-causal variant (a query of frame f sees keys of frames <= f)
+hipError_t launch_flash(int dtype, int d_c, int d_rope, const FlashParams& p, bool split, bool causal,
+                        hipStream_t s);
 hipError_t launch_up_v(int dtype, int d_c, int d_rope, const UpVParams& p, hipStream_t s);
 // the rotation pass of the attention kernel alone (rotated kR of the window
 // into p.krot, fallback count cleared)

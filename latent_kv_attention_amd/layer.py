@@ -56,6 +56,19 @@ class LatentLayer:
                           self.workspace, stream)
         return out
 
+    def attend_frame_causal(self, q_nope, q_r, q_frame_first: int, q_n_frames: int, out=None, stream=None):
+        """attend() with the frame-causal mask inside the chunk (a query of frame
+        f sees keys of frames <= f)."""
+        if q_n_frames > self.max_chunk_frames:
+            raise ValueError("chunk larger than the workspace was sized for")
+        if out is None:
+            out = torch.empty(self.B, q_n_frames * self.T, self.cfg.n_heads, self.cfg.d_head, dtype=self.dtype,
+                              device=self.device)
+        _lib.chunk_attend_frame_causal(self.shape, q_nope, q_r, q_frame_first, q_n_frames, self.w["w_uk"],
+                                       self.w["w_uv"], self.cache, self.slot_frame, self.tables, self.rope_t_first,
+                                       self.rope_n_t, out, self.workspace, stream)
+        return out
+
     def attend_heads(self, q_nope, q_r, q_frame_first: int, q_n_frames: int, out=None, stream=None):
         """Same as attend(), by the per-head form (keys and values of every head
         expanded for the window, then per-head attention)."""

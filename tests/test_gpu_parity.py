@@ -368,6 +368,68 @@ def test_full_step_batch_and_partial_fill():
     assert_step_close(got, ref, cfg.dtype, label="wan_small B=3 fill=3")
 
 
+def _causal_step(cfg, seed, prefill_frames, chunk_first):
+    """Frames written one by one, then the chunk; frame-causal attention of the
+    chunk's queries against the oracle's frame-causal step."""
+    w, wd = device_weights(cfg, seed)
+    layer = LatentLayer(cfg, wd, batch=1, rope_n_t=64)
+    st = Stream(cfg, seed=seed)
+    ring = O.RingCache(cfg.window_frames, cfg.tokens_per_frame, cfg.d_c, cfg.d_rope)
+    for f in prefill_frames:
+        x = st.x(f)
+        layer.write(to_torch(x[None], cfg.dtype), f, 1)
+        ring.write(f, *O.latents(x, w["w_dkv"], w["w_kr"]))
+    xc = st.xs(chunk_first, cfg.chunk_frames)
+    layer.write(to_torch(xc[None], cfg.dtype), chunk_first, cfg.chunk_frames)
+    qn, qr = st.q(chunk_first)
+    out = layer.attend_frame_causal(to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype), chunk_first,
+                                    cfg.chunk_frames)
+    _sync()
+    ref = O.chunk_step(O.dims_of(cfg), w, ring, xc, chunk_first, qn, qr, frame_causal=True)
+    return to_numpy(out)[0], ref
+
+
+@pytest.mark.parametrize("name", STAGE_CONFIGS)
+def test_full_step_frame_causal(name):
+    """Two-frame chunk after two earlier frames: queries of the chunk's first
+    frame must not see the second frame's keys."""
+    cfg = get_config(name).with_(chunk_frames=2, window_frames=4)
+    got, ref = _causal_step(cfg, 41, [0, 1], 2)
+    assert_step_close(got, ref, cfg.dtype, label=f"{name} frame-causal step")
+
+
+def test_full_step_frame_causal_wrapped_ring():
+    """Three-frame chunk into a four-frame ring that already wrapped: the
+    window holds frames 3..6 in rotated slots; frame f sees 3..f."""
+    cfg = get_config("wan_small").with_(chunk_frames=3, window_frames=4)
+    got, ref = _causal_step(cfg, 42, [0, 1, 2, 3], 4)
+    assert_step_close(got, ref, cfg.dtype, label="wan_small frame-causal wrapped ring")
+
+
+def test_wan_full_size_frame_causal_sampled_rows():
+    """Wan2.1-1.3B shape, 3-frame chunk over a full 21-frame window, frame
+    causal: 64 sampled rows of the three chunk frames against the oracle."""
+    cfg = get_config("wan")
+    w, wd = device_weights(cfg, seed=0)
+    layer = LatentLayer(cfg, wd, batch=1, rope_n_t=64)
+    st = Stream(cfg, seed=0)
+    layer.write(to_torch(st.xs(0, 18)[None], cfg.dtype), 0, 18)
+    layer.write(to_torch(st.xs(18, 3)[None], cfg.dtype), 18, 3)
+    qn, qr = st.q(18)
+    out = layer.attend_frame_causal(to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype), 18, 3)
+    _sync()
+    got = to_numpy(out)[0]
+    T = cfg.tokens_per_frame
+    rng = np.random.default_rng(5)
+    edge = [0, T - 1, T, 2 * T - 1, 2 * T, cfg.n_q - 1]
+    rows = np.unique(np.concatenate([edge, rng.choice(cfg.n_q, 64 - len(edge), replace=False)]))
+    xs = {f: st.x(f) for f in range(21)}
+    for k in range(3):  # rows of chunk frame 18 + k see frames 0 .. 18 + k
+        sel = rows[(rows >= k * T) & (rows < (k + 1) * T)]
+        ref = oracle_step_rows(cfg, w, xs, list(range(19 + k)), qn, qr, 18, sel)
+        assert_step_close(got[sel], ref, cfg.dtype, label=f"wan full size frame-causal, frame {18 + k}")
+
+
 def test_rollout_ring_eviction_and_time_advance():
     """Successive 1-frame chunks over a 3-frame window: eviction starts at the
     4th chunk and t advances to 9; every step matches the oracle's ring."""
