@@ -285,6 +285,44 @@ def per_head_report(base, args):
         torch.cuda.empty_cache()
 
 
+def frame_causal_report(cfg, args):
+    """The attention side (mla_chunk_attend) with and without the frame-causal
+    mask inside the chunk, at the Wan shape. One JSON report line."""
+    import numpy as np
+    import torch
+
+    import latent_kv_attention_amd as mla
+
+    ctx = setup_step(cfg, 0)
+    ctx.write()
+    ws = torch.empty(mla.chunk_attend_workspace_bytes(ctx.shape, cfg.chunk_frames), dtype=torch.uint8, device="cuda")
+    outs = {k: torch.empty_like(ctx.out) for k in ("full", "causal")}
+    calls = {"full": mla.chunk_attend, "causal": mla.chunk_attend_frame_causal}
+    ts = {k: [] for k in calls}
+    for rnd in range(args.warmup + args.steps):
+        for k, fn in calls.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn(ctx.shape, ctx.qn, ctx.qr, ctx.chunk_first, cfg.chunk_frames, ctx.w["w_uk"], ctx.w["w_uv"], ctx.cache,
+               ctx.slot_frame, ctx.tables, 0, ctx.n_t, outs[k], ws)
+            b.record()
+            torch.cuda.synchronize()
+            if rnd >= args.warmup:
+                ts[k].append(a.elapsed_time(b))
+    T = cfg.tokens_per_frame
+    # keys each chunk frame may not see: the later chunk frames
+    masked_frac = sum(cfg.chunk_frames - 1 - k for k in range(cfg.chunk_frames)) / (cfg.chunk_frames * cfg.window_frames)
+    print(json.dumps({
+        "report": "frame-causal vs full attention inside the chunk, Wan2.1-1.3B-shaped chunk step (4680 queries x "
+                  "32760 keys), 1 MI355X",
+        "full_attend_ms": round(float(np.median(ts["full"])), 4),
+        "frame_causal_attend_ms": round(float(np.median(ts["causal"])), 4),
+        "masked_key_fraction": round(masked_frac, 4),
+        "rows_identical_in_last_frame": bool(torch.equal(outs["full"][(cfg.chunk_frames - 1) * T:],
+                                                         outs["causal"][(cfg.chunk_frames - 1) * T:])),
+        "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -297,6 +335,8 @@ def main():
                     help="rotating x buffers for the cold-cache cache-write measurement (0 = skip)")
     ap.add_argument("--per-head", action="store_true",
                     help="time the per-head form against the latent form at every width (report lines) and exit")
+    ap.add_argument("--frame-causal", action="store_true",
+                    help="time the attention side with and without the frame-causal mask (report line) and exit")
     ap.add_argument("--latent-sweep", action="store_true",
                     help="time the step at every latent width with kernels (one report line each) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -337,6 +377,9 @@ def main():
         return
     if args.per_head:
         per_head_report(cfg, args)
+        return
+    if args.frame_causal:
+        frame_causal_report(cfg, args)
         return
     ctx = setup_step(cfg, args.kv_splits)
     ms_step, per = time_steps(ctx, args.steps, args.warmup)

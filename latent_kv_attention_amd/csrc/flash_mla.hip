@@ -171,6 +171,7 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
   __shared__ int frame_of[kMaxSlots];  // frame held by the r-th valid slot (frame-causal variant)
   __shared__ int n_valid_sh;
   __shared__ int keytab[2][kBN];  // per key of a tile: byte offset of its cache row
+  __shared__ int keyfr[CAUSAL ? 2 : 1][CAUSAL ? kBN : 1];  // per key of a tile: its frame (frame-causal variant)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -311,7 +312,10 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
         const int ln = opaque(lane) + wave * 64;
         const int v = min(tile_of(pos) * kBN + ln, n_keys - 1);
         const int rank = div_floor(v, p.T, p.inv_T), tok = v - rank * p.T;
-        if (ln < kBN) tab[ln] = (slot_of[rank] * p.T + tok) * F::DK * (int)sizeof(T);
+        if (ln < kBN) {
+          tab[ln] = (slot_of[rank] * p.T + tok) * F::DK * (int)sizeof(T);
+          if constexpr (CAUSAL) keyfr[tab == keytab[0] ? 0 : 1][ln] = frame_of[rank];
+        }
       }
     };
 
@@ -373,7 +377,7 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     };
     // probabilities 2^s, packed into the B operand of the value product; with
     // RAGGED, keys at or past n_keys (kfirst = key index of the half) get 0
-    auto probs = [&](const sblk& s, v8 (&pb)[kNMB], int kfirst, auto ragged_c, bool masked) {
+    auto probs = [&](const sblk& s, v8 (&pb)[kNMB], int kfirst, auto ragged_c) {
       constexpr bool RAGGED = decltype(ragged_c)::value;
 #pragma unroll
       for (int mb = 0; mb < kNMB; ++mb) {
@@ -384,12 +388,6 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
           for (int i = 0; i < 4; ++i) {
             float e = fast_exp2(s[kb][mb][i]);
             if constexpr (RAGGED) e = kfirst + kb * 16 + lg * 4 + i < n_keys ? e : 0.f;
-            if constexpr (CAUSAL) {
-              if (masked) {
-                const int key = min(kfirst + kb * 16 + lg * 4 + i, n_keys - 1);
-                e = frame_of[div_floor(key, p.T, p.inv_T)] <= qfr[mb] ? e : 0.f;
-              }
-            }
             f8[kb * 4 + i] = e;
             l_run[mb] += e;
           }
@@ -414,7 +412,7 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     // frame-causal variant: frames of the tile's keys against the row
     // block's query frames (a tile spans at most kBN / T + 2 slot ranks)
     auto tile_class = [&](int kbase) -> int {
-      const int r0 = kbase / p.T, r1 = (min(kbase + kBN, n_keys) - 1) / p.T;
+      const int r0 = div_floor(kbase, p.T, p.inv_T), r1 = div_floor(min(kbase + kBN, n_keys) - 1, p.T, p.inv_T);
       int fmin = 0x7fffffff, fmax = -0x7fffffff;
       for (int r = r0; r <= r1; ++r) {
         const int f = frame_of[r];
@@ -439,17 +437,36 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
       }
       if (pos + 2 < n_visit) describe(pos + 2, keytab[CUR]);
       const int kbase = tile_of(pos) * kBN;
-      int cls = 0;  // 0: all keys visible to the block, 1: masked per key, 2: none visible
-      if constexpr (CAUSAL) cls = tile_class(kbase);
-      if (cls != 2) {
+      auto halves = [&](bool masked) {
 #pragma unroll 1
         for (int half = 0; half < NKC2; ++half) {
           sblk s;
           scores(cur, cur_r, half, s, negref);
+          if constexpr (CAUSAL) {
+            // scores of keys from frames after the row's frame drop out
+            if (masked) {
+              const int* kfr = keyfr[CAUSAL ? CUR : 0] + half * 32;
+#pragma unroll
+              for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int f = kfr[kb * 16 + lg * 4 + i];
+#pragma unroll
+                  for (int mb = 0; mb < kNMB; ++mb) s[kb][mb][i] = f <= qfr[mb] ? s[kb][mb][i] : -__builtin_inff();
+                }
+            }
+          }
           v8 pb[kNMB];
-          probs(s, pb, kbase + half * 32, ragged_c, cls == 1);
+          probs(s, pb, kbase + half * 32, ragged_c);
           values(cur, half, pb);
         }
+      };
+      if constexpr (CAUSAL) {
+        // 0: all keys visible to the block, 1: masked per key, 2: none visible
+        const int cls = tile_class(kbase);
+        if (cls != 2) halves(cls == 1);
+      } else {
+        halves(false);
       }
       __builtin_amdgcn_s_waitcnt(0);  // direct loads of the next tile have landed
       __syncthreads();
