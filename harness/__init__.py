@@ -11,6 +11,7 @@ from .gen import (  # noqa: F401
     to_bf16_bits,
     from_bf16_bits,
     layer_weights,
+    query_weights,
     frame_tokens,
     chunk_queries,
 )

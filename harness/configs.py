@@ -31,7 +31,13 @@ class MLAConfig:
     rope_base: float = 10000.0
     # frames held in the window when the chunk attends (chunk included)
     window_fill: int = 0
+    # query latent width; 0 selects 3 * d_c (the pages leave it open)
+    d_cq: int = 0
     note: str = field(default="", compare=False)
+
+    @property
+    def q_latent(self) -> int:
+        return self.d_cq or 3 * self.d_c
 
     @property
     def tokens_per_frame(self) -> int:

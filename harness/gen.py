@@ -17,6 +17,7 @@ import numpy as np
 from .configs import MLAConfig
 
 TAG_W_DKV, TAG_W_KR, TAG_W_UK, TAG_W_UV, TAG_X, TAG_QN, TAG_QR, TAG_POOL = range(1, 9)
+TAG_W_DQ, TAG_W_UQ, TAG_W_QR, TAG_W_O = range(9, 13)
 
 
 def _rng(seed: int, stream: int, layer: int, tag: int, index: int) -> np.random.Generator:
@@ -63,6 +64,21 @@ def layer_weights(cfg: MLAConfig, seed: int = 0, layer: int = 0) -> dict:
     w_uv = _rng(seed, 0, layer, TAG_W_UV, 0).standard_normal((nh, dh, dc)) / np.sqrt(dc)
     return {k: round_to(v, cfg.dtype) for k, v in
             dict(w_dkv=w_dkv, w_kr=w_kr, w_uk=w_uk, w_uv=w_uv).items()}
+
+
+def query_weights(cfg: MLAConfig, seed: int = 0, layer: int = 0) -> dict:
+    """Query-path and output weights of one layer, rounded to cfg.dtype.
+
+    w_dq [d_cq, hidden], w_uq [n_heads, d_head, d_cq], w_qr [n_heads, d_rope, d_cq],
+    w_o [hidden, n_heads * d_head]; d_cq = cfg.q_latent. Scaled by 1/sqrt(fan-in)
+    so that queries and outputs keep unit-order entries for unit-order tokens.
+    """
+    h, dq, dr, nh, dh = cfg.hidden, cfg.q_latent, cfg.d_rope, cfg.n_heads, cfg.d_head
+    w_dq = _rng(seed, 0, layer, TAG_W_DQ, 0).standard_normal((dq, h)) / np.sqrt(h)
+    w_uq = _rng(seed, 0, layer, TAG_W_UQ, 0).standard_normal((nh, dh, dq)) / np.sqrt(dq)
+    w_qr = _rng(seed, 0, layer, TAG_W_QR, 0).standard_normal((nh, dr, dq)) / np.sqrt(dq)
+    w_o = _rng(seed, 0, layer, TAG_W_O, 0).standard_normal((h, nh * dh)) / np.sqrt(nh * dh)
+    return {k: round_to(v, cfg.dtype) for k, v in dict(w_dq=w_dq, w_uq=w_uq, w_qr=w_qr, w_o=w_o).items()}
 
 
 POOL_FRAMES = 64

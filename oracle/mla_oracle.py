@@ -21,6 +21,13 @@ What is computed, per layer and per stream:
   s_ijh = scale (q_ih . k_jh + R(p_i) qR_ih . k^rope_j)   content + positional [Method]
   o_ih  = sum_j softmax_j(s_ijh) v_jh   over every valid key of the sliding
                                         window, the chunk's own frames included [Abstract]
+Query path and output (layer_step):
+  cQ_i  = W_dq x_i                      query latent of the token             [Method]
+  q_ih  = W_uq[h] cQ_i,  qR_ih = W_qr[h] cQ_i   per-head content query and
+                                        unrotated positional query            [Method]
+  u_i   = W_o [o_i1 ; ... ; o_iH]       output projection of the concatenated
+                                        heads (reading: standard multi-head
+                                        attention; the pages do not name it)
 
 Readings where the pages are silent (each one is listed with its reason in
 the design notes of the repository):
@@ -37,6 +44,11 @@ the design notes of the repository):
     visible. Off unless asked for.
   * The ring buffer keeps frame f in slot f mod W; a slot is valid iff its
     recorded frame index is >= 0.
+  * Query path: the pages derive the query latent from the token and the
+    per-head positional query from the query latent; the per-head content
+    query is read as coming from the same latent through its own per-head
+    up-projection. Its width d_cq is not given; no normalisation is applied
+    between the projections (none is named).
 
 Functions marked "absorbed" re-associate the same products (the GPU's form);
 they are used for stage-by-stage checks and as a self-check, never as the
@@ -51,6 +63,7 @@ __all__ = [
     "rotate_pairs", "rope3d", "frame_positions", "latents", "reconstruct", "attend",
     "RingCache", "chunk_step", "absorbed_query", "attend_latent", "up_project", "frame_causal_mask",
     "chunk_step_absorbed", "cache_scalars_per_token", "dense_scalars_per_token",
+    "query_project", "output_project", "layer_step",
 ]
 
 
@@ -274,6 +287,38 @@ def chunk_step(cfg_dims: dict, w: dict, ring: RingCache, x_chunk, frame_first: i
     q_rope = rope3d(q_r, tq, yq, xq, split, base)
     visible = frame_causal_mask(tq, t) if frame_causal else None
     return attend(q_nope, q_rope, k_nope, k_rope, v, scale, visible=visible)
+
+
+# ---------------------------------------------------------------- query path and output [Method]
+
+def query_project(x, w_dq, w_uq, w_qr):
+    """Query latent and per-head queries of tokens x [N, hidden]:
+    cQ = x W_dq^T [N, d_cq]; q_nope[i, h] = W_uq[h] cQ_i [N, H, d_h];
+    q_r[i, h] = W_qr[h] cQ_i [N, H, d_rope], unrotated (the rotation belongs to
+    the attention, where the query's position is known)."""
+    x = np.asarray(x, np.float64)
+    c_q = x @ np.asarray(w_dq, np.float64).T
+    q_nope = np.einsum("nc,hdc->nhd", c_q, np.asarray(w_uq, np.float64), optimize=True)
+    q_r = np.einsum("nc,hdc->nhd", c_q, np.asarray(w_qr, np.float64), optimize=True)
+    return c_q, q_nope, q_r
+
+
+def output_project(o, w_o) -> np.ndarray:
+    """u_i = W_o [o_i1 ; ... ; o_iH]: o [N, H, d_h], W_o [hidden, H*d_h] -> [N, hidden]."""
+    o = np.asarray(o, np.float64)
+    return o.reshape(o.shape[0], -1) @ np.asarray(w_o, np.float64).T
+
+
+def layer_step(cfg_dims: dict, w: dict, ring: RingCache, x_chunk, frame_first: int, scale: float | None = None,
+               frame_causal: bool = False):
+    """The whole attention layer for one chunk of one stream: the chunk's tokens
+    give the queries (query_project) and, through the cache write, keys of the
+    window; the heads' outputs are projected back to the token width.
+    w additionally holds w_dq, w_uq, w_qr, w_o. Returns (u [Nq, hidden],
+    out [Nq, H, d_h], q_nope, q_r)."""
+    _, q_nope, q_r = query_project(x_chunk, w["w_dq"], w["w_uq"], w["w_qr"])
+    out = chunk_step(cfg_dims, w, ring, x_chunk, frame_first, q_nope, q_r, scale=scale, frame_causal=frame_causal)
+    return output_project(out, w["w_o"]), out, q_nope, q_r
 
 
 # ---------------------------------------------------------------- absorbed form (stage checks)

@@ -430,6 +430,41 @@ def test_wan_full_size_frame_causal_sampled_rows():
         assert_step_close(got[sel], ref, cfg.dtype, label=f"wan full size frame-causal, frame {18 + k}")
 
 
+def test_denoising_rewrites_of_the_chunk():
+    """Chunk-wise generation re-writes the chunk's frames once per denoising
+    step: each step's latents replace the previous step's in the same slots,
+    the other window frames stay, and each step attends to the window as it
+    stands. After the last re-write the cache, the slot map and the attention
+    are bit-identical to a layer that wrote only the final latents."""
+    cfg = get_config("wan_small").with_(window_frames=4, chunk_frames=2)
+    w, wd = device_weights(cfg, seed=44)
+    st = Stream(cfg, seed=44)
+    first = 3  # frames 0..2 written before; the chunk 3, 4 wraps into slots 3, 0
+    layer = LatentLayer(cfg, wd, batch=1, rope_n_t=16)
+    layer.write(to_torch(st.xs(0, first)[None], cfg.dtype), 0, first)
+    qn, qr = st.q(first)
+    qn_t, qr_t = to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype)
+    steps = [Stream(cfg, seed=440 + k) for k in range(3)] + [st]  # noisy steps, then the final latents
+    for k, src in enumerate(steps):
+        layer.write(to_torch(src.xs(first, 2)[None], cfg.dtype), first, 2)
+        out = layer.attend(qn_t, qr_t, first, 2)
+        _sync()
+        xs = {1: st.x(1), 2: st.x(2), 3: src.x(3), 4: src.x(4)}
+        ref = oracle_step_rows(cfg, w, xs, [1, 2, 3, 4], qn, qr, first)
+        assert_step_close(to_numpy(out)[0], ref, cfg.dtype, label=f"denoising step {k}")
+    assert to_numpy(layer.slot_frame)[0].tolist() == [4, 1, 2, 3]
+
+    once = LatentLayer(cfg, wd, batch=1, rope_n_t=16)
+    once.write(to_torch(st.xs(0, first)[None], cfg.dtype), 0, first)
+    once.write(to_torch(st.xs(first, 2)[None], cfg.dtype), first, 2)
+    out_once = once.attend(qn_t, qr_t, first, 2)
+    _sync()
+    assert torch.equal(layer.cache.view(torch.int16) if cfg.dtype == "bf16" else layer.cache,
+                       once.cache.view(torch.int16) if cfg.dtype == "bf16" else once.cache)
+    assert torch.equal(layer.slot_frame, once.slot_frame)
+    assert torch.equal(out.view(torch.int16), out_once.view(torch.int16))
+
+
 def test_rollout_ring_eviction_and_time_advance():
     """Successive 1-frame chunks over a 3-frame window: eviction starts at the
     4th chunk and t advances to 9; every step matches the oracle's ring."""

@@ -67,6 +67,33 @@ def _attend_softmax_over_heads(qn, qr, kn, kr, v, scale, block=64, visible=None)
     return np.einsum("qhk,khd->qhd", p, v)
 
 
+_orig_query_project = O.query_project
+
+
+def _query_heads_transposed(x, w_dq, w_uq, w_qr):
+    # per-head weights read as [d_h, H, d_cq]: heads and components interleaved
+    nh, dh, dq = np.shape(w_uq)
+    w_t = np.asarray(w_uq).reshape(dh, nh, dq).transpose(1, 0, 2)
+    return _orig_query_project(x, w_dq, w_t, w_qr)
+
+
+def _query_rope_from_token(x, w_dq, w_uq, w_qr):
+    # positional query taken from the content query's first components
+    c_q, qn, qr = _orig_query_project(x, w_dq, w_uq, w_qr)
+    return c_q, qn, qn[..., :qr.shape[-1]].copy()
+
+
+def _output_heads_interleaved(o, w_o):
+    o = np.asarray(o, np.float64)
+    return o.transpose(0, 2, 1).reshape(o.shape[0], -1) @ np.asarray(w_o, np.float64).T
+
+
+def _output_transposed(o, w_o):
+    o = np.asarray(o, np.float64)
+    w = np.asarray(w_o, np.float64)
+    return o.reshape(o.shape[0], -1) @ w.reshape(w.shape[1], w.shape[0])
+
+
 MUTATIONS = {
     "rotation_sign": ("rotate_pairs", _rot_sign_flip),
     "half_split_pairs": ("rotate_pairs", _rot_half_split),
@@ -78,6 +105,10 @@ MUTATIONS = {
     "softmax_axis": ("attend", _attend_softmax_over_heads),
     "causal_mask_ignored": ("attend", _attend_mask_ignored),
     "causal_mask_strict": ("frame_causal_mask", _causal_strict),
+    "query_heads_transposed": ("query_project", _query_heads_transposed),
+    "query_rope_from_content": ("query_project", _query_rope_from_token),
+    "output_heads_interleaved": ("output_project", _output_heads_interleaved),
+    "output_weight_transposed": ("output_project", _output_transposed),
 }
 
 
@@ -87,7 +118,8 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
     monkeypatch.setattr(O, attr, fn)
     caught = 0
     for check in (P.test_oracle_matches_brute_force_tiny, P.test_rope3d_blocks_equal_textbook_1d,
-                  P.test_oracle_matches_brute_force_partial_window, P.test_frame_causal_matches_brute_force):
+                  P.test_oracle_matches_brute_force_partial_window, P.test_frame_causal_matches_brute_force,
+                  lambda: P.test_layer_step_matches_brute_force(False)):
         try:
             check()
         except AssertionError:
@@ -102,3 +134,4 @@ def test_unmutated_oracle_passes_same_checks():
     P.test_rope3d_blocks_equal_textbook_1d()
     P.test_oracle_matches_brute_force_partial_window()
     P.test_frame_causal_matches_brute_force()
+    P.test_layer_step_matches_brute_force(False)

@@ -13,7 +13,7 @@ import os
 import numpy as np
 import pytest
 
-from harness import chunk_queries, frame_tokens, get_config, layer_weights
+from harness import chunk_queries, frame_tokens, get_config, layer_weights, query_weights
 from oracle import mla_oracle as O
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "paper_counts.json")
@@ -153,6 +153,20 @@ def test_ring_eviction_closed_form():
     assert ring.c[1, 0, 0] == 9 and ring.kr[2, 1, 1] == -6
     with pytest.raises(ValueError):
         ring.write(0, np.zeros((10, 3)), np.zeros((10, 2)))
+
+
+def test_ring_rewrite_of_a_chunk_replaces_only_its_slots():
+    # denoising re-writes the chunk's frames: values written with their own
+    # frame index make the state after any run of re-writes readable by hand
+    ring = O.RingCache(4, 2, 3, 2)
+    for f in range(3):
+        ring.write(f, np.full((2, 3), f, float), np.full((2, 2), -f, float))
+    for step in range(3):  # chunk = frames 3, 4 (slots 3, 0), re-written per step
+        c = np.repeat(np.array([[100.0 * step + 3], [100.0 * step + 4]]), 2, axis=0) * np.ones((4, 3))
+        ring.write(3, c, -c[:, :2])
+        assert ring.slot_frame.tolist() == [4, 1, 2, 3]
+        assert ring.c[0, 0, 0] == 100 * step + 4 and ring.c[3, 1, 2] == 100 * step + 3
+        assert ring.c[1, 0, 0] == 1 and ring.c[2, 1, 1] == 2 and ring.kr[2, 0, 0] == -2
 
 
 def test_ring_slot_layout_does_not_change_output():
@@ -395,6 +409,84 @@ def test_oracle_stage_functions_match_brute_force_pieces():
     xs = [frame_tokens(cfg, f) for f in range(3)]
     bf = _brute_force_step(cfg, w, xs, [0, 1, 2], None, qn, qr, cf)
     np.testing.assert_allclose(O.up_project(lat, w["w_uv"]), bf, atol=1e-12)
+
+
+# ------------------------------------------------------------------ query path and output projection
+
+def _brute_force_layer(cfg, w, wq, xs_window, frames_window, x_chunk, q_frame_first, frame_causal=False):
+    """The whole layer by loops: query latent, per-head queries, the brute-force
+    attention above, then the output projection summed head by head."""
+    nh, dh, dr, dq = cfg.n_heads, cfg.d_head, cfg.d_rope, cfg.q_latent
+    n = x_chunk.shape[0]
+    qn = np.zeros((n, nh, dh))
+    qr = np.zeros((n, nh, dr))
+    for i in range(n):
+        cq = [sum(wq["w_dq"][a][b] * x_chunk[i][b] for b in range(cfg.hidden)) for a in range(dq)]
+        for h in range(nh):
+            for d in range(dh):
+                qn[i, h, d] = sum(wq["w_uq"][h][d][a] * cq[a] for a in range(dq))
+            for d in range(dr):
+                qr[i, h, d] = sum(wq["w_qr"][h][d][a] * cq[a] for a in range(dq))
+    o = _brute_force_step(cfg, w, xs_window, frames_window, None, qn, qr, q_frame_first, frame_causal)
+    u = np.zeros((n, cfg.hidden))
+    for i in range(n):
+        for j in range(cfg.hidden):
+            u[i, j] = sum(wq["w_o"][j][h * dh + d] * o[i, h, d] for h in range(nh) for d in range(dh))
+    return u
+
+
+@pytest.mark.parametrize("frame_causal", [False, True])
+def test_layer_step_matches_brute_force(frame_causal):
+    cfg = get_config("tiny").with_(chunk_frames=2, d_cq=24)
+    w, wq = layer_weights(cfg, seed=21), query_weights(cfg, seed=21)
+    ring = O.RingCache(cfg.window_frames, cfg.tokens_per_frame, cfg.d_c, cfg.d_rope)
+    c, kr = O.latents(frame_tokens(cfg, 0, seed=21), w["w_dkv"], w["w_kr"])
+    ring.write(0, c, kr)
+    xc = np.concatenate([frame_tokens(cfg, f, seed=21) for f in (1, 2)])
+    u, out, qn, qr = O.layer_step(_dims(cfg), {**w, **wq}, ring, xc, 1, frame_causal=frame_causal)
+    assert u.shape == (2 * cfg.tokens_per_frame, cfg.hidden)
+    xs = [frame_tokens(cfg, f, seed=21) for f in range(3)]
+    bf = _brute_force_layer(cfg, w, wq, xs, [0, 1, 2], xc, 1, frame_causal)
+    np.testing.assert_allclose(u, bf, rtol=0, atol=1e-12)
+
+
+def test_layer_with_full_rank_query_latent_equals_dense_mha_layer():
+    """With the identity as query down-projection (d_cq = hidden) and full-rank
+    key/value latents, the layer is a dense multi-head attention layer with a
+    decoupled rotary key: q_h = W_Q[h] x, qR_h = W_QR[h] x, u = sum_h W_O[h] o_h."""
+    cfg = get_config("tiny").with_(hidden=12)
+    n_h, d_h, dr = cfg.n_heads, cfg.d_head, cfg.d_rope
+    d_c = 2 * n_h * d_h
+    cfg = cfg.with_(d_c=d_c, d_cq=cfg.hidden)
+    rng = np.random.default_rng(8)
+    WK, WV, WQ = (rng.standard_normal((n_h * d_h, cfg.hidden)) / np.sqrt(cfg.hidden) for _ in range(3))
+    WQR = rng.standard_normal((n_h * dr, cfg.hidden)) / np.sqrt(cfg.hidden)
+    WO = rng.standard_normal((cfg.hidden, n_h * d_h)) / np.sqrt(n_h * d_h)
+    w_kr = rng.standard_normal((dr, cfg.hidden)) / np.sqrt(cfg.hidden)
+    w_uk = np.zeros((n_h, d_h, d_c))
+    w_uv = np.zeros((n_h, d_h, d_c))
+    for h in range(n_h):
+        for d in range(d_h):
+            w_uk[h, d, h * d_h + d] = 1.0
+            w_uv[h, d, n_h * d_h + h * d_h + d] = 1.0
+    w = dict(w_dkv=np.concatenate([WK, WV]), w_kr=w_kr, w_uk=w_uk, w_uv=w_uv, w_dq=np.eye(cfg.hidden),
+             w_uq=WQ.reshape(n_h, d_h, cfg.hidden), w_qr=WQR.reshape(n_h, dr, cfg.hidden), w_o=WO)
+    ring = O.RingCache(cfg.window_frames, cfg.tokens_per_frame, d_c, dr)
+    xs = [rng.standard_normal((cfg.tokens_per_frame, cfg.hidden)) for _ in range(3)]
+    for f in range(2):
+        c, kr = O.latents(xs[f], w["w_dkv"], w["w_kr"])
+        ring.write(f, c, kr)
+    u, _, _, _ = O.layer_step(_dims(cfg), w, ring, xs[2], 2)
+    xk = np.concatenate(xs)
+    t, y, x = O.frame_positions([0, 1, 2], cfg.grid_y, cfg.grid_x)
+    kr_rot = O.rope3d(xk @ w_kr.T, t, y, x, cfg.rope_split, cfg.rope_base)
+    tq, yq, xq = O.frame_positions([2], cfg.grid_y, cfg.grid_x)
+    qn = np.stack([xs[2] @ WQ[h * d_h:(h + 1) * d_h].T for h in range(n_h)], axis=1)
+    qr = np.stack([xs[2] @ WQR[h * dr:(h + 1) * dr].T for h in range(n_h)], axis=1)
+    qr_rot = O.rope3d(qr, tq, yq, xq, cfg.rope_split, cfg.rope_base)
+    o = _naive_mha(xk, qn, qr_rot, kr_rot, WK, WV, n_h, d_h, O.default_scale(d_h, dr))
+    ref = sum(o[:, h] @ WO[:, h * d_h:(h + 1) * d_h].T for h in range(n_h))
+    np.testing.assert_allclose(u, ref, atol=1e-12)
 
 
 # ------------------------------------------------------------------ input generator sanity
