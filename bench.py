@@ -323,6 +323,66 @@ def frame_causal_report(cfg, args):
         "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic"}), flush=True)
 
 
+def projections_report(cfg, args):
+    """The query path (mla_query_project: query latent, per-head content and
+    positional queries) and the output projection (mla_output_project) at the
+    Wan shape, and the whole layer built from them (query path, cache write,
+    mla_chunk_attend, output projection). One JSON report line."""
+    import numpy as np
+    import torch
+
+    import latent_kv_attention_amd as mla
+    from harness import frame_tokens, layer_weights, query_weights
+    from harness.torch_io import to_torch
+    from latent_kv_attention_amd.layer import LatentLayer
+
+    dev = "cuda"
+    print(f"[bench] projections: generating inputs (d_cq {cfg.q_latent})", file=sys.stderr, flush=True)
+    w = {k: to_torch(v, cfg.dtype, dev) for k, v in {**layer_weights(cfg, 0), **query_weights(cfg, 0)}.items()}
+    layer = LatentLayer(cfg, w, batch=1, rope_n_t=64)
+    chunk_first = cfg.window_frames - cfg.chunk_frames
+    x_pre = to_torch(np.concatenate([frame_tokens(cfg, f) for f in range(chunk_first)])[None], cfg.dtype, dev)
+    layer.write(x_pre, 0, chunk_first)
+    del x_pre
+    x = to_torch(np.concatenate([frame_tokens(cfg, chunk_first + i) for i in range(cfg.chunk_frames)])[None],
+                 cfg.dtype, dev)
+    o = torch.randn(1, cfg.n_q, cfg.n_heads, cfg.d_head, device=dev).to(torch.bfloat16)
+    u = torch.empty(1, cfg.n_q, cfg.hidden, dtype=torch.bfloat16, device=dev)
+    calls = {
+        "query_project": lambda: layer.project_queries(x, cfg.chunk_frames),
+        "output_project": lambda: layer.project_output(o, cfg.chunk_frames, out=u),
+        "layer_step": lambda: layer.step(x, chunk_first, cfg.chunk_frames),
+    }
+    ts = {k: [] for k in calls}
+    for rnd in range(args.warmup + args.steps):
+        for k, fn in calls.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            if rnd >= args.warmup:
+                ts[k].append(a.elapsed_time(b))
+    ms = {k: float(np.median(v)) for k, v in ts.items()}
+    M, H = cfg.n_q, cfg.n_heads
+    q_fl = 2.0 * M * (cfg.hidden * cfg.q_latent + cfg.q_latent * H * (cfg.d_head + cfg.d_rope))
+    o_fl = 2.0 * M * H * cfg.d_head * cfg.hidden
+    tf = lambda fl, t: fl / (t * 1e-3) / 1e12
+    print(json.dumps({
+        "report": "query path and output projection around the chunk step, Wan2.1-1.3B shape (4680 chunk tokens, "
+                  "hidden 1536, d_cq %d), 1 MI355X" % cfg.q_latent,
+        "query_project_ms": round(ms["query_project"], 4), "query_project_flops": q_fl,
+        "query_project_TFLOPs": round(tf(q_fl, ms["query_project"]), 1),
+        "output_project_ms": round(ms["output_project"], 4), "output_project_flops": o_fl,
+        "output_project_TFLOPs": round(tf(o_fl, ms["output_project"]), 1),
+        "projections_frac_of_bf16_peak": round(tf(q_fl + o_fl, ms["query_project"] + ms["output_project"])
+                                               / PEAK_BF16_TFLOPS, 4),
+        "layer_step_ms": round(ms["layer_step"], 4),
+        "projections_share_of_layer": round((ms["query_project"] + ms["output_project"]) / ms["layer_step"], 4),
+        "finite": bool(torch.isfinite(u.float()).all()),
+        "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,6 +397,8 @@ def main():
                     help="time the per-head form against the latent form at every width (report lines) and exit")
     ap.add_argument("--frame-causal", action="store_true",
                     help="time the attention side with and without the frame-causal mask (report line) and exit")
+    ap.add_argument("--projections", action="store_true",
+                    help="time the query path, the output projection and the whole layer (report line) and exit")
     ap.add_argument("--latent-sweep", action="store_true",
                     help="time the step at every latent width with kernels (one report line each) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -380,6 +442,9 @@ def main():
         return
     if args.frame_causal:
         frame_causal_report(cfg, args)
+        return
+    if args.projections:
+        projections_report(cfg, args)
         return
     ctx = setup_step(cfg, args.kv_splits)
     ms_step, per = time_steps(ctx, args.steps, args.warmup)

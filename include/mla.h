@@ -250,6 +250,42 @@ mla_status mla_chunk_attend_heads(const mla_shape* shape, const void* q_nope, co
                                   int32_t rope_t_first, int32_t rope_n_t, void* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- query path
+ * Queries of the chunk's tokens (hyper.ai summary, Method: a query latent is
+ * derived from each token, and the per-head positional query is computed
+ * from that latent and rotated at attention time; the per-head content query
+ * is read as the query latent's own per-head up-projection):
+ *   c_q[r]        = W_dq x[r]                 (rounded to dtype)
+ *   q_nope[r][h]  = W_uq[h] c_q[r]
+ *   q_r[r][h]     = W_qr[h] c_q[r]            (unrotated; mla_absorb_q and the
+ *                                               chunk_attend calls rotate it)
+ *   d_cq          query latent width: a multiple of 8, at most 65536 (the
+ *                 pages leave it open)
+ *   x      (device) [B][n_frames * T][hidden]  the chunk's tokens (the same
+ *                   rows mla_cache_write takes)
+ *   w_dq   (device) [d_cq][hidden]
+ *   w_uq   (device) [H][d_head][d_cq]
+ *   w_qr   (device) [H][d_rope][d_cq]
+ *   c_q    (device) [B][n_frames * T][d_cq]      output (the query latent)
+ *   q_nope (device) [B][n_frames * T][H][d_head] output
+ *   q_r    (device) [B][n_frames * T][H][d_rope] output
+ * Three matrix products on `stream`; fp32 accumulation. d_rope must be a
+ * multiple of 8. n_frames < 1 returns MLA_ERR_RANGE. */
+mla_status mla_query_project(const mla_shape* shape, int32_t d_cq, const void* x, int32_t n_frames,
+                             const void* w_dq, const void* w_uq, const void* w_qr, void* c_q, void* q_nope,
+                             void* q_r, void* stream);
+
+/* ---------------------------------------------------------------- output projection
+ * u[r] = W_o [o[r][0]; ...; o[r][H-1]]: the concatenated heads projected back
+ * to the token width (the output projection of multi-head attention; the
+ * pages do not describe it).
+ *   o   (device) [B][n_frames * T][H][d_head]  (out of the chunk_attend calls)
+ *   w_o (device) [hidden][H * d_head]
+ *   u   (device) [B][n_frames * T][hidden]      output
+ * One matrix product on `stream`; fp32 accumulation. */
+mla_status mla_output_project(const mla_shape* shape, const void* o, int32_t n_frames, const void* w_o, void* u,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -2,12 +2,12 @@
 
 The compute lives in libmla355.so (HIP kernels for gfx950 behind the C ABI in
 include/mla.h); this package only binds it. See `_lib` for the calls and
-`step` for a device-resident layer state that strings them together.
+`layer` for a device-resident layer state that strings them together.
 """
 from ._lib import (  # noqa: F401
     MLA_BF16, MLA_F32, MlaError, MlaShape, EXPORTS, LIB_PATH,
     abi_version, shape_check, qabs_dim, make_shape, lib,
     rope3d_table_floats, rope3d_tables, cache_write, absorb_q, flash_workspace_bytes, flash_attend,
     up_v, chunk_attend_workspace_bytes, chunk_attend, chunk_attend_heads_workspace_bytes, chunk_attend_heads,
-    chunk_attend_frame_causal,
+    chunk_attend_frame_causal, query_project, output_project,
 )

@@ -27,6 +27,7 @@ EXPORTS = [
     "mla_flash_workspace_bytes", "mla_flash_attend", "mla_up_v",
     "mla_chunk_attend_workspace_bytes", "mla_chunk_attend",
     "mla_chunk_attend_heads_workspace_bytes", "mla_chunk_attend_heads", "mla_chunk_attend_frame_causal",
+    "mla_query_project", "mla_output_project",
 ]
 
 
@@ -67,6 +68,8 @@ _SIGS = {
     "mla_chunk_attend_heads_workspace_bytes": (_SZ, [_SP, _I]),
     "mla_chunk_attend_frame_causal": (_I, [_SP, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
     "mla_chunk_attend_heads": (_I, [_SP, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
+    "mla_query_project": (_I, [_SP, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P]),
+    "mla_output_project": (_I, [_SP, _P, _I, _P, _P, _P]),
 }
 
 
@@ -200,3 +203,15 @@ def chunk_attend_frame_causal(shape: MlaShape, q_nope, q_r, q_frame_first: int, 
                                                q_n_frames, _ptr(w_uk), _ptr(w_uv), _ptr(cache), _ptr(slot_frame),
                                                _ptr(tables), rope_t_first, rope_n_t, _ptr(out), _ptr(workspace),
                                                nbytes, _stream(stream)))
+
+
+def query_project(shape: MlaShape, d_cq: int, x, n_frames: int, w_dq, w_uq, w_qr, c_q, q_nope, q_r,
+                  stream=None) -> None:
+    _check("mla_query_project",
+           lib().mla_query_project(ctypes.byref(shape), d_cq, _ptr(x), n_frames, _ptr(w_dq), _ptr(w_uq), _ptr(w_qr),
+                                   _ptr(c_q), _ptr(q_nope), _ptr(q_r), _stream(stream)))
+
+
+def output_project(shape: MlaShape, o, n_frames: int, w_o, u, stream=None) -> None:
+    _check("mla_output_project",
+           lib().mla_output_project(ctypes.byref(shape), _ptr(o), n_frames, _ptr(w_o), _ptr(u), _stream(stream)))

@@ -20,7 +20,7 @@ LIB_NAME = "libmla355.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["mla_abi.hip", "rope_tables.hip", "cache_write.hip", "absorb_q.hip", "flash_mla.hip", "up_v.hip",
-           "heads_mha.hip"]
+           "heads_mha.hip", "proj_gemm.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU instructions.
 HIPCC_FLAGS = [

@@ -556,3 +556,64 @@ MLA_API mla_status mla_chunk_attend_heads(const mla_shape* shape, const void* q_
   return from_hip(mla::launch_heads(shape->d_c, shape->d_rope, shape->d_head, p, f.split, s));
 }
 
+
+namespace {
+
+constexpr int kMaxQueryLatent = 1 << 16;
+
+mla_status gemm(const mla_shape* s, const void* a, const void* b, void* c, int64_t M, int N, int K,
+                hipStream_t st) {
+  mla::GemmParams p{};
+  p.a = a;
+  p.b = b;
+  p.c = c;
+  p.M = (int)M;
+  p.N = N;
+  p.K = K;
+  p.lda = K;
+  p.ldb = K;
+  p.ldc = N;
+  return from_hip(mla::launch_gemm_nt(s->dtype, p, mla::gemm_tile_rows(p.M, N, device_cus()), st));
+}
+
+mla_status check_projection_rows(const mla_shape* s, int n_frames, int64_t* rows) {
+  if (n_frames < 1) return MLA_ERR_RANGE;
+  *rows = (int64_t)s->batch * n_frames * tokens_per_frame(s);
+  if (*rows > INT32_MAX / 2) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
+}  // namespace
+
+MLA_API mla_status mla_query_project(const mla_shape* shape, int32_t d_cq, const void* x, int32_t n_frames,
+                                     const void* w_dq, const void* w_uq, const void* w_qr, void* c_q, void* q_nope,
+                                     void* q_r, void* stream) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!x || !w_dq || !w_uq || !w_qr || !c_q || !q_nope || !q_r) return MLA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_dq) || !aligned16(w_uq) || !aligned16(w_qr) || !aligned16(c_q) ||
+      !aligned16(q_nope) || !aligned16(q_r))
+    return MLA_ERR_ALIGN;
+  if (d_cq < 8 || d_cq % 8 != 0 || d_cq > kMaxQueryLatent) return MLA_ERR_SHAPE;
+  if ((int64_t)shape->n_heads * shape->d_head > kMaxQueryLatent ||
+      (int64_t)shape->n_heads * shape->d_rope > kMaxQueryLatent || shape->d_rope % 8 != 0)
+    return MLA_ERR_SHAPE;
+  int64_t rows = 0;
+  if ((st = check_projection_rows(shape, n_frames, &rows)) != MLA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = gemm(shape, x, w_dq, c_q, rows, d_cq, shape->hidden, s)) != MLA_OK) return st;
+  if ((st = gemm(shape, c_q, w_uq, q_nope, rows, shape->n_heads * shape->d_head, d_cq, s)) != MLA_OK) return st;
+  return gemm(shape, c_q, w_qr, q_r, rows, shape->n_heads * shape->d_rope, d_cq, s);
+}
+
+MLA_API mla_status mla_output_project(const mla_shape* shape, const void* o, int32_t n_frames, const void* w_o,
+                                      void* u, void* stream) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!o || !w_o || !u) return MLA_ERR_NULL;
+  if (!aligned16(o) || !aligned16(w_o) || !aligned16(u)) return MLA_ERR_ALIGN;
+  if ((int64_t)shape->n_heads * shape->d_head > kMaxQueryLatent) return MLA_ERR_SHAPE;
+  int64_t rows = 0;
+  if ((st = check_projection_rows(shape, n_frames, &rows)) != MLA_OK) return st;
+  return gemm(shape, o, w_o, u, rows, shape->hidden, shape->n_heads * shape->d_head, (hipStream_t)stream);
+}

@@ -116,6 +116,17 @@ struct HeadsParams {
   float qscale;            // softmax scale * log2(e)
 };
 
+// C[M][N] = A[M][K] B[N][K]^T (rows of B are output features), fp32
+// accumulation, C in the operands' type. K, N, lda, ldb, ldc multiples of 8;
+// pointers 16-byte aligned.
+struct GemmParams {
+  const void* a;
+  const void* b;
+  void* c;
+  int M, N, K, lda, ldb, ldc;
+  int tiles_n, n_logical, per_xcd;  // filled by the launcher
+};
+
 hipError_t launch_rope_tables(const RopeTableParams& p, hipStream_t s);
 hipError_t launch_cache_write(int dtype, int d_c, int d_rope, const CacheWriteParams& p, hipStream_t s);
 hipError_t launch_absorb_q(int dtype, int d_c, int d_rope, const AbsorbParams& p, hipStream_t s);
@@ -129,5 +140,9 @@ hipError_t launch_rope_window(int dtype, int d_c, int d_rope, const FlashParams&
 bool heads_supported(int dtype, int d_c, int d_rope, int d_head);
 int heads_tile_keys(int d_head, int d_rope);  // keys per tile of the per-head attention kernel
 hipError_t launch_heads(int d_c, int d_rope, int d_head, const HeadsParams& p, bool split, hipStream_t s);
+// rows per work-group tile of the projection GEMM (128 or 64) for a problem
+// of M x N outputs on n_cu compute units
+int gemm_tile_rows(int M, int N, int n_cu);
+hipError_t launch_gemm_nt(int dtype, const GemmParams& p, int tile_rows, hipStream_t s);
 
 }  // namespace mla

@@ -1,0 +1,133 @@
+// Dense projections on either side of the chunk attention (hyper.ai summary
+// of VideoMLA, Method section): the query latent cQ = W_dq x of each chunk
+// token, the per-head content and positional queries W_uq[h] cQ and
+// W_qr[h] cQ, and the output projection W_o [o_1; ...; o_H] of the
+// concatenated heads (the standard multi-head attention output; the pages do
+// not spell it out).
+//
+// All of them are one GEMM shape: C[M][N] = A[M][K] B[N][K]^T, with the
+// weight B stored as [out features][in features], so both operands are
+// contiguous along the contraction and each lane's 8-element matrix-core
+// operand is one 16-byte row piece, read from LDS without a transpose.
+//
+// Work-group tile BM x 128 outputs (BM = 128 or 64), 64-wide K steps: the
+// next step's operands are loaded into registers while the matrix cores
+// work on the current one from LDS. Rows of the staged tiles are padded by
+// 16 bytes, so the 16 rows of one operand read fall on distinct banks. The
+// output tile leaves through LDS in 16-byte row pieces. Tiles are numbered
+// row-major and dealt to the 8 XCDs in contiguous ranges, so tiles that
+// share A rows share an L2.
+#include "mla_common.hpp"
+#include "mla_internal.hpp"
+
+namespace mla {
+
+namespace {
+constexpr int kGemmBN = 128;
+constexpr int kGemmBK = 64;
+constexpr int kGemmXcds = 8;
+}  // namespace
+
+template <typename T, int BM>
+__global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
+  typedef typename V8<T>::type v8;
+  constexpr int BN = kGemmBN, BK = kGemmBK;
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int LDK = BK + PAD;                 // staged row stride (elements)
+  constexpr int LDC = BN + PAD;                 // output staging row stride
+  constexpr int CHUNKS = BK / 8;                // 8-element pieces per staged row
+  constexpr int NLD = (BM + BN) * CHUNKS / 256; // pieces per thread per K step
+  constexpr int WM = BM / 2, WN = BN / 2;       // wave tile (2 x 2 waves)
+  constexpr int NMB = WM / 16, NNB = WN / 16;
+  static_assert((BM + BN) * CHUNKS % 256 == 0, "whole pieces per thread");
+  static_assert(BM * LDC <= (BM + BN) * LDK, "output tile fits in the staging buffer");
+  __shared__ __attribute__((aligned(16))) T lds[(BM + BN) * LDK];
+
+  const int logical = (blockIdx.x % kGemmXcds) * p.per_xcd + blockIdx.x / kGemmXcds;
+  if (logical >= p.n_logical) return;
+  const int row0 = (logical / p.tiles_n) * BM;
+  const int col0 = (logical % p.tiles_n) * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // staged row r < BM is A row row0 + r, else B row col0 + r - BM; rows past
+  // the end repeat the last row (their products are never stored)
+  const T* src[NLD];
+  int dst[NLD], kof[NLD];
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const int e = tid + 256 * j;
+    const int r = e / CHUNKS, c = e % CHUNKS;
+    src[j] = r < BM ? (const T*)p.a + (size_t)min(row0 + r, p.M - 1) * p.lda + c * 8
+                    : (const T*)p.b + (size_t)min(col0 + r - BM, p.N - 1) * p.ldb + c * 8;
+    dst[j] = r * LDK + c * 8;
+    kof[j] = c * 8;
+  }
+  v8 stage[NLD];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) stage[j] = k0 + kof[j] < p.K ? load8<T>(src[j] + k0) : zero8<T>();
+  };
+
+  f32x4 acc[NMB][NNB] = {};
+  fetch(0);
+  for (int k0 = 0; k0 < p.K; k0 += BK) {
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) store8<T>(lds + dst[j], stage[j]);
+    __syncthreads();
+    if (k0 + BK < p.K) fetch(k0 + BK);
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      v8 af[NMB], bf[NNB];
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) af[mb] = lds_load8<T>(lds + (wm * WM + mb * 16 + li) * LDK + kk * 32 + lg * 8);
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb)
+        bf[nb] = lds_load8<T>(lds + (BM + wn * WN + nb * 16 + li) * LDK + kk * 32 + lg * 8);
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NNB; ++nb) acc[mb][nb] = mma16(af[mb], bf[nb], acc[mb][nb]);
+    }
+  }
+
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        lds[(wm * WM + mb * 16 + lg * 4 + i) * LDC + wn * WN + nb * 16 + li] = to_t<T>(acc[mb][nb][i]);
+  __syncthreads();
+  for (int e = tid; e < BM * (BN / 8); e += 256) {
+    const int r = e / (BN / 8), c8 = (e % (BN / 8)) * 8;
+    if (row0 + r < p.M && col0 + c8 < p.N)
+      store8<T>((T*)p.c + (size_t)(row0 + r) * p.ldc + col0 + c8, lds_load8<T>(lds + r * LDC + c8));
+  }
+}
+
+int gemm_tile_rows(int M, int N, int n_cu) {
+  const long long big = (long long)((M + 127) / 128) * ((N + kGemmBN - 1) / kGemmBN);
+  return big >= n_cu ? 128 : 64;
+}
+
+template <typename T, int BM>
+static hipError_t launch_gemm_t(GemmParams p, hipStream_t s) {
+  p.tiles_n = (p.N + kGemmBN - 1) / kGemmBN;
+  p.n_logical = ((p.M + BM - 1) / BM) * p.tiles_n;
+  p.per_xcd = (p.n_logical + kGemmXcds - 1) / kGemmXcds;
+  hipLaunchKernelGGL((gemm_nt_kernel<T, BM>), dim3(p.per_xcd * kGemmXcds), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nt(int dtype, const GemmParams& p, int tile_rows, hipStream_t s) {
+  if (p.M <= 0 || p.N <= 0) return hipSuccess;
+  if (tile_rows == 128) return dtype == 0 ? launch_gemm_t<bf16, 128>(p, s) : launch_gemm_t<float, 128>(p, s);
+  if (tile_rows == 64) return dtype == 0 ? launch_gemm_t<bf16, 64>(p, s) : launch_gemm_t<float, 64>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mla

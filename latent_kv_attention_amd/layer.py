@@ -38,6 +38,7 @@ class LatentLayer:
         self.workspace = torch.empty(_lib.chunk_attend_workspace_bytes(self.shape, nf), dtype=torch.uint8,
                                      device=device)
         self.heads_workspace = None  # allocated on the first per-head call
+        self.q_buffers = None        # query latent and queries, allocated on the first projection
 
     def write(self, x, frame_first: int, n_frames: int, stream=None) -> None:
         """Cache write of frames frame_first .. +n_frames (x [B][n_frames*T][hidden])."""
@@ -86,3 +87,45 @@ class LatentLayer:
                                 self.cache, self.slot_frame, self.tables, self.rope_t_first, self.rope_n_t, out,
                                 self.heads_workspace, stream)
         return out
+
+    def project_queries(self, x, n_frames: int, stream=None):
+        """Query latent and per-head queries of the chunk's tokens x
+        [B][n_frames*T][hidden] -> (c_q, q_nope, q_r), views of buffers this
+        layer owns (overwritten by the next call). Needs w_dq, w_uq, w_qr."""
+        if n_frames > self.max_chunk_frames:
+            raise ValueError("chunk larger than the buffers were sized for")
+        for k in ("w_dq", "w_uq", "w_qr"):
+            if k not in self.w:
+                raise ValueError(f"the query path needs {k}")
+        d_cq = self.w["w_dq"].shape[0]
+        H, n = self.cfg.n_heads, n_frames * self.T
+        widths = (d_cq, H * self.cfg.d_head, H * self.cfg.d_rope)
+        if self.q_buffers is None or self.q_buffers[0].numel() != self.B * self.max_chunk_frames * self.T * d_cq:
+            rows = self.B * self.max_chunk_frames * self.T
+            self.q_buffers = tuple(torch.empty(rows * w, dtype=self.dtype, device=self.device) for w in widths)
+        # leading elements of the flat buffers, viewed [B][n][...] (contiguous)
+        c_q = self.q_buffers[0][:self.B * n * d_cq].view(self.B, n, d_cq)
+        q_nope = self.q_buffers[1][:self.B * n * widths[1]].view(self.B, n, H, self.cfg.d_head)
+        q_r = self.q_buffers[2][:self.B * n * widths[2]].view(self.B, n, H, self.cfg.d_rope)
+        _lib.query_project(self.shape, d_cq, x, n_frames, self.w["w_dq"], self.w["w_uq"], self.w["w_qr"], c_q, q_nope,
+                           q_r, stream)
+        return c_q, q_nope, q_r
+
+    def project_output(self, o, n_frames: int, out=None, stream=None):
+        """u = W_o [o_1; ...; o_H] for the heads' outputs o [B][n_frames*T][H][d_head]."""
+        if "w_o" not in self.w:
+            raise ValueError("the output projection needs w_o")
+        if out is None:
+            out = torch.empty(self.B, n_frames * self.T, self.cfg.hidden, dtype=self.dtype, device=self.device)
+        _lib.output_project(self.shape, o, n_frames, self.w["w_o"], out, stream)
+        return out
+
+    def step(self, x, frame_first: int, n_frames: int, frame_causal: bool = False, stream=None):
+        """The whole layer for one chunk: queries from the chunk's tokens, the
+        cache write of the same tokens, the attention over the window, and the
+        output projection -> u [B][n_frames*T][hidden]."""
+        _, q_nope, q_r = self.project_queries(x, n_frames, stream)
+        self.write(x, frame_first, n_frames, stream)
+        attend = self.attend_frame_causal if frame_causal else self.attend
+        o = attend(q_nope, q_r, frame_first, n_frames, stream=stream)
+        return self.project_output(o, n_frames, stream=stream)

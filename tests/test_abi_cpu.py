@@ -122,6 +122,15 @@ def test_entry_points_reject_bad_arguments_before_launch(built_lib):
     f32 = _shape("wan_small_f32")
     assert lib.mla_chunk_attend_heads(ctypes.byref(f32), fake, fake, 0, 1, fake, fake, fake, fake, fake, 0, 21,
                                       fake, fake, 1 << 40, None) == 6
+    # query path and output projection: NULL, alignment, query latent width, frame count
+    assert lib.mla_query_project(sp, 576, fake, 3, fake, fake, None, fake, fake, fake, None) == 1
+    assert lib.mla_query_project(sp, 576, fake, 3, fake, fake, fake, odd, fake, fake, None) == 4
+    assert lib.mla_query_project(sp, 572, fake, 3, fake, fake, fake, fake, fake, fake, None) == 2
+    assert lib.mla_query_project(sp, 0, fake, 3, fake, fake, fake, fake, fake, fake, None) == 2
+    assert lib.mla_query_project(sp, 576, fake, 0, fake, fake, fake, fake, fake, fake, None) == 8
+    assert lib.mla_output_project(sp, fake, 3, None, fake, None) == 1
+    assert lib.mla_output_project(sp, fake, 3, fake, odd, None) == 4
+    assert lib.mla_output_project(sp, fake, -1, fake, fake, None) == 8
     # unsupported latent width
     bad = _shape(d_c=96)
     assert lib.mla_cache_write(ctypes.byref(bad), fake, fake, fake, 0, 3, fake, fake, None) == 6

@@ -1,0 +1,148 @@
+"""Parity of the query path (mla_query_project), the output projection
+(mla_output_project) and the whole layer built from them with the fp64
+oracle.
+
+The projections are plain matrix products with fp32 accumulation and one
+rounding of each stored result; the query latent is stored in the element
+type before the per-head products read it. The bound used for a product
+y = A b whose operand b was rounded (relative error u_b) and whose result is
+rounded (u_y) is the standard forward bound
+    |y_gpu - y| <= u_b (|A| |b|) + u_y |y| + K * 2^-22 (|A| |b|),
+evaluated by the oracle in fp64 (K = contraction length; the last term is
+the fp32 accumulation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import latent_kv_attention_amd as mla
+from latent_kv_attention_amd.layer import LatentLayer
+from harness import chunk_queries, get_config, query_weights
+from oracle import mla_oracle as O
+
+from .gpu_common import Stream, assert_step_close, device_weights, to_numpy, to_torch
+
+pytestmark = pytest.mark.gpu
+
+PROJ_CONFIGS = ["tiny", "tiny_bf16", "wan_small", "wan_small_f32", "wan_small_c160r64"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib(built_lib):
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    mla.lib()
+    yield
+
+
+def _unit(dtype):
+    return 2.0 ** -8 if dtype == "bf16" else 2.0 ** -24
+
+
+def _assert_product_close(got, ref, absprod, dtype, k, rounded_operand, label):
+    u = _unit(dtype)
+    bound = (u if rounded_operand else 0.0) * absprod + u * np.abs(ref) + k * 2.0 ** -22 * absprod + 1e-30
+    bad = np.abs(got - ref) > bound
+    print(f"[proj] {label} max_abs={np.abs(got - ref).max():.3e} violations={int(bad.sum())}", flush=True)
+    assert not bad.any(), (label, int(bad.sum()))
+    assert np.isfinite(got).all()
+
+
+def _weights(cfg, seed):
+    w, wd = device_weights(cfg, seed)
+    wq = query_weights(cfg, seed)
+    return {**w, **wq}, {**wd, **{k: to_torch(v, cfg.dtype) for k, v in wq.items()}}
+
+
+def _check_query_path(cfg, seed, x, n_frames, B=1, rows=None):
+    """x [B, n, hidden] (host, rounded): GPU query path vs the oracle."""
+    w, wd = _weights(cfg, seed)
+    layer = LatentLayer(cfg, wd, batch=B, rope_n_t=64, max_chunk_frames=n_frames)
+    c_q, qn, qr = layer.project_queries(to_torch(x, cfg.dtype).contiguous(), n_frames)
+    torch.cuda.synchronize()
+    c_q, qn, qr = to_numpy(c_q), to_numpy(qn), to_numpy(qr)
+    xr = x.reshape(-1, cfg.hidden)
+    sel = np.arange(xr.shape[0]) if rows is None else rows
+    xs = xr[sel]
+    c_ref, qn_ref, qr_ref = O.query_project(xs, w["w_dq"], w["w_uq"], w["w_qr"])
+    _assert_product_close(c_q.reshape(-1, cfg.q_latent)[sel], c_ref, np.abs(xs) @ np.abs(w["w_dq"]).T, cfg.dtype,
+                          cfg.hidden, False, f"{cfg.name} c_q")
+    # magnitudes |W_uq| |c_q| for the bound
+    ac = np.abs(c_ref)
+    an = np.einsum("nc,hdc->nhd", ac, np.abs(w["w_uq"]))
+    ar = np.einsum("nc,hdc->nhd", ac, np.abs(w["w_qr"]))
+    _assert_product_close(qn.reshape(-1, cfg.n_heads, cfg.d_head)[sel], qn_ref, an, cfg.dtype, cfg.q_latent, True,
+                          f"{cfg.name} q_nope")
+    _assert_product_close(qr.reshape(-1, cfg.n_heads, cfg.d_rope)[sel], qr_ref, ar, cfg.dtype, cfg.q_latent, True,
+                          f"{cfg.name} q_r")
+
+
+@pytest.mark.parametrize("name", PROJ_CONFIGS)
+def test_query_project(name):
+    cfg = get_config(name)
+    st = Stream(cfg, seed=51)
+    x = st.xs(0, cfg.chunk_frames)[None]
+    _check_query_path(cfg, 51, x, cfg.chunk_frames)
+
+
+def test_query_project_batch_ragged_rows_and_narrow_latent():
+    """Three streams of a 2-frame chunk (396 rows: ragged against every
+    row tile) with a query latent of 40 (a partial K step and a partial
+    column tile)."""
+    cfg = get_config("wan_small").with_(d_cq=40)
+    x = np.stack([Stream(cfg, seed=52, stream=b).xs(0, 2) for b in range(3)])
+    _check_query_path(cfg, 52, x, 2, B=3)
+
+
+def test_query_project_wan_full_size_sampled_rows():
+    """Wan2.1-1.3B shape: the 4680 tokens of a 3-frame chunk, d_cq 576; 200
+    sampled rows (first and last rows and 128-row tile edges included)."""
+    cfg = get_config("wan")
+    x = Stream(cfg, seed=53).xs(0, 3)[None]
+    rng = np.random.default_rng(3)
+    edge = [0, 1, 63, 64, 127, 128, 4607, 4608, cfg.n_q - 1]
+    rows = np.unique(np.concatenate([edge, rng.choice(cfg.n_q, 200 - len(edge), replace=False)]))
+    _check_query_path(cfg, 53, x, 3, rows=rows)
+
+
+@pytest.mark.parametrize("name", PROJ_CONFIGS)
+def test_output_project(name):
+    cfg = get_config(name)
+    w, wd = _weights(cfg, 54)
+    layer = LatentLayer(cfg, wd, batch=2, rope_n_t=64)
+    # seeded stand-ins for the heads' outputs (unit-order entries)
+    o = np.stack([chunk_queries(cfg, 0, seed=54, stream=b)[0] for b in range(2)])
+    u = layer.project_output(to_torch(o, cfg.dtype).contiguous(), cfg.chunk_frames)
+    torch.cuda.synchronize()
+    got = to_numpy(u).reshape(-1, cfg.hidden)
+    of = o.reshape(-1, cfg.n_heads * cfg.d_head)
+    ref = O.output_project(o.reshape(-1, cfg.n_heads, cfg.d_head), w["w_o"])
+    _assert_product_close(got, ref, np.abs(of) @ np.abs(w["w_o"]).T, cfg.dtype, cfg.n_heads * cfg.d_head, False,
+                          f"{name} u")
+
+
+def _layer_steps(cfg, seed, n_chunks, frame_causal=False):
+    """Chunk after chunk through LatentLayer.step (queries from the tokens,
+    cache write, attention, output projection) against O.layer_step."""
+    w, wd = _weights(cfg, seed)
+    layer = LatentLayer(cfg, wd, batch=1, rope_n_t=64)
+    ring = O.RingCache(cfg.window_frames, cfg.tokens_per_frame, cfg.d_c, cfg.d_rope)
+    st = Stream(cfg, seed=seed)
+    for k in range(n_chunks):
+        f0 = k * cfg.chunk_frames
+        x = st.xs(f0, cfg.chunk_frames)
+        u = layer.step(to_torch(x[None], cfg.dtype), f0, cfg.chunk_frames, frame_causal=frame_causal)
+        torch.cuda.synchronize()
+        ref, _, _, _ = O.layer_step(O.dims_of(cfg), w, ring, x, f0, frame_causal=frame_causal)
+        assert_step_close(to_numpy(u)[0], ref, cfg.dtype, label=f"{cfg.name} layer step chunk {k}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "wan_small", "wan_small_f32", "wan_small_c128r32"])
+def test_layer_step(name):
+    cfg = get_config(name)
+    n_chunks = cfg.window_frames // cfg.chunk_frames + 2  # the ring wraps
+    _layer_steps(cfg, 55, n_chunks)
+
+
+def test_layer_step_frame_causal():
+    cfg = get_config("wan_small").with_(chunk_frames=2, window_frames=4)
+    _layer_steps(cfg, 56, 3, frame_causal=True)
