@@ -348,21 +348,30 @@ def projections_report(cfg, args):
                  cfg.dtype, dev)
     o = torch.randn(1, cfg.n_q, cfg.n_heads, cfg.d_head, device=dev).to(torch.bfloat16)
     u = torch.empty(1, cfg.n_q, cfg.hidden, dtype=torch.bfloat16, device=dev)
+    # the same products through torch's library GEMM (context only)
+    x2, o2 = x.view(cfg.n_q, cfg.hidden), o.view(cfg.n_q, cfg.n_heads * cfg.d_head)
+    w_q = torch.cat([w["w_uq"].reshape(-1, cfg.q_latent), w["w_qr"].reshape(-1, cfg.q_latent)]).contiguous()
+    lin = torch.nn.functional.linear
     calls = {
         "query_project": lambda: layer.project_queries(x, cfg.chunk_frames),
         "output_project": lambda: layer.project_output(o, cfg.chunk_frames, out=u),
         "layer_step": lambda: layer.step(x, chunk_first, cfg.chunk_frames),
+        "library_query": lambda: lin(lin(x2, w["w_dq"]), w_q),
+        "library_output": lambda: lin(o2, w["w_o"]),
     }
+    # each sample: `reps` calls back to back between two events on the stream
+    reps = 10
     ts = {k: [] for k in calls}
     for rnd in range(args.warmup + args.steps):
         for k, fn in calls.items():
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            fn()
+            for _ in range(reps):
+                fn()
             b.record()
             torch.cuda.synchronize()
             if rnd >= args.warmup:
-                ts[k].append(a.elapsed_time(b))
+                ts[k].append(a.elapsed_time(b) / reps)
     ms = {k: float(np.median(v)) for k, v in ts.items()}
     M, H = cfg.n_q, cfg.n_heads
     q_fl = 2.0 * M * (cfg.hidden * cfg.q_latent + cfg.q_latent * H * (cfg.d_head + cfg.d_rope))
@@ -377,6 +386,8 @@ def projections_report(cfg, args):
         "output_project_TFLOPs": round(tf(o_fl, ms["output_project"]), 1),
         "projections_frac_of_bf16_peak": round(tf(q_fl + o_fl, ms["query_project"] + ms["output_project"])
                                                / PEAK_BF16_TFLOPS, 4),
+        "library_gemm_query_ms": round(ms["library_query"], 4),
+        "library_gemm_output_ms": round(ms["library_output"], 4),
         "layer_step_ms": round(ms["layer_step"], 4),
         "projections_share_of_layer": round((ms["query_project"] + ms["output_project"]) / ms["layer_step"], 4),
         "finite": bool(torch.isfinite(u.float()).all()),

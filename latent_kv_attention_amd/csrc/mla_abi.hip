@@ -561,18 +561,24 @@ namespace {
 
 constexpr int kMaxQueryLatent = 1 << 16;
 
-mla_status gemm(const mla_shape* s, const void* a, const void* b, void* c, int64_t M, int N, int K,
-                hipStream_t st) {
+// C = A B^T with the output features split in two parts (n >= n_split: weight
+// b2, output c2); n_split = N for a single part.
+mla_status gemm(const mla_shape* s, const void* a, const void* b, const void* b2, void* c, void* c2, int64_t M,
+                int N, int n_split, int K, hipStream_t st) {
   mla::GemmParams p{};
   p.a = a;
   p.b = b;
+  p.b2 = b2;
   p.c = c;
+  p.c2 = c2;
   p.M = (int)M;
   p.N = N;
   p.K = K;
   p.lda = K;
   p.ldb = K;
-  p.ldc = N;
+  p.ldc = n_split;
+  p.ldc2 = N - n_split;
+  p.n_split = n_split;
   return from_hip(mla::launch_gemm_nt(s->dtype, p, mla::gemm_tile_rows(p.M, N, device_cus()), st));
 }
 
@@ -595,15 +601,15 @@ MLA_API mla_status mla_query_project(const mla_shape* shape, int32_t d_cq, const
       !aligned16(q_nope) || !aligned16(q_r))
     return MLA_ERR_ALIGN;
   if (d_cq < 8 || d_cq % 8 != 0 || d_cq > kMaxQueryLatent) return MLA_ERR_SHAPE;
-  if ((int64_t)shape->n_heads * shape->d_head > kMaxQueryLatent ||
-      (int64_t)shape->n_heads * shape->d_rope > kMaxQueryLatent || shape->d_rope % 8 != 0)
+  if ((int64_t)shape->n_heads * (shape->d_head + shape->d_rope) > kMaxQueryLatent || shape->d_rope % 8 != 0)
     return MLA_ERR_SHAPE;
   int64_t rows = 0;
   if ((st = check_projection_rows(shape, n_frames, &rows)) != MLA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  if ((st = gemm(shape, x, w_dq, c_q, rows, d_cq, shape->hidden, s)) != MLA_OK) return st;
-  if ((st = gemm(shape, c_q, w_uq, q_nope, rows, shape->n_heads * shape->d_head, d_cq, s)) != MLA_OK) return st;
-  return gemm(shape, c_q, w_qr, q_r, rows, shape->n_heads * shape->d_rope, d_cq, s);
+  if ((st = gemm(shape, x, w_dq, nullptr, c_q, nullptr, rows, d_cq, d_cq, shape->hidden, s)) != MLA_OK) return st;
+  // content and positional queries in one product over the same query latent
+  const int n_nope = shape->n_heads * shape->d_head;
+  return gemm(shape, c_q, w_uq, w_qr, q_nope, q_r, rows, n_nope + shape->n_heads * shape->d_rope, n_nope, d_cq, s);
 }
 
 MLA_API mla_status mla_output_project(const mla_shape* shape, const void* o, int32_t n_frames, const void* w_o,
@@ -615,5 +621,6 @@ MLA_API mla_status mla_output_project(const mla_shape* shape, const void* o, int
   if ((int64_t)shape->n_heads * shape->d_head > kMaxQueryLatent) return MLA_ERR_SHAPE;
   int64_t rows = 0;
   if ((st = check_projection_rows(shape, n_frames, &rows)) != MLA_OK) return st;
-  return gemm(shape, o, w_o, u, rows, shape->hidden, shape->n_heads * shape->d_head, (hipStream_t)stream);
+  return gemm(shape, o, w_o, nullptr, u, nullptr, rows, shape->hidden, shape->hidden, shape->n_heads * shape->d_head,
+              (hipStream_t)stream);
 }

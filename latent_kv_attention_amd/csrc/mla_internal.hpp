@@ -117,13 +117,17 @@ struct HeadsParams {
 };
 
 // C[M][N] = A[M][K] B[N][K]^T (rows of B are output features), fp32
-// accumulation, C in the operands' type. K, N, lda, ldb, ldc multiples of 8;
-// pointers 16-byte aligned.
+// accumulation, C in the operands' type. Features n >= n_split take their
+// weight row from B2 (row n - n_split) and land in C2 (column n - n_split,
+// row stride ldc2); n_split = N for one part. K, N, n_split and all strides
+// multiples of 8; pointers 16-byte aligned.
 struct GemmParams {
   const void* a;
   const void* b;
+  const void* b2;
   void* c;
-  int M, N, K, lda, ldb, ldc;
+  void* c2;
+  int M, N, K, lda, ldb, ldc, ldc2, n_split;
   int tiles_n, n_logical, per_xcd;  // filled by the launcher
 };
 
@@ -140,8 +144,8 @@ hipError_t launch_rope_window(int dtype, int d_c, int d_rope, const FlashParams&
 bool heads_supported(int dtype, int d_c, int d_rope, int d_head);
 int heads_tile_keys(int d_head, int d_rope);  // keys per tile of the per-head attention kernel
 hipError_t launch_heads(int d_c, int d_rope, int d_head, const HeadsParams& p, bool split, hipStream_t s);
-// rows per work-group tile of the projection GEMM (128 or 64) for a problem
-// of M x N outputs on n_cu compute units
+// tile of the projection GEMM (128 x 128 or 64 x 64, given by its rows) for
+// a problem of M x N outputs on n_cu compute units
 int gemm_tile_rows(int M, int N, int n_cu);
 hipError_t launch_gemm_nt(int dtype, const GemmParams& p, int tile_rows, hipStream_t s);
 

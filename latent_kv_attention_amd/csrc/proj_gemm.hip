@@ -10,38 +10,45 @@
 // contiguous along the contraction and each lane's 8-element matrix-core
 // operand is one 16-byte row piece, read from LDS without a transpose.
 //
-// Work-group tile BM x 128 outputs (BM = 128 or 64), 64-wide K steps: the
-// next step's operands are loaded into registers while the matrix cores
-// work on the current one from LDS. Rows of the staged tiles are padded by
-// 16 bytes, so the 16 rows of one operand read fall on distinct banks. The
-// output tile leaves through LDS in 16-byte row pieces. Tiles are numbered
-// row-major and dealt to the 8 XCDs in contiguous ranges, so tiles that
-// share A rows share an L2.
+// Work-group tile 128 x 128 outputs, or 64 x 64 when the problem has too
+// few 128-tiles to fill the chip; 64-wide K steps through two LDS stage
+// buffers: the next step's operands are loaded into registers while the
+// matrix cores work on the current one, then stored into the other buffer
+// (one barrier per step). Rows of the staged tiles are padded by 16 bytes,
+// so the 16 rows of one operand read fall on distinct banks. The output tile
+// leaves through LDS in 16-byte row pieces. Tiles are numbered row-major and
+// dealt to the 8 XCDs in contiguous ranges, so tiles that share A rows share
+// an L2.
+//
+// The output features may come in two parts with their own weight and
+// output arrays (features n >= n_split: weight B2 row n - n_split, output
+// C2 column n - n_split), so that the per-head content and positional
+// queries, which read the same query latent, are one launch.
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
 namespace mla {
 
 namespace {
-constexpr int kGemmBN = 128;
 constexpr int kGemmBK = 64;
 constexpr int kGemmXcds = 8;
 }  // namespace
 
-template <typename T, int BM>
+template <typename T, int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   typedef typename V8<T>::type v8;
-  constexpr int BN = kGemmBN, BK = kGemmBK;
+  constexpr int BK = kGemmBK;
   constexpr int PAD = 16 / sizeof(T);
   constexpr int LDK = BK + PAD;                 // staged row stride (elements)
   constexpr int LDC = BN + PAD;                 // output staging row stride
   constexpr int CHUNKS = BK / 8;                // 8-element pieces per staged row
   constexpr int NLD = (BM + BN) * CHUNKS / 256; // pieces per thread per K step
+  constexpr int STAGE = (BM + BN) * LDK;        // elements of one stage buffer
   constexpr int WM = BM / 2, WN = BN / 2;       // wave tile (2 x 2 waves)
   constexpr int NMB = WM / 16, NNB = WN / 16;
   static_assert((BM + BN) * CHUNKS % 256 == 0, "whole pieces per thread");
-  static_assert(BM * LDC <= (BM + BN) * LDK, "output tile fits in the staging buffer");
-  __shared__ __attribute__((aligned(16))) T lds[(BM + BN) * LDK];
+  static_assert(BM * LDC <= 2 * STAGE, "output tile fits in the stage buffers");
+  __shared__ __attribute__((aligned(16))) T lds[2 * STAGE];
 
   const int logical = (blockIdx.x % kGemmXcds) * p.per_xcd + blockIdx.x / kGemmXcds;
   if (logical >= p.n_logical) return;
@@ -51,16 +58,22 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   const int li = lane & 15, lg = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // staged row r < BM is A row row0 + r, else B row col0 + r - BM; rows past
-  // the end repeat the last row (their products are never stored)
+  // staged row r < BM is A row row0 + r, else output feature n = col0 + r - BM
+  // (B row n, or B2 row n - n_split past the split); rows past the end
+  // repeat the last row (their products are never stored)
   const T* src[NLD];
   int dst[NLD], kof[NLD];
 #pragma unroll
   for (int j = 0; j < NLD; ++j) {
     const int e = tid + 256 * j;
     const int r = e / CHUNKS, c = e % CHUNKS;
-    src[j] = r < BM ? (const T*)p.a + (size_t)min(row0 + r, p.M - 1) * p.lda + c * 8
-                    : (const T*)p.b + (size_t)min(col0 + r - BM, p.N - 1) * p.ldb + c * 8;
+    if (r < BM) {
+      src[j] = (const T*)p.a + (size_t)min(row0 + r, p.M - 1) * p.lda + c * 8;
+    } else {
+      const int n = min(col0 + r - BM, p.N - 1);
+      src[j] = n < p.n_split ? (const T*)p.b + (size_t)n * p.ldb + c * 8
+                             : (const T*)p.b2 + (size_t)(n - p.n_split) * p.ldb + c * 8;
+    }
     dst[j] = r * LDK + c * 8;
     kof[j] = c * 8;
   }
@@ -69,31 +82,42 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < NLD; ++j) stage[j] = k0 + kof[j] < p.K ? load8<T>(src[j] + k0) : zero8<T>();
   };
+  auto stash = [&](T* buf) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) store8<T>(buf + dst[j], stage[j]);
+  };
 
   f32x4 acc[NMB][NNB] = {};
-  fetch(0);
-  for (int k0 = 0; k0 < p.K; k0 += BK) {
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) store8<T>(lds + dst[j], stage[j]);
-    __syncthreads();
-    if (k0 + BK < p.K) fetch(k0 + BK);
+  auto compute = [&](const T* buf) {
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
       v8 af[NMB], bf[NNB];
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) af[mb] = lds_load8<T>(lds + (wm * WM + mb * 16 + li) * LDK + kk * 32 + lg * 8);
+      for (int mb = 0; mb < NMB; ++mb) af[mb] = lds_load8<T>(buf + (wm * WM + mb * 16 + li) * LDK + kk * 32 + lg * 8);
 #pragma unroll
       for (int nb = 0; nb < NNB; ++nb)
-        bf[nb] = lds_load8<T>(lds + (BM + wn * WN + nb * 16 + li) * LDK + kk * 32 + lg * 8);
+        bf[nb] = lds_load8<T>(buf + (BM + wn * WN + nb * 16 + li) * LDK + kk * 32 + lg * 8);
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NNB; ++nb) acc[mb][nb] = mma16(af[mb], bf[nb], acc[mb][nb]);
     }
+  };
+
+  // two stage buffers: step k computes from buffer k % 2 while the operands
+  // of step k + 1 travel to registers and then into the other buffer, which
+  // every wave finished reading before the barrier that ended step k - 1
+  const int nk = (p.K + BK - 1) / BK;
+  fetch(0);
+  stash(lds);
+  __syncthreads();
+  for (int k = 0; k < nk; ++k) {
+    if (k + 1 < nk) fetch((k + 1) * BK);
+    compute(lds + (k & 1) * STAGE);
+    if (k + 1 < nk) stash(lds + ((k + 1) & 1) * STAGE);
+    __syncthreads();
   }
 
-  __syncthreads();
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -102,31 +126,37 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
       for (int i = 0; i < 4; ++i)
         lds[(wm * WM + mb * 16 + lg * 4 + i) * LDC + wn * WN + nb * 16 + li] = to_t<T>(acc[mb][nb][i]);
   __syncthreads();
+  // 8-column pieces never straddle n_split (both multiples of 8)
   for (int e = tid; e < BM * (BN / 8); e += 256) {
     const int r = e / (BN / 8), c8 = (e % (BN / 8)) * 8;
-    if (row0 + r < p.M && col0 + c8 < p.N)
-      store8<T>((T*)p.c + (size_t)(row0 + r) * p.ldc + col0 + c8, lds_load8<T>(lds + r * LDC + c8));
+    const int n = col0 + c8;
+    if (row0 + r < p.M && n < p.N) {
+      T* dstp = n < p.n_split ? (T*)p.c + (size_t)(row0 + r) * p.ldc + n
+                              : (T*)p.c2 + (size_t)(row0 + r) * p.ldc2 + (n - p.n_split);
+      store8<T>(dstp, lds_load8<T>(lds + r * LDC + c8));
+    }
   }
 }
 
 int gemm_tile_rows(int M, int N, int n_cu) {
-  const long long big = (long long)((M + 127) / 128) * ((N + kGemmBN - 1) / kGemmBN);
+  const long long big = (long long)((M + 127) / 128) * ((N + 127) / 128);
   return big >= n_cu ? 128 : 64;
 }
 
-template <typename T, int BM>
+template <typename T, int BM, int BN>
 static hipError_t launch_gemm_t(GemmParams p, hipStream_t s) {
-  p.tiles_n = (p.N + kGemmBN - 1) / kGemmBN;
+  p.tiles_n = (p.N + BN - 1) / BN;
   p.n_logical = ((p.M + BM - 1) / BM) * p.tiles_n;
   p.per_xcd = (p.n_logical + kGemmXcds - 1) / kGemmXcds;
-  hipLaunchKernelGGL((gemm_nt_kernel<T, BM>), dim3(p.per_xcd * kGemmXcds), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN>), dim3(p.per_xcd * kGemmXcds), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_nt(int dtype, const GemmParams& p, int tile_rows, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
-  if (tile_rows == 128) return dtype == 0 ? launch_gemm_t<bf16, 128>(p, s) : launch_gemm_t<float, 128>(p, s);
-  if (tile_rows == 64) return dtype == 0 ? launch_gemm_t<bf16, 64>(p, s) : launch_gemm_t<float, 64>(p, s);
+  if (tile_rows == 128)
+    return dtype == 0 ? launch_gemm_t<bf16, 128, 128>(p, s) : launch_gemm_t<float, 128, 128>(p, s);
+  if (tile_rows == 64) return dtype == 0 ? launch_gemm_t<bf16, 64, 64>(p, s) : launch_gemm_t<float, 64, 64>(p, s);
   return hipErrorInvalidValue;
 }
 
