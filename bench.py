@@ -394,6 +394,111 @@ def projections_report(cfg, args):
         "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic"}), flush=True)
 
 
+def configs_report(args):
+    """Multi-layer and multi-stream workloads of the Wan shape, one JSON report
+    line each (not the bench line): a 30-layer model whose windows fill over 7
+    chunks; 8 streams with full windows through 30 layers; an 80-chunk,
+    30-layer rollout whose rings evict from the 8th chunk on. Each layer has
+    its own weights and ring; per layer and chunk: cache write, query absorb,
+    attention, up-projection (mla_cache_write + mla_chunk_attend). Inputs
+    come from device-resident pools (64 token frames, 4 query sets); the
+    content does not change the work. Timed with HIP events around the whole
+    run after one untimed warm-up chunk per layer."""
+    import numpy as np
+    import torch
+
+    import latent_kv_attention_amd as mla
+    from harness import chunk_queries, frame_tokens, get_config, layer_weights
+    from harness.torch_io import to_torch
+    from latent_kv_attention_amd.layer import LatentLayer
+
+    dev = "cuda"
+    base = get_config("wan")
+    T = base.tokens_per_frame
+    print("[bench] configs: device pools", file=sys.stderr, flush=True)
+    # token pool with two wrap-around frames, so any 3 consecutive pool frames are one view
+    pool = torch.empty(66, T, base.hidden, dtype=torch.bfloat16, device=dev)
+    for i in range(64):
+        pool[i] = to_torch(frame_tokens(base, i), "bf16", dev)
+    pool[64:] = pool[:2]
+    qpool = [tuple(to_torch(a, "bf16", dev) for a in chunk_queries(base, 3 * i)) for i in range(4)]
+
+    def x_of(stream, layer, f0):
+        i = (f0 + 7 * layer + 13 * stream) % 64
+        return pool[i:i + 3].reshape(1, 3 * T, base.hidden)
+
+    def run(name, B, n_chunks, prefill_frames):
+        cfg = get_config(name)
+        L = cfg.layers
+        layers = []
+        for l in range(L):
+            wd = {k: to_torch(v, "bf16", dev) for k, v in layer_weights(cfg, 0, l).items()}
+            layers.append(LatentLayer(cfg, wd, batch=B, rope_n_t=256))
+        xb = torch.empty(B, 3 * T, base.hidden, dtype=torch.bfloat16, device=dev)
+        qn = torch.stack([qpool[b % 4][0] for b in range(B)])
+        qr = torch.stack([qpool[b % 4][1] for b in range(B)])
+        out = torch.empty(B, 3 * T, cfg.n_heads, cfg.d_head, dtype=torch.bfloat16, device=dev)
+
+        def fill(l, f0):
+            for b in range(B):
+                xb[b] = x_of(b, l, f0)[0]
+            return xb
+
+        for l, layer in enumerate(layers):  # prefill (untimed)
+            for f0 in range(0, prefill_frames, 3):
+                layer.write(fill(l, f0), f0, 3)
+        first = prefill_frames
+        for l, layer in enumerate(layers):  # warm-up chunk, rewritten in the timed run
+            layer.write(fill(l, first), first, 3)
+            layer.attend(qn, qr, first, 3, out=out)
+        torch.cuda.synchronize()
+        # token inputs of every (chunk, layer) gathered before the clock starts
+        xs = {}
+        for k in range(n_chunks):
+            for l in range(L):
+                f0 = first + 3 * k
+                key = tuple((f0 + 7 * l + 13 * b) % 64 for b in range(B))
+                if key not in xs:
+                    xs[key] = torch.stack([x_of(b, l, f0)[0] for b in range(B)]) if B > 1 else x_of(0, l, f0)
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for k in range(n_chunks):
+            f0 = first + 3 * k
+            for l, layer in enumerate(layers):
+                key = tuple((f0 + 7 * l + 13 * b) % 64 for b in range(B))
+                layer.write(xs[key], f0, 3)
+                layer.attend(qn, qr, f0, 3, out=out)
+        e.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(e)
+        assert torch.isfinite(out.float()).all()
+        # attention FLOPs: window of min(W, frames written) frames at each chunk
+        fl = 0.0
+        for k in range(n_chunks):
+            nk = min(cfg.window_frames, first + 3 * k + 3) * T
+            fl += L * B * 2.0 * 3 * T * nk * cfg.n_heads * (2 * cfg.d_c + cfg.d_rope)
+        slots = [int(v) for v in layers[0].slot_frame[0].cpu()]
+        del layers
+        torch.cuda.empty_cache()
+        return ms, fl, slots
+
+    runs = [("wan_fill30", 1, 7, 0, "30 layers x 7 chunks, windows filling 3 -> 21 frames"),
+            ("wan_batch8", 8, 1, 18, "8 streams x 30 layers, one chunk over full 21-frame windows"),
+            ("wan_rollout", 1, 80, 0, "80 chunks x 30 layers (frames 0..239), rings evicting from chunk 8")]
+    for name, B, n_chunks, prefill, what in runs:
+        print(f"[bench] configs: {name}", file=sys.stderr, flush=True)
+        ms, fl, slots = run(name, B, n_chunks, prefill)
+        print(json.dumps({
+            "report": f"Wan2.1-1.3B-shaped workload: {what}, 1 MI355X",
+            "config": name, "streams": B, "layers": 30, "chunks": n_chunks, "total_ms": round(ms, 2),
+            "ms_per_layer_chunk": round(ms / (30 * n_chunks), 4),
+            "ms_per_chunk_all_layers": round(ms / n_chunks, 3),
+            "attention_TFLOP": round(fl / 1e12, 2), "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 1),
+            "cache_MB_resident": round(30 * B * 21 * T * 224 * 2 / 1e6, 1),
+            "last_slot_frames_layer0": slots,
+            "dtype": "bf16", "data": "synthetic"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -410,6 +515,8 @@ def main():
                     help="time the attention side with and without the frame-causal mask (report line) and exit")
     ap.add_argument("--projections", action="store_true",
                     help="time the query path, the output projection and the whole layer (report line) and exit")
+    ap.add_argument("--configs", action="store_true",
+                    help="time the 30-layer fill, 8-stream and 80-chunk rollout workloads (report lines) and exit")
     ap.add_argument("--latent-sweep", action="store_true",
                     help="time the step at every latent width with kernels (one report line each) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -456,6 +563,9 @@ def main():
         return
     if args.projections:
         projections_report(cfg, args)
+        return
+    if args.configs:
+        configs_report(args)
         return
     ctx = setup_step(cfg, args.kv_splits)
     ms_step, per = time_steps(ctx, args.steps, args.warmup)
