@@ -33,6 +33,8 @@
  *     MLA_F32 (float). Accumulation is fp32 in both cases. RoPE tables are
  *     always float.
  *   - Every device pointer must be 16-byte aligned.
+ *   - The *_workspace_bytes queries return 0 for any shape, chunk size or
+ *     split that the matching call rejects.
  *   - Errors are reported by return value before anything is enqueued
  *     (MLA_ERR_NULL, _SHAPE, _DTYPE, _ALIGN, _WORKSPACE, _UNSUPPORTED,
  *     _RANGE), or MLA_ERR_HIP if a launch fails. No C++ exception crosses

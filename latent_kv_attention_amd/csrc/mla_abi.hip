@@ -39,17 +39,19 @@ mla_status check_shape(const mla_shape* s) {
   if (s->window_frames < 1 || s->window_frames > kMaxWindow) return MLA_ERR_SHAPE;
   if (s->d_rope_t < 0 || s->d_rope_y < 0 || s->d_rope_x < 0) return MLA_ERR_SHAPE;
   if (s->d_rope_t % 2 || s->d_rope_y % 2 || s->d_rope_x % 2) return MLA_ERR_SHAPE;
-  if (s->d_rope_t + s->d_rope_y + s->d_rope_x != s->d_rope) return MLA_ERR_SHAPE;
+  if ((int64_t)s->d_rope_t + s->d_rope_y + s->d_rope_x != s->d_rope) return MLA_ERR_SHAPE;
   if (s->d_c < 1 || s->d_rope < 1) return MLA_ERR_SHAPE;
   if (!(s->rope_base > 0.f) || !isfinite(s->rope_base)) return MLA_ERR_SHAPE;
   if (!isfinite(s->softmax_scale)) return MLA_ERR_SHAPE;
+  // (each product below is bounded by the checks before it, so none overflows)
   const int64_t T = (int64_t)s->grid_y * s->grid_x;
+  // the attention kernel splits key indices with a float reciprocal (exact
+  // below 2^22 keys per window)
+  if (T > mla::kMaxWindowKeys || T * s->window_frames > mla::kMaxWindowKeys) return MLA_ERR_SHAPE;
+  if (s->d_c > (1 << 16) || s->d_rope > (1 << 16)) return MLA_ERR_SHAPE;
   // per-stream cache element offsets are 32-bit inside the kernels
   if (T * s->window_frames * (s->d_c + s->d_rope) > INT32_MAX) return MLA_ERR_SHAPE;
   if ((int64_t)s->batch * s->window_frames * T * (s->d_c + s->d_rope) > INT64_C(1) << 40) return MLA_ERR_SHAPE;
-  // the attention kernel splits key indices with a float reciprocal (exact
-  // below 2^22 keys per window)
-  if (T * s->window_frames > mla::kMaxWindowKeys) return MLA_ERR_SHAPE;
   if (!latent_supported(s->d_c, s->d_rope)) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
@@ -386,7 +388,10 @@ MLA_API mla_status mla_absorb_q(const mla_shape* shape, const void* q_nope, cons
 }
 
 MLA_API size_t mla_flash_workspace_bytes(const mla_shape* shape, int32_t q_n_frames, int32_t kv_splits) {
-  if (check_shape(shape) != MLA_OK || q_n_frames < 1 || kv_splits < 0 || kv_splits > kMaxSplits) return 0;
+  // 0 for any shape or chunk size that the calls themselves reject
+  if (check_shape(shape) != MLA_OK || check_query_args(shape, 0, q_n_frames) != MLA_OK || kv_splits < 0 ||
+      kv_splits > kMaxSplits)
+    return 0;
   return flash_ws_bytes(shape, q_n_frames, kv_splits);
 }
 
@@ -420,7 +425,7 @@ MLA_API mla_status mla_up_v(const mla_shape* shape, const void* o_lat, int32_t q
 }
 
 MLA_API size_t mla_chunk_attend_workspace_bytes(const mla_shape* shape, int32_t q_n_frames) {
-  if (check_shape(shape) != MLA_OK || q_n_frames < 1) return 0;
+  if (check_shape(shape) != MLA_OK || check_query_args(shape, 0, q_n_frames) != MLA_OK) return 0;
   const size_t rows = (size_t)shape->batch * q_n_frames * tokens_per_frame(shape) * shape->n_heads;
   return round256(rows * qabs_dim(shape) * elt_size(shape)) + round256(rows * shape->d_c * elt_size(shape)) +
          flash_ws_bytes(shape, q_n_frames, 0);
@@ -478,7 +483,7 @@ MLA_API mla_status mla_chunk_attend_frame_causal(const mla_shape* shape, const v
 }
 
 MLA_API size_t mla_chunk_attend_heads_workspace_bytes(const mla_shape* shape, int32_t q_n_frames) {
-  if (check_shape(shape) != MLA_OK || q_n_frames < 1) return 0;
+  if (check_shape(shape) != MLA_OK || check_query_args(shape, 0, q_n_frames) != MLA_OK) return 0;
   if (!mla::heads_supported(shape->dtype == MLA_BF16 ? 0 : 1, shape->d_c, shape->d_rope, shape->d_head)) return 0;
   return heads_ws_layout(shape, q_n_frames).total;
 }
