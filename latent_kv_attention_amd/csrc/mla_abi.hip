@@ -570,6 +570,8 @@ constexpr int kMaxQueryLatent = 1 << 16;
 // b2, output c2); n_split = N for a single part.
 mla_status gemm(const mla_shape* s, const void* a, const void* b, const void* b2, void* c, void* c2, int64_t M,
                 int N, int n_split, int K, hipStream_t st) {
+  // work-group tiles (at most 64 x 64 outputs each) are counted in 32 bits
+  if (((M + 63) / 64) * ((N + 63) / 64) > (INT64_C(1) << 30)) return MLA_ERR_SHAPE;
   mla::GemmParams p{};
   p.a = a;
   p.b = b;

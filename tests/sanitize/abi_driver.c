@@ -147,6 +147,16 @@ int main(void) {
   EXPECT(mla_query_project(&s, 576, p, INT_MAX, p, p, p, p, p, p, NULL), MLA_ERR_SHAPE);
   EXPECT(mla_query_project(&s, 576, p, 3, p, p, p, p, p, p, NULL), MLA_ERR_HIP);
   EXPECT(mla_output_project(&s, p, 0, p, p, NULL), MLA_ERR_RANGE);
+  {
+    mla_shape t = s; /* 2^29 rows: fine for 1536 outputs, too many tiles for 65536 */
+    t.batch = 1 << 13;
+    t.grid_y = 64;
+    t.grid_x = 64;
+    t.window_frames = 1;
+    EXPECT(mla_shape_check(&t), MLA_OK);
+    EXPECT(mla_output_project(&t, p, 16, p, p, NULL), MLA_ERR_HIP);
+    EXPECT(mla_query_project(&t, 65536, p, 16, p, p, p, p, p, p, NULL), MLA_ERR_SHAPE);
+  }
   EXPECT(mla_output_project(&s, p, 3, p, p, NULL), MLA_ERR_HIP);
 
   printf("%s: %d unexpected statuses\n", failures ? "FAILED" : "ok", failures);
