@@ -239,8 +239,12 @@ def per_head_report(base, args):
 
     import latent_kv_attention_amd as mla
 
-    for dc, dr, split in SWEEP_WIDTHS:
-        cfg = base.with_(d_c=dc, d_rope=dr, rope_split=split)
+    # every latent width at the 3-frame chunk, then 1- and 2-frame chunks at the
+    # Wan width (the expansion is per call, so its share grows as the chunk shrinks)
+    cases = [base.with_(d_c=dc, d_rope=dr, rope_split=split) for dc, dr, split in SWEEP_WIDTHS]
+    cases += [base.with_(chunk_frames=nf) for nf in (1, 2)]
+    for cfg in cases:
+        dc, dr = cfg.d_c, cfg.d_rope
         ctx = setup_step(cfg, args.kv_splits)
         ms_latent, per_latent = time_steps(ctx, args.steps, args.warmup)
         ws = torch.empty(mla.chunk_attend_heads_workspace_bytes(ctx.shape, cfg.chunk_frames), dtype=torch.uint8,
@@ -271,9 +275,9 @@ def per_head_report(base, args):
         expand_fl = 4.0 * nk * H * cfg.d_head * cfg.d_c
         latent_ms = per_latent["absorb_q"] + per_latent["flash_attend"] + per_latent["up_v"]
         print(json.dumps({
-            "report": "per-head form vs latent form, Wan2.1-1.3B-shaped chunk step (4680 queries x 32760 keys), "
+            "report": f"per-head form vs latent form, Wan2.1-1.3B-shaped chunk step ({cfg.n_q} queries x 32760 keys), "
                       "1 MI355X",
-            "d_c": dc, "d_rope": dr, "d_head": cfg.d_head,
+            "d_c": dc, "d_rope": dr, "d_head": cfg.d_head, "chunk_frames": cfg.chunk_frames, "n_q": cfg.n_q,
             "per_head_attend_ms": round(ms_a, 4), "latent_attend_ms": round(latent_ms, 4),
             "per_head_step_ms": round(ms_w + ms_a, 4), "latent_step_ms": round(ms_latent, 4),
             "speedup_attend": round(latent_ms / ms_a, 3),
