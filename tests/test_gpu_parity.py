@@ -362,6 +362,17 @@ def test_flash_attend_other_latent_widths(name, kv_splits):
     assert_step_close(got, ref, cfg.dtype, label=f"{name} flash splits={kv_splits}")
 
 
+@pytest.mark.parametrize("name", ["wan_small", "wan_small_f32"])
+@pytest.mark.parametrize("heads,d_head,hidden", [(3, 256, 200), (5, 64, 72), (1, 8, 8)])
+def test_full_step_other_head_shapes(name, heads, d_head, hidden):
+    """Head counts, head widths (the largest the library takes, 256, and the
+    smallest, 8) and token widths (not multiples of 64, so the cache write
+    takes its general kernel) other than the Wan ones, on a 5 x 7 grid."""
+    cfg = get_config(name).with_(n_heads=heads, d_head=d_head, hidden=hidden, grid_y=5, grid_x=7)
+    got, ref = _full_step(cfg, seed=16)
+    assert_step_close(got, ref, cfg.dtype, label=f"{name} H={heads} d_head={d_head} hidden={hidden}")
+
+
 def test_full_step_batch_and_partial_fill():
     cfg = get_config("wan_small")
     got, ref = _full_step(cfg, seed=12, B=3, fill=3)
