@@ -288,6 +288,38 @@ mla_status mla_query_project(const mla_shape* shape, int32_t d_cq, const void* x
 mla_status mla_output_project(const mla_shape* shape, const void* o, int32_t n_frames, const void* w_o, void* u,
                               void* stream);
 
+/* ---------------------------------------------------------------- whole layer
+ * One layer's chunk step in one call, on `stream`, in this order:
+ * mla_query_project (queries from the chunk's tokens x), mla_cache_write
+ * (the same tokens into the ring), mla_chunk_attend or, with frame_causal
+ * != 0, mla_chunk_attend_frame_causal (the chunk's queries over the
+ * window), mla_output_project (u = W_o of the heads' outputs). The query
+ * latent, the queries, the heads' outputs and the attention's workspace are
+ * carved from `workspace` (at least mla_layer_step_workspace_bytes bytes;
+ * its contents on entry do not matter). Every part's arguments are checked
+ * before the first launch, with the statuses the parts document.
+ *   weights (host) struct of device pointers, the layouts of the parts;
+ *   x (device) [B][n_frames * T][hidden]; frames frame_first ..
+ *   frame_first + n_frames - 1 (n_frames <= window_frames), which are also
+ *   the query frames (rope tables must cover them); cache, slot_frame as
+ *   for mla_cache_write; u (device) [B][n_frames * T][hidden] output. */
+typedef struct mla_layer_weights {
+  const void* w_dkv; /* [d_c][hidden] */
+  const void* w_kr;  /* [d_rope][hidden] */
+  const void* w_dq;  /* [d_cq][hidden] */
+  const void* w_uq;  /* [H][d_head][d_cq] */
+  const void* w_qr;  /* [H][d_rope][d_cq] */
+  const void* w_uk;  /* [H][d_head][d_c] */
+  const void* w_uv;  /* [H][d_head][d_c] */
+  const void* w_o;   /* [hidden][H * d_head] */
+} mla_layer_weights;
+
+size_t mla_layer_step_workspace_bytes(const mla_shape* shape, int32_t d_cq, int32_t n_frames);
+mla_status mla_layer_step(const mla_shape* shape, int32_t d_cq, const mla_layer_weights* weights, const void* x,
+                          int32_t frame_first, int32_t n_frames, void* cache, int32_t* slot_frame,
+                          const float* rope_tables, int32_t rope_t_first, int32_t rope_n_t, int32_t frame_causal,
+                          void* u, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

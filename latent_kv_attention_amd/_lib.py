@@ -27,7 +27,7 @@ EXPORTS = [
     "mla_flash_workspace_bytes", "mla_flash_attend", "mla_up_v",
     "mla_chunk_attend_workspace_bytes", "mla_chunk_attend",
     "mla_chunk_attend_heads_workspace_bytes", "mla_chunk_attend_heads", "mla_chunk_attend_frame_causal",
-    "mla_query_project", "mla_output_project",
+    "mla_query_project", "mla_output_project", "mla_layer_step_workspace_bytes", "mla_layer_step",
 ]
 
 
@@ -36,6 +36,10 @@ class MlaShape(ctypes.Structure):
         "batch", "hidden", "n_heads", "d_head", "d_c", "d_rope", "d_rope_t", "d_rope_y", "d_rope_x",
         "grid_y", "grid_x", "window_frames", "dtype")] + [("rope_base", ctypes.c_float),
                                                           ("softmax_scale", ctypes.c_float)]
+
+
+class MlaLayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_dkv", "w_kr", "w_dq", "w_uq", "w_qr", "w_uk", "w_uv", "w_o")]
 
 
 class MlaError(RuntimeError):
@@ -70,6 +74,9 @@ _SIGS = {
     "mla_chunk_attend_heads": (_I, [_SP, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
     "mla_query_project": (_I, [_SP, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P]),
     "mla_output_project": (_I, [_SP, _P, _I, _P, _P, _P]),
+    "mla_layer_step_workspace_bytes": (_SZ, [_SP, _I, _I]),
+    "mla_layer_step": (_I, [_SP, _I, ctypes.POINTER(MlaLayerWeights), _P, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P,
+                            _SZ, _P]),
 }
 
 
@@ -215,3 +222,22 @@ def query_project(shape: MlaShape, d_cq: int, x, n_frames: int, w_dq, w_uq, w_qr
 def output_project(shape: MlaShape, o, n_frames: int, w_o, u, stream=None) -> None:
     _check("mla_output_project",
            lib().mla_output_project(ctypes.byref(shape), _ptr(o), n_frames, _ptr(w_o), _ptr(u), _stream(stream)))
+
+
+def layer_weights_struct(w: dict) -> MlaLayerWeights:
+    """The eight weight tensors of a layer (dict of device tensors) as the ABI's struct."""
+    return MlaLayerWeights(*[w[k].data_ptr() for k in ("w_dkv", "w_kr", "w_dq", "w_uq", "w_qr", "w_uk", "w_uv", "w_o")])
+
+
+def layer_step_workspace_bytes(shape: MlaShape, d_cq: int, n_frames: int) -> int:
+    return lib().mla_layer_step_workspace_bytes(ctypes.byref(shape), d_cq, n_frames)
+
+
+def layer_step(shape: MlaShape, d_cq: int, weights: MlaLayerWeights, x, frame_first: int, n_frames: int, cache,
+               slot_frame, tables, rope_t_first: int, rope_n_t: int, frame_causal: bool, u, workspace,
+               stream=None) -> None:
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("mla_layer_step",
+           lib().mla_layer_step(ctypes.byref(shape), d_cq, ctypes.byref(weights), _ptr(x), frame_first, n_frames,
+                                _ptr(cache), _ptr(slot_frame), _ptr(tables), rope_t_first, rope_n_t,
+                                1 if frame_causal else 0, _ptr(u), _ptr(workspace), nbytes, _stream(stream)))

@@ -340,9 +340,12 @@ MLA_API mla_status mla_rope3d_tables(const mla_shape* shape, int32_t t_first, in
   return from_hip(mla::launch_rope_tables(p, (hipStream_t)stream));
 }
 
-MLA_API mla_status mla_cache_write(const mla_shape* shape, const void* x, const void* w_dkv, const void* w_kr,
+// Each *_impl validates, then (run = true) enqueues; with run = false it
+// only validates, so that a composite call can check every part before it
+// enqueues anything.
+static mla_status cache_write_impl(const mla_shape* shape, const void* x, const void* w_dkv, const void* w_kr,
                                    int32_t frame_first, int32_t n_frames, void* cache, int32_t* slot_frame,
-                                   void* stream) {
+                                   void* stream, bool run) {
   mla_status st = check_shape(shape);
   if (st != MLA_OK) return st;
   if (!x || !w_dkv || !w_kr || !cache || !slot_frame) return MLA_ERR_NULL;
@@ -353,6 +356,7 @@ MLA_API mla_status mla_cache_write(const mla_shape* shape, const void* x, const 
     return MLA_ERR_RANGE;
   const int64_t rows = (int64_t)shape->batch * n_frames * tokens_per_frame(shape);
   if (rows > INT32_MAX / 2) return MLA_ERR_SHAPE;
+  if (!run) return MLA_OK;
   mla::CacheWriteParams p;
   p.x = x;
   p.w_dkv = w_dkv;
@@ -370,6 +374,12 @@ MLA_API mla_status mla_cache_write(const mla_shape* shape, const void* x, const 
   p.n_frames = n_frames;
   p.batch = shape->batch;
   return from_hip(mla::launch_cache_write(shape->dtype, shape->d_c, shape->d_rope, p, (hipStream_t)stream));
+}
+
+MLA_API mla_status mla_cache_write(const mla_shape* shape, const void* x, const void* w_dkv, const void* w_kr,
+                                   int32_t frame_first, int32_t n_frames, void* cache, int32_t* slot_frame,
+                                   void* stream) {
+  return cache_write_impl(shape, x, w_dkv, w_kr, frame_first, n_frames, cache, slot_frame, stream, true);
 }
 
 MLA_API mla_status mla_absorb_q(const mla_shape* shape, const void* q_nope, const void* q_r, int32_t q_frame_first,
@@ -435,7 +445,7 @@ static mla_status chunk_attend_impl(const mla_shape* shape, const void* q_nope, 
                                     int32_t q_frame_first, int32_t q_n_frames, const void* w_uk, const void* w_uv,
                                     const void* cache, const int32_t* slot_frame, const float* rope_tables,
                                     int32_t rope_t_first, int32_t rope_n_t, void* out, void* workspace,
-                                    size_t workspace_bytes, void* stream, bool frame_causal) {
+                                    size_t workspace_bytes, void* stream, bool frame_causal, bool run = true) {
   mla_status st = check_shape(shape);
   if (st != MLA_OK) return st;
   if (!q_nope || !q_r || !w_uk || !w_uv || !cache || !slot_frame || !out || !workspace) return MLA_ERR_NULL;
@@ -448,6 +458,7 @@ static mla_status chunk_attend_impl(const mla_shape* shape, const void* q_nope, 
     return MLA_ERR_RANGE;
   if (!flash_plan_ok(flash_plan(shape, q_n_frames, 0))) return MLA_ERR_SHAPE;
   if (workspace_bytes < mla_chunk_attend_workspace_bytes(shape, q_n_frames)) return MLA_ERR_WORKSPACE;
+  if (!run) return MLA_OK;
   const size_t rows = (size_t)shape->batch * q_n_frames * tokens_per_frame(shape) * shape->n_heads;
   char* ws = (char*)workspace;
   void* q_abs = ws;
@@ -566,12 +577,16 @@ namespace {
 
 constexpr int kMaxQueryLatent = 1 << 16;
 
+// work-group tiles of a projection (at most 64 x 64 outputs each) are counted in 32 bits
+mla_status check_gemm_tiles(int64_t M, int64_t N) {
+  return ((M + 63) / 64) * ((N + 63) / 64) > (INT64_C(1) << 30) ? MLA_ERR_SHAPE : MLA_OK;
+}
+
 // C = A B^T with the output features split in two parts (n >= n_split: weight
 // b2, output c2); n_split = N for a single part.
 mla_status gemm(const mla_shape* s, const void* a, const void* b, const void* b2, void* c, void* c2, int64_t M,
                 int N, int n_split, int K, hipStream_t st) {
-  // work-group tiles (at most 64 x 64 outputs each) are counted in 32 bits
-  if (((M + 63) / 64) * ((N + 63) / 64) > (INT64_C(1) << 30)) return MLA_ERR_SHAPE;
+  if (check_gemm_tiles(M, N) != MLA_OK) return MLA_ERR_SHAPE;
   mla::GemmParams p{};
   p.a = a;
   p.b = b;
@@ -598,9 +613,9 @@ mla_status check_projection_rows(const mla_shape* s, int n_frames, int64_t* rows
 
 }  // namespace
 
-MLA_API mla_status mla_query_project(const mla_shape* shape, int32_t d_cq, const void* x, int32_t n_frames,
+static mla_status query_project_impl(const mla_shape* shape, int32_t d_cq, const void* x, int32_t n_frames,
                                      const void* w_dq, const void* w_uq, const void* w_qr, void* c_q, void* q_nope,
-                                     void* q_r, void* stream) {
+                                     void* q_r, void* stream, bool run) {
   mla_status st = check_shape(shape);
   if (st != MLA_OK) return st;
   if (!x || !w_dq || !w_uq || !w_qr || !c_q || !q_nope || !q_r) return MLA_ERR_NULL;
@@ -612,15 +627,25 @@ MLA_API mla_status mla_query_project(const mla_shape* shape, int32_t d_cq, const
     return MLA_ERR_SHAPE;
   int64_t rows = 0;
   if ((st = check_projection_rows(shape, n_frames, &rows)) != MLA_OK) return st;
+  const int n_nope = shape->n_heads * shape->d_head;
+  if ((st = check_gemm_tiles(rows, d_cq)) != MLA_OK ||
+      (st = check_gemm_tiles(rows, n_nope + shape->n_heads * shape->d_rope)) != MLA_OK)
+    return st;
+  if (!run) return MLA_OK;
   hipStream_t s = (hipStream_t)stream;
   if ((st = gemm(shape, x, w_dq, nullptr, c_q, nullptr, rows, d_cq, d_cq, shape->hidden, s)) != MLA_OK) return st;
   // content and positional queries in one product over the same query latent
-  const int n_nope = shape->n_heads * shape->d_head;
   return gemm(shape, c_q, w_uq, w_qr, q_nope, q_r, rows, n_nope + shape->n_heads * shape->d_rope, n_nope, d_cq, s);
 }
 
-MLA_API mla_status mla_output_project(const mla_shape* shape, const void* o, int32_t n_frames, const void* w_o,
-                                      void* u, void* stream) {
+MLA_API mla_status mla_query_project(const mla_shape* shape, int32_t d_cq, const void* x, int32_t n_frames,
+                                     const void* w_dq, const void* w_uq, const void* w_qr, void* c_q, void* q_nope,
+                                     void* q_r, void* stream) {
+  return query_project_impl(shape, d_cq, x, n_frames, w_dq, w_uq, w_qr, c_q, q_nope, q_r, stream, true);
+}
+
+static mla_status output_project_impl(const mla_shape* shape, const void* o, int32_t n_frames, const void* w_o,
+                                      void* u, void* stream, bool run) {
   mla_status st = check_shape(shape);
   if (st != MLA_OK) return st;
   if (!o || !w_o || !u) return MLA_ERR_NULL;
@@ -628,6 +653,81 @@ MLA_API mla_status mla_output_project(const mla_shape* shape, const void* o, int
   if ((int64_t)shape->n_heads * shape->d_head > kMaxQueryLatent) return MLA_ERR_SHAPE;
   int64_t rows = 0;
   if ((st = check_projection_rows(shape, n_frames, &rows)) != MLA_OK) return st;
+  if ((st = check_gemm_tiles(rows, shape->hidden)) != MLA_OK) return st;
+  if (!run) return MLA_OK;
   return gemm(shape, o, w_o, nullptr, u, nullptr, rows, shape->hidden, shape->hidden, shape->n_heads * shape->d_head,
               (hipStream_t)stream);
+}
+
+MLA_API mla_status mla_output_project(const mla_shape* shape, const void* o, int32_t n_frames, const void* w_o,
+                                      void* u, void* stream) {
+  return output_project_impl(shape, o, n_frames, w_o, u, stream, true);
+}
+
+// ---------------------------------------------------------------- whole layer
+namespace {
+
+// Layer-step workspace: query latent, queries, the heads' outputs, then the
+// attention side's own workspace.
+struct LayerWs {
+  size_t c_q, q_nope, q_r, o, attend, total;
+};
+
+LayerWs layer_ws_layout(const mla_shape* s, int d_cq, int n_frames) {
+  const size_t rows = (size_t)s->batch * n_frames * tokens_per_frame(s);
+  const size_t e = elt_size(s);
+  LayerWs w;
+  w.c_q = 0;
+  w.q_nope = w.c_q + round256(rows * d_cq * e);
+  w.q_r = w.q_nope + round256(rows * s->n_heads * s->d_head * e);
+  w.o = w.q_r + round256(rows * s->n_heads * s->d_rope * e);
+  w.attend = w.o + round256(rows * s->n_heads * s->d_head * e);
+  w.total = w.attend + mla_chunk_attend_workspace_bytes(s, n_frames);
+  return w;
+}
+
+}  // namespace
+
+MLA_API size_t mla_layer_step_workspace_bytes(const mla_shape* shape, int32_t d_cq, int32_t n_frames) {
+  if (check_shape(shape) != MLA_OK || check_query_args(shape, 0, n_frames) != MLA_OK || d_cq < 8 || d_cq % 8 != 0 ||
+      d_cq > kMaxQueryLatent || mla_chunk_attend_workspace_bytes(shape, n_frames) == 0)
+    return 0;
+  return layer_ws_layout(shape, d_cq, n_frames).total;
+}
+
+MLA_API mla_status mla_layer_step(const mla_shape* shape, int32_t d_cq, const mla_layer_weights* weights,
+                                  const void* x, int32_t frame_first, int32_t n_frames, void* cache,
+                                  int32_t* slot_frame, const float* rope_tables, int32_t rope_t_first,
+                                  int32_t rope_n_t, int32_t frame_causal, void* u, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!weights || !workspace) return MLA_ERR_NULL;
+  if (!aligned16(workspace)) return MLA_ERR_ALIGN;
+  if (d_cq < 8 || d_cq % 8 != 0 || d_cq > kMaxQueryLatent) return MLA_ERR_SHAPE;
+  if ((st = check_query_args(shape, frame_first, n_frames)) != MLA_OK) return st;
+  const size_t need = mla_layer_step_workspace_bytes(shape, d_cq, n_frames);
+  if (need == 0) return MLA_ERR_SHAPE;
+  if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  const LayerWs w = layer_ws_layout(shape, d_cq, n_frames);
+  char* ws = (char*)workspace;
+  void *c_q = ws + w.c_q, *q_nope = ws + w.q_nope, *q_r = ws + w.q_r, *o = ws + w.o;
+  const bool causal = frame_causal != 0;
+  const mla_layer_weights& W = *weights;
+  // every part is validated before the first launch
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool run = pass == 1;
+    if ((st = query_project_impl(shape, d_cq, x, n_frames, W.w_dq, W.w_uq, W.w_qr, c_q, q_nope, q_r, stream, run)) !=
+        MLA_OK)
+      return st;
+    if ((st = cache_write_impl(shape, x, W.w_dkv, W.w_kr, frame_first, n_frames, cache, slot_frame, stream, run)) !=
+        MLA_OK)
+      return st;
+    if ((st = chunk_attend_impl(shape, q_nope, q_r, frame_first, n_frames, W.w_uk, W.w_uv, cache, slot_frame,
+                                rope_tables, rope_t_first, rope_n_t, o, ws + w.attend, w.total - w.attend, stream,
+                                causal, run)) != MLA_OK)
+      return st;
+    if ((st = output_project_impl(shape, o, n_frames, W.w_o, u, stream, run)) != MLA_OK) return st;
+  }
+  return MLA_OK;
 }

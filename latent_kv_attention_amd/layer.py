@@ -39,6 +39,7 @@ class LatentLayer:
                                      device=device)
         self.heads_workspace = None  # allocated on the first per-head call
         self.q_buffers = None        # query latent and queries, allocated on the first projection
+        self.layer_workspace = None  # (d_cq, workspace, weight struct) of step(), allocated on its first call
 
     def write(self, x, frame_first: int, n_frames: int, stream=None) -> None:
         """Cache write of frames frame_first .. +n_frames (x [B][n_frames*T][hidden])."""
@@ -120,10 +121,33 @@ class LatentLayer:
         _lib.output_project(self.shape, o, n_frames, self.w["w_o"], out, stream)
         return out
 
-    def step(self, x, frame_first: int, n_frames: int, frame_causal: bool = False, stream=None):
-        """The whole layer for one chunk: queries from the chunk's tokens, the
-        cache write of the same tokens, the attention over the window, and the
-        output projection -> u [B][n_frames*T][hidden]."""
+    def step(self, x, frame_first: int, n_frames: int, frame_causal: bool = False, out=None, stream=None):
+        """The whole layer for one chunk in one library call (mla_layer_step):
+        queries from the chunk's tokens, the cache write of the same tokens,
+        the attention over the window, and the output projection
+        -> u [B][n_frames*T][hidden]. Needs all eight weights."""
+        if n_frames > self.max_chunk_frames:
+            raise ValueError("chunk larger than the workspace was sized for")
+        for k in ("w_dq", "w_uq", "w_qr", "w_o"):
+            if k not in self.w:
+                raise ValueError(f"the layer step needs {k}")
+        d_cq = self.w["w_dq"].shape[0]
+        if self.layer_workspace is None or self.layer_workspace[0] != d_cq:
+            n = _lib.layer_step_workspace_bytes(self.shape, d_cq, self.max_chunk_frames)
+            if n == 0:
+                raise ValueError("the layer step does not support this shape")
+            self.layer_workspace = (d_cq, torch.empty(n, dtype=torch.uint8, device=self.device),
+                                    _lib.layer_weights_struct(self.w))
+        if out is None:
+            out = torch.empty(self.B, n_frames * self.T, self.cfg.hidden, dtype=self.dtype, device=self.device)
+        _lib.layer_step(self.shape, d_cq, self.layer_workspace[2], x, frame_first, n_frames, self.cache,
+                        self.slot_frame, self.tables, self.rope_t_first, self.rope_n_t, frame_causal, out,
+                        self.layer_workspace[1], stream)
+        return out
+
+    def step_composed(self, x, frame_first: int, n_frames: int, frame_causal: bool = False, stream=None):
+        """step() as four separate library calls (mla_query_project,
+        mla_cache_write, mla_chunk_attend[_frame_causal], mla_output_project)."""
         _, q_nope, q_r = self.project_queries(x, n_frames, stream)
         self.write(x, frame_first, n_frames, stream)
         attend = self.attend_frame_causal if frame_causal else self.attend

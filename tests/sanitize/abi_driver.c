@@ -159,6 +159,25 @@ int main(void) {
   }
   EXPECT(mla_output_project(&s, p, 3, p, p, NULL), MLA_ERR_HIP);
 
+  /* whole layer */
+  {
+    mla_layer_weights lw = {p, p, p, p, p, p, p, p};
+    const size_t need = mla_layer_step_workspace_bytes(&s, 576, 3);
+    EXPECT(need > mla_chunk_attend_workspace_bytes(&s, 3), 1);
+    EXPECT(mla_layer_step_workspace_bytes(&s, 572, 3), 0);
+    EXPECT(mla_layer_step_workspace_bytes(&s, 576, 0), 0);
+    EXPECT(mla_layer_step(&s, 576, NULL, p, 18, 3, p, sf, tab, 0, 21, 0, p, p, need, NULL), MLA_ERR_NULL);
+    EXPECT(mla_layer_step(&s, 576, &lw, p, 18, 3, p, sf, tab, 0, 21, 0, p, p, need - 1, NULL), MLA_ERR_WORKSPACE);
+    EXPECT(mla_layer_step(&s, 576, &lw, p, 18, 22, p, sf, tab, 0, 40, 0, p, p, big, NULL), MLA_ERR_RANGE);
+    EXPECT(mla_layer_step(&s, 576, &lw, p, 18, 3, p, sf, tab, 19, 21, 0, p, p, need, NULL), MLA_ERR_RANGE);
+    lw.w_o = NULL;
+    EXPECT(mla_layer_step(&s, 576, &lw, p, 18, 3, p, sf, tab, 0, 21, 0, p, p, need, NULL), MLA_ERR_NULL);
+    lw.w_o = odd;
+    EXPECT(mla_layer_step(&s, 576, &lw, p, 18, 3, p, sf, tab, 0, 21, 1, p, p, need, NULL), MLA_ERR_ALIGN);
+    lw.w_o = p;
+    EXPECT(mla_layer_step(&s, 576, &lw, p, 18, 3, p, sf, tab, 0, 21, 1, p, p, need, NULL), MLA_ERR_HIP);
+  }
+
   printf("%s: %d unexpected statuses\n", failures ? "FAILED" : "ok", failures);
   return failures != 0;
 }

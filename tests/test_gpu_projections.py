@@ -146,3 +146,27 @@ def test_layer_step(name):
 def test_layer_step_frame_causal():
     cfg = get_config("wan_small").with_(chunk_frames=2, window_frames=4)
     _layer_steps(cfg, 56, 3, frame_causal=True)
+
+
+@pytest.mark.parametrize("name", ["wan_small", "wan_small_f32"])
+@pytest.mark.parametrize("frame_causal", [False, True])
+def test_layer_step_single_call_equals_composed_calls(name, frame_causal):
+    """mla_layer_step runs the same kernels as mla_query_project,
+    mla_cache_write, mla_chunk_attend[_frame_causal] and mla_output_project
+    called one by one: the outputs, caches and slot tables are bit-identical,
+    chunk after chunk through ring wrap, with three streams."""
+    cfg = get_config(name).with_(window_frames=4, chunk_frames=2)
+    w, wd = _weights(cfg, 57)
+    one = LatentLayer(cfg, wd, batch=3, rope_n_t=16)
+    four = LatentLayer(cfg, wd, batch=3, rope_n_t=16)
+    streams = [Stream(cfg, seed=57, stream=b) for b in range(3)]
+    view = (lambda t: t.view(torch.int16)) if cfg.dtype == "bf16" else (lambda t: t.view(torch.int32))
+    for k in range(4):
+        f0 = 2 * k
+        x = to_torch(np.stack([s_.xs(f0, 2) for s_ in streams]), cfg.dtype)
+        u1 = one.step(x, f0, 2, frame_causal=frame_causal)
+        u4 = four.step_composed(x, f0, 2, frame_causal=frame_causal)
+        torch.cuda.synchronize()
+        assert torch.isfinite(u1.float()).all()
+        assert torch.equal(view(u1), view(u4)), f"chunk {k}"
+        assert torch.equal(view(one.cache), view(four.cache)) and torch.equal(one.slot_frame, four.slot_frame)
