@@ -356,10 +356,25 @@ def projections_report(cfg, args):
     x2, o2 = x.view(cfg.n_q, cfg.hidden), o.view(cfg.n_q, cfg.n_heads * cfg.d_head)
     w_q = torch.cat([w["w_uq"].reshape(-1, cfg.q_latent), w["w_qr"].reshape(-1, cfg.q_latent)]).contiguous()
     lin = torch.nn.functional.linear
+    # the fused query path (absorbed weights) on a second layer of the same weights and window
+    fused = LatentLayer(cfg, w, batch=1, rope_n_t=64)
+    fused.cache.copy_(layer.cache)
+    fused.slot_frame.copy_(layer.slot_frame)
+    fused.absorb_query_weights()
+    Q = mla.qabs_dim(layer.shape)
+    q_abs = torch.empty(1, cfg.n_q, cfg.n_heads, Q, dtype=torch.bfloat16, device=dev)
+
+    def unfused_query_to_qabs():
+        _, qn, qr = layer.project_queries(x, cfg.chunk_frames)
+        mla.absorb_q(layer.shape, qn, qr, chunk_first, cfg.chunk_frames, w["w_uk"], layer.tables, 0, 64, q_abs)
+
     calls = {
         "query_project": lambda: layer.project_queries(x, cfg.chunk_frames),
+        "query_to_qabs_unfused": unfused_query_to_qabs,
+        "query_project_absorbed": lambda: fused.project_queries_absorbed(x, chunk_first, cfg.chunk_frames),
         "output_project": lambda: layer.project_output(o, cfg.chunk_frames, out=u),
         "layer_step": lambda: layer.step(x, chunk_first, cfg.chunk_frames),
+        "layer_step_fused": lambda: fused.step(x, chunk_first, cfg.chunk_frames),
         "library_query": lambda: lin(lin(x2, w["w_dq"]), w_q),
         "library_output": lambda: lin(o2, w["w_o"]),
     }
@@ -393,6 +408,11 @@ def projections_report(cfg, args):
         "library_gemm_query_ms": round(ms["library_query"], 4),
         "library_gemm_output_ms": round(ms["library_output"], 4),
         "layer_step_ms": round(ms["layer_step"], 4),
+        "query_to_qabs_unfused_ms": round(ms["query_to_qabs_unfused"], 4),
+        "query_project_absorbed_ms": round(ms["query_project_absorbed"], 4),
+        "query_project_absorbed_TFLOPs": round(tf(2.0 * M * cfg.q_latent * (cfg.hidden + H * Q),
+                                                  ms["query_project_absorbed"]), 1),
+        "layer_step_fused_ms": round(ms["layer_step_fused"], 4),
         "projections_share_of_layer": round((ms["query_project"] + ms["output_project"]) / ms["layer_step"], 4),
         "finite": bool(torch.isfinite(u.float()).all()),
         "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic"}), flush=True)

@@ -277,6 +277,35 @@ mla_status mla_query_project(const mla_shape* shape, int32_t d_cq, const void* x
                              const void* w_dq, const void* w_uq, const void* w_qr, void* c_q, void* q_nope,
                              void* q_r, void* stream);
 
+/* ---------------------------------------------------------------- absorbed query path
+ * The query path with the key up-projection folded in (the re-association
+ * of the hyper.ai summary's content score, applied to the query path as
+ * well): W_uk[h]^T q_nope[h] = (W_uk[h]^T W_uq[h]) c_q, so one product of
+ * the query latent with per-head absorbed weights gives the attention's
+ * query directly.
+ * mla_query_absorb_weights (once per layer, when the weights change):
+ *   w_qabs[h][j][:] = (W_uk[h]^T W_uq[h])[j][:]  for j < d_c   (fp32 sums, rounded to dtype)
+ *                   = W_qr[h][j - d_c][:]        for d_c <= j < d_c + d_rope
+ *                   = 0                          up to Q = mla_qabs_dim
+ *   w_uq (device) [H][d_head][d_cq], w_qr [H][d_rope][d_cq], w_uk [H][d_head][d_c],
+ *   w_qabs (device) [H][Q][d_cq] output.
+ * mla_query_project_absorbed: c_q = W_dq x (rounded), then
+ *   q_abs[r][h] = g [ (w_qabs c_q)[h][0..d_c) | R(t, y, x) (w_qabs c_q)[h][d_c..) | 0 ]
+ * with g = softmax scale * log2(e) and (t, y, x) the position of token r
+ * (frame q_frame_first + r / T within its stream), rounded once: the input
+ * of mla_flash_attend, equal to mla_query_project + mla_absorb_q up to
+ * rounding.
+ *   x (device) [B][n_frames * T][hidden]; w_dq [d_cq][hidden];
+ *   rope_tables as for mla_absorb_q (must cover the query frames);
+ *   c_q (device) [B][n_frames * T][d_cq] output; q_abs (device)
+ *   [B][n_frames * T][H][Q] output. */
+mla_status mla_query_absorb_weights(const mla_shape* shape, int32_t d_cq, const void* w_uq, const void* w_qr,
+                                    const void* w_uk, void* w_qabs, void* stream);
+mla_status mla_query_project_absorbed(const mla_shape* shape, int32_t d_cq, const void* x, int32_t q_frame_first,
+                                      int32_t n_frames, const void* w_dq, const void* w_qabs,
+                                      const float* rope_tables, int32_t rope_t_first, int32_t rope_n_t, void* c_q,
+                                      void* q_abs, void* stream);
+
 /* ---------------------------------------------------------------- output projection
  * u[r] = W_o [o[r][0]; ...; o[r][H-1]]: the concatenated heads projected back
  * to the token width (the output projection of multi-head attention; the
@@ -312,6 +341,9 @@ typedef struct mla_layer_weights {
   const void* w_uk;  /* [H][d_head][d_c] */
   const void* w_uv;  /* [H][d_head][d_c] */
   const void* w_o;   /* [hidden][H * d_head] */
+  const void* w_qabs; /* optional, [H][Q][d_cq] from mla_query_absorb_weights: when set,
+                         the queries go through mla_query_project_absorbed (w_uq, w_qr,
+                         w_uk are then not read) */
 } mla_layer_weights;
 
 size_t mla_layer_step_workspace_bytes(const mla_shape* shape, int32_t d_cq, int32_t n_frames);

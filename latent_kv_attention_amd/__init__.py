@@ -10,5 +10,5 @@ from ._lib import (  # noqa: F401
     rope3d_table_floats, rope3d_tables, cache_write, absorb_q, flash_workspace_bytes, flash_attend,
     up_v, chunk_attend_workspace_bytes, chunk_attend, chunk_attend_heads_workspace_bytes, chunk_attend_heads,
     chunk_attend_frame_causal, query_project, output_project, MlaLayerWeights, layer_weights_struct,
-    layer_step_workspace_bytes, layer_step,
+    layer_step_workspace_bytes, layer_step, query_absorb_weights, query_project_absorbed,
 )

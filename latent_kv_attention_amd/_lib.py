@@ -28,6 +28,7 @@ EXPORTS = [
     "mla_chunk_attend_workspace_bytes", "mla_chunk_attend",
     "mla_chunk_attend_heads_workspace_bytes", "mla_chunk_attend_heads", "mla_chunk_attend_frame_causal",
     "mla_query_project", "mla_output_project", "mla_layer_step_workspace_bytes", "mla_layer_step",
+    "mla_query_absorb_weights", "mla_query_project_absorbed",
 ]
 
 
@@ -39,7 +40,8 @@ class MlaShape(ctypes.Structure):
 
 
 class MlaLayerWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("w_dkv", "w_kr", "w_dq", "w_uq", "w_qr", "w_uk", "w_uv", "w_o")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_dkv", "w_kr", "w_dq", "w_uq", "w_qr", "w_uk", "w_uv", "w_o",
+                                                "w_qabs")]
 
 
 class MlaError(RuntimeError):
@@ -75,6 +77,8 @@ _SIGS = {
     "mla_query_project": (_I, [_SP, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P]),
     "mla_output_project": (_I, [_SP, _P, _I, _P, _P, _P]),
     "mla_layer_step_workspace_bytes": (_SZ, [_SP, _I, _I]),
+    "mla_query_absorb_weights": (_I, [_SP, _I, _P, _P, _P, _P, _P]),
+    "mla_query_project_absorbed": (_I, [_SP, _I, _P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P]),
     "mla_layer_step": (_I, [_SP, _I, ctypes.POINTER(MlaLayerWeights), _P, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P,
                             _SZ, _P]),
 }
@@ -225,8 +229,10 @@ def output_project(shape: MlaShape, o, n_frames: int, w_o, u, stream=None) -> No
 
 
 def layer_weights_struct(w: dict) -> MlaLayerWeights:
-    """The eight weight tensors of a layer (dict of device tensors) as the ABI's struct."""
-    return MlaLayerWeights(*[w[k].data_ptr() for k in ("w_dkv", "w_kr", "w_dq", "w_uq", "w_qr", "w_uk", "w_uv", "w_o")])
+    """A layer's weight tensors (dict of device tensors) as the ABI's struct;
+    w_qabs is optional (absent: the unfused query path)."""
+    names = ("w_dkv", "w_kr", "w_dq", "w_uq", "w_qr", "w_uk", "w_uv", "w_o", "w_qabs")
+    return MlaLayerWeights(*[w[k].data_ptr() if w.get(k) is not None else None for k in names])
 
 
 def layer_step_workspace_bytes(shape: MlaShape, d_cq: int, n_frames: int) -> int:
@@ -241,3 +247,17 @@ def layer_step(shape: MlaShape, d_cq: int, weights: MlaLayerWeights, x, frame_fi
            lib().mla_layer_step(ctypes.byref(shape), d_cq, ctypes.byref(weights), _ptr(x), frame_first, n_frames,
                                 _ptr(cache), _ptr(slot_frame), _ptr(tables), rope_t_first, rope_n_t,
                                 1 if frame_causal else 0, _ptr(u), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def query_absorb_weights(shape: MlaShape, d_cq: int, w_uq, w_qr, w_uk, w_qabs, stream=None) -> None:
+    _check("mla_query_absorb_weights",
+           lib().mla_query_absorb_weights(ctypes.byref(shape), d_cq, _ptr(w_uq), _ptr(w_qr), _ptr(w_uk), _ptr(w_qabs),
+                                          _stream(stream)))
+
+
+def query_project_absorbed(shape: MlaShape, d_cq: int, x, q_frame_first: int, n_frames: int, w_dq, w_qabs, tables,
+                           rope_t_first: int, rope_n_t: int, c_q, q_abs, stream=None) -> None:
+    _check("mla_query_project_absorbed",
+           lib().mla_query_project_absorbed(ctypes.byref(shape), d_cq, _ptr(x), q_frame_first, n_frames, _ptr(w_dq),
+                                            _ptr(w_qabs), _ptr(tables), rope_t_first, rope_n_t, _ptr(c_q),
+                                            _ptr(q_abs), _stream(stream)))

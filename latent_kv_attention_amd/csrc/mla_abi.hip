@@ -441,6 +441,42 @@ MLA_API size_t mla_chunk_attend_workspace_bytes(const mla_shape* shape, int32_t 
          flash_ws_bytes(shape, q_n_frames, 0);
 }
 
+// Attention over the window from absorbed queries (mla_flash_attend with the
+// automatic split, then mla_up_v); workspace = [o_lat | flash workspace].
+static size_t attend_absorbed_ws_bytes(const mla_shape* shape, int32_t q_n_frames) {
+  const size_t rows = (size_t)shape->batch * q_n_frames * tokens_per_frame(shape) * shape->n_heads;
+  return round256(rows * shape->d_c * elt_size(shape)) + flash_ws_bytes(shape, q_n_frames, 0);
+}
+
+static mla_status attend_absorbed_impl(const mla_shape* shape, const void* q_abs, int32_t q_frame_first,
+                                       int32_t q_n_frames, const void* w_uv, const void* cache,
+                                       const int32_t* slot_frame, const float* rope_tables, int32_t rope_t_first,
+                                       int32_t rope_n_t, void* out, void* workspace, size_t workspace_bytes,
+                                       void* stream, bool frame_causal, bool run) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!q_abs || !w_uv || !cache || !slot_frame || !out || !workspace) return MLA_ERR_NULL;
+  if (!aligned16(q_abs) || !aligned16(w_uv) || !aligned16(cache) || !aligned16(slot_frame) || !aligned16(out) ||
+      !aligned16(workspace))
+    return MLA_ERR_ALIGN;
+  if ((st = check_tables(shape, rope_tables, rope_t_first, rope_n_t)) != MLA_OK) return st;
+  if ((st = check_query_args(shape, q_frame_first, q_n_frames)) != MLA_OK) return st;
+  if (q_frame_first < rope_t_first || (int64_t)q_frame_first + q_n_frames > (int64_t)rope_t_first + rope_n_t)
+    return MLA_ERR_RANGE;
+  if (!flash_plan_ok(flash_plan(shape, q_n_frames, 0))) return MLA_ERR_SHAPE;
+  if (workspace_bytes < attend_absorbed_ws_bytes(shape, q_n_frames)) return MLA_ERR_WORKSPACE;
+  if (!run) return MLA_OK;
+  const size_t rows = (size_t)shape->batch * q_n_frames * tokens_per_frame(shape) * shape->n_heads;
+  char* ws = (char*)workspace;
+  void* o_lat = ws;
+  ws += round256(rows * shape->d_c * elt_size(shape));
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = do_flash(shape, q_abs, q_n_frames, cache, slot_frame, rope_tables, rope_t_first, rope_n_t, o_lat, 0,
+                     ws, s, frame_causal, q_frame_first)) != MLA_OK)
+    return st;
+  return do_up_v(shape, o_lat, q_n_frames, w_uv, out, s);
+}
+
 static mla_status chunk_attend_impl(const mla_shape* shape, const void* q_nope, const void* q_r,
                                     int32_t q_frame_first, int32_t q_n_frames, const void* w_uk, const void* w_uv,
                                     const void* cache, const int32_t* slot_frame, const float* rope_tables,
@@ -458,21 +494,21 @@ static mla_status chunk_attend_impl(const mla_shape* shape, const void* q_nope, 
     return MLA_ERR_RANGE;
   if (!flash_plan_ok(flash_plan(shape, q_n_frames, 0))) return MLA_ERR_SHAPE;
   if (workspace_bytes < mla_chunk_attend_workspace_bytes(shape, q_n_frames)) return MLA_ERR_WORKSPACE;
-  if (!run) return MLA_OK;
+  // workspace = [q_abs | o_lat | flash workspace]
   const size_t rows = (size_t)shape->batch * q_n_frames * tokens_per_frame(shape) * shape->n_heads;
+  const size_t qabs_bytes = round256(rows * qabs_dim(shape) * elt_size(shape));
   char* ws = (char*)workspace;
-  void* q_abs = ws;
-  ws += round256(rows * qabs_dim(shape) * elt_size(shape));
-  void* o_lat = ws;
-  ws += round256(rows * shape->d_c * elt_size(shape));
-  hipStream_t s = (hipStream_t)stream;
-  if ((st = do_absorb(shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk, rope_tables, rope_t_first, rope_n_t,
-                      q_abs, s)) != MLA_OK)
+  if ((st = attend_absorbed_impl(shape, ws, q_frame_first, q_n_frames, w_uv, cache, slot_frame, rope_tables,
+                                 rope_t_first, rope_n_t, out, ws + qabs_bytes, workspace_bytes - qabs_bytes, stream,
+                                 frame_causal, false)) != MLA_OK)
     return st;
-  if ((st = do_flash(shape, q_abs, q_n_frames, cache, slot_frame, rope_tables, rope_t_first, rope_n_t, o_lat, 0,
-                     ws, s, frame_causal, q_frame_first)) != MLA_OK)
+  if (!run) return MLA_OK;
+  if ((st = do_absorb(shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk, rope_tables, rope_t_first, rope_n_t, ws,
+                      (hipStream_t)stream)) != MLA_OK)
     return st;
-  return do_up_v(shape, o_lat, q_n_frames, w_uv, out, s);
+  return attend_absorbed_impl(shape, ws, q_frame_first, q_n_frames, w_uv, cache, slot_frame, rope_tables,
+                              rope_t_first, rope_n_t, out, ws + qabs_bytes, workspace_bytes - qabs_bytes, stream,
+                              frame_causal, true);
 }
 
 MLA_API mla_status mla_chunk_attend(const mla_shape* shape, const void* q_nope, const void* q_r, int32_t q_frame_first,
@@ -664,6 +700,84 @@ MLA_API mla_status mla_output_project(const mla_shape* shape, const void* o, int
   return output_project_impl(shape, o, n_frames, w_o, u, stream, true);
 }
 
+// ---------------------------------------------------------------- absorbed query path
+MLA_API mla_status mla_query_absorb_weights(const mla_shape* shape, int32_t d_cq, const void* w_uq, const void* w_qr,
+                                            const void* w_uk, void* w_qabs, void* stream) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!w_uq || !w_qr || !w_uk || !w_qabs) return MLA_ERR_NULL;
+  if (!aligned16(w_uq) || !aligned16(w_qr) || !aligned16(w_uk) || !aligned16(w_qabs)) return MLA_ERR_ALIGN;
+  if (d_cq < 8 || d_cq % 8 != 0 || d_cq > kMaxQueryLatent || shape->d_rope % 8 != 0) return MLA_ERR_SHAPE;
+  if ((int64_t)shape->n_heads * qabs_dim(shape) > kMaxQueryLatent) return MLA_ERR_SHAPE;
+  mla::QabsWeightParams p;
+  p.w_uq = w_uq;
+  p.w_qr = w_qr;
+  p.w_uk = w_uk;
+  p.w_qabs = w_qabs;
+  p.H = shape->n_heads;
+  p.d_head = shape->d_head;
+  p.dc = shape->d_c;
+  p.dr = shape->d_rope;
+  p.kp = qabs_dim(shape);
+  p.d_cq = d_cq;
+  return from_hip(mla::launch_qabs_weights(shape->dtype, p, (hipStream_t)stream));
+}
+
+static mla_status query_project_absorbed_impl(const mla_shape* shape, int32_t d_cq, const void* x,
+                                              int32_t q_frame_first, int32_t n_frames, const void* w_dq,
+                                              const void* w_qabs, const float* rope_tables, int32_t rope_t_first,
+                                              int32_t rope_n_t, void* c_q, void* q_abs, void* stream, bool run) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!x || !w_dq || !w_qabs || !c_q || !q_abs) return MLA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_dq) || !aligned16(w_qabs) || !aligned16(c_q) || !aligned16(q_abs))
+    return MLA_ERR_ALIGN;
+  if (d_cq < 8 || d_cq % 8 != 0 || d_cq > kMaxQueryLatent || shape->d_rope % 8 != 0) return MLA_ERR_SHAPE;
+  const int n_abs = shape->n_heads * qabs_dim(shape);
+  if ((int64_t)shape->n_heads * qabs_dim(shape) > kMaxQueryLatent) return MLA_ERR_SHAPE;
+  if ((st = check_tables(shape, rope_tables, rope_t_first, rope_n_t)) != MLA_OK) return st;
+  if ((st = check_query_args(shape, q_frame_first, n_frames)) != MLA_OK) return st;
+  if (q_frame_first < rope_t_first || (int64_t)q_frame_first + n_frames > (int64_t)rope_t_first + rope_n_t)
+    return MLA_ERR_RANGE;
+  int64_t rows = 0;
+  if ((st = check_projection_rows(shape, n_frames, &rows)) != MLA_OK) return st;
+  if ((st = check_gemm_tiles(rows, d_cq)) != MLA_OK || (st = check_gemm_tiles(rows, n_abs)) != MLA_OK) return st;
+  if (!run) return MLA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = gemm(shape, x, w_dq, nullptr, c_q, nullptr, rows, d_cq, d_cq, shape->hidden, s)) != MLA_OK) return st;
+  mla::GemmParams p{};
+  p.a = c_q;
+  p.b = w_qabs;
+  p.c = q_abs;
+  p.M = (int)rows;
+  p.N = n_abs;
+  p.K = d_cq;
+  p.lda = d_cq;
+  p.ldb = d_cq;
+  p.ldc = n_abs;
+  p.ldc2 = 0;
+  p.n_split = n_abs;
+  p.qa.tables = rope_tables;
+  p.qa.rl = rope_layout(shape, rope_t_first, rope_n_t);
+  p.qa.kp = qabs_dim(shape);
+  p.qa.dc = shape->d_c;
+  p.qa.dr = shape->d_rope;
+  p.qa.n_q = (int)(n_frames * tokens_per_frame(shape));
+  p.qa.T = (int)tokens_per_frame(shape);
+  p.qa.grid_x = shape->grid_x;
+  p.qa.q_frame_first = q_frame_first;
+  p.qa.qscale = scale_log2(shape);
+  return from_hip(mla::launch_gemm_qabs(shape->dtype, p, mla::gemm_tile_rows(p.M, p.N, device_cus()), s));
+}
+
+MLA_API mla_status mla_query_project_absorbed(const mla_shape* shape, int32_t d_cq, const void* x,
+                                              int32_t q_frame_first, int32_t n_frames, const void* w_dq,
+                                              const void* w_qabs, const float* rope_tables, int32_t rope_t_first,
+                                              int32_t rope_n_t, void* c_q, void* q_abs, void* stream) {
+  return query_project_absorbed_impl(shape, d_cq, x, q_frame_first, n_frames, w_dq, w_qabs, rope_tables,
+                                     rope_t_first, rope_n_t, c_q, q_abs, stream, true);
+}
+
 // ---------------------------------------------------------------- whole layer
 namespace {
 
@@ -714,6 +828,30 @@ MLA_API mla_status mla_layer_step(const mla_shape* shape, int32_t d_cq, const ml
   void *c_q = ws + w.c_q, *q_nope = ws + w.q_nope, *q_r = ws + w.q_r, *o = ws + w.o;
   const bool causal = frame_causal != 0;
   const mla_layer_weights& W = *weights;
+  if (W.w_qabs) {
+    // fused query path: the query latent's product with the absorbed weights
+    // is already the attention's query; workspace = [c_q | q_abs | o | o_lat, flash]
+    const size_t rows = (size_t)shape->batch * n_frames * tokens_per_frame(shape) * shape->n_heads;
+    char* q_abs = ws + w.q_nope;
+    char* o2 = q_abs + round256(rows * qabs_dim(shape) * elt_size(shape));
+    char* att = o2 + round256(rows * shape->d_head * elt_size(shape));
+    if (att > ws + w.total) return MLA_ERR_WORKSPACE;  // cannot happen: the layout is smaller than the unfused one
+    const size_t att_bytes = (size_t)(ws + w.total - att);
+    for (int pass = 0; pass < 2; ++pass) {
+      const bool run = pass == 1;
+      if ((st = query_project_absorbed_impl(shape, d_cq, x, frame_first, n_frames, W.w_dq, W.w_qabs, rope_tables,
+                                            rope_t_first, rope_n_t, c_q, q_abs, stream, run)) != MLA_OK)
+        return st;
+      if ((st = cache_write_impl(shape, x, W.w_dkv, W.w_kr, frame_first, n_frames, cache, slot_frame, stream, run)) !=
+          MLA_OK)
+        return st;
+      if ((st = attend_absorbed_impl(shape, q_abs, frame_first, n_frames, W.w_uv, cache, slot_frame, rope_tables,
+                                     rope_t_first, rope_n_t, o2, att, att_bytes, stream, causal, run)) != MLA_OK)
+        return st;
+      if ((st = output_project_impl(shape, o2, n_frames, W.w_o, u, stream, run)) != MLA_OK) return st;
+    }
+    return MLA_OK;
+  }
   // every part is validated before the first launch
   for (int pass = 0; pass < 2; ++pass) {
     const bool run = pass == 1;

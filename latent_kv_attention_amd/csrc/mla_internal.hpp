@@ -121,6 +121,19 @@ struct HeadsParams {
 // weight row from B2 (row n - n_split) and land in C2 (column n - n_split,
 // row stride ldc2); n_split = N for one part. K, N, n_split and all strides
 // multiples of 8; pointers 16-byte aligned.
+// Epilogue of the absorbed-query product (GemmParams::qabs): the output row of
+// a token is its absorbed queries [H][kp], head h = [dc latent | dr
+// positional | zero pad]; the positional part is rotated by 3D-RoPE at the
+// token's (t, y, x) and every value is multiplied by qscale before the one
+// rounding to the element type.
+struct GemmQabs {
+  const float* tables;
+  RopeLayout rl;
+  int kp, dc, dr;
+  int n_q, T, grid_x, q_frame_first;  // tokens per stream, per frame; frame of token 0
+  float qscale;                       // softmax scale * log2(e)
+};
+
 struct GemmParams {
   const void* a;
   const void* b;
@@ -129,6 +142,17 @@ struct GemmParams {
   void* c2;
   int M, N, K, lda, ldb, ldc, ldc2, n_split;
   int tiles_n, n_logical, per_xcd;  // filled by the launcher
+  GemmQabs qa;                      // used only by the absorbed-query launch
+};
+
+// Absorbed query weight of each head: w_qabs[h][j][:] = (W_uk[h]^T W_uq[h])[j][:]
+// for j < dc, W_qr[h][j - dc][:] for dc <= j < dc + dr, zero up to kp.
+struct QabsWeightParams {
+  const void* w_uq;  // [H][d_head][d_cq]
+  const void* w_qr;  // [H][dr][d_cq]
+  const void* w_uk;  // [H][d_head][dc]
+  void* w_qabs;      // [H][kp][d_cq]
+  int H, d_head, dc, dr, kp, d_cq;
 };
 
 hipError_t launch_rope_tables(const RopeTableParams& p, hipStream_t s);
@@ -148,5 +172,8 @@ hipError_t launch_heads(int d_c, int d_rope, int d_head, const HeadsParams& p, b
 // a problem of M x N outputs on n_cu compute units
 int gemm_tile_rows(int M, int N, int n_cu);
 hipError_t launch_gemm_nt(int dtype, const GemmParams& p, int tile_rows, hipStream_t s);
+// the same product with the absorbed-query epilogue (p.qa)
+hipError_t launch_gemm_qabs(int dtype, const GemmParams& p, int tile_rows, hipStream_t s);
+hipError_t launch_qabs_weights(int dtype, const QabsWeightParams& p, hipStream_t s);
 
 }  // namespace mla

@@ -24,8 +24,17 @@
 // output arrays (features n >= n_split: weight B2 row n - n_split, output
 // C2 column n - n_split), so that the per-head content and positional
 // queries, which read the same query latent, are one launch.
+//
+// Absorbed-query variant (QABS): the weight is the per-head stack
+// [W_uk[h]^T W_uq[h] ; W_qr[h] ; 0] (qabs_weights_kernel), so one product
+// of the query latent gives every head's absorbed content query and
+// unrotated positional query, and the epilogue finishes them the way the
+// attention reads them: the output tile is staged in float, positional
+// pairs are rotated by 3D-RoPE at the row's (t, y, x), everything is scaled
+// by the softmax factor in log2 units, then rounded once.
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
+#include "rope_device.hpp"
 
 namespace mla {
 
@@ -34,7 +43,7 @@ constexpr int kGemmBK = 64;
 constexpr int kGemmXcds = 8;
 }  // namespace
 
-template <typename T, int BM, int BN>
+template <typename T, int BM, int BN, bool QABS>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   typedef typename V8<T>::type v8;
   constexpr int BK = kGemmBK;
@@ -48,6 +57,8 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   constexpr int NMB = WM / 16, NNB = WN / 16;
   static_assert((BM + BN) * CHUNKS % 256 == 0, "whole pieces per thread");
   static_assert(BM * LDC <= 2 * STAGE, "output tile fits in the stage buffers");
+  constexpr int LDF = BN + 4;  // float output staging row stride (QABS)
+  static_assert(!QABS || BM * LDF * 4 <= 2 * STAGE * (int)sizeof(T), "float output tile fits in the stage buffers");
   __shared__ __attribute__((aligned(16))) T lds[2 * STAGE];
 
   const int logical = (blockIdx.x % kGemmXcds) * p.per_xcd + blockIdx.x / kGemmXcds;
@@ -118,6 +129,42 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
     __syncthreads();
   }
 
+  if constexpr (QABS) {
+    float* ft = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ft[(wm * WM + mb * 16 + lg * 4 + i) * LDF + wn * WN + nb * 16 + li] = acc[mb][nb][i];
+    __syncthreads();
+    const GemmQabs& q = p.qa;
+    // 8-column pieces lie inside one region of a head's row (dc, dr, kp are multiples of 8)
+    for (int e = tid; e < BM * (BN / 8); e += 256) {
+      const int r = e / (BN / 8), c8 = (e % (BN / 8)) * 8;
+      const int row = row0 + r, n = col0 + c8;
+      if (row >= p.M || n >= p.N) continue;
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = ft[r * LDF + c8 + j];
+      const int jj = n % q.kp;
+      if (jj >= q.dc && jj < q.dc + q.dr) {
+        const int i = row % q.n_q;
+        const int t = q.q_frame_first + i / q.T, tok = i % q.T;
+        const int y = tok / q.grid_x, x = tok % q.grid_x;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float c, sn;
+          rope_cos_sin(q.rl, q.tables, (jj - q.dc) / 2 + k, t, y, x, c, sn);
+          rotate_pair(f[2 * k], f[2 * k + 1], c, sn);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] *= q.qscale;
+      store8<T>((T*)p.c + (size_t)row * p.ldc + n, pack8<T>(f));
+    }
+    return;
+  }
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -143,21 +190,58 @@ int gemm_tile_rows(int M, int N, int n_cu) {
   return big >= n_cu ? 128 : 64;
 }
 
-template <typename T, int BM, int BN>
+template <typename T, int BM, int BN, bool QABS>
 static hipError_t launch_gemm_t(GemmParams p, hipStream_t s) {
   p.tiles_n = (p.N + BN - 1) / BN;
   p.n_logical = ((p.M + BM - 1) / BM) * p.tiles_n;
   p.per_xcd = (p.n_logical + kGemmXcds - 1) / kGemmXcds;
-  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN>), dim3(p.per_xcd * kGemmXcds), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, QABS>), dim3(p.per_xcd * kGemmXcds), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_nt(int dtype, const GemmParams& p, int tile_rows, hipStream_t s) {
+template <bool QABS>
+static hipError_t launch_gemm_any(int dtype, const GemmParams& p, int tile_rows, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   if (tile_rows == 128)
-    return dtype == 0 ? launch_gemm_t<bf16, 128, 128>(p, s) : launch_gemm_t<float, 128, 128>(p, s);
-  if (tile_rows == 64) return dtype == 0 ? launch_gemm_t<bf16, 64, 64>(p, s) : launch_gemm_t<float, 64, 64>(p, s);
+    return dtype == 0 ? launch_gemm_t<bf16, 128, 128, QABS>(p, s) : launch_gemm_t<float, 128, 128, QABS>(p, s);
+  if (tile_rows == 64)
+    return dtype == 0 ? launch_gemm_t<bf16, 64, 64, QABS>(p, s) : launch_gemm_t<float, 64, 64, QABS>(p, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_nt(int dtype, const GemmParams& p, int tile_rows, hipStream_t s) {
+  return launch_gemm_any<false>(dtype, p, tile_rows, s);
+}
+
+hipError_t launch_gemm_qabs(int dtype, const GemmParams& p, int tile_rows, hipStream_t s) {
+  return launch_gemm_any<true>(dtype, p, tile_rows, s);
+}
+
+// Absorbed query weights, once per layer: one thread per output element,
+// fp32 sums over d_head, rounded once to the element type.
+template <typename T>
+__global__ __launch_bounds__(256) void qabs_weights_kernel(QabsWeightParams p) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int j = blockIdx.y, h = blockIdx.z;
+  if (c >= p.d_cq) return;
+  float v = 0.f;
+  if (j < p.dc) {
+    const T* uk = (const T*)p.w_uk + (size_t)h * p.d_head * p.dc + j;
+    const T* uq = (const T*)p.w_uq + (size_t)h * p.d_head * p.d_cq + c;
+    for (int i = 0; i < p.d_head; ++i) v += to_f<T>(uk[(size_t)i * p.dc]) * to_f<T>(uq[(size_t)i * p.d_cq]);
+  } else if (j < p.dc + p.dr) {
+    v = to_f<T>(((const T*)p.w_qr)[((size_t)h * p.dr + (j - p.dc)) * p.d_cq + c]);
+  }
+  ((T*)p.w_qabs)[((size_t)h * p.kp + j) * p.d_cq + c] = to_t<T>(v);
+}
+
+hipError_t launch_qabs_weights(int dtype, const QabsWeightParams& p, hipStream_t s) {
+  dim3 grid((p.d_cq + 255) / 256, p.kp, p.H);
+  if (dtype == 0)
+    hipLaunchKernelGGL(qabs_weights_kernel<bf16>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(qabs_weights_kernel<float>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace mla

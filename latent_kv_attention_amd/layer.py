@@ -112,6 +112,32 @@ class LatentLayer:
                            q_r, stream)
         return c_q, q_nope, q_r
 
+    def absorb_query_weights(self, stream=None):
+        """Compute the absorbed query weights [H][Q][d_cq] (W_uk[h]^T W_uq[h]
+        stacked over W_qr[h]) once; from then on step() takes the fused query
+        path and project_queries_absorbed() is available."""
+        d_cq = self.w["w_dq"].shape[0]
+        Q = _lib.qabs_dim(self.shape)
+        w_qabs = torch.empty(self.cfg.n_heads, Q, d_cq, dtype=self.dtype, device=self.device)
+        _lib.query_absorb_weights(self.shape, d_cq, self.w["w_uq"], self.w["w_qr"], self.w["w_uk"], w_qabs, stream)
+        self.w = {**self.w, "w_qabs": w_qabs}
+        self.layer_workspace = None  # the weight struct now carries w_qabs
+        return w_qabs
+
+    def project_queries_absorbed(self, x, q_frame_first: int, n_frames: int, stream=None):
+        """(c_q, q_abs) of the chunk's tokens by the fused query path: q_abs
+        [B][n_frames*T][H][Q] is the attention's input (scaled, rotated)."""
+        if "w_qabs" not in self.w:
+            raise ValueError("call absorb_query_weights() first")
+        d_cq = self.w["w_dq"].shape[0]
+        n = n_frames * self.T
+        c_q = torch.empty(self.B, n, d_cq, dtype=self.dtype, device=self.device)
+        q_abs = torch.empty(self.B, n, self.cfg.n_heads, _lib.qabs_dim(self.shape), dtype=self.dtype,
+                            device=self.device)
+        _lib.query_project_absorbed(self.shape, d_cq, x, q_frame_first, n_frames, self.w["w_dq"], self.w["w_qabs"],
+                                    self.tables, self.rope_t_first, self.rope_n_t, c_q, q_abs, stream)
+        return c_q, q_abs
+
     def project_output(self, o, n_frames: int, out=None, stream=None):
         """u = W_o [o_1; ...; o_H] for the heads' outputs o [B][n_frames*T][H][d_head]."""
         if "w_o" not in self.w:
@@ -125,7 +151,8 @@ class LatentLayer:
         """The whole layer for one chunk in one library call (mla_layer_step):
         queries from the chunk's tokens, the cache write of the same tokens,
         the attention over the window, and the output projection
-        -> u [B][n_frames*T][hidden]. Needs all eight weights."""
+        -> u [B][n_frames*T][hidden]. Needs all eight weights; after
+        absorb_query_weights() the queries take the fused path."""
         if n_frames > self.max_chunk_frames:
             raise ValueError("chunk larger than the workspace was sized for")
         for k in ("w_dq", "w_uq", "w_qr", "w_o"):

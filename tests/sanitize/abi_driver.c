@@ -159,9 +159,19 @@ int main(void) {
   }
   EXPECT(mla_output_project(&s, p, 3, p, p, NULL), MLA_ERR_HIP);
 
+  /* absorbed query path */
+  EXPECT(mla_query_absorb_weights(&s, 576, p, p, NULL, p, NULL), MLA_ERR_NULL);
+  EXPECT(mla_query_absorb_weights(&s, 576, p, p, p, odd, NULL), MLA_ERR_ALIGN);
+  EXPECT(mla_query_absorb_weights(&s, 570, p, p, p, p, NULL), MLA_ERR_SHAPE);
+  EXPECT(mla_query_absorb_weights(&s, 576, p, p, p, p, NULL), MLA_ERR_HIP);
+  EXPECT(mla_query_project_absorbed(&s, 576, p, 18, 3, p, p, tab, 0, 21, p, NULL, NULL), MLA_ERR_NULL);
+  EXPECT(mla_query_project_absorbed(&s, 576, p, 18, 3, p, p, tab, 19, 21, p, p, NULL), MLA_ERR_RANGE);
+  EXPECT(mla_query_project_absorbed(&s, 576, p, 18, 0, p, p, tab, 0, 21, p, p, NULL), MLA_ERR_RANGE);
+  EXPECT(mla_query_project_absorbed(&s, 576, p, 18, 3, p, p, tab, 0, 21, p, p, NULL), MLA_ERR_HIP);
+
   /* whole layer */
   {
-    mla_layer_weights lw = {p, p, p, p, p, p, p, p};
+    mla_layer_weights lw = {p, p, p, p, p, p, p, p, NULL};
     const size_t need = mla_layer_step_workspace_bytes(&s, 576, 3);
     EXPECT(need > mla_chunk_attend_workspace_bytes(&s, 3), 1);
     EXPECT(mla_layer_step_workspace_bytes(&s, 572, 3), 0);
@@ -175,6 +185,11 @@ int main(void) {
     lw.w_o = odd;
     EXPECT(mla_layer_step(&s, 576, &lw, p, 18, 3, p, sf, tab, 0, 21, 1, p, p, need, NULL), MLA_ERR_ALIGN);
     lw.w_o = p;
+    EXPECT(mla_layer_step(&s, 576, &lw, p, 18, 3, p, sf, tab, 0, 21, 1, p, p, need, NULL), MLA_ERR_HIP);
+    lw.w_qabs = p; /* fused query path */
+    lw.w_uq = lw.w_qr = lw.w_uk = NULL; /* not read */
+    EXPECT(mla_layer_step(&s, 576, &lw, p, 18, 3, p, sf, tab, 0, 21, 0, p, p, need - 1, NULL), MLA_ERR_WORKSPACE);
+    EXPECT(mla_layer_step(&s, 576, &lw, p, 18, 3, p, sf, tab, 19, 21, 0, p, p, need, NULL), MLA_ERR_RANGE);
     EXPECT(mla_layer_step(&s, 576, &lw, p, 18, 3, p, sf, tab, 0, 21, 1, p, p, need, NULL), MLA_ERR_HIP);
   }
 

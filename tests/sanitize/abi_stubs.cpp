@@ -17,4 +17,6 @@ int heads_tile_keys(int, int d_rope) { return d_rope > 32 ? 64 : 128; }
 hipError_t launch_heads(int, int, int, const HeadsParams&, bool, hipStream_t) { return hipErrorInvalidValue; }
 int gemm_tile_rows(int, int, int) { return 64; }
 hipError_t launch_gemm_nt(int, const GemmParams&, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_gemm_qabs(int, const GemmParams&, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_qabs_weights(int, const QabsWeightParams&, hipStream_t) { return hipErrorInvalidValue; }
 }  // namespace mla

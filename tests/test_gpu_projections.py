@@ -170,3 +170,90 @@ def test_layer_step_single_call_equals_composed_calls(name, frame_causal):
         assert torch.isfinite(u1.float()).all()
         assert torch.equal(view(u1), view(u4)), f"chunk {k}"
         assert torch.equal(view(one.cache), view(four.cache)) and torch.equal(one.slot_frame, four.slot_frame)
+
+
+# ------------------------------------------------------------------ fused (absorbed) query path
+
+def _u(dtype):
+    return _unit(dtype)
+
+
+@pytest.mark.parametrize("name", ["tiny", "wan_small", "wan_small_f32", "wan_small_c160r64"])
+def test_query_absorb_weights(name):
+    """w_qabs[h] = [W_uk[h]^T W_uq[h] ; W_qr[h] ; 0] against the fp64 product
+    (one rounding, fp32 sums over d_head)."""
+    cfg = get_config(name)
+    w, wd = _weights(cfg, 58)
+    layer = LatentLayer(cfg, wd, batch=1, rope_n_t=16)
+    got = to_numpy(layer.absorb_query_weights())
+    torch.cuda.synchronize()
+    dc, dr, H = cfg.d_c, cfg.d_rope, cfg.n_heads
+    ref = np.zeros(got.shape)
+    ref[:, :dc] = np.einsum("hic,hiq->hcq", w["w_uk"], w["w_uq"])
+    ref[:, dc:dc + dr] = w["w_qr"]
+    absprod = np.zeros(got.shape)
+    absprod[:, :dc] = np.einsum("hic,hiq->hcq", np.abs(w["w_uk"]), np.abs(w["w_uq"]))
+    _assert_product_close(got, ref, absprod, cfg.dtype, cfg.d_head, False, f"{name} w_qabs")
+    assert not got[:, dc + dr:].any()
+
+
+def _check_absorbed_queries(cfg, seed, B, n_frames, q_frame_first):
+    w, wd = _weights(cfg, seed)
+    layer = LatentLayer(cfg, wd, batch=B, rope_n_t=64, max_chunk_frames=n_frames)
+    layer.absorb_query_weights()
+    x = np.stack([Stream(cfg, seed=seed, stream=b).xs(q_frame_first, n_frames) for b in range(B)])
+    c_q, q_abs = layer.project_queries_absorbed(to_torch(x, cfg.dtype).contiguous(), q_frame_first, n_frames)
+    torch.cuda.synchronize()
+    got = to_numpy(q_abs).reshape(-1, cfg.n_heads, q_abs.shape[-1])
+    xr = x.reshape(-1, cfg.hidden)
+    c_ref, qn, qr = O.query_project(xr, w["w_dq"], w["w_uq"], w["w_qr"])
+    n = n_frames * cfg.tokens_per_frame
+    tq, yq, xq = O.frame_positions(q_frame_first + np.arange(n_frames), cfg.grid_y, cfg.grid_x)
+    tq, yq, xq = (np.tile(a, B) for a in (tq, yq, xq))
+    ref = O.absorbed_query(qn, qr, w["w_uk"], tq, yq, xq, cfg.rope_split, cfg.rope_base)
+    g = float(np.float32(O.default_scale(cfg.d_head, cfg.d_rope) * np.log2(np.e)))
+    dc, dr = cfg.d_c, cfg.d_rope
+    # magnitudes: |W_abs| |c_q| per latent column; rotated columns mix a pair
+    ac = np.abs(c_ref)
+    a_lat = np.einsum("nq,hcq->nhc", ac, np.einsum("hic,hiq->hcq", np.abs(w["w_uk"]), np.abs(w["w_uq"])))
+    a_rope = np.einsum("nq,hdq->nhd", ac, np.abs(w["w_qr"]))
+    a_rope = np.repeat(a_rope[..., 0::2] + a_rope[..., 1::2], 2, axis=-1)
+    absprod = g * np.concatenate([a_lat, a_rope], axis=-1)
+    u = _u(cfg.dtype)
+    # c_q and the absorbed weight are each rounded once before the fp32 product
+    bound = 2.01 * u * absprod + u * np.abs(g * ref) + cfg.q_latent * 2.0 ** -22 * absprod + 1e-30
+    d = np.abs(got[..., :dc + dr] - g * ref)
+    print(f"[proj] {cfg.name} q_abs fused max_abs={d.max():.3e} violations={int((d > bound).sum())}", flush=True)
+    assert not (d > bound).any()
+    assert not got[..., dc + dr:].any()
+    assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("name", ["tiny", "wan_small", "wan_small_f32", "wan_small_c160r64"])
+def test_query_project_absorbed(name):
+    cfg = get_config(name)
+    _check_absorbed_queries(cfg, 59, B=2, n_frames=cfg.chunk_frames, q_frame_first=5)
+
+
+def test_query_project_absorbed_wan_full_size():
+    cfg = get_config("wan")
+    _check_absorbed_queries(cfg, 60, B=1, n_frames=3, q_frame_first=18)
+
+
+@pytest.mark.parametrize("name", ["tiny", "wan_small", "wan_small_f32"])
+def test_layer_step_fused_query_path(name):
+    """The whole layer with the fused query path, chunk after chunk through
+    ring wrap, against the oracle's layer step."""
+    cfg = get_config(name)
+    w, wd = _weights(cfg, 61)
+    layer = LatentLayer(cfg, wd, batch=1, rope_n_t=64)
+    layer.absorb_query_weights()
+    ring = O.RingCache(cfg.window_frames, cfg.tokens_per_frame, cfg.d_c, cfg.d_rope)
+    st = Stream(cfg, seed=61)
+    for k in range(cfg.window_frames // cfg.chunk_frames + 2):
+        f0 = k * cfg.chunk_frames
+        x = st.xs(f0, cfg.chunk_frames)
+        u = layer.step(to_torch(x[None], cfg.dtype), f0, cfg.chunk_frames, frame_causal=(k % 2 == 1))
+        torch.cuda.synchronize()
+        ref, _, _, _ = O.layer_step(O.dims_of(cfg), w, ring, x, f0, frame_causal=(k % 2 == 1))
+        assert_step_close(to_numpy(u)[0], ref, cfg.dtype, label=f"{name} fused layer step chunk {k}")
