@@ -5,17 +5,21 @@
 // temperature in log2 units (qscale = scale * log2 e) so that scores come out
 // of the matrix product ready for exp2:
 //   q_abs[b,i,h] = qscale [ W_uk[h]^T q_nope[b,i,h] | R(t,y,x) q_r[b,i,h] | 0 ... ]
-// Work-group: 64 query tokens x one head. The 32-row slabs of W_uk[h] are
-// staged in LDS and read with the transposing LDS load, because the
-// contraction runs over W_uk's row index.
+// Work-group: 128 query tokens x one head (8 waves of 16 tokens, so W_uk[h]
+// is read once per 128 tokens). The 32-row slabs of W_uk[h] are staged in
+// LDS and read with the transposing LDS load, because the contraction runs
+// over W_uk's row index.
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 #include "rope_device.hpp"
 
 namespace mla {
 
+constexpr int kAbsorbRows = 128;               // query tokens per work-group
+constexpr int kAbsorbThreads = kAbsorbRows * 4;  // one wave per 16 tokens
+
 template <typename T, int DC, int DR>
-__global__ __launch_bounds__(256) void absorb_q_kernel(AbsorbParams p) {
+__global__ __launch_bounds__(kAbsorbThreads) void absorb_q_kernel(AbsorbParams p) {
   typedef typename V8<T>::type v8;
   constexpr int KP = (DC + DR + 31) / 32 * 32;
   constexpr int PADE = 16 / sizeof(T);
@@ -24,7 +28,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(AbsorbParams p) {
   __shared__ __attribute__((aligned(16))) T wl[32 * LS];
 
   const int h = blockIdx.y;
-  const int row0 = blockIdx.x * 64;
+  const int row0 = blockIdx.x * kAbsorbRows;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int H = p.H, dh = p.d_head;
@@ -37,7 +41,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(AbsorbParams p) {
   f32x4 acc[NNB] = {};
   for (int k0 = 0; k0 < dh; k0 += 32) {
     __syncthreads();
-    for (int e = tid; e < 32 * (DC / 8); e += 256) {
+    for (int e = tid; e < 32 * (DC / 8); e += kAbsorbThreads) {
       const int r = e / (DC / 8), c8 = (e % (DC / 8)) * 8;
       const v8 v = (k0 + r < dh) ? load8<T>(wbase + (size_t)(k0 + r) * DC + c8) : zero8<T>();
       store8<T>(wl + r * LS + c8, v);
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(AbsorbParams p) {
 
   // rotated positional part and zero padding
   constexpr int NPR = DR / 2;
-  for (int e = tid; e < 64 * NPR; e += 256) {
+  for (int e = tid; e < kAbsorbRows * NPR; e += kAbsorbThreads) {
     const int r = row0 + e / NPR, pr = e % NPR;
     if (r >= p.rows) continue;
     const int i = r % p.n_q;
@@ -80,7 +84,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(AbsorbParams p) {
   }
   if constexpr (KP > DC + DR) {
     constexpr int NPAD = KP - DC - DR;
-    for (int e = tid; e < 64 * NPAD; e += 256) {
+    for (int e = tid; e < kAbsorbRows * NPAD; e += kAbsorbThreads) {
       const int r = row0 + e / NPAD;
       if (r >= p.rows) continue;
       qa[((size_t)r * H + h) * KP + DC + DR + e % NPAD] = to_t<T>(0.f);
@@ -90,8 +94,8 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(AbsorbParams p) {
 
 template <typename T, int DC, int DR>
 static hipError_t launch_absorb_t(const AbsorbParams& p, hipStream_t s) {
-  dim3 grid((p.rows + 63) / 64, p.H);
-  hipLaunchKernelGGL((absorb_q_kernel<T, DC, DR>), grid, dim3(256), 0, s, p);
+  dim3 grid((p.rows + kAbsorbRows - 1) / kAbsorbRows, p.H);
+  hipLaunchKernelGGL((absorb_q_kernel<T, DC, DR>), grid, dim3(kAbsorbThreads), 0, s, p);
   return hipGetLastError();
 }
 
