@@ -11,8 +11,9 @@
 // the latent form's 2 Nq Nk H (d_c + d_rope + d_c); the expansion adds
 // 4 Nk H d_head d_c products and writes 4 Nk H d_head bytes (bf16).
 //
-// Attention layout (bf16): a row block is 256 query tokens of one head (8
-// waves x 32 rows, two waves per SIMD); one work-group per compute unit
+// Attention layout (bf16): a row block is 384 query tokens of one head (8
+// waves x 48 rows, two waves per SIMD: each staged key and value fragment
+// feeds three row blocks' products); one work-group per compute unit
 // takes an equal share of the (row block, key tile) units, and row blocks
 // shared by several work-groups are merged afterwards. Key tiles of 128 keys are staged in LDS, double buffered, with
 // direct global->LDS loads from three contiguous row sets: k_exp (rows 272
@@ -162,8 +163,9 @@ __global__ __launch_bounds__(256) void heads_qcat_kernel(HeadsParams p) {
 // ---------------------------------------------------------------- attention
 template <int DH, int DR>
 struct HeadsTile {
-  static constexpr int kWaves = 8, kThreads = 512, kNMB = 2;
+  static constexpr int kWaves = 8, kThreads = 512, kNMB = 3;
   static constexpr int kRowsWave = kNMB * 16, kRowsBlock = kWaves * kRowsWave;
+  static_assert(kRowsBlock == kHeadsRowsPerBlock, "the host plans row blocks of this size");
   static constexpr int QP = DH + DR;           // contraction width of QK
   static constexpr int NKC = QP / 32, NKCH = DH / 32, NDB = DH / 16;
   static constexpr int LSK = DH + 8;           // k rows (elements): 16 rows of a QK read hit 16 bank groups
@@ -458,7 +460,8 @@ constexpr int kHeadsMergeRows = 32;
 
 template <int DH>
 __global__ __launch_bounds__(256) void heads_combine_kernel(HeadsParams p) {
-  constexpr int RB = 256, NCH = DH / 8;
+  constexpr int RB = kHeadsRowsPerBlock, NCH = DH / 8;
+  static_assert(RB % kHeadsMergeRows == 0, "merge groups tile a row block");
   __shared__ long long slot_base[kMaxMergePieces];
   const long long G = p.grid;
   const long long rbg = blockIdx.x / (RB / kHeadsMergeRows);
@@ -584,8 +587,7 @@ static hipError_t launch_heads_t(const HeadsParams& p, bool split, hipStream_t s
   hipLaunchKernelGGL((heads_flash_kernel<DH, DR>), dim3(p.grid), dim3(F::kThreads), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (split) {
-    static_assert(F::kRowsBlock == 256, "merge groups tile a 256-row block");
-    hipLaunchKernelGGL((heads_combine_kernel<DH>), dim3(p.batch * p.H * p.n_rb * (256 / kHeadsMergeRows)),
+    hipLaunchKernelGGL((heads_combine_kernel<DH>), dim3(p.batch * p.H * p.n_rb * (kHeadsRowsPerBlock / kHeadsMergeRows)),
                        dim3(256), 0, s, p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }

@@ -247,14 +247,14 @@ mla_status check_query_args(const mla_shape* s, int q_frame_first, int q_n_frame
   return MLA_OK;
 }
 
-// Work split of the per-head attention kernel: (row block of 256 tokens of
+// Work split of the per-head attention kernel: (row block of 384 tokens of
 // one (stream, head), key tile) units shared evenly by one work-group per
 // compute unit, as for the latent form.
 FlashPlan heads_plan(const mla_shape* s, int q_n_frames) {
   FlashPlan f;
   const int64_t nq = (int64_t)q_n_frames * tokens_per_frame(s);
   const int tk = mla::heads_tile_keys(s->d_head, s->d_rope);
-  f.n_rb = (int)((nq + 255) / 256);
+  f.n_rb = (int)((nq + mla::kHeadsRowsPerBlock - 1) / mla::kHeadsRowsPerBlock);
   f.nt_max = (int)((s->window_frames * tokens_per_frame(s) + tk - 1) / tk);
   const int64_t row_blocks = (int64_t)s->batch * s->n_heads * f.n_rb;
   f.units = row_blocks * f.nt_max;
@@ -287,7 +287,7 @@ HeadsWs heads_ws_layout(const mla_shape* s, int q_n_frames) {
   w.q_cat = w.v_exp + round256((size_t)s->batch * s->n_heads * nk * s->d_head * e);
   w.part_o = w.q_cat + round256((size_t)s->batch * s->n_heads * nq * (s->d_head + s->d_rope) * e);
   const FlashPlan f = heads_plan(s, q_n_frames);
-  const size_t slots = f.split ? (size_t)f.grid * 2 * 256 : 0;
+  const size_t slots = f.split ? (size_t)f.grid * 2 * mla::kHeadsRowsPerBlock : 0;
   w.part_l = w.part_o + round256(slots * s->d_head * e);
   w.total = w.part_l + round256(slots * 2 * sizeof(float));
   return w;

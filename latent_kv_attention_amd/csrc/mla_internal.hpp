@@ -106,11 +106,11 @@ struct HeadsParams {
   const void* krot;        // [B][W * T][d_rope]: rotated kR (the rotation pass of the latent form)
   int* fallback_count;     // rows listed for the exact fallback
   int* fallback_rows;      // [B * H * Nq], as (b * H + h) * Nq + i
-  void* part_o;            // [G][2][256][d_head] partial outputs o_g / l_g (split row blocks only)
-  float* part_l;           // [G][2][256][2] (reference, sum)
+  void* part_o;            // [G][2][rows per block][d_head] partial outputs o_g / l_g (split row blocks only)
+  float* part_l;           // [G][2][rows per block][2] (reference, sum)
   RopeLayout rl;
   int batch, H, Nq, T, W, grid_x, q_frame_first;
-  int n_rb, nt_max;        // row blocks of 256 tokens per (stream, head); key tiles of a full window
+  int n_rb, nt_max;        // row blocks of kHeadsRowsPerBlock tokens per (stream, head); key tiles of a full window
   long long units;         // batch * H * n_rb * nt_max
   int grid;                // G, work-groups of the attention kernel
   float qscale;            // softmax scale * log2(e)
@@ -165,6 +165,9 @@ hipError_t launch_up_v(int dtype, int d_c, int d_rope, const UpVParams& p, hipSt
 // the rotation pass of the attention kernel alone (rotated kR of the window
 // into p.krot, fallback count cleared)
 hipError_t launch_rope_window(int dtype, int d_c, int d_rope, const FlashParams& p, hipStream_t s);
+// Query tokens per row block of the per-head attention kernel (8 waves of
+// 48 tokens of one head).
+constexpr int kHeadsRowsPerBlock = 384;
 bool heads_supported(int dtype, int d_c, int d_rope, int d_head);
 int heads_tile_keys(int d_head, int d_rope);  // keys per tile of the per-head attention kernel
 hipError_t launch_heads(int d_c, int d_rope, int d_head, const HeadsParams& p, bool split, hipStream_t s);

@@ -93,7 +93,7 @@ def test_heads_wan_full_size_sampled_rows():
     """Wan2.1-1.3B shape, 3-frame chunk over a full 21-frame window, in the
     launch configuration the width sweep times; 64 sampled query rows (all
     heads, full window) against the oracle, including first and last rows and
-    the boundaries of the 256-token row blocks."""
+    the boundaries of the 384-token row blocks and of the last, ragged one."""
     cfg = get_config("wan")
     w, wd = device_weights(cfg, seed=0)
     layer = LatentLayer(cfg, wd, batch=1, rope_n_t=64)
@@ -105,7 +105,7 @@ def test_heads_wan_full_size_sampled_rows():
     torch.cuda.synchronize()
     got = to_numpy(out)[0]
     rng = np.random.default_rng(1)
-    edge = [0, 1, 255, 256, 511, 512, cfg.n_q // 2, cfg.n_q - 256, cfg.n_q - 1]
+    edge = [0, 1, 383, 384, 767, 768, cfg.n_q // 2, 12 * 384 - 1, 12 * 384, cfg.n_q - 1]
     rows = np.unique(np.concatenate([edge, rng.choice(cfg.n_q, 64 - len(edge), replace=False)]))
     xs = {f: st.x(f) for f in range(21)}
     ref = oracle_step_rows(cfg, w, xs, list(range(21)), qn, qr, 18, rows)
