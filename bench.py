@@ -510,6 +510,8 @@ def configs_report(args):
             ("wan_batch8", 8, 1, 18, "8 streams x 30 layers, one chunk over full 21-frame windows"),
             ("wan_rollout", 1, 80, 0, "80 chunks x 30 layers (frames 0..239), rings evicting from chunk 8")]
     for name, B, n_chunks, prefill, what in runs:
+        if args.configs and name not in args.configs:
+            continue
         print(f"[bench] configs: {name}", file=sys.stderr, flush=True)
         ms, fl, slots = run(name, B, n_chunks, prefill)
         print(json.dumps({
@@ -539,8 +541,9 @@ def main():
                     help="time the attention side with and without the frame-causal mask (report line) and exit")
     ap.add_argument("--projections", action="store_true",
                     help="time the query path, the output projection and the whole layer (report line) and exit")
-    ap.add_argument("--configs", action="store_true",
-                    help="time the 30-layer fill, 8-stream and 80-chunk rollout workloads (report lines) and exit")
+    ap.add_argument("--configs", nargs="*", default=None, metavar="NAME",
+                    help="time the 30-layer fill (wan_fill30), 8-stream (wan_batch8) and 80-chunk rollout "
+                         "(wan_rollout) workloads, or only those named (report lines) and exit")
     ap.add_argument("--latent-sweep", action="store_true",
                     help="time the step at every latent width with kernels (one report line each) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -588,7 +591,7 @@ def main():
     if args.projections:
         projections_report(cfg, args)
         return
-    if args.configs:
+    if args.configs is not None:
         configs_report(args)
         return
     ctx = setup_step(cfg, args.kv_splits)
