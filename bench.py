@@ -630,6 +630,32 @@ def main():
         copy_bytes = 2 * x_chunk.numel() * x_chunk.element_size()
         del xs_cold, dst
 
+    # larger writes, where the launch cost is spread over more bytes: a
+    # 21-frame prefill of one stream, and a 3-frame chunk of 8 streams
+    # (seeded device-side tokens; content does not change the work)
+    big_writes = {}
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    for label, B, nf in (("prefill_21_frames", 1, 21), ("batch8_3_frames", 8, 3)):
+        shp = mla.make_shape(cfg, batch=B)
+        xb = torch.randn(B, nf * cfg.tokens_per_frame, cfg.hidden, generator=gen, device="cuda").to(torch.bfloat16)
+        cb = torch.zeros(B, cfg.window_frames, cfg.tokens_per_frame, cfg.d_c + cfg.d_rope, dtype=torch.bfloat16,
+                         device="cuda")
+        sb = torch.full((B, cfg.window_frames), -1, dtype=torch.int32, device="cuda")
+        ts = []
+        for i in range(6):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            mla.cache_write(shp, xb, w["w_dkv"], w["w_kr"], 0, nf, cb, sb)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        rows = B * nf * cfg.tokens_per_frame
+        byts = rows * cfg.hidden * 2 + (cfg.d_c + cfg.d_rope) * cfg.hidden * 2 + rows * (cfg.d_c + cfg.d_rope) * 2
+        ms = float(np.median(ts[1:]))
+        big_writes[label] = {"bytes": byts, "ms": round(ms, 4), "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
+                             "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+        del xb, cb, sb
+
     fl = step_flops(cfg)
     cw_bytes = cache_write_bytes(cfg)
     flash_tflops = fl["flash"] / (per["flash_attend"] * 1e-3) / 1e12
@@ -666,6 +692,7 @@ def main():
         "cache_write_hbm_frac_cold": round(cw_bytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4) if cold else None,
         "kernel_ms": {k: round(v, 4) for k, v in per.items()},
         "cache_write_cold_ms": round(cold, 4) if cold else None,
+        "cache_write_large": big_writes,
         "copy_reference": {"what": "device copy of a 14.38 MB x buffer (cold, single launches), reads + writes",
                            "bytes": copy_bytes, "ms": round(copy_single, 4),
                            "GBps": round(copy_bytes / (copy_single * 1e-3) / 1e9, 1)} if cold else None,
