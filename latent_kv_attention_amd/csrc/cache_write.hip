@@ -179,6 +179,136 @@ __global__ __launch_bounds__(256) void cache_write_staged_kernel(CacheWriteParam
   }
 }
 
+// Writes of many tokens (a window prefill, a chunk of many streams): tiles
+// of 128 token rows x all outputs, so that every x row is read from memory
+// by one work-group only, and W (at most 0.8 MB, the same for every tile)
+// is served by the L2. Four waves in 2 x 2: 64 rows x NCB 16-output blocks
+// each. 64-wide K steps through three LDS stage buffers (two in flight),
+// direct global->LDS loads, 16-byte chunks XOR-permuted by row; the
+// output tile leaves through LDS in 16-byte row pieces.
+namespace {
+constexpr int kWM = 128;                            // token rows per tile
+constexpr int kWK = 64;                             // K per stage
+constexpr int kWChunks = kWK * 2 / 16;              // 16-byte chunks per staged row (8)
+}  // namespace
+
+template <int NSTAGE, int NCB>
+__global__ __launch_bounds__(256) void cache_write_wide_kernel(CacheWriteParams p, int n_logical, int per_xcd) {
+  constexpr int WN = 2 * NCB * 16;                  // outputs (= d_c + d_rope)
+  constexpr int ROWS = kWM + WN;                    // staged rows per stage
+  constexpr int INSTR = ROWS * kWChunks / 64;       // direct-load instructions per stage
+  constexpr int INSTR_WAVE = (INSTR + 3) / 4;
+  constexpr int ELEMS = INSTR * 64 * 8;             // bf16 per stage buffer (whole instructions)
+  constexpr int OLD = WN + 8;                       // output staging row stride
+  static_assert(ROWS * kWChunks % 64 == 0, "whole direct-load instructions per stage");
+  static_assert((kWM / 2) * OLD <= ELEMS, "half the output tile fits in one stage buffer");
+  static_assert(INSTR_WAVE < 32, "two stages of loads within the vmcnt range");
+  __shared__ __attribute__((aligned(16))) bf16 wb0[ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 wb1[ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 wb2[ELEMS];
+  const int logical = xcd_logical(blockIdx.x, per_xcd);
+  if (logical >= n_logical) return;
+  const int row0 = logical * kWM;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int wr = wave >> 1, wc = wave & 1;
+
+  if (logical == 0) {
+    for (int e = tid; e < p.batch * p.n_frames; e += blockDim.x) {
+      const int b = e / p.n_frames, f = p.frame_first + e % p.n_frames;
+      p.slot_frame[b * p.W + f % p.W] = f;
+    }
+  }
+
+  // instruction i fills staged rows 8 i .. 8 i + 7; lane L writes row
+  // 8 i + L / 8, LDS chunk L % 8, which holds global chunk (L % 8) ^ (L / 8)
+  const char* src[INSTR_WAVE];
+  int dst_off[INSTR_WAVE];
+#pragma unroll
+  for (int k = 0; k < INSTR_WAVE; ++k) {
+    const int instr = min(wave + 4 * k, INSTR - 1);
+    const int sr = instr * 8 + (lane >> 3), c = (lane & 7) ^ (lane >> 3);
+    const bf16* rowp;
+    if (sr < kWM) {
+      rowp = (const bf16*)p.x + (size_t)min(row0 + sr, p.rows - 1) * p.hidden;
+    } else {
+      const int n = sr - kWM;
+      rowp = n < p.d_c ? (const bf16*)p.w_dkv + (size_t)n * p.hidden
+                       : (const bf16*)p.w_kr + (size_t)(n - p.d_c) * p.hidden;
+    }
+    src[k] = (const char*)(rowp + c * 8);
+    dst_off[k] = instr * 64 * 8;
+  }
+  const int k_start = logical % NSTAGE;  // staggered K order (W lines not all requested at once)
+  auto issue = [&](int stage, bf16* buf) {
+    int ks = stage + k_start;
+    ks = ks >= NSTAGE ? ks - NSTAGE : ks;
+#pragma unroll
+    for (int k = 0; k < INSTR_WAVE; ++k)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[k] + ks * kWK * 2),
+                                       (MLA_LDS void*)(MLA_LDS bf16*)(buf + dst_off[k]), 16, 0, 0);
+  };
+
+  f32x4 acc[4][NCB] = {};
+  // staged row r, logical chunk c: element (r * 8 + (c ^ (r % 8))) * 8
+  auto compute = [&](const bf16* buf) {
+#pragma unroll
+    for (int kc = 0; kc < kWK / 32; ++kc) {
+      const int c = kc * 4 + lg;
+      bf16x8 aop[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int ra = wr * 64 + mb * 16 + li;
+        aop[mb] = load8<bf16>(buf + (ra * kWChunks + (c ^ (ra & 7))) * 8);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NCB; ++nb) {
+        const int rb = kWM + (wc * NCB + nb) * 16 + li;
+        const bf16x8 bop = load8<bf16>(buf + (rb * kWChunks + (c ^ (rb & 7))) * 8);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = mma16(aop[mb], bop, acc[mb][nb]);
+      }
+    }
+  };
+
+  auto buf = [&](int i) -> bf16* { return i == 0 ? wb0 : i == 1 ? wb1 : wb2; };
+  issue(0, buf(0));
+  if (NSTAGE > 1) issue(1, buf(1));
+#pragma unroll
+  for (int s = 0; s < NSTAGE; ++s) {
+    if (s + 1 < NSTAGE)
+      wait_vm<INSTR_WAVE>();  // this stage's loads have landed, the next one's may not
+    else
+      wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    if (s + 2 < NSTAGE) issue(s + 2, buf((s + 2) % 3));
+    compute(buf(s % 3));
+  }
+
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // output rows 0..63 (wave row 0) staged in the first buffer, 64..127 in the second
+  bf16* ot = wr == 0 ? wb0 : wb1;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NCB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ot[(mb * 16 + lg * 4 + i) * OLD + (wc * NCB + nb) * 16 + li] = (bf16)acc[mb][nb][i];
+  __syncthreads();
+  for (int e = tid; e < kWM * (WN / 8); e += 256) {
+    const int r = e / (WN / 8), c8 = (e % (WN / 8)) * 8;
+    const int row = row0 + r;
+    if (row >= p.rows) continue;
+    const int b = row / p.rows_per_b, local = row - b * p.rows_per_b;
+    const int f = p.frame_first + local / p.T, tok = local % p.T;
+    bf16* dst = (bf16*)p.cache + (((size_t)b * p.W + f % p.W) * p.T + tok) * WN + c8;
+    const bf16* srcp = (r < kWM / 2 ? wb0 + r * OLD : wb1 + (r - kWM / 2) * OLD) + c8;
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(srcp);
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p, int n_tiles_n, int n_logical,
                                                           int per_xcd) {
@@ -246,6 +376,22 @@ hipError_t launch_cache_write(int dtype, int d_c, int d_rope, const CacheWritePa
   (void)d_c;
   (void)d_rope;
   const int n_out = p.d_c + p.d_rope;
+  // many tokens: tiles over all outputs once there is at least one 128-row
+  // tile per compute unit (x is then read once; below that the narrower
+  // tiles below keep every compute unit busy)
+  if (dtype == 0 && p.hidden == 1536 && (p.rows + kWM - 1) / kWM >= 256 &&
+      (n_out == 224 || n_out == 160 || n_out == 256)) {
+    const int n_logical = (p.rows + kWM - 1) / kWM;
+    const int per_xcd = (n_logical + kXcds - 1) / kXcds;
+    const dim3 grid(per_xcd * kXcds);
+    if (n_out == 224)
+      hipLaunchKernelGGL((cache_write_wide_kernel<1536 / kWK, 7>), grid, dim3(256), 0, s, p, n_logical, per_xcd);
+    else if (n_out == 160)
+      hipLaunchKernelGGL((cache_write_wide_kernel<1536 / kWK, 5>), grid, dim3(256), 0, s, p, n_logical, per_xcd);
+    else
+      hipLaunchKernelGGL((cache_write_wide_kernel<1536 / kWK, 8>), grid, dim3(256), 0, s, p, n_logical, per_xcd);
+    return hipGetLastError();
+  }
   if (dtype == 0 && p.hidden == 1536 && n_out % 8 == 0 && p.rows >= 1) {
     const int n_tiles_n = (n_out + kSN - 1) / kSN;
     const int n_logical = ((p.rows + kSM - 1) / kSM) * n_tiles_n;

@@ -84,6 +84,33 @@ def test_cache_write_and_ring(name):
         assert_rounded_close(cache[s_, :, cfg.d_c:], kr, cfg.dtype, label=f"{name} kR slot {s_}")
 
 
+@pytest.mark.parametrize("name,B,n_frames", [("wan", 1, 21), ("wan_small_c128r32", 32, 16),
+                                             ("wan_small_c192r64", 32, 16)])
+def test_cache_write_many_tokens(name, B, n_frames):
+    """Writes of at least 256 tiles of 128 tokens (a whole 21-frame Wan window
+    in one call; 32 streams of a 16-frame window at other latent widths), which
+    take the kernel with tiles over all outputs: sampled cache rows of every
+    written frame against the oracle's latents, and the slot table."""
+    cfg = get_config(name).with_(window_frames=n_frames)
+    w, wd = device_weights(cfg, seed=17)
+    layer = LatentLayer(cfg, wd, batch=B, rope_n_t=64)
+    streams = [Stream(cfg, seed=17, stream=b, pooled=True) for b in range(B)]
+    x = np.stack([s_.xs(0, n_frames) for s_ in streams])
+    layer.write(to_torch(x, cfg.dtype), 0, n_frames)
+    _sync()
+    cache = to_numpy(layer.cache)
+    assert (to_numpy(layer.slot_frame) == np.arange(n_frames)[None, :]).all()
+    rng = np.random.default_rng(17)
+    T = cfg.tokens_per_frame
+    for b in sorted({0, B - 1, int(rng.integers(B))}):
+        for f in range(n_frames):
+            toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 6, replace=False)]))
+            c, kr = O.latents(x[b, f * T + toks], w["w_dkv"], w["w_kr"])
+            got = cache[b, f, toks]
+            assert_rounded_close(got, np.concatenate([c, kr], axis=-1), cfg.dtype,
+                                 label=f"{name} many-token write b={b} f={f}")
+
+
 def test_cache_write_batch_streams():
     cfg = get_config("wan_small")
     w, wd = device_weights(cfg, seed=4)
