@@ -444,6 +444,29 @@ def test_full_step_frame_causal_wrapped_ring():
     assert_step_close(got, ref, cfg.dtype, label="wan_small frame-causal wrapped ring")
 
 
+def test_frame_causal_one_frame_chunk_and_empty_window():
+    """A one-frame chunk sees every window key under the frame-causal mask,
+    so the variant returns the same bits as the unmasked call; over an empty
+    window both return zeros."""
+    cfg = get_config("wan_small").with_(chunk_frames=1, window_frames=4)
+    w, wd = device_weights(cfg, seed=43)
+    st = Stream(cfg, seed=43)
+    layer = LatentLayer(cfg, wd, batch=2, rope_n_t=16)
+    qn, qr = st.q(3)
+    qn_t = to_torch(np.stack([qn, qn]), cfg.dtype)
+    qr_t = to_torch(np.stack([qr, qr]), cfg.dtype)
+    empty_full = layer.attend(qn_t, qr_t, 3, 1)
+    empty_causal = layer.attend_frame_causal(qn_t, qr_t, 3, 1)
+    _sync()
+    assert not to_numpy(empty_full).any() and not to_numpy(empty_causal).any()
+    layer.write(to_torch(np.stack([st.xs(0, 4), Stream(cfg, seed=44).xs(0, 4)]), cfg.dtype), 0, 4)
+    full = layer.attend(qn_t, qr_t, 3, 1)
+    causal = layer.attend_frame_causal(qn_t, qr_t, 3, 1)
+    _sync()
+    assert torch.isfinite(full.float()).all()
+    assert torch.equal(full.view(torch.int16), causal.view(torch.int16))
+
+
 def test_wan_full_size_frame_causal_sampled_rows():
     """Wan2.1-1.3B shape, 3-frame chunk over a full 21-frame window, frame
     causal: 64 sampled rows of the three chunk frames against the oracle."""
