@@ -376,10 +376,11 @@ hipError_t launch_cache_write(int dtype, int d_c, int d_rope, const CacheWritePa
   (void)d_c;
   (void)d_rope;
   const int n_out = p.d_c + p.d_rope;
-  // many tokens: tiles over all outputs once there is at least one 128-row
-  // tile per compute unit (x is then read once; below that the narrower
-  // tiles below keep every compute unit busy)
-  if (dtype == 0 && p.hidden == 1536 && (p.rows + kWM - 1) / kWM >= 256 &&
+  // many tokens: tiles over all outputs from 96 tiles of 128 rows on (x is
+  // read once; a work-group's K loop takes about the same time at any size,
+  // so below that the narrower tiles, spread over every compute unit, finish
+  // first; measured crossover between 74 and 110 tiles)
+  if (dtype == 0 && p.hidden == 1536 && (p.rows + kWM - 1) / kWM >= 96 &&
       (n_out == 224 || n_out == 160 || n_out == 256)) {
     const int n_logical = (p.rows + kWM - 1) / kWM;
     const int per_xcd = (n_logical + kXcds - 1) / kXcds;
