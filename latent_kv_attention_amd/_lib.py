@@ -114,8 +114,20 @@ def _check(fn, code):
         raise MlaError(fn, code)
 
 
-def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+def _ptr(t, dtype: str | None = None):
+    """Device address of a tensor. The kernels read and write dense row-major
+    buffers in GPU memory at that address, so a tensor in host memory, a
+    strided view or (for the typed arguments: slot table int32, RoPE tables
+    float32) another element type is refused here, before any call."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"mla: expected a GPU tensor, got one on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"mla: expected a contiguous tensor, got strides {tuple(t.stride())}")
+    if dtype is not None and str(t.dtype) != "torch." + dtype:
+        raise ValueError(f"mla: expected {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream):
@@ -142,21 +154,21 @@ def rope3d_table_floats(shape: MlaShape, n_t: int) -> int:
 
 
 def rope3d_tables(shape: MlaShape, t_first: int, n_t: int, tables, stream=None) -> None:
-    _check("mla_rope3d_tables", lib().mla_rope3d_tables(ctypes.byref(shape), t_first, n_t, _ptr(tables),
+    _check("mla_rope3d_tables", lib().mla_rope3d_tables(ctypes.byref(shape), t_first, n_t, _ptr(tables, "float32"),
                                                         _stream(stream)))
 
 
 def cache_write(shape: MlaShape, x, w_dkv, w_kr, frame_first: int, n_frames: int, cache, slot_frame,
                 stream=None) -> None:
     _check("mla_cache_write", lib().mla_cache_write(ctypes.byref(shape), _ptr(x), _ptr(w_dkv), _ptr(w_kr),
-                                                    frame_first, n_frames, _ptr(cache), _ptr(slot_frame),
+                                                    frame_first, n_frames, _ptr(cache), _ptr(slot_frame, "int32"),
                                                     _stream(stream)))
 
 
 def absorb_q(shape: MlaShape, q_nope, q_r, q_frame_first: int, q_n_frames: int, w_uk, tables,
              rope_t_first: int, rope_n_t: int, q_abs, stream=None) -> None:
     _check("mla_absorb_q", lib().mla_absorb_q(ctypes.byref(shape), _ptr(q_nope), _ptr(q_r), q_frame_first,
-                                              q_n_frames, _ptr(w_uk), _ptr(tables), rope_t_first, rope_n_t,
+                                              q_n_frames, _ptr(w_uk), _ptr(tables, "float32"), rope_t_first, rope_n_t,
                                               _ptr(q_abs), _stream(stream)))
 
 
@@ -168,7 +180,7 @@ def flash_attend(shape: MlaShape, q_abs, q_n_frames: int, cache, slot_frame, tab
                  rope_n_t: int, o_lat, workspace, kv_splits: int = 0, stream=None) -> None:
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("mla_flash_attend", lib().mla_flash_attend(ctypes.byref(shape), _ptr(q_abs), q_n_frames, _ptr(cache),
-                                                      _ptr(slot_frame), _ptr(tables), rope_t_first, rope_n_t,
+                                                      _ptr(slot_frame, "int32"), _ptr(tables, "float32"), rope_t_first, rope_n_t,
                                                       _ptr(o_lat), kv_splits, _ptr(workspace), nbytes,
                                                       _stream(stream)))
 
@@ -187,7 +199,7 @@ def chunk_attend(shape: MlaShape, q_nope, q_r, q_frame_first: int, q_n_frames: i
     nbytes = workspace.numel() * workspace.element_size()
     _check("mla_chunk_attend", lib().mla_chunk_attend(ctypes.byref(shape), _ptr(q_nope), _ptr(q_r), q_frame_first,
                                                       q_n_frames, _ptr(w_uk), _ptr(w_uv), _ptr(cache),
-                                                      _ptr(slot_frame), _ptr(tables), rope_t_first, rope_n_t,
+                                                      _ptr(slot_frame, "int32"), _ptr(tables, "float32"), rope_t_first, rope_n_t,
                                                       _ptr(out), _ptr(workspace), nbytes, _stream(stream)))
 
 
@@ -200,7 +212,7 @@ def chunk_attend_heads(shape: MlaShape, q_nope, q_r, q_frame_first: int, q_n_fra
     nbytes = workspace.numel() * workspace.element_size()
     _check("mla_chunk_attend_heads",
            lib().mla_chunk_attend_heads(ctypes.byref(shape), _ptr(q_nope), _ptr(q_r), q_frame_first, q_n_frames,
-                                        _ptr(w_uk), _ptr(w_uv), _ptr(cache), _ptr(slot_frame), _ptr(tables),
+                                        _ptr(w_uk), _ptr(w_uv), _ptr(cache), _ptr(slot_frame, "int32"), _ptr(tables, "float32"),
                                         rope_t_first, rope_n_t, _ptr(out), _ptr(workspace), nbytes,
                                         _stream(stream)))
 
@@ -211,8 +223,8 @@ def chunk_attend_frame_causal(shape: MlaShape, q_nope, q_r, q_frame_first: int, 
     nbytes = workspace.numel() * workspace.element_size()
     _check("mla_chunk_attend_frame_causal",
            lib().mla_chunk_attend_frame_causal(ctypes.byref(shape), _ptr(q_nope), _ptr(q_r), q_frame_first,
-                                               q_n_frames, _ptr(w_uk), _ptr(w_uv), _ptr(cache), _ptr(slot_frame),
-                                               _ptr(tables), rope_t_first, rope_n_t, _ptr(out), _ptr(workspace),
+                                               q_n_frames, _ptr(w_uk), _ptr(w_uv), _ptr(cache), _ptr(slot_frame, "int32"),
+                                               _ptr(tables, "float32"), rope_t_first, rope_n_t, _ptr(out), _ptr(workspace),
                                                nbytes, _stream(stream)))
 
 
@@ -232,7 +244,7 @@ def layer_weights_struct(w: dict) -> MlaLayerWeights:
     """A layer's weight tensors (dict of device tensors) as the ABI's struct;
     w_qabs is optional (absent: the unfused query path)."""
     names = ("w_dkv", "w_kr", "w_dq", "w_uq", "w_qr", "w_uk", "w_uv", "w_o", "w_qabs")
-    return MlaLayerWeights(*[w[k].data_ptr() if w.get(k) is not None else None for k in names])
+    return MlaLayerWeights(*[_ptr(w.get(k)) for k in names])
 
 
 def layer_step_workspace_bytes(shape: MlaShape, d_cq: int, n_frames: int) -> int:
@@ -245,7 +257,7 @@ def layer_step(shape: MlaShape, d_cq: int, weights: MlaLayerWeights, x, frame_fi
     nbytes = workspace.numel() * workspace.element_size()
     _check("mla_layer_step",
            lib().mla_layer_step(ctypes.byref(shape), d_cq, ctypes.byref(weights), _ptr(x), frame_first, n_frames,
-                                _ptr(cache), _ptr(slot_frame), _ptr(tables), rope_t_first, rope_n_t,
+                                _ptr(cache), _ptr(slot_frame, "int32"), _ptr(tables, "float32"), rope_t_first, rope_n_t,
                                 1 if frame_causal else 0, _ptr(u), _ptr(workspace), nbytes, _stream(stream)))
 
 
@@ -259,5 +271,5 @@ def query_project_absorbed(shape: MlaShape, d_cq: int, x, q_frame_first: int, n_
                            rope_t_first: int, rope_n_t: int, c_q, q_abs, stream=None) -> None:
     _check("mla_query_project_absorbed",
            lib().mla_query_project_absorbed(ctypes.byref(shape), d_cq, _ptr(x), q_frame_first, n_frames, _ptr(w_dq),
-                                            _ptr(w_qabs), _ptr(tables), rope_t_first, rope_n_t, _ptr(c_q),
+                                            _ptr(w_qabs), _ptr(tables, "float32"), rope_t_first, rope_n_t, _ptr(c_q),
                                             _ptr(q_abs), _stream(stream)))

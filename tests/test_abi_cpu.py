@@ -135,3 +135,43 @@ def test_entry_points_reject_bad_arguments_before_launch(built_lib):
     bad = _shape(d_c=96)
     assert lib.mla_cache_write(ctypes.byref(bad), fake, fake, fake, 0, 3, fake, fake, None) == 6
     assert lib.mla_shape_check(None) == 1
+
+
+def test_binding_refuses_host_strided_and_mistyped_tensors():
+    """The Python binding passes only dense GPU buffers: a tensor in host
+    memory, a strided view or a slot table / RoPE table of another element
+    type is refused before the library is called (a host address handed to
+    a kernel would fault the GPU)."""
+    import torch
+
+    s = mla.make_shape(get_config("wan_small"))
+    host = torch.zeros(4, 4)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        mla.cache_write(s, host, host, host, 0, 1, host, host)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        mla.layer_weights_struct({"w_dkv": host})
+    # the contiguity and dtype checks run on tensors that claim to be on the GPU
+    class _Fake:
+        is_cuda = True
+
+        def __init__(self, contiguous=True, dtype="torch.bfloat16"):
+            self._c, self.dtype = contiguous, dtype
+
+        def is_contiguous(self):
+            return self._c
+
+        def stride(self):
+            return (1, 4)
+
+        def data_ptr(self):
+            return 256
+
+    from latent_kv_attention_amd._lib import _ptr
+    with pytest.raises(ValueError, match="contiguous"):
+        _ptr(_Fake(contiguous=False))
+    with pytest.raises(ValueError, match="int32"):
+        _ptr(_Fake(dtype="torch.int64"), "int32")
+    with pytest.raises(ValueError, match="float32"):
+        _ptr(_Fake(dtype="torch.bfloat16"), "float32")
+    assert _ptr(_Fake(dtype="torch.int32"), "int32").value == 256
+    assert _ptr(None) is None
