@@ -569,6 +569,27 @@ def test_wan_full_size_sampled_rows():
     assert_step_close(got[rows], ref, cfg.dtype, label="wan full size, sampled rows")
 
 
+def test_wan_maximum_window_sampled_rows():
+    """The largest window the library accepts (64 frames: 99,840 latent keys
+    at the Wan grid, 780 key tiles per row block) with the Wan head shapes:
+    a 3-frame chunk at frames 61..63 over the full ring, sampled rows checked
+    by the oracle (all heads, full window)."""
+    cfg = get_config("wan").with_(name="wan_window64", window_frames=64)
+    w, wd = device_weights(cfg, seed=9)
+    st = Stream(cfg, seed=9, pooled=True)
+    memo = LatentMemo(cfg, w, st)
+    layer = LatentLayer(cfg, wd, batch=1, rope_n_t=64)
+    for f0 in range(0, 64, 16):
+        layer.write(to_torch(st.xs(f0, 16)[None], cfg.dtype), f0, 16)
+    qn, qr = st.q(61)
+    out = layer.attend(to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype), 61, 3)
+    _sync()
+    assert sorted(layer.slot_frame.cpu().numpy()[0].tolist()) == list(range(64))
+    rows = sample_rows(cfg, 32, seed=64)
+    ref = oracle_rows_memo(cfg, w, memo, range(64), qn, qr, 61, rows)
+    assert_step_close(to_numpy(out)[0][rows], ref, cfg.dtype, label="wan, 64-frame window, sampled rows")
+
+
 def test_wan_window_fill_over_chunks_and_layers():
     """Thirty-layer chunk step shape: each layer has its own weights and ring;
     chunk k writes frames 3k..3k+2 and attends over frames 0..3k+2 (window
