@@ -564,7 +564,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "this build has no multi-GPU path.", file=sys.stderr)
+              "the library has no multi-GPU path (independent streams shard over GPUs with no exchange).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
