@@ -29,6 +29,7 @@ METRIC = "MLA chunk-attention TFLOP/s + cache-write GB/s, Wan-1.3B shape, 1 MI35
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak (AMD spec)
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "flash_mla_wan_traffic.json")
+CEILING_LIB = os.path.join(ROOT, "latent_kv_attention_amd", "libmla355_ceiling.so")
 # sources of the attention entry point's kernels and of its work split; the
 # committed traffic record is used only while these are unchanged
 FLASH_SOURCES = ["latent_kv_attention_amd/csrc/flash_mla.hip", "latent_kv_attention_amd/csrc/mla_common.hpp",
@@ -47,6 +48,47 @@ def flash_source_hash() -> str:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def mfma_ceiling(iters: int = 20000, reps: int = 5):
+    """Dense bf16 matrix-core rate of a pure product loop (no memory or LDS
+    traffic) in the attention kernel's occupancy: one 512-thread work-group
+    per compute unit, 8 independent accumulators per wave. HIP events on the
+    launch stream around single launches, median of `reps`. None when the
+    probe library has not been built."""
+    import ctypes
+    import numpy as np
+    import torch
+    if not os.path.exists(CEILING_LIB):
+        return None
+    lib = ctypes.CDLL(CEILING_LIB)
+    lib.mla_ceiling_flops.restype = ctypes.c_double
+    lib.mla_ceiling_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.mla_ceiling_run.restype = ctypes.c_int32
+    lib.mla_ceiling_run.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run(n):
+        rc = lib.mla_ceiling_run(blocks, n, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"mla_ceiling_run failed: {rc}")
+
+    run(1000)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run(iters)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ms = float(np.median(ts))
+    tflops = lib.mla_ceiling_flops(blocks, iters) / (ms * 1e-3) / 1e12
+    return {"what": f"pure v_mfma_f32_16x16x32_bf16 loop, {blocks} work-groups x 8 waves (2 per SIMD)",
+            "ms": round(ms, 4), "TFLOPs": round(tflops, 1), "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
 
 
 def step_flops(cfg):
@@ -546,9 +588,15 @@ def main():
                          "(wan_rollout) workloads, or only those named (report lines) and exit")
     ap.add_argument("--latent-sweep", action="store_true",
                     help="time the step at every latent width with kernels (one report line each) and exit")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only time the pure matrix-core loop (the attainable bf16 rate) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (to scale HBM byte counters) and exit")
     args = ap.parse_args()
+
+    if args.mfma_ceiling:
+        print(json.dumps({"mfma_attainable": mfma_ceiling()}), flush=True)
+        return
 
     if args.copy_calibration:
         import torch
@@ -659,6 +707,7 @@ def main():
     fl = step_flops(cfg)
     cw_bytes = cache_write_bytes(cfg)
     flash_tflops = fl["flash"] / (per["flash_attend"] * 1e-3) / 1e12
+    ceiling = mfma_ceiling()
     traffic = None
     if os.path.exists(COUNTERS_FILE):
         rec = json.load(open(COUNTERS_FILE))
@@ -686,7 +735,9 @@ def main():
         "roofline": {"kernel": "mla_flash_attend (" + " + ".join(FLASH_KERNELS) + ")", "bound": "mfma",
                      "achieved": round(flash_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(flash_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "flops_per_launch": fl["flash"]},
+                     "traffic": traffic, "flops_per_launch": fl["flash"],
+                     "frac_of_attainable": round(flash_tflops / ceiling["TFLOPs"], 4) if ceiling else None},
+        "mfma_attainable": ceiling,
         "cache_write_GBps": round(cw_bytes / (per["cache_write"] * 1e-3) / 1e9, 1),
         "cache_write_cold_GBps": round(cw_bytes / (cold * 1e-3) / 1e9, 1) if cold else None,
         "cache_write_hbm_frac_cold": round(cw_bytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4) if cold else None,

@@ -22,6 +22,11 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["mla_abi.hip", "rope_tables.hip", "cache_write.hip", "absorb_q.hip", "flash_mla.hip", "up_v.hip",
            "heads_mha.hip", "proj_gemm.hip"]
 
+# The matrix-core ceiling probe (a measurement aid for bench.py) goes into a
+# library of its own, so libmla355.so exports exactly what include/mla.h declares.
+CEILING_SOURCE = "mfma_ceiling.hip"
+CEILING_LIB_PATH = os.path.join(HERE, "libmla355_ceiling.so")
+
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU instructions.
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
@@ -70,12 +75,13 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
              verbose)
         return obj
 
-    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 4)))
+    jobs = jobs or min(len(SOURCES) + 1, max(1, (os.cpu_count() or 4)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB_PATH + ".tmp"
-    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB_PATH)
+        objs = list(ex.map(compile_one, SOURCES + [CEILING_SOURCE]))
+    for path, parts in ((LIB_PATH, objs[:-1]), (CEILING_LIB_PATH, objs[-1:])):
+        tmp = path + ".tmp"
+        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *parts], verbose)
+        os.replace(tmp, path)
     return LIB_PATH
 
 
