@@ -175,3 +175,24 @@ def test_binding_refuses_host_strided_and_mistyped_tensors():
         _ptr(_Fake(dtype="torch.bfloat16"), "float32")
     assert _ptr(_Fake(dtype="torch.int32"), "int32").value == 256
     assert _ptr(None) is None
+
+
+def test_ceiling_probe_library_loads_and_checks_arguments():
+    """The matrix-core ceiling probe (its own library, used by bench.py) loads,
+    counts its FLOPs as documented, and refuses out-of-range launches before
+    any HIP call."""
+    from latent_kv_attention_amd import build as _build
+    if not os.path.exists(_build.CEILING_LIB_PATH):
+        _build.build()
+    lib = ctypes.CDLL(_build.CEILING_LIB_PATH)
+    lib.mla_ceiling_flops.restype = ctypes.c_double
+    lib.mla_ceiling_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.mla_ceiling_run.restype = ctypes.c_int32
+    lib.mla_ceiling_run.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.mla_ceiling_flops(256, 20000) == 256 * 8 * 20000 * 8 * 2 * 16 * 16 * 32
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.mla_ceiling_run(0, 10, fake, None) == 1
+    assert lib.mla_ceiling_run(256, 0, fake, None) == 1
+    assert lib.mla_ceiling_run(256, 10, None, None) == 1
+    # the attention library does not carry the probe
+    assert not hasattr(mla.lib(), "mla_ceiling_run")
