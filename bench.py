@@ -110,20 +110,40 @@ def cache_write_bytes(cfg):
     return e * (cfg.n_q * cfg.hidden + (cfg.d_c + cfg.d_rope) * cfg.hidden + cfg.n_q * (cfg.d_c + cfg.d_rope))
 
 
-def cpu_baseline(cfg, sample_tokens: int, seed: int = 0):
+def cpu_model() -> str:
+    """Model name of the host CPU, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# worker threads the oracle may use: the host CPUs this process may run on,
+# at most 16 (the CPU share of one GPU on the machines this runs on)
+CPU_THREAD_CAP = 16
+
+
+def cpu_baseline(cfg, sample_tokens: int, seed: int = 0, gpu_out=None):
     """The fp64 oracle as it stands, on a bounded sample of the same workload:
     latents of the whole 21-frame window, explicit per-head reconstruction of
     every key and value, and attention for the first `sample_tokens` query
     tokens of the chunk (all heads, full window). Credited with the absorbed-
     path FLOPs of that sample (cache write of the chunk + attention of those
-    rows), so the rate is in the metric's unit."""
+    rows), so the rate is in the metric's unit. With gpu_out (the timed
+    step's output, same seeded inputs) the oracle rows are also compared with
+    it element by element."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
 
     from harness import chunk_queries, frame_tokens, layer_weights
     from oracle import mla_oracle as O
 
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    affinity = len(os.sched_getaffinity(0))
+    cores = min(affinity, CPU_THREAD_CAP)
     w = layer_weights(cfg, seed)
     frames = list(range(cfg.window_frames))
     xs = [frame_tokens(cfg, f, seed) for f in frames]
@@ -139,17 +159,27 @@ def cpu_baseline(cfg, sample_tokens: int, seed: int = 0):
         rows = np.arange(sample_tokens)
         tq, yq, xq = O.frame_positions(chunk_first + np.arange(cfg.chunk_frames), cfg.grid_y, cfg.grid_x)
         q_rope = O.rope3d(qr[rows], tq[rows], yq[rows], xq[rows], cfg.rope_split, cfg.rope_base)
-        O.attend(qn[rows], q_rope, k_nope, k_rope, v, O.default_scale(cfg.d_head, cfg.d_rope))
+        ref = O.attend(qn[rows], q_rope, k_nope, k_rope, v, O.default_scale(cfg.d_head, cfg.d_rope))
         dt = time.perf_counter() - t0
     fl = step_flops(cfg)
     frac = sample_tokens / cfg.n_q
     credited = fl["cache_write"] + frac * (fl["absorb"] + fl["flash"] + fl["up_v"])
-    return {"value": credited / dt / 1e12, "unit": "TFLOP/s", "cores": int(min(cores, used)), "kind": "oracle",
-            "sample": f"fp64 oracle: latents of 21 frames x 1560 tokens, per-head reconstruction of all "
-                      f"32760 keys and values, attention of the first {sample_tokens} of 4680 query tokens "
-                      f"(all 12 heads, full window); {dt:.2f} s, credited with the chunk cache write plus "
-                      f"{sample_tokens}/4680 of the attention-side FLOPs",
-            "seconds": round(dt, 3)}
+    res = {"value": credited / dt / 1e12, "unit": "TFLOP/s", "cores": int(min(cores, used)), "kind": "oracle",
+           "sample": f"fp64 oracle: latents of 21 frames x 1560 tokens, per-head reconstruction of all "
+                     f"32760 keys and values, attention of the first {sample_tokens} of 4680 query tokens "
+                     f"(all 12 heads, full window); {dt:.2f} s, credited with the chunk cache write plus "
+                     f"{sample_tokens}/4680 of the attention-side FLOPs",
+           "seconds": round(dt, 3), "cpu_model": cpu_model(), "host_logical_cpus": os.cpu_count(),
+           "affinity_cpus": affinity, "thread_cap": CPU_THREAD_CAP}
+    if gpu_out is not None:
+        got = np.asarray(gpu_out, np.float64)[:sample_tokens]
+        d = np.abs(got - ref)
+        res["parity_vs_gpu_out"] = {
+            "outputs_compared": int(d.size), "max_abs": float(d.max()), "mean_abs": float(d.mean()),
+            "rel_rms": float(np.linalg.norm(got - ref) / np.linalg.norm(ref)),
+            "gates": {"max_abs": 2e-2, "mean_abs": 2e-3, "rel_rms": 1e-2},
+            "pass": bool(d.max() <= 2e-2 and d.mean() <= 2e-3 and np.linalg.norm(got - ref) <= 1e-2 * np.linalg.norm(ref))}
+    return res
 
 
 def setup_step(cfg, kv_splits, dev="cuda"):
@@ -755,7 +785,7 @@ def main():
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline: oracle on {args.cpu_sample_tokens} query tokens", file=sys.stderr,
               flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens, gpu_out=ctx.out.float().cpu().numpy())
     print(json.dumps(result), flush=True)
 
 

@@ -167,9 +167,11 @@ mla_status mla_absorb_q(const mla_shape* shape, const void* q_nope, const void* 
  * over every key j of every slot of stream b with slot_frame[b][s] >= 0
  * (no intra-chunk mask); rows with no valid key get zeros.
  *   q_abs (device) [B][N_q][H][Q] from mla_absorb_q; cache, slot_frame as
- *   written by mla_cache_write; rope_tables as for mla_absorb_q (every
- *   frame held in the window must lie in the table range: frames outside it
- *   are read from the clamped table row, a wrong but memory-safe result).
+ *   written by mla_cache_write; rope_tables from mla_rope3d_tables (any
+ *   rope_t_first >= 0, rope_n_t >= 1): the keys' spatial angles are read from
+ *   them, while the temporal angles of the frames held in the window are
+ *   formed during the call by the same computation the tables use, so window
+ *   frames need not lie in the table's range.
  *   o_lat (device) [B][N_q][H][d_c], dtype.
  *   workspace (device) of at least mla_flash_workspace_bytes(shape,
  *   q_n_frames, kv_splits) bytes; its contents on entry do not matter. The
@@ -191,6 +193,20 @@ mla_status mla_flash_attend(const mla_shape* shape, const void* q_abs, int32_t q
                             const int32_t* slot_frame, const float* rope_tables, int32_t rope_t_first,
                             int32_t rope_n_t, void* o_lat, int32_t kv_splits, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- a4, frame-causal
+ * mla_flash_attend under the frame-causal mask inside the chunk (the
+ * chunk-wise autoregressive reading of the hyper.ai summary, Method, and the
+ * chatpaper.ai abstract): the row of query token i (frame
+ * q_frame_first + i / T) takes only the keys of slots holding frames
+ * <= that frame; a row with no such key gets zeros. Same arguments,
+ * workspace (mla_flash_workspace_bytes) and errors as mla_flash_attend,
+ * plus q_frame_first >= 0 (else MLA_ERR_RANGE). */
+mla_status mla_flash_attend_frame_causal(const mla_shape* shape, const void* q_abs, int32_t q_frame_first,
+                                         int32_t q_n_frames, const void* cache, const int32_t* slot_frame,
+                                         const float* rope_tables, int32_t rope_t_first, int32_t rope_n_t,
+                                         void* o_lat, int32_t kv_splits, void* workspace, size_t workspace_bytes,
+                                         void* stream);
 
 /* ---------------------------------------------------------------- a5
  * Value up-projection (hyper.ai summary, Method: v = W_uv[h] c, so

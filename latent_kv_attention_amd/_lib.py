@@ -24,7 +24,7 @@ STATUS = {
 EXPORTS = [
     "mla_abi_version", "mla_status_string", "mla_shape_check", "mla_qabs_dim",
     "mla_rope3d_table_floats", "mla_rope3d_tables", "mla_cache_write", "mla_absorb_q",
-    "mla_flash_workspace_bytes", "mla_flash_attend", "mla_up_v",
+    "mla_flash_workspace_bytes", "mla_flash_attend", "mla_flash_attend_frame_causal", "mla_up_v",
     "mla_chunk_attend_workspace_bytes", "mla_chunk_attend",
     "mla_chunk_attend_heads_workspace_bytes", "mla_chunk_attend_heads", "mla_chunk_attend_frame_causal",
     "mla_query_project", "mla_output_project", "mla_layer_step_workspace_bytes", "mla_layer_step",
@@ -68,6 +68,7 @@ _SIGS = {
     "mla_absorb_q": (_I, [_SP, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P]),
     "mla_flash_workspace_bytes": (_SZ, [_SP, _I, _I]),
     "mla_flash_attend": (_I, [_SP, _P, _I, _P, _P, _P, _I, _I, _P, _I, _P, _SZ, _P]),
+    "mla_flash_attend_frame_causal": (_I, [_SP, _P, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P, _SZ, _P]),
     "mla_up_v": (_I, [_SP, _P, _I, _P, _P, _P]),
     "mla_chunk_attend_workspace_bytes": (_SZ, [_SP, _I]),
     "mla_chunk_attend": (_I, [_SP, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
@@ -183,6 +184,17 @@ def flash_attend(shape: MlaShape, q_abs, q_n_frames: int, cache, slot_frame, tab
                                                       _ptr(slot_frame, "int32"), _ptr(tables, "float32"), rope_t_first, rope_n_t,
                                                       _ptr(o_lat), kv_splits, _ptr(workspace), nbytes,
                                                       _stream(stream)))
+
+
+def flash_attend_frame_causal(shape: MlaShape, q_abs, q_frame_first: int, q_n_frames: int, cache, slot_frame,
+                              tables, rope_t_first: int, rope_n_t: int, o_lat, workspace, kv_splits: int = 0,
+                              stream=None) -> None:
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("mla_flash_attend_frame_causal",
+           lib().mla_flash_attend_frame_causal(ctypes.byref(shape), _ptr(q_abs), q_frame_first, q_n_frames,
+                                               _ptr(cache), _ptr(slot_frame, "int32"), _ptr(tables, "float32"),
+                                               rope_t_first, rope_n_t, _ptr(o_lat), kv_splits, _ptr(workspace),
+                                               nbytes, _stream(stream)))
 
 
 def up_v(shape: MlaShape, o_lat, q_n_frames: int, w_uv, out, stream=None) -> None:

@@ -20,7 +20,10 @@
 // block starts from -r_i instead of 0), so a probability costs one exp2; no
 // running maximum is tracked and the output accumulators are never rescaled.
 // A row whose probability sum exceeds 2^100 (a logit gap beyond ~70 nats) is
-// listed and recomputed by an exact two-pass kernel.
+// listed and recomputed by an exact two-pass kernel. Under the frame-causal
+// mask a row may see none of its first 32 keys; it then takes the maximum of
+// those (invisible) scores, its visible probabilities can underflow, and a
+// row that sees keys but sums below 2^-100 is listed as well.
 //
 // Layout of the work (bf16):
 //   * the 12 heads of a query are consecutive rows (all heads share the
@@ -62,7 +65,8 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
-constexpr float kSumLimit = 1.2676506e30f;  // 2^100
+constexpr float kSumLimit = 0x1p100f;
+constexpr float kSumMin = 0x1p-100f;
 }  // namespace
 
 // bf16: 8 waves x 32 rows (two waves per SIMD) and 128-key tiles; float
@@ -121,26 +125,40 @@ struct FlashTile {
 // rank r, token tok) of stream b gets R(t, y, x) kR, with t the frame held
 // by the r-th valid slot and (y, x) the token's grid cell, rounded to the
 // cache's element type. Row v of the stream's block of p.krot. One thread per
-// rotary pair; grid (pair blocks, slots, stream groups). It also clears the
-// count of rows handed to the exact fallback.
+// rotary pair; grid (pair blocks, slots, stream groups). The temporal angles
+// of the slot's frame are formed here (any frame index; the caller's tables
+// only need to cover the query frames), the spatial ones come from the
+// tables. It also clears the count of rows handed to the exact fallback.
 template <typename T, int DC, int DR>
 __global__ __launch_bounds__(256) void rope_window_kernel(FlashParams p) {
   constexpr int NP = DR / 2;
+  __shared__ float t_cs[2][NP];  // cos, sin of the temporal pairs at the slot's frame
   if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *p.fallback_count = 0;
   const int slot = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= p.T * NP) return;
+  const bool active = e < p.T * NP;
   const int tok = e / NP, k = e - tok * NP;
   const int y = tok / p.grid_x, x = tok - y * p.grid_x;
+  const int n_tp = p.rl.d_t / 2;
   for (int b = blockIdx.z; b < p.batch; b += gridDim.z) {
     const int32_t* sf = p.slot_frame + (size_t)b * p.W;
-    const int f = sf[slot];
+    const int f = sf[slot];  // uniform over the work-group
     if (f < 0) continue;
+    __syncthreads();  // the previous stream's angles are no longer read
+    if ((int)threadIdx.x < n_tp) rope_axis_cos_sin(p.rope_base, f, threadIdx.x, p.rl.d_t, &t_cs[0][threadIdx.x],
+                                                   &t_cs[1][threadIdx.x]);
+    __syncthreads();
+    if (!active) continue;
     int rank = 0;
     for (int j = 0; j < slot; ++j) rank += sf[j] >= 0 ? 1 : 0;
     const T* src = (const T*)p.cache + (((size_t)b * p.W + slot) * p.T + tok) * (DC + DR) + DC + 2 * k;
     float a0 = to_f<T>(src[0]), a1 = to_f<T>(src[1]), cs, sn;
-    rope_cos_sin(p.rl, p.tables, k, f, y, x, cs, sn);
+    if (k < n_tp) {
+      cs = t_cs[0][k];
+      sn = t_cs[1][k];
+    } else {
+      rope_cos_sin(p.rl, p.tables, k, 0, y, x, cs, sn);
+    }
     rotate_pair(a0, a1, cs, sn);
     T* dst = (T*)p.krot + ((size_t)b * p.W * p.T + (size_t)rank * p.T + tok) * DR + 2 * k;
     dst[0] = to_t<T>(a0);
@@ -171,7 +189,10 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
   __shared__ int frame_of[kMaxSlots];  // frame held by the r-th valid slot (frame-causal variant)
   __shared__ int n_valid_sh;
   __shared__ int keytab[2][kBN];  // per key of a tile: byte offset of its cache row
-  __shared__ int keyfr[CAUSAL ? 2 : 1][CAUSAL ? kBN : 1];  // per key of a tile: its frame (frame-causal variant)
+  // per key of a tile: its frame (frame-causal variant), for position p in
+  // entry p mod 3: the descriptors of position p + 2 are written while tile p
+  // is masked, and tile p + 1's are read in the next step
+  __shared__ int keyfr[CAUSAL ? 3 : 1][CAUSAL ? kBN : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -314,7 +335,7 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
         const int rank = div_floor(v, p.T, p.inv_T), tok = v - rank * p.T;
         if (ln < kBN) {
           tab[ln] = (slot_of[rank] * p.T + tok) * F::DK * (int)sizeof(T);
-          if constexpr (CAUSAL) keyfr[tab == keytab[0] ? 0 : 1][ln] = frame_of[rank];
+          if constexpr (CAUSAL) keyfr[pos % 3][ln] = frame_of[rank];
         }
       }
     };
@@ -445,7 +466,7 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
           if constexpr (CAUSAL) {
             // scores of keys from frames after the row's frame drop out
             if (masked) {
-              const int* kfr = keyfr[CAUSAL ? CUR : 0] + half * 32;
+              const int* kfr = keyfr[CAUSAL ? pos % 3 : 0] + half * 32;
 #pragma unroll
               for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -535,6 +556,28 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     }
 
     // ---- epilogue
+    // Does row mb see any key of this segment? Every visited key for the
+    // unmasked kernel; for the frame-causal one, any key whose frame is at
+    // most the row's (skipped tiles hold none: their frames exceed every
+    // frame of the row block). A row that sees keys but whose sum stayed
+    // below 2^-100 took its reference from keys it cannot see (none of its
+    // first 32 visited keys was visible) and may have lost its visible
+    // probabilities to underflow; like an overflowing row it goes to the
+    // exact fallback.
+    bool sees[kNMB];
+    if constexpr (CAUSAL) {
+      int fmin_seg = 0x7fffffff;  // earliest frame among the visited keys
+      if (n_visit > 0) {
+        const int r_lo = div_floor(tile_begin * kBN, p.T, p.inv_T);
+        const int r_hi = div_floor(min(tile_end * kBN, n_keys) - 1, p.T, p.inv_T);
+        for (int r = r_lo; r <= r_hi; ++r) fmin_seg = min(fmin_seg, frame_of[r]);
+      }
+#pragma unroll
+      for (int mb = 0; mb < kNMB; ++mb) sees[mb] = fmin_seg <= qfr[mb];
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < kNMB; ++mb) sees[mb] = n_visit > 0;
+    }
     const int eln = opaque(lane);
     const int eli = eln & 15, elg = eln >> 4;
 #pragma unroll
@@ -542,9 +585,10 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
       const float l = wave_sum_across_groups(l_run[mb]);
       const int row = rb * F::kRowsBlock + wave * F::kRowsWave + mb * 16 + eli;
       if (row >= p.Mb) continue;
+      // false for inf / NaN as well
+      const bool ok = l <= kSumLimit && (l >= kSumMin || !sees[mb]);
+      const float inv = (ok && l > 0.f) ? 1.f / l : 0.f;
       if (whole) {
-        const bool ok = l <= kSumLimit;  // false for inf / NaN as well
-        const float inv = (ok && l > 0.f) ? 1.f / l : 0.f;
         T* dst = (T*)p.o_lat + ((size_t)b * p.Mb + row) * DC;
 #pragma unroll
         for (int db = 0; db < F::NDB; ++db)
@@ -553,20 +597,20 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
         if (!ok && elg == 0) p.fallback_rows[atomicAdd(p.fallback_count, 1)] = b * p.Mb + row;
       } else {
         // partial output normalised by its own sum (values of the size of
-        // the latent, so the cache's element type holds them), plus the
-        // reference and the sum in float for the merge
+        // the latent, so the cache's element type holds them), plus, in
+        // float for the merge, log2 of the piece's total weight (reference +
+        // log2 of the sum; -inf for a piece without keys the row sees) and a
+        // status (+inf when the row needs the exact fallback)
         const size_t prow = ((size_t)blockIdx.x * 2 + (first_seg ? 0 : 1)) * F::kRowsBlock + row - rb * F::kRowsBlock;
-        const bool ok = l <= kSumLimit;
-        const float inv = (ok && l > 0.f) ? 1.f / l : 0.f;
         T* dst = (T*)p.part_o + prow * DC;
 #pragma unroll
         for (int db = 0; db < F::NDB; ++db)
 #pragma unroll
           for (int i = 0; i < 4; ++i) dst[db * 16 + elg * 4 + i] = to_t<T>(o[db][mb][i] * inv);
         if (elg == 0) {
-          const bool empty = n_visit == 0;  // no keys: weight 0 in the merge
-          p.part_l[prow * 2] = empty ? -__builtin_inff() : -negref[mb][0];
-          p.part_l[prow * 2 + 1] = l;
+          const bool weighted = ok && l > 0.f;
+          p.part_l[prow * 2] = weighted ? -negref[mb][0] + __builtin_amdgcn_logf(l) : -__builtin_inff();
+          p.part_l[prow * 2 + 1] = ok ? 0.f : __builtin_inff();
         }
       }
     }
@@ -575,8 +619,13 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
 
 // Merge of the partial results of a row block shared by work-groups
 // g0..g1 (the work-groups whose unit ranges meet the row block's units
-// [a, a + nt_max)): with M = max_g r_g and w_g = 2^(r_g - M), and each piece
-// stored as o_g / l_g, o = sum_g w_g l_g (o_g / l_g) / sum_g w_g l_g.
+// [a, a + nt_max)). Piece g holds o_g / l_g and lw_g = r_g + log2 l_g, the
+// log2 of its total weight sum_j 2^(s_j) (r_g its reference); with
+// M = max_g lw_g and w_g = 2^(lw_g - M) <= 1 the row is
+// o = sum_g w_g (o_g / l_g) / sum_g w_g. The heaviest piece has w_g = 1, so
+// a piece can only underflow when its share is below 2^-126; pieces with no
+// key the row sees have lw_g = -inf and weigh 0. A piece flagged for the
+// exact fallback (status > 2^100) sends the whole row there.
 // Work-group g's piece sits in its slot 0 when its range starts inside the
 // row block, else in its slot 1. A work-group takes kMergeRows rows of one
 // row block: the piece bookkeeping is computed once (uniform), then threads
@@ -619,7 +668,7 @@ __global__ __launch_bounds__(256) void flash_combine_kernel(FlashParams p) {
     if (M > -__builtin_inff()) {
       for (int k = 0; k < np; ++k) {
         const size_t pr = (size_t)slot_base[k] + local;
-        const float wl = fast_exp2(p.part_l[pr * 2] - M) * p.part_l[pr * 2 + 1];
+        const float wl = fast_exp2(p.part_l[pr * 2] - M);
         L += wl;
         const chunk_t raw = *reinterpret_cast<const chunk_t*>((const T*)p.part_o + pr * DC + c0);
         float v[CH];
@@ -686,21 +735,18 @@ __global__ __launch_bounds__(256) void flash_exact_kernel(FlashParams p) {
     __syncthreads();
     const int n_keys = n_valid_sh * p.T;
     const T* cache_b = (const T*)p.cache + (size_t)b * p.W * p.T * DK;
+    // the window's rotated positional keys, as the main kernel read them
+    const T* krot_b = (const T*)p.krot + (size_t)b * p.W * p.T * DR;
     // frame-causal variant: keys of frames after the row's query frame are skipped
     const int qframe = p.q_frame_first + (grow - b * p.Mb) / (p.T * p.H);
     auto visible = [&](int v) { return !CAUSAL || frame_of[v / p.T] <= qframe; };
     auto score = [&](int v) {
       const int rank = v / p.T, tok = v - rank * p.T;
       const T* row = cache_b + ((size_t)slot_of[rank] * p.T + tok) * DK;
-      const int y = tok / p.grid_x, x = tok - y * p.grid_x;
+      const T* kr = krot_b + (size_t)v * DR;
       float s = 0.f;
       for (int d = 0; d < DC; ++d) s += q[d] * to_f<T>(row[d]);
-      for (int k = 0; k < DR / 2; ++k) {
-        float a0 = to_f<T>(row[DC + 2 * k]), a1 = to_f<T>(row[DC + 2 * k + 1]), cs, sn;
-        rope_cos_sin(p.rl, p.tables, k, frame_of[rank], y, x, cs, sn);
-        rotate_pair(a0, a1, cs, sn);
-        s += q[DC + 2 * k] * to_f<T>(to_t<T>(a0)) + q[DC + 2 * k + 1] * to_f<T>(to_t<T>(a1));
-      }
+      for (int d = 0; d < DR; ++d) s += q[DC + d] * to_f<T>(kr[d]);
       return s;
     };
     // pass 1: exact maximum

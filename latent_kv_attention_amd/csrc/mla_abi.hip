@@ -223,6 +223,7 @@ mla_status do_flash(const mla_shape* s, const void* q_abs, int q_n_frames, const
   p.units = f.units;
   p.grid = f.grid;
   p.scale_log2 = scale_log2(s);
+  p.rope_base = (double)s->rope_base;
   p.H = s->n_heads;
   p.q_frame_first = q_frame_first;
   return from_hip(mla::launch_flash(s->dtype, s->d_c, s->d_rope, p, f.split, frame_causal, st));
@@ -405,23 +406,41 @@ MLA_API size_t mla_flash_workspace_bytes(const mla_shape* shape, int32_t q_n_fra
   return flash_ws_bytes(shape, q_n_frames, kv_splits);
 }
 
-MLA_API mla_status mla_flash_attend(const mla_shape* shape, const void* q_abs, int32_t q_n_frames, const void* cache,
-                                    const int32_t* slot_frame, const float* rope_tables, int32_t rope_t_first,
-                                    int32_t rope_n_t, void* o_lat, int32_t kv_splits, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
+static mla_status flash_attend_impl(const mla_shape* shape, const void* q_abs, int32_t q_frame_first,
+                                    int32_t q_n_frames, const void* cache, const int32_t* slot_frame,
+                                    const float* rope_tables, int32_t rope_t_first, int32_t rope_n_t, void* o_lat,
+                                    int32_t kv_splits, void* workspace, size_t workspace_bytes, void* stream,
+                                    bool frame_causal) {
   mla_status st = check_shape(shape);
   if (st != MLA_OK) return st;
   if (!q_abs || !cache || !slot_frame || !o_lat) return MLA_ERR_NULL;
   if (!aligned16(q_abs) || !aligned16(cache) || !aligned16(slot_frame) || !aligned16(o_lat)) return MLA_ERR_ALIGN;
   if ((st = check_tables(shape, rope_tables, rope_t_first, rope_n_t)) != MLA_OK) return st;
-  if ((st = check_query_args(shape, 0, q_n_frames)) != MLA_OK) return st;
+  if ((st = check_query_args(shape, q_frame_first, q_n_frames)) != MLA_OK) return st;
   if (kv_splits < 0 || kv_splits > kMaxSplits) return MLA_ERR_RANGE;
   if (!workspace) return MLA_ERR_NULL;
   if (!aligned16(workspace)) return MLA_ERR_ALIGN;
   if (!flash_plan_ok(flash_plan(shape, q_n_frames, kv_splits))) return MLA_ERR_SHAPE;
   if (workspace_bytes < flash_ws_bytes(shape, q_n_frames, kv_splits)) return MLA_ERR_WORKSPACE;
   return do_flash(shape, q_abs, q_n_frames, cache, slot_frame, rope_tables, rope_t_first, rope_n_t, o_lat, kv_splits,
-                  workspace, (hipStream_t)stream);
+                  workspace, (hipStream_t)stream, frame_causal, q_frame_first);
+}
+
+MLA_API mla_status mla_flash_attend(const mla_shape* shape, const void* q_abs, int32_t q_n_frames, const void* cache,
+                                    const int32_t* slot_frame, const float* rope_tables, int32_t rope_t_first,
+                                    int32_t rope_n_t, void* o_lat, int32_t kv_splits, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return flash_attend_impl(shape, q_abs, 0, q_n_frames, cache, slot_frame, rope_tables, rope_t_first, rope_n_t, o_lat,
+                           kv_splits, workspace, workspace_bytes, stream, false);
+}
+
+MLA_API mla_status mla_flash_attend_frame_causal(const mla_shape* shape, const void* q_abs, int32_t q_frame_first,
+                                                 int32_t q_n_frames, const void* cache, const int32_t* slot_frame,
+                                                 const float* rope_tables, int32_t rope_t_first, int32_t rope_n_t,
+                                                 void* o_lat, int32_t kv_splits, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+  return flash_attend_impl(shape, q_abs, q_frame_first, q_n_frames, cache, slot_frame, rope_tables, rope_t_first,
+                           rope_n_t, o_lat, kv_splits, workspace, workspace_bytes, stream, true);
 }
 
 MLA_API mla_status mla_up_v(const mla_shape* shape, const void* o_lat, int32_t q_n_frames, const void* w_uv,
@@ -573,6 +592,7 @@ MLA_API mla_status mla_chunk_attend_heads(const mla_shape* shape, const void* q_
   fp.grid_y = shape->grid_y;
   fp.grid_x = shape->grid_x;
   fp.batch = shape->batch;
+  fp.rope_base = (double)shape->rope_base;
   hipError_t e = mla::launch_rope_window(shape->dtype == MLA_BF16 ? 0 : 1, shape->d_c, shape->d_rope, fp, s);
   if (e != hipSuccess) return MLA_ERR_HIP;
   mla::HeadsParams p = {};

@@ -58,7 +58,7 @@ struct FlashParams {
   void* o_lat;             // [B][Mb][d_c]
   void* part_o;            // [G][2][rows per block][d_c] partial outputs o_g / l_g, element type of the
                            // cache (split row blocks only)
-  float* part_l;           // [G][2][rows per block][2] (reference, sum)
+  float* part_l;           // [G][2][rows per block][2] (log2 of the piece's weight, status)
   void* krot;              // [B][W * T][d_rope] rotated kR of each stream's valid keys, in key order
   int* fallback_count;     // rows listed for the exact fallback
   int* fallback_rows;      // [B * Mb]
@@ -71,6 +71,7 @@ struct FlashParams {
   long long units;         // batch * n_rb * nt_max
   int grid;                // G, work-groups of the attention kernel
   float scale_log2;        // softmax scale * log2(e)
+  double rope_base;        // RoPE base (the keys' temporal angles are formed per call)
 };
 
 constexpr int kFallbackBlocks = 64;

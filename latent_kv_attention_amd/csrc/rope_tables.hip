@@ -5,6 +5,7 @@
 // float once.
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
+#include "rope_device.hpp"
 
 namespace mla {
 
@@ -40,10 +41,10 @@ __global__ __launch_bounds__(256) void rope_tables_kernel(RopeTableParams p) {
     off_s = rl.off_sx;
     idx = q;
   }
-  const double inv_freq = pow(p.base, -2.0 * (double)i / (double)d);
-  const double ang = (double)pos * inv_freq;
-  p.tables[off_c + idx] = (float)cos(ang);
-  p.tables[off_s + idx] = (float)sin(ang);
+  float c, sn;
+  rope_axis_cos_sin(p.base, pos, i, d, &c, &sn);
+  p.tables[off_c + idx] = c;
+  p.tables[off_s + idx] = sn;
 }
 
 hipError_t launch_rope_tables(const RopeTableParams& p, hipStream_t s) {

@@ -29,17 +29,31 @@ class LatentLayer:
         self.cache = torch.zeros(self.B, cfg.window_frames, self.T, cfg.d_c + cfg.d_rope, dtype=self.dtype,
                                  device=device)
         self.slot_frame = torch.full((self.B, cfg.window_frames), -1, dtype=torch.int32, device=device)
-        self.rope_t_first, self.rope_n_t = rope_t_first, rope_n_t
-        self.tables = torch.empty(_lib.rope3d_table_floats(self.shape, rope_n_t), dtype=torch.float32,
-                                  device=device)
-        _lib.rope3d_tables(self.shape, rope_t_first, rope_n_t, self.tables)
         nf = max_chunk_frames or cfg.chunk_frames
+        # RoPE tables: the queries' frames must lie in their t range (the
+        # window keys' temporal angles are formed by the attention call for
+        # any frame); the range moves with the chunks (ensure_tables)
+        self.rope_t_first, self.rope_n_t = rope_t_first, max(rope_n_t, nf)
+        self.tables = torch.empty(_lib.rope3d_table_floats(self.shape, self.rope_n_t), dtype=torch.float32,
+                                  device=device)
+        _lib.rope3d_tables(self.shape, self.rope_t_first, self.rope_n_t, self.tables)
         self.max_chunk_frames = nf
         self.workspace = torch.empty(_lib.chunk_attend_workspace_bytes(self.shape, nf), dtype=torch.uint8,
                                      device=device)
         self.heads_workspace = None  # allocated on the first per-head call
         self.q_buffers = None        # query latent and queries, allocated on the first projection
         self.layer_workspace = None  # (d_cq, workspace, weight struct) of step(), allocated on its first call
+
+    def ensure_tables(self, frame_first: int, n_frames: int, stream=None) -> None:
+        """Move the tables' t range so that it covers frames frame_first ..
+        frame_first + n_frames - 1 (a rollout runs past any fixed range): the
+        range restarts at frame_first, same length, refilled on `stream`."""
+        if frame_first >= self.rope_t_first and frame_first + n_frames <= self.rope_t_first + self.rope_n_t:
+            return
+        if frame_first < 0 or n_frames > self.rope_n_t:
+            raise ValueError("query frames outside what the RoPE tables can cover")
+        self.rope_t_first = frame_first
+        _lib.rope3d_tables(self.shape, self.rope_t_first, self.rope_n_t, self.tables, stream)
 
     def write(self, x, frame_first: int, n_frames: int, stream=None) -> None:
         """Cache write of frames frame_first .. +n_frames (x [B][n_frames*T][hidden])."""
@@ -53,6 +67,7 @@ class LatentLayer:
         if out is None:
             out = torch.empty(self.B, q_n_frames * self.T, self.cfg.n_heads, self.cfg.d_head, dtype=self.dtype,
                               device=self.device)
+        self.ensure_tables(q_frame_first, q_n_frames, stream)
         _lib.chunk_attend(self.shape, q_nope, q_r, q_frame_first, q_n_frames, self.w["w_uk"], self.w["w_uv"],
                           self.cache, self.slot_frame, self.tables, self.rope_t_first, self.rope_n_t, out,
                           self.workspace, stream)
@@ -66,6 +81,7 @@ class LatentLayer:
         if out is None:
             out = torch.empty(self.B, q_n_frames * self.T, self.cfg.n_heads, self.cfg.d_head, dtype=self.dtype,
                               device=self.device)
+        self.ensure_tables(q_frame_first, q_n_frames, stream)
         _lib.chunk_attend_frame_causal(self.shape, q_nope, q_r, q_frame_first, q_n_frames, self.w["w_uk"],
                                        self.w["w_uv"], self.cache, self.slot_frame, self.tables, self.rope_t_first,
                                        self.rope_n_t, out, self.workspace, stream)
@@ -84,6 +100,7 @@ class LatentLayer:
         if out is None:
             out = torch.empty(self.B, q_n_frames * self.T, self.cfg.n_heads, self.cfg.d_head, dtype=self.dtype,
                               device=self.device)
+        self.ensure_tables(q_frame_first, q_n_frames, stream)
         _lib.chunk_attend_heads(self.shape, q_nope, q_r, q_frame_first, q_n_frames, self.w["w_uk"], self.w["w_uv"],
                                 self.cache, self.slot_frame, self.tables, self.rope_t_first, self.rope_n_t, out,
                                 self.heads_workspace, stream)
@@ -134,6 +151,7 @@ class LatentLayer:
         c_q = torch.empty(self.B, n, d_cq, dtype=self.dtype, device=self.device)
         q_abs = torch.empty(self.B, n, self.cfg.n_heads, _lib.qabs_dim(self.shape), dtype=self.dtype,
                             device=self.device)
+        self.ensure_tables(q_frame_first, n_frames, stream)
         _lib.query_project_absorbed(self.shape, d_cq, x, q_frame_first, n_frames, self.w["w_dq"], self.w["w_qabs"],
                                     self.tables, self.rope_t_first, self.rope_n_t, c_q, q_abs, stream)
         return c_q, q_abs
@@ -167,6 +185,7 @@ class LatentLayer:
                                     _lib.layer_weights_struct(self.w))
         if out is None:
             out = torch.empty(self.B, n_frames * self.T, self.cfg.hidden, dtype=self.dtype, device=self.device)
+        self.ensure_tables(frame_first, n_frames, stream)
         _lib.layer_step(self.shape, d_cq, self.layer_workspace[2], x, frame_first, n_frames, self.cache,
                         self.slot_frame, self.tables, self.rope_t_first, self.rope_n_t, frame_causal, out,
                         self.layer_workspace[1], stream)

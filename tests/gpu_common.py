@@ -68,8 +68,10 @@ def device_weights(cfg, seed=0, layer=0):
     return w, {k: to_torch(v, cfg.dtype) for k, v in w.items()}
 
 
-def oracle_step_rows(cfg, w, stream_frames_x: dict, window_frames, q_nope, q_r, q_frame_first, rows=None):
-    """Oracle output for the chosen query rows (all heads, full window)."""
+def oracle_step_rows(cfg, w, stream_frames_x: dict, window_frames, q_nope, q_r, q_frame_first, rows=None,
+                     frame_causal=False):
+    """Oracle output for the chosen query rows (all heads, full window; under
+    the frame-causal mask when asked)."""
     c_list, kr_list = [], []
     for f in window_frames:
         c, kr = O.latents(stream_frames_x[f], w["w_dkv"], w["w_kr"])
@@ -85,7 +87,9 @@ def oracle_step_rows(cfg, w, stream_frames_x: dict, window_frames, q_nope, q_r, 
     if rows is None:
         rows = np.arange(nq)
     q_rope = O.rope3d(q_r[rows], tq[rows], yq[rows], xq[rows], cfg.rope_split, cfg.rope_base)
-    return O.attend(q_nope[rows], q_rope, k_nope, k_rope, v, O.default_scale(cfg.d_head, cfg.d_rope))
+    visible = O.frame_causal_mask(tq[rows], t) if frame_causal else None
+    return O.attend(q_nope[rows], q_rope, k_nope, k_rope, v, O.default_scale(cfg.d_head, cfg.d_rope),
+                    visible=visible)
 
 
 class LatentMemo:

@@ -159,9 +159,11 @@ def _qscale(cfg):
     return float(np.float32(O.default_scale(cfg.d_head, cfg.d_rope) * np.log2(np.e)))
 
 
-def _flash_inputs(cfg, seed, fill_frames, q_frame, q_scale=1.0):
+def _flash_inputs(cfg, seed, fill_frames, q_frame, q_scale=1.0, frame_causal=False, plant=None):
     """Oracle-made, storage-rounded inputs of the flash step: cache rows,
-    slot map and absorbed queries, plus the oracle's latent output."""
+    slot map and absorbed queries, plus the oracle's latent output (under the
+    frame-causal mask when asked). plant = (slot, token, factor) scales that
+    cache row (latent and positional key) by factor before the oracle runs."""
     st = Stream(cfg, seed=seed)
     from harness import layer_weights
     wts = layer_weights(cfg, seed)
@@ -173,6 +175,9 @@ def _flash_inputs(cfg, seed, fill_frames, q_frame, q_scale=1.0):
         cache[f % W, :, :cfg.d_c] = round_to(c, cfg.dtype)
         cache[f % W, :, cfg.d_c:] = round_to(kr, cfg.dtype)
         slot_frame[f % W] = f
+    if plant is not None:
+        slot, tok, factor = plant
+        cache[slot, tok] = round_to(cache[slot, tok] * factor, cfg.dtype)
     qn, qr = st.q(q_frame, q_scale=q_scale)
     t, y, x = O.frame_positions(q_frame + np.arange(cfg.chunk_frames), cfg.grid_y, cfg.grid_x)
     # the absorbed query carries scale * log2(e); with it, exp(ln2 * s') is the
@@ -184,22 +189,28 @@ def _flash_inputs(cfg, seed, fill_frames, q_frame, q_scale=1.0):
     kr_all = cache[valid, :, cfg.d_c:].reshape(-1, cfg.d_rope)
     tk, yk, xk = O.frame_positions(slot_frame[valid], cfg.grid_y, cfg.grid_x)
     k_rope = O.rope3d(kr_all, tk, yk, xk, cfg.rope_split, cfg.rope_base)
-    ref = O.attend_latent(q_abs, c_all, k_rope, float(np.log(2.0)))
+    visible = O.frame_causal_mask(t, tk) if frame_causal else None
+    ref = O.attend_latent(q_abs, c_all, k_rope, float(np.log(2.0)), visible=visible)
     return cache, slot_frame, q_abs, ref
 
 
-def _run_flash(cfg, cache, slot_frame, q_abs, kv_splits=0, n_t=64, want_fallback_count=False):
+def _run_flash(cfg, cache, slot_frame, q_abs, kv_splits=0, n_t=64, want_fallback_count=False, frame_causal=False,
+               q_frame_first=0, rope_t_first=0):
     shape = mla.make_shape(cfg)
     Q = mla.qabs_dim(shape)
     qa = np.zeros(q_abs.shape[:-1] + (Q,))
     qa[..., :q_abs.shape[-1]] = q_abs
     tables = torch.empty(mla.rope3d_table_floats(shape, n_t), dtype=torch.float32, device="cuda")
-    mla.rope3d_tables(shape, 0, n_t, tables)
+    mla.rope3d_tables(shape, rope_t_first, n_t, tables)
     o_lat = torch.empty(q_abs.shape[0], cfg.n_heads, cfg.d_c, dtype=torch.bfloat16 if cfg.dtype == "bf16"
                         else torch.float32, device="cuda")
     ws = torch.empty(mla.flash_workspace_bytes(shape, cfg.chunk_frames, kv_splits), dtype=torch.uint8, device="cuda")
-    mla.flash_attend(shape, to_torch(qa, cfg.dtype), cfg.chunk_frames, to_torch(cache[None], cfg.dtype),
-                     torch.from_numpy(slot_frame[None].copy()).cuda(), tables, 0, n_t, o_lat, ws, kv_splits)
+    args = (to_torch(cache[None], cfg.dtype), torch.from_numpy(slot_frame[None].copy()).cuda(), tables, rope_t_first,
+            n_t, o_lat, ws, kv_splits)
+    if frame_causal:
+        mla.flash_attend_frame_causal(shape, to_torch(qa, cfg.dtype), q_frame_first, cfg.chunk_frames, *args)
+    else:
+        mla.flash_attend(shape, to_torch(qa, cfg.dtype), cfg.chunk_frames, *args)
     _sync()
     if want_fallback_count:  # the fallback row count sits at the start of the flash workspace
         return to_numpy(o_lat), int(ws[:4].view(torch.int32).item())
@@ -312,6 +323,65 @@ def test_flash_attend_empty_window_gives_zeros():
     sf[:] = -1
     got = _run_flash(cfg, cache, sf, q_abs)
     assert not got.any()
+
+
+def test_flash_attend_key_frames_outside_the_table_range():
+    """The window's temporal angles are formed by the call for any frame: a
+    window at frames 300..304 with tables covering only the chunk's own
+    frames (302..304) and, separately, tables covering none of them."""
+    cfg = get_config("wan_small")
+    cache, sf, q_abs, ref = _flash_inputs(cfg, 19, list(range(300, 305)), 303)
+    for t_first, n_t in ((303, 2), (0, 4)):
+        got = _run_flash(cfg, cache, sf, q_abs, n_t=n_t, rope_t_first=t_first)
+        assert_step_close(got, ref, cfg.dtype, label=f"keys outside tables t_first={t_first} n_t={n_t}")
+
+
+@pytest.mark.parametrize("name", ["wan_small_f32", "wan_small"])
+@pytest.mark.parametrize("kv_splits", [0, 1, 3])
+@pytest.mark.parametrize("wrapped", [False, True])
+def test_flash_attend_frame_causal(name, kv_splits, wrapped):
+    """The frame-causal attention stage on its own: a 3-frame chunk in a
+    6-frame window, plain (frames 0..5) or wrapped (frames 3..8 in rotated
+    slots). At fp32 the tiles hold 32 keys and a frame 35, so frame
+    boundaries fall inside tiles; with one key range per row block (kv_splits
+    1) a work-group walks all 7 tiles, so the per-key frames of a tile are
+    still being read when those of the tile two ahead are written."""
+    cfg = get_config(name).with_(chunk_frames=3, window_frames=6)
+    frames = list(range(3, 9)) if wrapped else list(range(6))
+    q_frame = frames[-1] - 2
+    cache, sf, q_abs, ref = _flash_inputs(cfg, 23, frames, q_frame, frame_causal=True)
+    got = _run_flash(cfg, cache, sf, q_abs, kv_splits, frame_causal=True, q_frame_first=q_frame)
+    assert_step_close(got, ref, cfg.dtype, label=f"{name} frame-causal flash splits={kv_splits} wrapped={wrapped}")
+
+
+@pytest.mark.parametrize("name,plant_tok", [("wan_small_f32", 30), ("wan_small", 8)])
+def test_flash_attend_frame_causal_reference_from_unseen_keys(name, plant_tok):
+    """First chunk of a rollout (the window holds only the chunk's frames 0..2),
+    queries x50 and one key of frame 2 scaled x3. A work-group visits the
+    range's last tile first, which holds frame-2 keys: the rows of frame 0
+    (and at fp32 of frame 1) see none of their first 32 keys and take the
+    maximum of those scores as reference, the planted key among them. Where it
+    scores far above every key the row sees, the row's sum underflows; such
+    rows must be listed for the exact pass (fallback count > 0 with one range
+    per row block) and match the oracle's masked softmax."""
+    cfg = get_config(name).with_(chunk_frames=3, window_frames=3)
+    T = cfg.tokens_per_frame
+    cache, sf, q_abs, ref = _flash_inputs(cfg, 24, [0, 1, 2], 0, q_scale=50.0, frame_causal=True,
+                                          plant=(2, plant_tok, 3.0))
+    from .gpu_common import errors
+    for splits in (1, 0, 2):
+        got, n_fallback = _run_flash(cfg, cache, sf, q_abs, splits, want_fallback_count=True, frame_causal=True,
+                                     q_frame_first=0)
+        e = errors(got, ref)
+        print(f"[parity] {name} causal unseen-reference splits={splits} fallback rows={n_fallback} {e}", flush=True)
+        if splits == 1:
+            assert n_fallback > 0
+        zero_rows = int((np.abs(got).reshape(-1, cfg.d_c).max(axis=1) == 0).sum())
+        assert zero_rows == 0, zero_rows
+        if cfg.dtype == "f32":
+            assert e["max_abs"] <= 5e-3 and e["rel_rms"] <= 5e-3, e
+        else:
+            assert_step_close(got, ref, cfg.dtype, label=f"{name} unseen-reference splits={splits}", sharp=True)
 
 
 # ------------------------------------------------------------------ a5 up-projection
@@ -467,28 +537,50 @@ def test_frame_causal_one_frame_chunk_and_empty_window():
     assert torch.equal(full.view(torch.int16), causal.view(torch.int16))
 
 
-def test_wan_full_size_frame_causal_sampled_rows():
-    """Wan2.1-1.3B shape, 3-frame chunk over a full 21-frame window, frame
-    causal: 64 sampled rows of the three chunk frames against the oracle."""
+def _wan_chunk(frames_written, seed):
+    """A Wan-shaped layer whose ring received frames 0 .. frames_written - 1 in
+    3-frame writes; the last three are the chunk. Returns (cfg, w, layer, st,
+    chunk_first, qn, qr, window frames)."""
     cfg = get_config("wan")
-    w, wd = device_weights(cfg, seed=0)
+    w, wd = device_weights(cfg, seed=seed)
     layer = LatentLayer(cfg, wd, batch=1, rope_n_t=64)
-    st = Stream(cfg, seed=0)
-    layer.write(to_torch(st.xs(0, 18)[None], cfg.dtype), 0, 18)
-    layer.write(to_torch(st.xs(18, 3)[None], cfg.dtype), 18, 3)
-    qn, qr = st.q(18)
-    out = layer.attend_frame_causal(to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype), 18, 3)
+    st = Stream(cfg, seed=seed)
+    for f0 in range(0, frames_written, 3):
+        layer.write(to_torch(st.xs(f0, 3)[None], cfg.dtype), f0, 3)
+    chunk_first = frames_written - 3
+    qn, qr = st.q(chunk_first)
+    window = list(range(max(0, frames_written - cfg.window_frames), frames_written))
+    return cfg, w, layer, st, chunk_first, qn, qr, window
+
+
+@pytest.mark.parametrize("frame_causal", [False, True])
+def test_wan_full_size_every_row(frame_causal):
+    """The Wan2.1-1.3B chunk the benchmark times (3-frame chunk, 4680 query
+    tokens, over a full 21-frame window of 32760 keys), through the
+    attention call it uses: every one of the 4680 x 12 x 128 outputs against
+    the oracle's explicit per-head reconstruction, without and with the
+    frame-causal mask."""
+    cfg, w, layer, st, chunk_first, qn, qr, window = _wan_chunk(21, seed=0)
+    attend = layer.attend_frame_causal if frame_causal else layer.attend
+    out = attend(to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype), chunk_first, 3)
     _sync()
     got = to_numpy(out)[0]
-    T = cfg.tokens_per_frame
-    rng = np.random.default_rng(5)
-    edge = [0, T - 1, T, 2 * T - 1, 2 * T, cfg.n_q - 1]
-    rows = np.unique(np.concatenate([edge, rng.choice(cfg.n_q, 64 - len(edge), replace=False)]))
-    xs = {f: st.x(f) for f in range(21)}
-    for k in range(3):  # rows of chunk frame 18 + k see frames 0 .. 18 + k
-        sel = rows[(rows >= k * T) & (rows < (k + 1) * T)]
-        ref = oracle_step_rows(cfg, w, xs, list(range(19 + k)), qn, qr, 18, sel)
-        assert_step_close(got[sel], ref, cfg.dtype, label=f"wan full size frame-causal, frame {18 + k}")
+    ref = oracle_step_rows(cfg, w, {f: st.x(f) for f in window}, window, qn, qr, chunk_first,
+                           frame_causal=frame_causal)
+    assert_step_close(got, ref, cfg.dtype, label=f"wan full size, every row, frame_causal={frame_causal}")
+
+
+def test_wan_full_size_frame_causal_wrapped_ring():
+    """Frame-causal chunk at the Wan shape after the ring wrapped: frames
+    0..38 written, so the window holds frames 18..38 with the chunk (36..38) in
+    slots 15..17 and slot order no longer frame order. Every output against
+    the oracle."""
+    cfg, w, layer, st, chunk_first, qn, qr, window = _wan_chunk(39, seed=7)
+    assert sorted(layer.slot_frame.cpu().numpy()[0].tolist()) == window
+    out = layer.attend_frame_causal(to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype), chunk_first, 3)
+    _sync()
+    ref = oracle_step_rows(cfg, w, {f: st.x(f) for f in window}, window, qn, qr, chunk_first, frame_causal=True)
+    assert_step_close(to_numpy(out)[0], ref, cfg.dtype, label="wan full size frame-causal wrapped ring")
 
 
 def test_denoising_rewrites_of_the_chunk():
@@ -545,28 +637,26 @@ def test_rollout_ring_eviction_and_time_advance():
         assert_step_close(to_numpy(out)[0], ref, cfg.dtype, label=f"rollout frame {f}")
 
 
-def test_wan_full_size_sampled_rows():
-    """Wan2.1-1.3B shape, 3-frame chunk over a full 21-frame window (4680 q x
-    32760 k), in the launch configuration the benchmark times; the oracle
-    checks 96 sampled query rows (all heads, full window), including the
-    first and last rows and tile-boundary rows."""
-    cfg = get_config("wan")
-    w, wd = device_weights(cfg, seed=0)
-    T = cfg.tokens_per_frame
-    layer = LatentLayer(cfg, wd, batch=1, rope_n_t=64)
-    st = Stream(cfg, seed=0)
-    layer.write(to_torch(st.xs(0, 18)[None], cfg.dtype), 0, 18)
-    layer.write(to_torch(st.xs(18, 3)[None], cfg.dtype), 18, 3)
-    qn, qr = st.q(18)
-    out = layer.attend(to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype), 18, 3)
-    _sync()
-    got = to_numpy(out)[0]
-    rng = np.random.default_rng(0)
-    edge = [0, 1, 21, 22, 42, 43, cfg.n_q // 2, T - 1, T, 2 * T - 1, 2 * T, cfg.n_q - 22, cfg.n_q - 1]
-    rows = np.unique(np.concatenate([edge, rng.choice(cfg.n_q, 96 - len(edge), replace=False)]))
-    xs = {f: st.x(f) for f in range(21)}
-    ref = oracle_step_rows(cfg, w, xs, list(range(21)), qn, qr, 18, rows)
-    assert_step_close(got[rows], ref, cfg.dtype, label="wan full size, sampled rows")
+@pytest.mark.parametrize("rope_n_t,first,last", [(256, 250, 262), (8, 0, 30)])
+def test_rollout_past_the_rope_table_range(rope_n_t, first, last):
+    """One-frame chunks through a 3-frame ring past the end of the layer's
+    RoPE table range (the default 256 frames, and an 8-frame range that moves
+    several times): the layer moves its tables with the queries, the window
+    keys' temporal angles need none, and every step matches the oracle."""
+    cfg = get_config("wan_small").with_(window_frames=3, chunk_frames=1)
+    w, wd = device_weights(cfg, seed=31)
+    layer = LatentLayer(cfg, wd, batch=1, rope_n_t=rope_n_t)
+    st = Stream(cfg, seed=31)
+    ring = O.RingCache(3, cfg.tokens_per_frame, cfg.d_c, cfg.d_rope)
+    for f in range(first, last + 1):
+        x = st.x(f)
+        layer.write(to_torch(x[None], cfg.dtype), f, 1)
+        qn, qr = st.q(f)
+        out = layer.attend(to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype), f, 1)
+        _sync()
+        assert layer.rope_t_first <= f < layer.rope_t_first + layer.rope_n_t
+        ref = O.chunk_step(O.dims_of(cfg), w, ring, x, f, qn, qr)
+        assert_step_close(to_numpy(out)[0], ref, cfg.dtype, label=f"rollout past the table, frame {f}")
 
 
 def test_wan_maximum_window_sampled_rows():
