@@ -72,7 +72,8 @@ typedef enum mla_status {
   MLA_ERR_WORKSPACE = 5,   /* workspace smaller than the *_workspace_bytes query */
   MLA_ERR_UNSUPPORTED = 6, /* (d_c, d_rope) has no kernel instantiation */
   MLA_ERR_HIP = 7,         /* a HIP launch failed */
-  MLA_ERR_RANGE = 8        /* frame or table index arguments out of range */
+  MLA_ERR_RANGE = 8,       /* frame or table index arguments out of range */
+  MLA_ERR_SCRATCH = 9      /* needs more than the fixed scratch of mla_flash_attend_noalloc */
 } mla_status;
 
 typedef enum mla_dtype { MLA_BF16 = 0, MLA_F32 = 1 } mla_dtype;
@@ -193,6 +194,25 @@ mla_status mla_flash_attend(const mla_shape* shape, const void* q_abs, int32_t q
                             const int32_t* slot_frame, const float* rope_tables, int32_t rope_t_first,
                             int32_t rope_n_t, void* o_lat, int32_t kv_splits, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- a4, no allocation
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * mla_flash_attend with its workspace replaced by a fixed scratch array of
+ * MLA_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on each GPU it
+ * runs on, from the first call with that GPU current until the process ends.
+ * The call itself allocates nothing. Same arguments, result and errors as
+ * mla_flash_attend without workspace / workspace_bytes; a problem whose
+ * mla_flash_workspace_bytes exceeds the scratch returns MLA_ERR_SCRATCH
+ * before anything is enqueued (the Wan2.1 chunk, 3 frames over a 21-frame
+ * window, needs about 53 MB at one stream with kv_splits = 0). Every call on
+ * one GPU uses that GPU's single array: calls that may overlap on one GPU
+ * (several streams, several host threads) race on it and must be ordered by
+ * the caller. */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+mla_status mla_flash_attend_noalloc(const mla_shape* shape, const void* q_abs, int32_t q_n_frames, const void* cache,
+                                    const int32_t* slot_frame, const float* rope_tables, int32_t rope_t_first,
+                                    int32_t rope_n_t, void* o_lat, int32_t kv_splits, void* stream);
 
 /* ---------------------------------------------------------------- a4, frame-causal
  * mla_flash_attend under the frame-causal mask inside the chunk (the

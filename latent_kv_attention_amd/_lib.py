@@ -17,14 +17,15 @@ MLA_BF16, MLA_F32 = 0, 1
 
 STATUS = {
     0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_SHAPE", 3: "MLA_ERR_DTYPE", 4: "MLA_ERR_ALIGN",
-    5: "MLA_ERR_WORKSPACE", 6: "MLA_ERR_UNSUPPORTED", 7: "MLA_ERR_HIP", 8: "MLA_ERR_RANGE",
+    5: "MLA_ERR_WORKSPACE", 6: "MLA_ERR_UNSUPPORTED", 7: "MLA_ERR_HIP", 8: "MLA_ERR_RANGE", 9: "MLA_ERR_SCRATCH",
 }
 
 # every symbol include/mla.h declares
 EXPORTS = [
     "mla_abi_version", "mla_status_string", "mla_shape_check", "mla_qabs_dim",
     "mla_rope3d_table_floats", "mla_rope3d_tables", "mla_cache_write", "mla_absorb_q",
-    "mla_flash_workspace_bytes", "mla_flash_attend", "mla_flash_attend_frame_causal", "mla_up_v",
+    "mla_flash_workspace_bytes", "mla_flash_attend", "mla_flash_attend_frame_causal", "mla_flash_attend_noalloc",
+    "mla_up_v",
     "mla_chunk_attend_workspace_bytes", "mla_chunk_attend",
     "mla_chunk_attend_heads_workspace_bytes", "mla_chunk_attend_heads", "mla_chunk_attend_frame_causal",
     "mla_query_project", "mla_output_project", "mla_layer_step_workspace_bytes", "mla_layer_step",
@@ -69,6 +70,7 @@ _SIGS = {
     "mla_flash_workspace_bytes": (_SZ, [_SP, _I, _I]),
     "mla_flash_attend": (_I, [_SP, _P, _I, _P, _P, _P, _I, _I, _P, _I, _P, _SZ, _P]),
     "mla_flash_attend_frame_causal": (_I, [_SP, _P, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P, _SZ, _P]),
+    "mla_flash_attend_noalloc": (_I, [_SP, _P, _I, _P, _P, _P, _I, _I, _P, _I, _P]),
     "mla_up_v": (_I, [_SP, _P, _I, _P, _P, _P]),
     "mla_chunk_attend_workspace_bytes": (_SZ, [_SP, _I]),
     "mla_chunk_attend": (_I, [_SP, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
@@ -195,6 +197,17 @@ def flash_attend_frame_causal(shape: MlaShape, q_abs, q_frame_first: int, q_n_fr
                                                _ptr(cache), _ptr(slot_frame, "int32"), _ptr(tables, "float32"),
                                                rope_t_first, rope_n_t, _ptr(o_lat), kv_splits, _ptr(workspace),
                                                nbytes, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MLA_NOALLOC_SCRATCH_BYTES
+
+
+def flash_attend_noalloc(shape: MlaShape, q_abs, q_n_frames: int, cache, slot_frame, tables, rope_t_first: int,
+                         rope_n_t: int, o_lat, kv_splits: int = 0, stream=None) -> None:
+    _check("mla_flash_attend_noalloc",
+           lib().mla_flash_attend_noalloc(ctypes.byref(shape), _ptr(q_abs), q_n_frames, _ptr(cache),
+                                          _ptr(slot_frame, "int32"), _ptr(tables, "float32"), rope_t_first, rope_n_t,
+                                          _ptr(o_lat), kv_splits, _stream(stream)))
 
 
 def up_v(shape: MlaShape, o_lat, q_n_frames: int, w_uv, out, stream=None) -> None:

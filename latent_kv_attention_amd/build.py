@@ -20,7 +20,7 @@ LIB_NAME = "libmla355.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["mla_abi.hip", "rope_tables.hip", "cache_write.hip", "absorb_q.hip", "flash_mla.hip", "up_v.hip",
-           "heads_mha.hip", "proj_gemm.hip"]
+           "heads_mha.hip", "proj_gemm.hip", "noalloc.hip"]
 
 # The matrix-core ceiling probe (a measurement aid for bench.py) goes into a
 # library of its own, so libmla355.so exports exactly what include/mla.h declares.

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "../../include/mla.h"
+#include "abi_internal.hpp"
 #include "mla_internal.hpp"
 
 #define MLA_API extern "C" __attribute__((visibility("default")))
@@ -309,6 +310,7 @@ MLA_API const char* mla_status_string(int32_t status) {
     case MLA_ERR_UNSUPPORTED: return "(d_c, d_rope) has no kernel instantiation";
     case MLA_ERR_HIP: return "HIP launch failed";
     case MLA_ERR_RANGE: return "frame or table index out of range";
+    case MLA_ERR_SCRATCH: return "the call needs more scratch than the library's fixed per-device buffer holds";
     default: return "unknown status";
   }
 }
@@ -441,6 +443,30 @@ MLA_API mla_status mla_flash_attend_frame_causal(const mla_shape* shape, const v
                                                  size_t workspace_bytes, void* stream) {
   return flash_attend_impl(shape, q_abs, q_frame_first, q_n_frames, cache, slot_frame, rope_tables, rope_t_first,
                            rope_n_t, o_lat, kv_splits, workspace, workspace_bytes, stream, true);
+}
+
+// Argument checks and launch of mla_flash_attend with the workspace supplied
+// separately (the allocation-free entry point keeps its own).
+mla_status mla_abi::flash_check(const mla_shape* shape, const void* q_abs, int32_t q_n_frames, const void* cache,
+                                const int32_t* slot_frame, const float* rope_tables, int32_t rope_t_first,
+                                int32_t rope_n_t, const void* o_lat, int32_t kv_splits, size_t* ws_bytes) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!q_abs || !cache || !slot_frame || !o_lat) return MLA_ERR_NULL;
+  if (!aligned16(q_abs) || !aligned16(cache) || !aligned16(slot_frame) || !aligned16(o_lat)) return MLA_ERR_ALIGN;
+  if ((st = check_tables(shape, rope_tables, rope_t_first, rope_n_t)) != MLA_OK) return st;
+  if ((st = check_query_args(shape, 0, q_n_frames)) != MLA_OK) return st;
+  if (kv_splits < 0 || kv_splits > kMaxSplits) return MLA_ERR_RANGE;
+  if (!flash_plan_ok(flash_plan(shape, q_n_frames, kv_splits))) return MLA_ERR_SHAPE;
+  *ws_bytes = flash_ws_bytes(shape, q_n_frames, kv_splits);
+  return MLA_OK;
+}
+
+mla_status mla_abi::flash_run(const mla_shape* shape, const void* q_abs, int32_t q_n_frames, const void* cache,
+                              const int32_t* slot_frame, const float* rope_tables, int32_t rope_t_first,
+                              int32_t rope_n_t, void* o_lat, int32_t kv_splits, void* workspace, void* stream) {
+  return do_flash(shape, q_abs, q_n_frames, cache, slot_frame, rope_tables, rope_t_first, rope_n_t, o_lat, kv_splits,
+                  workspace, (hipStream_t)stream);
 }
 
 MLA_API mla_status mla_up_v(const mla_shape* shape, const void* o_lat, int32_t q_n_frames, const void* w_uv,

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(built_lib):
 def test_abi_version_and_status_strings(built_lib):
     assert mla.abi_version() == 1
     lib = mla.lib()
-    for code in range(9):
+    for code in range(10):
         s = lib.mla_status_string(code)
         assert isinstance(s, bytes) and len(s) > 0
     assert lib.mla_status_string(99) == b"unknown status"
