@@ -34,14 +34,9 @@ HIPCC_FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
-# Per-source additions. The attention kernel runs at the register limit; the
-# backend's own register-pressure trackers give its scheduler a tighter
-# estimate there (about 2% faster, measured), and the scheduling strategy
-# that groups memory instructions issues more LDS operand reads ahead of
-# their products (about 1.4% faster, measured three times).
-SOURCE_FLAGS = {
-    "flash_mla.hip": ["-mllvm", "-amdgpu-use-amdgpu-trackers", "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
-}
+# Per-source additions (none at present: the attention kernel orders its
+# own operand reads and products with scheduling barriers).
+SOURCE_FLAGS: dict = {}
 
 
 def _hipcc() -> str:

@@ -35,16 +35,20 @@
 //     work-group that visits them: every row block visits every key;
 //   * keys stream in 128-key tiles through LDS, double-buffered, one barrier
 //     per tile. Both parts go global -> LDS directly (no registers): the
-//     latent into rows 480 bytes apart, which keeps both LDS read patterns
-//     below free of bank conflicts, the rotated kR into a packed region
-//     whose 16-byte units are XOR-swizzled by key for the same reason;
+//     latent into rows 416 bytes apart, which keeps both LDS read patterns
+//     below nearly free of bank conflicts, the rotated kR into a packed
+//     region whose 16-byte units are XOR-swizzled by key for the same reason;
+//   * within a tile each wave is software-pipelined over 32-key halves: the
+//     score products of half h + 1 are issued with the exponentials of half
+//     h between them, then the value products of half h; operand reads are
+//     issued one or two products ahead (scheduling barriers keep that order);
 //   * scores are formed transposed, S^T = K Q^T (keys as rows), so a lane
 //     holds 4 keys of one query row and the probabilities already sit in the
 //     lane layout of the B operand of O^T = C^T P^T. The C^T operand is read
 //     from the same LDS tile with the transposing LDS load: the latent is
 //     staged once for both products;
 //   * kv_splits > 1 partitions the key tiles; each split keeps its own
-//     reference and a second pass merges the (reference, output, sum) triples.
+//     reference and a second pass merges the pieces by log2 of their weight.
 #include <type_traits>
 
 #include "mla_common.hpp"
@@ -67,6 +71,22 @@ __device__ __forceinline__ int opaque(int x) {
 
 constexpr float kSumLimit = 0x1p100f;
 constexpr float kSumMin = 0x1p-100f;
+
+// Work-groups are dealt to the 8 XCDs round-robin (work-group i runs on XCD
+// i mod 8). Work-group i gets logical index (XCD-major) so that each XCD's
+// work-groups take consecutive unit ranges: with several streams an XCD then
+// walks few windows and its L2 serves them, instead of every XCD touching
+// every stream's window. A bijection of [0, G) for any G.
+constexpr int kXcds = 8;
+
+// Fourth word of a raw buffer resource (no format conversion, no swizzle):
+// byte offsets past num_records read as zero.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ int xcd_major(int id, int G) {
+  const int q = G / kXcds, r = G % kXcds;
+  const int x = id % kXcds, k = id / kXcds;
+  return x * q + min(x, r) + k;
+}
 }  // namespace
 
 // bf16: 8 waves x 32 rows (two waves per SIMD) and 128-key tiles; float
@@ -223,14 +243,15 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     kr_pk[k] = (instr < F::KR_INSTR && n < kBN) ? (n << 16) | ((F::kr_slot(n, us) * F::CPU + ci) * 16) : -1;
   }
 
-  // Work-group g takes units [g U / G, (g + 1) U / G) of the (row block, key
-  // tile) grid, as consecutive segments of at most one row block each. A
+  // Work-group g (logical index) takes units [g U / G, (g + 1) U / G) of the
+  // (row block, key tile) grid, as consecutive segments of at most one row block each. A
   // segment that covers its whole row block writes the normalised output; a
   // partial one writes (output, reference, sum) to slot 0 (the work-group's
   // first segment) or 1 (its last) for the merge pass.
   const long long G = p.grid;
-  const long long u_first = (long long)blockIdx.x * p.units / G;
-  const long long u_last = ((long long)blockIdx.x + 1) * p.units / G;
+  const int g = xcd_major(blockIdx.x, p.grid);
+  const long long u_first = (long long)g * p.units / G;
+  const long long u_last = ((long long)g + 1) * p.units / G;
   //
   // Segments are taken last to first: a range that ends inside a row block
   // starts with that block's first tiles, so at any moment most work-groups
@@ -340,6 +361,14 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
       }
     };
 
+    // Buffer resources of the stream's cache and rotated keys. The direct
+    // loads use the buffer form: its LDS writes are counted on the vector
+    // memory counter alone, so the compiler keeps exact (partial) waits for
+    // the LDS operand reads while a tile's loads are in flight.
+    const __amdgpu_buffer_rsrc_t cache_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)cache_b, 0, (int)((size_t)p.W * p.T * F::DK * sizeof(T)), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t krot_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)krot_b, 0, (int)((size_t)p.W * p.T * DR * sizeof(T)), kBufferWord3);
     // ---- latent part: global -> LDS, lane order = LDS order (no registers)
     auto issue_latent = [&](const int* tab, T* buf) {
 #pragma unroll
@@ -347,9 +376,8 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
         const int instr = wave + kWaves * k;
         const int pk = opaque(lat_pk[k]);
         if (instr < F::N_INSTR && pk >= 0) {
-          const char* src = cache_b + (unsigned)(tab[pk >> 16] + (pk & 0xffff));
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                           (MLA_LDS void*)(MLA_LDS T*)(buf + instr * 64 * F::CB), 16, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(cache_rs, (MLA_LDS void*)(MLA_LDS T*)(buf + instr * 64 * F::CB), 16,
+                                                   (unsigned)(tab[pk >> 16] + (pk & 0xffff)), 0, 0, 0);
         }
       }
     };
@@ -363,9 +391,8 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
         const int pk = opaque(kr_pk[k]);
         if (instr < F::KR_INSTR && pk >= 0) {
           const int v = min(kbase + (pk >> 16), n_keys - 1);
-          const char* src = krot_b + (unsigned)(v * DR * (int)sizeof(T) + (pk & 0xffff));
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                           (MLA_LDS void*)(MLA_LDS T*)(buf + instr * 64 * F::CB), 16, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(krot_rs, (MLA_LDS void*)(MLA_LDS T*)(buf + instr * 64 * F::CB), 16,
+                                                   (unsigned)(v * DR * (int)sizeof(T) + (pk & 0xffff)), 0, 0, 0);
         }
       }
     };
@@ -394,35 +421,6 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
 #pragma unroll
           for (int mb = 0; mb < kNMB; ++mb) s[kb][mb] = mma16(a, qf[mb][kc], kc == 0 ? seed[mb] : s[kb][mb]);
         }
-      }
-    };
-    // probabilities 2^s, packed into the B operand of the value product; with
-    // RAGGED, keys at or past n_keys (kfirst = key index of the half) get 0
-    auto probs = [&](const sblk& s, v8 (&pb)[kNMB], int kfirst, auto ragged_c) {
-      constexpr bool RAGGED = decltype(ragged_c)::value;
-#pragma unroll
-      for (int mb = 0; mb < kNMB; ++mb) {
-        float f8[8];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float e = fast_exp2(s[kb][mb][i]);
-            if constexpr (RAGGED) e = kfirst + kb * 16 + lg * 4 + i < n_keys ? e : 0.f;
-            f8[kb * 4 + i] = e;
-            l_run[mb] += e;
-          }
-        pb[mb] = pack8<T>(f8);
-      }
-    };
-    // O^T[d][row] += C^T[d][key] P^T[key][row]; key slot j of lane group g is
-    // key 4g+j (j < 4) or 16+4g+(j-4) of the half, matching S^T's layout
-    auto values = [&](const T* kt, int half, const v8 (&pb)[kNMB]) {
-#pragma unroll
-      for (int db = 0; db < F::NDB; ++db) {
-        const v8 a = lds_tr8(kt, F::LS, half * 32 + lg * 4, half * 32 + 16 + lg * 4, db * 16);
-#pragma unroll
-        for (int mb = 0; mb < kNMB; ++mb) o[db][mb] = mma16(a, pb[mb], o[db][mb]);
       }
     };
     auto buf_of = [&](auto par_c) -> T* { return decltype(par_c)::value == 0 ? kv0 : kv1; };
@@ -459,10 +457,7 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
       if (pos + 2 < n_visit) describe(pos + 2, keytab[CUR]);
       const int kbase = tile_of(pos) * kBN;
       auto halves = [&](bool masked) {
-#pragma unroll 1
-        for (int half = 0; half < NKC2; ++half) {
-          sblk s;
-          scores(cur, cur_r, half, s, negref);
+        auto mask = [&](sblk& s, int half) {
           if constexpr (CAUSAL) {
             // scores of keys from frames after the row's frame drop out
             if (masked) {
@@ -477,10 +472,102 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
                 }
             }
           }
+        };
+        // A operand of the score product S^T = K Q^T: keys 16 kb .. of the
+        // half, contraction dims 32 kc .. (latent, rotated kR or zero padding)
+        auto kop = [&](int half, int kc, int kb) -> v8 {
+          const int row = (half * 2 + kb) * 16 + li, dim = kc * 32 + lg * 8;
+          auto rope_unit = [&]() { return lds_load8<T>(cur_r + row * DR + F::kr_slot(row, (dim - DC) / 8) * 8); };
+          if ((kc + 1) * 32 <= DC) return lds_load8<T>(cur + row * F::LS + dim);
+          if (kc * 32 >= DC && (kc + 1) * 32 <= F::DK) return rope_unit();
+          return dim < DC ? lds_load8<T>(cur + row * F::LS + dim) : (dim < F::DK ? rope_unit() : zero8<T>());
+        };
+        // A operand of the value product O^T[d][row] += C^T[d][key] P^T[key][row]
+        // for latent dims 16 db ..: key slot j of lane group lg is key
+        // 4 lg + j (j < 4) or 16 + 4 lg + (j - 4) of the half, matching the
+        // layout of the scores S^T (so the probabilities never leave registers)
+        auto vop = [&](int half, int db) -> v8 {
+          return lds_tr8(cur, F::LS, half * 32 + lg * 4, half * 32 + 16 + lg * 4, db * 16);
+        };
+        constexpr bool RAGGED = decltype(ragged_c)::value;
+        // exponentials of 16-row block mb, key block kb of a half: 4 values
+        auto expo = [&](const sblk& s, float (&f)[kNMB][8], int mb, int kb, int kfirst) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float e = fast_exp2(s[kb][mb][i]);
+            if constexpr (RAGGED) e = kfirst + kb * 16 + lg * 4 + i < n_keys ? e : 0.f;
+            f[mb][kb * 4 + i] = e;
+            l_run[mb] += e;
+          }
+        };
+        // one half: the scores of half + 1 (when NEXT) with the
+        // exponentials of this half spread between their products, then the
+        // value products of this half; operand reads run ahead of use
+        auto body = [&](int half, sblk& s_cur, sblk& s_nxt, auto next_c) {
+          constexpr bool NEXT = decltype(next_c)::value;
+          const int kfirst = kbase + half * 32;
+          mask(s_cur, half);
+          float f[kNMB][8];
+          if constexpr (NEXT) {
+            v8 ka[2][2];
+            ka[0][0] = kop(half + 1, 0, 0);
+            ka[0][1] = kop(half + 1, 0, 1);
+#pragma unroll
+            for (int kc = 0; kc < F::NKC; ++kc) {
+              if (kc + 1 < F::NKC) {
+                ka[(kc + 1) & 1][0] = kop(half + 1, kc + 1, 0);
+                ka[(kc + 1) & 1][1] = kop(half + 1, kc + 1, 1);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+              for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int mb = 0; mb < kNMB; ++mb)
+                  s_nxt[kb][mb] = mma16(ka[kc & 1][kb], qf[mb][kc], kc == 0 ? negref[mb] : s_nxt[kb][mb]);
+              // exponential chunk kc of the 2 kNMB (mb, kb) chunks of this half
+              // (all remaining ones at the last step), interleaved with the
+              // products one for one
+#pragma unroll
+              for (int c = kc; c < (kc + 1 == F::NKC ? 2 * kNMB : kc + 1); ++c)
+                if (c < 2 * kNMB) expo(s_cur, f, c / 2, c % 2, kfirst);
+#pragma unroll
+              for (int grp = 0; grp < 2 * kNMB; ++grp) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
+#pragma unroll
+            for (int c = 0; c < 2 * kNMB; ++c) expo(s_cur, f, c / 2, c % 2, kfirst);
+          }
           v8 pb[kNMB];
-          probs(s, pb, kbase + half * 32, ragged_c);
-          values(cur, half, pb);
+#pragma unroll
+          for (int mb = 0; mb < kNMB; ++mb) pb[mb] = pack8<T>(f[mb]);
+          v8 va[3];
+          va[0] = vop(half, 0);
+          va[1] = vop(half, 1);
+#pragma unroll
+          for (int db = 0; db < F::NDB; ++db) {
+            if (db + 2 < F::NDB) va[(db + 2) % 3] = vop(half, db + 2);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mb = 0; mb < kNMB; ++mb) o[db][mb] = mma16(va[db % 3], pb[mb], o[db][mb]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        };
+        sblk s_cur;
+        scores(cur, cur_r, 0, s_cur, negref);
+#pragma unroll 1
+        for (int half = 0; half + 1 < NKC2; ++half) {
+          sblk s_nxt;
+          body(half, s_cur, s_nxt, std::integral_constant<bool, true>());
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int mb = 0; mb < kNMB; ++mb) s_cur[kb][mb] = s_nxt[kb][mb];
         }
+        body(NKC2 - 1, s_cur, s_cur, std::integral_constant<bool, false>());
       };
       if constexpr (CAUSAL) {
         // 0: all keys visible to the block, 1: masked per key, 2: none visible
@@ -601,7 +688,7 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
         // float for the merge, log2 of the piece's total weight (reference +
         // log2 of the sum; -inf for a piece without keys the row sees) and a
         // status (+inf when the row needs the exact fallback)
-        const size_t prow = ((size_t)blockIdx.x * 2 + (first_seg ? 0 : 1)) * F::kRowsBlock + row - rb * F::kRowsBlock;
+        const size_t prow = ((size_t)g * 2 + (first_seg ? 0 : 1)) * F::kRowsBlock + row - rb * F::kRowsBlock;
         T* dst = (T*)p.part_o + prow * DC;
 #pragma unroll
         for (int db = 0; db < F::NDB; ++db)
