@@ -356,6 +356,8 @@ def per_head_report(base, args):
             "per_head_own_TFLOPs": round((attn_fl + expand_fl) / (ms_a * 1e-3) / 1e12, 2),
             "per_head_attention_flops": attn_fl, "per_head_expansion_flops": expand_fl,
             "max_abs_diff_vs_latent_form": round(float(diff.max()), 5),
+            "form_mla_chunk_attend_takes": {mla.FORM_LATENT: "latent", mla.FORM_HEADS: "per-head"}[
+                mla.chunk_attend_form(ctx.shape, cfg.chunk_frames)],
             "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic"}), flush=True)
         del ctx, ws, out_h
         torch.cuda.empty_cache()

@@ -238,16 +238,39 @@ mla_status mla_up_v(const mla_shape* shape, const void* o_lat, int32_t q_n_frame
                     void* stream);
 
 /* ---------------------------------------------------------------- a3..a5
- * The whole attention side of the step: mla_absorb_q, mla_flash_attend and
- * mla_up_v in sequence on `stream`, with q_abs and o_lat carved from
- * `workspace` (at least mla_chunk_attend_workspace_bytes bytes).
+ * The whole attention side of the step (hyper.ai summary, Method: the score
+ * and value through the shared latent), in one of two forms that give the
+ * same result up to rounding:
+ *   - the latent form, mla_chunk_attend_latent: mla_absorb_q,
+ *     mla_flash_attend and mla_up_v in sequence on `stream`, with q_abs and
+ *     o_lat carved from `workspace`;
+ *   - the per-head form, mla_chunk_attend_heads (below).
+ * mla_chunk_attend takes the form mla_chunk_attend_form names for the shape
+ * and chunk size: the per-head form where it is supported (bf16,
+ * d_head = 128), does at least 15% fewer products per (query, key, head)
+ * (2 d_head + d_rope against 2 d_c + d_rope) and the chunk has at least 1024
+ * query tokens per stream to repay its per-call expansion of the window's
+ * keys and values; else the latent form. At the Wan2.1 shape (d_c 192,
+ * 3-frame chunks of 4680 tokens) that is the per-head form.
+ * mla_chunk_attend_workspace_bytes covers both the latent form and, where
+ * mla_chunk_attend takes it, the per-head form (so one workspace serves
+ * mla_chunk_attend, mla_chunk_attend_latent and
+ * mla_chunk_attend_frame_causal).
  * Arguments as above; out (device) [B][N_q][H][d_head]. */
+#define MLA_FORM_LATENT 0
+#define MLA_FORM_HEADS 1
+int32_t mla_chunk_attend_form(const mla_shape* shape, int32_t q_n_frames); /* -1 if invalid */
 size_t mla_chunk_attend_workspace_bytes(const mla_shape* shape, int32_t q_n_frames);
 mla_status mla_chunk_attend(const mla_shape* shape, const void* q_nope, const void* q_r, int32_t q_frame_first,
                             int32_t q_n_frames, const void* w_uk, const void* w_uv, const void* cache,
                             const int32_t* slot_frame, const float* rope_tables, int32_t rope_t_first,
                             int32_t rope_n_t, void* out, void* workspace, size_t workspace_bytes,
                             void* stream);
+mla_status mla_chunk_attend_latent(const mla_shape* shape, const void* q_nope, const void* q_r,
+                                   int32_t q_frame_first, int32_t q_n_frames, const void* w_uk, const void* w_uv,
+                                   const void* cache, const int32_t* slot_frame, const float* rope_tables,
+                                   int32_t rope_t_first, int32_t rope_n_t, void* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- a3..a5, frame-causal
  * mla_chunk_attend with a frame-causal mask inside the chunk (the
@@ -356,9 +379,10 @@ mla_status mla_output_project(const mla_shape* shape, const void* o, int32_t n_f
 /* ---------------------------------------------------------------- whole layer
  * One layer's chunk step in one call, on `stream`, in this order:
  * mla_query_project (queries from the chunk's tokens x), mla_cache_write
- * (the same tokens into the ring), mla_chunk_attend or, with frame_causal
- * != 0, mla_chunk_attend_frame_causal (the chunk's queries over the
- * window), mla_output_project (u = W_o of the heads' outputs). The query
+ * (the same tokens into the ring), mla_chunk_attend in the form
+ * mla_chunk_attend_form names or, with frame_causal != 0,
+ * mla_chunk_attend_frame_causal (the chunk's queries over the window),
+ * mla_output_project (u = W_o of the heads' outputs). The query
  * latent, the queries, the heads' outputs and the attention's workspace are
  * carved from `workspace` (at least mla_layer_step_workspace_bytes bytes;
  * its contents on entry do not matter). Every part's arguments are checked
@@ -377,9 +401,10 @@ typedef struct mla_layer_weights {
   const void* w_uk;  /* [H][d_head][d_c] */
   const void* w_uv;  /* [H][d_head][d_c] */
   const void* w_o;   /* [hidden][H * d_head] */
-  const void* w_qabs; /* optional, [H][Q][d_cq] from mla_query_absorb_weights: when set,
-                         the queries go through mla_query_project_absorbed (w_uq, w_qr,
-                         w_uk are then not read) */
+  const void* w_qabs; /* optional, [H][Q][d_cq] from mla_query_absorb_weights: when set and
+                         the latent form runs, the queries go through
+                         mla_query_project_absorbed. The per-head form needs w_uq, w_qr
+                         and w_uk; where any of them is NULL the latent form runs */
 } mla_layer_weights;
 
 size_t mla_layer_step_workspace_bytes(const mla_shape* shape, int32_t d_cq, int32_t n_frames);

@@ -26,7 +26,7 @@ EXPORTS = [
     "mla_rope3d_table_floats", "mla_rope3d_tables", "mla_cache_write", "mla_absorb_q",
     "mla_flash_workspace_bytes", "mla_flash_attend", "mla_flash_attend_frame_causal", "mla_flash_attend_noalloc",
     "mla_up_v",
-    "mla_chunk_attend_workspace_bytes", "mla_chunk_attend",
+    "mla_chunk_attend_workspace_bytes", "mla_chunk_attend", "mla_chunk_attend_latent", "mla_chunk_attend_form",
     "mla_chunk_attend_heads_workspace_bytes", "mla_chunk_attend_heads", "mla_chunk_attend_frame_causal",
     "mla_query_project", "mla_output_project", "mla_layer_step_workspace_bytes", "mla_layer_step",
     "mla_query_absorb_weights", "mla_query_project_absorbed",
@@ -74,6 +74,8 @@ _SIGS = {
     "mla_up_v": (_I, [_SP, _P, _I, _P, _P, _P]),
     "mla_chunk_attend_workspace_bytes": (_SZ, [_SP, _I]),
     "mla_chunk_attend": (_I, [_SP, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
+    "mla_chunk_attend_latent": (_I, [_SP, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
+    "mla_chunk_attend_form": (_I, [_SP, _I]),
     "mla_chunk_attend_heads_workspace_bytes": (_SZ, [_SP, _I]),
     "mla_chunk_attend_frame_causal": (_I, [_SP, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
     "mla_chunk_attend_heads": (_I, [_SP, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
@@ -226,6 +228,24 @@ def chunk_attend(shape: MlaShape, q_nope, q_r, q_frame_first: int, q_n_frames: i
                                                       q_n_frames, _ptr(w_uk), _ptr(w_uv), _ptr(cache),
                                                       _ptr(slot_frame, "int32"), _ptr(tables, "float32"), rope_t_first, rope_n_t,
                                                       _ptr(out), _ptr(workspace), nbytes, _stream(stream)))
+
+
+FORM_LATENT, FORM_HEADS = 0, 1
+
+
+def chunk_attend_form(shape: MlaShape, q_n_frames: int) -> int:
+    """Which form mla_chunk_attend takes: FORM_LATENT or FORM_HEADS (-1: invalid)."""
+    return lib().mla_chunk_attend_form(ctypes.byref(shape), q_n_frames)
+
+
+def chunk_attend_latent(shape: MlaShape, q_nope, q_r, q_frame_first: int, q_n_frames: int, w_uk, w_uv, cache,
+                        slot_frame, tables, rope_t_first: int, rope_n_t: int, out, workspace, stream=None) -> None:
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("mla_chunk_attend_latent",
+           lib().mla_chunk_attend_latent(ctypes.byref(shape), _ptr(q_nope), _ptr(q_r), q_frame_first, q_n_frames,
+                                         _ptr(w_uk), _ptr(w_uv), _ptr(cache), _ptr(slot_frame, "int32"),
+                                         _ptr(tables, "float32"), rope_t_first, rope_n_t, _ptr(out), _ptr(workspace),
+                                         nbytes, _stream(stream)))
 
 
 def chunk_attend_heads_workspace_bytes(shape: MlaShape, q_n_frames: int) -> int:

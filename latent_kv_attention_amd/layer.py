@@ -61,7 +61,8 @@ class LatentLayer:
                          self.slot_frame, stream)
 
     def attend(self, q_nope, q_r, q_frame_first: int, q_n_frames: int, out=None, stream=None):
-        """Attention of the chunk's queries over the window -> out [B][N_q][H][d_head]."""
+        """Attention of the chunk's queries over the window -> out [B][N_q][H][d_head]
+        (mla_chunk_attend: the latent or the per-head form, by shape)."""
         if q_n_frames > self.max_chunk_frames:
             raise ValueError("chunk larger than the workspace was sized for")
         if out is None:
@@ -71,6 +72,19 @@ class LatentLayer:
         _lib.chunk_attend(self.shape, q_nope, q_r, q_frame_first, q_n_frames, self.w["w_uk"], self.w["w_uv"],
                           self.cache, self.slot_frame, self.tables, self.rope_t_first, self.rope_n_t, out,
                           self.workspace, stream)
+        return out
+
+    def attend_latent(self, q_nope, q_r, q_frame_first: int, q_n_frames: int, out=None, stream=None):
+        """attend() by the latent form whatever the shape (mla_chunk_attend_latent)."""
+        if q_n_frames > self.max_chunk_frames:
+            raise ValueError("chunk larger than the workspace was sized for")
+        if out is None:
+            out = torch.empty(self.B, q_n_frames * self.T, self.cfg.n_heads, self.cfg.d_head, dtype=self.dtype,
+                              device=self.device)
+        self.ensure_tables(q_frame_first, q_n_frames, stream)
+        _lib.chunk_attend_latent(self.shape, q_nope, q_r, q_frame_first, q_n_frames, self.w["w_uk"], self.w["w_uv"],
+                                 self.cache, self.slot_frame, self.tables, self.rope_t_first, self.rope_n_t, out,
+                                 self.workspace, stream)
         return out
 
     def attend_frame_causal(self, q_nope, q_r, q_frame_first: int, q_n_frames: int, out=None, stream=None):

@@ -553,21 +553,24 @@ def _wan_chunk(frames_written, seed):
     return cfg, w, layer, st, chunk_first, qn, qr, window
 
 
-@pytest.mark.parametrize("frame_causal", [False, True])
-def test_wan_full_size_every_row(frame_causal):
+def test_wan_full_size_every_row():
     """The Wan2.1-1.3B chunk the benchmark times (3-frame chunk, 4680 query
-    tokens, over a full 21-frame window of 32760 keys), through the
-    attention call it uses: every one of the 4680 x 12 x 128 outputs against
-    the oracle's explicit per-head reconstruction, without and with the
-    frame-causal mask."""
+    tokens, over a full 21-frame window of 32760 keys): every one of the
+    4680 x 12 x 128 outputs against the oracle's explicit per-head
+    reconstruction, through the latent form (the attention call the
+    benchmark times), through mla_chunk_attend (which takes the per-head
+    form at this shape), and under the frame-causal mask."""
     cfg, w, layer, st, chunk_first, qn, qr, window = _wan_chunk(21, seed=0)
-    attend = layer.attend_frame_causal if frame_causal else layer.attend
-    out = attend(to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype), chunk_first, 3)
+    assert mla.chunk_attend_form(layer.shape, 3) == mla.FORM_HEADS
+    q = (to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype), chunk_first, 3)
+    outs = {"latent": layer.attend_latent(*q), "selected": layer.attend(*q), "frame-causal": layer.attend_frame_causal(*q)}
     _sync()
-    got = to_numpy(out)[0]
-    ref = oracle_step_rows(cfg, w, {f: st.x(f) for f in window}, window, qn, qr, chunk_first,
-                           frame_causal=frame_causal)
-    assert_step_close(got, ref, cfg.dtype, label=f"wan full size, every row, frame_causal={frame_causal}")
+    xs = {f: st.x(f) for f in window}
+    ref = oracle_step_rows(cfg, w, xs, window, qn, qr, chunk_first)
+    for k in ("latent", "selected"):
+        assert_step_close(to_numpy(outs[k])[0], ref, cfg.dtype, label=f"wan full size, every row, {k}")
+    ref = oracle_step_rows(cfg, w, xs, window, qn, qr, chunk_first, frame_causal=True)
+    assert_step_close(to_numpy(outs["frame-causal"])[0], ref, cfg.dtype, label="wan full size, every row, frame-causal")
 
 
 def test_wan_full_size_frame_causal_wrapped_ring():

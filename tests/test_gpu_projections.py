@@ -143,6 +143,30 @@ def test_layer_step(name):
     _layer_steps(cfg, 55, n_chunks)
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_layer_step_where_the_per_head_form_is_taken(fused):
+    """A 32 x 32 grid with the Wan head shapes: a one-frame chunk has 1024
+    queries, so the layer step takes the per-head attention (also when the
+    absorbed query weights are set, since the per-head weights are there
+    too); chunk after chunk through ring wrap against O.layer_step, and the
+    frame-causal step on the same layer (latent form) in between."""
+    cfg = get_config("wan_small").with_(grid_y=32, grid_x=32, window_frames=3, chunk_frames=1)
+    w, wd = _weights(cfg, 58)
+    layer = LatentLayer(cfg, wd, batch=1, rope_n_t=64)
+    assert mla.chunk_attend_form(layer.shape, 1) == mla.FORM_HEADS
+    if fused:
+        layer.absorb_query_weights()
+    ring = O.RingCache(cfg.window_frames, cfg.tokens_per_frame, cfg.d_c, cfg.d_rope)
+    st = Stream(cfg, seed=58)
+    for f0 in range(5):
+        x = st.xs(f0, 1)
+        causal = f0 == 3
+        u = layer.step(to_torch(x[None], cfg.dtype), f0, 1, frame_causal=causal)
+        torch.cuda.synchronize()
+        ref, _, _, _ = O.layer_step(O.dims_of(cfg), w, ring, x, f0, frame_causal=causal)
+        assert_step_close(to_numpy(u)[0], ref, cfg.dtype, label=f"per-head layer step fused={fused} frame {f0}")
+
+
 def test_layer_step_frame_causal():
     cfg = get_config("wan_small").with_(chunk_frames=2, window_frames=4)
     _layer_steps(cfg, 56, 3, frame_causal=True)

@@ -70,7 +70,7 @@ def test_rollout_snapshot_and_restore_is_bitwise_identical():
           flush=True)
 
 
-@pytest.mark.parametrize("attend", ["attend", "attend_frame_causal", "attend_heads"])
+@pytest.mark.parametrize("attend", ["attend_latent", "attend_frame_causal", "attend_heads"])
 def test_repeated_calls_are_bitwise_identical(attend):
     """The Wan chunk step (its row blocks split between work-groups and
     merged) repeated on the same inputs gives the same bits, for the latent
