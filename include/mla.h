@@ -378,8 +378,12 @@ mla_status mla_output_project(const mla_shape* shape, const void* o, int32_t n_f
 
 /* ---------------------------------------------------------------- whole layer
  * One layer's chunk step in one call, on `stream`, in this order:
- * mla_query_project (queries from the chunk's tokens x), mla_cache_write
- * (the same tokens into the ring), mla_chunk_attend in the form
+ * mla_query_project (queries from the chunk's tokens x) together with
+ * mla_cache_write (the same tokens into the ring): the query latent and the
+ * cached rows [c | kR] come from one product of x with
+ * [W_dq ; W_dkv ; W_kR], so x is read once (the cached rows equal
+ * mla_cache_write's up to the order of the fp32 sums); then
+ * mla_chunk_attend in the form
  * mla_chunk_attend_form names or, with frame_causal != 0,
  * mla_chunk_attend_frame_causal (the chunk's queries over the window),
  * mla_output_project (u = W_o of the heads' outputs). The query

@@ -753,7 +753,44 @@ mla_status gemm(const mla_shape* s, const void* a, const void* b, const void* b2
   p.ldc = n_split;
   p.ldc2 = N - n_split;
   p.n_split = n_split;
+  p.n_split2 = N;
   return from_hip(mla::launch_gemm_nt(s->dtype, p, mla::gemm_tile_rows(p.M, N, device_cus()), st));
+}
+
+// The query latent and the cache write of the same tokens in one product:
+// x [W_dq ; W_dkv ; W_kR]^T, the first d_cq features into c_q, the rest
+// ([c | kR] of each token) into ring slot f mod W of its frame f, which the
+// kernel also records in slot_frame. Arguments checked by the callers.
+mla_status gemm_query_latent_and_cache(const mla_shape* s, int d_cq, const void* x, const void* w_dq,
+                                       const void* w_dkv, const void* w_kr, int frame_first, int n_frames,
+                                       void* c_q, void* cache, int32_t* slot_frame, hipStream_t st) {
+  const int64_t M = (int64_t)s->batch * n_frames * tokens_per_frame(s);
+  const int N = d_cq + s->d_c + s->d_rope;
+  if (check_gemm_tiles(M, N) != MLA_OK) return MLA_ERR_SHAPE;
+  mla::GemmParams p{};
+  p.a = x;
+  p.b = w_dq;
+  p.b2 = w_dkv;
+  p.b3 = w_kr;
+  p.c = c_q;
+  p.c2 = cache;
+  p.M = (int)M;
+  p.N = N;
+  p.K = s->hidden;
+  p.lda = s->hidden;
+  p.ldb = s->hidden;
+  p.ldc = d_cq;
+  p.ldc2 = s->d_c + s->d_rope;
+  p.n_split = d_cq;
+  p.n_split2 = d_cq + s->d_c;
+  p.ring.slot_frame = slot_frame;
+  p.ring.rows_per_b = (int)(n_frames * tokens_per_frame(s));
+  p.ring.T = (int)tokens_per_frame(s);
+  p.ring.W = s->window_frames;
+  p.ring.frame_first = frame_first;
+  p.ring.n_frames = n_frames;
+  p.ring.batch = s->batch;
+  return from_hip(mla::launch_gemm_ring(s->dtype, p, mla::gemm_tile_rows(p.M, N, device_cus()), st));
 }
 
 mla_status check_projection_rows(const mla_shape* s, int n_frames, int64_t* rows) {
@@ -765,9 +802,11 @@ mla_status check_projection_rows(const mla_shape* s, int n_frames, int64_t* rows
 
 }  // namespace
 
+// cq_ready: c_q already holds the query latent (the layer step computes it
+// together with the cache write); only the per-head queries are launched.
 static mla_status query_project_impl(const mla_shape* shape, int32_t d_cq, const void* x, int32_t n_frames,
                                      const void* w_dq, const void* w_uq, const void* w_qr, void* c_q, void* q_nope,
-                                     void* q_r, void* stream, bool run) {
+                                     void* q_r, void* stream, bool run, bool cq_ready = false) {
   mla_status st = check_shape(shape);
   if (st != MLA_OK) return st;
   if (!x || !w_dq || !w_uq || !w_qr || !c_q || !q_nope || !q_r) return MLA_ERR_NULL;
@@ -785,7 +824,8 @@ static mla_status query_project_impl(const mla_shape* shape, int32_t d_cq, const
     return st;
   if (!run) return MLA_OK;
   hipStream_t s = (hipStream_t)stream;
-  if ((st = gemm(shape, x, w_dq, nullptr, c_q, nullptr, rows, d_cq, d_cq, shape->hidden, s)) != MLA_OK) return st;
+  if (!cq_ready && (st = gemm(shape, x, w_dq, nullptr, c_q, nullptr, rows, d_cq, d_cq, shape->hidden, s)) != MLA_OK)
+    return st;
   // content and positional queries in one product over the same query latent
   return gemm(shape, c_q, w_uq, w_qr, q_nope, q_r, rows, n_nope + shape->n_heads * shape->d_rope, n_nope, d_cq, s);
 }
@@ -842,7 +882,8 @@ MLA_API mla_status mla_query_absorb_weights(const mla_shape* shape, int32_t d_cq
 static mla_status query_project_absorbed_impl(const mla_shape* shape, int32_t d_cq, const void* x,
                                               int32_t q_frame_first, int32_t n_frames, const void* w_dq,
                                               const void* w_qabs, const float* rope_tables, int32_t rope_t_first,
-                                              int32_t rope_n_t, void* c_q, void* q_abs, void* stream, bool run) {
+                                              int32_t rope_n_t, void* c_q, void* q_abs, void* stream, bool run,
+                                              bool cq_ready = false) {
   mla_status st = check_shape(shape);
   if (st != MLA_OK) return st;
   if (!x || !w_dq || !w_qabs || !c_q || !q_abs) return MLA_ERR_NULL;
@@ -860,7 +901,8 @@ static mla_status query_project_absorbed_impl(const mla_shape* shape, int32_t d_
   if ((st = check_gemm_tiles(rows, d_cq)) != MLA_OK || (st = check_gemm_tiles(rows, n_abs)) != MLA_OK) return st;
   if (!run) return MLA_OK;
   hipStream_t s = (hipStream_t)stream;
-  if ((st = gemm(shape, x, w_dq, nullptr, c_q, nullptr, rows, d_cq, d_cq, shape->hidden, s)) != MLA_OK) return st;
+  if (!cq_ready && (st = gemm(shape, x, w_dq, nullptr, c_q, nullptr, rows, d_cq, d_cq, shape->hidden, s)) != MLA_OK)
+    return st;
   mla::GemmParams p{};
   p.a = c_q;
   p.b = w_qabs;
@@ -873,6 +915,7 @@ static mla_status query_project_absorbed_impl(const mla_shape* shape, int32_t d_
   p.ldc = n_abs;
   p.ldc2 = 0;
   p.n_split = n_abs;
+  p.n_split2 = n_abs;
   p.qa.tables = rope_tables;
   p.qa.rl = rope_layout(shape, rope_t_first, rope_n_t);
   p.qa.kp = qabs_dim(shape);
@@ -938,6 +981,9 @@ MLA_API mla_status mla_layer_step(const mla_shape* shape, int32_t d_cq, const ml
   if ((st = check_query_args(shape, frame_first, n_frames)) != MLA_OK) return st;
   const size_t need = mla_layer_step_workspace_bytes(shape, d_cq, n_frames);
   if (need == 0) return MLA_ERR_SHAPE;
+  if (check_gemm_tiles((int64_t)shape->batch * n_frames * tokens_per_frame(shape), d_cq + shape->d_c + shape->d_rope) !=
+      MLA_OK)
+    return MLA_ERR_SHAPE;
   if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
   const LayerWs w = layer_ws_layout(shape, d_cq, n_frames);
   char* ws = (char*)workspace;
@@ -958,11 +1004,15 @@ MLA_API mla_status mla_layer_step(const mla_shape* shape, int32_t d_cq, const ml
     const size_t att_bytes = (size_t)(ws + w.total - att);
     for (int pass = 0; pass < 2; ++pass) {
       const bool run = pass == 1;
-      if ((st = query_project_absorbed_impl(shape, d_cq, x, frame_first, n_frames, W.w_dq, W.w_qabs, rope_tables,
-                                            rope_t_first, rope_n_t, c_q, q_abs, stream, run)) != MLA_OK)
-        return st;
-      if ((st = cache_write_impl(shape, x, W.w_dkv, W.w_kr, frame_first, n_frames, cache, slot_frame, stream, run)) !=
+      // the query latent and the cache write in one pass over x, then the rest
+      if ((st = cache_write_impl(shape, x, W.w_dkv, W.w_kr, frame_first, n_frames, cache, slot_frame, stream, false)) !=
           MLA_OK)
+        return st;
+      if (run && (st = gemm_query_latent_and_cache(shape, d_cq, x, W.w_dq, W.w_dkv, W.w_kr, frame_first, n_frames, c_q,
+                                                   cache, slot_frame, (hipStream_t)stream)) != MLA_OK)
+        return st;
+      if ((st = query_project_absorbed_impl(shape, d_cq, x, frame_first, n_frames, W.w_dq, W.w_qabs, rope_tables,
+                                            rope_t_first, rope_n_t, c_q, q_abs, stream, run, true)) != MLA_OK)
         return st;
       if ((st = attend_absorbed_impl(shape, q_abs, frame_first, n_frames, W.w_uv, cache, slot_frame, rope_tables,
                                      rope_t_first, rope_n_t, o2, att, att_bytes, stream, causal, run)) != MLA_OK)
@@ -974,11 +1024,15 @@ MLA_API mla_status mla_layer_step(const mla_shape* shape, int32_t d_cq, const ml
   // every part is validated before the first launch
   for (int pass = 0; pass < 2; ++pass) {
     const bool run = pass == 1;
-    if ((st = query_project_impl(shape, d_cq, x, n_frames, W.w_dq, W.w_uq, W.w_qr, c_q, q_nope, q_r, stream, run)) !=
+    // the query latent and the cache write in one pass over x, then the rest
+    if ((st = cache_write_impl(shape, x, W.w_dkv, W.w_kr, frame_first, n_frames, cache, slot_frame, stream, false)) !=
         MLA_OK)
       return st;
-    if ((st = cache_write_impl(shape, x, W.w_dkv, W.w_kr, frame_first, n_frames, cache, slot_frame, stream, run)) !=
-        MLA_OK)
+    if (run && (st = gemm_query_latent_and_cache(shape, d_cq, x, W.w_dq, W.w_dkv, W.w_kr, frame_first, n_frames, c_q,
+                                                 cache, slot_frame, (hipStream_t)stream)) != MLA_OK)
+      return st;
+    if ((st = query_project_impl(shape, d_cq, x, n_frames, W.w_dq, W.w_uq, W.w_qr, c_q, q_nope, q_r, stream, run,
+                                 true)) != MLA_OK)
       return st;
     if (heads) {
       st = chunk_attend_heads_impl(shape, q_nope, q_r, frame_first, n_frames, W.w_uk, W.w_uv, cache, slot_frame,

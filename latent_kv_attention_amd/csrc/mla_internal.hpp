@@ -135,15 +135,30 @@ struct GemmQabs {
   float qscale;                       // softmax scale * log2(e)
 };
 
+// Ring epilogue of a product whose second output part is the cache write:
+// token row r (stream b = r / rows_per_b, chunk token t = r % rows_per_b) of
+// part 2 goes to cache row (b W + (frame_first + t / T) mod W) T + t mod T
+// (row stride ldc2 = d_c + d_rope), and slot_frame[b][f mod W] = f is set for
+// every written frame f.
+struct GemmRing {
+  int32_t* slot_frame;  // nullptr: part 2 is a plain matrix
+  int rows_per_b, T, W, frame_first, n_frames, batch;
+};
+
 struct GemmParams {
   const void* a;
   const void* b;
   const void* b2;
+  const void* b3;
   void* c;
   void* c2;
-  int M, N, K, lda, ldb, ldc, ldc2, n_split;
+  // features n < n_split: weight b row n, output c column n; n_split <= n <
+  // n_split2: weight b2 row n - n_split; n >= n_split2: weight b3 row
+  // n - n_split2; both of the last two land in c2 column n - n_split
+  int M, N, K, lda, ldb, ldc, ldc2, n_split, n_split2;
   int tiles_n, n_logical, per_xcd;  // filled by the launcher
   GemmQabs qa;                      // used only by the absorbed-query launch
+  GemmRing ring;                    // used only by the ring launch
 };
 
 // Absorbed query weight of each head: w_qabs[h][j][:] = (W_uk[h]^T W_uq[h])[j][:]
@@ -178,6 +193,8 @@ int gemm_tile_rows(int M, int N, int n_cu);
 hipError_t launch_gemm_nt(int dtype, const GemmParams& p, int tile_rows, hipStream_t s);
 // the same product with the absorbed-query epilogue (p.qa)
 hipError_t launch_gemm_qabs(int dtype, const GemmParams& p, int tile_rows, hipStream_t s);
+// the same product with part 2 scattered into the ring cache (p.ring)
+hipError_t launch_gemm_ring(int dtype, const GemmParams& p, int tile_rows, hipStream_t s);
 hipError_t launch_qabs_weights(int dtype, const QabsWeightParams& p, hipStream_t s);
 
 }  // namespace mla

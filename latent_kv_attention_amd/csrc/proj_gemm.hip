@@ -23,7 +23,14 @@
 // The output features may come in two parts with their own weight and
 // output arrays (features n >= n_split: weight B2 row n - n_split, output
 // C2 column n - n_split), so that the per-head content and positional
-// queries, which read the same query latent, are one launch.
+// queries, which read the same query latent, are one launch. The second
+// part's weight may itself be two arrays (B2, then B3 from n_split2 on).
+//
+// Ring variant (RING): the second part is the cache write of the same
+// tokens (hyper.ai summary, Method: the query latent and the compressed
+// latent both come from the token): x [W_dq ; W_dkv ; W_kR]^T gives the
+// query latent and each token's cached row [c | kR] in one pass over x, and
+// the epilogue stores the cached rows into their ring slots.
 //
 // Absorbed-query variant (QABS): the weight is the per-head stack
 // [W_uk[h]^T W_uq[h] ; W_qr[h] ; 0] (qabs_weights_kernel), so one product
@@ -43,7 +50,7 @@ constexpr int kGemmBK = 64;
 constexpr int kGemmXcds = 8;
 }  // namespace
 
-template <typename T, int BM, int BN, bool QABS>
+template <typename T, int BM, int BN, bool QABS, bool RING>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
   typedef typename V8<T>::type v8;
   constexpr int BK = kGemmBK;
@@ -63,6 +70,14 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
 
   const int logical = (blockIdx.x % kGemmXcds) * p.per_xcd + blockIdx.x / kGemmXcds;
   if (logical >= p.n_logical) return;
+  if constexpr (RING) {
+    if (logical == 0) {
+      for (int e = threadIdx.x; e < p.ring.batch * p.ring.n_frames; e += blockDim.x) {
+        const int b = e / p.ring.n_frames, f = p.ring.frame_first + e % p.ring.n_frames;
+        p.ring.slot_frame[b * p.ring.W + f % p.ring.W] = f;
+      }
+    }
+  }
   const int row0 = (logical / p.tiles_n) * BM;
   const int col0 = (logical % p.tiles_n) * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -83,7 +98,8 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
     } else {
       const int n = min(col0 + r - BM, p.N - 1);
       src[j] = n < p.n_split ? (const T*)p.b + (size_t)n * p.ldb + c * 8
-                             : (const T*)p.b2 + (size_t)(n - p.n_split) * p.ldb + c * 8;
+               : n < p.n_split2 ? (const T*)p.b2 + (size_t)(n - p.n_split) * p.ldb + c * 8
+                                : (const T*)p.b3 + (size_t)(n - p.n_split2) * p.ldb + c * 8;
     }
     dst[j] = r * LDK + c * 8;
     kof[j] = c * 8;
@@ -178,8 +194,13 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmParams p) {
     const int r = e / (BN / 8), c8 = (e % (BN / 8)) * 8;
     const int n = col0 + c8;
     if (row0 + r < p.M && n < p.N) {
-      T* dstp = n < p.n_split ? (T*)p.c + (size_t)(row0 + r) * p.ldc + n
-                              : (T*)p.c2 + (size_t)(row0 + r) * p.ldc2 + (n - p.n_split);
+      size_t row2 = (size_t)(row0 + r);
+      if constexpr (RING) {
+        const GemmRing& g = p.ring;
+        const int b = (row0 + r) / g.rows_per_b, t = (row0 + r) - b * g.rows_per_b;
+        row2 = ((size_t)b * g.W + (g.frame_first + t / g.T) % g.W) * g.T + t % g.T;
+      }
+      T* dstp = n < p.n_split ? (T*)p.c + (size_t)(row0 + r) * p.ldc + n : (T*)p.c2 + row2 * p.ldc2 + (n - p.n_split);
       store8<T>(dstp, lds_load8<T>(lds + r * LDC + c8));
     }
   }
@@ -190,31 +211,36 @@ int gemm_tile_rows(int M, int N, int n_cu) {
   return big >= n_cu ? 128 : 64;
 }
 
-template <typename T, int BM, int BN, bool QABS>
+template <typename T, int BM, int BN, bool QABS, bool RING>
 static hipError_t launch_gemm_t(GemmParams p, hipStream_t s) {
   p.tiles_n = (p.N + BN - 1) / BN;
   p.n_logical = ((p.M + BM - 1) / BM) * p.tiles_n;
   p.per_xcd = (p.n_logical + kGemmXcds - 1) / kGemmXcds;
-  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, QABS>), dim3(p.per_xcd * kGemmXcds), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_nt_kernel<T, BM, BN, QABS, RING>), dim3(p.per_xcd * kGemmXcds), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
-template <bool QABS>
+template <bool QABS, bool RING>
 static hipError_t launch_gemm_any(int dtype, const GemmParams& p, int tile_rows, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   if (tile_rows == 128)
-    return dtype == 0 ? launch_gemm_t<bf16, 128, 128, QABS>(p, s) : launch_gemm_t<float, 128, 128, QABS>(p, s);
+    return dtype == 0 ? launch_gemm_t<bf16, 128, 128, QABS, RING>(p, s)
+                      : launch_gemm_t<float, 128, 128, QABS, RING>(p, s);
   if (tile_rows == 64)
-    return dtype == 0 ? launch_gemm_t<bf16, 64, 64, QABS>(p, s) : launch_gemm_t<float, 64, 64, QABS>(p, s);
+    return dtype == 0 ? launch_gemm_t<bf16, 64, 64, QABS, RING>(p, s) : launch_gemm_t<float, 64, 64, QABS, RING>(p, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_nt(int dtype, const GemmParams& p, int tile_rows, hipStream_t s) {
-  return launch_gemm_any<false>(dtype, p, tile_rows, s);
+  return launch_gemm_any<false, false>(dtype, p, tile_rows, s);
 }
 
 hipError_t launch_gemm_qabs(int dtype, const GemmParams& p, int tile_rows, hipStream_t s) {
-  return launch_gemm_any<true>(dtype, p, tile_rows, s);
+  return launch_gemm_any<true, false>(dtype, p, tile_rows, s);
+}
+
+hipError_t launch_gemm_ring(int dtype, const GemmParams& p, int tile_rows, hipStream_t s) {
+  return launch_gemm_any<false, true>(dtype, p, tile_rows, s);
 }
 
 // Absorbed query weights, once per layer: one thread per output element,
