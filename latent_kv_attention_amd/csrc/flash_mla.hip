@@ -143,7 +143,8 @@ struct FlashTile {
 
 // 3D-RoPE of the window's positional keys, once per call: key v = (slot
 // rank r, token tok) of stream b gets R(t, y, x) kR, with t the frame held
-// by the r-th valid slot and (y, x) the token's grid cell, rounded to the
+// by the slot of rank r (valid slots ranked by frame, window_rank) and
+// (y, x) the token's grid cell, rounded to the
 // cache's element type. Row v of the stream's block of p.krot. One thread per
 // rotary pair; grid (pair blocks, slots, stream groups). The temporal angles
 // of the slot's frame are formed here (any frame index; the caller's tables
@@ -169,8 +170,7 @@ __global__ __launch_bounds__(256) void rope_window_kernel(FlashParams p) {
                                                    &t_cs[1][threadIdx.x]);
     __syncthreads();
     if (!active) continue;
-    int rank = 0;
-    for (int j = 0; j < slot; ++j) rank += sf[j] >= 0 ? 1 : 0;
+    const int rank = window_rank_of_slot(sf, p.W, slot);
     const T* src = (const T*)p.cache + (((size_t)b * p.W + slot) * p.T + tok) * (DC + DR) + DC + 2 * k;
     float a0 = to_f<T>(src[0]), a1 = to_f<T>(src[1]), cs, sn;
     if (k < n_tp) {
@@ -257,43 +257,42 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
   // starts with that block's first tiles, so at any moment most work-groups
   // read the same few key tiles and share them through the L2.
   for (long long u = u_last; u > u_first;) {
-    const long long rbg = (u - 1) / p.nt_max;  // row block over all streams
-    const long long seg0 = max(u_first, rbg * p.nt_max);
-    const int j0 = (int)(seg0 - rbg * p.nt_max);
-    const int j1 = (int)(u - rbg * p.nt_max);
+    long long rbg, ua;  // row block over all streams, its first unit
+    int nt;             // its unit count
+    locate_unit(p.classes, p.n_rb, u - 1, rbg, ua, nt);
+    const long long seg0 = max(u_first, ua);
+    const int j0 = (int)(seg0 - ua);
+    const int j1 = (int)(u - ua);
     const bool first_seg = seg0 == u_first;
-    const bool whole = j0 == 0 && j1 == p.nt_max;
+    const bool whole = j0 == 0 && j1 == nt;
     u = seg0;
     const int b = (int)(rbg / p.n_rb), rb = (int)(rbg - (long long)b * p.n_rb);
     const int row_wave = rb * F::kRowsBlock + wave * F::kRowsWave;
     __syncthreads();  // LDS of the previous segment is no longer read
 
-    // valid ring slots of stream b in slot order
+    // valid ring slots of stream b in key order (by frame, window_rank)
     if (wave == 0) {
       const int f = lane < p.W ? p.slot_frame[b * p.W + lane] : -1;
-      const unsigned long long mask = __ballot(f >= 0);
+      const int rank = window_rank(f, lane);
       if (f >= 0) {
-        const int rank = __popcll(mask & ((1ull << lane) - 1ull));
         slot_of[rank] = lane;
         if constexpr (CAUSAL) frame_of[rank] = f;
       }
+      const unsigned long long mask = __ballot(f >= 0);
       if (lane == 0) n_valid_sh = __popcll(mask);
     }
     __syncthreads();
 
     const int n_keys = n_valid_sh * p.T;
-    const int n_tiles = (n_keys + kBN - 1) / kBN;
-    // this segment's share of the window's tiles (units map onto the tiles
-    // of a full window; a partly filled window scales proportionally)
-    const int tile_begin = (int)((long long)j0 * n_tiles / p.nt_max);
-    const int tile_end = (int)((long long)j1 * n_tiles / p.nt_max);
-    const int n_visit = max(0, tile_end - tile_begin);
 
     // frame-causal variant: query frame of this lane's two rows (rows are
     // (token, head) pairs, H per token, T tokens per frame) and the range of
     // query frames of the row block
     int qfr[kNMB] = {};
     int rb_fmin = 0, rb_fmax = 0;
+    // keys the row block visits: the whole window, or under the frame-causal
+    // mask the prefix of frames up to its last row's (keys are in frame order)
+    int n_keys_rb = n_keys;
     if constexpr (CAUSAL) {
       const int rows_per_frame = p.T * p.H;
 #pragma unroll
@@ -304,7 +303,16 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
       const int r_first = rb * F::kRowsBlock, r_last = min(r_first + F::kRowsBlock, p.Mb) - 1;
       rb_fmin = p.q_frame_first + r_first / rows_per_frame;
       rb_fmax = p.q_frame_first + r_last / rows_per_frame;
+      int n_vis = 0;
+      for (int r = 0; r < n_valid_sh; ++r) n_vis += frame_of[r] <= rb_fmax ? 1 : 0;
+      n_keys_rb = n_vis * p.T;
     }
+    // this segment's share of the row block's tiles (units map onto the
+    // tiles of a full window; a partly filled window scales proportionally)
+    const int n_tiles = (n_keys_rb + kBN - 1) / kBN;
+    const int tile_begin = (int)((long long)j0 * n_tiles / nt);
+    const int tile_end = (int)((long long)j1 * n_tiles / nt);
+    const int n_visit = max(0, tile_end - tile_begin);
 
     // queries of this wave (B operand of S^T = K Q^T), kept in registers
     v8 qf[kNMB][F::NKC];
@@ -429,15 +437,11 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     typedef std::integral_constant<int, 1> B1;
 
     // frame-causal variant: frames of the tile's keys against the row
-    // block's query frames (a tile spans at most kBN / T + 2 slot ranks)
+    // block's query frames; keys are in frame order, so the tile's first and
+    // last keys hold its earliest and latest frames
     auto tile_class = [&](int kbase) -> int {
-      const int r0 = div_floor(kbase, p.T, p.inv_T), r1 = div_floor(min(kbase + kBN, n_keys) - 1, p.T, p.inv_T);
-      int fmin = 0x7fffffff, fmax = -0x7fffffff;
-      for (int r = r0; r <= r1; ++r) {
-        const int f = frame_of[r];
-        fmin = min(fmin, f);
-        fmax = max(fmax, f);
-      }
+      const int fmin = frame_of[div_floor(kbase, p.T, p.inv_T)];
+      const int fmax = frame_of[div_floor(min(kbase + kBN, n_keys) - 1, p.T, p.inv_T)];
       return fmin > rb_fmax ? 2 : (fmax <= rb_fmin ? 0 : 1);
     };
 
@@ -706,7 +710,7 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
 
 // Merge of the partial results of a row block shared by work-groups
 // g0..g1 (the work-groups whose unit ranges meet the row block's units
-// [a, a + nt_max)). Piece g holds o_g / l_g and lw_g = r_g + log2 l_g, the
+// [a, a + nt)). Piece g holds o_g / l_g and lw_g = r_g + log2 l_g, the
 // log2 of its total weight sum_j 2^(s_j) (r_g its reference); with
 // M = max_g lw_g and w_g = 2^(lw_g - M) <= 1 the row is
 // o = sum_g w_g (o_g / l_g) / sum_g w_g. The heaviest piece has w_g = 1, so
@@ -728,10 +732,12 @@ __global__ __launch_bounds__(256) void flash_combine_kernel(FlashParams p) {
   const long long G = p.grid;
   const long long rbg = blockIdx.x / (RB / kMergeRows);
   const int row_lo = (int)(blockIdx.x % (RB / kMergeRows)) * kMergeRows;
-  const long long a = rbg * p.nt_max;
+  long long a;
+  int nt;
+  row_block_units(p.classes, p.n_rb, rbg, a, nt);
   // largest g whose range starts at or before unit x
   auto owner = [&](long long x) { return ((x + 1) * G - 1) / p.units; };
-  const long long g0 = owner(a), g1 = owner(a + p.nt_max - 1);
+  const long long g0 = owner(a), g1 = owner(a + nt - 1);
   if (g0 == g1) return;  // one work-group covered the row block and wrote it
   const int np = (int)(g1 - g0 + 1);  // <= kMaxMergePieces by the host's cap on G
   if ((int)threadIdx.x < np) {
@@ -810,12 +816,12 @@ __global__ __launch_bounds__(256) void flash_exact_kernel(FlashParams p) {
     __syncthreads();
     if (tid < 64) {
       const int f = tid < p.W ? p.slot_frame[b * p.W + tid] : -1;
-      const unsigned long long mask = __ballot(f >= 0);
+      const int rank = window_rank(f, tid);
       if (f >= 0) {
-        const int rank = __popcll(mask & ((1ull << tid) - 1ull));
         slot_of[rank] = tid;
         frame_of[rank] = f;
       }
+      const unsigned long long mask = __ballot(f >= 0);
       if (tid == 0) n_valid_sh = __popcll(mask);
     }
     for (int d = tid; d < DK; d += 256) q[d] = to_f<T>(((const T*)p.q_abs)[(size_t)grow * KP + d]);

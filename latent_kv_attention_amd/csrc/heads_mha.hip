@@ -51,11 +51,12 @@ __device__ __forceinline__ void store4_bf16(bf16* dst, float a, float b, float c
   *reinterpret_cast<u32x2*>(dst) = u32x2{w0, w1};
 }
 
-// valid slots of stream b in slot order (wave 0); returns nothing, fills LDS
+// valid slots of stream b in key order (by frame, window_rank; wave 0); fills LDS
 __device__ __forceinline__ void slot_ranks(const HeadsParams& p, int b, int lane, int* slot_of, int* n_valid) {
   const int f = lane < p.W ? p.slot_frame[b * p.W + lane] : -1;
+  const int rank = window_rank(f, lane);  // key order of the rotated kR (rope_window_kernel)
+  if (f >= 0) slot_of[rank] = lane;
   const unsigned long long mask = __ballot(f >= 0);
-  if (f >= 0) slot_of[__popcll(mask & ((1ull << lane) - 1ull))] = lane;
   if (lane == 0) *n_valid = __popcll(mask);
 }
 }  // namespace

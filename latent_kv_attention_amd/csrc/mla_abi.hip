@@ -111,15 +111,50 @@ struct FlashPlan {
   int64_t units;
   int grid;
   bool split;  // some row block is shared by several work-groups
+  mla::UnitClasses classes;
 };
 
-FlashPlan flash_plan(const mla_shape* s, int q_n_frames, int kv_splits) {
+// With the frame-causal mask and the automatic split, a row block's units
+// cover only the keys its rows may see: with keys in frame order, the frames
+// up to its last row's, W - (q_n_frames - 1 - k) frames of a full window for
+// a row block whose last row is a query of chunk frame k. Without the mask
+// (or with fixed key splits) every row block has the nt_max tiles of a full
+// window.
+FlashPlan flash_plan(const mla_shape* s, int q_n_frames, int kv_splits, bool causal = false) {
   FlashPlan f;
-  const int64_t Mb = (int64_t)q_n_frames * tokens_per_frame(s) * s->n_heads;
+  const int64_t T = tokens_per_frame(s);
+  const int64_t Mb = (int64_t)q_n_frames * T * s->n_heads;
   const int rpb = flash_rows_per_block(s), tk = flash_tile_keys(s);
   f.n_rb = (int)((Mb + rpb - 1) / rpb);
-  f.nt_max = (int)((s->window_frames * tokens_per_frame(s) + tk - 1) / tk);
-  f.units = (int64_t)s->batch * f.n_rb * f.nt_max;
+  f.nt_max = (int)((s->window_frames * T + tk - 1) / tk);
+  mla::UnitClasses& c = f.classes;
+  c = mla::UnitClasses{};
+  if (causal && kv_splits == 0 && q_n_frames <= mla::kMaxUnitClasses) {
+    const int64_t rows_per_frame = T * s->n_heads;
+    int64_t u = 0;
+    c.n = 0;
+    for (int k = 0; k < q_n_frames; ++k) {
+      // row blocks whose last row lies in chunk frame k
+      const int64_t end = k + 1 < q_n_frames ? ((k + 1) * rows_per_frame) / rpb : f.n_rb;
+      const int64_t start = c.n == 0 ? 0 : c.rb_end[c.n - 1];
+      if (end <= start) continue;
+      const int64_t frames = (int64_t)s->window_frames - (q_n_frames - 1 - k);
+      const int nt = (int)(frames < 1 ? 1 : (frames * T + tk - 1) / tk);
+      c.rb_end[c.n] = (int)end;
+      c.nt[c.n] = nt;
+      c.u0[c.n] = u;
+      u += (end - start) * nt;
+      ++c.n;
+    }
+    c.per_stream = u;
+  } else {
+    c.n = 1;
+    c.rb_end[0] = f.n_rb;
+    c.nt[0] = f.nt_max;
+    c.u0[0] = 0;
+    c.per_stream = (int64_t)f.n_rb * f.nt_max;
+  }
+  f.units = (int64_t)s->batch * c.per_stream;
   const int64_t row_blocks = (int64_t)s->batch * f.n_rb;
   int64_t g = kv_splits > 0 ? row_blocks * kv_splits : device_cus();
   if (g > f.units) g = f.units;
@@ -128,7 +163,7 @@ FlashPlan flash_plan(const mla_shape* s, int q_n_frames, int kv_splits) {
   if (g < 1) g = 1;
   if (g > (INT64_C(1) << 23)) g = INT64_C(1) << 23;  // rejected by flash_plan_ok
   f.grid = (int)g;
-  f.split = !(f.units % g == 0 && (f.units / g) % f.nt_max == 0);
+  f.split = c.n > 1 || !(f.units % g == 0 && (f.units / g) % f.nt_max == 0);
   return f;
 }
 
@@ -158,8 +193,12 @@ FlashWs flash_ws_layout(const mla_shape* s, int q_n_frames, const FlashPlan& f) 
   return w;
 }
 
+// (covers both masks: the frame-causal plan may split row blocks where the
+// plain one does not)
 size_t flash_ws_bytes(const mla_shape* s, int q_n_frames, int kv_splits) {
-  return flash_ws_layout(s, q_n_frames, flash_plan(s, q_n_frames, kv_splits)).total;
+  const size_t a = flash_ws_layout(s, q_n_frames, flash_plan(s, q_n_frames, kv_splits, false)).total;
+  const size_t b = flash_ws_layout(s, q_n_frames, flash_plan(s, q_n_frames, kv_splits, true)).total;
+  return a > b ? a : b;
 }
 
 mla_status from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
@@ -196,7 +235,7 @@ mla_status do_absorb(const mla_shape* s, const void* q_nope, const void* q_r, in
 mla_status do_flash(const mla_shape* s, const void* q_abs, int q_n_frames, const void* cache,
                     const int32_t* slot_frame, const float* tables, int rope_t_first, int rope_n_t, void* o_lat,
                     int kv_splits, void* ws, hipStream_t st, bool frame_causal = false, int q_frame_first = 0) {
-  const FlashPlan f = flash_plan(s, q_n_frames, kv_splits);
+  const FlashPlan f = flash_plan(s, q_n_frames, kv_splits, frame_causal);
   mla::FlashParams p;
   p.q_abs = q_abs;
   p.cache = cache;
@@ -222,6 +261,7 @@ mla_status do_flash(const mla_shape* s, const void* q_abs, int q_n_frames, const
   p.n_rb = f.n_rb;
   p.nt_max = f.nt_max;
   p.units = f.units;
+  p.classes = f.classes;
   p.grid = f.grid;
   p.scale_log2 = scale_log2(s);
   p.rope_base = (double)s->rope_base;

@@ -182,6 +182,33 @@ __device__ __forceinline__ float wave_sum_across_groups(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Order of a stream's window keys: by the frame their slot holds, oldest
+// first (ties, which the ring never produces, by slot), token order inside a
+// frame. Rank of the slot whose frame is `f` (this lane's slot `lane`, -1 =
+// empty) among the valid slots; every lane of the wave passes its own slot.
+// With keys in frame order, the keys a query of frame q may see under the
+// frame-causal mask are a prefix of the window.
+__device__ __forceinline__ int window_rank(int f, int lane) {
+  int r = 0;
+#pragma unroll 8
+  for (int j = 0; j < 64; ++j) {
+    const int fj = __shfl(f, j, 64);
+    r += (fj >= 0 && (fj < f || (fj == f && j < lane))) ? 1 : 0;
+  }
+  return r;
+}
+
+// The same rank from the slot table directly (one thread, W reads).
+__device__ __forceinline__ int window_rank_of_slot(const int32_t* sf, int W, int slot) {
+  const int f = sf[slot];
+  int r = 0;
+  for (int j = 0; j < W; ++j) {
+    const int fj = sf[j];
+    r += (fj >= 0 && (fj < f || (fj == f && j < slot))) ? 1 : 0;
+  }
+  return r;
+}
+
 // Rotation of one interleaved pair by the angle whose cos/sin are given.
 __device__ __forceinline__ void rotate_pair(float& a, float& b, float c, float s) {
   const float a0 = a, b0 = b;

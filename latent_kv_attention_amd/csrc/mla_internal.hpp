@@ -45,11 +45,49 @@ struct AbsorbParams {
   float qscale;        // softmax scale * log2(e)
 };
 
-// The attention work is a grid of units (row block, key tile): n_rb row
-// blocks per stream, nt_max tiles of a full window per row block, units =
-// batch * n_rb * nt_max in row-block-major order. Work-group g of G takes
-// units [g U / G, (g + 1) U / G); a row block that falls to several
+// The attention work is a grid of units (row block, key tile) in
+// row-block-major order. Row blocks come in classes of consecutive blocks
+// (one class without the frame-causal mask; with it, class k holds the row
+// blocks whose last row is a query of chunk frame k), and every row block of
+// class k has nt[k] units, the key tiles of the window part its rows may see
+// when the window is full (the frames up to its last row's). Work-group g of
+// G takes units [g U / G, (g + 1) U / G); a row block that falls to several
 // work-groups is finished by a merge pass over their partial results.
+constexpr int kMaxUnitClasses = 64;
+struct UnitClasses {
+  int n;                          // classes
+  int rb_end[kMaxUnitClasses];    // row block after the last of class k (within a stream)
+  int nt[kMaxUnitClasses];        // units per row block of class k
+  long long u0[kMaxUnitClasses];  // first unit of class k within a stream
+  long long per_stream;           // units of one stream
+};
+
+// Row block rbg (over all streams) holding unit u: its first unit a and its
+// unit count nt.
+__host__ __device__ inline void locate_unit(const UnitClasses& c, int n_rb, long long u, long long& rbg,
+                                            long long& a, int& nt) {
+  const long long b = u / c.per_stream, v = u - b * c.per_stream;
+  int k = 0;
+  while (k + 1 < c.n && v >= c.u0[k + 1]) ++k;
+  const int rb0 = k == 0 ? 0 : c.rb_end[k - 1];
+  const long long r = (v - c.u0[k]) / c.nt[k];
+  rbg = b * n_rb + rb0 + r;
+  a = b * c.per_stream + c.u0[k] + r * c.nt[k];
+  nt = c.nt[k];
+}
+
+// First unit and unit count of row block rbg (over all streams).
+__host__ __device__ inline void row_block_units(const UnitClasses& c, int n_rb, long long rbg, long long& a,
+                                                int& nt) {
+  const long long b = rbg / n_rb;
+  const int rb = (int)(rbg - b * n_rb);
+  int k = 0;
+  while (k + 1 < c.n && rb >= c.rb_end[k]) ++k;
+  const int rb0 = k == 0 ? 0 : c.rb_end[k - 1];
+  a = b * c.per_stream + c.u0[k] + (long long)(rb - rb0) * c.nt[k];
+  nt = c.nt[k];
+}
+
 struct FlashParams {
   const void* q_abs;       // [B][Mb][Q]
   const void* cache;       // [B][W][T][d_c + d_rope]
@@ -68,7 +106,8 @@ struct FlashParams {
   float inv_T, inv_grid_x; // 1/T and 1/grid_x (key index -> slot, row, column)
   int n_rb, nt_max;        // row blocks per stream, key tiles of a full window
   int H, q_frame_first;    // heads; first query frame (frame-causal variant)
-  long long units;         // batch * n_rb * nt_max
+  long long units;         // all units: batch * classes.per_stream
+  UnitClasses classes;
   int grid;                // G, work-groups of the attention kernel
   float scale_log2;        // softmax scale * log2(e)
   double rope_base;        // RoPE base (the keys' temporal angles are formed per call)
