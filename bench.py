@@ -238,8 +238,11 @@ def setup_step(cfg, kv_splits, dev="cuda"):
     def write():
         mla.cache_write(shape, x_chunk, w["w_dkv"], w["w_kr"], chunk_first, cfg.chunk_frames, cache, slot_frame)
 
+    def flash():
+        mla.flash_attend(shape, q_abs, cfg.chunk_frames, cache, slot_frame, tables, 0, n_t, o_lat, ws, kv_splits)
+
     return types.SimpleNamespace(shape=shape, w=w, x_chunk=x_chunk, chunk_first=chunk_first, cache=cache,
-                                 slot_frame=slot_frame, out=out, step=step, write=write, qn=qn, qr=qr,
+                                 slot_frame=slot_frame, out=out, step=step, write=write, flash=flash, qn=qn, qr=qr,
                                  tables=tables, n_t=n_t)
 
 
@@ -559,9 +562,11 @@ def configs_report(args):
             for f0 in range(0, prefill_frames, 3):
                 layer.write(fill(l, f0), f0, 3)
         first = prefill_frames
+        attend = (lambda layer, *a, **k: layer.attend_latent(*a, **k)) if args.configs_form == "latent" else \
+            (lambda layer, *a, **k: layer.attend(*a, **k))
         for l, layer in enumerate(layers):  # warm-up chunk, rewritten in the timed run
             layer.write(fill(l, first), first, 3)
-            layer.attend(qn, qr, first, 3, out=out)
+            attend(layer, qn, qr, first, 3, out=out)
         torch.cuda.synchronize()
         # token inputs of every (chunk, layer) gathered before the clock starts
         xs = {}
@@ -578,7 +583,7 @@ def configs_report(args):
             for l, layer in enumerate(layers):
                 key = tuple((f0 + 7 * l + 13 * b) % 64 for b in range(B))
                 layer.write(xs[key], f0, 3)
-                layer.attend(qn, qr, f0, 3, out=out)
+                attend(layer, qn, qr, f0, 3, out=out)
         e.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(e)
@@ -603,7 +608,8 @@ def configs_report(args):
         ms, fl, slots = run(name, B, n_chunks, prefill)
         print(json.dumps({
             "report": f"Wan2.1-1.3B-shaped workload: {what}, 1 MI355X",
-            "config": name, "streams": B, "layers": 30, "chunks": n_chunks, "total_ms": round(ms, 2),
+            "config": name, "form": args.configs_form, "streams": B, "layers": 30, "chunks": n_chunks,
+            "total_ms": round(ms, 2),
             "ms_per_layer_chunk": round(ms / (30 * n_chunks), 4),
             "ms_per_chunk_all_layers": round(ms / n_chunks, 3),
             "attention_TFLOP": round(fl / 1e12, 2), "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 1),
@@ -631,6 +637,9 @@ def main():
     ap.add_argument("--configs", nargs="*", default=None, metavar="NAME",
                     help="time the 30-layer fill (wan_fill30), 8-stream (wan_batch8) and 80-chunk rollout "
                          "(wan_rollout) workloads, or only those named (report lines) and exit")
+    ap.add_argument("--configs-form", choices=["latent", "selected"], default="latent",
+                    help="attention form of --configs: the latent form (mla_chunk_attend_latent, the benchmark's "
+                         "kernel) or the one mla_chunk_attend selects for the shape")
     ap.add_argument("--latent-sweep", action="store_true",
                     help="time the step at every latent width with kernels (one report line each) and exit")
     ap.add_argument("--mfma-ceiling", action="store_true",

@@ -139,6 +139,11 @@ struct FlashTile {
   static_assert(DC % 16 == 0 && DR % 8 == 0 && (DR / 8 & (DR / 8 - 1)) == 0,
                 "latent in 16-wide blocks; kR in a power-of-two number of 8-element units");
   static_assert(LS % 4 == 0 && (LS * sizeof(T)) % 16 == 0, "LDS rows must stay 16-byte aligned");
+  // The pipelined tile body keeps a second score block and operands of the
+  // next half in registers besides the queries (4 NKC kNMB registers) and
+  // the output accumulators (4 NDB kNMB); where those two take more than 152
+  // of the 256 (d_c 192 with d_rope 64) it spills, and the plain body runs.
+  static constexpr bool kPipelined = 4 * (NKC + NDB) * kNMB <= 152;
 };
 
 // 3D-RoPE of the window's positional keys, once per call: key v = (slot
@@ -560,18 +565,28 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
             __builtin_amdgcn_sched_barrier(0);
           }
         };
-        sblk s_cur;
-        scores(cur, cur_r, 0, s_cur, negref);
+        if constexpr (F::kPipelined) {
+          sblk s_cur;
+          scores(cur, cur_r, 0, s_cur, negref);
 #pragma unroll 1
-        for (int half = 0; half + 1 < NKC2; ++half) {
-          sblk s_nxt;
-          body(half, s_cur, s_nxt, std::integral_constant<bool, true>());
+          for (int half = 0; half + 1 < NKC2; ++half) {
+            sblk s_nxt;
+            body(half, s_cur, s_nxt, std::integral_constant<bool, true>());
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int mb = 0; mb < kNMB; ++mb) s_cur[kb][mb] = s_nxt[kb][mb];
+              for (int mb = 0; mb < kNMB; ++mb) s_cur[kb][mb] = s_nxt[kb][mb];
+          }
+          body(NKC2 - 1, s_cur, s_cur, std::integral_constant<bool, false>());
+        } else {
+          // one half after the other (no second score block in flight)
+#pragma unroll 1
+          for (int half = 0; half < NKC2; ++half) {
+            sblk s;
+            scores(cur, cur_r, half, s, negref);
+            body(half, s, s, std::integral_constant<bool, false>());
+          }
         }
-        body(NKC2 - 1, s_cur, s_cur, std::integral_constant<bool, false>());
       };
       if constexpr (CAUSAL) {
         // 0: all keys visible to the block, 1: masked per key, 2: none visible
