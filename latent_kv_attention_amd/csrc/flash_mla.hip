@@ -38,10 +38,11 @@
 //     latent into rows 416 bytes apart, which keeps both LDS read patterns
 //     below nearly free of bank conflicts, the rotated kR into a packed
 //     region whose 16-byte units are XOR-swizzled by key for the same reason;
-//   * within a tile each wave is software-pipelined over 32-key halves: the
-//     score products of half h + 1 are issued with the exponentials of half
-//     h between them, then the value products of half h; operand reads are
-//     issued one or two products ahead (scheduling barriers keep that order);
+//   * within a tile each wave takes 32-key halves one after the other:
+//     score products, exponentials, value products; the operand reads run
+//     three products ahead of their use (scheduling barriers keep that
+//     order), and the other wave of the SIMD runs its products while this
+//     one computes exponentials;
 //   * scores are formed transposed, S^T = K Q^T (keys as rows), so a lane
 //     holds 4 keys of one query row and the probabilities already sit in the
 //     lane layout of the B operand of O^T = C^T P^T. The C^T operand is read
@@ -69,6 +70,12 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+// Operand reads of the tile body run this many products ahead: score
+// operands kDQ contraction steps, value operands kDV d-blocks. The two waves
+// of a SIMD hide each other's exponentials; what stalls the matrix core is
+// the latency of the LDS reads, and the registers left beside the queries
+// and output accumulators hold three steps of operands.
+constexpr int kDQ = 3, kDV = 3;
 constexpr float kSumLimit = 0x1p100f;
 constexpr float kSumMin = 0x1p-100f;
 
@@ -139,11 +146,6 @@ struct FlashTile {
   static_assert(DC % 16 == 0 && DR % 8 == 0 && (DR / 8 & (DR / 8 - 1)) == 0,
                 "latent in 16-wide blocks; kR in a power-of-two number of 8-element units");
   static_assert(LS % 4 == 0 && (LS * sizeof(T)) % 16 == 0, "LDS rows must stay 16-byte aligned");
-  // The pipelined tile body keeps a second score block and operands of the
-  // next half in registers besides the queries (4 NKC kNMB registers) and
-  // the output accumulators (4 NDB kNMB); where those two take more than 152
-  // of the 256 (d_c 192 with d_rope 64) it spills, and the plain body runs.
-  static constexpr bool kPipelined = 4 * (NKC + NDB) * kNMB <= 152;
 };
 
 // 3D-RoPE of the window's positional keys, once per call: key v = (slot
@@ -248,29 +250,49 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     kr_pk[k] = (instr < F::KR_INSTR && n < kBN) ? (n << 16) | ((F::kr_slot(n, us) * F::CPU + ci) * 16) : -1;
   }
 
-  // Work-group g (logical index) takes units [g U / G, (g + 1) U / G) of the
-  // (row block, key tile) grid, as consecutive segments of at most one row block each. A
-  // segment that covers its whole row block writes the normalised output; a
-  // partial one writes (output, reference, sum) to slot 0 (the work-group's
-  // first segment) or 1 (its last) for the merge pass.
+  // Work-group g (logical index) first takes its whole row blocks, one per
+  // round (row block k G + g): all work-groups start a round together and
+  // walk the keys in the same order, so the work-groups of an XCD, which
+  // hold consecutive row blocks, read the same key tiles at the same time
+  // and share them through its L2. Then its range of the remaining units,
+  // [u_rest + g R / G', u_rest + (g + 1) R / G'), as consecutive segments of
+  // at most one row block each. A segment that covers its whole row block
+  // writes the normalised output; a partial one writes (output, reference,
+  // sum) to slot 0 (the work-group's first segment of the range) or 1 (its
+  // last) for the merge pass.
   const long long G = p.grid;
   const int g = xcd_major(blockIdx.x, p.grid);
-  const long long u_first = (long long)g * p.units / G;
-  const long long u_last = ((long long)g + 1) * p.units / G;
+  const long long rounds = p.rb_whole / G;
+  const long long rest = p.units - p.u_rest;
+  const long long u_first = g < p.grid_rest ? p.u_rest + (long long)g * rest / p.grid_rest : p.units;
+  const long long u_last = g < p.grid_rest ? p.u_rest + ((long long)g + 1) * rest / p.grid_rest : p.units;
   //
-  // Segments are taken last to first: a range that ends inside a row block
-  // starts with that block's first tiles, so at any moment most work-groups
-  // read the same few key tiles and share them through the L2.
-  for (long long u = u_last; u > u_first;) {
+  // Segments of the range are taken last to first: a range that ends inside
+  // a row block starts with that block's first tiles, so at any moment most
+  // work-groups read the same few key tiles and share them through the L2.
+  long long round = 0;
+  for (long long u = u_last;;) {
     long long rbg, ua;  // row block over all streams, its first unit
     int nt;             // its unit count
-    locate_unit(p.classes, p.n_rb, u - 1, rbg, ua, nt);
-    const long long seg0 = max(u_first, ua);
-    const int j0 = (int)(seg0 - ua);
-    const int j1 = (int)(u - ua);
-    const bool first_seg = seg0 == u_first;
+    int j0, j1;         // the segment's units within the row block
+    bool first_seg;
+    if (round < rounds) {
+      rbg = round * G + g;
+      ++round;
+      row_block_units(p.classes, p.n_rb, rbg, ua, nt);
+      j0 = 0;
+      j1 = nt;
+      first_seg = false;
+    } else {
+      if (u <= u_first) break;
+      locate_unit(p.classes, p.n_rb, u - 1, rbg, ua, nt);
+      const long long seg0 = max(u_first, ua);
+      j0 = (int)(seg0 - ua);
+      j1 = (int)(u - ua);
+      first_seg = seg0 == u_first;
+      u = seg0;
+    }
     const bool whole = j0 == 0 && j1 == nt;
-    u = seg0;
     const int b = (int)(rbg / p.n_rb), rb = (int)(rbg - (long long)b * p.n_rb);
     const int row_wave = rb * F::kRowsBlock + wave * F::kRowsWave;
     __syncthreads();  // LDS of the previous segment is no longer read
@@ -509,84 +531,53 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
             l_run[mb] += e;
           }
         };
-        // one half: the scores of half + 1 (when NEXT) with the
-        // exponentials of this half spread between their products, then the
-        // value products of this half; operand reads run ahead of use
-        auto body = [&](int half, sblk& s_cur, sblk& s_nxt, auto next_c) {
-          constexpr bool NEXT = decltype(next_c)::value;
-          const int kfirst = kbase + half * 32;
-          mask(s_cur, half);
-          float f[kNMB][8];
-          if constexpr (NEXT) {
-            v8 ka[2][2];
-            ka[0][0] = kop(half + 1, 0, 0);
-            ka[0][1] = kop(half + 1, 0, 1);
-#pragma unroll
-            for (int kc = 0; kc < F::NKC; ++kc) {
-              if (kc + 1 < F::NKC) {
-                ka[(kc + 1) & 1][0] = kop(half + 1, kc + 1, 0);
-                ka[(kc + 1) & 1][1] = kop(half + 1, kc + 1, 1);
-              }
-              __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-              for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int mb = 0; mb < kNMB; ++mb)
-                  s_nxt[kb][mb] = mma16(ka[kc & 1][kb], qf[mb][kc], kc == 0 ? negref[mb] : s_nxt[kb][mb]);
-              // exponential chunk kc of the 2 kNMB (mb, kb) chunks of this half
-              // (all remaining ones at the last step), interleaved with the
-              // products one for one
-#pragma unroll
-              for (int c = kc; c < (kc + 1 == F::NKC ? 2 * kNMB : kc + 1); ++c)
-                if (c < 2 * kNMB) expo(s_cur, f, c / 2, c % 2, kfirst);
-#pragma unroll
-              for (int grp = 0; grp < 2 * kNMB; ++grp) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-              }
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          } else {
-#pragma unroll
-            for (int c = 0; c < 2 * kNMB; ++c) expo(s_cur, f, c / 2, c % 2, kfirst);
-          }
-          v8 pb[kNMB];
-#pragma unroll
-          for (int mb = 0; mb < kNMB; ++mb) pb[mb] = pack8<T>(f[mb]);
-          v8 va[3];
-          va[0] = vop(half, 0);
-          va[1] = vop(half, 1);
-#pragma unroll
-          for (int db = 0; db < F::NDB; ++db) {
-            if (db + 2 < F::NDB) va[(db + 2) % 3] = vop(half, db + 2);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int mb = 0; mb < kNMB; ++mb) o[db][mb] = mma16(va[db % 3], pb[mb], o[db][mb]);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+        // one half: the score products (operands read kDQ contraction steps
+        // ahead), the exponentials, then the value products (operands read
+        // kDV d-blocks ahead); scheduling barriers keep each read that far
+        // ahead of its product
+        v8 ka[kDQ + 1][2];
+        auto fetch = [&](int half, int kc) {
+          ka[kc % (kDQ + 1)][0] = kop(half, kc, 0);
+          ka[kc % (kDQ + 1)][1] = kop(half, kc, 1);
         };
-        if constexpr (F::kPipelined) {
-          sblk s_cur;
-          scores(cur, cur_r, 0, s_cur, negref);
-#pragma unroll 1
-          for (int half = 0; half + 1 < NKC2; ++half) {
-            sblk s_nxt;
-            body(half, s_cur, s_nxt, std::integral_constant<bool, true>());
+        auto one_half = [&](int half) {
+          sblk s;
+#pragma unroll
+          for (int d = 0; d < kDQ; ++d)
+            if (d < F::NKC) fetch(half, d);
+#pragma unroll
+          for (int kc = 0; kc < F::NKC; ++kc) {
+            if (kc + kDQ < F::NKC) fetch(half, kc + kDQ);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-              for (int mb = 0; mb < kNMB; ++mb) s_cur[kb][mb] = s_nxt[kb][mb];
+              for (int mb = 0; mb < kNMB; ++mb)
+                s[kb][mb] = mma16(ka[kc % (kDQ + 1)][kb], qf[mb][kc], kc == 0 ? negref[mb] : s[kb][mb]);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          body(NKC2 - 1, s_cur, s_cur, std::integral_constant<bool, false>());
-        } else {
-          // one half after the other (no second score block in flight)
+          mask(s, half);
+          float f[kNMB][8];
+#pragma unroll
+          for (int c = 0; c < 2 * kNMB; ++c) expo(s, f, c / 2, c % 2, kbase + half * 32);
+          v8 pb[kNMB];
+#pragma unroll
+          for (int mb = 0; mb < kNMB; ++mb) pb[mb] = pack8<T>(f[mb]);
+          v8 va[kDV + 1];
+#pragma unroll
+          for (int d = 0; d < kDV; ++d)
+            if (d < F::NDB) va[d] = vop(half, d);
+#pragma unroll
+          for (int db = 0; db < F::NDB; ++db) {
+            if (db + kDV < F::NDB) va[(db + kDV) % (kDV + 1)] = vop(half, db + kDV);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mb = 0; mb < kNMB; ++mb) o[db][mb] = mma16(va[db % (kDV + 1)], pb[mb], o[db][mb]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        };
 #pragma unroll 1
-          for (int half = 0; half < NKC2; ++half) {
-            sblk s;
-            scores(cur, cur_r, half, s, negref);
-            body(half, s, s, std::integral_constant<bool, false>());
-          }
-        }
+        for (int half = 0; half < NKC2; ++half) one_half(half);
       };
       if constexpr (CAUSAL) {
         // 0: all keys visible to the block, 1: masked per key, 2: none visible
@@ -744,20 +735,21 @@ __global__ __launch_bounds__(256) void flash_combine_kernel(FlashParams p) {
   constexpr int NCH = DC / CH;
   typedef typename std::conditional<sizeof(T) == 2, u32x4, f32x4>::type chunk_t;
   __shared__ long long slot_base[kMaxMergePieces];  // first partial row of each piece
-  const long long G = p.grid;
-  const long long rbg = blockIdx.x / (RB / kMergeRows);
+  // row blocks from rb_whole on (the ones dealt whole in rounds are done)
+  const long long rbg = p.rb_whole + blockIdx.x / (RB / kMergeRows);
   const int row_lo = (int)(blockIdx.x % (RB / kMergeRows)) * kMergeRows;
   long long a;
   int nt;
   row_block_units(p.classes, p.n_rb, rbg, a, nt);
-  // largest g whose range starts at or before unit x
-  auto owner = [&](long long x) { return ((x + 1) * G - 1) / p.units; };
+  const long long Gr = p.grid_rest, rest = p.units - p.u_rest;
+  // largest g whose range of the remaining units starts at or before unit x
+  auto owner = [&](long long x) { return ((x - p.u_rest + 1) * Gr - 1) / rest; };
   const long long g0 = owner(a), g1 = owner(a + nt - 1);
   if (g0 == g1) return;  // one work-group covered the row block and wrote it
-  const int np = (int)(g1 - g0 + 1);  // <= kMaxMergePieces by the host's cap on G
+  const int np = (int)(g1 - g0 + 1);  // <= kMaxMergePieces by the host's cap on G'
   if ((int)threadIdx.x < np) {
     const long long g = g0 + threadIdx.x;
-    const long long start = g * p.units / G;
+    const long long start = p.u_rest + g * rest / Gr;
     slot_base[threadIdx.x] = (g * 2 + (start >= a ? 0 : 1)) * RB;
   }
   __syncthreads();
@@ -901,10 +893,11 @@ static hipError_t launch_flash_v(const FlashParams& p, bool split, hipStream_t s
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((flash_mla_kernel<T, DC, DR, CAUSAL>), dim3(p.grid), dim3(F::kThreads), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (split) {
+  if (split && (long long)p.batch * p.n_rb > p.rb_whole) {
     static_assert(F::kRowsBlock % kMergeRows == 0, "merge groups tile a row block");
     hipLaunchKernelGGL((flash_combine_kernel<T, DC, F::kRowsBlock>),
-                       dim3(p.batch * p.n_rb * (F::kRowsBlock / kMergeRows)), dim3(256), 0, s, p);
+                       dim3(((long long)p.batch * p.n_rb - p.rb_whole) * (F::kRowsBlock / kMergeRows)), dim3(256), 0,
+                       s, p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   hipLaunchKernelGGL((flash_exact_kernel<T, DC, DR, CAUSAL>), dim3(kFallbackBlocks), dim3(256), 0, s, p);

@@ -105,12 +105,18 @@ int device_cus() {
 // Work split of the attention kernel: `grid` work-groups share `units`
 // (row block, key tile) pairs evenly. kv_splits = s > 0 gives every row
 // block s equal key ranges (s = 1: one work-group per row block);
-// kv_splits = 0 uses one work-group per compute unit.
+// kv_splits = 0 uses one work-group per compute unit, and where there are
+// at least as many row blocks as work-groups (several streams) and all row
+// blocks have the same units, deals the first whole multiple of `grid` row
+// blocks out whole, in rounds, and shares the rest.
 struct FlashPlan {
   int n_rb, nt_max;
   int64_t units;
   int grid;
-  bool split;  // some row block is shared by several work-groups
+  int64_t rb_whole;  // row blocks dealt whole in rounds (a multiple of grid)
+  int64_t u_rest;    // first unit after them
+  int grid_rest;     // work-groups sharing the units from u_rest on
+  bool split;        // some row block is shared by several work-groups
   mla::UnitClasses classes;
 };
 
@@ -163,7 +169,19 @@ FlashPlan flash_plan(const mla_shape* s, int q_n_frames, int kv_splits, bool cau
   if (g < 1) g = 1;
   if (g > (INT64_C(1) << 23)) g = INT64_C(1) << 23;  // rejected by flash_plan_ok
   f.grid = (int)g;
-  f.split = c.n > 1 || !(f.units % g == 0 && (f.units / g) % f.nt_max == 0);
+  f.rb_whole = 0;
+  if (kv_splits == 0 && c.n == 1 && row_blocks >= g) f.rb_whole = row_blocks / g * g;
+  f.u_rest = f.rb_whole * f.nt_max;
+  const int64_t rest = f.units - f.u_rest;
+  // the rest: at most kMaxMergePieces - 1 work-groups per remaining row block
+  int64_t gr = g;
+  if (f.rb_whole > 0) {
+    const int64_t rb_rest = row_blocks - f.rb_whole;
+    if (gr > (mla::kMaxMergePieces - 1) * rb_rest) gr = (mla::kMaxMergePieces - 1) * rb_rest;
+    if (gr > rest) gr = rest;
+  }
+  f.grid_rest = (int)gr;
+  f.split = c.n > 1 || (rest > 0 && !(rest % gr == 0 && (rest / gr) % f.nt_max == 0));
   return f;
 }
 
@@ -263,6 +281,9 @@ mla_status do_flash(const mla_shape* s, const void* q_abs, int q_n_frames, const
   p.units = f.units;
   p.classes = f.classes;
   p.grid = f.grid;
+  p.rb_whole = f.rb_whole;
+  p.u_rest = f.u_rest;
+  p.grid_rest = f.grid_rest;
   p.scale_log2 = scale_log2(s);
   p.rope_base = (double)s->rope_base;
   p.H = s->n_heads;
@@ -305,6 +326,9 @@ FlashPlan heads_plan(const mla_shape* s, int q_n_frames) {
   if (g > (mla::kMaxMergePieces - 1) * row_blocks) g = (mla::kMaxMergePieces - 1) * row_blocks;
   if (g < 1) g = 1;
   f.grid = (int)g;
+  f.rb_whole = 0;
+  f.u_rest = 0;
+  f.grid_rest = (int)g;
   f.split = !(f.units % g == 0 && (f.units / g) % f.nt_max == 0);
   return f;
 }

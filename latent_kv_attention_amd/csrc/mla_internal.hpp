@@ -50,9 +50,13 @@ struct AbsorbParams {
 // (one class without the frame-causal mask; with it, class k holds the row
 // blocks whose last row is a query of chunk frame k), and every row block of
 // class k has nt[k] units, the key tiles of the window part its rows may see
-// when the window is full (the frames up to its last row's). Work-group g of
-// G takes units [g U / G, (g + 1) U / G); a row block that falls to several
-// work-groups is finished by a merge pass over their partial results.
+// when the window is full (the frames up to its last row's). The first
+// rb_whole row blocks (a multiple of G, all streams counted) are dealt whole
+// in rounds: work-group g takes row block k G + g in round k. The units left,
+// [u_rest, U), are shared by work-groups g < G' (grid_rest): g takes
+// [u_rest + g R / G', u_rest + (g + 1) R / G'), R = U - u_rest; a row block
+// that falls to several work-groups is finished by a merge pass over their
+// partial results.
 constexpr int kMaxUnitClasses = 64;
 struct UnitClasses {
   int n;                          // classes
@@ -109,6 +113,9 @@ struct FlashParams {
   long long units;         // all units: batch * classes.per_stream
   UnitClasses classes;
   int grid;                // G, work-groups of the attention kernel
+  long long rb_whole;      // row blocks dealt whole in rounds (a multiple of G)
+  long long u_rest;        // first unit after them
+  int grid_rest;           // work-groups sharing the units from u_rest on
   float scale_log2;        // softmax scale * log2(e)
   double rope_base;        // RoPE base (the keys' temporal angles are formed per call)
 };

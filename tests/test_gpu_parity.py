@@ -476,6 +476,19 @@ def test_full_step_batch_and_partial_fill():
     assert_step_close(got, ref, cfg.dtype, label="wan_small B=3 fill=3")
 
 
+def test_full_step_many_streams_whole_row_blocks():
+    """40 streams of 7 row blocks each: 280 row blocks, more than one per
+    work-group (one per compute unit), so the first whole multiple of the
+    work-group count goes out as whole row blocks in a round and the rest
+    are shared unit by unit (3 key tiles per row block, pieces merged).
+    Every element of every stream against the oracle."""
+    cfg = get_config("wan_small")
+    got, ref = _full_step(cfg, seed=13, B=40)
+    print(f"[parity] 40 streams, {40 * 7} row blocks", flush=True)
+    for b in range(40):
+        assert_step_close(got[b], ref[b], cfg.dtype, label=f"wan_small stream {b} of 40")
+
+
 def _causal_step(cfg, seed, prefill_frames, chunk_first):
     """Frames written one by one, then the chunk; frame-causal attention of the
     chunk's queries against the oracle's frame-causal step."""
@@ -720,17 +733,22 @@ def test_wan_batch8_streams_full_windows():
     for f0 in range(0, 21, 3):  # three frames of all streams per write (bounded host memory)
         layer.write(to_torch(np.stack([s.xs(f0, 3) for s in streams]), cfg.dtype), f0, 3)
     qs = [s.q(18) for s in streams]
-    out = layer.attend(to_torch(np.stack([q[0] for q in qs]), cfg.dtype),
-                       to_torch(np.stack([q[1] for q in qs]), cfg.dtype), 18, 3)
+    qn = to_torch(np.stack([q[0] for q in qs]), cfg.dtype)
+    qr = to_torch(np.stack([q[1] for q in qs]), cfg.dtype)
+    # the latent form (1536 row blocks dealt whole in six rounds, the other 224
+    # shared) and the form the selecting call takes at this shape
+    got = {"latent": to_numpy(layer.attend_latent(qn, qr, 18, 3))}
     _sync()
-    got = to_numpy(out)
+    got["selected"] = to_numpy(layer.attend(qn, qr, 18, 3))
+    _sync()
     sf = layer.slot_frame.cpu().numpy()
     assert (sf == np.arange(21)[None, :]).all()
     for b in range(B):
-        rows = sample_rows(cfg, 12, seed=b)
+        rows = sample_rows(cfg, 16, seed=b)
         memo = LatentMemo(cfg, w, streams[b])
         ref = oracle_rows_memo(cfg, w, memo, range(21), qs[b][0], qs[b][1], 18, rows)
-        assert_step_close(got[b][rows], ref, cfg.dtype, label=f"batch8 stream {b}")
+        for form, g in got.items():
+            assert_step_close(g[b][rows], ref, cfg.dtype, label=f"batch8 stream {b} {form}")
 
 
 def test_wan_rollout_80_chunks_ring_eviction():
