@@ -216,10 +216,6 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
   __shared__ int frame_of[kMaxSlots];  // frame held by the r-th valid slot (frame-causal variant)
   __shared__ int n_valid_sh;
   __shared__ int keytab[2][kBN];  // per key of a tile: byte offset of its cache row
-  // per key of a tile: its frame (frame-causal variant), for position p in
-  // entry p mod 3: the descriptors of position p + 2 are written while tile p
-  // is masked, and tile p + 1's are read in the next step
-  __shared__ int keyfr[CAUSAL ? 3 : 1][CAUSAL ? kBN : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -312,27 +308,32 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
 
     const int n_keys = n_valid_sh * p.T;
 
-    // frame-causal variant: query frame of this lane's two rows (rows are
-    // (token, head) pairs, H per token, T tokens per frame) and the range of
-    // query frames of the row block
-    int qfr[kNMB] = {};
-    int rb_fmin = 0, rb_fmax = 0;
-    // keys the row block visits: the whole window, or under the frame-causal
-    // mask the prefix of frames up to its last row's (keys are in frame order)
-    int n_keys_rb = n_keys;
+    // Frame-causal variant: keys are in frame order, so the keys a row may
+    // see are a prefix of the window, those of the valid slots whose frame
+    // is at most the row's query frame (rows are (token, head) pairs, H per
+    // token, T tokens per frame). vis_end: the end of that prefix for this
+    // lane's two rows; vis_lo / n_keys_rb: for the row block's first and
+    // last rows (the keys every row sees, and the keys the block visits).
+    int vis_end[kNMB];
+    int vis_lo = n_keys, n_keys_rb = n_keys;
     if constexpr (CAUSAL) {
       const int rows_per_frame = p.T * p.H;
+      auto visible_keys = [&](int qf) {
+        int n = 0;
+        for (int r = 0; r < n_valid_sh; ++r) n += frame_of[r] <= qf ? 1 : 0;
+        return n * p.T;
+      };
 #pragma unroll
       for (int mb = 0; mb < kNMB; ++mb) {
         const int row = row_wave + mb * 16 + li;
-        qfr[mb] = row < p.Mb ? p.q_frame_first + row / rows_per_frame : 0x7fffffff;
+        vis_end[mb] = row < p.Mb ? visible_keys(p.q_frame_first + row / rows_per_frame) : n_keys;
       }
       const int r_first = rb * F::kRowsBlock, r_last = min(r_first + F::kRowsBlock, p.Mb) - 1;
-      rb_fmin = p.q_frame_first + r_first / rows_per_frame;
-      rb_fmax = p.q_frame_first + r_last / rows_per_frame;
-      int n_vis = 0;
-      for (int r = 0; r < n_valid_sh; ++r) n_vis += frame_of[r] <= rb_fmax ? 1 : 0;
-      n_keys_rb = n_vis * p.T;
+      vis_lo = visible_keys(p.q_frame_first + r_first / rows_per_frame);
+      n_keys_rb = visible_keys(p.q_frame_first + r_last / rows_per_frame);
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < kNMB; ++mb) vis_end[mb] = n_keys;
     }
     // this segment's share of the row block's tiles (units map onto the
     // tiles of a full window; a partly filled window scales proportionally)
@@ -340,6 +341,22 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     const int tile_begin = (int)((long long)j0 * n_tiles / nt);
     const int tile_end = (int)((long long)j1 * n_tiles / nt);
     const int n_visit = max(0, tile_end - tile_begin);
+    // Positions 0 .. n_lim - 1 visit the range's last tiles, last first,
+    // through the tile body that gives keys past a limit zero weight (past
+    // the window: the last tile can be ragged; frame-causal variant: past
+    // the row's visible prefix); the other positions visit the rest of the
+    // range in order with the plain body. Frame-causal: the limited tiles
+    // are those not seen whole by every row of the block (keys from vis_lo
+    // on), at least one, and an odd count where the range allows, so that
+    // the plain positions start on the same tile buffer as without the mask.
+    int n_lim = n_visit > 0 ? 1 : 0;
+    if constexpr (CAUSAL) {
+      if (n_visit > 0) {
+        int m = max(1, tile_end - max(tile_begin, vis_lo / kBN));
+        if (m % 2 == 0) m = min(m + 1, n_visit);
+        n_lim = m;
+      }
+    }
 
     // queries of this wave (B operand of S^T = K Q^T), kept in registers
     v8 qf[kNMB][F::NKC];
@@ -381,18 +398,13 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
       const int r = a - q * d;
       return q + (r >= d ? 1 : 0) - (r < 0 ? 1 : 0);
     };
-    // position 0 visits the last tile of the range (the one that can be
-    // ragged), positions 1.. the others in order
-    auto tile_of = [&](int pos) { return pos == 0 ? tile_end - 1 : tile_begin + pos - 1; };
+    auto tile_of = [&](int pos) { return pos < n_lim ? tile_end - 1 - pos : tile_begin + pos - n_lim; };
     auto describe = [&](int pos, int* tab) {
       if (wave < (kBN + 63) / 64) {
         const int ln = opaque(lane) + wave * 64;
         const int v = min(tile_of(pos) * kBN + ln, n_keys - 1);
         const int rank = div_floor(v, p.T, p.inv_T), tok = v - rank * p.T;
-        if (ln < kBN) {
-          tab[ln] = (slot_of[rank] * p.T + tok) * F::DK * (int)sizeof(T);
-          if constexpr (CAUSAL) keyfr[pos % 3][ln] = frame_of[rank];
-        }
+        if (ln < kBN) tab[ln] = (slot_of[rank] * p.T + tok) * F::DK * (int)sizeof(T);
       }
     };
 
@@ -463,19 +475,11 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     typedef std::integral_constant<int, 0> B0;
     typedef std::integral_constant<int, 1> B1;
 
-    // frame-causal variant: frames of the tile's keys against the row
-    // block's query frames; keys are in frame order, so the tile's first and
-    // last keys hold its earliest and latest frames
-    auto tile_class = [&](int kbase) -> int {
-      const int fmin = frame_of[div_floor(kbase, p.T, p.inv_T)];
-      const int fmax = frame_of[div_floor(min(kbase + kBN, n_keys) - 1, p.T, p.inv_T)];
-      return fmin > rb_fmax ? 2 : (fmax <= rb_fmin ? 0 : 1);
-    };
 
     // One tile: start the loads of the next position (descriptors ready),
     // describe the one after, consume this tile half by half, wait for the
     // next tile's loads, barrier.
-    auto step = [&](int pos, auto cur_c, auto ragged_c) {
+    auto step = [&](int pos, auto cur_c, auto limited_c) {
       constexpr int CUR = decltype(cur_c)::value;
       typedef std::integral_constant<int, CUR ^ 1> nxt_c;
       T* cur = buf_of(cur_c);
@@ -487,23 +491,7 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
       }
       if (pos + 2 < n_visit) describe(pos + 2, keytab[CUR]);
       const int kbase = tile_of(pos) * kBN;
-      auto halves = [&](bool masked) {
-        auto mask = [&](sblk& s, int half) {
-          if constexpr (CAUSAL) {
-            // scores of keys from frames after the row's frame drop out
-            if (masked) {
-              const int* kfr = keyfr[CAUSAL ? pos % 3 : 0] + half * 32;
-#pragma unroll
-              for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const int f = kfr[kb * 16 + lg * 4 + i];
-#pragma unroll
-                  for (int mb = 0; mb < kNMB; ++mb) s[kb][mb][i] = f <= qfr[mb] ? s[kb][mb][i] : -__builtin_inff();
-                }
-            }
-          }
-        };
+      auto halves = [&]() {
         // A operand of the score product S^T = K Q^T: keys 16 kb .. of the
         // half, contraction dims 32 kc .. (latent, rotated kR or zero padding)
         auto kop = [&](int half, int kc, int kb) -> v8 {
@@ -520,13 +508,20 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
         auto vop = [&](int half, int db) -> v8 {
           return lds_tr8(cur, F::LS, half * 32 + lg * 4, half * 32 + 16 + lg * 4, db * 16);
         };
-        constexpr bool RAGGED = decltype(ragged_c)::value;
-        // exponentials of 16-row block mb, key block kb of a half: 4 values
+        constexpr bool LIMITED = decltype(limited_c)::value;
+        // exponentials of 16-row block mb, key block kb of a half: 4 values;
+        // keys past the window (a ragged tile) and, when masked, keys past
+        // the row's visible prefix weigh zero (vis_end <= n_keys)
         auto expo = [&](const sblk& s, float (&f)[kNMB][8], int mb, int kb, int kfirst) {
+          // limited body: key kfirst + 4 lg + 16 kb + i is kept when
+          // 16 kb + i < lim, the limit being the row's visible prefix under the
+          // frame-causal mask (within the window), else the window's end
+          int lim = 0;
+          if constexpr (LIMITED) lim = (CAUSAL ? vis_end[mb] : n_keys) - kfirst - 4 * opaque(lg);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float e = fast_exp2(s[kb][mb][i]);
-            if constexpr (RAGGED) e = kfirst + kb * 16 + lg * 4 + i < n_keys ? e : 0.f;
+            if constexpr (LIMITED) e = kb * 16 + i < lim ? e : 0.f;
             f[mb][kb * 4 + i] = e;
             l_run[mb] += e;
           }
@@ -556,7 +551,6 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
                 s[kb][mb] = mma16(ka[kc % (kDQ + 1)][kb], qf[mb][kc], kc == 0 ? negref[mb] : s[kb][mb]);
             __builtin_amdgcn_sched_barrier(0);
           }
-          mask(s, half);
           float f[kNMB][8];
 #pragma unroll
           for (int c = 0; c < 2 * kNMB; ++c) expo(s, f, c / 2, c % 2, kbase + half * 32);
@@ -579,13 +573,7 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
 #pragma unroll 1
         for (int half = 0; half < NKC2; ++half) one_half(half);
       };
-      if constexpr (CAUSAL) {
-        // 0: all keys visible to the block, 1: masked per key, 2: none visible
-        const int cls = tile_class(kbase);
-        if (cls != 2) halves(cls == 1);
-      } else {
-        halves(false);
-      }
+      halves();
       __builtin_amdgcn_s_waitcnt(0);  // direct loads of the next tile have landed
       __syncthreads();
     };
@@ -630,7 +618,7 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
               const int key = kbase + kb * 16 + lg * 4 + i;
               if (key < n_keys) {
                 mx_all = fmaxf(mx_all, s[kb][mb][i]);
-                if (frame_of[div_floor(key, p.T, p.inv_T)] <= qfr[mb]) mx = fmaxf(mx, s[kb][mb][i]);
+                if (key < vis_end[mb]) mx = fmaxf(mx, s[kb][mb][i]);
               }
             }
           mx = wave_max_across_groups(mx);
@@ -639,17 +627,23 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
         }
         negref[mb] = f32x4{-mx, -mx, -mx, -mx};
       }
-      // position 0 is the only tile that can be ragged
-      step(0, B0(), std::integral_constant<bool, true>());
+      step(0, B0(), std::true_type());
     }
     {
-      typedef std::integral_constant<bool, false> Full;
       int pos = 1;
-      for (; pos + 1 < n_visit; pos += 2) {
-        step(pos, B1(), Full());
-        step(pos + 1, B0(), Full());
+      if constexpr (CAUSAL) {
+        // the other limited positions (n_lim is odd unless it is n_visit)
+        for (; pos + 1 < n_lim; pos += 2) {
+          step(pos, B1(), std::true_type());
+          step(pos + 1, B0(), std::true_type());
+        }
+        if (pos < n_lim) step(pos++, B1(), std::true_type());
       }
-      if (pos < n_visit) step(pos, B1(), Full());
+      for (; pos + 1 < n_visit; pos += 2) {
+        step(pos, B1(), std::false_type());
+        step(pos + 1, B0(), std::false_type());
+      }
+      if (pos < n_visit) step(pos, B1(), std::false_type());
     }
 
     // ---- epilogue
@@ -663,14 +657,9 @@ __global__ __launch_bounds__((FlashTile<T, DC, DR>::kThreads), 1) void flash_mla
     // exact fallback.
     bool sees[kNMB];
     if constexpr (CAUSAL) {
-      int fmin_seg = 0x7fffffff;  // earliest frame among the visited keys
-      if (n_visit > 0) {
-        const int r_lo = div_floor(tile_begin * kBN, p.T, p.inv_T);
-        const int r_hi = div_floor(min(tile_end * kBN, n_keys) - 1, p.T, p.inv_T);
-        for (int r = r_lo; r <= r_hi; ++r) fmin_seg = min(fmin_seg, frame_of[r]);
-      }
+      // the segment visits keys from tile_begin kBN on
 #pragma unroll
-      for (int mb = 0; mb < kNMB; ++mb) sees[mb] = fmin_seg <= qfr[mb];
+      for (int mb = 0; mb < kNMB; ++mb) sees[mb] = n_visit > 0 && tile_begin * kBN < vis_end[mb];
     } else {
 #pragma unroll
       for (int mb = 0; mb < kNMB; ++mb) sees[mb] = n_visit > 0;
