@@ -27,7 +27,6 @@ namespace mla {
 namespace {
 constexpr int kRowsPerBlock = 64;
 constexpr int kColsPerBlock = 32;
-constexpr int kXcds = 8;
 
 // staged bf16 kernel
 constexpr int kSM = 80;                           // token rows per tile (5 x 16)

@@ -79,21 +79,9 @@ constexpr int kDQ = 3, kDV = 3;
 constexpr float kSumLimit = 0x1p100f;
 constexpr float kSumMin = 0x1p-100f;
 
-// Work-groups are dealt to the 8 XCDs round-robin (work-group i runs on XCD
-// i mod 8). Work-group i gets logical index (XCD-major) so that each XCD's
-// work-groups take consecutive unit ranges: with several streams an XCD then
-// walks few windows and its L2 serves them, instead of every XCD touching
-// every stream's window. A bijection of [0, G) for any G.
-constexpr int kXcds = 8;
-
 // Fourth word of a raw buffer resource (no format conversion, no swizzle):
 // byte offsets past num_records read as zero.
 constexpr int kBufferWord3 = 0x00020000;
-__device__ __forceinline__ int xcd_major(int id, int G) {
-  const int q = G / kXcds, r = G % kXcds;
-  const int x = id % kXcds, k = id / kXcds;
-  return x * q + min(x, r) + k;
-}
 }  // namespace
 
 // bf16: 8 waves x 32 rows (two waves per SIMD) and 128-key tiles; float

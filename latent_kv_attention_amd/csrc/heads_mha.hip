@@ -233,22 +233,43 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
   typedef std::integral_constant<int, 0> B0;
   typedef std::integral_constant<int, 1> B1;
 
-  // Work-group g takes units [g U / G, (g + 1) U / G) of the (row block, key
-  // tile) grid as segments of at most one row block each, last to first (so
-  // most work-groups read the same few key tiles at any moment). A segment
-  // covering its whole row block writes the output; a partial one writes
-  // (output / sum, reference, sum) to slot 0 (the work-group's first segment)
-  // or 1 (its last) for the merge pass.
+  // Work-group g (logical index, XCD-major) first takes its whole row
+  // blocks, one per round (row block k G + g: the work-groups of an XCD hold
+  // consecutive row blocks, mostly of one (stream, head), and walk its keys
+  // in step, sharing them through the L2), then its range of the remaining
+  // units, [u_rest + g R / G', u_rest + (g + 1) R / G'), as segments of at
+  // most one row block each, last to first (so most work-groups read the
+  // same few key tiles at any moment). A segment covering its whole row
+  // block writes the output; a partial one writes (output / sum, reference,
+  // sum) to slot 0 (the work-group's first segment of the range) or 1 (its
+  // last) for the merge pass.
   const long long G = p.grid;
-  const long long u_first = (long long)blockIdx.x * p.units / G;
-  const long long u_last = ((long long)blockIdx.x + 1) * p.units / G;
-  for (long long u = u_last; u > u_first;) {
-    const long long rbg = (u - 1) / p.nt_max;  // row block over all (stream, head) pairs
-    const long long seg0 = max(u_first, rbg * p.nt_max);
-    const int j0 = (int)(seg0 - rbg * p.nt_max), j1 = (int)(u - rbg * p.nt_max);
-    const bool first_seg = seg0 == u_first;
+  const int g = xcd_major(blockIdx.x, p.grid);
+  const long long rounds = p.rb_whole / G;
+  const long long rest = p.units - p.u_rest;
+  const long long u_first = g < p.grid_rest ? p.u_rest + (long long)g * rest / p.grid_rest : p.units;
+  const long long u_last = g < p.grid_rest ? p.u_rest + ((long long)g + 1) * rest / p.grid_rest : p.units;
+  long long round = 0;
+  for (long long u = u_last;;) {
+    long long rbg;  // row block over all (stream, head) pairs
+    int j0, j1;
+    bool first_seg;
+    if (round < rounds) {
+      rbg = round * G + g;
+      ++round;
+      j0 = 0;
+      j1 = p.nt_max;
+      first_seg = false;
+    } else {
+      if (u <= u_first) break;
+      rbg = (u - 1) / p.nt_max;
+      const long long seg0 = max(u_first, rbg * p.nt_max);
+      j0 = (int)(seg0 - rbg * p.nt_max);
+      j1 = (int)(u - rbg * p.nt_max);
+      first_seg = seg0 == u_first;
+      u = seg0;
+    }
     const bool whole = j0 == 0 && j1 == p.nt_max;
-    u = seg0;
     const int bh = (int)(rbg / p.n_rb), rb = (int)(rbg - (long long)bh * p.n_rb);  // bh = b * H + h
     const int h = bh % p.H, b = bh / p.H;
     __syncthreads();  // LDS of the previous segment is no longer read
@@ -438,7 +459,7 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
         if (!ok && elg == 0) p.fallback_rows[atomicAdd(p.fallback_count, 1)] = bh * p.Nq + tok;
       } else {
         const size_t prow =
-            ((size_t)blockIdx.x * 2 + (first_seg ? 0 : 1)) * F::kRowsBlock + (tok - rb * F::kRowsBlock);
+            ((size_t)g * 2 + (first_seg ? 0 : 1)) * F::kRowsBlock + (tok - rb * F::kRowsBlock);
         bf16* dst = (bf16*)p.part_o + prow * DH;
 #pragma unroll
         for (int db = 0; db < F::NDB; ++db)
@@ -464,17 +485,19 @@ __global__ __launch_bounds__(256) void heads_combine_kernel(HeadsParams p) {
   constexpr int RB = kHeadsRowsPerBlock, NCH = DH / 8;
   static_assert(RB % kHeadsMergeRows == 0, "merge groups tile a row block");
   __shared__ long long slot_base[kMaxMergePieces];
-  const long long G = p.grid;
-  const long long rbg = blockIdx.x / (RB / kHeadsMergeRows);
+  // row blocks from rb_whole on (the ones dealt whole in rounds are done)
+  const long long rbg = p.rb_whole + blockIdx.x / (RB / kHeadsMergeRows);
   const int row_lo = (int)(blockIdx.x % (RB / kHeadsMergeRows)) * kHeadsMergeRows;
   const long long a = rbg * p.nt_max;
-  auto owner = [&](long long x) { return ((x + 1) * G - 1) / p.units; };  // largest g starting at or before x
+  const long long Gr = p.grid_rest, rest = p.units - p.u_rest;
+  // largest g whose range of the remaining units starts at or before unit x
+  auto owner = [&](long long x) { return ((x - p.u_rest + 1) * Gr - 1) / rest; };
   const long long g0 = owner(a), g1 = owner(a + p.nt_max - 1);
   if (g0 == g1) return;  // one work-group covered the row block and wrote it
-  const int np = (int)(g1 - g0 + 1);  // <= kMaxMergePieces by the host's cap on G
+  const int np = (int)(g1 - g0 + 1);  // <= kMaxMergePieces by the host's cap on G'
   if ((int)threadIdx.x < np) {
     const long long g = g0 + threadIdx.x;
-    const long long start = g * p.units / G;
+    const long long start = p.u_rest + g * rest / Gr;
     slot_base[threadIdx.x] = (g * 2 + (start >= a ? 0 : 1)) * RB;
   }
   __syncthreads();
@@ -587,8 +610,9 @@ static hipError_t launch_heads_t(const HeadsParams& p, bool split, hipStream_t s
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL((heads_flash_kernel<DH, DR>), dim3(p.grid), dim3(F::kThreads), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (split) {
-    hipLaunchKernelGGL((heads_combine_kernel<DH>), dim3(p.batch * p.H * p.n_rb * (kHeadsRowsPerBlock / kHeadsMergeRows)),
+  if (split && (long long)p.batch * p.H * p.n_rb > p.rb_whole) {
+    hipLaunchKernelGGL((heads_combine_kernel<DH>),
+                       dim3(((long long)p.batch * p.H * p.n_rb - p.rb_whole) * (kHeadsRowsPerBlock / kHeadsMergeRows)),
                        dim3(256), 0, s, p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }

@@ -326,10 +326,18 @@ FlashPlan heads_plan(const mla_shape* s, int q_n_frames) {
   if (g > (mla::kMaxMergePieces - 1) * row_blocks) g = (mla::kMaxMergePieces - 1) * row_blocks;
   if (g < 1) g = 1;
   f.grid = (int)g;
-  f.rb_whole = 0;
-  f.u_rest = 0;
-  f.grid_rest = (int)g;
-  f.split = !(f.units % g == 0 && (f.units / g) % f.nt_max == 0);
+  // whole row blocks in rounds where there are enough of them, the rest shared
+  f.rb_whole = row_blocks >= g ? row_blocks / g * g : 0;
+  f.u_rest = f.rb_whole * f.nt_max;
+  const int64_t rest = f.units - f.u_rest;
+  int64_t gr = g;
+  if (f.rb_whole > 0) {
+    const int64_t rb_rest = row_blocks - f.rb_whole;
+    if (gr > (mla::kMaxMergePieces - 1) * rb_rest) gr = (mla::kMaxMergePieces - 1) * rb_rest;
+    if (gr > rest) gr = rest;
+  }
+  f.grid_rest = (int)gr;
+  f.split = rest > 0 && !(rest % gr == 0 && (rest / gr) % f.nt_max == 0);
   return f;
 }
 
@@ -784,6 +792,9 @@ static mla_status chunk_attend_heads_impl(const mla_shape* shape, const void* q_
   p.nt_max = f.nt_max;
   p.units = f.units;
   p.grid = f.grid;
+  p.rb_whole = f.rb_whole;
+  p.u_rest = f.u_rest;
+  p.grid_rest = f.grid_rest;
   p.qscale = scale_log2(shape);
   return from_hip(mla::launch_heads(shape->d_c, shape->d_rope, shape->d_head, p, f.split, s));
 }

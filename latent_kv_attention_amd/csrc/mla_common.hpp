@@ -209,6 +209,18 @@ __device__ __forceinline__ int window_rank_of_slot(const int32_t* sf, int W, int
   return r;
 }
 
+// Work-groups are dealt to the 8 XCDs round-robin (work-group i runs on XCD
+// i mod 8). Work-group i gets logical index (XCD-major) so that each XCD's
+// work-groups take consecutive work: with several streams (or heads) an XCD
+// then walks few key sets and its L2 serves them, instead of every XCD
+// touching every one. A bijection of [0, G) for any G.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_major(int id, int G) {
+  const int q = G / kXcds, r = G % kXcds;
+  const int x = id % kXcds, k = id / kXcds;
+  return x * q + min(x, r) + k;
+}
+
 // Rotation of one interleaved pair by the angle whose cos/sin are given.
 __device__ __forceinline__ void rotate_pair(float& a, float& b, float c, float s) {
   const float a0 = a, b0 = b;

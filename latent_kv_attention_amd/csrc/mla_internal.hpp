@@ -160,6 +160,9 @@ struct HeadsParams {
   int n_rb, nt_max;        // row blocks of kHeadsRowsPerBlock tokens per (stream, head); key tiles of a full window
   long long units;         // batch * H * n_rb * nt_max
   int grid;                // G, work-groups of the attention kernel
+  long long rb_whole;      // row blocks dealt whole in rounds (a multiple of G)
+  long long u_rest;        // first unit after them
+  int grid_rest;           // work-groups sharing the units from u_rest on
   float qscale;            // softmax scale * log2(e)
 };
 

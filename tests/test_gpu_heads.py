@@ -71,6 +71,18 @@ def test_heads_batch_and_partial_fill():
     assert_step_close(got, ref, cfg.dtype, label="wan_small per-head B=3 fill=3")
 
 
+def test_heads_many_streams_whole_row_blocks():
+    """30 streams x 12 heads of one row block each: 360 row blocks, more than
+    one per work-group, so the first whole multiple of the work-group count
+    goes out as whole row blocks in a round and the rest are shared (pieces
+    merged). Every element of every stream against the oracle."""
+    cfg = get_config("wan_small")
+    got, ref, _ = _step(cfg, seed=34, B=30)
+    print(f"[heads] 30 streams, {30 * 12} row blocks", flush=True)
+    for b in range(30):
+        assert_step_close(got[b], ref[b], cfg.dtype, label=f"wan_small per-head stream {b} of 30")
+
+
 def test_heads_rollout_ring_eviction():
     """Successive 1-frame chunks over a 3-frame window: eviction from the 4th
     chunk on and t advancing to 9; every step matches the oracle's ring."""
