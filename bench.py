@@ -246,11 +246,11 @@ def setup_step(cfg, kv_splits, dev="cuda"):
                                  tables=tables, n_t=n_t)
 
 
-def settle_clock(ctx, window=20, tol=0.01, max_windows=40):
+def settle_clock(ctx, window=20, tol=0.01, min_windows=5, max_windows=40):
     """The GPU raises its clock over the first tens of milliseconds of load
     after idle (set-up is mostly host work): a timed window started from idle
-    runs the step 4-5% slower than the sustained rate. Before the warm-up and
-    timed steps, run windows of `window` untimed-for-the-result steps until
+    runs the step 4-25% slower than the sustained rate. Before the warm-up and
+    timed steps, run at least `min_windows` windows of `window` steps, until
     two consecutive windows agree within `tol` (at most `max_windows`).
     Returns the first and last window times, reported in the bench line."""
     import torch
@@ -264,12 +264,12 @@ def settle_clock(ctx, window=20, tol=0.01, max_windows=40):
         b.record()
         torch.cuda.synchronize()
         ts.append(a.elapsed_time(b) / window)
-        if len(ts) >= 2 and abs(ts[-1] - ts[-2]) <= tol * ts[-1]:
+        if len(ts) >= min_windows and abs(ts[-1] - ts[-2]) <= tol * ts[-1]:
             break
     print(f"[bench] clock settle: {len(ts)} windows of {window} steps, {ts[0]:.4f} -> {ts[-1]:.4f} ms/step",
           file=sys.stderr, flush=True)
-    return {"what": f"untimed windows of {window} steps run before the warm-up until two consecutive windows agree "
-                    f"within {tol:.0%} (the clock ramps up under load after idle)",
+    return {"what": f"untimed windows of {window} steps run before the warm-up, at least {min_windows} and until two "
+                    f"consecutive windows agree within {tol:.0%} (the clock ramps up under load after idle)",
             "windows": len(ts), "first_window_ms_per_step": round(ts[0], 4), "last_window_ms_per_step": round(ts[-1], 4)}
 
 

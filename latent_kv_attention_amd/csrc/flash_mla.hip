@@ -139,45 +139,65 @@ struct FlashTile {
 // 3D-RoPE of the window's positional keys, once per call: key v = (slot
 // rank r, token tok) of stream b gets R(t, y, x) kR, with t the frame held
 // by the slot of rank r (valid slots ranked by frame, window_rank) and
-// (y, x) the token's grid cell, rounded to the
-// cache's element type. Row v of the stream's block of p.krot. One thread per
-// rotary pair; grid (pair blocks, slots, stream groups). The temporal angles
-// of the slot's frame are formed here (any frame index; the caller's tables
-// only need to cover the query frames), the spatial ones come from the
-// tables. It also clears the count of rows handed to the exact fallback.
+// (y, x) the token's grid cell, rounded to the cache's element type. Row v
+// of the stream's block of p.krot. One thread per 8 elements (4 rotary
+// pairs, one 16-byte piece in bf16); grid (unit blocks, slots, stream
+// groups). Wave 0 of a work-group ranks the slot and sets up the temporal
+// angles of its frame: the table's entries where the table covers the frame
+// (the table kernel formed them with the same function), else formed here
+// (any frame index; the caller's tables only need to cover the query
+// frames). The spatial angles come from the tables. It also clears the count
+// of rows handed to the exact fallback.
 template <typename T, int DC, int DR>
 __global__ __launch_bounds__(256) void rope_window_kernel(FlashParams p) {
-  constexpr int NP = DR / 2;
-  __shared__ float t_cs[2][NP];  // cos, sin of the temporal pairs at the slot's frame
+  constexpr int NP = DR / 2, U = DR / 8;  // rotary pairs, 8-element units per key
+  __shared__ float t_cs[2][NP];            // cos, sin of the temporal pairs at the slot's frame
+  __shared__ int rank_sh;                  // the slot's rank among the valid slots
   if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *p.fallback_count = 0;
   const int slot = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
-  const bool active = e < p.T * NP;
-  const int tok = e / NP, k = e - tok * NP;
+  const bool active = e < p.T * U;
+  const int tok = e / U, q = e - tok * U;  // unit q: pairs 4 q .. 4 q + 3
   const int y = tok / p.grid_x, x = tok - y * p.grid_x;
   const int n_tp = p.rl.d_t / 2;
   for (int b = blockIdx.z; b < p.batch; b += gridDim.z) {
     const int32_t* sf = p.slot_frame + (size_t)b * p.W;
     const int f = sf[slot];  // uniform over the work-group
     if (f < 0) continue;
-    __syncthreads();  // the previous stream's angles are no longer read
-    if ((int)threadIdx.x < n_tp) rope_axis_cos_sin(p.rope_base, f, threadIdx.x, p.rl.d_t, &t_cs[0][threadIdx.x],
-                                                   &t_cs[1][threadIdx.x]);
+    __syncthreads();  // the previous stream's rank and angles are no longer read
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const int r = window_rank(lane < p.W ? sf[lane] : -1, lane);
+      if (lane == slot) rank_sh = r;
+      if (lane < n_tp) {
+        if (f >= p.rl.t_first && f < p.rl.t_first + p.rl.n_t) {
+          const int off = (f - p.rl.t_first) * n_tp + lane;
+          t_cs[0][lane] = p.tables[p.rl.off_ct + off];
+          t_cs[1][lane] = p.tables[p.rl.off_st + off];
+        } else {
+          rope_axis_cos_sin(p.rope_base, f, lane, p.rl.d_t, &t_cs[0][lane], &t_cs[1][lane]);
+        }
+      }
+    }
     __syncthreads();
     if (!active) continue;
-    const int rank = window_rank_of_slot(sf, p.W, slot);
-    const T* src = (const T*)p.cache + (((size_t)b * p.W + slot) * p.T + tok) * (DC + DR) + DC + 2 * k;
-    float a0 = to_f<T>(src[0]), a1 = to_f<T>(src[1]), cs, sn;
-    if (k < n_tp) {
-      cs = t_cs[0][k];
-      sn = t_cs[1][k];
-    } else {
-      rope_cos_sin(p.rl, p.tables, k, 0, y, x, cs, sn);
+    const T* src = (const T*)p.cache + (((size_t)b * p.W + slot) * p.T + tok) * (DC + DR) + DC + 8 * q;
+    float a[8];
+    unpack8<T>(load8<T>(src), a);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = 4 * q + j;
+      float cs, sn;
+      if (k < n_tp) {
+        cs = t_cs[0][k];
+        sn = t_cs[1][k];
+      } else {
+        rope_cos_sin(p.rl, p.tables, k, 0, y, x, cs, sn);
+      }
+      rotate_pair(a[2 * j], a[2 * j + 1], cs, sn);
     }
-    rotate_pair(a0, a1, cs, sn);
-    T* dst = (T*)p.krot + ((size_t)b * p.W * p.T + (size_t)rank * p.T + tok) * DR + 2 * k;
-    dst[0] = to_t<T>(a0);
-    dst[1] = to_t<T>(a1);
+    T* dst = (T*)p.krot + ((size_t)b * p.W * p.T + (size_t)rank_sh * p.T + tok) * DR + 8 * q;
+    store8<T>(dst, pack8<T>(a));
   }
 }
 
@@ -864,7 +884,7 @@ __global__ __launch_bounds__(256) void flash_exact_kernel(FlashParams p) {
 template <typename T, int DC, int DR, bool CAUSAL>
 static hipError_t launch_flash_v(const FlashParams& p, bool split, hipStream_t s) {
   typedef FlashTile<T, DC, DR> F;
-  hipLaunchKernelGGL((rope_window_kernel<T, DC, DR>), dim3((p.T * (DR / 2) + 255) / 256, p.W, min(p.batch, 65535)),
+  hipLaunchKernelGGL((rope_window_kernel<T, DC, DR>), dim3((p.T * (DR / 8) + 255) / 256, p.W, min(p.batch, 65535)),
                      dim3(256), 0, s, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -888,7 +908,7 @@ static hipError_t launch_flash_t(const FlashParams& p, bool split, bool causal, 
 
 template <typename T, int DC, int DR>
 static hipError_t launch_rope_window_t(const FlashParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((rope_window_kernel<T, DC, DR>), dim3((p.T * (DR / 2) + 255) / 256, p.W, min(p.batch, 65535)),
+  hipLaunchKernelGGL((rope_window_kernel<T, DC, DR>), dim3((p.T * (DR / 8) + 255) / 256, p.W, min(p.batch, 65535)),
                      dim3(256), 0, s, p);
   return hipGetLastError();
 }
