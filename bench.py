@@ -313,6 +313,7 @@ def latent_sweep(base, args):
     for dc, dr, split in SWEEP_WIDTHS:
         cfg = base.with_(d_c=dc, d_rope=dr, rope_split=split)
         ctx = setup_step(cfg, args.kv_splits)
+        settle_clock(ctx)
         ms_step, per = time_steps(ctx, args.steps, args.warmup)
         fl = step_flops(cfg)
         fl_tf = fl["flash"] / (per["flash_attend"] * 1e-3) / 1e12
@@ -348,6 +349,7 @@ def per_head_report(base, args):
     for cfg in cases:
         dc, dr = cfg.d_c, cfg.d_rope
         ctx = setup_step(cfg, args.kv_splits)
+        settle_clock(ctx)
         ms_latent, per_latent = time_steps(ctx, args.steps, args.warmup)
         ws = torch.empty(mla.chunk_attend_heads_workspace_bytes(ctx.shape, cfg.chunk_frames), dtype=torch.uint8,
                          device="cuda")
@@ -402,6 +404,7 @@ def frame_causal_report(cfg, args):
     import latent_kv_attention_amd as mla
 
     ctx = setup_step(cfg, 0)
+    settle_clock(ctx)
     ctx.write()
     ws = torch.empty(mla.chunk_attend_workspace_bytes(ctx.shape, cfg.chunk_frames), dtype=torch.uint8, device="cuda")
     outs = {k: torch.empty_like(ctx.out) for k in ("full", "causal")}
