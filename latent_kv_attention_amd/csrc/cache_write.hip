@@ -113,20 +113,29 @@ __global__ __launch_bounds__(256) void cache_write_staged_kernel(CacheWriteParam
   const bool active = col0 + wave * 16 < n_out;  // this wave's 16 outputs exist
   f32x4 acc[kSM / 16] = {};
   // operand reads: staged row r, logical chunk c -> element (r * kSChunks + (c ^ (r % kSChunks))) * 8
+  // all of a stage's operand reads first, then its products: with one wave
+  // per SIMD nothing else hides the LDS latency, so the reads go out
+  // together and the products follow (9% faster than reading each operand
+  // just before its product)
   auto compute = [&](const bf16* buf) {
     if (!active) return;
+    bf16x8 bop[kSK / 32], aop[kSK / 32][kSM / 16];
 #pragma unroll
     for (int kc = 0; kc < kSK / 32; ++kc) {
       const int c = kc * 4 + lg;
       const int rb = kSM + wave * 16 + li;
-      const bf16x8 bop = load8<bf16>(buf + (rb * kSChunks + (c ^ (rb & (kSChunks - 1)))) * 8);
+      bop[kc] = load8<bf16>(buf + (rb * kSChunks + (c ^ (rb & (kSChunks - 1)))) * 8);
 #pragma unroll
       for (int mb = 0; mb < kSM / 16; ++mb) {
         const int ra = mb * 16 + li;
-        const bf16x8 aop = load8<bf16>(buf + (ra * kSChunks + (c ^ (ra & (kSChunks - 1)))) * 8);
-        acc[mb] = mma16(aop, bop, acc[mb]);
+        aop[kc][mb] = load8<bf16>(buf + (ra * kSChunks + (c ^ (ra & (kSChunks - 1)))) * 8);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kc = 0; kc < kSK / 32; ++kc)
+#pragma unroll
+      for (int mb = 0; mb < kSM / 16; ++mb) acc[mb] = mma16(aop[kc][mb], bop[kc], acc[mb]);
   };
 
   // kSBufs - 1 stages in flight: wait for this wave's loads of stage s
@@ -250,24 +259,31 @@ __global__ __launch_bounds__(256) void cache_write_wide_kernel(CacheWriteParams 
 
   f32x4 acc[4][NCB] = {};
   // staged row r, logical chunk c: element (r * 8 + (c ^ (r % 8))) * 8
+  // all of a stage's operand reads first, then its products (one wave per
+  // SIMD: nothing else hides the LDS latency)
   auto compute = [&](const bf16* buf) {
+    bf16x8 aop[kWK / 32][4], bop[kWK / 32][NCB];
 #pragma unroll
     for (int kc = 0; kc < kWK / 32; ++kc) {
       const int c = kc * 4 + lg;
-      bf16x8 aop[4];
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const int ra = wr * 64 + mb * 16 + li;
-        aop[mb] = load8<bf16>(buf + (ra * kWChunks + (c ^ (ra & 7))) * 8);
+        aop[kc][mb] = load8<bf16>(buf + (ra * kWChunks + (c ^ (ra & 7))) * 8);
       }
 #pragma unroll
       for (int nb = 0; nb < NCB; ++nb) {
         const int rb = kWM + (wc * NCB + nb) * 16 + li;
-        const bf16x8 bop = load8<bf16>(buf + (rb * kWChunks + (c ^ (rb & 7))) * 8);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = mma16(aop[mb], bop, acc[mb][nb]);
+        bop[kc][nb] = load8<bf16>(buf + (rb * kWChunks + (c ^ (rb & 7))) * 8);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kc = 0; kc < kWK / 32; ++kc)
+#pragma unroll
+      for (int nb = 0; nb < NCB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = mma16(aop[kc][mb], bop[kc][nb], acc[mb][nb]);
   };
 
   auto buf = [&](int i) -> bf16* { return i == 0 ? wb0 : i == 1 ? wb1 : wb2; };
