@@ -316,6 +316,16 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
 
     // position 0 visits the last tile of the range (the one that can be
     // ragged), positions 1.. the others in order
+    // buffer resources of the head's expanded keys and values and the
+    // stream's rotated kR: the buffer form of the direct loads counts its LDS
+    // writes on the vector-memory counter alone, so the operand reads keep
+    // exact partial waits while the next tile's loads are in flight
+    const __amdgpu_buffer_rsrc_t k_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)kb_src, 0, (int)((size_t)p.W * p.T * DH * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t v_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)vb_src, 0, (int)((size_t)p.W * p.T * DH * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t r_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)rb_src, 0, (int)((size_t)p.W * p.T * DR * 2), 0x00020000);
     auto tile_of = [&](int pos) { return pos == 0 ? tile_end - 1 : tile_begin + pos - 1; };
     auto issue = [&](int pos, bf16* kt, bf16* vt, bf16* rt) {
       const int kbase = tile_of(pos) * kBN;
@@ -324,9 +334,8 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
         const int pk = opaque_h(kpk[k]);
         if (pk >= 0) {
           const int v = min(kbase + (pk >> 16), n_keys - 1);
-          __builtin_amdgcn_global_load_lds(
-              (const __attribute__((address_space(1))) void*)(kb_src + (unsigned)(v * DH * 2 + (pk & 0xffff))),
-              (MLA_LDS void*)(MLA_LDS bf16*)(kt + (wave + kWaves * k) * 64 * 8), 16, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rs, (MLA_LDS void*)(MLA_LDS bf16*)(kt + (wave + kWaves * k) * 64 * 8), 16,
+                                                   (unsigned)(v * DH * 2 + (pk & 0xffff)), 0, 0, 0);
         }
       }
 #pragma unroll
@@ -334,9 +343,8 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
         const int pk = opaque_h(vpk[k]);
         if (pk >= 0) {
           const int v = min(kbase + (pk >> 16), n_keys - 1);
-          __builtin_amdgcn_global_load_lds(
-              (const __attribute__((address_space(1))) void*)(vb_src + (unsigned)(v * DH * 2 + (pk & 0xffff))),
-              (MLA_LDS void*)(MLA_LDS bf16*)(vt + (wave + kWaves * k) * 64 * 8), 16, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rs, (MLA_LDS void*)(MLA_LDS bf16*)(vt + (wave + kWaves * k) * 64 * 8), 16,
+                                                   (unsigned)(v * DH * 2 + (pk & 0xffff)), 0, 0, 0);
         }
       }
 #pragma unroll
@@ -344,9 +352,8 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
         const int pk = opaque_h(rpk[k]);
         if (pk >= 0) {
           const int v = min(kbase + (pk >> 16), n_keys - 1);
-          __builtin_amdgcn_global_load_lds(
-              (const __attribute__((address_space(1))) void*)(rb_src + (unsigned)(v * DR * 2 + (pk & 0xffff))),
-              (MLA_LDS void*)(MLA_LDS bf16*)(rt + (wave + kWaves * k) * 64 * 8), 16, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r_rs, (MLA_LDS void*)(MLA_LDS bf16*)(rt + (wave + kWaves * k) * 64 * 8), 16,
+                                                   (unsigned)(v * DR * 2 + (pk & 0xffff)), 0, 0, 0);
         }
       }
     };
@@ -380,12 +387,54 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
         pb[mb] = pack8<bf16>(f8);
       }
     };
-    auto values = [&](const bf16* vt, int half, const v8 (&pb)[kNMB]) {
+    // The tile body's products with their operand reads run ahead: score
+    // operands DQ contraction steps, value operands DV d-blocks (scheduling
+    // barriers keep each read that far ahead of its product).
+    auto scores_ahead = [&](const bf16* kt, const bf16* rt, int half, sblk& s) {
+      constexpr int DQ = DR > 32 ? 2 : 3;  // the wider positional part leaves fewer registers
+      v8 ka[DQ + 1][2];
+      auto kop = [&](int kc, int kb) -> v8 {
+        const int row = (half * 2 + kb) * 16 + li, dim = kc * 32 + lg * 8;
+        return kc < F::NKCH ? lds_load8<bf16>(kt + row * F::LSK + dim)
+                            : lds_load8<bf16>(rt + row * DR + F::kr_slot(row, (dim - DH) / 8) * 8);
+      };
+#pragma unroll
+      for (int d = 0; d < DQ; ++d)
+        if (d < F::NKC) {
+          ka[d][0] = kop(d, 0);
+          ka[d][1] = kop(d, 1);
+        }
+#pragma unroll
+      for (int kc = 0; kc < F::NKC; ++kc) {
+        if (kc + DQ < F::NKC) {
+          ka[(kc + DQ) % (DQ + 1)][0] = kop(kc + DQ, 0);
+          ka[(kc + DQ) % (DQ + 1)][1] = kop(kc + DQ, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int mb = 0; mb < kNMB; ++mb)
+            s[kb][mb] = mma16(ka[kc % (DQ + 1)][kb], qf[mb][kc], kc == 0 ? negref[mb] : s[kb][mb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto vop = [&](const bf16* vt, int half, int db) {
+      return lds_tr8(vt, F::LSV, half * 32 + lg * 4, half * 32 + 16 + lg * 4, db * 16);
+    };
+    auto values_ahead = [&](const bf16* vt, int half, const v8 (&pb)[kNMB]) {
+      constexpr int DV = 3;
+      v8 va[DV + 1];
+#pragma unroll
+      for (int d = 0; d < DV; ++d)
+        if (d < F::NDB) va[d] = vop(vt, half, d);
 #pragma unroll
       for (int db = 0; db < F::NDB; ++db) {
-        const v8 a = lds_tr8(vt, F::LSV, half * 32 + lg * 4, half * 32 + 16 + lg * 4, db * 16);
+        if (db + DV < F::NDB) va[(db + DV) % (DV + 1)] = vop(vt, half, db + DV);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mb = 0; mb < kNMB; ++mb) o[db][mb] = mma16(a, pb[mb], o[db][mb]);
+        for (int mb = 0; mb < kNMB; ++mb) o[db][mb] = mma16(va[db % (DV + 1)], pb[mb], o[db][mb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     auto step = [&](int pos, auto cur_c, auto ragged_c) {
@@ -401,10 +450,10 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
 #pragma unroll 1
       for (int half = 0; half < NKC2; ++half) {
         sblk s;
-        scores(kt, rt, half, s, negref);
+        scores_ahead(kt, rt, half, s);
         v8 pb[kNMB];
         probs(s, pb, kbase + half * 32, ragged_c);
-        values(vt, half, pb);
+        values_ahead(vt, half, pb);
       }
       __builtin_amdgcn_s_waitcnt(0);  // direct loads of the next tile have landed
       __syncthreads();
