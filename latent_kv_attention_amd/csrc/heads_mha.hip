@@ -391,7 +391,7 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
     // operands DQ contraction steps, value operands DV d-blocks (scheduling
     // barriers keep each read that far ahead of its product).
     auto scores_ahead = [&](const bf16* kt, const bf16* rt, int half, sblk& s) {
-      constexpr int DQ = DR > 32 ? 2 : 3;  // the wider positional part leaves fewer registers
+      constexpr int DQ = DR > 32 ? 1 : 3;  // the wider positional part leaves fewer registers
       v8 ka[DQ + 1][2];
       auto kop = [&](int kc, int kb) -> v8 {
         const int row = (half * 2 + kb) * 16 + li, dim = kc * 32 + lg * 8;
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
       return lds_tr8(vt, F::LSV, half * 32 + lg * 4, half * 32 + 16 + lg * 4, db * 16);
     };
     auto values_ahead = [&](const bf16* vt, int half, const v8 (&pb)[kNMB]) {
-      constexpr int DV = 3;
+      constexpr int DV = DR > 32 ? 2 : 3;
       v8 va[DV + 1];
 #pragma unroll
       for (int d = 0; d < DV; ++d)
