@@ -247,8 +247,8 @@ mla_status mla_up_v(const mla_shape* shape, const void* o_lat, int32_t q_n_frame
  *   - the per-head form, mla_chunk_attend_heads (below).
  * mla_chunk_attend takes the form mla_chunk_attend_form names for the shape
  * and chunk size: the per-head form where it is supported (bf16,
- * d_head = 128), does at least 15% fewer products per (query, key, head)
- * (2 d_head + d_rope against 2 d_c + d_rope) and the chunk has at least 1024
+ * d_head = 128), does at least 20% fewer products per (query, key, head)
+ * (2 d_head + d_rope against 2 d_c + d_rope) and the chunk has at least 2048
  * query tokens per stream to repay its per-call expansion of the window's
  * keys and values; else the latent form. At the Wan2.1 shape (d_c 192,
  * 3-frame chunks of 4680 tokens) that is the per-head form.

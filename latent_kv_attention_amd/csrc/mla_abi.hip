@@ -564,13 +564,15 @@ static size_t heads_ws_bytes(const mla_shape* shape, int32_t q_n_frames);
 // 2 d_head + d_rope products per (query, key, head) against the latent
 // form's 2 d_c + d_rope, plus a per-call expansion of the window's keys and
 // values (4 d_head d_c products per key and head) that only a large enough
-// chunk repays: it is taken where it is supported, saves at least 15% of the
-// products, and the chunk has at least 1024 query tokens per stream.
-// Measured at the Wan2.1 width (d_c 192, d_rope 32): 1.25x faster at a
-// 3-frame chunk (4680 queries), 1.07x at 1 frame (1560); 0.89x at
-// (d_c, d_rope) = (128, 32), where the products are equal.
-constexpr double kHeadsMinProductRatio = 1.15;
-constexpr int64_t kHeadsMinQueries = 1024;
+// chunk repays: it is taken where it is supported, saves at least 20% of the
+// products, and the chunk has at least 2048 query tokens per stream.
+// Measured with both forms' kernels as they are (latent form in the step,
+// clock settled): at the Wan2.1 width (d_c 192, d_rope 32) the per-head form
+// is 1.15x faster at a 3-frame chunk (4680 queries), 1.07x at 2 frames
+// (3120) and 0.96x at 1 frame (1560); 1.14x at (192, 64), 1.00x at
+// (160, 64) (products ratio 1.2) and 0.76x at (128, 32) (ratio 1.0).
+constexpr double kHeadsMinProductRatio = 1.25;
+constexpr int64_t kHeadsMinQueries = 2048;
 
 static bool heads_preferred(const mla_shape* s, int32_t q_n_frames) {
   if (!mla::heads_supported(s->dtype == MLA_BF16 ? 0 : 1, s->d_c, s->d_rope, s->d_head)) return false;

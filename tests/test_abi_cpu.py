@@ -200,17 +200,19 @@ def test_ceiling_probe_library_loads_and_checks_arguments():
 
 def test_chunk_attend_form_selection(built_lib):
     """mla_chunk_attend takes the per-head form at the Wan2.1 width for chunks
-    of at least 1024 queries per stream, and the latent form for small
+    of at least 2048 queries per stream, and the latent form for small
     chunks, equal product counts (d_c 128), fp32 and unsupported head widths."""
     def form(name, nf, **kw):
         return mla.chunk_attend_form(mla.make_shape(get_config(name).with_(**kw)), nf)
-    assert form("wan", 3) == mla.FORM_HEADS and form("wan", 1) == mla.FORM_HEADS
+    assert form("wan", 3) == mla.FORM_HEADS and form("wan", 2) == mla.FORM_HEADS
+    assert form("wan", 1) == mla.FORM_LATENT                             # 1560 queries
     assert form("wan", 3, batch=8) == mla.FORM_HEADS
     assert form("wan_small", 2) == mla.FORM_LATENT                       # 132 queries
-    assert form("wan_small", 1, grid_y=32, grid_x=32) == mla.FORM_HEADS  # 1024 queries
-    assert form("wan_small", 1, grid_y=31, grid_x=33) == mla.FORM_LATENT  # 1023
+    assert form("wan_small", 1, grid_y=32, grid_x=64) == mla.FORM_HEADS  # 2048 queries
+    assert form("wan_small", 1, grid_y=31, grid_x=66) == mla.FORM_LATENT  # 2046
     assert form("wan", 3, d_c=128) == mla.FORM_LATENT
-    assert form("wan", 3, d_c=160, d_rope=64, rope_split=(16, 24, 24)) == mla.FORM_HEADS
+    assert form("wan", 3, d_c=160, d_rope=64, rope_split=(16, 24, 24)) == mla.FORM_LATENT  # ratio 1.2
+    assert form("wan", 3, d_c=192, d_rope=64, rope_split=(16, 24, 24)) == mla.FORM_HEADS
     assert form("wan", 3, dtype="f32") == mla.FORM_LATENT
     assert form("wan", 3, d_head=64) == mla.FORM_LATENT
     assert form("wan", 0) == -1

@@ -145,12 +145,12 @@ def test_layer_step(name):
 
 @pytest.mark.parametrize("fused", [False, True])
 def test_layer_step_where_the_per_head_form_is_taken(fused):
-    """A 32 x 32 grid with the Wan head shapes: a one-frame chunk has 1024
+    """A 32 x 64 grid with the Wan head shapes: a one-frame chunk has 2048
     queries, so the layer step takes the per-head attention (also when the
     absorbed query weights are set, since the per-head weights are there
     too); chunk after chunk through ring wrap against O.layer_step, and the
     frame-causal step on the same layer (latent form) in between."""
-    cfg = get_config("wan_small").with_(grid_y=32, grid_x=32, window_frames=3, chunk_frames=1)
+    cfg = get_config("wan_small").with_(grid_y=32, grid_x=64, window_frames=3, chunk_frames=1)
     w, wd = _weights(cfg, 58)
     layer = LatentLayer(cfg, wd, batch=1, rope_n_t=64)
     assert mla.chunk_attend_form(layer.shape, 1) == mla.FORM_HEADS
