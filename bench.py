@@ -396,8 +396,10 @@ def per_head_report(base, args):
 
 
 def frame_causal_report(cfg, args):
-    """The attention side (mla_chunk_attend) with and without the frame-causal
-    mask inside the chunk, at the Wan shape. One JSON report line."""
+    """The attention side with and without the frame-causal mask inside the
+    chunk, at the Wan shape, in both forms (mla_chunk_attend_latent /
+    mla_chunk_attend_latent_frame_causal and mla_chunk_attend_heads /
+    mla_chunk_attend_heads_frame_causal). One JSON report line."""
     import numpy as np
     import torch
 
@@ -407,34 +409,40 @@ def frame_causal_report(cfg, args):
     settle_clock(ctx)
     ctx.write()
     ws = torch.empty(mla.chunk_attend_workspace_bytes(ctx.shape, cfg.chunk_frames), dtype=torch.uint8, device="cuda")
-    outs = {k: torch.empty_like(ctx.out) for k in ("full", "causal")}
-    # the latent form on both sides (mla_chunk_attend takes the per-head form
-    # at this shape, which has no frame-causal variant)
-    calls = {"full": mla.chunk_attend_latent, "causal": mla.chunk_attend_frame_causal}
+    hws = torch.empty(mla.chunk_attend_heads_workspace_bytes(ctx.shape, cfg.chunk_frames), dtype=torch.uint8,
+                      device="cuda")
+    calls = {"latent_full": (mla.chunk_attend_latent, ws),
+             "latent_causal": (mla.chunk_attend_latent_frame_causal, ws),
+             "heads_full": (mla.chunk_attend_heads, hws),
+             "heads_causal": (mla.chunk_attend_heads_frame_causal, hws)}
+    outs = {k: torch.empty_like(ctx.out) for k in calls}
     ts = {k: [] for k in calls}
     for rnd in range(args.warmup + args.steps):
-        for k, fn in calls.items():
+        for k, (fn, w) in calls.items():
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             fn(ctx.shape, ctx.qn, ctx.qr, ctx.chunk_first, cfg.chunk_frames, ctx.w["w_uk"], ctx.w["w_uv"], ctx.cache,
-               ctx.slot_frame, ctx.tables, 0, ctx.n_t, outs[k], ws)
+               ctx.slot_frame, ctx.tables, 0, ctx.n_t, outs[k], w)
             b.record()
             torch.cuda.synchronize()
             if rnd >= args.warmup:
                 ts[k].append(a.elapsed_time(b))
     T = cfg.tokens_per_frame
+    last = (cfg.chunk_frames - 1) * T
     # keys each chunk frame may not see: the later chunk frames
     masked_frac = sum(cfg.chunk_frames - 1 - k for k in range(cfg.chunk_frames)) / (cfg.chunk_frames * cfg.window_frames)
-    full_ms, causal_ms = float(np.median(ts["full"])), float(np.median(ts["causal"]))
+    ms = {k: float(np.median(v)) for k, v in ts.items()}
+    selected = "heads" if mla.chunk_attend_form(ctx.shape, cfg.chunk_frames) == mla.FORM_HEADS else "latent"
     print(json.dumps({
-        "report": "frame-causal vs full attention inside the chunk (latent form), Wan2.1-1.3B-shaped chunk step "
+        "report": "frame-causal vs full attention inside the chunk, both forms, Wan2.1-1.3B-shaped chunk step "
                   "(4680 queries x 32760 keys), 1 MI355X",
-        "full_attend_ms": round(full_ms, 4),
-        "frame_causal_attend_ms": round(causal_ms, 4),
+        **{f"{k}_attend_ms": round(v, 4) for k, v in ms.items()},
         "masked_key_fraction": round(masked_frac, 4),
-        "time_ratio": round(causal_ms / full_ms, 4),
-        "rows_identical_in_last_frame": bool(torch.equal(outs["full"][(cfg.chunk_frames - 1) * T:],
-                                                         outs["causal"][(cfg.chunk_frames - 1) * T:])),
+        "latent_time_ratio": round(ms["latent_causal"] / ms["latent_full"], 4),
+        "heads_time_ratio": round(ms["heads_causal"] / ms["heads_full"], 4),
+        "selected_form": selected,
+        "rows_identical_in_last_frame": {
+            f: bool(torch.equal(outs[f + "_full"][last:], outs[f + "_causal"][last:])) for f in ("latent", "heads")},
         "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic"}), flush=True)
 
 

@@ -279,13 +279,21 @@ mla_status mla_chunk_attend_latent(const mla_shape* shape, const void* q_nope, c
  * only the keys of frames <= f. Keys of earlier chunks are all visible and
  * a query always sees its own frame's keys (when they are in the window).
  * Same arguments, workspace (mla_chunk_attend_workspace_bytes) and errors as
- * mla_chunk_attend. Key tiles that no row of a 256-row block can see are
- * skipped; tiles that every row sees run unmasked. */
+ * mla_chunk_attend, and the same choice of form (mla_chunk_attend_form):
+ * mla_chunk_attend_latent_frame_causal and
+ * mla_chunk_attend_heads_frame_causal (below, with the per-head form's
+ * workspace) force one. Only the key tiles a row block may see are visited;
+ * tiles that every row of a block sees run unmasked. */
 mla_status mla_chunk_attend_frame_causal(const mla_shape* shape, const void* q_nope, const void* q_r,
                                          int32_t q_frame_first, int32_t q_n_frames, const void* w_uk,
                                          const void* w_uv, const void* cache, const int32_t* slot_frame,
                                          const float* rope_tables, int32_t rope_t_first, int32_t rope_n_t,
                                          void* out, void* workspace, size_t workspace_bytes, void* stream);
+mla_status mla_chunk_attend_latent_frame_causal(const mla_shape* shape, const void* q_nope, const void* q_r,
+                                                int32_t q_frame_first, int32_t q_n_frames, const void* w_uk,
+                                                const void* w_uv, const void* cache, const int32_t* slot_frame,
+                                                const float* rope_tables, int32_t rope_t_first, int32_t rope_n_t,
+                                                void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- a3'..a5'
  * Per-head form of the same step (hyper.ai summary, Method: per-head keys
@@ -310,6 +318,14 @@ mla_status mla_chunk_attend_heads(const mla_shape* shape, const void* q_nope, co
                                   const void* cache, const int32_t* slot_frame, const float* rope_tables,
                                   int32_t rope_t_first, int32_t rope_n_t, void* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
+/* The per-head form with the frame-causal mask of
+ * mla_chunk_attend_frame_causal; arguments, workspace and errors as
+ * mla_chunk_attend_heads. */
+mla_status mla_chunk_attend_heads_frame_causal(const mla_shape* shape, const void* q_nope, const void* q_r,
+                                               int32_t q_frame_first, int32_t q_n_frames, const void* w_uk,
+                                               const void* w_uv, const void* cache, const int32_t* slot_frame,
+                                               const float* rope_tables, int32_t rope_t_first, int32_t rope_n_t,
+                                               void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- query path
  * Queries of the chunk's tokens (hyper.ai summary, Method: a query latent is

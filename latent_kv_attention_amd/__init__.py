@@ -10,6 +10,6 @@ from ._lib import (  # noqa: F401
     rope3d_table_floats, rope3d_tables, cache_write, absorb_q, flash_workspace_bytes, flash_attend,
     flash_attend_frame_causal, flash_attend_noalloc, NOALLOC_SCRATCH_BYTES,
     up_v, chunk_attend_workspace_bytes, chunk_attend, chunk_attend_latent, chunk_attend_form, FORM_LATENT, FORM_HEADS, chunk_attend_heads_workspace_bytes, chunk_attend_heads,
-    chunk_attend_frame_causal, query_project, output_project, MlaLayerWeights, layer_weights_struct,
+    chunk_attend_frame_causal, chunk_attend_latent_frame_causal, chunk_attend_heads_frame_causal, query_project, output_project, MlaLayerWeights, layer_weights_struct,
     layer_step_workspace_bytes, layer_step, query_absorb_weights, query_project_absorbed,
 )

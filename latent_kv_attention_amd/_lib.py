@@ -28,6 +28,7 @@ EXPORTS = [
     "mla_up_v",
     "mla_chunk_attend_workspace_bytes", "mla_chunk_attend", "mla_chunk_attend_latent", "mla_chunk_attend_form",
     "mla_chunk_attend_heads_workspace_bytes", "mla_chunk_attend_heads", "mla_chunk_attend_frame_causal",
+    "mla_chunk_attend_latent_frame_causal", "mla_chunk_attend_heads_frame_causal",
     "mla_query_project", "mla_output_project", "mla_layer_step_workspace_bytes", "mla_layer_step",
     "mla_query_absorb_weights", "mla_query_project_absorbed",
 ]
@@ -79,6 +80,8 @@ _SIGS = {
     "mla_chunk_attend_heads_workspace_bytes": (_SZ, [_SP, _I]),
     "mla_chunk_attend_frame_causal": (_I, [_SP, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
     "mla_chunk_attend_heads": (_I, [_SP, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
+    "mla_chunk_attend_latent_frame_causal": (_I, [_SP, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
+    "mla_chunk_attend_heads_frame_causal": (_I, [_SP, _P, _P, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
     "mla_query_project": (_I, [_SP, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P]),
     "mla_output_project": (_I, [_SP, _P, _I, _P, _P, _P]),
     "mla_layer_step_workspace_bytes": (_SZ, [_SP, _I, _I]),
@@ -262,15 +265,34 @@ def chunk_attend_heads(shape: MlaShape, q_nope, q_r, q_frame_first: int, q_n_fra
                                         _stream(stream)))
 
 
+def _chunk_attend_call(name, shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk, w_uv, cache, slot_frame, tables,
+                       rope_t_first, rope_n_t, out, workspace, stream):
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(name, getattr(lib(), name)(ctypes.byref(shape), _ptr(q_nope), _ptr(q_r), q_frame_first, q_n_frames,
+                                      _ptr(w_uk), _ptr(w_uv), _ptr(cache), _ptr(slot_frame, "int32"),
+                                      _ptr(tables, "float32"), rope_t_first, rope_n_t, _ptr(out), _ptr(workspace),
+                                      nbytes, _stream(stream)))
+
+
 def chunk_attend_frame_causal(shape: MlaShape, q_nope, q_r, q_frame_first: int, q_n_frames: int, w_uk, w_uv, cache,
                               slot_frame, tables, rope_t_first: int, rope_n_t: int, out, workspace,
                               stream=None) -> None:
-    nbytes = workspace.numel() * workspace.element_size()
-    _check("mla_chunk_attend_frame_causal",
-           lib().mla_chunk_attend_frame_causal(ctypes.byref(shape), _ptr(q_nope), _ptr(q_r), q_frame_first,
-                                               q_n_frames, _ptr(w_uk), _ptr(w_uv), _ptr(cache), _ptr(slot_frame, "int32"),
-                                               _ptr(tables, "float32"), rope_t_first, rope_n_t, _ptr(out), _ptr(workspace),
-                                               nbytes, _stream(stream)))
+    _chunk_attend_call("mla_chunk_attend_frame_causal", shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk, w_uv,
+                       cache, slot_frame, tables, rope_t_first, rope_n_t, out, workspace, stream)
+
+
+def chunk_attend_latent_frame_causal(shape: MlaShape, q_nope, q_r, q_frame_first: int, q_n_frames: int, w_uk, w_uv,
+                                     cache, slot_frame, tables, rope_t_first: int, rope_n_t: int, out, workspace,
+                                     stream=None) -> None:
+    _chunk_attend_call("mla_chunk_attend_latent_frame_causal", shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk,
+                       w_uv, cache, slot_frame, tables, rope_t_first, rope_n_t, out, workspace, stream)
+
+
+def chunk_attend_heads_frame_causal(shape: MlaShape, q_nope, q_r, q_frame_first: int, q_n_frames: int, w_uk, w_uv,
+                                    cache, slot_frame, tables, rope_t_first: int, rope_n_t: int, out, workspace,
+                                    stream=None) -> None:
+    _chunk_attend_call("mla_chunk_attend_heads_frame_causal", shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk,
+                       w_uv, cache, slot_frame, tables, rope_t_first, rope_n_t, out, workspace, stream)
 
 
 def query_project(shape: MlaShape, d_cq: int, x, n_frames: int, w_dq, w_uq, w_qr, c_q, q_nope, q_r,

@@ -22,8 +22,9 @@
 // of the value product do not conflict). Scores are formed transposed,
 // S^T = K Q^T, so the probabilities land in the operand layout of
 // O^T = V^T P^T; the softmax uses a fixed per-row reference (the maximum of
-// the first 32 keys' scores) and lists rows whose sum overflows for an
-// exact two-pass kernel, as the latent form does.
+// the first 32 keys' scores) and lists rows whose sum leaves [2^-100, 2^100]
+// for an exact two-pass kernel, as the latent form does; the frame-causal
+// variant walks each row's visible prefix of the window.
 #include <type_traits>
 
 #include "mla_common.hpp"
@@ -34,7 +35,8 @@ namespace mla {
 
 namespace {
 constexpr int kSlots = 64;
-constexpr float kHeadsSumLimit = 1.2676506e30f;  // 2^100
+constexpr float kHeadsSumLimit = 0x1p100f;
+constexpr float kHeadsSumMin = 0x1p-100f;
 constexpr int kExpWaves = 8;
 constexpr int kExpKeys = kExpWaves * 64;  // keys per expansion work-group
 
@@ -191,7 +193,13 @@ struct HeadsTile {
   static_assert(DH % 32 == 0 && DR % 32 == 0 && (U8 & (U8 - 1)) == 0, "whole 32-wide contraction blocks");
 };
 
-template <int DH, int DR>
+// CAUSAL: the frame-causal variant (a query of frame f attends only keys of
+// frames <= f). Keys are in frame order, so the keys a row sees are a prefix
+// of the window; as in the latent form, only the units a row block may see
+// are dealt out (classes of row blocks), the tiles not seen whole by every
+// row of a block are visited first through the limited tile body (keys past
+// each row's prefix weigh zero), the rest with the plain body.
+template <int DH, int DR, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
   typedef HeadsTile<DH, DR> F;
   constexpr int kBN = F::kBN, kNMB = F::kNMB, kWaves = F::kWaves, NKC2 = F::NKC2;
@@ -205,6 +213,10 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
   __shared__ __attribute__((aligned(16))) bf16 r0[F::R_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 r1[F::R_ELEMS];
   __shared__ int n_valid_sh;
+  __shared__ int frame_of[CAUSAL ? kSlots : 1];  // frame held by the r-th valid slot
+  // frame-causal: end of each row's visible key prefix (in LDS, not in
+  // registers: the tile body keeps its load descriptors resident)
+  __shared__ int vis_sh[CAUSAL ? F::kRowsBlock : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -251,44 +263,87 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
   const long long u_last = g < p.grid_rest ? p.u_rest + ((long long)g + 1) * rest / p.grid_rest : p.units;
   long long round = 0;
   for (long long u = u_last;;) {
-    long long rbg;  // row block over all (stream, head) pairs
+    long long rbg, ua;  // row block over all (stream, head) pairs, its first unit
+    int nt;             // its unit count
     int j0, j1;
     bool first_seg;
     if (round < rounds) {
       rbg = round * G + g;
       ++round;
+      row_block_units(p.classes, p.n_rb, rbg, ua, nt);
       j0 = 0;
-      j1 = p.nt_max;
+      j1 = nt;
       first_seg = false;
     } else {
       if (u <= u_first) break;
-      rbg = (u - 1) / p.nt_max;
-      const long long seg0 = max(u_first, rbg * p.nt_max);
-      j0 = (int)(seg0 - rbg * p.nt_max);
-      j1 = (int)(u - rbg * p.nt_max);
+      locate_unit(p.classes, p.n_rb, u - 1, rbg, ua, nt);
+      const long long seg0 = max(u_first, ua);
+      j0 = (int)(seg0 - ua);
+      j1 = (int)(u - ua);
       first_seg = seg0 == u_first;
       u = seg0;
     }
-    const bool whole = j0 == 0 && j1 == p.nt_max;
+    const bool whole = j0 == 0 && j1 == nt;
     const int bh = (int)(rbg / p.n_rb), rb = (int)(rbg - (long long)bh * p.n_rb);  // bh = b * H + h
     const int h = bh % p.H, b = bh / p.H;
     __syncthreads();  // LDS of the previous segment is no longer read
     if (wave == 0) {
       const int f = lane < p.W ? p.slot_frame[b * p.W + lane] : -1;
+      if constexpr (CAUSAL) {
+        const int rank = window_rank(f, lane);
+        if (f >= 0) frame_of[rank] = f;
+      }
       const unsigned long long mask = __ballot(f >= 0);
       if (lane == 0) n_valid_sh = __popcll(mask);
     }
     __syncthreads();
     const int n_keys = n_valid_sh * p.T;
-    const int n_tiles = (n_keys + kBN - 1) / kBN;
-    // this segment's share of the window's tiles (units map onto the tiles
-    // of a full window; a partly filled window scales proportionally)
-    const int tile_begin = (int)((long long)j0 * n_tiles / p.nt_max);
-    const int tile_end = (int)((long long)j1 * n_tiles / p.nt_max);
+    const int tok_wave = rb * F::kRowsBlock + wave * F::kRowsWave;
+    // Frame-causal variant: the end of the visible prefix of each row of the
+    // wave (vis_sh, read through vis_end: T times the valid slots whose frame
+    // is at most the row's), of the block's first row (vis_lo: every row sees
+    // the keys before it) and of its last row (n_keys_rb: the keys the block
+    // visits). A wave writes and reads only its own rows' entries.
+    int vis_lo = n_keys, n_keys_rb = n_keys;
+    if constexpr (CAUSAL) {
+      auto visible_keys = [&](int qf) {
+        int n = 0;
+        for (int r = 0; r < n_valid_sh; ++r) n += frame_of[r] <= qf ? 1 : 0;
+        return n * p.T;
+      };
+#pragma unroll
+      for (int mb = 0; mb < kNMB; ++mb) {
+        const int tok = tok_wave + mb * 16 + li;
+        if (lg == 0)
+          vis_sh[wave * F::kRowsWave + mb * 16 + li] = tok < p.Nq ? visible_keys(p.q_frame_first + tok / p.T) : n_keys;
+      }
+      const int t_first = rb * F::kRowsBlock, t_last = min(t_first + F::kRowsBlock, p.Nq) - 1;
+      vis_lo = visible_keys(p.q_frame_first + t_first / p.T);
+      n_keys_rb = visible_keys(p.q_frame_first + t_last / p.T);
+    }
+    // visible prefix of the lane's row mb (the window's keys without the mask)
+    auto vis_end = [&](int mb) { return CAUSAL ? vis_sh[wave * F::kRowsWave + mb * 16 + li] : n_keys; };
+    const int n_tiles = (n_keys_rb + kBN - 1) / kBN;
+    // this segment's share of the row block's tiles (units map onto the
+    // tiles of a full window; a partly filled window scales proportionally)
+    const int tile_begin = (int)((long long)j0 * n_tiles / nt);
+    const int tile_end = (int)((long long)j1 * n_tiles / nt);
     const int n_visit = max(0, tile_end - tile_begin);
+    // Positions 0 .. n_lim - 1 visit the range's last tiles, last first,
+    // through the limited body (past the window for the ragged last tile;
+    // past the row's prefix under the frame-causal mask: the tiles not seen
+    // whole by every row of the block, an odd count where the range allows,
+    // so the plain positions start on the same tile buffer).
+    int n_lim = n_visit > 0 ? 1 : 0;
+    if constexpr (CAUSAL) {
+      if (n_visit > 0) {
+        int m = max(1, tile_end - max(tile_begin, vis_lo / kBN));
+        if (m % 2 == 0) m = min(m + 1, n_visit);
+        n_lim = m;
+      }
+    }
 
     // queries of this wave (B operand of S^T = K Q^T), kept in registers
-    const int tok_wave = rb * F::kRowsBlock + wave * F::kRowsWave;
     const bf16* qb = (const bf16*)p.q_cat + (size_t)bh * p.Nq * F::QP;
     v8 qf[kNMB][F::NKC];
 #pragma unroll
@@ -314,8 +369,6 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
     const char* vb_src = (const char*)((const bf16*)p.v_exp + head_rows * DH);
     const char* rb_src = (const char*)((const bf16*)p.krot + (size_t)b * p.W * p.T * DR);
 
-    // position 0 visits the last tile of the range (the one that can be
-    // ragged), positions 1.. the others in order
     // buffer resources of the head's expanded keys and values and the
     // stream's rotated kR: the buffer form of the direct loads counts its LDS
     // writes on the vector-memory counter alone, so the operand reads keep
@@ -326,7 +379,7 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
         __builtin_amdgcn_make_buffer_rsrc((void*)vb_src, 0, (int)((size_t)p.W * p.T * DH * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t r_rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)rb_src, 0, (int)((size_t)p.W * p.T * DR * 2), 0x00020000);
-    auto tile_of = [&](int pos) { return pos == 0 ? tile_end - 1 : tile_begin + pos - 1; };
+    auto tile_of = [&](int pos) { return pos < n_lim ? tile_end - 1 - pos : tile_begin + pos - n_lim; };
     auto issue = [&](int pos, bf16* kt, bf16* vt, bf16* rt) {
       const int kbase = tile_of(pos) * kBN;
 #pragma unroll
@@ -370,17 +423,22 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
         }
       }
     };
-    auto probs = [&](const sblk& s, v8 (&pb)[kNMB], int kfirst, auto ragged_c) {
-      constexpr bool RAGGED = decltype(ragged_c)::value;
+    // limited body: key kfirst + 4 lg + 16 kb + i is kept when 16 kb + i <
+    // lim, the limit being the row's visible prefix under the frame-causal
+    // mask, else the window's end (the lane offset recomputed here)
+    auto probs = [&](const sblk& s, v8 (&pb)[kNMB], int kfirst, auto limited_c) {
+      constexpr bool LIMITED = decltype(limited_c)::value;
 #pragma unroll
       for (int mb = 0; mb < kNMB; ++mb) {
         float f8[8];
+        int lim = 0;
+        if constexpr (LIMITED) lim = vis_end(mb) - kfirst - 4 * opaque_h(lg);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float e = fast_exp2(s[kb][mb][i]);
-            if constexpr (RAGGED) e = kfirst + kb * 16 + lg * 4 + i < n_keys ? e : 0.f;
+            if constexpr (LIMITED) e = kb * 16 + i < lim ? e : 0.f;
             f8[kb * 4 + i] = e;
             l_run[mb] += e;
           }
@@ -423,7 +481,7 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
       return lds_tr8(vt, F::LSV, half * 32 + lg * 4, half * 32 + 16 + lg * 4, db * 16);
     };
     auto values_ahead = [&](const bf16* vt, int half, const v8 (&pb)[kNMB]) {
-      constexpr int DV = DR > 32 ? 2 : 3;
+      constexpr int DV = DR > 32 ? (CAUSAL ? 1 : 2) : 3;  // (the masked variant's limited body keeps more live)
       v8 va[DV + 1];
 #pragma unroll
       for (int d = 0; d < DV; ++d)
@@ -437,7 +495,7 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    auto step = [&](int pos, auto cur_c, auto ragged_c) {
+    auto step = [&](int pos, auto cur_c, auto limited_c) {
       constexpr int CUR = decltype(cur_c)::value;
       const bf16* kt = CUR == 0 ? k0 : k1;
       const bf16* vt = CUR == 0 ? v0 : v1;
@@ -452,7 +510,7 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
         sblk s;
         scores_ahead(kt, rt, half, s);
         v8 pb[kNMB];
-        probs(s, pb, kbase + half * 32, ragged_c);
+        probs(s, pb, kbase + half * 32, limited_c);
         values_ahead(vt, half, pb);
       }
       __builtin_amdgcn_s_waitcnt(0);  // direct loads of the next tile have landed
@@ -468,28 +526,50 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
       sblk s;
       const f32x4 zs[kNMB] = {};
       scores(k0, r0, 0, s, zs);
+      // (frame-causal: over the visible keys among them, else over all of them)
 #pragma unroll
       for (int mb = 0; mb < kNMB; ++mb) {
-        float mx = -__builtin_inff();
+        float mx = -__builtin_inff(), mx_all = -__builtin_inff();
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (kbase + kb * 16 + lg * 4 + i < n_keys) mx = fmaxf(mx, s[kb][mb][i]);
+          for (int i = 0; i < 4; ++i) {
+            const int key = kbase + kb * 16 + lg * 4 + i;
+            if (key < n_keys) {
+              mx_all = fmaxf(mx_all, s[kb][mb][i]);
+              if (key < vis_end(mb)) mx = fmaxf(mx, s[kb][mb][i]);
+            }
+          }
         mx = wave_max_across_groups(mx);
+        if constexpr (CAUSAL) {
+          mx_all = wave_max_across_groups(mx_all);
+          mx = mx > -__builtin_inff() ? mx : mx_all;
+        }
         negref[mb] = f32x4{-mx, -mx, -mx, -mx};
       }
-      step(0, B0(), std::integral_constant<bool, true>());
-      typedef std::integral_constant<bool, false> Full;
+      step(0, B0(), std::true_type());
       int pos = 1;
-      for (; pos + 1 < n_visit; pos += 2) {
-        step(pos, B1(), Full());
-        step(pos + 1, B0(), Full());
+      if constexpr (CAUSAL) {
+        for (; pos + 1 < n_lim; pos += 2) {
+          step(pos, B1(), std::true_type());
+          step(pos + 1, B0(), std::true_type());
+        }
+        if (pos < n_lim) step(pos++, B1(), std::true_type());
       }
-      if (pos < n_visit) step(pos, B1(), Full());
+      for (; pos + 1 < n_visit; pos += 2) {
+        step(pos, B1(), std::false_type());
+        step(pos + 1, B0(), std::false_type());
+      }
+      if (pos < n_visit) step(pos, B1(), std::false_type());
     }
 
-    // epilogue: a lane holds four consecutive outputs of one row
+    // epilogue: a lane holds four consecutive outputs of one row. A row that
+    // sees keys of this segment but whose sum left [2^-100, 2^100] (its
+    // reference came from keys it cannot see, or its scores spread beyond
+    // the bound) goes to the exact fallback.
+    bool sees[kNMB];
+#pragma unroll
+    for (int mb = 0; mb < kNMB; ++mb) sees[mb] = n_visit > 0 && tile_begin * kBN < vis_end(mb);
     const int eln = opaque_h(lane);
     const int eli = eln & 15, elg = eln >> 4;
 #pragma unroll
@@ -497,7 +577,7 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
       const float l = wave_sum_across_groups(l_run[mb]);
       const int tok = tok_wave + mb * 16 + eli;
       if (tok >= p.Nq) continue;
-      const bool ok = l <= kHeadsSumLimit;  // false for inf / NaN as well
+      const bool ok = l <= kHeadsSumLimit && (l >= kHeadsSumMin || !sees[mb]);  // false for inf / NaN
       const float inv = (ok && l > 0.f) ? 1.f / l : 0.f;
       if (whole) {
         bf16* dst = (bf16*)p.out + (((size_t)b * p.Nq + tok) * p.H + h) * DH;
@@ -514,9 +594,12 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
         for (int db = 0; db < F::NDB; ++db)
           store4_bf16(dst + db * 16 + elg * 4, o[db][mb][0] * inv, o[db][mb][1] * inv, o[db][mb][2] * inv,
                       o[db][mb][3] * inv);
+        // log2 of the piece's weight (reference + log2 of the sum; -inf for a
+        // piece without keys the row sees) and its status (+inf: exact fallback)
         if (elg == 0) {
-          p.part_l[prow * 2] = n_visit == 0 ? -__builtin_inff() : -negref[mb][0];
-          p.part_l[prow * 2 + 1] = l;
+          const bool weighted = ok && l > 0.f;
+          p.part_l[prow * 2] = weighted ? -negref[mb][0] + __builtin_amdgcn_logf(l) : -__builtin_inff();
+          p.part_l[prow * 2 + 1] = ok ? 0.f : __builtin_inff();
         }
       }
     }
@@ -524,9 +607,11 @@ __global__ __launch_bounds__(512, 1) void heads_flash_kernel(HeadsParams p) {
 }
 
 // Merge of the partial results of a row block shared by work-groups g0..g1
-// (the work-groups whose unit ranges meet the row block's units): with
-// M = max_g r_g and w_g = 2^(r_g - M) l_g, out = sum_g w_g (o_g / l_g) / sum_g w_g.
-// A work-group takes 32 rows of one row block.
+// (the work-groups whose unit ranges meet the row block's units [a, a + nt)):
+// piece g holds o_g / l_g and lw_g = r_g + log2 l_g; with M = max_g lw_g and
+// w_g = 2^(lw_g - M), out = sum_g w_g (o_g / l_g) / sum_g w_g. Pieces with
+// no key the row sees have lw_g = -inf and weigh 0; a flagged piece sends
+// the row to the exact fallback. A work-group takes 32 rows of one row block.
 constexpr int kHeadsMergeRows = 32;
 
 template <int DH>
@@ -537,11 +622,13 @@ __global__ __launch_bounds__(256) void heads_combine_kernel(HeadsParams p) {
   // row blocks from rb_whole on (the ones dealt whole in rounds are done)
   const long long rbg = p.rb_whole + blockIdx.x / (RB / kHeadsMergeRows);
   const int row_lo = (int)(blockIdx.x % (RB / kHeadsMergeRows)) * kHeadsMergeRows;
-  const long long a = rbg * p.nt_max;
+  long long a;
+  int nt;
+  row_block_units(p.classes, p.n_rb, rbg, a, nt);
   const long long Gr = p.grid_rest, rest = p.units - p.u_rest;
   // largest g whose range of the remaining units starts at or before unit x
   auto owner = [&](long long x) { return ((x - p.u_rest + 1) * Gr - 1) / rest; };
-  const long long g0 = owner(a), g1 = owner(a + p.nt_max - 1);
+  const long long g0 = owner(a), g1 = owner(a + nt - 1);
   if (g0 == g1) return;  // one work-group covered the row block and wrote it
   const int np = (int)(g1 - g0 + 1);  // <= kMaxMergePieces by the host's cap on G'
   if ((int)threadIdx.x < np) {
@@ -566,7 +653,7 @@ __global__ __launch_bounds__(256) void heads_combine_kernel(HeadsParams p) {
     if (M > -__builtin_inff()) {
       for (int k = 0; k < np; ++k) {
         const size_t pr = (size_t)slot_base[k] + local;
-        const float wl = fast_exp2(p.part_l[pr * 2] - M) * p.part_l[pr * 2 + 1];
+        const float wl = fast_exp2(p.part_l[pr * 2] - M);
         L += wl;
         float v[8];
         unpack8<bf16>(load8<bf16>((const bf16*)p.part_o + pr * DH + c0), v);
@@ -586,13 +673,14 @@ __global__ __launch_bounds__(256) void heads_combine_kernel(HeadsParams p) {
 // Rows listed by the attention kernel, recomputed with the textbook two-pass
 // softmax over the expanded keys and values. One work-group per listed row
 // (grid-stride over the list).
-template <int DH, int DR>
+template <int DH, int DR, bool CAUSAL>
 __global__ __launch_bounds__(256) void heads_exact_kernel(HeadsParams p) {
   constexpr int QP = DH + DR, CHUNK = 256;
   __shared__ float q[QP];
   __shared__ float pr[CHUNK];
   __shared__ float red[256];
   __shared__ int n_valid_sh;
+  __shared__ int frame_of[kSlots];
   const int tid = threadIdx.x;
   const int count = *p.fallback_count;
   for (int idx = blockIdx.x; idx < count; idx += gridDim.x) {
@@ -601,12 +689,17 @@ __global__ __launch_bounds__(256) void heads_exact_kernel(HeadsParams p) {
     __syncthreads();
     if (tid < 64) {
       const int f = tid < p.W ? p.slot_frame[b * p.W + tid] : -1;
+      const int rank = window_rank(f, tid);
+      if (f >= 0) frame_of[rank] = f;
       const unsigned long long mask = __ballot(f >= 0);
       if (tid == 0) n_valid_sh = __popcll(mask);
     }
     for (int d = tid; d < QP; d += 256) q[d] = to_f<bf16>(((const bf16*)p.q_cat)[(size_t)row * QP + d]);
     __syncthreads();
     const int n_keys = n_valid_sh * p.T;
+    // frame-causal variant: keys of frames after the row's query frame are skipped
+    const int qframe = p.q_frame_first + i / p.T;
+    auto visible = [&](int v) { return !CAUSAL || frame_of[v / p.T] <= qframe; };
     const size_t head_rows = (size_t)bh * p.W * p.T;
     const bf16* kx = (const bf16*)p.k_exp + head_rows * DH;
     const bf16* vx = (const bf16*)p.v_exp + head_rows * DH;
@@ -618,7 +711,8 @@ __global__ __launch_bounds__(256) void heads_exact_kernel(HeadsParams p) {
       return s;
     };
     float mx = -__builtin_inff();
-    for (int v = tid; v < n_keys; v += 256) mx = fmaxf(mx, score(v));
+    for (int v = tid; v < n_keys; v += 256)
+      if (visible(v)) mx = fmaxf(mx, score(v));
     red[tid] = mx;
     __syncthreads();
     for (int s = 128; s > 0; s >>= 1) {
@@ -630,7 +724,7 @@ __global__ __launch_bounds__(256) void heads_exact_kernel(HeadsParams p) {
     float acc = 0.f, lsum = 0.f;
     for (int j0 = 0; j0 < n_keys; j0 += CHUNK) {
       const int v = j0 + tid;
-      pr[tid] = v < n_keys ? fast_exp2(score(v) - m) : 0.f;  // scores are log2-scaled
+      pr[tid] = v < n_keys && visible(v) ? fast_exp2(score(v) - m) : 0.f;  // scores are log2-scaled
       __syncthreads();
       if (tid < DH) {
         const int nv = min(CHUNK, n_keys - j0);
@@ -646,7 +740,7 @@ __global__ __launch_bounds__(256) void heads_exact_kernel(HeadsParams p) {
   }
 }
 
-template <int DC, int DR, int DH>
+template <int DC, int DR, int DH, bool CAUSAL>
 static hipError_t launch_heads_t(const HeadsParams& p, bool split, hipStream_t s) {
   typedef HeadsTile<DH, DR> F;
   const int nk_max = p.W * p.T;
@@ -657,7 +751,7 @@ static hipError_t launch_heads_t(const HeadsParams& p, bool split, hipStream_t s
   const long long pieces = (long long)p.batch * p.Nq * p.H * ((DH + DR) / 8);
   hipLaunchKernelGGL((heads_qcat_kernel<DH, DR>), dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL((heads_flash_kernel<DH, DR>), dim3(p.grid), dim3(F::kThreads), 0, s, p);
+  hipLaunchKernelGGL((heads_flash_kernel<DH, DR, CAUSAL>), dim3(p.grid), dim3(F::kThreads), 0, s, p);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (split && (long long)p.batch * p.H * p.n_rb > p.rb_whole) {
     hipLaunchKernelGGL((heads_combine_kernel<DH>),
@@ -665,7 +759,7 @@ static hipError_t launch_heads_t(const HeadsParams& p, bool split, hipStream_t s
                        dim3(256), 0, s, p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  hipLaunchKernelGGL((heads_exact_kernel<DH, DR>), dim3(kFallbackBlocks), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((heads_exact_kernel<DH, DR, CAUSAL>), dim3(kFallbackBlocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -682,13 +776,19 @@ int heads_tile_keys(int d_head, int d_rope) {
   return 0;
 }
 
-hipError_t launch_heads(int d_c, int d_rope, int d_head, const HeadsParams& p, bool split, hipStream_t s) {
+template <int DC, int DR>
+static hipError_t launch_heads_c(const HeadsParams& p, bool split, bool causal, hipStream_t s) {
+  return causal ? launch_heads_t<DC, DR, 128, true>(p, split, s) : launch_heads_t<DC, DR, 128, false>(p, split, s);
+}
+
+hipError_t launch_heads(int d_c, int d_rope, int d_head, const HeadsParams& p, bool split, bool causal,
+                        hipStream_t s) {
   if (p.batch <= 0 || p.Nq <= 0 || p.grid <= 0) return hipSuccess;
   if (d_head != 128) return hipErrorInvalidValue;
-  if (d_c == 192 && d_rope == 32) return launch_heads_t<192, 32, 128>(p, split, s);
-  if (d_c == 128 && d_rope == 32) return launch_heads_t<128, 32, 128>(p, split, s);
-  if (d_c == 160 && d_rope == 64) return launch_heads_t<160, 64, 128>(p, split, s);
-  if (d_c == 192 && d_rope == 64) return launch_heads_t<192, 64, 128>(p, split, s);
+  if (d_c == 192 && d_rope == 32) return launch_heads_c<192, 32>(p, split, causal, s);
+  if (d_c == 128 && d_rope == 32) return launch_heads_c<128, 32>(p, split, causal, s);
+  if (d_c == 160 && d_rope == 64) return launch_heads_c<160, 64>(p, split, causal, s);
+  if (d_c == 192 && d_rope == 64) return launch_heads_c<192, 64>(p, split, causal, s);
   return hipErrorInvalidValue;
 }
 

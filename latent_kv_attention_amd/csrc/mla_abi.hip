@@ -106,9 +106,11 @@ int device_cus() {
 // (row block, key tile) pairs evenly. kv_splits = s > 0 gives every row
 // block s equal key ranges (s = 1: one work-group per row block);
 // kv_splits = 0 uses one work-group per compute unit, and where there are
-// at least as many row blocks as work-groups (several streams) and all row
-// blocks have the same units, deals the first whole multiple of `grid` row
-// blocks out whole, in rounds, and shares the rest.
+// at least as many row blocks as work-groups (several streams) deals the
+// first whole multiple of `grid` row blocks out whole, in rounds, and shares
+// the units after them. (Under the frame-causal mask the row blocks of a
+// round differ in units by the window frames their rows may not see, at
+// most the chunk's length in frames.)
 struct FlashPlan {
   int n_rb, nt_max;
   int64_t units;
@@ -170,8 +172,11 @@ FlashPlan flash_plan(const mla_shape* s, int q_n_frames, int kv_splits, bool cau
   if (g > (INT64_C(1) << 23)) g = INT64_C(1) << 23;  // rejected by flash_plan_ok
   f.grid = (int)g;
   f.rb_whole = 0;
-  if (kv_splits == 0 && c.n == 1 && row_blocks >= g) f.rb_whole = row_blocks / g * g;
-  f.u_rest = f.rb_whole * f.nt_max;
+  if (kv_splits == 0 && row_blocks >= g) f.rb_whole = row_blocks / g * g;
+  long long u_rest;
+  int nt_unused;
+  mla::row_block_units(c, f.n_rb, f.rb_whole, u_rest, nt_unused);  // (rb_whole = all row blocks: U)
+  f.u_rest = u_rest;
   const int64_t rest = f.units - f.u_rest;
   // the rest: at most kMaxMergePieces - 1 work-groups per remaining row block
   int64_t gr = g;
@@ -312,15 +317,47 @@ mla_status check_query_args(const mla_shape* s, int q_frame_first, int q_n_frame
 
 // Work split of the per-head attention kernel: (row block of 384 tokens of
 // one (stream, head), key tile) units shared evenly by one work-group per
-// compute unit, as for the latent form.
-FlashPlan heads_plan(const mla_shape* s, int q_n_frames) {
+// compute unit, as for the latent form (whole row blocks in rounds where
+// there are enough of them). Under the frame-causal mask the row blocks of a
+// (stream, head) form classes by the chunk frame of their last token, each
+// with the units of the window part its tokens may see.
+FlashPlan heads_plan(const mla_shape* s, int q_n_frames, bool causal = false) {
   FlashPlan f;
-  const int64_t nq = (int64_t)q_n_frames * tokens_per_frame(s);
+  const int64_t T = tokens_per_frame(s);
+  const int64_t nq = (int64_t)q_n_frames * T;
   const int tk = mla::heads_tile_keys(s->d_head, s->d_rope);
-  f.n_rb = (int)((nq + mla::kHeadsRowsPerBlock - 1) / mla::kHeadsRowsPerBlock);
-  f.nt_max = (int)((s->window_frames * tokens_per_frame(s) + tk - 1) / tk);
-  const int64_t row_blocks = (int64_t)s->batch * s->n_heads * f.n_rb;
-  f.units = row_blocks * f.nt_max;
+  const int rpb = mla::kHeadsRowsPerBlock;
+  f.n_rb = (int)((nq + rpb - 1) / rpb);
+  f.nt_max = (int)((s->window_frames * T + tk - 1) / tk);
+  mla::UnitClasses& c = f.classes;
+  c = mla::UnitClasses{};
+  if (causal && q_n_frames <= mla::kMaxUnitClasses) {
+    int64_t u = 0;
+    c.n = 0;
+    for (int k = 0; k < q_n_frames; ++k) {
+      // row blocks whose last token lies in chunk frame k
+      const int64_t end = k + 1 < q_n_frames ? ((k + 1) * T) / rpb : f.n_rb;
+      const int64_t start = c.n == 0 ? 0 : c.rb_end[c.n - 1];
+      if (end <= start) continue;
+      const int64_t frames = (int64_t)s->window_frames - (q_n_frames - 1 - k);
+      const int nt = (int)(frames < 1 ? 1 : (frames * T + tk - 1) / tk);
+      c.rb_end[c.n] = (int)end;
+      c.nt[c.n] = nt;
+      c.u0[c.n] = u;
+      u += (end - start) * nt;
+      ++c.n;
+    }
+    c.per_stream = u;
+  } else {
+    c.n = 1;
+    c.rb_end[0] = f.n_rb;
+    c.nt[0] = f.nt_max;
+    c.u0[0] = 0;
+    c.per_stream = (int64_t)f.n_rb * f.nt_max;
+  }
+  const int64_t pairs = (int64_t)s->batch * s->n_heads;
+  const int64_t row_blocks = pairs * f.n_rb;
+  f.units = pairs * c.per_stream;
   int64_t g = device_cus();
   if (g > f.units) g = f.units;
   if (g > (mla::kMaxMergePieces - 1) * row_blocks) g = (mla::kMaxMergePieces - 1) * row_blocks;
@@ -328,7 +365,10 @@ FlashPlan heads_plan(const mla_shape* s, int q_n_frames) {
   f.grid = (int)g;
   // whole row blocks in rounds where there are enough of them, the rest shared
   f.rb_whole = row_blocks >= g ? row_blocks / g * g : 0;
-  f.u_rest = f.rb_whole * f.nt_max;
+  long long u_rest;
+  int nt_unused;
+  mla::row_block_units(c, f.n_rb, f.rb_whole, u_rest, nt_unused);  // (rb_whole = all row blocks: U)
+  f.u_rest = u_rest;
   const int64_t rest = f.units - f.u_rest;
   int64_t gr = g;
   if (f.rb_whole > 0) {
@@ -337,7 +377,7 @@ FlashPlan heads_plan(const mla_shape* s, int q_n_frames) {
     if (gr > rest) gr = rest;
   }
   f.grid_rest = (int)gr;
-  f.split = rest > 0 && !(rest % gr == 0 && (rest / gr) % f.nt_max == 0);
+  f.split = c.n > 1 || (rest > 0 && !(rest % gr == 0 && (rest / gr) % f.nt_max == 0));
   return f;
 }
 
@@ -360,8 +400,14 @@ HeadsWs heads_ws_layout(const mla_shape* s, int q_n_frames) {
   w.v_exp = w.k_exp + round256((size_t)s->batch * s->n_heads * nk * s->d_head * e);
   w.q_cat = w.v_exp + round256((size_t)s->batch * s->n_heads * nk * s->d_head * e);
   w.part_o = w.q_cat + round256((size_t)s->batch * s->n_heads * nq * (s->d_head + s->d_rope) * e);
-  const FlashPlan f = heads_plan(s, q_n_frames);
-  const size_t slots = f.split ? (size_t)f.grid * 2 * mla::kHeadsRowsPerBlock : 0;
+  // partial slots for either mask (the frame-causal plan may split row
+  // blocks where the plain one does not)
+  size_t slots = 0;
+  for (const bool causal : {false, true}) {
+    const FlashPlan f = heads_plan(s, q_n_frames, causal);
+    const size_t n = f.split ? (size_t)f.grid * 2 * mla::kHeadsRowsPerBlock : 0;
+    slots = n > slots ? n : slots;
+  }
   w.part_l = w.part_o + round256(slots * s->d_head * e);
   w.total = w.part_l + round256(slots * 2 * sizeof(float));
   return w;
@@ -669,7 +715,8 @@ static mla_status chunk_attend_heads_impl(const mla_shape* shape, const void* q_
                                           int32_t q_frame_first, int32_t q_n_frames, const void* w_uk,
                                           const void* w_uv, const void* cache, const int32_t* slot_frame,
                                           const float* rope_tables, int32_t rope_t_first, int32_t rope_n_t, void* out,
-                                          void* workspace, size_t workspace_bytes, void* stream, bool run);
+                                          void* workspace, size_t workspace_bytes, void* stream, bool run,
+                                          bool frame_causal);
 
 MLA_API mla_status mla_chunk_attend(const mla_shape* shape, const void* q_nope, const void* q_r, int32_t q_frame_first,
                                     int32_t q_n_frames, const void* w_uk, const void* w_uv, const void* cache,
@@ -681,7 +728,8 @@ MLA_API mla_status mla_chunk_attend(const mla_shape* shape, const void* q_nope, 
   if ((st = check_query_args(shape, q_frame_first, q_n_frames)) != MLA_OK) return st;
   if (heads_preferred(shape, q_n_frames))
     return chunk_attend_heads_impl(shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk, w_uv, cache, slot_frame,
-                                   rope_tables, rope_t_first, rope_n_t, out, workspace, workspace_bytes, stream, true);
+                                   rope_tables, rope_t_first, rope_n_t, out, workspace, workspace_bytes, stream, true,
+                                   false);
   return chunk_attend_impl(shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk, w_uv, cache, slot_frame, rope_tables,
                            rope_t_first, rope_n_t, out, workspace, workspace_bytes, stream, false);
 }
@@ -700,6 +748,23 @@ MLA_API mla_status mla_chunk_attend_frame_causal(const mla_shape* shape, const v
                                                  const void* w_uv, const void* cache, const int32_t* slot_frame,
                                                  const float* rope_tables, int32_t rope_t_first, int32_t rope_n_t,
                                                  void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status st = check_shape(shape);
+  if (st != MLA_OK) return st;
+  if ((st = check_query_args(shape, q_frame_first, q_n_frames)) != MLA_OK) return st;
+  if (heads_preferred(shape, q_n_frames))
+    return chunk_attend_heads_impl(shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk, w_uv, cache, slot_frame,
+                                   rope_tables, rope_t_first, rope_n_t, out, workspace, workspace_bytes, stream, true,
+                                   true);
+  return chunk_attend_impl(shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk, w_uv, cache, slot_frame, rope_tables,
+                           rope_t_first, rope_n_t, out, workspace, workspace_bytes, stream, true);
+}
+
+MLA_API mla_status mla_chunk_attend_latent_frame_causal(const mla_shape* shape, const void* q_nope, const void* q_r,
+                                                        int32_t q_frame_first, int32_t q_n_frames, const void* w_uk,
+                                                        const void* w_uv, const void* cache,
+                                                        const int32_t* slot_frame, const float* rope_tables,
+                                                        int32_t rope_t_first, int32_t rope_n_t, void* out,
+                                                        void* workspace, size_t workspace_bytes, void* stream) {
   return chunk_attend_impl(shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk, w_uv, cache, slot_frame, rope_tables,
                            rope_t_first, rope_n_t, out, workspace, workspace_bytes, stream, true);
 }
@@ -720,14 +785,27 @@ MLA_API mla_status mla_chunk_attend_heads(const mla_shape* shape, const void* q_
                                           const float* rope_tables, int32_t rope_t_first, int32_t rope_n_t,
                                           void* out, void* workspace, size_t workspace_bytes, void* stream) {
   return chunk_attend_heads_impl(shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk, w_uv, cache, slot_frame,
-                                 rope_tables, rope_t_first, rope_n_t, out, workspace, workspace_bytes, stream, true);
+                                 rope_tables, rope_t_first, rope_n_t, out, workspace, workspace_bytes, stream, true,
+                                 false);
+}
+
+MLA_API mla_status mla_chunk_attend_heads_frame_causal(const mla_shape* shape, const void* q_nope, const void* q_r,
+                                                       int32_t q_frame_first, int32_t q_n_frames, const void* w_uk,
+                                                       const void* w_uv, const void* cache, const int32_t* slot_frame,
+                                                       const float* rope_tables, int32_t rope_t_first,
+                                                       int32_t rope_n_t, void* out, void* workspace,
+                                                       size_t workspace_bytes, void* stream) {
+  return chunk_attend_heads_impl(shape, q_nope, q_r, q_frame_first, q_n_frames, w_uk, w_uv, cache, slot_frame,
+                                 rope_tables, rope_t_first, rope_n_t, out, workspace, workspace_bytes, stream, true,
+                                 true);
 }
 
 static mla_status chunk_attend_heads_impl(const mla_shape* shape, const void* q_nope, const void* q_r,
                                           int32_t q_frame_first, int32_t q_n_frames, const void* w_uk,
                                           const void* w_uv, const void* cache, const int32_t* slot_frame,
                                           const float* rope_tables, int32_t rope_t_first, int32_t rope_n_t, void* out,
-                                          void* workspace, size_t workspace_bytes, void* stream, bool run) {
+                                          void* workspace, size_t workspace_bytes, void* stream, bool run,
+                                          bool frame_causal) {
   mla_status st = check_shape(shape);
   if (st != MLA_OK) return st;
   if (!mla::heads_supported(shape->dtype == MLA_BF16 ? 0 : 1, shape->d_c, shape->d_rope, shape->d_head))
@@ -740,7 +818,7 @@ static mla_status chunk_attend_heads_impl(const mla_shape* shape, const void* q_
   if ((st = check_query_args(shape, q_frame_first, q_n_frames)) != MLA_OK) return st;
   if (q_frame_first < rope_t_first || (int64_t)q_frame_first + q_n_frames > (int64_t)rope_t_first + rope_n_t)
     return MLA_ERR_RANGE;
-  const FlashPlan f = heads_plan(shape, q_n_frames);
+  const FlashPlan f = heads_plan(shape, q_n_frames, frame_causal);
   if (!flash_plan_ok(f)) return MLA_ERR_SHAPE;
   const HeadsWs w = heads_ws_layout(shape, q_n_frames);
   if (workspace_bytes < w.total) return MLA_ERR_WORKSPACE;
@@ -793,12 +871,13 @@ static mla_status chunk_attend_heads_impl(const mla_shape* shape, const void* q_
   p.n_rb = f.n_rb;
   p.nt_max = f.nt_max;
   p.units = f.units;
+  p.classes = f.classes;
   p.grid = f.grid;
   p.rb_whole = f.rb_whole;
   p.u_rest = f.u_rest;
   p.grid_rest = f.grid_rest;
   p.qscale = scale_log2(shape);
-  return from_hip(mla::launch_heads(shape->d_c, shape->d_rope, shape->d_head, p, f.split, s));
+  return from_hip(mla::launch_heads(shape->d_c, shape->d_rope, shape->d_head, p, f.split, frame_causal, s));
 }
 
 
@@ -1067,9 +1146,9 @@ MLA_API mla_status mla_layer_step(const mla_shape* shape, int32_t d_cq, const ml
   void *c_q = ws + w.c_q, *q_nope = ws + w.q_nope, *q_r = ws + w.q_r, *o = ws + w.o;
   const bool causal = frame_causal != 0;
   const mla_layer_weights& W = *weights;
-  // the per-head form where mla_chunk_attend would take it (it needs the
-  // per-head queries, so the unfused query path, and has no frame-causal mask)
-  const bool heads = !causal && heads_preferred(shape, n_frames) && W.w_uq && W.w_qr && W.w_uk;
+  // the per-head form where mla_chunk_attend (or its frame-causal variant)
+  // would take it (it needs the per-head queries, so the unfused query path)
+  const bool heads = heads_preferred(shape, n_frames) && W.w_uq && W.w_qr && W.w_uk;
   if (W.w_qabs && !heads) {
     // fused query path: the query latent's product with the absorbed weights
     // is already the attention's query; workspace = [c_q | q_abs | o | o_lat, flash]
@@ -1114,7 +1193,7 @@ MLA_API mla_status mla_layer_step(const mla_shape* shape, int32_t d_cq, const ml
     if (heads) {
       st = chunk_attend_heads_impl(shape, q_nope, q_r, frame_first, n_frames, W.w_uk, W.w_uv, cache, slot_frame,
                                    rope_tables, rope_t_first, rope_n_t, o, ws + w.attend, w.total - w.attend, stream,
-                                   run);
+                                   run, causal);
     } else {
       st = chunk_attend_impl(shape, q_nope, q_r, frame_first, n_frames, W.w_uk, W.w_uv, cache, slot_frame, rope_tables,
                              rope_t_first, rope_n_t, o, ws + w.attend, w.total - w.attend, stream, causal, run);

@@ -154,11 +154,12 @@ struct HeadsParams {
   int* fallback_count;     // rows listed for the exact fallback
   int* fallback_rows;      // [B * H * Nq], as (b * H + h) * Nq + i
   void* part_o;            // [G][2][rows per block][d_head] partial outputs o_g / l_g (split row blocks only)
-  float* part_l;           // [G][2][rows per block][2] (reference, sum)
+  float* part_l;           // [G][2][rows per block][2] (log2 of the piece's weight, status)
   RopeLayout rl;
   int batch, H, Nq, T, W, grid_x, q_frame_first;
   int n_rb, nt_max;        // row blocks of kHeadsRowsPerBlock tokens per (stream, head); key tiles of a full window
-  long long units;         // batch * H * n_rb * nt_max
+  long long units;         // all units: batch * H * classes.per_stream
+  UnitClasses classes;     // per (stream, head): row-block classes and their unit counts
   int grid;                // G, work-groups of the attention kernel
   long long rb_whole;      // row blocks dealt whole in rounds (a multiple of G)
   long long u_rest;        // first unit after them
@@ -235,7 +236,9 @@ hipError_t launch_rope_window(int dtype, int d_c, int d_rope, const FlashParams&
 constexpr int kHeadsRowsPerBlock = 384;
 bool heads_supported(int dtype, int d_c, int d_rope, int d_head);
 int heads_tile_keys(int d_head, int d_rope);  // keys per tile of the per-head attention kernel
-hipError_t launch_heads(int d_c, int d_rope, int d_head, const HeadsParams& p, bool split, hipStream_t s);
+// causal: the frame-causal variant (a query of frame f sees keys of frames <= f)
+hipError_t launch_heads(int d_c, int d_rope, int d_head, const HeadsParams& p, bool split, bool causal,
+                        hipStream_t s);
 // tile of the projection GEMM (128 x 128 or 64 x 64, given by its rows) for
 // a problem of M x N outputs on n_cu compute units
 int gemm_tile_rows(int M, int N, int n_cu);

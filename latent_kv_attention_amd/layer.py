@@ -87,37 +87,60 @@ class LatentLayer:
                                  self.workspace, stream)
         return out
 
-    def attend_frame_causal(self, q_nope, q_r, q_frame_first: int, q_n_frames: int, out=None, stream=None):
-        """attend() with the frame-causal mask inside the chunk (a query of frame
-        f sees keys of frames <= f)."""
+    def _out(self, q_n_frames: int, out):
         if q_n_frames > self.max_chunk_frames:
             raise ValueError("chunk larger than the workspace was sized for")
         if out is None:
             out = torch.empty(self.B, q_n_frames * self.T, self.cfg.n_heads, self.cfg.d_head, dtype=self.dtype,
                               device=self.device)
+        return out
+
+    def _heads_ws(self):
+        if self.heads_workspace is None:
+            n = _lib.chunk_attend_heads_workspace_bytes(self.shape, self.max_chunk_frames)
+            if n == 0:
+                raise ValueError("the per-head form does not support this shape")
+            self.heads_workspace = torch.empty(n, dtype=torch.uint8, device=self.device)
+        return self.heads_workspace
+
+    def attend_frame_causal(self, q_nope, q_r, q_frame_first: int, q_n_frames: int, out=None, stream=None):
+        """attend() with the frame-causal mask inside the chunk (a query of frame
+        f sees keys of frames <= f); the form as attend() takes it."""
+        out = self._out(q_n_frames, out)
         self.ensure_tables(q_frame_first, q_n_frames, stream)
         _lib.chunk_attend_frame_causal(self.shape, q_nope, q_r, q_frame_first, q_n_frames, self.w["w_uk"],
                                        self.w["w_uv"], self.cache, self.slot_frame, self.tables, self.rope_t_first,
                                        self.rope_n_t, out, self.workspace, stream)
         return out
 
+    def attend_latent_frame_causal(self, q_nope, q_r, q_frame_first: int, q_n_frames: int, out=None, stream=None):
+        """attend_frame_causal() by the latent form whatever the shape."""
+        out = self._out(q_n_frames, out)
+        self.ensure_tables(q_frame_first, q_n_frames, stream)
+        _lib.chunk_attend_latent_frame_causal(self.shape, q_nope, q_r, q_frame_first, q_n_frames, self.w["w_uk"],
+                                              self.w["w_uv"], self.cache, self.slot_frame, self.tables,
+                                              self.rope_t_first, self.rope_n_t, out, self.workspace, stream)
+        return out
+
     def attend_heads(self, q_nope, q_r, q_frame_first: int, q_n_frames: int, out=None, stream=None):
         """Same as attend(), by the per-head form (keys and values of every head
         expanded for the window, then per-head attention)."""
-        if q_n_frames > self.max_chunk_frames:
-            raise ValueError("chunk larger than the workspace was sized for")
-        if self.heads_workspace is None:
-            n = _lib.chunk_attend_heads_workspace_bytes(self.shape, self.max_chunk_frames)
-            if n == 0:
-                raise ValueError("the per-head form does not support this shape")
-            self.heads_workspace = torch.empty(n, dtype=torch.uint8, device=self.device)
-        if out is None:
-            out = torch.empty(self.B, q_n_frames * self.T, self.cfg.n_heads, self.cfg.d_head, dtype=self.dtype,
-                              device=self.device)
+        out = self._out(q_n_frames, out)
+        ws = self._heads_ws()
         self.ensure_tables(q_frame_first, q_n_frames, stream)
         _lib.chunk_attend_heads(self.shape, q_nope, q_r, q_frame_first, q_n_frames, self.w["w_uk"], self.w["w_uv"],
                                 self.cache, self.slot_frame, self.tables, self.rope_t_first, self.rope_n_t, out,
-                                self.heads_workspace, stream)
+                                ws, stream)
+        return out
+
+    def attend_heads_frame_causal(self, q_nope, q_r, q_frame_first: int, q_n_frames: int, out=None, stream=None):
+        """attend_frame_causal() by the per-head form."""
+        out = self._out(q_n_frames, out)
+        ws = self._heads_ws()
+        self.ensure_tables(q_frame_first, q_n_frames, stream)
+        _lib.chunk_attend_heads_frame_causal(self.shape, q_nope, q_r, q_frame_first, q_n_frames, self.w["w_uk"],
+                                             self.w["w_uv"], self.cache, self.slot_frame, self.tables,
+                                             self.rope_t_first, self.rope_n_t, out, ws, stream)
         return out
 
     def project_queries(self, x, n_frames: int, stream=None):

@@ -105,7 +105,7 @@ class LatentMemo:
         return self.memo[f]
 
 
-def oracle_rows_memo(cfg, w, memo: LatentMemo, window_frames, q_nope, q_r, q_frame_first, rows):
+def oracle_rows_memo(cfg, w, memo: LatentMemo, window_frames, q_nope, q_r, q_frame_first, rows, frame_causal=False):
     """oracle_step_rows with the window's latents taken from a LatentMemo."""
     window_frames = list(window_frames)
     c = np.concatenate([memo.get(f)[0] for f in window_frames])
@@ -116,7 +116,9 @@ def oracle_rows_memo(cfg, w, memo: LatentMemo, window_frames, q_nope, q_r, q_fra
     nq = q_nope.shape[0]
     tq, yq, xq = O.frame_positions(q_frame_first + np.arange(nq // cfg.tokens_per_frame), cfg.grid_y, cfg.grid_x)
     q_rope = O.rope3d(q_r[rows], tq[rows], yq[rows], xq[rows], cfg.rope_split, cfg.rope_base)
-    return O.attend(q_nope[rows], q_rope, k_nope, k_rope, v, O.default_scale(cfg.d_head, cfg.d_rope))
+    visible = O.frame_causal_mask(tq[rows], t) if frame_causal else None
+    return O.attend(q_nope[rows], q_rope, k_nope, k_rope, v, O.default_scale(cfg.d_head, cfg.d_rope),
+                    visible=visible)
 
 
 def sample_rows(cfg, n, seed):

@@ -14,7 +14,7 @@ hipError_t launch_up_v(int, int, int, const UpVParams&, hipStream_t) { return hi
 hipError_t launch_rope_window(int, int, int, const FlashParams&, hipStream_t) { return hipErrorInvalidValue; }
 bool heads_supported(int dtype, int, int, int d_head) { return dtype == 0 && d_head == 128; }
 int heads_tile_keys(int, int d_rope) { return d_rope > 32 ? 64 : 128; }
-hipError_t launch_heads(int, int, int, const HeadsParams&, bool, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_heads(int, int, int, const HeadsParams&, bool, bool, hipStream_t) { return hipErrorInvalidValue; }
 int gemm_tile_rows(int, int, int) { return 64; }
 hipError_t launch_gemm_nt(int, const GemmParams&, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_gemm_qabs(int, const GemmParams&, int, hipStream_t) { return hipErrorInvalidValue; }

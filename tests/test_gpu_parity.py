@@ -400,8 +400,10 @@ def test_up_v(name):
 
 # ------------------------------------------------------------------ the whole step
 
-def _full_step(cfg, seed=0, q_scale=1.0, B=1, fill=None):
-    """Prefill the window, write the chunk, attend; returns (gpu, oracle) per stream."""
+def _full_step(cfg, seed=0, q_scale=1.0, B=1, fill=None, attend="attend", frame_causal=False):
+    """Prefill the window, write the chunk, attend (the layer method named;
+    frame_causal for the oracle when it applies the mask); returns (gpu,
+    oracle) per stream."""
     w, wd = device_weights(cfg, seed)
     W, T = cfg.window_frames, cfg.tokens_per_frame
     fill = W if fill is None else fill
@@ -417,15 +419,15 @@ def _full_step(cfg, seed=0, q_scale=1.0, B=1, fill=None):
     xc = np.stack([s_.xs(chunk_first, cfg.chunk_frames) for s_ in streams])
     layer.write(to_torch(xc, cfg.dtype), chunk_first, cfg.chunk_frames)
     qs = [s_.q(chunk_first, q_scale=q_scale) for s_ in streams]
-    out = layer.attend(to_torch(np.stack([q[0] for q in qs]), cfg.dtype),
-                       to_torch(np.stack([q[1] for q in qs]), cfg.dtype), chunk_first, cfg.chunk_frames)
+    out = getattr(layer, attend)(to_torch(np.stack([q[0] for q in qs]), cfg.dtype),
+                                 to_torch(np.stack([q[1] for q in qs]), cfg.dtype), chunk_first, cfg.chunk_frames)
     _sync()
     got = to_numpy(out)
     refs = []
     for b, s_ in enumerate(streams):
         frames = list(range(max(0, fill - W), fill))
         xs = {f: s_.x(f) for f in frames}
-        refs.append(oracle_step_rows(cfg, w, xs, frames, qs[b][0], qs[b][1], chunk_first))
+        refs.append(oracle_step_rows(cfg, w, xs, frames, qs[b][0], qs[b][1], chunk_first, frame_causal=frame_causal))
     return got, np.stack(refs)
 
 
@@ -487,6 +489,19 @@ def test_full_step_many_streams_whole_row_blocks():
     print(f"[parity] 40 streams, {40 * 7} row blocks", flush=True)
     for b in range(40):
         assert_step_close(got[b], ref[b], cfg.dtype, label=f"wan_small stream {b} of 40")
+
+
+def test_frame_causal_many_streams_whole_row_blocks():
+    """The same 40 streams under the frame-causal mask (latent form): the 7
+    row blocks of a stream fall into two classes (3 ending in the chunk's
+    first frame, which visit 4 of the 5 window frames, and 4 ending in its
+    second), the first 256 of the 280 row blocks go out whole in a round
+    (work-groups holding row blocks of either class) and the units after
+    them are shared. Every element of every stream against the oracle."""
+    cfg = get_config("wan_small")
+    got, ref = _full_step(cfg, seed=14, B=40, attend="attend_latent_frame_causal", frame_causal=True)
+    for b in range(40):
+        assert_step_close(got[b], ref[b], cfg.dtype, label=f"wan_small frame-causal stream {b} of 40")
 
 
 def _causal_step(cfg, seed, prefill_frames, chunk_first):
@@ -572,31 +587,38 @@ def test_wan_full_size_every_row():
     4680 x 12 x 128 outputs against the oracle's explicit per-head
     reconstruction, through the latent form (the attention call the
     benchmark times), through mla_chunk_attend (which takes the per-head
-    form at this shape), and under the frame-causal mask."""
+    form at this shape), and under the frame-causal mask through
+    mla_chunk_attend_frame_causal (the per-head form here too) and the
+    latent form's frame-causal call."""
     cfg, w, layer, st, chunk_first, qn, qr, window = _wan_chunk(21, seed=0)
     assert mla.chunk_attend_form(layer.shape, 3) == mla.FORM_HEADS
     q = (to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype), chunk_first, 3)
-    outs = {"latent": layer.attend_latent(*q), "selected": layer.attend(*q), "frame-causal": layer.attend_frame_causal(*q)}
+    outs = {"latent": layer.attend_latent(*q), "selected": layer.attend(*q),
+            "frame-causal selected": layer.attend_frame_causal(*q),
+            "frame-causal latent": layer.attend_latent_frame_causal(*q)}
     _sync()
     xs = {f: st.x(f) for f in window}
     ref = oracle_step_rows(cfg, w, xs, window, qn, qr, chunk_first)
     for k in ("latent", "selected"):
         assert_step_close(to_numpy(outs[k])[0], ref, cfg.dtype, label=f"wan full size, every row, {k}")
     ref = oracle_step_rows(cfg, w, xs, window, qn, qr, chunk_first, frame_causal=True)
-    assert_step_close(to_numpy(outs["frame-causal"])[0], ref, cfg.dtype, label="wan full size, every row, frame-causal")
+    for k in ("frame-causal selected", "frame-causal latent"):
+        assert_step_close(to_numpy(outs[k])[0], ref, cfg.dtype, label=f"wan full size, every row, {k}")
 
 
 def test_wan_full_size_frame_causal_wrapped_ring():
     """Frame-causal chunk at the Wan shape after the ring wrapped: frames
     0..38 written, so the window holds frames 18..38 with the chunk (36..38) in
-    slots 15..17 and slot order no longer frame order. Every output against
-    the oracle."""
+    slots 15..17 and slot order no longer frame order. Every output of both
+    forms against the oracle."""
     cfg, w, layer, st, chunk_first, qn, qr, window = _wan_chunk(39, seed=7)
     assert sorted(layer.slot_frame.cpu().numpy()[0].tolist()) == window
-    out = layer.attend_frame_causal(to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype), chunk_first, 3)
+    q = (to_torch(qn[None], cfg.dtype), to_torch(qr[None], cfg.dtype), chunk_first, 3)
+    outs = {"per-head": layer.attend_heads_frame_causal(*q), "latent": layer.attend_latent_frame_causal(*q)}
     _sync()
     ref = oracle_step_rows(cfg, w, {f: st.x(f) for f in window}, window, qn, qr, chunk_first, frame_causal=True)
-    assert_step_close(to_numpy(out)[0], ref, cfg.dtype, label="wan full size frame-causal wrapped ring")
+    for k, o in outs.items():
+        assert_step_close(to_numpy(o)[0], ref, cfg.dtype, label=f"wan full size frame-causal wrapped ring, {k}")
 
 
 def test_denoising_rewrites_of_the_chunk():
@@ -736,19 +758,23 @@ def test_wan_batch8_streams_full_windows():
     qn = to_torch(np.stack([q[0] for q in qs]), cfg.dtype)
     qr = to_torch(np.stack([q[1] for q in qs]), cfg.dtype)
     # the latent form (1536 row blocks dealt whole in six rounds, the other 224
-    # shared) and the form the selecting call takes at this shape
-    got = {"latent": to_numpy(layer.attend_latent(qn, qr, 18, 3))}
-    _sync()
-    got["selected"] = to_numpy(layer.attend(qn, qr, 18, 3))
-    _sync()
+    # shared) and the form the selecting call takes at this shape, both also
+    # under the frame-causal mask (row blocks of three classes in the rounds)
+    calls = {"latent": layer.attend_latent, "selected": layer.attend,
+             "latent frame-causal": layer.attend_latent_frame_causal, "selected frame-causal": layer.attend_frame_causal}
+    got = {}
+    for form, fn in calls.items():
+        got[form] = to_numpy(fn(qn, qr, 18, 3))
+        _sync()
     sf = layer.slot_frame.cpu().numpy()
     assert (sf == np.arange(21)[None, :]).all()
     for b in range(B):
         rows = sample_rows(cfg, 16, seed=b)
         memo = LatentMemo(cfg, w, streams[b])
-        ref = oracle_rows_memo(cfg, w, memo, range(21), qs[b][0], qs[b][1], 18, rows)
+        refs = {causal: oracle_rows_memo(cfg, w, memo, range(21), qs[b][0], qs[b][1], 18, rows, frame_causal=causal)
+                for causal in (False, True)}
         for form, g in got.items():
-            assert_step_close(g[b][rows], ref, cfg.dtype, label=f"batch8 stream {b} {form}")
+            assert_step_close(g[b][rows], refs["frame-causal" in form], cfg.dtype, label=f"batch8 stream {b} {form}")
 
 
 def test_wan_rollout_80_chunks_ring_eviction():

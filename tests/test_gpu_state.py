@@ -70,11 +70,12 @@ def test_rollout_snapshot_and_restore_is_bitwise_identical():
           flush=True)
 
 
-@pytest.mark.parametrize("attend", ["attend_latent", "attend_frame_causal", "attend_heads"])
+@pytest.mark.parametrize("attend", ["attend_latent", "attend_latent_frame_causal", "attend_heads",
+                                    "attend_heads_frame_causal"])
 def test_repeated_calls_are_bitwise_identical(attend):
     """The Wan chunk step (its row blocks split between work-groups and
-    merged) repeated on the same inputs gives the same bits, for the latent
-    form, its frame-causal variant and the per-head form."""
+    merged) repeated on the same inputs gives the same bits, for both forms
+    with and without the frame-causal mask."""
     cfg = get_config("wan")
     w, wd = device_weights(cfg, seed=7)
     st = Stream(cfg, seed=7, pooled=True)
