@@ -600,8 +600,10 @@ def configs_report(args):
             for f0 in range(0, prefill_frames, 3):
                 layer.write(fill(l, f0), f0, 3)
         first = prefill_frames
-        attend = (lambda layer, *a, **k: layer.attend_latent(*a, **k)) if args.configs_form == "latent" else \
-            (lambda layer, *a, **k: layer.attend(*a, **k))
+        method = {("latent", False): "attend_latent", ("selected", False): "attend",
+                  ("latent", True): "attend_latent_frame_causal",
+                  ("selected", True): "attend_frame_causal"}[(args.configs_form, args.configs_causal)]
+        attend = lambda layer, *a, **k: getattr(layer, method)(*a, **k)
         for l, layer in enumerate(layers):  # warm-up chunk, rewritten in the timed run
             layer.write(fill(l, first), first, 3)
             attend(layer, qn, qr, first, 3, out=out)
@@ -646,7 +648,8 @@ def configs_report(args):
         ms, fl, slots = run(name, B, n_chunks, prefill)
         print(json.dumps({
             "report": f"Wan2.1-1.3B-shaped workload: {what}, 1 MI355X",
-            "config": name, "form": args.configs_form, "streams": B, "layers": 30, "chunks": n_chunks,
+            "config": name, "form": args.configs_form, "mask": "frame-causal" if args.configs_causal else "none",
+            "streams": B, "layers": 30, "chunks": n_chunks,
             "total_ms": round(ms, 2),
             "ms_per_layer_chunk": round(ms / (30 * n_chunks), 4),
             "ms_per_chunk_all_layers": round(ms / n_chunks, 3),
@@ -678,6 +681,9 @@ def main():
     ap.add_argument("--configs-form", choices=["latent", "selected"], default="latent",
                     help="attention form of --configs: the latent form (mla_chunk_attend_latent, the benchmark's "
                          "kernel) or the one mla_chunk_attend selects for the shape")
+    ap.add_argument("--configs-causal", action="store_true",
+                    help="--configs with the frame-causal mask inside each chunk (the attention FLOPs stay "
+                         "those of the unmasked step)")
     ap.add_argument("--latent-sweep", action="store_true",
                     help="time the step at every latent width with kernels (one report line each) and exit")
     ap.add_argument("--mfma-ceiling", action="store_true",
