@@ -494,10 +494,11 @@ def projections_report(cfg, args):
         "output_project": lambda: layer.project_output(o, cfg.chunk_frames, out=u),
         "layer_step": lambda: layer.step(x, chunk_first, cfg.chunk_frames),
         "layer_step_fused": lambda: fused.step(x, chunk_first, cfg.chunk_frames),
-        # the latent form (frame-causal): one call (query latent and cache
-        # write in one product over x) against the four calls one by one
-        "layer_step_latent_one_call": lambda: layer.step(x, chunk_first, cfg.chunk_frames, frame_causal=True),
-        "layer_step_latent_four_calls": lambda: layer.step_composed(x, chunk_first, cfg.chunk_frames,
+        # frame-causal layer step (the form mla_chunk_attend_form names): one
+        # call (query latent and cache write in one product over x) against
+        # the four calls one by one
+        "layer_step_causal_one_call": lambda: layer.step(x, chunk_first, cfg.chunk_frames, frame_causal=True),
+        "layer_step_causal_four_calls": lambda: layer.step_composed(x, chunk_first, cfg.chunk_frames,
                                                                     frame_causal=True),
         "library_query": lambda: lin(lin(x2, w["w_dq"]), w_q),
         "library_output": lambda: lin(o2, w["w_o"]),
@@ -539,8 +540,8 @@ def projections_report(cfg, args):
         "layer_step_fused_ms": round(ms["layer_step_fused"], 4),
         "layer_step_form": {mla.FORM_LATENT: "latent", mla.FORM_HEADS: "per-head"}[
             mla.chunk_attend_form(layer.shape, cfg.chunk_frames)],
-        "layer_step_latent_frame_causal_one_call_ms": round(ms["layer_step_latent_one_call"], 4),
-        "layer_step_latent_frame_causal_four_calls_ms": round(ms["layer_step_latent_four_calls"], 4),
+        "layer_step_frame_causal_one_call_ms": round(ms["layer_step_causal_one_call"], 4),
+        "layer_step_frame_causal_four_calls_ms": round(ms["layer_step_causal_four_calls"], 4),
         "projections_share_of_layer": round((ms["query_project"] + ms["output_project"]) / ms["layer_step"], 4),
         "finite": bool(torch.isfinite(u.float()).all()),
         "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic"}), flush=True)
