@@ -66,13 +66,24 @@ __device__ __forceinline__ void slot_ranks(const HeadsParams& p, int b, int lane
 // ---------------------------------------------------------------- expansion
 // k_exp / v_exp rows of 512 keys of one head of one stream. Both weight
 // matrices of the head are staged in LDS; each wave takes 64 keys and
-// computes out^T = W c^T in 16 x 16 blocks, so a lane holds four consecutive
-// outputs of one key and stores them as one 8-byte piece.
+// computes out^T = W c^T in 16 x 16 blocks. The staged weight rows are
+// permuted so that the blocks 2m and 2m + 1 leave a lane with outputs
+// 32 m + 8 lg .. 32 m + 8 lg + 7 of one key (lg = lane / 16), stored as one
+// 16-byte piece; the four lanes of a key write 64 contiguous bytes.
+// Staged row of output feature d (within one matrix): block nb = 2 (d / 32)
+// + ((d mod 8) >= 4), row 4 ((d mod 32) / 8) + d mod 4 of that block.
+__host__ __device__ constexpr int expand_row(int d) {
+  return (2 * (d / 32) + ((d % 8) >= 4 ? 1 : 0)) * 16 + 4 * ((d % 32) / 8) + d % 4;
+}
+
 template <int DC, int DR, int DH>
 __global__ __launch_bounds__(512) void expand_kv_kernel(HeadsParams p) {
   constexpr int LSW = DC + 16;  // LDS row stride of the staged weights (elements)
   constexpr int NKC = DC / 32;
   constexpr int NNB = DH / 16;
+  constexpr int CPW = DC / 8;                  // 16-byte pieces per weight row
+  constexpr int WPT = (2 * DH * CPW + 511) / 512;  // pieces per thread
+  static_assert(DH % 32 == 0, "pairs of 16-row blocks");
   __shared__ __attribute__((aligned(16))) bf16 wl[2 * DH * LSW];
   __shared__ int slot_of[kSlots];
   __shared__ int n_valid_sh;
@@ -80,19 +91,24 @@ __global__ __launch_bounds__(512) void expand_kv_kernel(HeadsParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   if (wave == 0) slot_ranks(p, b, lane, slot_of, &n_valid_sh);
-  for (int e = tid; e < 2 * DH * (DC / 8); e += 512) {
-    const int r = e / (DC / 8), c8 = (e - r * (DC / 8)) * 8;
-    const bf16* src = (const bf16*)(r < DH ? p.w_uk : p.w_uv) + ((size_t)h * DH + (r < DH ? r : r - DH)) * DC + c8;
-    store8<bf16>(wl + r * LSW + c8, load8<bf16>(src));
+  // every weight piece of this thread requested before any is written to LDS
+  bf16x8 wst[WPT];
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int e = tid + 512 * i;
+    if (e < 2 * DH * CPW) {
+      const int r = e / CPW, c8 = (e - r * CPW) * 8;
+      wst[i] = load8<bf16>((const bf16*)(r < DH ? p.w_uk : p.w_uv) + ((size_t)h * DH + (r < DH ? r : r - DH)) * DC + c8);
+    }
   }
-  __syncthreads();
+  __syncthreads();  // slot ranks
   const int n_keys = n_valid_sh * p.T;
+  if (blockIdx.x * kExpKeys >= n_keys) return;  // the whole work-group past the window
   const int v0 = blockIdx.x * kExpKeys + wave * 64;
-  if (v0 >= n_keys) return;
 
   // c of this wave's 64 keys (keys past the window alias the last key; their
   // outputs are not stored), as the B operand: key li of block mb, dims
-  // kc * 32 + lg * 8
+  // kc * 32 + lg * 8; requested before the weights land in LDS
   const bf16* cache_b = (const bf16*)p.cache + (size_t)b * p.W * p.T * (DC + DR);
   bf16x8 cb[4][NKC];
 #pragma unroll
@@ -103,25 +119,44 @@ __global__ __launch_bounds__(512) void expand_kv_kernel(HeadsParams p) {
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) cb[mb][kc] = load8<bf16>(row + kc * 32 + lg * 8);
   }
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int e = tid + 512 * i;
+    if (e < 2 * DH * CPW) {
+      const int r = e / CPW, c8 = (e - r * CPW) * 8;
+      const int m = r < DH ? 0 : 1, d = r - m * DH;
+      store8<bf16>(wl + (m * DH + expand_row(d)) * LSW + c8, wst[i]);
+    }
+  }
+  __syncthreads();
+  if (v0 >= n_keys) return;
+
   const size_t head_rows = (size_t)(b * p.H + h) * p.W * p.T;
+  const bool full = v0 + 64 <= n_keys;
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
     bf16* dst = (bf16*)(which == 0 ? p.k_exp : p.v_exp) + head_rows * DH;
-#pragma unroll 2
-    for (int nb = 0; nb < NNB; ++nb) {
-      f32x4 acc[4] = {};
+#pragma unroll 1
+    for (int m = 0; m < NNB / 2; ++m) {
+      f32x4 acc[2][4] = {};
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        const bf16x8 a = lds_load8<bf16>(wl + (which * DH + nb * 16 + li) * LSW + kc * 32 + lg * 8);
+      for (int half = 0; half < 2; ++half) {
+        const int nb = 2 * m + half;
+        bf16x8 a[NKC];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[mb] = mma16(a, cb[mb][kc], acc[mb]);
+        for (int kc = 0; kc < NKC; ++kc) a[kc] = lds_load8<bf16>(wl + (which * DH + nb * 16 + li) * LSW + kc * 32 + lg * 8);
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) acc[half][mb] = mma16(a[kc], cb[mb][kc], acc[half][mb]);
       }
-      // lane: outputs nb * 16 + lg * 4 + (0..3) of key v0 + mb * 16 + li
+      // lane: outputs 32 m + 8 lg + (0..7) of key v0 + 16 mb + li
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const int v = v0 + mb * 16 + li;
-        if (v < n_keys)
-          store4_bf16(dst + (size_t)v * DH + nb * 16 + lg * 4, acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
+        float f[8] = {acc[0][mb][0], acc[0][mb][1], acc[0][mb][2], acc[0][mb][3],
+                      acc[1][mb][0], acc[1][mb][1], acc[1][mb][2], acc[1][mb][3]};
+        if (full || v < n_keys) store8<bf16>(dst + (size_t)v * DH + m * 32 + lg * 8, pack8<bf16>(f));
       }
     }
   }
