@@ -149,7 +149,8 @@ def test_layer_step_where_the_per_head_form_is_taken(fused):
     queries, so the layer step takes the per-head attention (also when the
     absorbed query weights are set, since the per-head weights are there
     too); chunk after chunk through ring wrap against O.layer_step, and the
-    frame-causal step on the same layer (latent form) in between."""
+    frame-causal step on the same layer (which, with one chunk frame, masks
+    nothing) in between."""
     cfg = get_config("wan_small").with_(grid_y=32, grid_x=64, window_frames=3, chunk_frames=1)
     w, wd = _weights(cfg, 58)
     layer = LatentLayer(cfg, wd, batch=1, rope_n_t=64)
@@ -165,6 +166,25 @@ def test_layer_step_where_the_per_head_form_is_taken(fused):
         torch.cuda.synchronize()
         ref, _, _, _ = O.layer_step(O.dims_of(cfg), w, ring, x, f0, frame_causal=causal)
         assert_step_close(to_numpy(u)[0], ref, cfg.dtype, label=f"per-head layer step fused={fused} frame {f0}")
+
+
+def test_layer_step_frame_causal_per_head_form():
+    """Two-frame chunks of 2048-token frames (32 x 64 grid) over a 3-frame
+    ring: the frame-causal layer step takes the per-head form, and the
+    queries of a chunk's first frame must not see its second frame; two
+    chunks (the second after the ring wrapped) against O.layer_step."""
+    cfg = get_config("wan_small").with_(grid_y=32, grid_x=64, window_frames=3, chunk_frames=2)
+    w, wd = _weights(cfg, 59)
+    layer = LatentLayer(cfg, wd, batch=1, rope_n_t=64)
+    assert mla.chunk_attend_form(layer.shape, 2) == mla.FORM_HEADS
+    ring = O.RingCache(cfg.window_frames, cfg.tokens_per_frame, cfg.d_c, cfg.d_rope)
+    st = Stream(cfg, seed=59)
+    for f0 in (0, 2):
+        x = st.xs(f0, 2)
+        u = layer.step(to_torch(x[None], cfg.dtype), f0, 2, frame_causal=True)
+        torch.cuda.synchronize()
+        ref, _, _, _ = O.layer_step(O.dims_of(cfg), w, ring, x, f0, frame_causal=True)
+        assert_step_close(to_numpy(u)[0], ref, cfg.dtype, label=f"per-head frame-causal layer step frame {f0}")
 
 
 def test_layer_step_frame_causal():
