@@ -67,15 +67,10 @@ __device__ __forceinline__ void slot_ranks(const HeadsParams& p, int b, int lane
 // k_exp / v_exp rows of 512 keys of one head of one stream. Both weight
 // matrices of the head are staged in LDS; each wave takes 64 keys and
 // computes out^T = W c^T in 16 x 16 blocks. The staged weight rows are
-// permuted so that the blocks 2m and 2m + 1 leave a lane with outputs
-// 32 m + 8 lg .. 32 m + 8 lg + 7 of one key (lg = lane / 16), stored as one
-// 16-byte piece; the four lanes of a key write 64 contiguous bytes.
-// Staged row of output feature d (within one matrix): block nb = 2 (d / 32)
-// + ((d mod 8) >= 4), row 4 ((d mod 32) / 8) + d mod 4 of that block.
-__host__ __device__ constexpr int expand_row(int d) {
-  return (2 * (d / 32) + ((d % 8) >= 4 ? 1 : 0)) * 16 + 4 * ((d % 32) / 8) + d % 4;
-}
-
+// in expand_pos order, so the blocks 2m and 2m + 1 leave a lane with
+// outputs 32 m + 8 lg .. 32 m + 8 lg + 7 of one key (lg = lane / 16),
+// stored as one 16-byte piece; the four lanes of a key write 64 contiguous
+// bytes.
 template <int DC, int DR, int DH>
 __global__ __launch_bounds__(512) void expand_kv_kernel(HeadsParams p) {
   constexpr int LSW = DC + 16;  // LDS row stride of the staged weights (elements)
@@ -125,7 +120,7 @@ __global__ __launch_bounds__(512) void expand_kv_kernel(HeadsParams p) {
     if (e < 2 * DH * CPW) {
       const int r = e / CPW, c8 = (e - r * CPW) * 8;
       const int m = r < DH ? 0 : 1, d = r - m * DH;
-      store8<bf16>(wl + (m * DH + expand_row(d)) * LSW + c8, wst[i]);
+      store8<bf16>(wl + (m * DH + expand_pos(d)) * LSW + c8, wst[i]);
     }
   }
   __syncthreads();

@@ -163,6 +163,30 @@ __device__ __forceinline__ f32x8 lds_tr8(const float* m, int stride, int rowA, i
   return v;
 }
 
+// Output-feature order of the projection kernels that store 8-element
+// pieces: a weight whose output features are staged at position
+// expand_pos(d) (as rows, or as columns read through lds_tr8) makes the
+// 16 x 16 output blocks 2m and 2m + 1 of a product leave lane l (g = l / 16)
+// with features 32 m + 8 g .. 32 m + 8 g + 7 of one column (the C layout
+// holds rows 4 g .. 4 g + 3 of each block), stored as one piece. Features
+// 4 j .. 4 j + 3 stay consecutive.
+__host__ __device__ constexpr int expand_pos(int d) {
+  return (2 * (d / 32) + ((d % 8) >= 4 ? 1 : 0)) * 16 + 4 * ((d % 32) / 8) + d % 4;
+}
+
+// Elements 4 h .. 4 h + 3 of an 8-element vector to p (8-byte aligned for
+// bf16, 16-byte for float).
+template <typename T>
+__device__ __forceinline__ void store_half8(T* p, typename V8<T>::type v, int h) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 u = __builtin_bit_cast(u32x4, v);
+    *reinterpret_cast<u32x2*>(p) = h == 0 ? u32x2{u.x, u.y} : u32x2{u.z, u.w};
+  } else {
+    const u32x8 u = __builtin_bit_cast(u32x8, v);
+    *reinterpret_cast<u32x4*>(p) = h == 0 ? u32x4{u[0], u[1], u[2], u[3]} : u32x4{u[4], u[5], u[6], u[7]};
+  }
+}
+
 // 8 consecutive elements from LDS (16-byte aligned).
 template <typename T>
 __device__ __forceinline__ typename V8<T>::type lds_load8(const T* p) {
