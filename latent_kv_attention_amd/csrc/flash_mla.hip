@@ -162,6 +162,16 @@ __global__ __launch_bounds__(256) void rope_window_kernel(FlashParams p) {
   const int n_tp = p.rl.d_t / 2;
   for (int b = blockIdx.z; b < p.batch; b += gridDim.z) {
     const int32_t* sf = p.slot_frame + (size_t)b * p.W;
+    // this unit's kR values and spatial angles, requested before the slot's
+    // rank and temporal angles (neither depends on them)
+    float a[8];
+    float cs[4], sn[4];
+    if (active) {
+      unpack8<T>(load8<T>((const T*)p.cache + (((size_t)b * p.W + slot) * p.T + tok) * (DC + DR) + DC + 8 * q), a);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * q + j >= n_tp) rope_cos_sin(p.rl, p.tables, 4 * q + j, 0, y, x, cs[j], sn[j]);
+    }
     const int f = sf[slot];  // uniform over the work-group
     if (f < 0) continue;
     __syncthreads();  // the previous stream's rank and angles are no longer read
@@ -181,20 +191,14 @@ __global__ __launch_bounds__(256) void rope_window_kernel(FlashParams p) {
     }
     __syncthreads();
     if (!active) continue;
-    const T* src = (const T*)p.cache + (((size_t)b * p.W + slot) * p.T + tok) * (DC + DR) + DC + 8 * q;
-    float a[8];
-    unpack8<T>(load8<T>(src), a);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = 4 * q + j;
-      float cs, sn;
       if (k < n_tp) {
-        cs = t_cs[0][k];
-        sn = t_cs[1][k];
-      } else {
-        rope_cos_sin(p.rl, p.tables, k, 0, y, x, cs, sn);
+        cs[j] = t_cs[0][k];
+        sn[j] = t_cs[1][k];
       }
-      rotate_pair(a[2 * j], a[2 * j + 1], cs, sn);
+      rotate_pair(a[2 * j], a[2 * j + 1], cs[j], sn[j]);
     }
     T* dst = (T*)p.krot + ((size_t)b * p.W * p.T + (size_t)rank_sh * p.T + tok) * DR + 8 * q;
     store8<T>(dst, pack8<T>(a));
