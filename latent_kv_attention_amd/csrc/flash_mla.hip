@@ -123,13 +123,15 @@ struct FlashTile {
   static constexpr int KR_ELEMS = kBN * DR;
   static constexpr int KR_INSTR = (kBN * RCK + 63) / 64;
   static constexpr int KR_INSTR_WAVE = (KR_INSTR + kWaves - 1) / kWaves;
-  // unit slot of unit u of tile key n (an involution in u): 16 / U8 keys
-  // fill one 256-byte bank cycle, and the XOR moves the next such group of
-  // keys to other units, so the 16 keys of one bf16 S^T read land in 16
-  // different bank groups
+  // unit slot of unit u of tile key n (an involution in u), chosen by
+  // measuring the bank conflicts of the S^T reads (16 keys, one unit each)
+  // per layout: with 64-byte bf16 keys (4 units) keys 8 apart take
+  // disjoint unit pairs (conflict-free; XOR by (n / 4) mod 4 conflicted
+  // 2-way), with 128-byte keys XOR by (n / 2) mod 8 is conflict-free
   static constexpr int KR_SH = U8 >= 16 ? 0 : U8 == 8 ? 1 : U8 == 4 ? 2 : U8 == 2 ? 3 : 4;  // log2(16 / U8)
   __host__ __device__ static constexpr int kr_slot(int n, int u) {
-    return U8 > 1 && U8 <= 16 ? (u ^ ((n >> KR_SH) & (U8 - 1))) : u;
+    return sizeof(T) == 2 && U8 == 4 ? (u ^ (((n >> 3) & 1) * 2))
+                                     : U8 > 1 && U8 <= 16 ? (u ^ ((n >> KR_SH) & (U8 - 1))) : u;
   }
   static_assert(DC % 16 == 0 && DR % 8 == 0 && (DR / 8 & (DR / 8 - 1)) == 0,
                 "latent in 16-wide blocks; kR in a power-of-two number of 8-element units");

@@ -205,9 +205,13 @@ struct HeadsTile {
   static constexpr int LSV = DH + 16;          // v rows: four rows of a transposing read hit disjoint banks
   static constexpr int CPRK = LSK / 8, CPRV = LSV / 8, CH = DH / 8;
   static constexpr int U8 = DR / 8;            // 16-byte kR units per key
+  // kR unit u of key n sits at kr_slot(n, u), chosen by measuring the bank
+  // conflicts of the QK reads per layout: with 64-byte keys (4 units) keys 8
+  // apart take disjoint unit pairs (XOR by (n / 4) mod 4 conflicted 2-way),
+  // with 128-byte keys XOR by (n / 2) mod 8 is conflict-free
   static constexpr int KR_SH = U8 >= 16 ? 0 : U8 == 8 ? 1 : U8 == 4 ? 2 : U8 == 2 ? 3 : 4;
   __host__ __device__ static constexpr int kr_slot(int n, int u) {
-    return U8 > 1 && U8 <= 16 ? (u ^ ((n >> KR_SH) & (U8 - 1))) : u;
+    return U8 == 4 ? (u ^ (((n >> 3) & 1) * 2)) : U8 > 1 && U8 <= 16 ? (u ^ ((n >> KR_SH) & (U8 - 1))) : u;
   }
   static constexpr int instr(int keys, int chunks_per_key) { return (keys * chunks_per_key + 63) / 64; }
   static constexpr int buf_bytes(int keys) {
