@@ -105,7 +105,7 @@ template <typename T, int DC, int DR>
 __global__ __launch_bounds__(kAbsorbThreads) void absorb_q_wide_kernel(AbsorbParams p) {
   typedef typename V8<T>::type v8;
   constexpr int KP = (DC + DR + 31) / 32 * 32;
-  constexpr int PADE = 16 / sizeof(T);
+  constexpr int PADE = 32 / sizeof(T);  // 32-byte row pad: a stride of 2 mod 4 16-byte chunks
   constexpr int LS = DC + PADE;
   constexpr int CPR = DC / 8;  // 8-element pieces per weight row
   constexpr int NKM = kAbsorbWideMaxHead / 32;

@@ -75,7 +75,7 @@ template <typename T, int DC>
 __global__ __launch_bounds__(256) void up_v_wide_kernel(UpVParams p) {
   typedef typename V8<T>::type v8;
   constexpr int NKC = DC / 32;
-  constexpr int PADE = 16 / sizeof(T);
+  constexpr int PADE = 32 / sizeof(T);  // 32-byte row pad: a stride of 2 mod 4 16-byte chunks
   constexpr int LS = DC + PADE;
   constexpr int CPR = DC / 8;  // 8-element pieces per weight row
   constexpr int WPT = (kUpVWideMaxHead * CPR + 255) / 256;
