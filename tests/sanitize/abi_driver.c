@@ -138,6 +138,26 @@ int main(void) {
   EXPECT(mla_chunk_attend_frame_causal(&s, p, p, 18, 3, p, p, p, sf, tab, 0, 21, p, p, big, NULL), MLA_ERR_HIP);
   EXPECT(mla_chunk_attend_heads(&s, p, p, 18, 3, p, p, p, sf, tab, 0, 21, p, p, 16, NULL), MLA_ERR_WORKSPACE);
   EXPECT(mla_chunk_attend_heads(&s, p, p, 18, 3, p, p, p, sf, tab, 0, 21, p, p, big, NULL), MLA_ERR_HIP);
+  EXPECT(mla_chunk_attend_latent_frame_causal(&s, p, p, 18, 3, p, p, p, sf, tab, 0, 21, p, p, 16, NULL),
+         MLA_ERR_WORKSPACE);
+  EXPECT(mla_chunk_attend_latent_frame_causal(&s, p, p, 18, 3, p, p, p, sf, tab, 0, 21, p, p, big, NULL), MLA_ERR_HIP);
+  EXPECT(mla_chunk_attend_heads_frame_causal(&s, p, p, 18, 3, p, p, p, sf, tab, 0, 21, p, p, 16, NULL),
+         MLA_ERR_WORKSPACE);
+  EXPECT(mla_chunk_attend_heads_frame_causal(&s, p, p, 18, 3, p, p, p, sf, tab, 0, 21, p, p, big, NULL), MLA_ERR_HIP);
+  {
+    /* several streams: both plans deal whole row blocks in rounds, also
+       with the row-block classes of the frame-causal mask */
+    mla_shape t = s;
+    t.batch = 8;
+    EXPECT(mla_chunk_attend_latent_frame_causal(&t, p, p, 18, 3, p, p, p, sf, tab, 0, 21, p, p, big, NULL), MLA_ERR_HIP);
+    EXPECT(mla_chunk_attend_heads_frame_causal(&t, p, p, 18, 3, p, p, p, sf, tab, 0, 21, p, p, big, NULL), MLA_ERR_HIP);
+    EXPECT(mla_chunk_attend_frame_causal(&t, p, p, 18, 3, p, p, p, sf, tab, 0, 21, p, p, big, NULL), MLA_ERR_HIP);
+    EXPECT(mla_chunk_attend(&t, p, p, 18, 3, p, p, p, sf, tab, 0, 21, p, p, big, NULL), MLA_ERR_HIP);
+    /* a 64-frame chunk over a 64-frame window: the most row-block classes a plan builds */
+    t.window_frames = 64;
+    EXPECT(mla_chunk_attend_heads_frame_causal(&t, p, p, 0, 64, p, p, p, sf, tab, 0, 64, p, p, big, NULL), MLA_ERR_HIP);
+    EXPECT(mla_chunk_attend_latent_frame_causal(&t, p, p, 0, 64, p, p, p, sf, tab, 0, 64, p, p, big, NULL), MLA_ERR_HIP);
+  }
 
   /* query path and output projection */
   EXPECT(mla_query_project(&s, 576, p, 3, p, p, NULL, p, p, p, NULL), MLA_ERR_NULL);
