@@ -11,11 +11,17 @@
 // bf16 with hidden = 1536 (the Wan2.1-1.3B width): work-group tiles of 80
 // token rows x 64 outputs (236 tiles for a 3-frame Wan chunk, all resident
 // at once). Both operands stream through LDS in 128-wide K steps with direct
-// global->LDS loads, two steps in flight; each staged row is 256 bytes and
-// its 16-byte chunks are XOR-permuted by the row index so the 16 rows that a
-// matrix-core operand read touches hit different banks. Each wave owns one
-// 16-column block of all five 16-row blocks. The output tile goes through
-// LDS once more so that rows leave in 16-byte stores.
+// global->LDS loads, two steps in flight through four stage buffers; each
+// staged row is 256 bytes and its 16-byte chunks are XOR-permuted by the row
+// index so the 16 rows that a matrix-core operand read touches hit different
+// banks. The four waves split the tile 2 x 2 (two or three 16-row blocks by
+// two 16-column blocks). A wave reads the operands of the next K step into
+// a second register set while the products of the current one run, one
+// read between two products, so that the LDS and the matrix cores of a
+// compute unit work at the same time (the barrier of each step keeps the
+// waves in step, so with reads and products in separate phases the whole
+// unit alternated between the two). The output tile goes through LDS once
+// more so that rows leave in 16-byte stores.
 //
 // Other shapes (fp32, small latents, other widths) use a plain kernel
 // with 64 x 32 tiles and operands loaded straight from global memory.
@@ -38,10 +44,10 @@ constexpr int kSInstr = kSRows * kSChunks / 64;   // direct-load instructions pe
 constexpr int kSInstrWave = (kSInstr + 3) / 4;    // per wave (9)
 constexpr int kSElems = kSRows * kSK;             // bf16 elements per stage buffer
 constexpr int kSOutLd = kSN + 8;                  // output staging row stride (elements)
-constexpr int kSBufs = 3;                         // stage buffers; kSBufs - 1 stages in flight
 static_assert(kSRows * kSChunks % 64 == 0, "whole direct-load instructions per stage");
 static_assert(kSM * kSOutLd <= kSElems, "output staging fits in one stage buffer");
-static_assert(kSBufs == 3 && (kSBufs - 2) * kSInstrWave < 64, "three named stage buffers; vmcnt range");
+static_assert(2 * kSInstrWave < 64, "vmcnt range");
+static_assert(4 * kSElems * 2 <= 160 * 1024, "four stage buffers fit in LDS");
 }  // namespace
 
 // Wait until at most N vector-memory operations of this wave are in flight.
@@ -51,9 +57,105 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// The same, and also until this wave's LDS operations have all returned.
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
 // XCD-major order: consecutive logical tiles (which share token rows) land on
 // one XCD, whose L2 then serves the repeated x reads.
 __device__ __forceinline__ int xcd_logical(int id, int per_xcd) { return (id % kXcds) * per_xcd + id / kXcds; }
+
+// One wave's share of the K loop: NMB row blocks from rb0 on by the two
+// column blocks from column 32 wc on. Four stage buffers; iteration s waits
+// for this wave's loads of stage s + 1 (stage s + 2 may stay in flight),
+// meets the other waves at a barrier (every wave's loads of s + 1 have
+// landed, and every wave has finished the products of s - 1, whose buffer
+// stage s + 3 now takes), starts stage s + 3, and then reads the operands of
+// s + 1 into one register set while the products of s run from the other,
+// reads and products interleaved one for one so that the LDS and the matrix
+// cores work at the same time. The barrier is the bare instruction: a full
+// __syncthreads() would also wait for every outstanding load. The stage
+// loop is unrolled completely (NSTAGE is a template parameter) so that every
+// buffer is known at compile time and the compiler adds no waits of its own
+// for the loads still in flight.
+template <int NSTAGE, int NMB, typename Issue>
+__device__ __forceinline__ void staged_loop(bool active, int wc, int rb0, Issue& issue, bf16* sb0, bf16* sb1,
+                                            bf16* sb2, bf16* sb3, f32x4 (&acc)[3][2]) {
+  const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+  struct Ops {
+    bf16x8 b[kSK / 32][2], a[kSK / 32][NMB];
+  };
+  // staged row r, logical chunk c -> element (r * kSChunks + (c ^ (r % kSChunks))) * 8
+  auto read_ops = [&](const bf16* buf, Ops& o) {
+#pragma unroll
+    for (int kc = 0; kc < kSK / 32; ++kc) {
+      const int c = kc * 4 + lg;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int rb = kSM + wc * 32 + cb * 16 + li;
+        o.b[kc][cb] = load8<bf16>(buf + (rb * kSChunks + (c ^ (rb & (kSChunks - 1)))) * 8);
+      }
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int ra = (rb0 + mb) * 16 + li;
+        o.a[kc][mb] = load8<bf16>(buf + (ra * kSChunks + (c ^ (ra & (kSChunks - 1)))) * 8);
+      }
+    }
+  };
+  auto products = [&](const Ops& o) {
+#pragma unroll
+    for (int kc = 0; kc < kSK / 32; ++kc)
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) acc[mb][cb] = mma16(o.a[kc][mb], o.b[kc][cb], acc[mb][cb]);
+  };
+  constexpr int kReads = (kSK / 32) * (2 + NMB), kProducts = (kSK / 32) * NMB * 2;
+  auto buf = [&](int i) -> bf16* { return i == 0 ? sb0 : i == 1 ? sb1 : i == 2 ? sb2 : sb3; };
+  Ops ops[2];
+#pragma unroll
+  for (int s = 0; s < 3 && s < NSTAGE; ++s) issue(s, buf(s));
+  if (NSTAGE >= 3)
+    wait_vm<2 * kSInstrWave>();
+  else if (NSTAGE == 2)
+    wait_vm<kSInstrWave>();
+  else
+    wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  if (active) read_ops(buf(0), ops[0]);
+#pragma unroll
+  for (int s = 0; s < NSTAGE; ++s) {
+    if (s + 1 < NSTAGE) {
+      // the LDS reads of stage s, issued one iteration ago, are waited for
+      // here too, where they have long returned: a count of 15 cannot say
+      // "all but the reads issued next", so a wait the compiler placed among
+      // the products would wait for those as well
+      if (s + 2 < NSTAGE)
+        wait_vm_lds<kSInstrWave>();
+      else
+        wait_vm_lds<0>();
+      __builtin_amdgcn_s_barrier();
+      if (s + 3 < NSTAGE) issue(s + 3, buf((s + 3) % 4));
+      if (active) {
+        read_ops(buf((s + 1) % 4), ops[(s + 1) & 1]);
+        products(ops[s & 1]);
+        // one read, one product, ... then the reads left over
+#pragma unroll
+        for (int i = 0; i < kProducts; ++i) {
+          if (i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        if (kReads > kProducts) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kProducts, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    } else if (active) {
+      products(ops[s & 1]);
+    }
+  }
+}
 
 template <int NSTAGE>
 __global__ __launch_bounds__(256) void cache_write_staged_kernel(CacheWriteParams p, int n_tiles_n, int n_logical,
@@ -61,6 +163,7 @@ __global__ __launch_bounds__(256) void cache_write_staged_kernel(CacheWriteParam
   __shared__ __attribute__((aligned(16))) bf16 sb0[kSElems];
   __shared__ __attribute__((aligned(16))) bf16 sb1[kSElems];
   __shared__ __attribute__((aligned(16))) bf16 sb2[kSElems];
+  __shared__ __attribute__((aligned(16))) bf16 sb3[kSElems];
   const int logical = xcd_logical(blockIdx.x, per_xcd);
   if (logical >= n_logical) return;
   const int row0 = (logical / n_tiles_n) * kSM;
@@ -110,69 +213,31 @@ __global__ __launch_bounds__(256) void cache_write_staged_kernel(CacheWriteParam
                                        (MLA_LDS void*)(MLA_LDS bf16*)(buf + dst_off[k]), 16, 0, 0);
   };
 
-  const bool active = col0 + wave * 16 < n_out;  // this wave's 16 outputs exist
-  f32x4 acc[kSM / 16] = {};
-  // operand reads: staged row r, logical chunk c -> element (r * kSChunks + (c ^ (r % kSChunks))) * 8
-  // all of a stage's operand reads first, then its products: with one wave
-  // per SIMD nothing else hides the LDS latency, so the reads go out
-  // together and the products follow (9% faster than reading each operand
-  // just before its product)
-  auto compute = [&](const bf16* buf) {
-    if (!active) return;
-    bf16x8 bop[kSK / 32], aop[kSK / 32][kSM / 16];
-#pragma unroll
-    for (int kc = 0; kc < kSK / 32; ++kc) {
-      const int c = kc * 4 + lg;
-      const int rb = kSM + wave * 16 + li;
-      bop[kc] = load8<bf16>(buf + (rb * kSChunks + (c ^ (rb & (kSChunks - 1)))) * 8);
-#pragma unroll
-      for (int mb = 0; mb < kSM / 16; ++mb) {
-        const int ra = mb * 16 + li;
-        aop[kc][mb] = load8<bf16>(buf + (ra * kSChunks + (c ^ (ra & (kSChunks - 1)))) * 8);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kc = 0; kc < kSK / 32; ++kc)
-#pragma unroll
-      for (int mb = 0; mb < kSM / 16; ++mb) acc[mb] = mma16(aop[kc][mb], bop[kc], acc[mb]);
-  };
-
-  // kSBufs - 1 stages in flight: wait for this wave's loads of stage s
-  // (leaving the kSBufs - 2 later ones outstanding), barrier, start stage
-  // s + kSBufs - 1 into the buffer that stage s - 1 used, compute stage s. The
-  // barrier is the bare instruction: a full __syncthreads() would also wait
-  // for every outstanding load. The stage loop is unrolled completely
-  // (NSTAGE = hidden / 64 is a template parameter) so that every buffer is
-  // known at compile time and the compiler adds no waits of its own for the
-  // loads still in flight.
-  auto buf = [&](int i) -> bf16* { return i == 0 ? sb0 : i == 1 ? sb1 : sb2; };
-#pragma unroll
-  for (int s = 0; s < kSBufs - 1 && s < NSTAGE; ++s) issue(s, buf(s));
-#pragma unroll
-  for (int s = 0; s < NSTAGE; ++s) {
-    // stages issued after s that may stay in flight (folds to a constant)
-    switch (min(NSTAGE - 1 - s, kSBufs - 2)) {
-      case 0: wait_vm<0>(); break;
-      case 1: wait_vm<kSInstrWave>(); break;
-      case 2: wait_vm<2 * kSInstrWave>(); break;
-      case 3: wait_vm<3 * kSInstrWave>(); break;
-      default: wait_vm<4 * kSInstrWave>(); break;
-    }
-    __builtin_amdgcn_s_barrier();
-    if (s + kSBufs - 1 < NSTAGE) issue(s + kSBufs - 1, buf((s + kSBufs - 1) % kSBufs));
-    compute(buf(s % kSBufs));
-  }
+  // Waves in 2 x 2: wave w takes outputs 32 (w & 1) .. + 32 (two 16-column
+  // blocks) of row blocks 0-1 (w < 2) or 2-4 (w >= 2).
+  const int wr = wave >> 1, wc = wave & 1;
+  const int rb0 = wr == 0 ? 0 : 2;
+  const bool active = col0 + wc * 32 < n_out;  // this wave's outputs exist
+  f32x4 acc[3][2] = {};
+  if (wr == 0)
+    staged_loop<NSTAGE, 2>(active, wc, rb0, issue, sb0, sb1, sb2, sb3, acc);
+  else
+    staged_loop<NSTAGE, 3>(active, wc, rb0, issue, sb0, sb1, sb2, sb3, acc);
 
   // output tile -> LDS (bf16) -> 16-byte stores of whole row segments
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   bf16* ot = sb0;
   if (active) {
+    const int nmb = wr == 0 ? 2 : 3;
 #pragma unroll
-    for (int mb = 0; mb < kSM / 16; ++mb)
+    for (int mb = 0; mb < 3; ++mb)
+      if (mb < nmb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ot[(mb * 16 + lg * 4 + i) * kSOutLd + wave * 16 + li] = (bf16)acc[mb][i];
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            ot[((rb0 + mb) * 16 + lg * 4 + i) * kSOutLd + wc * 32 + cb * 16 + li] = (bf16)acc[mb][cb][i];
   }
   __syncthreads();
   const int n_cols = min(kSN, n_out - col0);  // a multiple of 8
