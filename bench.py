@@ -246,6 +246,51 @@ def setup_step(cfg, kv_splits, dev="cuda"):
                                  tables=tables, n_t=n_t)
 
 
+def graph_replay_writes(ctx, xs_cold, cw_bytes):
+    """GPU-side time of the chunk's cache write: len(xs_cold) writes captured
+    in one HIP graph, replayed between events on the launch stream, once over
+    the distinct (cold) x buffers and once over one buffer (warm). Each
+    replay's cache rows are compared with those of an eager write of the
+    same inputs (every buffer holds the same tokens)."""
+    import torch
+
+    import latent_kv_attention_amd as mla
+
+    cfg_frames = ctx.cache.shape[1]
+    n_frames = ctx.x_chunk.shape[0] // ctx.cache.shape[2]
+    slots = [(ctx.chunk_first + i) % cfg_frames for i in range(n_frames)]
+    w = ctx.w
+    mla.cache_write(ctx.shape, ctx.x_chunk, w["w_dkv"], w["w_kr"], ctx.chunk_first, n_frames, ctx.cache,
+                    ctx.slot_frame)
+    torch.cuda.synchronize()
+    ref = ctx.cache[:, slots].clone()
+    out = {"what": f"{len(xs_cold)} cache writes of the chunk replayed from one HIP graph, events around the replay "
+                   "(no host launch path between the kernels); per write"}
+    for label, bufs in (("cold", xs_cold), ("warm", [ctx.x_chunk] * len(xs_cold))):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for xb in bufs:
+                mla.cache_write(ctx.shape, xb, w["w_dkv"], w["w_kr"], ctx.chunk_first, n_frames, ctx.cache,
+                                ctx.slot_frame)
+        ok = True
+        times = []
+        for _ in range(3):
+            ctx.cache[:, slots] = 0
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) / len(bufs))
+            ok = ok and bool(torch.equal(ctx.cache[:, slots], ref))
+        del g
+        ms = float(min(times[1:]))
+        out[label] = {"ms": round(ms, 5), "GBps": round(cw_bytes / (ms * 1e-3) / 1e9, 1),
+                      "hbm_frac": round(cw_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "matches_eager": ok}
+    return out
+
+
 def settle_clock(ctx, window=20, tol=0.01, min_windows=5, max_windows=40):
     """The GPU raises its clock over the first tens of milliseconds of load
     after idle (set-up is mostly host work): a timed window started from idle
@@ -749,7 +794,7 @@ def main():
 
     # cold-cache cache write: rotate the input over more distinct buffers than the
     # 256 MB last-level cache holds
-    cold = copy_single = copy_bytes = None
+    cold = copy_single = copy_bytes = graph_writes = None
     if args.cold_buffers > 0:
         xs_cold = [x_chunk.clone() for _ in range(args.cold_buffers)]
         for i in range(3):
@@ -776,7 +821,13 @@ def main():
         torch.cuda.synchronize()
         copy_single = float(np.mean([a.elapsed_time(b) for a, b in ce[3:]]))
         copy_bytes = 2 * x_chunk.numel() * x_chunk.element_size()
-        del xs_cold, dst
+        del dst
+        # the same writes replayed from a HIP graph, so that the kernels run
+        # back to back with no host launch path between them: events around
+        # a replay give the GPU-side time per write, with x cold (the 40
+        # rotating buffers) and warm (one buffer 40 times)
+        graph_writes = graph_replay_writes(ctx, xs_cold, cache_write_bytes(cfg))
+        del xs_cold
 
     # larger writes, where the launch cost is spread over more bytes: a
     # 21-frame prefill of one stream, and a 3-frame chunk of 8 streams
@@ -843,6 +894,7 @@ def main():
         "cache_write_hbm_frac_cold": round(cw_bytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4) if cold else None,
         "kernel_ms": {k: round(v, 4) for k, v in per.items()},
         "cache_write_cold_ms": round(cold, 4) if cold else None,
+        "cache_write_graph": graph_writes,
         "cache_write_large": big_writes,
         "copy_reference": {"what": "device copy of a 14.38 MB x buffer (cold, single launches), reads + writes",
                            "bytes": copy_bytes, "ms": round(copy_single, 4),
